@@ -1,0 +1,225 @@
+"""Benchmark of the routed MoE block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+A step is one moe_forward (router -> top-k -> counts/offsets/positions ->
+dispatch -> grouped SwiGLU GEMMs -> combine) over one synthetic batch whose
+inputs already sit in HBM.  W untimed steps, then exactly K steps between two
+device synchronisations; one JSON line is printed.  Per-kernel durations come
+from HIP events the library records on the forward's own stream during the
+same timed steps; the dominant kernel is reported against its roofline.
+The CPU baseline times the float64 oracle on a bounded sample of the same
+batch on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from routing_dispatch_grouped_router_amd import binding as B  # noqa: E402
+from routing_dispatch_grouped_router_amd import workloads as W  # noqa: E402
+
+METRIC = "MoE-block fwd tokens/s on 1 MI355X; grouped-GEMM % MFMA peak; dispatch % HBM"
+DEFAULT_CONFIG = "bf16_e8"
+
+# MI355X published peaks
+HBM_GBPS = 8000.0
+MFMA_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}
+FP32_VECTOR_TFLOPS = 157.3
+
+
+def elem_bytes(act: str) -> int:
+    return {"f32": 4, "bf16": 2, "mxfp8": 1}[act]
+
+
+def stage_models(w: W.Workload) -> dict:
+    """Algorithmic work of one launch of each kernel: (bound, amount, unit, peak)."""
+    R, T, d, E, k, H = w.R, w.T, w.d, w.E, w.k, w.H
+    bin_ = 4 if w.act == "f32" else 2                 # x storage
+    bxe = elem_bytes(w.act)
+    bye = 4 if w.act == "f32" else 2
+    scale_b = R * d // 32 if w.act == "mxfp8" else 0
+    gemm_bound, gemm_peak = (("alu", FP32_VECTOR_TFLOPS) if w.act == "f32"
+                             else ("mfma", MFMA_TFLOPS[w.act]))
+    return {
+        "router_logits": ("hbm", T * d * bin_ + d * E * bin_ + T * E * 4, "GB/s", HBM_GBPS),
+        "route_topk": ("hbm", T * E * 4 + R * 4 * 3 + ((T + 255) // 256) * E * 4, "GB/s", HBM_GBPS),
+        "route_scan": ("hbm", 3 * ((T + 255) // 256) * E * 4 + (2 * E + 1) * 4, "GB/s", HBM_GBPS),
+        "dispatch": ("hbm", T * d * bin_ + R * d * bxe + scale_b + R * 4 * 3 + R * 4, "GB/s", HBM_GBPS),
+        "gemm1_gate_up_swiglu": (gemm_bound, 4.0 * R * d * H, "TFLOP/s", gemm_peak),
+        "gemm2_down": (gemm_bound, 2.0 * R * H * d, "TFLOP/s", gemm_peak),
+        "combine": ("hbm", R * d * bye + R * 8 + T * d * bye, "GB/s", HBM_GBPS),
+    }
+
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "gemm1_gate_up_swiglu": ["routing_dispatch_grouped_router_amd/csrc/gemm.hip",
+                             "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
+    "gemm2_down": ["routing_dispatch_grouped_router_amd/csrc/gemm.hip",
+                   "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
+    "dispatch": ["routing_dispatch_grouped_router_amd/csrc/dispatch.hip"],
+    "combine": ["routing_dispatch_grouped_router_amd/csrc/dispatch.hip"],
+}
+
+
+def measured_traffic(config: str, kernel: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    if there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    try:
+        entries = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    want = source_digest(KERNEL_SOURCES[kernel])
+    for e in entries:
+        if e.get("config") == config and e.get("kernel") == kernel and e.get("source_digest") == want:
+            return e.get("bytes_per_launch")
+    return None
+
+
+def cpu_baseline(w: W.Workload, host: dict, budget_s: float = 12.0) -> dict:
+    """Times the oracle (float64 NumPy) on the first tokens of the same batch."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    wg, wu, wd = (W.as_f64(host[n]) for n in ("w_gate", "w_up", "w_down"))
+    wr = W.as_f64(host["w_router"]) if host["w_router"] is not None else None
+
+    def run(n):
+        x = W.as_f64(host["x"][:n])
+        lg = None if host["logits"] is None else host["logits"][:n].double().numpy()
+        t0 = time.perf_counter()
+        O.forward(x, w.E, w.k, w.act, wg, wu, wd, w_router=wr, logits=lg)
+        return time.perf_counter() - t0
+
+    n = min(w.T, 256)
+    dt = run(n)
+    while dt < budget_s / 4 and n < w.T:
+        n = min(w.T, max(n * 2, int(n * budget_s / 3 / max(dt, 1e-3))))
+        dt = run(n)
+    reps, total, toks = 1, dt, n
+    while total < budget_s * 0.6 and reps < 5:
+        total += run(n)
+        toks += n
+        reps += 1
+    return {"value": toks / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle.forward (float64 NumPy) on the first {n} of {w.T} tokens of the "
+                      f"{w.name} batch, {reps} run(s), {total:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(W.ALL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the routed block: this build has no "
+              "multi-GPU path (no collectives, no sharding); run with --gpus 1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    w = W.ALL[args.config]
+    host = W.make_inputs(w)
+    d_in = {k: (None if v is None else v.to(dev)) for k, v in host.items()}
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned")
+    packed = B.pack_weights(p, d_in["w_gate"], d_in["w_up"], d_in["w_down"])
+    f = B.Forward(p, dev, debug_outputs=False)
+    if p.flags & B.MOE_LOGITS_GIVEN:
+        f.logits.copy_(d_in["logits"])
+
+    def step():
+        f(d_in["x"], packed=packed, w_router=d_in["w_router"], logits=f.logits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.set_profiling(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
+    stages = B.kernel_times()
+    B.set_profiling(False)
+    ms_step = ms_total / args.steps
+
+    models = stage_models(w)
+    stage_out = {}
+    for name, ms in stages:
+        bound, amount, unit, peak = models[name]
+        ach = (amount / (ms * 1e-3) / 1e9) if unit == "GB/s" else (amount / (ms * 1e-3) / 1e12)
+        stage_out[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(ach, 2), "unit": unit,
+                           "peak": peak, "frac": round(ach / peak, 4)}
+    dom = max(stages, key=lambda s: s[1])[0]
+    bound, amount, unit, peak = models[dom]
+    ach = stage_out[dom]["achieved"]
+    traffic = measured_traffic(w.name, dom)
+    gemm_ms = sum(ms for n, ms in stages if n.startswith("gemm"))
+    gemm_peak = models["gemm1_gate_up_swiglu"][3]
+    flops = w.expert_flops + w.router_flops
+    result = {
+        "metric": METRIC,
+        "value": round(w.T * args.steps / (ms_total * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.act,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": w.describe(), "T": w.T, "d_model": w.d, "n_experts": w.E, "top_k": w.k,
+                   "d_hidden": w.H, "router": w.router, "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                     "frac": round(ach / peak, 4), "traffic": traffic},
+        "block_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "grouped_gemm_frac_of_peak": round(6.0 * w.R * w.d * w.H / (gemm_ms * 1e-3) / 1e12 / gemm_peak, 4)
+        if gemm_ms > 0 else None,
+        "dispatch_frac_of_hbm": stage_out.get("dispatch", {}).get("frac"),
+        "combine_frac_of_hbm": stage_out.get("combine", {}).get("frac"),
+        "stages": stage_out,
+        "host_wall_s": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, host)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,192 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed MoE block forward.
+ *
+ * The block, as the Olmo-core MoE report describes it ("Supercharging Olmo-core
+ * for Efficient and Scalable MoE Training", Abstract; "Section 24: Conclusion",
+ * 24.1 and Evidence 3 / Figure 74; explainer "Olmo-core 3: an open training
+ * stack for trillion-parameter MoE", section "Olmo-core 3's answer: experts
+ * resident, data routed"):
+ *
+ *   router logits -> softmax + top-k -> per-expert counts / offsets / positions
+ *   computed and kept on the device -> rowwise dispatch that writes each token
+ *   row straight into its expert's segment (no separate permutation) ->
+ *   SwiGLU experts as a grouped GEMM whose group sizes never leave the device
+ *   (no padding of experts to a common capacity) -> gate-weighted combine
+ *   back to token order.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; the caller owns every buffer.  The library never
+ *    allocates device memory, never frees, never copies to the host and never
+ *    synchronises inside these calls (except moe_kernel_times, see there).
+ *    All work is enqueued on `stream` (a hipStream_t; NULL = default stream),
+ *    so calls on one stream are ordered and the whole sequence is capturable
+ *    in a HIP graph.
+ *  - Row-major layouts.  T tokens, d = d_model, E experts, k = top_k,
+ *    H = d_hidden, R = T*k routed rows.
+ *  - Storage types by `act_dtype`:
+ *        MOE_F32   : x, xe, h, ye, y float32; weights float32.
+ *        MOE_BF16  : x, xe, h, ye, y bfloat16; weights bfloat16; fp32 accumulate.
+ *        MOE_MXFP8 : x bfloat16; xe and h are MXFP8 (E4M3 codes, one E8M0
+ *                    scale byte per 32 consecutive elements along the GEMM
+ *                    contraction axis); weights given bfloat16 and stored
+ *                    MXFP8 by moe_pack_weights; ye and y bfloat16.
+ *    Logits and gates are always float32; indices int32.
+ *  - MXFP8 follows OCP Microscaling (MX) v1.0: E4M3 "FN" (bias 7, max 448, no
+ *    infinities), shared exponent floor(log2(amax)) - 8 clamped to [-127,127]
+ *    (all-zero block -> 2^-127), elements rounded to nearest-even, saturated
+ *    to +-448, sign kept on zero.  Payload 33/32 bytes per value (report
+ *    Section 24, Evidence 10).
+ *  - Routing: experts ranked by float32 logit, ties to the lower expert index
+ *    (-0.0 == +0.0); slot j of a token holds its j-th largest logit.  Gates
+ *    are the softmax over all E renormalised over the k selected experts.
+ *    Rows of one expert are ordered by ascending token index (stable), experts
+ *    back to back without padding: offsets[e] = sum of counts[e' < e].
+ *  - Shapes supported: 1 <= k <= min(E, 16), E <= 1024, T >= 1, and
+ *    d, H multiples of 64 (MOE_F32, MOE_BF16) or of 128 (MOE_MXFP8).
+ *  - Errors: every entry point returns MOE_OK or a negative MOE_ERR_* code.
+ *    Arguments are validated on the host before anything is enqueued; a
+ *    failed check enqueues nothing.  MOE_ERR_LAUNCH reports hipGetLastError()
+ *    after a launch.  Faults inside kernels surface at the caller's next
+ *    synchronisation.  Preconditions not checked: logits are finite; pos /
+ *    offsets buffers come from moe_route for the same problem.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK             0
+#define MOE_ERR_NULL      -1   /* a required pointer is NULL                      */
+#define MOE_ERR_SHAPE     -2   /* unsupported T, d, E, k or H                      */
+#define MOE_ERR_DTYPE     -3   /* unknown act_dtype, or flag not valid for it      */
+#define MOE_ERR_WORKSPACE -4   /* ws_bytes smaller than moe_workspace_bytes()      */
+#define MOE_ERR_LAUNCH    -5   /* a kernel launch or HIP runtime call failed       */
+#define MOE_ERR_STATE     -6   /* moe_kernel_times without a profiled forward      */
+
+#define MOE_F32   0
+#define MOE_BF16  1
+#define MOE_MXFP8 2
+
+/* flags */
+#define MOE_LOGITS_GIVEN     1  /* logits are an input; skip the router GEMM x . W_r     */
+#define MOE_IDENTITY_EXPERTS 2  /* test mode of moe_forward: ye := xe (f32 / bf16 only)  */
+
+typedef struct moe_problem {
+    int32_t T;          /* tokens                                 */
+    int32_t d_model;    /* d                                      */
+    int32_t n_experts;  /* E                                      */
+    int32_t top_k;      /* k                                      */
+    int32_t d_hidden;   /* H, expert SwiGLU hidden size           */
+    int32_t act_dtype;  /* MOE_F32 | MOE_BF16 | MOE_MXFP8         */
+    int32_t flags;      /* MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS */
+} moe_problem;
+
+/* Library version string and a readable name of a status code (host only). */
+const char* moe_version(void);
+const char* moe_status_string(int32_t status);
+
+/* Device workspace, in bytes, that is enough for every entry point below on
+ * problem p (host only, no GPU call).  Contents need no initialisation and are
+ * overwritten by every call. */
+int32_t moe_workspace_bytes(const moe_problem* p, size_t* bytes);
+
+/* Size in bytes of the packed expert weights for p (host only). */
+int32_t moe_packed_weight_bytes(const moe_problem* p, size_t* bytes);
+
+/* Packs the expert weights once, outside the timed path: re-lays them out with
+ * the contraction axis contiguous and, for MOE_MXFP8, quantises them.
+ *   w_gate, w_up : device [E, d, H]   (x . W convention), storage type above
+ *   w_down       : device [E, H, d]
+ *   packed       : device, moe_packed_weight_bytes() bytes, layout:
+ *     W1 [E][2H][d] : row n of expert e is gate column h = 32*(n/64) + n%32 when
+ *                     (n/32) is even, else up column h (same formula); i.e. 32
+ *                     gate columns then the matching 32 up columns, repeated.
+ *     W2 [E][d][H]  : W2[e][n][j] = w_down[e][j][n].
+ *     Elements are float32 / bfloat16 / E4M3 by act_dtype.  For MOE_MXFP8 the
+ *     E8M0 scales follow: S1 [E][2H][d/32], then S2 [E][d][H/32], each scale
+ *     covering 32 consecutive elements of a row.
+ *   Regions are W1, W2, S1, S2 in that order, each starting at a multiple of
+ *   256 bytes. */
+int32_t moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
+                         const void* w_down, void* packed, void* stream);
+
+/* Routing (report: count routes on the GPU, metadata kept on the device,
+ * Section 24.1 and Evidence 3).
+ *   x        : device [T, d] (storage type of act_dtype; MXFP8: bfloat16);
+ *              unused (may be NULL) with MOE_LOGITS_GIVEN
+ *   w_router : device [d, E], same type as x; unused with MOE_LOGITS_GIVEN
+ *   logits   : device float32 [T, E]; input with MOE_LOGITS_GIVEN, else output
+ *   topk_idx : device int32 [T, k] out;  topk_gate : device float32 [T, k] out
+ *   counts   : device int32 [E] out;     offsets   : device int32 [E+1] out
+ *   pos      : device int32 [T, k] out, row of (token, slot) in the expert-major
+ *              buffer: offsets[e] + number of earlier tokens routed to e
+ *   row_token: device int32 [R] out, row_token[pos[t][j]] = t
+ *   ws       : device workspace of ws_bytes bytes */
+int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                  int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                  int32_t* pos, int32_t* row_token, void* ws, size_t ws_bytes, void* stream);
+
+/* Rowwise dispatch (report Abstract: each token row written directly into its
+ * expert's buffer): xe[pos[t][j]] = x[t] for every slot.
+ *   x        : device [T, d]
+ *   pos      : device int32 [T, k] from moe_route
+ *   xe       : device [R, d] out (MOE_MXFP8: uint8 E4M3 codes)
+ *   xe_scale : device uint8 [R, d/32] out for MOE_MXFP8, else ignored (may be NULL) */
+int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, void* xe,
+                     uint8_t* xe_scale, void* stream);
+
+/* Expert SwiGLU FFN as a grouped GEMM whose groups are read from device
+ * memory (report: device-scheduled grouped GEMM, no padding to a capacity):
+ *   for every expert e and row r in [offsets[e], offsets[e+1]):
+ *     h  = silu(xe[r] . W_gate[e]) * (xe[r] . W_up[e])   (stored in workspace)
+ *     ye[r] = h . W_down[e]
+ *   xe, xe_scale : as written by moe_dispatch
+ *   packed_w     : from moe_pack_weights
+ *   offsets      : device int32 [E+1] from moe_route
+ *   ye           : device [R, d] out (float32 for MOE_F32, else bfloat16)
+ *   ws           : workspace (holds h) */
+int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* xe_scale,
+                           const void* packed_w, const int32_t* offsets, void* ye, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Combine back to token order (report Abstract: combine without a permutation):
+ *   y[t] = sum over j = 0..k-1, in slot order, of topk_gate[t][j] * ye[pos[t][j]],
+ *   accumulated in float32 and rounded to nearest-even into y.
+ *   ye : device [R, d]; y : device [T, d] out (float32 for MOE_F32, else bfloat16) */
+int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate,
+                    const int32_t* pos, void* y, void* stream);
+
+/* The whole block on one stream: route, dispatch, grouped SwiGLU, combine, with
+ * no host synchronisation between them.  Arguments as above; topk_idx,
+ * topk_gate, counts, offsets and pos are optional outputs (NULL: kept in the
+ * workspace only).  With MOE_IDENTITY_EXPERTS the grouped GEMM is skipped and
+ * ye := xe (MOE_F32 / MOE_BF16 only), so y[t] = x[t] * sum_j gate[t][j]. */
+int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                    const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
+                    int32_t* counts, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Per-kernel timing of moe_forward with HIP events recorded on its stream.
+ * moe_set_profiling(1) makes later moe_forward calls record an event before
+ * the first kernel and after each kernel (events are created on first use and
+ * kept; the last 128 calls keep separate events).  moe_set_profiling resets
+ * the count of profiled calls.  moe_kernel_times waits for the last profiled
+ * call to finish (this call synchronises on its final event) and writes up to
+ * max_n stage names and their durations in milliseconds averaged over the
+ * profiled calls (at most the last 128); *n receives the number of stages.
+ * Returns MOE_ERR_STATE when no profiled call completed its launches.  Not for
+ * use while a graph capture of moe_forward is in progress. */
+int32_t moe_set_profiling(int32_t enable);
+int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

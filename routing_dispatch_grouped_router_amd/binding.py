@@ -1,0 +1,281 @@
+"""Thin ctypes binding of libmoe.so (C ABI in include/moe.h).
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels.  torch provides device memory (output tensors are allocated with
+torch on the input's device) and the stream (torch's current stream, so
+torch.cuda events and synchronisation see the library's work).  Nothing here
+falls back to a CPU or torch implementation: if the library is not built, or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+ACT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
+MOE_LOGITS_GIVEN, MOE_IDENTITY_EXPERTS = 1, 2
+
+# every function the header declares, for the export check
+EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packed_weight_bytes",
+           "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
+           "moe_forward", "moe_set_profiling", "moe_kernel_times"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().moe_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+    @property
+    def act(self) -> str:
+        return {v: k for k, v in ACT.items()}[self.act_dtype]
+
+
+def problem(T, d, E, k, H, act, logits_given=False, identity=False) -> Problem:
+    flags = (MOE_LOGITS_GIVEN if logits_given else 0) | (MOE_IDENTITY_EXPERTS if identity else 0)
+    return Problem(T, d, E, k, H, ACT[act], flags)
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_I32 = ctypes.c_int32
+
+
+def lib():
+    """Load libmoe.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m routing_dispatch_grouped_router_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        PP = ctypes.POINTER(Problem)
+        L.moe_version.restype = ctypes.c_char_p
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [_I32]
+        L.moe_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
+        L.moe_packed_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
+        L.moe_pack_weights.argtypes = [PP, _P, _P, _P, _P, _P]
+        L.moe_route.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_dispatch.argtypes = [PP, _P, _P, _P, _P, _P]
+        L.moe_grouped_swiglu.argtypes = [PP, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_combine.argtypes = [PP, _P, _P, _P, _P, _P]
+        L.moe_forward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_set_profiling.argtypes = [_I32]
+        L.moe_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                       _I32, ctypes.POINTER(_I32)]
+        for name in EXPORTS:
+            if name not in ("moe_version", "moe_status_string"):
+                getattr(L, name).restype = _I32
+        _LIB = L
+    return _LIB
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoeError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t) -> torch.device:
+    return t.device
+
+
+def storage_dtype(act: str) -> torch.dtype:
+    return torch.float32 if act == "f32" else torch.bfloat16
+
+
+def out_dtype(act: str) -> torch.dtype:
+    return torch.float32 if act == "f32" else torch.bfloat16
+
+
+def _expect(t, shape, dtype, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+# ----------------------------------------------------------------------------- host-only queries
+
+
+def workspace_bytes(p: Problem) -> int:
+    n = _SZ()
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def packed_weight_bytes(p: Problem) -> int:
+    n = _SZ()
+    _check("moe_packed_weight_bytes", lib().moe_packed_weight_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def new_workspace(p: Problem, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- entry points
+
+
+def pack_weights(p: Problem, w_gate, w_up, w_down, stream=None) -> torch.Tensor:
+    dt = storage_dtype(p.act)
+    E, d, H = p.n_experts, p.d_model, p.d_hidden
+    _expect(w_gate, (E, d, H), dt, "w_gate")
+    _expect(w_up, (E, d, H), dt, "w_up")
+    _expect(w_down, (E, H, d), dt, "w_down")
+    packed = torch.empty(packed_weight_bytes(p), dtype=torch.uint8, device=w_gate.device)
+    _check("moe_pack_weights", lib().moe_pack_weights(ctypes.byref(p), _ptr(w_gate), _ptr(w_up),
+                                                      _ptr(w_down), _ptr(packed), _stream(stream)))
+    return packed
+
+
+def route(p: Problem, x=None, w_router=None, logits=None, ws=None, stream=None) -> dict:
+    """Returns dict(logits, idx, gate, counts, offsets, pos, row_token) as device tensors."""
+    T, E, k, d = p.T, p.n_experts, p.top_k, p.d_model
+    dev = (logits if logits is not None else x).device
+    if p.flags & MOE_LOGITS_GIVEN:
+        _expect(logits, (T, E), torch.float32, "logits")
+    else:
+        _expect(x, (T, d), storage_dtype(p.act), "x")
+        _expect(w_router, (d, E), storage_dtype(p.act), "w_router")
+        logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    out = dict(logits=logits,
+               idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               gate=torch.empty((T, k), dtype=torch.float32, device=dev),
+               counts=torch.empty((E,), dtype=torch.int32, device=dev),
+               offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               pos=torch.empty((T, k), dtype=torch.int32, device=dev),
+               row_token=torch.empty((T * k,), dtype=torch.int32, device=dev))
+    ws = new_workspace(p, dev) if ws is None else ws
+    _check("moe_route", lib().moe_route(
+        ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(out["idx"]), _ptr(out["gate"]),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["pos"]), _ptr(out["row_token"]),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def dispatch(p: Problem, x, pos, stream=None):
+    """Returns (xe, xe_scale); xe_scale is None unless MXFP8."""
+    T, d, k = p.T, p.d_model, p.top_k
+    R = T * k
+    _expect(x, (T, d), storage_dtype(p.act), "x")
+    _expect(pos, (T, k), torch.int32, "pos")
+    if p.act == "mxfp8":
+        xe = torch.empty((R, d), dtype=torch.uint8, device=x.device)
+        xs = torch.empty((R, d // 32), dtype=torch.uint8, device=x.device)
+    else:
+        xe = torch.empty((R, d), dtype=storage_dtype(p.act), device=x.device)
+        xs = None
+    _check("moe_dispatch", lib().moe_dispatch(ctypes.byref(p), _ptr(x), _ptr(pos), _ptr(xe), _ptr(xs),
+                                              _stream(stream)))
+    return xe, xs
+
+
+def grouped_swiglu(p: Problem, xe, xe_scale, packed, offsets, ws=None, stream=None):
+    R, d = p.T * p.top_k, p.d_model
+    _expect(offsets, (p.n_experts + 1,), torch.int32, "offsets")
+    ye = torch.empty((R, d), dtype=out_dtype(p.act), device=xe.device)
+    ws = new_workspace(p, xe.device) if ws is None else ws
+    _check("moe_grouped_swiglu", lib().moe_grouped_swiglu(
+        ctypes.byref(p), _ptr(xe), _ptr(xe_scale), _ptr(packed), _ptr(offsets), _ptr(ye), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return ye
+
+
+def combine(p: Problem, ye, gate, pos, stream=None):
+    T, d, k = p.T, p.d_model, p.top_k
+    _expect(ye, (T * k, d), out_dtype(p.act), "ye")
+    _expect(gate, (T, k), torch.float32, "gate")
+    _expect(pos, (T, k), torch.int32, "pos")
+    y = torch.empty((T, d), dtype=out_dtype(p.act), device=ye.device)
+    _check("moe_combine", lib().moe_combine(ctypes.byref(p), _ptr(ye), _ptr(gate), _ptr(pos), _ptr(y),
+                                            _stream(stream)))
+    return y
+
+
+class Forward:
+    """Preallocated state for repeated moe_forward calls (fixed buffer addresses)."""
+
+    def __init__(self, p: Problem, device, debug_outputs: bool = True):
+        self.p = p
+        T, E, k, d = p.T, p.n_experts, p.top_k, p.d_model
+        self.ws = new_workspace(p, device)
+        self.y = torch.empty((T, d), dtype=out_dtype(p.act), device=device)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.debug = debug_outputs
+        if debug_outputs:
+            self.idx = torch.empty((T, k), dtype=torch.int32, device=device)
+            self.gate = torch.empty((T, k), dtype=torch.float32, device=device)
+            self.counts = torch.empty((E,), dtype=torch.int32, device=device)
+            self.offsets = torch.empty((E + 1,), dtype=torch.int32, device=device)
+            self.pos = torch.empty((T, k), dtype=torch.int32, device=device)
+        else:
+            self.idx = self.gate = self.counts = self.offsets = self.pos = None
+
+    def __call__(self, x, packed=None, w_router=None, logits=None, stream=None):
+        p = self.p
+        _expect(x, (p.T, p.d_model), storage_dtype(p.act), "x")
+        if p.flags & MOE_LOGITS_GIVEN:
+            _expect(logits, (p.T, p.n_experts), torch.float32, "logits")
+            if logits.data_ptr() != self.logits.data_ptr():
+                self.logits.copy_(logits)
+        else:
+            _expect(w_router, (p.d_model, p.n_experts), storage_dtype(p.act), "w_router")
+        _check("moe_forward", lib().moe_forward(
+            ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(self.logits), _ptr(packed), _ptr(self.y),
+            _ptr(self.idx), _ptr(self.gate), _ptr(self.counts), _ptr(self.offsets), _ptr(self.pos),
+            _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        return self.y
+
+
+def forward(p: Problem, x, packed=None, w_router=None, logits=None, stream=None) -> dict:
+    f = Forward(p, x.device)
+    y = f(x, packed=packed, w_router=w_router, logits=logits, stream=stream)
+    return dict(y=y, logits=f.logits, idx=f.idx, gate=f.gate, counts=f.counts, offsets=f.offsets,
+                pos=f.pos)
+
+
+def set_profiling(enable: bool):
+    _check("moe_set_profiling", lib().moe_set_profiling(1 if enable else 0))
+
+
+def kernel_times() -> list[tuple[str, float]]:
+    """(stage name, milliseconds) of the last profiled moe_forward (synchronises on it)."""
+    names = (ctypes.c_char_p * 8)()
+    ms = (ctypes.c_float * 8)()
+    n = _I32()
+    _check("moe_kernel_times", lib().moe_kernel_times(names, ms, 8, ctypes.byref(n)))
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+
+
+def version() -> str:
+    return lib().moe_version().decode()

@@ -1,0 +1,341 @@
+// C ABI of the routed MoE block (declarations and contracts in include/moe.h).
+// Host-side only: validates arguments, carves the caller's workspace and
+// enqueues the gfx950 kernels on the caller's stream.  Nothing here allocates
+// device memory, copies to the host or synchronises, except moe_kernel_times.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstring>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t hist, base, h, h_scale, route_end, gemm_end;
+    size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, ye, total;
+};
+
+size_t act_bytes(int act) { return act == MOE_F32 ? 4 : (act == MOE_BF16 ? 2 : 1); }
+
+Layout layout(const moe_problem& p) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t T = p.T, E = p.n_experts, k = p.top_k, d = p.d_model, H = p.d_hidden;
+    const size_t R = T * k, nblk = route_blocks(p.T);
+    const bool mx = p.act_dtype == MOE_MXFP8;
+    L.hist = take(nblk * E * 4);
+    L.base = take(nblk * E * 4);
+    L.route_end = off;
+    L.h = take(R * H * act_bytes(p.act_dtype));
+    L.h_scale = take(mx ? R * H / 32 : 0);
+    L.gemm_end = off;
+    L.idx = take(R * 4);
+    L.gate = take(R * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.pos = take(R * 4);
+    L.row_token = take(R * 4);
+    L.xe = take(R * d * act_bytes(p.act_dtype));
+    L.xe_scale = take(mx ? R * d / 32 : 0);
+    L.ye = take(R * d * (p.act_dtype == MOE_F32 ? 4 : 2));
+    L.total = off;
+    return L;
+}
+
+struct Packed {
+    size_t w1, w2, s1, s2, total;
+};
+
+Packed packed_layout(const moe_problem& p) {
+    Packed P{};
+    const size_t E = p.n_experts, d = p.d_model, H = p.d_hidden, b = act_bytes(p.act_dtype);
+    const bool mx = p.act_dtype == MOE_MXFP8;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    P.w1 = take(E * 2 * H * d * b);
+    P.w2 = take(E * d * H * b);
+    P.s1 = take(mx ? E * 2 * H * d / 32 : 0);
+    P.s2 = take(mx ? E * d * H / 32 : 0);
+    P.total = off;
+    return P;
+}
+
+int32_t check_problem(const moe_problem* p) {
+    if (p == nullptr) return MOE_ERR_NULL;
+    if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16 && p->act_dtype != MOE_MXFP8)
+        return MOE_ERR_DTYPE;
+    if (p->flags & ~(MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS)) return MOE_ERR_DTYPE;
+    if ((p->flags & MOE_IDENTITY_EXPERTS) && p->act_dtype == MOE_MXFP8) return MOE_ERR_DTYPE;
+    if (p->T < 1 || p->n_experts < 1 || p->n_experts > kMaxExperts || p->top_k < 1 ||
+        p->top_k > std::min(p->n_experts, kMaxTopK) || p->d_model < 1 || p->d_hidden < 1)
+        return MOE_ERR_SHAPE;
+    const int mult = p->act_dtype == MOE_MXFP8 ? 128 : 64;
+    if (p->d_model % mult || p->d_hidden % mult) return MOE_ERR_SHAPE;
+    // row indices are int32 and element offsets of one row-block must stay in range
+    const long long R = (long long)p->T * p->top_k;
+    if (R > INT_MAX / 2 || (long long)p->d_model > INT_MAX / 8 || (long long)p->d_hidden > INT_MAX / 8)
+        return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int32_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+// ------------------------------------------------------------------ profiling (moe_forward only)
+// Events are recorded on the forward's own stream before the first kernel and
+// after each kernel.  Up to kMaxCalls consecutive calls keep their own event
+// sets, so the per-stage durations of a whole timed loop can be averaged
+// without synchronising inside it.
+constexpr int kMaxStages = 8;
+constexpr int kMaxCalls = 128;
+struct Profiler {
+    bool enabled = false;
+    int calls = 0;          // profiled calls since enabling
+    int n = 0;              // stages recorded in the current call
+    int stages = 0;         // stages of a complete call
+    hipEvent_t ev[kMaxCalls][kMaxStages + 1] = {};
+    const char* names[kMaxStages] = {};
+    int device = -1;
+} g_prof;
+
+int32_t prof_begin(hipStream_t s) {
+    if (!g_prof.enabled) return MOE_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (g_prof.device != dev) {
+        for (auto& row : g_prof.ev)
+            for (auto& e : row) {
+                if (e) hipEventDestroy(e);
+                e = nullptr;
+            }
+        for (auto& row : g_prof.ev)
+            for (auto& e : row)
+                if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_LAUNCH;
+        g_prof.device = dev;
+    }
+    g_prof.n = 0;
+    return launched(hipEventRecord(g_prof.ev[g_prof.calls % kMaxCalls][0], s));
+}
+
+int32_t prof_mark(const char* name, hipStream_t s) {
+    if (!g_prof.enabled || g_prof.n >= kMaxStages) return MOE_OK;
+    g_prof.names[g_prof.n] = name;
+    ++g_prof.n;
+    return launched(hipEventRecord(g_prof.ev[g_prof.calls % kMaxCalls][g_prof.n], s));
+}
+
+void prof_end() {
+    if (!g_prof.enabled) return;
+    g_prof.stages = g_prof.n;
+    ++g_prof.calls;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+
+const char* moe_status_string(int32_t status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "null pointer argument";
+        case MOE_ERR_SHAPE: return "unsupported problem shape";
+        case MOE_ERR_DTYPE: return "unsupported dtype or flag";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_LAUNCH: return "kernel launch or HIP runtime call failed";
+        case MOE_ERR_STATE: return "no profiled forward to report";
+        default: return "unknown status";
+    }
+}
+
+int32_t moe_workspace_bytes(const moe_problem* p, size_t* bytes) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (!bytes) return MOE_ERR_NULL;
+    *bytes = layout(*p).total;
+    return MOE_OK;
+}
+
+int32_t moe_packed_weight_bytes(const moe_problem* p, size_t* bytes) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (!bytes) return MOE_ERR_NULL;
+    *bytes = packed_layout(*p).total;
+    return MOE_OK;
+}
+
+int32_t moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
+                         const void* w_down, void* packed, void* stream) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (!w_gate || !w_up || !w_down || !packed) return MOE_ERR_NULL;
+    const Packed P = packed_layout(*p);
+    return launched(launch_pack(p->act_dtype, w_gate, w_up, w_down, at(packed, P.w1), at(packed, P.w2),
+                                reinterpret_cast<uint8_t*>(at(packed, P.s1)),
+                                reinterpret_cast<uint8_t*>(at(packed, P.s2)), p->n_experts, p->d_model,
+                                p->d_hidden, static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                  int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                  int32_t* pos, int32_t* row_token, void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    const bool given = p->flags & MOE_LOGITS_GIVEN;
+    if (!logits || !topk_idx || !topk_gate || !counts || !offsets || !pos || !row_token || !ws)
+        return MOE_ERR_NULL;
+    if (!given && (!x || !w_router)) return MOE_ERR_NULL;
+    const Layout L = layout(*p);
+    if (ws_bytes < L.route_end) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
+    int32_t* base = reinterpret_cast<int32_t*>(at(ws, L.base));
+    const int T = p->T, E = p->n_experts, k = p->top_k, d = p->d_model;
+    if (!given && (st = launched(launch_router_logits(p->act_dtype, x, w_router, logits, T, d, E, s))))
+        return st;
+    if ((st = launched(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, pos, hist, s)))) return st;
+    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, counts, offsets, s)))) return st;
+    return launched(launch_route_finalize(topk_idx, base, T, E, k, pos, row_token, s));
+}
+
+int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, void* xe,
+                     uint8_t* xe_scale, void* stream) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (!x || !pos || !xe || (p->act_dtype == MOE_MXFP8 && !xe_scale)) return MOE_ERR_NULL;
+    return launched(launch_dispatch(p->act_dtype, x, const_cast<int32_t*>(pos), nullptr, nullptr,
+                                    nullptr, xe, xe_scale, p->T, p->d_model, p->n_experts, p->top_k,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* xe_scale,
+                           const void* packed_w, const int32_t* offsets, void* ye, void* ws,
+                           size_t ws_bytes, void* stream) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    const bool mx = p->act_dtype == MOE_MXFP8;
+    if (!xe || !packed_w || !offsets || !ye || !ws || (mx && !xe_scale)) return MOE_ERR_NULL;
+    const Layout L = layout(*p);
+    if (ws_bytes < L.gemm_end) return MOE_ERR_WORKSPACE;
+    const Packed P = packed_layout(*p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int R = p->T * p->top_k, E = p->n_experts, d = p->d_model, H = p->d_hidden;
+    const void* pw = packed_w;
+    const uint8_t* s1 = reinterpret_cast<const uint8_t*>(static_cast<const char*>(pw) + P.s1);
+    const uint8_t* s2 = reinterpret_cast<const uint8_t*>(static_cast<const char*>(pw) + P.s2);
+    void* h = at(ws, L.h);
+    uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
+    if ((st = launched(launch_gemm1(p->act_dtype, xe, xe_scale, static_cast<const char*>(pw) + P.w1, s1,
+                                    offsets, h, hs, R, E, d, H, s))))
+        return st;
+    return launched(launch_gemm2(p->act_dtype, h, hs, static_cast<const char*>(pw) + P.w2, s2, offsets,
+                                 ye, R, E, d, H, s));
+}
+
+int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate, const int32_t* pos,
+                    void* y, void* stream) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (!ye || !topk_gate || !pos || !y) return MOE_ERR_NULL;
+    return launched(launch_combine(p->act_dtype, ye, topk_gate, pos, y, p->T, p->d_model, p->top_k,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                    const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
+                    int32_t* counts, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
+                    void* stream) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    const bool given = p->flags & MOE_LOGITS_GIVEN;
+    const bool identity = p->flags & MOE_IDENTITY_EXPERTS;
+    if (!x || !logits || !y || !ws || (!identity && !packed_w)) return MOE_ERR_NULL;
+    if (!given && !w_router) return MOE_ERR_NULL;
+    const Layout L = layout(*p);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int T = p->T, E = p->n_experts, k = p->top_k, d = p->d_model, H = p->d_hidden;
+    const int R = T * k, act = p->act_dtype;
+    int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(at(ws, L.idx));
+    float* gate = topk_gate ? topk_gate : reinterpret_cast<float*>(at(ws, L.gate));
+    int32_t* cnt = counts ? counts : reinterpret_cast<int32_t*>(at(ws, L.counts));
+    int32_t* off = offsets ? offsets : reinterpret_cast<int32_t*>(at(ws, L.offsets));
+    int32_t* ps = pos ? pos : reinterpret_cast<int32_t*>(at(ws, L.pos));
+    int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
+    int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
+    int32_t* base = reinterpret_cast<int32_t*>(at(ws, L.base));
+    void* xe = at(ws, L.xe);
+    uint8_t* xs = reinterpret_cast<uint8_t*>(at(ws, L.xe_scale));
+    void* ye = identity ? xe : at(ws, L.ye);
+
+    if ((st = prof_begin(s))) return st;
+    if (!given) {
+        if ((st = launched(launch_router_logits(act, x, w_router, logits, T, d, E, s)))) return st;
+        if ((st = prof_mark("router_logits", s))) return st;
+    }
+    if ((st = launched(launch_route_topk(logits, T, E, k, idx, gate, ps, hist, s)))) return st;
+    if ((st = prof_mark("route_topk", s))) return st;
+    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, cnt, off, s)))) return st;
+    if ((st = prof_mark("route_scan", s))) return st;
+    if ((st = launched(launch_dispatch(act, x, ps, idx, base, row_token, xe, xs, T, d, E, k, s))))
+        return st;
+    if ((st = prof_mark("dispatch", s))) return st;
+    if (!identity) {
+        const Packed P = packed_layout(*p);
+        const char* pw = static_cast<const char*>(packed_w);
+        void* h = at(ws, L.h);
+        uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
+        if ((st = launched(launch_gemm1(act, xe, xs, pw + P.w1, reinterpret_cast<const uint8_t*>(pw + P.s1),
+                                        off, h, hs, R, E, d, H, s))))
+            return st;
+        if ((st = prof_mark("gemm1_gate_up_swiglu", s))) return st;
+        if ((st = launched(launch_gemm2(act, h, hs, pw + P.w2, reinterpret_cast<const uint8_t*>(pw + P.s2),
+                                        off, ye, R, E, d, H, s))))
+            return st;
+        if ((st = prof_mark("gemm2_down", s))) return st;
+    }
+    if ((st = launched(launch_combine(act, ye, gate, ps, y, T, d, k, s)))) return st;
+    if ((st = prof_mark("combine", s))) return st;
+    prof_end();
+    return MOE_OK;
+}
+
+int32_t moe_set_profiling(int32_t enable) {
+    g_prof.enabled = enable != 0;
+    g_prof.calls = 0;
+    return MOE_OK;
+}
+
+int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* n) {
+    if (!n) return MOE_ERR_NULL;
+    if (g_prof.calls == 0) return MOE_ERR_STATE;
+    const int calls = std::min(g_prof.calls, kMaxCalls);
+    if (hipEventSynchronize(g_prof.ev[(g_prof.calls - 1) % kMaxCalls][g_prof.stages]) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+    *n = g_prof.stages;
+    for (int i = 0; i < g_prof.stages && i < max_n; ++i) {
+        double sum = 0.0;
+        for (int c = 0; c < calls; ++c) {
+            const int slot = (g_prof.calls - 1 - c) % kMaxCalls;
+            float t = 0.f;
+            if (hipEventElapsedTime(&t, g_prof.ev[slot][i], g_prof.ev[slot][i + 1]) != hipSuccess)
+                return MOE_ERR_LAUNCH;
+            sum += t;
+        }
+        if (ms) ms[i] = (float)(sum / calls);
+        if (names) names[i] = g_prof.names[i];
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// Rowwise dispatch and combine for gfx950.
+//
+// Dispatch writes every token row straight into its expert's segment of the
+// expert-major buffer at the position routing computed, with no separate
+// permutation pass ("Supercharging Olmo-core ...", Abstract: rowwise EP writes
+// each token directly into its expert's buffer; explainer "Olmo-core 3 ...",
+// section "Olmo-core 3's answer").  For MXFP8 the quantiser runs inside the
+// dispatch, producing the codes and scales the grouped GEMM reads directly
+// ("Section 24: Conclusion", 24.3: a quantiser must produce a layout the
+// transport and GEMM consume without conversion; Evidence 6 counted separate
+// quantise / swizzle kernels as overhead).
+//
+// Both kernels are HBM-bound streaming copies: one wavefront per token row,
+// 16-byte loads and stores, each source row read once and written k times
+// (dispatch) or k rows read and one written (combine).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kRowsPerBlock = 4;   // one wave per token, 4 waves per workgroup
+
+// Final position of (t, j): with `base` non-NULL, pos holds the within-block
+// rank and is rewritten here; every lane computes the value, lane j writes it.
+__device__ __forceinline__ int final_pos(int32_t* pos, const int32_t* topk_idx,
+                                         const int32_t* base, int32_t* row_token, int t, int j,
+                                         int k, int E, int lane) {
+    const size_t i = (size_t)t * k + j;
+    int p = pos[i];
+    if (base != nullptr) {
+        p += base[(size_t)(t / kRouteBlock) * E + topk_idx[i]];
+        if (lane == 0) {
+            row_token[p] = t;
+        }
+    }
+    return p;
+}
+
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restrict__ x,
+                                                            int32_t* __restrict__ pos,
+                                                            const int32_t* __restrict__ topk_idx,
+                                                            const int32_t* __restrict__ base,
+                                                            int32_t* __restrict__ row_token,
+                                                            uint4* __restrict__ xe, int T,
+                                                            int row_chunks, int E, int k) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int p[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) p[j] = final_pos(pos, topk_idx, base, row_token, t, j, k, E, lane);
+    if (base != nullptr) {
+        // all lanes have read the ranks before any lane overwrites them
+        __builtin_amdgcn_wave_barrier();
+        if (lane < k) {
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if (j == lane) pos[(size_t)t * k + j] = p[j];
+        }
+    }
+    const uint4* src = x + (size_t)t * row_chunks;
+    for (int c = lane; c < row_chunks; c += 64) {
+        uint4 v = src[c];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < k) xe[(size_t)p[j] * row_chunks + c] = v;
+    }
+}
+
+// MXFP8: each lane quantises 8 bf16 values; 4 adjacent lanes form one block of 32.
+__global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __restrict__ x,
+                                                             int32_t* __restrict__ pos,
+                                                             const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ row_token,
+                                                             uint2* __restrict__ xq,
+                                                             uint8_t* __restrict__ xs, int T, int d,
+                                                             int E, int k) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int p[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) p[j] = final_pos(pos, topk_idx, base, row_token, t, j, k, E, lane);
+    if (base != nullptr) {
+        __builtin_amdgcn_wave_barrier();
+        if (lane < k) {
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j)
+                if (j == lane) pos[(size_t)t * k + j] = p[j];
+        }
+    }
+    const int chunks = d / 8;                 // multiple of 64 lanes * ... (d % 128 == 0 -> 16 | chunks)
+    const uint4* src = x + (size_t)t * chunks;
+    for (int c = lane; c < chunks; c += 64) {
+        uint4 v = src[c];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const int se = mx_shared_exp(amax);
+        const float inv = mx_inv_scale(se);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
+        const uint2 q = make_uint2(lo, hi);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < k) {
+                xq[(size_t)p[j] * chunks + c] = q;
+                if ((lane & 3) == 0) xs[(size_t)p[j] * (d / 32) + (c >> 2)] = (uint8_t)(se + 127);
+            }
+        }
+    }
+}
+
+hipError_t launch_dispatch(int act, const void* x, int32_t* pos, const int32_t* topk_idx,
+                           const int32_t* base, int32_t* row_token, void* xe, uint8_t* xe_scale,
+                           int T, int d, int E, int k, hipStream_t s) {
+    dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
+    if (act == kMXFP8) {
+        hipLaunchKernelGGL(dispatch_mxfp8_kernel, grid, block, 0, s, static_cast<const uint4*>(x), pos,
+                           topk_idx, base, row_token, static_cast<uint2*>(xe), xe_scale, T, d, E, k);
+    } else {
+        const int row_chunks = d * (act == kF32 ? 4 : 2) / 16;
+        hipLaunchKernelGGL(dispatch_copy_kernel, grid, block, 0, s, static_cast<const uint4*>(x), pos,
+                           topk_idx, base, row_token, static_cast<uint4*>(xe), T, row_chunks, E, k);
+    }
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- combine
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ ye,
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ pos,
+                                                      uint4* __restrict__ y, int T, int row_chunks,
+                                                      int k) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int p[kMaxTopK];
+    float g[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+            p[j] = pos[(size_t)t * k + j];
+            g[j] = gate[(size_t)t * k + j];
+        }
+    }
+    for (int c = lane; c < row_chunks; c += 64) {
+        constexpr int kN = kBf16 ? 8 : 4;
+        float acc[kN];
+#pragma unroll
+        for (int i = 0; i < kN; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < k) {
+                uint4 v = ye[(size_t)p[j] * row_chunks + c];
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                if (kBf16) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[2 * i] = fmaf(g[j], __uint_as_float(w[i] << 16), acc[2 * i]);
+                        acc[2 * i + 1] = fmaf(g[j], __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(g[j], __uint_as_float(w[i]), acc[i]);
+                }
+            }
+        }
+        uint4 o;
+        if (kBf16) {
+            o.x = pack_bf16x2(acc[0], acc[1]);
+            o.y = pack_bf16x2(acc[2], acc[3]);
+            o.z = pack_bf16x2(acc[4], acc[5]);
+            o.w = pack_bf16x2(acc[6], acc[7]);
+        } else {
+            o.x = __float_as_uint(acc[0]);
+            o.y = __float_as_uint(acc[1]);
+            o.z = __float_as_uint(acc[2]);
+            o.w = __float_as_uint(acc[3]);
+        }
+        y[(size_t)t * row_chunks + c] = o;
+    }
+}
+
+hipError_t launch_combine(int act, const void* ye, const float* gate, const int32_t* pos, void* y,
+                          int T, int d, int k, hipStream_t s) {
+    dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
+    const bool bf = act != kF32;
+    const int row_chunks = d * (bf ? 2 : 4) / 16;
+    if (bf)
+        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, static_cast<const uint4*>(ye), gate,
+                           pos, static_cast<uint4*>(y), T, row_chunks, k);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, static_cast<const uint4*>(ye), gate,
+                           pos, static_cast<uint4*>(y), T, row_chunks, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

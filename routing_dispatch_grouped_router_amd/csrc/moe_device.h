@@ -1,0 +1,96 @@
+// Device-side helpers shared by the gfx950 kernels: bfloat16 and E4M3 encodes,
+// orderable routing keys, vector types.  Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// Native 16-byte vector for register-held tiles (HIP's uint4 wrapper can defeat
+// scalar replacement and end up in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// float32 -> bfloat16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Orderable routing key: larger key <=> larger logit, then lower expert index.
+// -0.0 is folded onto +0.0 so the two compare equal.
+__device__ __forceinline__ uint64_t route_key(float logit, int e) {
+    uint32_t u = __float_as_uint(logit);
+    if (u == 0x80000000u) u = 0u;
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) {
+    return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+    uint32_t ord = (uint32_t)(key >> 32);
+    uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo = __shfl_xor(lo, m);
+    hi = __shfl_xor(hi, m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// ---------------------------------------------------------------- MXFP8 (OCP MX v1.0)
+
+// Shared block exponent floor(log2(amax)) - 8 clamped to [-127, 127], from the
+// float32 exponent field (amax is finite and >= 0; zero or float32-subnormal
+// amax gives the floor -127 because floor(log2) <= -127 there).
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+    int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    if (ef == 0) return -127;
+    int se = ef - 127 - 8;
+    return se < -127 ? -127 : se;
+}
+
+// 2^-se as a float32 (se in [-127, 119] -> exponent field 127 - se in [8, 254]).
+__device__ __forceinline__ float mx_inv_scale(int se) {
+    return __uint_as_float((uint32_t)(127 - se) << 23);
+}
+
+// E4M3 "FN" code of v: round to nearest even, saturate to +-448, keep sign on zero.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    float a = __uint_as_float(u & 0x7FFFFFFFu);
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
+        code = (uint32_t)rintf(a * 512.0f);           // 0..8; 8 is the smallest normal
+    } else {
+        int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;      // -6..8
+        float m = __uint_as_float((__float_as_uint(a) & 0x007FFFFFu) | 0x3F800000u);  // [1,2)
+        uint32_t q = (uint32_t)rintf((m - 1.0f) * 8.0f);   // 0..8
+        if (q == 8u) { q = 0u; e += 1; }
+        code = ((uint32_t)(e + 7) << 3) | q;
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return sign | code;
+}
+
+}  // namespace moe

@@ -1,0 +1,63 @@
+// Host-side launch functions of the gfx950 kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per routing block: per-block expert histograms and within-block ranks
+// are computed over this many consecutive tokens.
+constexpr int kRouteBlock = 256;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+
+enum Act { kF32 = 0, kBF16 = 1, kMXFP8 = 2 };
+
+inline int route_blocks(int T) { return (T + kRouteBlock - 1) / kRouteBlock; }
+
+// logits[T][E] = x[T][d] . w[d][E]   (x, w float32 or bfloat16; fp32 accumulate)
+hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
+                                int E, hipStream_t s);
+
+// Top-k + gates + per-block histogram and within-block ranks.
+//   rank[T][k]   : rank of token t among the tokens of its routing block routed to the same expert
+//   hist[nblk][E]: per-block expert counts
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                             float* topk_gate, int32_t* rank, int32_t* hist, hipStream_t s);
+
+// counts, offsets and base[nblk][E] = offsets[e] + tokens of earlier blocks routed to e.
+hipError_t launch_route_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
+                             int32_t* offsets, hipStream_t s);
+
+// pos[t][j] (holding the rank on entry) += base[t / kRouteBlock][idx]; row_token[pos] = t.
+hipError_t launch_route_finalize(const int32_t* topk_idx, const int32_t* base, int T, int E, int k,
+                                 int32_t* pos, int32_t* row_token, hipStream_t s);
+
+// xe[pos[t][j]] = x[t] (copy), or MXFP8 codes + scales for act == kMXFP8.
+// With `base` non-NULL, pos holds within-block ranks on entry and is finalised
+// here (pos += base[blk][idx], row_token written) before the copy.
+hipError_t launch_dispatch(int act, const void* x, int32_t* pos, const int32_t* topk_idx,
+                           const int32_t* base, int32_t* row_token, void* xe, uint8_t* xe_scale,
+                           int T, int d, int E, int k, hipStream_t s);
+
+// y[t] = sum_j gate[t][j] * ye[pos[t][j]]   (ye/y float32 for kF32, else bfloat16)
+hipError_t launch_combine(int act, const void* ye, const float* gate, const int32_t* pos, void* y,
+                          int T, int d, int k, hipStream_t s);
+
+// Grouped GEMMs over expert segments [offsets[e], offsets[e+1]) of R rows.
+//   gemm1: h = silu(xe W_gate) * (xe W_up)   (packed W1 [E][2H][d])
+//   gemm2: ye = h W_down                      (packed W2 [E][d][H])
+hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
+                        const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
+                        int R, int E, int d, int H, hipStream_t s);
+hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const void* w2,
+                        const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
+                        int d, int H, hipStream_t s);
+
+// Weight packing (setup).
+hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
+                       void* w2, uint8_t* s1, uint8_t* s2, int E, int d, int H, hipStream_t s);
+
+}  // namespace moe

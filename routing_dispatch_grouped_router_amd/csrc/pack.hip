@@ -1,0 +1,98 @@
+// Expert weight packing (setup, outside the timed path).
+//
+// W1 [E][2H][d]: row n is gate column 32*(n/64) + n%32 when (n/32) is even,
+// else the up column with the same formula.  W2 [E][d][H] is W_down
+// transposed.  For MXFP8 the packed rows are quantised in blocks of 32 along
+// K with one E8M0 scale each (OCP MX v1.0), the forward weight cache of the
+// report ("Section 24: Conclusion", 24.3, two MXFP8 weight caches; only the
+// K-major forward one is needed here).
+//
+// One workgroup moves a 32 (K) x 64 (N) tile through LDS: reads are
+// coalesced along the source rows (N), writes along the packed rows (K).
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <typename TIn>
+__device__ __forceinline__ float ld(const TIn* p, size_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+// which == 1: W1 from (w_gate, w_up) [E][d][H];  which == 2: W2 from w_down [E][H][d].
+template <typename TIn, int OUT>   // OUT: 0 float32, 1 bfloat16, 2 MXFP8
+__global__ __launch_bounds__(256) void pack_kernel(const TIn* __restrict__ wg, const TIn* __restrict__ wu,
+                                                   const TIn* __restrict__ wd, void* __restrict__ out,
+                                                   uint8_t* __restrict__ scales, int which, int E, int d,
+                                                   int H) {
+    __shared__ float tile[32][65];
+    const int N = which == 1 ? 2 * H : d;
+    const int K = which == 1 ? d : H;
+    const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 32, e = blockIdx.z;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 32 * 64; i += 256) {
+        const int kk = i >> 6, nn = i & 63;
+        const int n = n0 + nn, k = k0 + kk;
+        float v;
+        if (which == 1) {
+            const int h = 32 * (n >> 6) + (n & 31);
+            const TIn* src = ((n >> 5) & 1) ? wu : wg;
+            v = ld<TIn>(src, ((size_t)e * d + k) * H + h);
+        } else {
+            v = ld<TIn>(wd, ((size_t)e * H + k) * d + n);
+        }
+        tile[kk][nn] = v;
+    }
+    __syncthreads();
+    const size_t row_base = (size_t)e * N;
+    if (OUT == 2) {
+        if (tid < 64) {
+            const int nn = tid;
+            float amax = 0.f;
+            for (int kk = 0; kk < 32; ++kk) amax = fmaxf(amax, fabsf(tile[kk][nn]));
+            const int se = mx_shared_exp(amax);
+            const float inv = mx_inv_scale(se);
+            uint8_t* q = static_cast<uint8_t*>(out) + (row_base + n0 + nn) * K + k0;
+            for (int w = 0; w < 8; ++w) {
+                uint32_t word = 0;
+                for (int b = 0; b < 4; ++b) word |= e4m3_encode(tile[4 * w + b][nn] * inv) << (8 * b);
+                reinterpret_cast<uint32_t*>(q)[w] = word;
+            }
+            scales[(row_base + n0 + nn) * (K / 32) + k0 / 32] = (uint8_t)(se + 127);
+        }
+    } else {
+        for (int i = tid; i < 32 * 64; i += 256) {
+            const int nn = i >> 5, kk = i & 31;
+            const size_t o = (row_base + n0 + nn) * K + k0 + kk;
+            if (OUT == 0) static_cast<float*>(out)[o] = tile[kk][nn];
+            else static_cast<uint16_t*>(out)[o] = f32_to_bf16(tile[kk][nn]);   // exact: input is bf16
+        }
+    }
+}
+
+hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
+                       void* w2, uint8_t* s1, uint8_t* s2, int E, int d, int H, hipStream_t s) {
+    dim3 block(256);
+    dim3 g1((2 * H) / 64, d / 32, E), g2(d / 64, H / 32, E);
+    if (act == kF32) {
+        auto wg = static_cast<const float*>(w_gate), wu = static_cast<const float*>(w_up),
+             wd = static_cast<const float*>(w_down);
+        hipLaunchKernelGGL((pack_kernel<float, 0>), g1, block, 0, s, wg, wu, wd, w1, nullptr, 1, E, d, H);
+        hipLaunchKernelGGL((pack_kernel<float, 0>), g2, block, 0, s, wg, wu, wd, w2, nullptr, 2, E, d, H);
+    } else {
+        auto wg = static_cast<const uint16_t*>(w_gate), wu = static_cast<const uint16_t*>(w_up),
+             wd = static_cast<const uint16_t*>(w_down);
+        if (act == kBF16) {
+            hipLaunchKernelGGL((pack_kernel<uint16_t, 1>), g1, block, 0, s, wg, wu, wd, w1, nullptr, 1, E, d, H);
+            hipLaunchKernelGGL((pack_kernel<uint16_t, 1>), g2, block, 0, s, wg, wu, wd, w2, nullptr, 2, E, d, H);
+        } else {
+            hipLaunchKernelGGL((pack_kernel<uint16_t, 2>), g1, block, 0, s, wg, wu, wd, w1, s1, 1, E, d, H);
+            hipLaunchKernelGGL((pack_kernel<uint16_t, 2>), g2, block, 0, s, wg, wu, wd, w2, s2, 2, E, d, H);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

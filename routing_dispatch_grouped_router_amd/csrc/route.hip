@@ -1,0 +1,313 @@
+// Routing kernels for gfx950: router logits, top-k with gates, per-block
+// expert histograms / ranks, the count-offset scan and position finalisation.
+//
+// Routing metadata never leaves the device ("Supercharging Olmo-core ...",
+// Abstract; "Section 24: Conclusion", 24.1 and Evidence 3 / Figure 74: the
+// original path copied route counts to the host, which stalled submission).
+// Positions are a stable counting sort by expert computed without global
+// atomics: each block of kRouteBlock tokens records, per expert, a bitmask of
+// its tokens; a token's rank is a popcount of the bits below it, and a single
+// scan over (block, expert) histograms turns ranks into global positions.
+// Results are therefore identical from run to run.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ----------------------------------------------------------------------------- router logits
+
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+    uint4 a = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+template <typename TIn>
+__device__ __forceinline__ float load1(const TIn* p);
+template <>
+__device__ __forceinline__ float load1<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// One wave computes 4 tokens x 8 experts at a time; lanes split d in runs of 8.
+constexpr int kRtTok = 4;
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restrict__ x,
+                                                            const TIn* __restrict__ w,
+                                                            float* __restrict__ logits, int T,
+                                                            int d, int E) {
+    const int lane = threadIdx.x & 63;
+    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int t0 = wave * kRtTok;
+    if (t0 >= T) return;
+    for (int e0 = 0; e0 < E; e0 += 8) {
+        float acc[kRtTok][8];
+#pragma unroll
+        for (int a = 0; a < kRtTok; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
+        for (int kb = lane * 8; kb < d; kb += 64 * 8) {
+            float xv[kRtTok][8];
+#pragma unroll
+            for (int a = 0; a < kRtTok; ++a) {
+                int t = min(t0 + a, T - 1);
+                load8<TIn>(x + (size_t)t * d + kb, xv[a]);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const TIn* wr = w + (size_t)(kb + q) * E + e0;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    float wv = (e0 + b < E) ? load1<TIn>(wr + b) : 0.f;
+#pragma unroll
+                    for (int a = 0; a < kRtTok; ++a) acc[a][b] = fmaf(xv[a][q], wv, acc[a][b]);
+                }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < kRtTok; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                float v = acc[a][b];
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+                acc[a][b] = v;
+            }
+        if (lane < kRtTok * 8) {
+            int a = lane >> 3, b = lane & 7;
+            float v = 0.f;
+#pragma unroll
+            for (int aa = 0; aa < kRtTok; ++aa)
+#pragma unroll
+                for (int bb = 0; bb < 8; ++bb)
+                    if (aa == a && bb == b) v = acc[aa][bb];
+            if (t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = v;
+        }
+    }
+}
+
+hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
+                                int E, hipStream_t s) {
+    int waves = (T + kRtTok - 1) / kRtTok;
+    dim3 grid((waves + 3) / 4), block(256);
+    if (act == kF32)
+        hipLaunchKernelGGL(router_logits_kernel<float>, grid, block, 0, s,
+                           static_cast<const float*>(x), static_cast<const float*>(w), logits, T, d, E);
+    else
+        hipLaunchKernelGGL(router_logits_kernel<uint16_t>, grid, block, 0, s,
+                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), logits, T,
+                           d, E);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- top-k
+
+// G lanes cooperate on one token, each holding V of its E logits (expert
+// r + G*v for lane r of the group).  k rounds of a group-wide max over
+// orderable 64-bit keys select the experts in (logit desc, index asc) order.
+template <int V>
+__global__ __launch_bounds__(1024) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                          int E, int k, int G,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_gate,
+                                                          int32_t* __restrict__ rank,
+                                                          int32_t* __restrict__ hist) {
+    constexpr int kWords = kRouteBlock / 32;
+    __shared__ uint32_t mask[kMaxExperts * kWords];
+    __shared__ int32_t s_idx[kRouteBlock * kMaxTopK];   // selected experts of this block
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int blk = blockIdx.x;
+    for (int i = tid; i < E * kWords; i += nthr) mask[i] = 0u;
+    __syncthreads();
+
+    const int r = tid % G;
+    const int grp = tid / G;
+    const int per_pass = nthr / G;
+    for (int lt = grp; lt < kRouteBlock; lt += per_pass) {
+        const int t = blk * kRouteBlock + lt;
+        if (t >= T) break;       // uniform within a group: G divides 64
+        uint64_t key[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            int e = r + G * v;
+            key[v] = (e < E) ? route_key(logits[(size_t)t * E + e], e) : 0ull;
+        }
+        uint64_t sel[kMaxTopK];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < k) {
+                uint64_t best = 0ull;
+#pragma unroll
+                for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
+                for (int m = 1; m < G; m <<= 1) {
+                    uint64_t o = shfl_xor_u64(best, m);
+                    best = o > best ? o : best;
+                }
+                sel[j] = best;
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    if (key[v] == best) key[v] = 0ull;
+            }
+        }
+        // gates: softmax over all E renormalised over the selected k equals the
+        // softmax over the k selected logits
+        const float l0 = key_logit(sel[0]);
+        float den = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j)
+            if (j < k) den += expf(key_logit(sel[j]) - l0);
+        const float inv = 1.0f / den;
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < k && (j % G) == r) {
+                int e = key_expert(sel[j]);
+                topk_idx[(size_t)t * k + j] = e;
+                s_idx[lt * k + j] = e;
+                topk_gate[(size_t)t * k + j] = expf(key_logit(sel[j]) - l0) * inv;
+                atomicOr(&mask[e * kWords + (lt >> 5)], 1u << (lt & 31));
+            }
+        }
+    }
+    __syncthreads();
+    // within-block rank of every (token, slot): popcount of earlier tokens of the same expert
+    for (int i = tid; i < kRouteBlock * k; i += nthr) {
+        const int lt = i / k, j = i % k;
+        const int t = blk * kRouteBlock + lt;
+        if (t >= T) continue;
+        const int e = s_idx[lt * k + j];
+        const uint32_t* me = mask + e * kWords;
+        int c = __popc(me[lt >> 5] & ((1u << (lt & 31)) - 1u));
+        for (int w = 0; w < (lt >> 5); ++w) c += __popc(me[w]);
+        rank[(size_t)t * k + j] = c;
+    }
+    for (int e = tid; e < E; e += nthr) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) c += __popc(mask[e * kWords + w]);
+        hist[(size_t)blk * E + e] = c;
+    }
+}
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
+                             float* topk_gate, int32_t* rank, int32_t* hist, hipStream_t s) {
+    // lanes per token: smallest power of two G <= 64 with E / G <= 8 (or 16 at G = 64)
+    int G = 1;
+    while (G < 64 && (E + G - 1) / G > 8) G <<= 1;
+    const int V = (E + G - 1) / G;
+    const int threads = min(1024, kRouteBlock * G);
+    dim3 grid(route_blocks(T)), block(threads);
+    if (V <= 8)
+        hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, G, topk_idx,
+                           topk_gate, rank, hist);
+    else
+        hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, G, topk_idx,
+                           topk_gate, rank, hist);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- scan
+
+// One workgroup of 1024 threads.  Thread (e, c) sums expert e's counts over a
+// contiguous chunk c of routing blocks; chunk partials are scanned per expert,
+// expert totals are scanned into offsets, and each thread then writes the
+// global base position of expert e for every block of its chunk.
+__global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist,
+                                                          int nblk, int E,
+                                                          int32_t* __restrict__ base,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets) {
+    __shared__ int32_t part[1024];
+    __shared__ int32_t tot[1024];
+    const int tid = threadIdx.x;
+    const int NC = 1024 / E;                       // chunks per expert (E <= 1024)
+    const int CS = (nblk + NC - 1) / NC;           // blocks per chunk
+    const int e = tid % E, c = tid / E;
+    const bool act = c < NC;
+    const int b0 = c * CS, b1 = min(nblk, b0 + CS);
+    int s = 0;
+    if (act)
+        for (int b = b0; b < b1; ++b) s += hist[(size_t)b * E + e];
+    part[tid] = s;
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int cc = 0; cc < NC; ++cc) {
+            int v = part[cc * E + tid];
+            part[cc * E + tid] = run;
+            run += v;
+        }
+        tot[tid] = run;
+    } else {
+        tot[tid] = 0;
+    }
+    __syncthreads();
+    // inclusive Hillis-Steele scan of tot[0..1024)
+    for (int off = 1; off < 1024; off <<= 1) {
+        int v = tid >= off ? tot[tid - off] : 0;
+        __syncthreads();
+        tot[tid] += v;
+        __syncthreads();
+    }
+    if (tid < E) {
+        int excl = tid == 0 ? 0 : tot[tid - 1];
+        offsets[tid] = excl;
+        counts[tid] = tot[tid] - excl;
+    }
+    if (tid == 0) offsets[E] = tot[E - 1];
+    if (act) {
+        int run = (e == 0 ? 0 : tot[e - 1]) + part[c * E + e];
+        for (int b = b0; b < b1; ++b) {
+            base[(size_t)b * E + e] = run;
+            run += hist[(size_t)b * E + e];
+        }
+    }
+}
+
+hipError_t launch_route_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
+                             int32_t* offsets, hipStream_t s) {
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nblk, E, base, counts,
+                       offsets);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- finalize
+
+__global__ __launch_bounds__(256) void route_finalize_kernel(const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ base,
+                                                             int T, int E, int k,
+                                                             int32_t* __restrict__ pos,
+                                                             int32_t* __restrict__ row_token) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)T * k) return;
+    const int t = (int)(i / k);
+    const int e = topk_idx[i];
+    const int p = base[(size_t)(t / kRouteBlock) * E + e] + pos[i];
+    pos[i] = p;
+    row_token[p] = t;
+}
+
+hipError_t launch_route_finalize(const int32_t* topk_idx, const int32_t* base, int T, int E, int k,
+                                 int32_t* pos, int32_t* row_token, hipStream_t s) {
+    const size_t n = (size_t)T * k;
+    hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       topk_idx, base, T, E, k, pos, row_token);
+    return hipGetLastError();
+}
+
+}  // namespace moe

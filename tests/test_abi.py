@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, sizes workspaces on the host and rejects bad
+arguments before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from routing_dispatch_grouped_router_amd import binding as B
+from routing_dispatch_grouped_router_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert len(declared) >= 12
+    assert sorted(B.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in B.version()
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(-4) == b"workspace too small"
+
+
+def _status(fn, *args):
+    return getattr(B.lib(), fn)(*args)
+
+
+def _prob(**kw):
+    base = dict(T=64, d=128, E=8, k=2, H=128, act="bf16")
+    base.update(kw)
+    return B.problem(base["T"], base["d"], base["E"], base["k"], base["H"], base["act"],
+                     logits_given=kw.get("logits_given", False), identity=kw.get("identity", False))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=9), -2), (dict(k=0), -2), (dict(E=1025, k=2), -2), (dict(T=0), -2),
+    (dict(d=96), -2), (dict(H=32), -2), (dict(act="mxfp8", d=192), -2),
+    (dict(k=17, E=32), -2), (dict(act="mxfp8", identity=True, d=128), -3),
+])
+def test_bad_shapes_rejected(lib, kw, code):
+    p = _prob(**kw)
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == code
+
+
+def test_bad_dtype_and_flags(lib):
+    p = _prob()
+    p.act_dtype = 7
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == -3
+    p = _prob()
+    p.flags = 64
+    assert lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == -3
+    assert lib.moe_workspace_bytes(None, ctypes.byref(n)) == -1
+
+
+def test_null_pointers_rejected_before_any_launch(lib):
+    p = _prob(logits_given=True)
+    V = ctypes.c_void_p
+    fake = V(0x1000)   # never dereferenced: validation fails first
+    assert lib.moe_route(ctypes.byref(p), None, None, None, fake, fake, fake, fake, fake, fake,
+                         fake, 1 << 30, None) == -1
+    assert lib.moe_dispatch(ctypes.byref(p), fake, None, fake, None, None) == -1
+    assert lib.moe_combine(ctypes.byref(p), fake, fake, None, fake, None) == -1
+    assert lib.moe_forward(ctypes.byref(p), None, None, fake, fake, fake, None, None, None, None,
+                           None, fake, 1 << 30, None) == -1
+    pm = _prob(act="mxfp8", logits_given=True)
+    assert lib.moe_dispatch(ctypes.byref(pm), fake, fake, fake, None, None) == -1
+    assert lib.moe_grouped_swiglu(ctypes.byref(pm), fake, None, fake, fake, fake, fake, 1 << 30,
+                                  None) == -1
+
+
+def test_small_workspace_rejected(lib):
+    p = _prob(logits_given=True)
+    need = B.workspace_bytes(p)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_forward(ctypes.byref(p), fake, None, fake, fake, fake, None, None, None, None,
+                           None, fake, need - 1, None) == -4
+    assert lib.moe_route(ctypes.byref(p), None, None, fake, fake, fake, fake, fake, fake, fake,
+                         fake, 16, None) == -4
+
+
+def test_kernel_times_without_profiled_forward(lib):
+    n = ctypes.c_int32()
+    assert lib.moe_set_profiling(0) == 0
+    assert lib.moe_kernel_times(None, None, 0, ctypes.byref(n)) == -6
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_workspace_and_packed_sizes(lib, name):
+    w = W.CONFIGS[name]
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned")
+    R = w.T * w.k
+    elem = {"f32": 4, "bf16": 2, "mxfp8": 1}[w.act]
+    ws = B.workspace_bytes(p)
+    # at least xe, h and ye of R rows
+    assert ws >= R * w.d * elem + R * w.H * elem + R * w.d * (4 if w.act == "f32" else 2)
+    assert ws < 4 * (R * w.d * 6 + R * w.H * 4) + (1 << 26)
+    pw = B.packed_weight_bytes(p)
+    want = 3 * w.E * w.d * w.H * elem
+    if w.act == "mxfp8":
+        want = want * 33 // 32          # one E8M0 byte per 32 elements
+    assert want <= pw < want + 4 * 256

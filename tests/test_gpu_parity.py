@@ -1,0 +1,295 @@
+"""Parity of the HIP path against the CPU oracle on an MI355X (marked gpu).
+
+Bars: routing indices, counts, offsets, positions, row_token and dispatched
+rows (including MXFP8 codes and scales) bit-exact; gates within 1e-5
+absolute; outputs within max-abs 1e-5 (float32), normwise relative 2e-2
+(bf16) and 6e-2 (MXFP8), where normwise relative = max|out - ref| / max|ref|.
+Routing of learned-router blocks is checked as a function of the float32
+logits the GPU computed (the oracle re-routes those logits); the logits
+themselves are checked against the oracle's float64 product.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from oracle import mxfp8 as MX
+from routing_dispatch_grouped_router_amd import binding as B
+from routing_dispatch_grouped_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+Y_TOL = {"f32": ("abs", 1e-5), "bf16": ("rel", 2e-2), "mxfp8": ("rel", 6e-2)}
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy()
+
+
+def _f64(t):
+    return _np(t).astype(np.float64)
+
+
+def check_y(act, out, ref, what="y"):
+    kind, tol = Y_TOL[act]
+    err = np.max(np.abs(out - ref))
+    if kind == "abs":
+        assert err <= tol, f"{what}: max abs err {err:.3e} > {tol}"
+    else:
+        rel = err / max(np.max(np.abs(ref)), 1e-30)
+        assert rel <= tol, f"{what}: normwise rel err {rel:.3e} > {tol}"
+
+
+def problem_of(w, identity=False):
+    return B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned",
+                     identity=identity)
+
+
+def device_inputs(w):
+    host = W.make_inputs(w)
+    dev = {k: (None if v is None else v.to(DEV)) for k, v in host.items()}
+    return host, dev
+
+
+def check_routing(w, gpu, logits64):
+    """gpu: dict of device tensors from moe_route / moe_forward."""
+    idx, gate = O.route(logits64, w.k)
+    counts, offsets, pos, row_token = O.route_metadata(idx, w.E)
+    assert np.array_equal(_np(gpu["idx"]), idx), "topk_idx"
+    assert np.max(np.abs(_f64(gpu["gate"]) - gate)) <= 1e-5, "topk_gate"
+    assert np.array_equal(_np(gpu["counts"]), counts), "counts"
+    assert np.array_equal(_np(gpu["offsets"]), offsets), "offsets"
+    assert np.array_equal(_np(gpu["pos"]), pos), "pos"
+    if gpu.get("row_token") is not None:
+        assert np.array_equal(_np(gpu["row_token"]), row_token), "row_token"
+    assert int(counts.sum()) == w.T * w.k
+    return idx, gate, counts, offsets, pos
+
+
+def check_logits(w, host, gpu_logits):
+    if w.router != "learned":
+        assert torch.equal(gpu_logits.cpu(), host["logits"])
+        return host["logits"].double().numpy()
+    want = O.router_logits(W.as_f64(host["x"]), W.as_f64(host["w_router"]))
+    got = _f64(gpu_logits)
+    assert np.max(np.abs(got - want)) <= 1e-5 * max(1.0, np.max(np.abs(want))), "router logits"
+    return got
+
+
+def oracle_weights(host):
+    return (W.as_f64(host["w_gate"]), W.as_f64(host["w_up"]), W.as_f64(host["w_down"]))
+
+
+SMALL_NAMES = ["tiny_f32"] + list(W.SMALL)
+
+
+@pytest.mark.parametrize("name", SMALL_NAMES)
+def test_stages_against_oracle(name):
+    w = W.get(name)
+    print(f"[stages] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    ws = B.new_workspace(p, DEV)
+    r = B.route(p, x=dev["x"], w_router=dev["w_router"], logits=dev["logits"], ws=ws)
+    torch.cuda.synchronize()
+    L = check_logits(w, host, r["logits"])
+    idx, gate, counts, offsets, pos = check_routing(w, r, L)
+
+    x64 = W.as_f64(host["x"])
+    xe, xs = B.dispatch(p, dev["x"], r["pos"])
+    if w.act == "mxfp8":
+        xq_ref, xs_ref = O.dispatch(x64, pos, "mxfp8")
+        assert np.array_equal(_np(xe), xq_ref), "MXFP8 codes"
+        assert np.array_equal(_np(xs), xs_ref), "MXFP8 scales"
+        xe_vals = MX.dequantize(xq_ref, xs_ref, axis=1)
+    else:
+        xe_ref = O.dispatch(x64, pos, w.act)
+        assert np.array_equal(_f64(xe), xe_ref), "dispatched rows"
+        xe_vals = xe_ref
+
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    ye = B.grouped_swiglu(p, xe, xs, packed, r["offsets"], ws=ws)
+    wg, wu, wd = oracle_weights(host)
+    ye_ref = O.experts(xe_vals, offsets, wg, wu, wd, w.act)
+    check_y(w.act, _f64(ye), ye_ref, "ye")
+
+    y = B.combine(p, ye, r["gate"], r["pos"])
+    y_from_gpu_ye = O.combine(_f64(ye), _f64(r["gate"]), pos, O.out_dtype(w.act))
+    # combine alone: float32 accumulation of identical inputs -> within output rounding
+    tol = 1e-6 if w.act == "f32" else 2 ** -7
+    assert np.max(np.abs(_f64(y) - y_from_gpu_ye)) <= tol * max(1.0, np.max(np.abs(y_from_gpu_ye)))
+    check_y(w.act, _f64(y), O.combine(ye_ref, gate, pos, O.out_dtype(w.act)))
+
+
+@pytest.mark.parametrize("name", SMALL_NAMES)
+def test_forward_against_oracle(name):
+    w = W.get(name)
+    print(f"[forward] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    out = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    L = check_logits(w, host, out["logits"])
+    check_routing(w, out, L)
+    wg, wu, wd = oracle_weights(host)
+    ref = O.forward(W.as_f64(host["x"]), w.E, w.k, w.act, wg, wu, wd, logits=L)
+    check_y(w.act, _f64(out["y"]), ref["y"])
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_identity_experts_round_trip(act):
+    w = W.Workload("identity", T=300, d=256, E=16, k=4, H=64, act=act, router="random", seed=77)
+    print(f"[identity] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w, identity=True)
+    out = B.forward(p, dev["x"], logits=dev["logits"])
+    y = _f64(out["y"])
+    x = W.as_f64(host["x"])
+    if act == "bf16":
+        assert np.array_equal(y, x)
+    else:
+        assert np.max(np.abs(y - x)) <= 1e-6 * np.max(np.abs(x))
+
+
+@pytest.mark.parametrize("name", ["small_bf16_zipf", "small_f32_learned", "small_mxfp8"])
+def test_deterministic_bitwise(name):
+    w = W.get(name)
+    print(f"[determinism] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    f = B.Forward(p, DEV)
+    outs = []
+    for _ in range(2):
+        f(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (f.y, f.idx, f.gate, f.counts, f.offsets, f.pos, f.logits)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_graph_capture_replay():
+    w = W.get("small_bf16_e32_random")
+    print(f"[graph] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    f = B.Forward(p, DEV)
+    f(dev["x"], packed=packed, logits=dev["logits"])
+    torch.cuda.synchronize()
+    eager = f.y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        f(dev["x"], packed=packed, logits=f.logits)     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f(dev["x"], packed=packed, logits=f.logits)
+    for i in range(4):
+        f.y.fill_(float("nan"))
+        scratch = torch.randn(1024, device=DEV) * i      # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(f.y, eager), f"replay {i}"
+        del scratch
+
+
+# ----------------------------------------------------------------------------- full-size configurations
+
+N_SAMPLE = 24
+
+
+def _sample_tokens(T, seed=0):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(8, T - 8), size=N_SAMPLE - 16, replace=False) if T > 32 else []
+    return np.unique(np.concatenate([np.arange(min(8, T)), np.arange(max(0, T - 8), T), mid])).astype(np.int64)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_full_size_config(name):
+    """The five block configurations at full size, run exactly as the benchmark
+    runs them (moe_forward with packed weights): routing checked bit-exactly on
+    every token, y on sampled tokens against the oracle."""
+    w = W.CONFIGS[name]
+    print(f"[full] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    f = B.Forward(p, DEV)
+    f(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    gpu = dict(idx=f.idx, gate=f.gate, counts=f.counts, offsets=f.offsets, pos=f.pos)
+    if w.router == "learned":
+        L = _f64(f.logits)
+        rows = _sample_tokens(w.T, 1)
+        want = O.router_logits(W.as_f64(host["x"][rows]), W.as_f64(host["w_router"]))
+        assert np.max(np.abs(L[rows] - want)) <= 1e-5 * max(1.0, np.max(np.abs(want)))
+    else:
+        L = check_logits(w, host, f.logits)
+    idx, gate, counts, offsets, pos = check_routing(w, gpu, L)
+    toks = _sample_tokens(w.T)
+    ref = O.forward_tokens(W.as_f64(host["x"]), idx, gate, toks, w.act, host["w_gate"],
+                           host["w_up"], host["w_down"])
+    check_y(w.act, _f64(f.y)[toks], ref)
+    yall = _f64(f.y)
+    assert np.all(np.isfinite(yall))
+
+
+# ----------------------------------------------------------------------------- MXFP8 packing
+
+
+def _unpack_w1(packed_w1, E, d, H):
+    """Undo the documented gate/up interleave: packed row n -> (gate|up, column h)."""
+    n = np.arange(2 * H)
+    h = 32 * (n // 64) + n % 32
+    is_up = (n // 32) % 2 == 1
+    gate = np.empty((E, H, d), packed_w1.dtype)
+    up = np.empty((E, H, d), packed_w1.dtype)
+    gate[:, h[~is_up]] = packed_w1[:, n[~is_up]]
+    up[:, h[is_up]] = packed_w1[:, n[is_up]]
+    return gate, up
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_packed_weight_layout(act):
+    w = W.Workload("pack", T=4, d=256, E=3, k=2, H=384 if act == "bf16" else 256, act=act,
+                   router="random", seed=5)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    buf = packed.cpu().numpy()
+    E, d, H = w.E, w.d, w.H
+    al = lambda x: (x + 255) // 256 * 256
+    if act == "bf16":
+        n1, n2 = E * 2 * H * d * 2, E * d * H * 2
+        w1 = buf[:n1].view(np.uint16).reshape(E, 2 * H, d)
+        w2 = buf[al(n1):al(n1) + n2].view(np.uint16).reshape(E, d, H)
+        bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+        g, u = _unpack_w1(w1, E, d, H)
+        assert np.array_equal(g, bits(host["w_gate"]).transpose(0, 2, 1))
+        assert np.array_equal(u, bits(host["w_up"]).transpose(0, 2, 1))
+        assert np.array_equal(w2, bits(host["w_down"]).transpose(0, 2, 1))
+    else:
+        n1, n2 = E * 2 * H * d, E * d * H
+        o1, o2 = 0, al(n1)
+        o3 = o2 + al(n2)
+        o4 = o3 + al(n1 // 32)
+        w1 = buf[o1:o1 + n1].reshape(E, 2 * H, d)
+        w2 = buf[o2:o2 + n2].reshape(E, d, H)
+        s1 = buf[o3:o3 + n1 // 32].reshape(E, 2 * H, d // 32)
+        s2 = buf[o4:o4 + n2 // 32].reshape(E, d, H // 32)
+        gq, uq = _unpack_w1(w1, E, d, H)
+        gs, us = _unpack_w1(s1, E, d // 32, H)
+        for e in range(E):
+            for (codes, scales, src) in ((gq[e], gs[e], host["w_gate"][e]), (uq[e], us[e], host["w_up"][e]),
+                                         (w2[e], s2[e], host["w_down"][e])):
+                q_ref, s_ref = MX.quantize(W.as_f64(src), axis=0)     # blocks along K
+                assert np.array_equal(codes, q_ref.T), "E4M3 codes"
+                assert np.array_equal(scales, s_ref.T), "E8M0 scales"
