@@ -71,9 +71,9 @@ def source_digest(files) -> str:
 
 
 KERNEL_SOURCES = {
-    "gemm1_gate_up_swiglu": ["routing_dispatch_grouped_router_amd/csrc/gemm.hip",
+    "gemm1_gate_up_swiglu": ["routing_dispatch_grouped_router_amd/csrc/gemm_pipe.hip",
                              "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
-    "gemm2_down": ["routing_dispatch_grouped_router_amd/csrc/gemm.hip",
+    "gemm2_down": ["routing_dispatch_grouped_router_amd/csrc/gemm_pipe.hip",
                    "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
     "dispatch": ["routing_dispatch_grouped_router_amd/csrc/dispatch.hip"],
     "combine": ["routing_dispatch_grouped_router_amd/csrc/dispatch.hip"],

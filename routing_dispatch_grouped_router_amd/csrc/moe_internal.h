@@ -56,6 +56,10 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
                         int d, int H, hipStream_t s);
 
+// Pipelined bf16 grouped GEMM (gemm_pipe.hip); epi 1 = SwiGLU epilogue (C has N/2 columns).
+hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C,
+                            const int32_t* offsets, int R, int E, int N, int K, int ldc, hipStream_t s);
+
 // Weight packing (setup).
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
                        void* w2, uint8_t* s1, uint8_t* s2, int E, int d, int H, hipStream_t s);
