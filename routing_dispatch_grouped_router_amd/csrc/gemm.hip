@@ -117,7 +117,6 @@ static int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu) {
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                         int R, int E, int d, int H, hipStream_t s) {
-    (void)xe_scale; (void)w1_scale; (void)h_scale;
     const int N = 2 * H, K = d;
     if (act == kBF16) {
         return launch_bf16_pipe(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
@@ -127,7 +126,8 @@ hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const 
         hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, block, 0, s, static_cast<const float*>(xe),
                            static_cast<const float*>(w1), static_cast<float*>(h), offsets, E, N, K, H);
     } else {
-        return hipErrorNotSupported;
+        return launch_fp8_pipe(1, static_cast<const uint8_t*>(xe), xe_scale, static_cast<const uint8_t*>(w1), w1_scale,
+                               h, h_scale, offsets, R, E, N, K, H, s);
     }
     return hipGetLastError();
 }
@@ -135,7 +135,6 @@ hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const 
 hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const void* w2,
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
                         int d, int H, hipStream_t s) {
-    (void)h_scale; (void)w2_scale;
     const int N = d, K = H;
     if (act == kBF16) {
         return launch_bf16_pipe(0, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
@@ -145,7 +144,8 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
         hipLaunchKernelGGL(gemm_f32_kernel<0>, grid, block, 0, s, static_cast<const float*>(h),
                            static_cast<const float*>(w2), static_cast<float*>(ye), offsets, E, N, K, d);
     } else {
-        return hipErrorNotSupported;
+        return launch_fp8_pipe(0, static_cast<const uint8_t*>(h), h_scale, static_cast<const uint8_t*>(w2), w2_scale,
+                               ye, nullptr, offsets, R, E, N, K, d, s);
     }
     return hipGetLastError();
 }

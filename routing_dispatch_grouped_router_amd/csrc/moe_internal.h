@@ -60,6 +60,12 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C,
                             const int32_t* offsets, int R, int E, int N, int K, int ldc, hipStream_t s);
 
+// Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K.
+// epi 0: bf16 C [.., ldc];  epi 1: SwiGLU then MXFP8 C codes [.., ldc] + scales Cs [.., ldc / 32].
+hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
+                           void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
+                           hipStream_t s);
+
 // Weight packing (setup).
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
                        void* w2, uint8_t* s1, uint8_t* s2, int E, int d, int H, hipStream_t s);
