@@ -19,6 +19,7 @@
 namespace moe {
 
 constexpr int kRowsPerBlock = 4;   // one wave per token, 4 waves per workgroup
+constexpr int kGroup = 4;          // 16-byte chunks per lane loaded before they are stored
 
 // Final position of (t, j): with `base` non-NULL, pos holds the within-block
 // rank and is rewritten here; every lane computes the value, lane j writes it.
@@ -59,12 +60,22 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
                 if (j == lane) pos[(size_t)t * k + j] = p[j];
         }
     }
-    const uint4* src = x + (size_t)t * row_chunks;
-    for (int c = lane; c < row_chunks; c += 64) {
-        uint4 v = src[c];
+    // all of a lane's loads of a group are issued before any store
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * row_chunks;
+    u32x4* dst = reinterpret_cast<u32x4*>(xe);
+    for (int c0 = lane; c0 < row_chunks; c0 += 64 * kGroup) {
+        u32x4 v[kGroup];
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
-            if (j < k) xe[(size_t)p[j] * row_chunks + c] = v;
+        for (int g = 0; g < kGroup; ++g)
+            if (c0 + 64 * g < row_chunks) v[g] = src[c0 + 64 * g];
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+            if (j < k) {
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g)
+                    if (c0 + 64 * g < row_chunks) dst[(size_t)p[j] * row_chunks + c0 + 64 * g] = v[g];
+            }
+        }
     }
 }
 
@@ -92,35 +103,44 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __rest
                 if (j == lane) pos[(size_t)t * k + j] = p[j];
         }
     }
-    const int chunks = d / 8;                 // multiple of 64 lanes * ... (d % 128 == 0 -> 16 | chunks)
-    const uint4* src = x + (size_t)t * chunks;
-    for (int c = lane; c < chunks; c += 64) {
-        uint4 v = src[c];
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float f[8];
+    // d % 128 == 0, so chunks (8 values each) is a multiple of 16 and the four
+    // lanes of a 32-value block are always valid together
+    const int chunks = d / 8;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * chunks;
+    for (int c0 = lane; c0 < chunks; c0 += 64 * kGroup) {
+        u32x4 v[kGroup];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[2 * i] = __uint_as_float(w[i] << 16);
-            f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-        float amax = 0.f;
+        for (int g = 0; g < kGroup; ++g)
+            if (c0 + 64 * g < chunks) v[g] = src[c0 + 64 * g];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        const int se = mx_shared_exp(amax);
-        const float inv = mx_inv_scale(se);
-        uint32_t lo = 0, hi = 0;
+        for (int g = 0; g < kGroup; ++g) {
+            const int c = c0 + 64 * g;
+            if (c >= chunks) continue;
+            float f[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = __uint_as_float(v[g][i] << 16);
+                f[2 * i + 1] = __uint_as_float(v[g][i] & 0xFFFF0000u);
+            }
+            float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
-        const uint2 q = make_uint2(lo, hi);
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            const int se = mx_shared_exp(amax);
+            const float inv = mx_inv_scale(se);
+            uint32_t lo = 0, hi = 0;
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-            if (j < k) {
-                xq[(size_t)p[j] * chunks + c] = q;
-                if ((lane & 3) == 0) xs[(size_t)p[j] * (d / 32) + (c >> 2)] = (uint8_t)(se + 127);
+            for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
+            const uint2 q = make_uint2(lo, hi);
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (j < k) {
+                    xq[(size_t)p[j] * chunks + c] = q;
+                    if ((lane & 3) == 0) xs[(size_t)p[j] * (d / 32) + (c >> 2)] = (uint8_t)(se + 127);
+                }
             }
         }
     }
@@ -153,49 +173,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
     int p[kMaxTopK];
-    float g[kMaxTopK];
+    float gt[kMaxTopK];
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
         if (j < k) {
             p[j] = pos[(size_t)t * k + j];
-            g[j] = gate[(size_t)t * k + j];
+            gt[j] = gate[(size_t)t * k + j];
         }
     }
-    for (int c = lane; c < row_chunks; c += 64) {
-        constexpr int kN = kBf16 ? 8 : 4;
-        float acc[kN];
+    const u32x4* src = reinterpret_cast<const u32x4*>(ye);
+    u32x4* dst = reinterpret_cast<u32x4*>(y);
+    constexpr int kN = kBf16 ? 8 : 4;
+    for (int c0 = lane; c0 < row_chunks; c0 += 64 * kGroup) {
+        float acc[kGroup][kN];
 #pragma unroll
-        for (int i = 0; i < kN; ++i) acc[i] = 0.f;
+        for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+            for (int i = 0; i < kN; ++i) acc[g][i] = 0.f;
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
             if (j < k) {
-                uint4 v = ye[(size_t)p[j] * row_chunks + c];
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
-                if (kBf16) {
+                // the group's rows of slot j are loaded together, then accumulated in slot order
+                u32x4 v[kGroup];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[2 * i] = fmaf(g[j], __uint_as_float(w[i] << 16), acc[2 * i]);
-                        acc[2 * i + 1] = fmaf(g[j], __uint_as_float(w[i] & 0xFFFF0000u), acc[2 * i + 1]);
+                for (int g = 0; g < kGroup; ++g)
+                    if (c0 + 64 * g < row_chunks) v[g] = src[(size_t)p[j] * row_chunks + c0 + 64 * g];
+#pragma unroll
+                for (int g = 0; g < kGroup; ++g) {
+                    if (c0 + 64 * g >= row_chunks) continue;
+                    if (kBf16) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[g][2 * i] = fmaf(gt[j], __uint_as_float(v[g][i] << 16), acc[g][2 * i]);
+                            acc[g][2 * i + 1] = fmaf(gt[j], __uint_as_float(v[g][i] & 0xFFFF0000u), acc[g][2 * i + 1]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[g][i] = fmaf(gt[j], __uint_as_float(v[g][i]), acc[g][i]);
                     }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] = fmaf(g[j], __uint_as_float(w[i]), acc[i]);
                 }
             }
         }
-        uint4 o;
-        if (kBf16) {
-            o.x = pack_bf16x2(acc[0], acc[1]);
-            o.y = pack_bf16x2(acc[2], acc[3]);
-            o.z = pack_bf16x2(acc[4], acc[5]);
-            o.w = pack_bf16x2(acc[6], acc[7]);
-        } else {
-            o.x = __float_as_uint(acc[0]);
-            o.y = __float_as_uint(acc[1]);
-            o.z = __float_as_uint(acc[2]);
-            o.w = __float_as_uint(acc[3]);
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            if (c0 + 64 * g >= row_chunks) continue;
+            u32x4 o;
+            if (kBf16) {
+                o = (u32x4){pack_bf16x2(acc[g][0], acc[g][1]), pack_bf16x2(acc[g][2], acc[g][3]),
+                            pack_bf16x2(acc[g][4], acc[g][5]), pack_bf16x2(acc[g][6], acc[g][7])};
+            } else {
+                o = (u32x4){__float_as_uint(acc[g][0]), __float_as_uint(acc[g][1]), __float_as_uint(acc[g][2]),
+                            __float_as_uint(acc[g][3])};
+            }
+            dst[(size_t)t * row_chunks + c0 + 64 * g] = o;
         }
-        y[(size_t)t * row_chunks + c] = o;
     }
 }
 

@@ -43,8 +43,19 @@ __device__ __forceinline__ float load1<float>(const float* p) { return *p; }
 template <>
 __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
 
-// One wave computes 4 tokens x 8 experts at a time; lanes split d in runs of 8.
-constexpr int kRtTok = 4;
+template <typename TIn>
+__device__ __forceinline__ void load8w(const TIn* p, float (&v)[8]);   // 8 consecutive weights
+template <>
+__device__ __forceinline__ void load8w<float>(const float* p, float (&v)[8]) { load8<float>(p, v); }
+template <>
+__device__ __forceinline__ void load8w<uint16_t>(const uint16_t* p, float (&v)[8]) { load8<uint16_t>(p, v); }
+
+// One wave computes 8 tokens x 8 experts at a time; lanes split d in runs of
+// 8 elements.  The 64 partial sums of a lane are reduce-scattered across the
+// wave (halving the value set at each of the 6 butterfly steps: 63 shuffles
+// instead of 6 per value), after which lane l holds the full sum of value l,
+// i.e. token l / 8, expert l % 8.
+constexpr int kRtTok = 8;
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restrict__ x,
@@ -55,49 +66,48 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restric
     const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int t0 = wave * kRtTok;
     if (t0 >= T) return;
+    const bool vec_w = (E & 7) == 0;
     for (int e0 = 0; e0 < E; e0 += 8) {
-        float acc[kRtTok][8];
+        float acc[64];
 #pragma unroll
-        for (int a = 0; a < kRtTok; ++a)
-#pragma unroll
-            for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
+        for (int i = 0; i < 64; ++i) acc[i] = 0.f;
         for (int kb = lane * 8; kb < d; kb += 64 * 8) {
             float xv[kRtTok][8];
 #pragma unroll
             for (int a = 0; a < kRtTok; ++a) {
-                int t = min(t0 + a, T - 1);
+                const int t = min(t0 + a, T - 1);
                 load8<TIn>(x + (size_t)t * d + kb, xv[a]);
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const TIn* wr = w + (size_t)(kb + q) * E + e0;
+                float wv[8];
+                if (vec_w) {
+                    load8w<TIn>(wr, wv);
+                } else {
 #pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    float wv = (e0 + b < E) ? load1<TIn>(wr + b) : 0.f;
-#pragma unroll
-                    for (int a = 0; a < kRtTok; ++a) acc[a][b] = fmaf(xv[a][q], wv, acc[a][b]);
+                    for (int b = 0; b < 8; ++b) wv[b] = (e0 + b < E) ? load1<TIn>(wr + b) : 0.f;
                 }
+#pragma unroll
+                for (int a = 0; a < kRtTok; ++a)
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) acc[a * 8 + b] = fmaf(xv[a][q], wv[b], acc[a * 8 + b]);
             }
         }
+        // reduce-scatter: at mask m the lane keeps the upper half of its current
+        // values if (lane & m) else the lower half, adding the partner's copy
 #pragma unroll
-        for (int a = 0; a < kRtTok; ++a)
+        for (int m = 32, n = 64; m >= 1; m >>= 1, n >>= 1) {
+            const bool up = (lane & m) != 0;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                float v = acc[a][b];
-#pragma unroll
-                for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-                acc[a][b] = v;
+            for (int i = 0; i < n / 2; ++i) {
+                const float keep = up ? acc[i + n / 2] : acc[i];
+                const float send = up ? acc[i] : acc[i + n / 2];
+                acc[i] = keep + __shfl_xor(send, m);
             }
-        if (lane < kRtTok * 8) {
-            int a = lane >> 3, b = lane & 7;
-            float v = 0.f;
-#pragma unroll
-            for (int aa = 0; aa < kRtTok; ++aa)
-#pragma unroll
-                for (int bb = 0; bb < 8; ++bb)
-                    if (aa == a && bb == b) v = acc[aa][bb];
-            if (t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = v;
         }
+        const int a = lane >> 3, b = lane & 7;
+        if (t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = acc[0];
     }
 }
 
