@@ -137,6 +137,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(W.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="before the timed steps, run one plain device copy of this many MiB (a known "
+                         "byte count that calibrates HBM counters such as FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the routed block: this build has no "
@@ -160,6 +163,14 @@ def main(argv=None):
 
     for _ in range(args.warmup):
         step()
+    if args.calibration_copy_mb > 0:
+        n = args.calibration_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     B.set_profiling(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
