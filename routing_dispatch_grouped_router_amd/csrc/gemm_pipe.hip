@@ -106,23 +106,73 @@ struct RingTile {
     static constexpr int A_DMA = BM / 16 / NW, B_DMA = BN / 16 / NW;   // 1 KB blocks per wave per stage
     static constexpr int P = A_DMA + B_DMA;                            // data DMAs per wave per K-tile
     static constexpr int STAGE_CHUNKS = (BM + BN) * 4;                 // 16-byte chunks per stage
+    static constexpr int NM = TM * TN;                                 // MFMAs per wave per k-step
+    static constexpr int EARLY = TN;                                   // MFMAs issued before a barrier
     static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "stage / wave mismatch");
     static_assert(TN % 2 == 0, "a wave's N range must hold whole gate/up pairs");
 };
 
-// Per-thread state of the ring: global bases (wave-uniform) and this lane's
-// DMA offsets for K-tile 0.
+// Rows and columns of one output tile.  The expert index is wave-uniform, so
+// the offsets reads are scalar loads.
+struct TileCoord {
+    int row0, rows, n0, e;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ TileCoord tile_coord(int tile, int NT, const int* s_tstart, int E,
+                                                const int32_t* __restrict__ offsets) {
+    const int mt = tile / NT, nt = tile - mt * NT;
+    TileCoord c;
+    c.e = __builtin_amdgcn_readfirstlane(tile_expert(s_tstart, E, mt));
+    const int o0 = offsets[c.e], o1 = offsets[c.e + 1];
+    c.row0 = o0 + (mt - __builtin_amdgcn_readfirstlane(s_tstart[c.e])) * BM;
+    c.rows = min(BM, o1 - c.row0);
+    c.n0 = nt * BN;
+    return c;
+}
+
+// Per-lane DMA state: global bases (wave-uniform), this lane's byte offsets of
+// K-tile 0, and the LDS ring.  A K-tile is 64 bytes of every row; rows past the
+// tile's valid range re-read the last valid row (their results are never
+// stored).  issue(kt) always starts the same number of loads, so every vmcnt
+// wait below is a constant: for kt past the last K-tile the source is clamped
+// to the last one and the stage written is one no later read uses.
 template <class TL>
 struct Ring {
     const void* Ag;
     const void* Bg;
     uint32_t offA[TL::A_DMA], offB[TL::B_DMA];
-    uint32_t ring_lds;      // LDS byte address of the ring
-    int nk, wave, lane;
+    uint32_t ring_lds;
+    int nk, wave, drow;
+    uint32_t dchunk;
 
-    // DMA of K-tile kt (64 bytes of every row) into stage kt % 4.
+    __device__ __forceinline__ void init(const void* A, uint32_t ring_addr, int K_tiles) {
+        const int lane = threadIdx.x & 63;
+        wave = threadIdx.x >> 6;
+        Ag = A;
+        ring_lds = ring_addr;
+        nk = K_tiles;
+        drow = lane >> 2;
+        dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    }
+
+    // row_bytes: bytes of one A / B row (the K extent)
+    __device__ __forceinline__ void setup(const TileCoord& c, const void* Be, int N, uint32_t row_bytes) {
+        Bg = Be;
+#pragma unroll
+        for (int i = 0; i < TL::A_DMA; ++i) {
+            const int r = 16 * (wave * TL::A_DMA + i) + drow;
+            offA[i] = (uint32_t)(c.row0 + min(r, c.rows - 1)) * row_bytes + dchunk;
+        }
+#pragma unroll
+        for (int i = 0; i < TL::B_DMA; ++i) {
+            const int r = 16 * (wave * TL::B_DMA + i) + drow;
+            offB[i] = (uint32_t)min(c.n0 + r, N - 1) * row_bytes + dchunk;
+        }
+    }
+
     __device__ __forceinline__ void issue(int kt) const {
-        const uint32_t ko = (uint32_t)kt * 64u;
+        const uint32_t ko = (uint32_t)min(kt, nk - 1) * 64u;
         const uint32_t st = ring_lds + (uint32_t)(kt & 3) * TL::STAGE_CHUNKS * 16u;
         const uint32_t la = __builtin_amdgcn_readfirstlane(st + wave * TL::A_DMA * 1024u);
         const uint32_t lb = __builtin_amdgcn_readfirstlane(st + TL::BM * 64u + wave * TL::B_DMA * 1024u);
@@ -132,6 +182,46 @@ struct Ring {
         for (int i = 0; i < TL::B_DMA; ++i) dma16(Bg, offB[i] + ko, lb + i * 1024u);
     }
 };
+
+// Output layout.  The MFMAs take the weight fragment as their first operand
+// and the activation fragment as their second, so accumulator (mi, ni) is the
+// transposed 32 x 32 block: lane l holds tile row mi*32 + l%32 and, in element
+// v, tile column ni*32 + 8*(v/4) + 4*(l/32) + v%4.  Each lane thus owns runs of
+// four consecutive columns of one row; one v_permlane32_swap per pair of runs
+// gives lane halves 0 and 1 the low and high 16 columns of a 32-column block.
+//
+// w0..w3: the four runs (q = 0..3) of one 32-column block as 32-bit words of
+// this lane; on return lane half 0 holds columns 0..15 and half 1 columns
+// 16..31 of the block, in order.
+__device__ __forceinline__ void gather_halves(uint32_t (&w)[4]) {
+    const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+    w[0] = s02[0];
+    w[1] = s02[1];
+    w[2] = s13[0];
+    w[3] = s13[1];
+}
+
+// bf16 block store: the 16 values of acc (one 32 x 32 block, this lane's row)
+// as bf16 columns [col0, col0 + 32) of row `grow` of C (if the row is valid).
+__device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_t ldc, int grow, bool valid,
+                                                 int col0, const float (&v)[16]) {
+    uint32_t lo[4], hi[4];   // run q: columns 8q + 4 half + (0, 1) and (2, 3)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        lo[q] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
+        hi[q] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+    }
+    gather_halves(lo);
+    gather_halves(hi);
+    // half 0: columns 0..15 = runs (w0 = q0 lo/hi of half 0, w1 = q0 of half 1, ...)
+    const int half = (threadIdx.x >> 5) & 1;
+    if (valid) {
+        u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)grow * ldc + col0 + 16 * half);
+        dst[0] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
+        dst[1] = (u32x4){lo[2], hi[2], lo[3], hi[3]};
+    }
+}
 
 // ============================================================================ bf16
 
@@ -146,14 +236,47 @@ __device__ __forceinline__ void bf_load(const u32x4* stage, int aoff, int boff, 
     for (int ni = 0; ni < TL::TN; ++ni) fb[ni] = __builtin_bit_cast(bf16x8, stage[boff + ni * 128]);
 }
 
-template <class TL>
+// MFMAs [FIRST, FIRST + COUNT) of the TM x TN block, row-major over (mi, ni).
+template <class TL, int FIRST, int COUNT>
 __device__ __forceinline__ void bf_mfma(const bf16x8 (&fa)[TL::TM], const bf16x8 (&fb)[TL::TN],
                                         f32x16 (&acc)[TL::TM][TL::TN]) {
 #pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi)
+    for (int i = FIRST; i < FIRST + COUNT; ++i) {
+        const int mi = i / TL::TN, ni = i % TL::TN;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+    }
+}
+
+// Epilogue of the bf16 kernel.  EPI 0: C = acc as bf16.  EPI 1: columns come
+// in gate/up pairs of 32; C column (pair column)/2 + j = silu(gate_j) * up_j.
+template <class TL, int EPI>
+__device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], uint16_t* __restrict__ C,
+                                            int ldc, int N, const TileCoord& c, int wm, int wn) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int ni = 0; ni < TL::TN; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    for (int mi = 0; mi < TL::TM; ++mi) {
+        const int r = wm * TL::WROWS + mi * 32 + (lane & 31);
+        const bool valid = r < c.rows;
+        if (EPI == 0) {
+#pragma unroll
+            for (int ni = 0; ni < TL::TN; ++ni) {
+                const int col0 = c.n0 + wn * TL::WCOLS + ni * 32;
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = acc[mi][ni][i];
+                store_bf16_block(C, (size_t)ldc, c.row0 + r, valid && col0 < N, col0, v);
+            }
+        } else {
+#pragma unroll
+            for (int np = 0; np < TL::TN / 2; ++np) {
+                const int pc = c.n0 + wn * TL::WCOLS + np * 64;
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
+                store_bf16_block(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v);
+            }
+        }
+    }
 }
 
 template <class TL, int EPI>   // EPI 0: C = A B (bf16);  1: C = silu(A Bgate) * (A Bup) (bf16, N/2 columns)
@@ -162,7 +285,8 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
                            uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int E, int N, int K,
                            int ldc) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
-    __shared__ u32x4 ring[TL::STAGES * TL::STAGE_CHUNKS];
+    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
+    __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
 
@@ -171,43 +295,26 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
     const int total = MT * NT;
     const int G = gridDim.x;
     const uint32_t rowbytes = (uint32_t)K * 2u;
+    int tile = xcd_slot(blockIdx.x, G);
+    if (tile >= total) return;
 
     Ring<TL> rg;
-    rg.lane = threadIdx.x & 63;
-    rg.wave = threadIdx.x >> 6;
-    rg.nk = K / 32;
-    rg.Ag = A;
-    rg.ring_lds = lds_addr(ring);
+    rg.init(A, lds_addr(ring), K / 32);
+    const int nk = rg.nk;
+    const int lane = threadIdx.x & 63;
     const int wm = rg.wave / TL::WN, wn = rg.wave % TL::WN;
-    const int fsw = ((rg.lane & 31) >> 2) & 3, half = rg.lane >> 5;
-    const int arow = (wm * TL::WROWS + (rg.lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (rg.lane & 31)) * 4;
+    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
+    const int arow = (wm * TL::WROWS + (lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 4;
     const int a0 = arow + ((0 + half) ^ fsw), a1 = arow + ((2 + half) ^ fsw);
     const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
-    const int drow = rg.lane >> 2;
-    const uint32_t dchunk = (uint32_t)((rg.lane & 3) ^ ((rg.lane >> 4) & 3)) * 16u;
 
-    for (int tile = xcd_slot(blockIdx.x, G); tile < total; tile += G) {
-        const int mt = tile / NT, nt = tile - mt * NT;
-        const int e = tile_expert(s_tstart, E, mt);
-        const int row0 = offsets[e] + (mt - s_tstart[e]) * BM;
-        const int rows = min(BM, offsets[e + 1] - row0);
-        const int n0 = nt * BN;
-        rg.Bg = B + (size_t)__builtin_amdgcn_readfirstlane(e) * N * K;
-#pragma unroll
-        for (int i = 0; i < TL::A_DMA; ++i) {
-            const int r = 16 * (rg.wave * TL::A_DMA + i) + drow;
-            rg.offA[i] = (uint32_t)(row0 + min(r, rows - 1)) * rowbytes + dchunk;
-        }
-#pragma unroll
-        for (int i = 0; i < TL::B_DMA; ++i) {
-            const int r = 16 * (rg.wave * TL::B_DMA + i) + drow;
-            rg.offB[i] = (uint32_t)min(n0 + r, N - 1) * rowbytes + dchunk;
-        }
-        ring_barrier();   // every wave is done reading the previous tile's stages
-        rg.issue(0);
-        if (rg.nk > 1) rg.issue(1);
-        if (rg.nk > 2) rg.issue(2);
+    TileCoord c = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets);
+    rg.setup(c, B + (size_t)c.e * N * K, N, rowbytes);
+    rg.issue(0);
+    rg.issue(1);
+    rg.issue(2);
 
+    for (;;) {
         f32x16 acc[TM][TN];
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
@@ -216,61 +323,51 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        if (rg.nk > 2) wait_vm<2 * TL::P>();
-        else if (rg.nk > 1) wait_vm<TL::P>();
-        else wait_vm<0>();
-        ring_barrier();
         bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+        wait_vm<2 * P>();   // K-tile 0 landed; 1 and 2 may stay in flight
+        ring_barrier();
         bf_load<TL>(ring, a0, b0, fa0, fb0);
-        for (int kt = 0; kt < rg.nk; ++kt) {
-            const u32x4* cur = ring + (kt & 3) * TL::STAGE_CHUNKS;
-            bf_load<TL>(cur, a1, b1, fa1, fb1);
-            bf_mfma<TL>(fa0, fb0, acc);
-            interleave_hint<TM + TN, TM * TN>();
-            if (kt + 1 < rg.nk) {
-                if (kt + 2 < rg.nk) wait_vm<TL::P>();    // K-tile kt + 2 may stay in flight
-                else wait_vm<0>();
-                ring_barrier();
-                if (kt + 3 < rg.nk) rg.issue(kt + 3);
-                bf_load<TL>(ring + ((kt + 1) & 3) * TL::STAGE_CHUNKS, a0, b0, fa0, fb0);
-            }
-            bf_mfma<TL>(fa1, fb1, acc);
-            interleave_hint<TM + TN, TM * TN>();
+        // K-tile kt: k-step 0 in set 0 (read during the previous K-tile), k-step 1
+        // read into set 1 while set 0 multiplies; then a few MFMAs of set 1, the
+        // wait for K-tile kt + 1 and the barrier, the DMA of kt + 3 into the stage
+        // everyone is done with, and set 0 of kt + 1 read between the remaining MFMAs.
+        for (int kt = 0; kt < nk - 1; ++kt) {
+            bf_load<TL>(ring + (kt & 3) * SC, a1, b1, fa1, fb1);
+            bf_mfma<TL, 0, NM>(fa0, fb0, acc);
+            interleave_hint<TM + TN, NM>();
+            __builtin_amdgcn_sched_barrier(0);
+            bf_mfma<TL, 0, EARLY>(fa1, fb1, acc);
+            wait_vm<P>();   // K-tile kt + 1 landed; kt + 2 may stay in flight
+            ring_barrier();
+            rg.issue(kt + 3);
+            bf_load<TL>(ring + ((kt + 1) & 3) * SC, a0, b0, fa0, fb0);
+            bf_mfma<TL, EARLY, NM - EARLY>(fa1, fb1, acc);
+            interleave_hint<TM + TN, NM - EARLY>();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        bf_load<TL>(ring + ((nk - 1) & 3) * SC, a1, b1, fa1, fb1);
+        bf_mfma<TL, 0, NM>(fa0, fb0, acc);
+        interleave_hint<TM + TN, NM>();
+        __builtin_amdgcn_sched_barrier(0);
+        bf_mfma<TL, 0, NM>(fa1, fb1, acc);
 
-        // accumulator (mi, ni)[v] holds tile row wm*WROWS + mi*32 + 8*(v/4) + 4*(lane/32) + v%4
-        // and tile column wn*WCOLS + ni*32 + lane%32
-        const int rbase = wm * TL::WROWS + 4 * half;
-        if (EPI == 0) {
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni) {
-                    const int col = n0 + wn * TL::WCOLS + ni * 32 + (rg.lane & 31);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = rbase + mi * 32 + 8 * (v >> 2) + (v & 3);
-                        if (r < rows && col < N)
-                            C[(size_t)(row0 + r) * ldc + col] = f32_to_bf16(acc[mi][ni][v]);
-                    }
-                }
-        } else {
-#pragma unroll
-            for (int np = 0; np < TN / 2; ++np) {
-                const int pc = n0 + wn * TL::WCOLS + np * 64;
-                if (pc >= N) continue;
-                const int hcol = pc / 2 + (rg.lane & 31);
-#pragma unroll
-                for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = rbase + mi * 32 + 8 * (v >> 2) + (v & 3);
-                        if (r < rows)
-                            C[(size_t)(row0 + r) * ldc + hcol] =
-                                f32_to_bf16(silu_mul_p(acc[mi][2 * np][v], acc[mi][2 * np + 1][v]));
-                    }
-            }
+        // Start the next tile's first three K-tiles before this tile's epilogue:
+        // once every wave is past its last fragment read (and the clamped loads
+        // past the end have landed) the whole ring is free.
+        const TileCoord cur = c;
+        const int next = tile + G;
+        wait_vm<0>();
+        ring_barrier();
+        if (next < total) {
+            c = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
+            rg.setup(c, B + (size_t)c.e * N * K, N, rowbytes);
+            rg.issue(0);
+            rg.issue(1);
+            rg.issue(2);
         }
+        bf_epilogue<TL, EPI>(acc, C, ldc, N, cur, wm, wn);
+        if (next >= total) break;
+        tile = next;
     }
 }
 
@@ -316,16 +413,79 @@ __device__ __forceinline__ void fp8_load(const u32x4* stage, const uint32_t* ssl
     }
 }
 
-template <class TL, int OPSEL>
+// MFMAs [FIRST, FIRST + COUNT) of the TM x TN block, row-major over (mi, ni).
+template <class TL, int OPSEL, int FIRST, int COUNT>
 __device__ __forceinline__ void fp8_mfma(const i32x8 (&fa)[TL::TM], const i32x8 (&fb)[TL::TN],
                                          const int (&sa)[TL::TM], const int (&sb)[TL::TN],
                                          f32x16 (&acc)[TL::TM][TL::TN]) {
 #pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi)
+    for (int i = FIRST; i < FIRST + COUNT; ++i) {
+        const int mi = i / TL::TN, ni = i % TL::TN;
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ni], fa[mi], acc[mi][ni], 0, 0, OPSEL,
+                                                                     sb[ni], OPSEL, sa[mi]);
+    }
+}
+
+// Epilogue of the MXFP8 kernel.  EPI 0: C = acc as bf16.  EPI 1: h = silu(gate)
+// * up per gate/up column pair, quantised to MXFP8 along h: each 32-column
+// block of one row is split over lanes l and l ^ 32, which agree on the block
+// maximum, take the shared exponent floor(log2 amax) - 8, and encode with the
+// hardware E4M3 conversion (round to nearest even) after clamping to +-448,
+// which is the saturating encode.
+template <class TL, int EPI>
+__device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], void* __restrict__ C,
+                                             uint8_t* __restrict__ Cs, int ldc, int N, const TileCoord& c, int wm,
+                                             int wn) {
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
 #pragma unroll
-        for (int ni = 0; ni < TL::TN; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[mi], fb[ni], acc[mi][ni], 0, 0, OPSEL,
-                                                                         sa[mi], OPSEL, sb[ni]);
+    for (int mi = 0; mi < TL::TM; ++mi) {
+        const int r = wm * TL::WROWS + mi * 32 + (lane & 31);
+        const bool valid = r < c.rows;
+        const size_t grow = (size_t)(c.row0 + r);
+        if (EPI == 0) {
+#pragma unroll
+            for (int ni = 0; ni < TL::TN; ++ni) {
+                const int col0 = c.n0 + wn * TL::WCOLS + ni * 32;
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = acc[mi][ni][i];
+                store_bf16_block(static_cast<uint16_t*>(C), (size_t)ldc, (int)grow, valid && col0 < N, col0, v);
+            }
+        } else {
+#pragma unroll
+            for (int np = 0; np < TL::TN / 2; ++np) {
+                const int pc = c.n0 + wn * TL::WCOLS + np * 64;
+                float v[16];
+                float amax = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
+                    amax = fmaxf(amax, fabsf(v[i]));
+                }
+                amax = fmaxf(amax, __shfl_xor(amax, 32));
+                const int se = mx_shared_exp(amax);
+                const float inv = mx_inv_scale(se);
+                uint32_t w[4];   // run q: 4 codes of columns 8q + 4 half + 0..3
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float x[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(v[4 * q + i] * inv, -448.f), 448.f);
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pk, true);
+                    w[q] = (uint32_t)pk;
+                }
+                gather_halves(w);
+                if (valid && pc < N) {
+                    const int hb = pc / 64;   // 32-wide h block of this pair
+                    uint8_t* Cq = static_cast<uint8_t*>(C);
+                    *reinterpret_cast<u32x4*>(Cq + grow * ldc + hb * 32 + 16 * half) = (u32x4){w[0], w[1], w[2], w[3]};
+                    if (half == 0) Cs[grow * (ldc / 32) + hb] = (uint8_t)(se + 127);
+                }
+            }
+        }
+    }
 }
 
 template <class TL, int EPI>   // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2
@@ -336,7 +496,8 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
                           int ldc) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
-    __shared__ u32x4 ring[TL::STAGES * TL::STAGE_CHUNKS];
+    constexpr int NM = TL::NM, EARLY = TL::EARLY, NR = 3 * (TM + TN), P = TL::P, SC = TL::STAGE_CHUNKS;
+    __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ uint32_t sring[2 * (BM + BN)];     // two scale slots: A rows then B rows
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
@@ -346,66 +507,56 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     const int total = MT * NT;
     const int G = gridDim.x;
     const int kb = K / 32;            // scale bytes per row
+    int tile = xcd_slot(blockIdx.x, G);
+    if (tile >= total) return;
 
     Ring<TL> rg;
-    rg.lane = threadIdx.x & 63;
-    rg.wave = threadIdx.x >> 6;
-    rg.nk = K / 64;
-    rg.Ag = A;
-    rg.ring_lds = lds_addr(ring);
+    rg.init(A, lds_addr(ring), K / 64);
+    const int nk = rg.nk;
+    const int lane = threadIdx.x & 63;
     const uint32_t sring_lds = lds_addr(sring);
     const int wm = rg.wave / TL::WN, wn = rg.wave % TL::WN;
-    const int fsw = ((rg.lane & 31) >> 2) & 3, half = rg.lane >> 5;
-    const int arow_i = wm * TL::WROWS + (rg.lane & 31), brow_i = wn * TL::WCOLS + (rg.lane & 31);
+    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
+    const int arow_i = wm * TL::WROWS + (lane & 31), brow_i = wn * TL::WCOLS + (lane & 31);
     const int a0 = arow_i * 4 + (half ^ fsw), a1 = arow_i * 4 + ((2 + half) ^ fsw);
     const int b0 = (BM + brow_i) * 4 + (half ^ fsw), b1 = (BM + brow_i) * 4 + ((2 + half) ^ fsw);
     const int sh = half * 8;
-    const int drow = rg.lane >> 2;
-    const uint32_t dchunk = (uint32_t)((rg.lane & 3) ^ ((rg.lane >> 4) & 3)) * 16u;
-    const int srow = SR * rg.wave + (rg.lane & (SR - 1));    // scale DMA row of this lane
-    const bool slane = rg.lane < SR;
+    const int srow = SR * rg.wave + (lane & (SR - 1));    // scale DMA row of this lane
+    const bool slane = lane < SR;
 
-    for (int tile = xcd_slot(blockIdx.x, G); tile < total; tile += G) {
-        const int mt = tile / NT, nt = tile - mt * NT;
-        const int e = tile_expert(s_tstart, E, mt);
-        const int row0 = offsets[e] + (mt - s_tstart[e]) * BM;
-        const int rows = min(BM, offsets[e + 1] - row0);
-        const int n0 = nt * BN;
-        const size_t eu = (size_t)__builtin_amdgcn_readfirstlane(e);
-        rg.Bg = B + eu * N * K;
-        const void* Bsg = Bs + eu * N * kb;
-#pragma unroll
-        for (int i = 0; i < TL::A_DMA; ++i) {
-            const int r = 16 * (rg.wave * TL::A_DMA + i) + drow;
-            rg.offA[i] = (uint32_t)(row0 + min(r, rows - 1)) * (uint32_t)K + dchunk;
-        }
-#pragma unroll
-        for (int i = 0; i < TL::B_DMA; ++i) {
-            const int r = 16 * (rg.wave * TL::B_DMA + i) + drow;
-            rg.offB[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + dchunk;
-        }
-        const uint32_t soA = (uint32_t)(row0 + min(srow, rows - 1)) * kb;
-        const uint32_t soB = (uint32_t)min(n0 + srow, N - 1) * kb;
-
-        // data of K-tile kt, plus (kt even) the scale dwords of K-tiles kt, kt + 1 into slot (kt / 2) & 1
-        auto issue = [&](int kt) {
-            rg.issue(kt);
-            if ((kt & 1) == 0) {
-                const uint32_t slot = sring_lds + (uint32_t)((kt >> 1) & 1) * (BM + BN) * 4u;
-                const uint32_t lsa = __builtin_amdgcn_readfirstlane(slot + rg.wave * SR * 4u);
-                const uint32_t lsb = __builtin_amdgcn_readfirstlane(slot + BM * 4u + rg.wave * SR * 4u);
-                if (slane) {
-                    dma4(As, soA + (uint32_t)kt * 2u, lsa);
-                    dma4(Bsg, soB + (uint32_t)kt * 2u, lsb);
-                }
+    TileCoord c;
+    const void* Bsg;
+    uint32_t soA, soB;
+    auto setup = [&](int t) {
+        c = tile_coord<BM, BN>(t, NT, s_tstart, E, offsets);
+        const size_t eu = (size_t)c.e;
+        rg.setup(c, B + eu * N * K, N, (uint32_t)K);
+        Bsg = Bs + eu * N * kb;
+        soA = (uint32_t)(c.row0 + min(srow, c.rows - 1)) * kb;
+        soB = (uint32_t)min(c.n0 + srow, N - 1) * kb;
+    };
+    // DMA of K-tile kt, plus (kt even) the scale dwords of K-tiles kt, kt + 1
+    // into slot (kt / 2) & 1; clamped past the end like the data.
+    auto issue = [&](int kt) {
+        rg.issue(kt);
+        if ((kt & 1) == 0) {
+            const uint32_t so = (uint32_t)min(kt, nk - 2) * 2u;
+            const uint32_t slot = sring_lds + (uint32_t)((kt >> 1) & 1) * (BM + BN) * 4u;
+            const uint32_t lsa = __builtin_amdgcn_readfirstlane(slot + rg.wave * SR * 4u);
+            const uint32_t lsb = __builtin_amdgcn_readfirstlane(slot + BM * 4u + rg.wave * SR * 4u);
+            if (SR == 64 || slane) {
+                dma4(As, soA + so, lsa);
+                dma4(Bsg, soB + so, lsb);
             }
-        };
+        }
+    };
 
-        ring_barrier();   // every wave is done reading the previous tile's stages and scales
-        issue(0);
-        if (rg.nk > 1) issue(1);
-        if (rg.nk > 2) issue(2);
+    setup(tile);
+    issue(0);
+    issue(1);
+    issue(2);
 
+    for (;;) {
         f32x16 acc[TM][TN];
 #pragma unroll
         for (int mi = 0; mi < TM; ++mi)
@@ -414,102 +565,62 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        // K-tile 0 (with scales) landed: tiles 1 (P) and 2 (P + PS) may stay in flight
-        if (rg.nk > 2) wait_vm<2 * TL::P + PS>();
-        else if (rg.nk > 1) wait_vm<TL::P>();
-        else wait_vm<0>();
-        ring_barrier();
         i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
         int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
+        wait_vm<2 * P + PS>();   // K-tile 0 and its scales landed; 1 and 2 may stay in flight
+        ring_barrier();
         fp8_load<TL>(ring, sring, a0, a1, b0, b1, arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
-        // nk is even (K % 128 == 0): K-tiles go in pairs (even: register set 0, op_sel 0;
-        // odd: register set 1, op_sel 2), the pair's scales in slot (kt / 2) & 1
-        for (int kt = 0; kt < rg.nk; kt += 2) {
-            fp8_mfma<TL, 0>(fa0, fb0, sa0, sb0, acc);
-            if (kt + 2 < rg.nk) wait_vm<TL::P + PS>();      // K-tile kt + 2 (with scales) may stay in flight
-            else wait_vm<0>();
-            ring_barrier();
-            if (kt + 3 < rg.nk) issue(kt + 3);
-            fp8_load<TL>(ring + ((kt + 1) & 3) * TL::STAGE_CHUNKS, sring + ((kt >> 1) & 1) * (BM + BN), a0, a1, b0,
-                         b1, arow_i, brow_i, sh, fa1, fb1, sa1, sb1);
-            interleave_hint<2 * (TM + TN), TM * TN>();
-            fp8_mfma<TL, 2>(fa1, fb1, sa1, sb1, acc);
-            if (kt + 2 < rg.nk) {
-                if (kt + 3 < rg.nk) wait_vm<TL::P>();        // K-tile kt + 3 may stay in flight
-                else wait_vm<0>();
-                ring_barrier();
-                if (kt + 4 < rg.nk) issue(kt + 4);
-                fp8_load<TL>(ring + ((kt + 2) & 3) * TL::STAGE_CHUNKS, sring + (((kt + 2) >> 1) & 1) * (BM + BN), a0,
-                             a1, b0, b1, arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
-                interleave_hint<2 * (TM + TN), TM * TN>();
-            }
-        }
 
-        const int rbase = wm * TL::WROWS + 4 * half;
-        if (EPI == 0) {
-            uint16_t* Cb = static_cast<uint16_t*>(C);
-#pragma unroll
-            for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < TN; ++ni) {
-                    const int col = n0 + wn * TL::WCOLS + ni * 32 + (rg.lane & 31);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = rbase + mi * 32 + 8 * (v >> 2) + (v & 3);
-                        if (r < rows && col < N)
-                            Cb[(size_t)(row0 + r) * ldc + col] = f32_to_bf16(acc[mi][ni][v]);
-                    }
-                }
-        } else {
-            // SwiGLU values of one gate/up column pair (32 h columns) of this
-            // wave's rows go through a per-wave LDS region of the ring; each lane
-            // then quantises whole 32-value blocks of a row and stores 32 codes
-            // with two 16-byte stores plus the block's scale byte.
-            ring_barrier();     // every wave is past its last fragment read
-            static_assert(TL::WROWS * 32 * 4 * TL::NW <= TL::STAGES * TL::STAGE_CHUNKS * 16, "staging region");
-            float* reg = reinterpret_cast<float*>(ring) + rg.wave * TL::WROWS * 32;
-            uint8_t* Cq = static_cast<uint8_t*>(C);
-#pragma unroll
-            for (int np = 0; np < TN / 2; ++np) {
-                const int pc = n0 + wn * TL::WCOLS + np * 64;
-                // [WROWS rows][32 columns], column c of row r at c ^ (r & 31)
-#pragma unroll
-                for (int mi = 0; mi < TM; ++mi)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                        reg[r * 32 + ((rg.lane & 31) ^ (r & 31))] =
-                            silu_mul_p(acc[mi][2 * np][v], acc[mi][2 * np + 1][v]);
-                    }
-                if (pc < N) {
-                    const int hb = pc / 64;              // 32-wide h block of this pair
-                    for (int r = rg.lane; r < TL::WROWS; r += 64) {
-                        const int grow = wm * TL::WROWS + r;
-                        float x[32];
-                        float amax = 0.f;
-#pragma unroll
-                        for (int c = 0; c < 32; ++c) {
-                            x[c] = reg[r * 32 + (c ^ (r & 31))];
-                            amax = fmaxf(amax, fabsf(x[c]));
-                        }
-                        const int se = mx_shared_exp(amax);
-                        const float inv = mx_inv_scale(se);
-                        uint32_t w[8];
-#pragma unroll
-                        for (int q = 0; q < 8; ++q)
-                            w[q] = e4m3_encode(x[4 * q] * inv) | (e4m3_encode(x[4 * q + 1] * inv) << 8) |
-                                   (e4m3_encode(x[4 * q + 2] * inv) << 16) | (e4m3_encode(x[4 * q + 3] * inv) << 24);
-                        if (grow < rows) {
-                            u32x4* dst = reinterpret_cast<u32x4*>(Cq + (size_t)(row0 + grow) * ldc + hb * 32);
-                            dst[0] = (u32x4){w[0], w[1], w[2], w[3]};
-                            dst[1] = (u32x4){w[4], w[5], w[6], w[7]};
-                            Cs[(size_t)(row0 + grow) * (ldc / 32) + hb] = (uint8_t)(se + 127);
-                        }
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();   // the region is rewritten for the next pair
-            }
+        // K-tiles go in pairs (kt even: register set 0, op_sel 0; kt + 1: set 1,
+        // op_sel 2), the pair's scales in slot (kt / 2) & 1.  Each half starts a
+        // few MFMAs on the fragments in hand, waits for the next K-tile, joins
+        // the barrier, refills the stage everyone is done with, and reads the
+        // next fragments between the remaining MFMAs.
+        for (int kt = 0; kt < nk - 2; kt += 2) {
+            fp8_mfma<TL, 0, 0, EARLY>(fa0, fb0, sa0, sb0, acc);
+            wait_vm<P + PS>();   // K-tile kt + 1 landed; kt + 2 (with scales) may stay in flight
+            ring_barrier();
+            issue(kt + 3);
+            fp8_load<TL>(ring + ((kt + 1) & 3) * SC, sring + ((kt >> 1) & 1) * (BM + BN), a0, a1, b0, b1, arow_i,
+                         brow_i, sh, fa1, fb1, sa1, sb1);
+            fp8_mfma<TL, 0, EARLY, NM - EARLY>(fa0, fb0, sa0, sb0, acc);
+            interleave_hint<NR, NM - EARLY>();
+            __builtin_amdgcn_sched_barrier(0);
+
+            fp8_mfma<TL, 2, 0, EARLY>(fa1, fb1, sa1, sb1, acc);
+            wait_vm<P>();        // K-tile kt + 2 landed; kt + 3 may stay in flight
+            ring_barrier();
+            issue(kt + 4);
+            fp8_load<TL>(ring + ((kt + 2) & 3) * SC, sring + (((kt + 2) >> 1) & 1) * (BM + BN), a0, a1, b0, b1,
+                         arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
+            fp8_mfma<TL, 2, EARLY, NM - EARLY>(fa1, fb1, sa1, sb1, acc);
+            interleave_hint<NR, NM - EARLY>();
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // last pair: K-tile nk - 2 in set 0, nk - 1 still to read
+        fp8_mfma<TL, 0, 0, EARLY>(fa0, fb0, sa0, sb0, acc);
+        wait_vm<0>();
+        ring_barrier();
+        fp8_load<TL>(ring + ((nk - 1) & 3) * SC, sring + (((nk - 2) >> 1) & 1) * (BM + BN), a0, a1, b0, b1, arow_i,
+                     brow_i, sh, fa1, fb1, sa1, sb1);
+        fp8_mfma<TL, 0, EARLY, NM - EARLY>(fa0, fb0, sa0, sb0, acc);
+        interleave_hint<NR, NM - EARLY>();
+        __builtin_amdgcn_sched_barrier(0);
+        fp8_mfma<TL, 2, 0, NM>(fa1, fb1, sa1, sb1, acc);
+
+        // next tile's first K-tiles go out before this tile's epilogue
+        const TileCoord cur = c;
+        const int next = tile + G;
+        ring_barrier();   // every wave is past its last fragment and scale read
+        if (next < total) {
+            setup(next);
+            issue(0);
+            issue(1);
+            issue(2);
+        }
+        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, cur, wm, wn);
+        if (next >= total) break;
+        tile = next;
     }
 }
 
