@@ -21,6 +21,9 @@ metadata stays on the device, dispatch and combine avoid a permutation):
 5. expert FFN      ye = (silu(xe W_gate) * (xe W_up)) W_down, per expert
 6. combine         y[t] = sum_j gate[t, j] * ye[pos[t, j]]
 
+and, beside step 3, the router statistics (mean router probability per expert,
+the Switch-style load-balancing scalar and the worst-case load imbalance).
+
 The pages give no formula for the router, the gate or the expert FFN; the
 readings taken (softmax-then-renormalise gates, SwiGLU experts, lowest-index
 tie-break, stored precision of each intermediate) are the workload definitions
@@ -130,6 +133,33 @@ def route_metadata(idx, n_experts: int):
     row_token = (order // k).astype(np.int32)
     return (counts.astype(np.int32), offsets.astype(np.int32),
             pos.reshape(T, k).astype(np.int32), row_token)
+
+
+def router_stats(logits, counts, k: int) -> dict:
+    """Router statistics of one block, in float64.
+
+    The report asks that requested route counts be inspected directly next to
+    the Switch-style load-balancing scalar, a cross term of soft router scores
+    and hard expert counts that can fall while the imbalance of the requested
+    routes grows ("Supercharging Olmo-core ...", "Section 24: Conclusion", 24.3
+    and Evidence 9 / Figure 45).  The pages print no formula for the scalar;
+    the Switch-Transformer form is taken:
+
+        P_e   = mean over tokens of softmax(L[t])[e]      (all E experts)
+        f_e   = counts[e] / (T k)                          (share of routed rows)
+        lbl   = E * sum_e f_e P_e                          (1 when both are uniform)
+        imbalance = max_e counts[e] / (T k / E)            (worst-case load / mean load)
+
+    Returns P [E], lbl, imbalance (float64).
+    """
+    L = np.asarray(logits, dtype=np.float64)
+    T, E = L.shape
+    z = np.exp(L - L.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0)
+    c = np.asarray(counts, dtype=np.float64)
+    f = c / (T * k)
+    return {"P": P, "lbl": float(E * np.sum(f * P)), "imbalance": float(c.max() / (T * k / E))}
 
 
 # ----------------------------------------------------------------------------- step 4

@@ -97,6 +97,30 @@ def _decode_fnuz(codes):
     return s * np.where((c & 0x7F) == 0x7F, np.nan, mag)
 
 
+def _stats_counts_over_tokens(logits, counts, k):
+    # f_e = counts / T instead of counts / (T k): the scalar scales with k
+    r = _orig_stats(logits, counts, k)
+    T = np.asarray(logits).shape[0]
+    E = np.asarray(logits).shape[1]
+    r["lbl"] = float(E * np.sum(np.asarray(counts, np.float64) / T * r["P"]))
+    return r
+
+
+def _stats_topk_probabilities(logits, counts, k):
+    # P from the renormalised top-k gates instead of the full softmax
+    idx = O.select_topk(logits, k)
+    g = O.gates(logits, idx)
+    L = np.asarray(logits, np.float64)
+    T, E = L.shape
+    dense = np.zeros((T, E))
+    np.put_along_axis(dense, np.asarray(idx, np.int64), g, axis=1)
+    P = dense.mean(0)
+    c = np.asarray(counts, np.float64)
+    return {"P": P, "lbl": float(E * np.sum(c / (T * k) * P)), "imbalance": float(c.max() / (T * k / E))}
+
+
+_orig_stats = O.router_stats
+
 ROUTING_PINS = [
     lambda gd: P.test_route_worked_example(gd),
     lambda gd: [P.test_topk_brute_force_with_ties(E, k) for E, k in [(3, 2), (4, 3), (5, 2)]],
@@ -108,6 +132,11 @@ EXPERT_PINS = [
     lambda gd: [P.test_single_expert_top1_is_dense_swiglu(a) for a in ("f32", "bf16")],
     lambda gd: P.test_identity_experts_round_trip(),
     lambda gd: [P.test_expert_relabelling_invariance(a) for a in ("f32", "bf16")],
+]
+STATS_PINS = [
+    lambda gd: P.test_router_stats_hand_examples(),
+    lambda gd: P.test_router_stats_uniform_and_invariants(),
+    lambda gd: P.test_router_stats_scalar_can_fall_while_imbalance_stays(),
 ]
 MX_PINS = [
     lambda gd: P.test_e4m3_golden_values(gd),
@@ -124,6 +153,8 @@ MUTATIONS = [
     ("gate and up projections swapped", O, "expert_ffn", _ffn_swapped, EXPERT_PINS),
     ("SiLU dropped", O, "expert_ffn", _ffn_no_silu, EXPERT_PINS),
     ("combine ignores gates", O, "combine", _combine_ungated, EXPERT_PINS),
+    ("load share over tokens, not routed rows", O, "router_stats", _stats_counts_over_tokens, STATS_PINS),
+    ("router probability from the top-k gates", O, "router_stats", _stats_topk_probabilities, STATS_PINS),
     ("E4M3 ties rounded away from zero", MX, "e4m3_round", _round_away, MX_PINS),
     ("ceil-based shared exponent", MX, "shared_exponent", _shared_exp_ceil, MX_PINS),
     ("FNUZ decode instead of OCP FN", MX, "e4m3_decode", _decode_fnuz, MX_PINS),

@@ -418,3 +418,60 @@ def test_learned_router_logits_are_a_matmul():
     want = (torch.from_numpy(x) @ torch.from_numpy(wr)).numpy()
     assert np.max(np.abs(L - want)) <= 1e-6 * np.max(np.abs(want))
     assert np.array_equal(L, L.astype(np.float32).astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- router statistics
+
+
+def test_router_stats_hand_examples():
+    """Two tokens, two experts, top-1, logits chosen so the softmax is in quarters."""
+    l3 = math.log(3.0)
+    # token 0 prefers expert 1 (3/4), token 1 prefers expert 0 (3/4): balanced
+    s = O.router_stats(np.array([[0.0, l3], [l3, 0.0]]), np.array([1, 1]), k=1)
+    assert np.allclose(s["P"], [0.5, 0.5], rtol=0, atol=1e-15)
+    assert abs(s["lbl"] - 1.0) < 1e-15 and s["imbalance"] == 1.0
+    # both tokens prefer expert 0 with probability 3/4: f = (1, 0), P = (3/4, 1/4)
+    s = O.router_stats(np.array([[l3, 0.0], [l3, 0.0]]), np.array([2, 0]), k=1)
+    assert np.allclose(s["P"], [0.75, 0.25], rtol=0, atol=1e-15)
+    assert abs(s["lbl"] - 1.5) < 1e-15 and s["imbalance"] == 2.0
+
+
+def test_router_stats_uniform_and_invariants():
+    rng = np.random.default_rng(5)
+    T, E, k = 64, 8, 2
+    # equal logits: P uniform; perfectly balanced counts give lbl = imbalance = 1
+    s = O.router_stats(np.zeros((T, E)), np.full(E, T * k // E), k)
+    assert np.allclose(s["P"], 1.0 / E, rtol=0, atol=1e-15)
+    assert abs(s["lbl"] - 1.0) < 1e-14 and s["imbalance"] == 1.0
+    # P is a probability vector; lbl is at most E * max(P) and at least E * min(P)
+    L = rng.normal(size=(T, E)) * 3.0
+    idx, _ = O.route(L, k)
+    counts, _, _, _ = O.route_metadata(idx, E)
+    s = O.router_stats(L, counts, k)
+    assert abs(s["P"].sum() - 1.0) < 1e-12 and (s["P"] > 0).all()
+    assert E * s["P"].min() - 1e-12 <= s["lbl"] <= E * s["P"].max() + 1e-12
+    assert s["imbalance"] == counts.max() / (T * k / E)
+    # shifting every logit of a token by a constant changes nothing
+    s2 = O.router_stats(L + rng.normal(size=(T, 1)) * 10.0, counts, k)
+    assert np.allclose(s2["P"], s["P"], rtol=1e-12, atol=0) and abs(s2["lbl"] - s["lbl"]) < 1e-12
+
+
+def test_router_stats_scalar_can_fall_while_imbalance_stays():
+    """The cross-term property the report warns about: with the hard counts
+    fixed (same top-1 choices), moving soft score mass between experts changes
+    the scalar while the worst-case imbalance is unchanged."""
+    T, E = 8, 4
+    # every token routes to expert 0 (imbalance E), but with varying confidence
+    sharp = np.zeros((T, E))
+    sharp[:, 0] = 4.0
+    soft = np.zeros((T, E))
+    soft[:, 0] = 0.5
+    counts = np.array([T, 0, 0, 0])
+    for L in (sharp, soft):
+        assert (O.select_topk(L, 1)[:, 0] == 0).all()
+    a, b = O.router_stats(sharp, counts, 1), O.router_stats(soft, counts, 1)
+    assert a["imbalance"] == b["imbalance"] == E
+    assert b["lbl"] < a["lbl"]
+    # with all rows on expert 0, lbl = E * P_0 exactly
+    p0 = math.exp(0.5) / (math.exp(0.5) + 3.0)
+    assert abs(b["lbl"] - E * p0) < 1e-14
