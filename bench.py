@@ -10,6 +10,12 @@ from HIP events the library records on the forward's own stream during the
 same timed steps; the dominant kernel is reported against its roofline.
 The CPU baseline times the float64 oracle on a bounded sample of the same
 batch on the host cores.
+
+Beside the main figure the line carries three comparison measurements, each
+outside the K timed steps: per-step times with the caches flushed before
+every step (cold_cache), the same block through the host-synchronising path
+(host_sync_variant: counts copied to the host and waited for before the
+grouped GEMMs), and the block with router statistics enabled.
 """
 from __future__ import annotations
 
@@ -130,11 +136,78 @@ def cpu_baseline(w: W.Workload, host: dict, budget_s: float = 12.0) -> dict:
                       f"{w.name} batch, {reps} run(s), {total:.1f} s"}
 
 
+def cold_cache_steps(step, dev, steps: int) -> dict:
+    """Per-step times with the L2s and the 256 MB Infinity Cache flushed first:
+    a 512 MiB buffer is rewritten before every step, outside the step's events."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    times = []
+    for i in range(steps):
+        flush.fill_(i & 0xFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    t = sorted(times)
+    q = lambda f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]
+    return {"ms_per_step_median": round(q(0.5), 5), "p10": round(q(0.1), 5), "p90": round(q(0.9), 5),
+            "flush": "512 MiB device write before each step"}
+
+
+def host_sync_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device: float) -> dict:
+    """The same block through moe_forward_host_sync (counts copied to the host and
+    waited for before the grouped GEMMs), timed like the main loop."""
+    f = B.Forward(p, dev, debug_outputs=False, host_sync=True)
+    if p.flags & B.MOE_LOGITS_GIVEN:
+        f.logits.copy_(d_in["logits"])
+    run = lambda: f(d_in["x"], packed=packed, w_router=d_in["w_router"], logits=f.logits)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    B.set_profiling(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    stages = dict(B.kernel_times())
+    B.set_profiling(False)
+    ms = start.elapsed_time(stop) / steps
+    return {"ms_per_step": round(ms, 5), "host_count_wait_ms": round(stages.get("host_count_wait", 0.0), 5),
+            "slowdown_vs_device_resident": round(ms / ms_device, 4)}
+
+
+def router_stats_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device: float) -> dict:
+    """The block with the router statistics computed in the routing pass, and their values."""
+    f = B.Forward(p, dev, debug_outputs=False, stats=True)
+    if p.flags & B.MOE_LOGITS_GIVEN:
+        f.logits.copy_(d_in["logits"])
+    run = lambda: f(d_in["x"], packed=packed, w_router=d_in["w_router"], logits=f.logits)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    st = f.router_stats.cpu().numpy()
+    E = p.n_experts
+    return {"ms_per_step": round(ms, 5), "overhead_ms": round(ms - ms_device, 5),
+            "balance_scalar": float(st[E]), "worst_case_imbalance": float(st[E + 1]),
+            "mean_router_prob_min_max": [float(st[:E].min()), float(st[:E].max())]}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(W.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -226,6 +299,9 @@ def main(argv=None):
         "stages": stage_out,
         "host_wall_s": round(wall, 4),
     }
+    result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
+    result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
+    result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(result))

@@ -19,7 +19,8 @@
  *  - Pointers named as device pointers must point to device memory of the
  *    current HIP device; the caller owns every buffer.  The library never
  *    allocates device memory, never frees, never copies to the host and never
- *    synchronises inside these calls (except moe_kernel_times, see there).
+ *    synchronises inside these calls (except moe_kernel_times and the
+ *    comparison path moe_forward_host_sync, see there).
  *    All work is enqueued on `stream` (a hipStream_t; NULL = default stream),
  *    so calls on one stream are ordered and the whole sequence is capturable
  *    in a HIP graph.
@@ -68,7 +69,7 @@ extern "C" {
 #define MOE_ERR_DTYPE     -3   /* unknown act_dtype, or flag not valid for it      */
 #define MOE_ERR_WORKSPACE -4   /* ws_bytes smaller than moe_workspace_bytes()      */
 #define MOE_ERR_LAUNCH    -5   /* a kernel launch or HIP runtime call failed       */
-#define MOE_ERR_STATE     -6   /* moe_kernel_times without a profiled forward      */
+#define MOE_ERR_STATE     -6   /* no profiled forward yet; inconsistent host counts */
 
 #define MOE_F32   0
 #define MOE_BF16  1
@@ -128,10 +129,21 @@ int32_t moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w
  *   pos      : device int32 [T, k] out, row of (token, slot) in the expert-major
  *              buffer: offsets[e] + number of earlier tokens routed to e
  *   row_token: device int32 [R] out, row_token[pos[t][j]] = t
+ *   router_stats : device float32 [E + 2] out, or NULL to skip.  The report
+ *              asks that the requested route counts be inspected next to the
+ *              Switch-style balance scalar, which mixes soft router scores with
+ *              hard counts ("Section 24: Conclusion", 24.3 and Evidence 9 /
+ *              Figure 45); its formula is not printed, the Switch form is used:
+ *                [e]     P_e = mean over tokens of softmax(logits[t])[e]
+ *                [E]     E * sum_e (counts[e] / (T k)) * P_e
+ *                [E + 1] max_e counts[e] / (T k / E)   (worst-case load / mean)
+ *              Computed in the top-k pass; sums run in a fixed order, so the
+ *              values are reproducible bit for bit.
  *   ws       : device workspace of ws_bytes bytes */
 int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, float* logits,
                   int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
-                  int32_t* pos, int32_t* row_token, void* ws, size_t ws_bytes, void* stream);
+                  int32_t* pos, int32_t* row_token, float* router_stats, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* Rowwise dispatch (report Abstract: each token row written directly into its
  * expert's buffer): xe[pos[t][j]] = x[t] for every slot.
@@ -165,13 +177,32 @@ int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate
 
 /* The whole block on one stream: route, dispatch, grouped SwiGLU, combine, with
  * no host synchronisation between them.  Arguments as above; topk_idx,
- * topk_gate, counts, offsets and pos are optional outputs (NULL: kept in the
- * workspace only).  With MOE_IDENTITY_EXPERTS the grouped GEMM is skipped and
- * ye := xe (MOE_F32 / MOE_BF16 only), so y[t] = x[t] * sum_j gate[t][j]. */
+ * topk_gate, counts, offsets, pos and router_stats are optional outputs (NULL:
+ * kept in the workspace only, or for router_stats not computed).  With
+ * MOE_IDENTITY_EXPERTS the grouped GEMM is skipped and ye := xe (MOE_F32 /
+ * MOE_BF16 only), so y[t] = x[t] * sum_j gate[t][j]. */
 int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, float* logits,
                     const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
-                    int32_t* counts, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
-                    void* stream);
+                    int32_t* counts, int32_t* offsets, int32_t* pos, float* router_stats, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* The same block with one host wait, for comparison with moe_forward: the
+ * original MoE path the report measures against needed the per-expert routing
+ * counts on the CPU before the grouped-GEMM group sizes were known ("Section
+ * 24: Conclusion", 24.1 and Evidence 3 / Figure 74: one device-to-host copy
+ * and host wait per routed block).  After routing, the counts are copied to
+ * host_counts (host memory of E int32, owned by the caller; pinned memory
+ * avoids a staging copy) and the calling thread waits for the stream before it
+ * sizes the grouped-GEMM grids from them and enqueues the rest.  Every output
+ * is bit-identical to moe_forward's (same kernels; only the grid size and the
+ * wait differ).  Not capturable in a HIP graph.  With profiling on (below) the
+ * stage "host_count_wait" is the GPU time from the end of routing until work
+ * resumes after the wait.  Errors: as moe_forward, MOE_ERR_NULL for a NULL
+ * host_counts, MOE_ERR_STATE if the copied counts do not sum to T*k. */
+int32_t moe_forward_host_sync(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                              const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
+                              int32_t* counts, int32_t* offsets, int32_t* pos, float* router_stats, void* ws,
+                              size_t ws_bytes, void* stream, int32_t* host_counts);
 
 /* Per-kernel timing of moe_forward with HIP events recorded on its stream.
  * moe_set_profiling(1) makes later moe_forward calls record an event before

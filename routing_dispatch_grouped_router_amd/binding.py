@@ -24,7 +24,7 @@ MOE_LOGITS_GIVEN, MOE_IDENTITY_EXPERTS = 1, 2
 # every function the header declares, for the export check
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packed_weight_bytes",
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
-           "moe_forward", "moe_set_profiling", "moe_kernel_times"]
+           "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times"]
 
 
 class MoeError(RuntimeError):
@@ -70,11 +70,12 @@ def lib():
         L.moe_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_packed_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_pack_weights.argtypes = [PP, _P, _P, _P, _P, _P]
-        L.moe_route.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_route.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.moe_dispatch.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_grouped_swiglu.argtypes = [PP, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.moe_combine.argtypes = [PP, _P, _P, _P, _P, _P]
-        L.moe_forward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_forward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_forward_host_sync.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
         L.moe_set_profiling.argtypes = [_I32]
         L.moe_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                        _I32, ctypes.POINTER(_I32)]
@@ -158,8 +159,10 @@ def pack_weights(p: Problem, w_gate, w_up, w_down, stream=None) -> torch.Tensor:
     return packed
 
 
-def route(p: Problem, x=None, w_router=None, logits=None, ws=None, stream=None) -> dict:
-    """Returns dict(logits, idx, gate, counts, offsets, pos, row_token) as device tensors."""
+def route(p: Problem, x=None, w_router=None, logits=None, ws=None, stream=None, stats=False) -> dict:
+    """Returns dict(logits, idx, gate, counts, offsets, pos, row_token) as device tensors,
+    plus router_stats [E + 2] (mean router probability per expert, balance scalar,
+    worst-case imbalance) when stats=True."""
     T, E, k, d = p.T, p.n_experts, p.top_k, p.d_model
     dev = (logits if logits is not None else x).device
     if p.flags & MOE_LOGITS_GIVEN:
@@ -174,12 +177,13 @@ def route(p: Problem, x=None, w_router=None, logits=None, ws=None, stream=None) 
                counts=torch.empty((E,), dtype=torch.int32, device=dev),
                offsets=torch.empty((E + 1,), dtype=torch.int32, device=dev),
                pos=torch.empty((T, k), dtype=torch.int32, device=dev),
-               row_token=torch.empty((T * k,), dtype=torch.int32, device=dev))
+               row_token=torch.empty((T * k,), dtype=torch.int32, device=dev),
+               router_stats=torch.empty((E + 2,), dtype=torch.float32, device=dev) if stats else None)
     ws = new_workspace(p, dev) if ws is None else ws
     _check("moe_route", lib().moe_route(
         ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(out["idx"]), _ptr(out["gate"]),
         _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["pos"]), _ptr(out["row_token"]),
-        _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(out["router_stats"]), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 
@@ -225,13 +229,21 @@ def combine(p: Problem, ye, gate, pos, stream=None):
 class Forward:
     """Preallocated state for repeated moe_forward calls (fixed buffer addresses)."""
 
-    def __init__(self, p: Problem, device, debug_outputs: bool = True):
+    def __init__(self, p: Problem, device, debug_outputs: bool = True, host_sync: bool = False,
+                 stats: bool = False):
+        """host_sync: call moe_forward_host_sync (counts copied to a pinned host
+        buffer and waited for before the grouped GEMMs) instead of moe_forward.
+        stats: also compute the router statistics into self.router_stats [E + 2]."""
         self.p = p
+        self.host_sync = host_sync
+        self.host_counts = (torch.empty((p.n_experts,), dtype=torch.int32, pin_memory=True)
+                            if host_sync else None)
         T, E, k, d = p.T, p.n_experts, p.top_k, p.d_model
         self.ws = new_workspace(p, device)
         self.y = torch.empty((T, d), dtype=out_dtype(p.act), device=device)
         self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
         self.debug = debug_outputs
+        self.router_stats = (torch.empty((E + 2,), dtype=torch.float32, device=device) if stats else None)
         if debug_outputs:
             self.idx = torch.empty((T, k), dtype=torch.int32, device=device)
             self.gate = torch.empty((T, k), dtype=torch.float32, device=device)
@@ -250,18 +262,23 @@ class Forward:
                 self.logits.copy_(logits)
         else:
             _expect(w_router, (p.d_model, p.n_experts), storage_dtype(p.act), "w_router")
-        _check("moe_forward", lib().moe_forward(
-            ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(self.logits), _ptr(packed), _ptr(self.y),
-            _ptr(self.idx), _ptr(self.gate), _ptr(self.counts), _ptr(self.offsets), _ptr(self.pos),
-            _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        args = (ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(self.logits), _ptr(packed), _ptr(self.y),
+                _ptr(self.idx), _ptr(self.gate), _ptr(self.counts), _ptr(self.offsets), _ptr(self.pos),
+                _ptr(self.router_stats), _ptr(self.ws), self.ws.numel(), _stream(stream))
+        if self.host_sync:
+            _check("moe_forward_host_sync", lib().moe_forward_host_sync(
+                *args, ctypes.c_void_p(self.host_counts.data_ptr())))
+        else:
+            _check("moe_forward", lib().moe_forward(*args))
         return self.y
 
 
-def forward(p: Problem, x, packed=None, w_router=None, logits=None, stream=None) -> dict:
-    f = Forward(p, x.device)
+def forward(p: Problem, x, packed=None, w_router=None, logits=None, stream=None, host_sync=False,
+            stats=False) -> dict:
+    f = Forward(p, x.device, host_sync=host_sync, stats=stats)
     y = f(x, packed=packed, w_router=w_router, logits=logits, stream=stream)
     return dict(y=y, logits=f.logits, idx=f.idx, gate=f.gate, counts=f.counts, offsets=f.offsets,
-                pos=f.pos)
+                pos=f.pos, host_counts=f.host_counts, router_stats=f.router_stats)
 
 
 def set_profiling(enable: bool):
@@ -270,10 +287,10 @@ def set_profiling(enable: bool):
 
 def kernel_times() -> list[tuple[str, float]]:
     """(stage name, milliseconds) of the last profiled moe_forward (synchronises on it)."""
-    names = (ctypes.c_char_p * 8)()
-    ms = (ctypes.c_float * 8)()
+    names = (ctypes.c_char_p * 16)()
+    ms = (ctypes.c_float * 16)()
     n = _I32()
-    _check("moe_kernel_times", lib().moe_kernel_times(names, ms, 8, ctypes.byref(n)))
+    _check("moe_kernel_times", lib().moe_kernel_times(names, ms, 16, ctypes.byref(n)))
     return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 

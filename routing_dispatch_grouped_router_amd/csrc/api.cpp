@@ -1,7 +1,8 @@
 // C ABI of the routed MoE block (declarations and contracts in include/moe.h).
 // Host-side only: validates arguments, carves the caller's workspace and
 // enqueues the gfx950 kernels on the caller's stream.  Nothing here allocates
-// device memory, copies to the host or synchronises, except moe_kernel_times.
+// device memory, copies to the host or synchronises, except moe_kernel_times
+// and the host-synchronising comparison path moe_forward_host_sync.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -18,7 +19,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t hist, base, h, h_scale, route_end, gemm_end;
+    size_t hist, base, psum, h, h_scale, route_end, gemm_end;
     size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, ye, total;
 };
 
@@ -33,6 +34,7 @@ Layout layout(const moe_problem& p) {
     const bool mx = p.act_dtype == MOE_MXFP8;
     L.hist = take(nblk * E * 4);
     L.base = take(nblk * E * 4);
+    L.psum = take(nblk * E * 4);
     L.route_end = off;
     L.h = take(R * H * act_bytes(p.act_dtype));
     L.h_scale = take(mx ? R * H / 32 : 0);
@@ -95,7 +97,7 @@ char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
 // after each kernel.  Up to kMaxCalls consecutive calls keep their own event
 // sets, so the per-stage durations of a whole timed loop can be averaged
 // without synchronising inside it.
-constexpr int kMaxStages = 8;
+constexpr int kMaxStages = 10;
 constexpr int kMaxCalls = 128;
 struct Profiler {
     bool enabled = false;
@@ -188,7 +190,8 @@ int32_t moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w
 
 int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, float* logits,
                   int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
-                  int32_t* pos, int32_t* row_token, void* ws, size_t ws_bytes, void* stream) {
+                  int32_t* pos, int32_t* row_token, float* router_stats, void* ws, size_t ws_bytes,
+                  void* stream) {
     int32_t st = check_problem(p);
     if (st) return st;
     const bool given = p->flags & MOE_LOGITS_GIVEN;
@@ -200,11 +203,14 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, flo
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
     int32_t* base = reinterpret_cast<int32_t*>(at(ws, L.base));
+    float* psum = router_stats ? reinterpret_cast<float*>(at(ws, L.psum)) : nullptr;
     const int T = p->T, E = p->n_experts, k = p->top_k, d = p->d_model;
     if (!given && (st = launched(launch_router_logits(p->act_dtype, x, w_router, logits, T, d, E, s))))
         return st;
-    if ((st = launched(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, pos, hist, s)))) return st;
-    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, counts, offsets, s)))) return st;
+    if ((st = launched(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, pos, hist, psum, s)))) return st;
+    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, counts, offsets, psum, router_stats, T,
+                                         k, s))))
+        return st;
     return launched(launch_route_finalize(topk_idx, base, T, E, k, pos, row_token, s));
 }
 
@@ -236,10 +242,10 @@ int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* 
     void* h = at(ws, L.h);
     uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
     if ((st = launched(launch_gemm1(p->act_dtype, xe, xe_scale, static_cast<const char*>(pw) + P.w1, s1,
-                                    offsets, h, hs, R, E, d, H, s))))
+                                    offsets, h, hs, R, E, d, H, nullptr, s))))
         return st;
     return launched(launch_gemm2(p->act_dtype, h, hs, static_cast<const char*>(pw) + P.w2, s2, offsets,
-                                 ye, R, E, d, H, s));
+                                 ye, R, E, d, H, nullptr, s));
 }
 
 int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate, const int32_t* pos,
@@ -251,10 +257,19 @@ int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate
                                    static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, float* logits,
-                    const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
-                    int32_t* counts, int32_t* offsets, int32_t* pos, void* ws, size_t ws_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The block on one stream.  With host_counts == NULL nothing waits for the
+// host.  Otherwise the per-expert counts are copied to host_counts right after
+// routing and the host waits for them before sizing and launching the grouped
+// GEMMs, as the original MoE path did (routing counts on the CPU before the
+// group sizes are known); everything the kernels compute is the same.
+int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                     const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
+                     int32_t* counts, int32_t* offsets, int32_t* pos, float* router_stats, void* ws,
+                     size_t ws_bytes, void* stream, int32_t* host_counts) {
     int32_t st = check_problem(p);
     if (st) return st;
     const bool given = p->flags & MOE_LOGITS_GIVEN;
@@ -274,6 +289,7 @@ int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, f
     int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, L.row_token));
     int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
     int32_t* base = reinterpret_cast<int32_t*>(at(ws, L.base));
+    float* psum = router_stats ? reinterpret_cast<float*>(at(ws, L.psum)) : nullptr;
     void* xe = at(ws, L.xe);
     uint8_t* xs = reinterpret_cast<uint8_t*>(at(ws, L.xe_scale));
     void* ye = identity ? xe : at(ws, L.ye);
@@ -283,10 +299,20 @@ int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, f
         if ((st = launched(launch_router_logits(act, x, w_router, logits, T, d, E, s)))) return st;
         if ((st = prof_mark("router_logits", s))) return st;
     }
-    if ((st = launched(launch_route_topk(logits, T, E, k, idx, gate, ps, hist, s)))) return st;
+    if ((st = launched(launch_route_topk(logits, T, E, k, idx, gate, ps, hist, psum, s)))) return st;
     if ((st = prof_mark("route_topk", s))) return st;
-    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, cnt, off, s)))) return st;
+    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, cnt, off, psum, router_stats, T, k, s))))
+        return st;
     if ((st = prof_mark("route_scan", s))) return st;
+    if (host_counts) {
+        if ((st = launched(hipMemcpyAsync(host_counts, cnt, (size_t)E * 4, hipMemcpyDeviceToHost, s)))) return st;
+        if ((st = launched(hipStreamSynchronize(s)))) return st;
+        long rows = 0;
+        for (int e = 0; e < E; ++e) rows += host_counts[e];
+        if (rows != (long)R) return MOE_ERR_STATE;
+        // GPU time from the end of routing until work resumes after the host wait
+        if ((st = prof_mark("host_count_wait", s))) return st;
+    }
     if ((st = launched(launch_dispatch(act, x, ps, idx, base, row_token, xe, xs, T, d, E, k, s))))
         return st;
     if ((st = prof_mark("dispatch", s))) return st;
@@ -296,11 +322,11 @@ int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, f
         void* h = at(ws, L.h);
         uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
         if ((st = launched(launch_gemm1(act, xe, xs, pw + P.w1, reinterpret_cast<const uint8_t*>(pw + P.s1),
-                                        off, h, hs, R, E, d, H, s))))
+                                        off, h, hs, R, E, d, H, host_counts, s))))
             return st;
         if ((st = prof_mark("gemm1_gate_up_swiglu", s))) return st;
         if ((st = launched(launch_gemm2(act, h, hs, pw + P.w2, reinterpret_cast<const uint8_t*>(pw + P.s2),
-                                        off, ye, R, E, d, H, s))))
+                                        off, ye, R, E, d, H, host_counts, s))))
             return st;
         if ((st = prof_mark("gemm2_down", s))) return st;
     }
@@ -308,6 +334,27 @@ int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, f
     if ((st = prof_mark("combine", s))) return st;
     prof_end();
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_forward(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                    const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
+                    int32_t* counts, int32_t* offsets, int32_t* pos, float* router_stats, void* ws,
+                    size_t ws_bytes, void* stream) {
+    return forward_impl(p, x, w_router, logits, packed_w, y, topk_idx, topk_gate, counts, offsets, pos,
+                        router_stats, ws, ws_bytes, stream, nullptr);
+}
+
+int32_t moe_forward_host_sync(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                              const void* packed_w, void* y, int32_t* topk_idx, float* topk_gate,
+                              int32_t* counts, int32_t* offsets, int32_t* pos, float* router_stats, void* ws,
+                              size_t ws_bytes, void* stream, int32_t* host_counts) {
+    if (!host_counts) return MOE_ERR_NULL;
+    return forward_impl(p, x, w_router, logits, packed_w, y, topk_idx, topk_gate, counts, offsets, pos,
+                        router_stats, ws, ws_bytes, stream, host_counts);
 }
 
 int32_t moe_set_profiling(int32_t enable) {

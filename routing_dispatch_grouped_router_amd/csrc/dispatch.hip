@@ -129,12 +129,8 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __rest
             amax = fmaxf(amax, __shfl_xor(amax, 2));
             const int se = mx_shared_exp(amax);
             const float inv = mx_inv_scale(se);
-            uint32_t lo = 0, hi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
-            const uint2 q = make_uint2(lo, hi);
+            const uint2 q = make_uint2(e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                                       e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
 #pragma unroll
             for (int j = 0; j < kMaxTopK; ++j) {
                 if (j < k) {

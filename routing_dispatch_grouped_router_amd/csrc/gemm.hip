@@ -106,9 +106,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ----------------------------------------------------------------------------- launchers
 
-static int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu) {
-    const long mt_bound = (long)R / BM + (long)min(E, R);
-    const long tiles = mt_bound * ((N + BN - 1) / BN);
+int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts) {
+    long mt = (long)R / BM + (long)min(E, R);
+    if (host_counts) {
+        mt = 0;
+        for (int e = 0; e < E; ++e) mt += (host_counts[e] + BM - 1) / BM;
+    }
+    const long tiles = mt * ((N + BN - 1) / BN);
     long g = min(tiles, (long)256 * per_cu);
     g = (g + kXcds - 1) / kXcds * kXcds;
     return (int)max(g, (long)kXcds);
@@ -116,36 +120,36 @@ static int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu) {
 
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
-                        int R, int E, int d, int H, hipStream_t s) {
+                        int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s) {
     const int N = 2 * H, K = d;
     if (act == kBF16) {
         return launch_bf16_pipe(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
-                                static_cast<uint16_t*>(h), offsets, R, E, N, K, H, s);
+                                static_cast<uint16_t*>(h), offsets, R, E, N, K, H, host_counts, s);
     } else if (act == kF32) {
-        dim3 grid(persistent_grid(R, E, N, f32g::BM, f32g::BN, 4)), block(f32g::NTHR);
+        dim3 grid(persistent_grid(R, E, N, f32g::BM, f32g::BN, 4, host_counts)), block(f32g::NTHR);
         hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, block, 0, s, static_cast<const float*>(xe),
                            static_cast<const float*>(w1), static_cast<float*>(h), offsets, E, N, K, H);
     } else {
         return launch_fp8_pipe(1, static_cast<const uint8_t*>(xe), xe_scale, static_cast<const uint8_t*>(w1), w1_scale,
-                               h, h_scale, offsets, R, E, N, K, H, s);
+                               h, h_scale, offsets, R, E, N, K, H, host_counts, s);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const void* w2,
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
-                        int d, int H, hipStream_t s) {
+                        int d, int H, const int32_t* host_counts, hipStream_t s) {
     const int N = d, K = H;
     if (act == kBF16) {
         return launch_bf16_pipe(0, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w2),
-                                static_cast<uint16_t*>(ye), offsets, R, E, N, K, d, s);
+                                static_cast<uint16_t*>(ye), offsets, R, E, N, K, d, host_counts, s);
     } else if (act == kF32) {
-        dim3 grid(persistent_grid(R, E, N, f32g::BM, f32g::BN, 4)), block(f32g::NTHR);
+        dim3 grid(persistent_grid(R, E, N, f32g::BM, f32g::BN, 4, host_counts)), block(f32g::NTHR);
         hipLaunchKernelGGL(gemm_f32_kernel<0>, grid, block, 0, s, static_cast<const float*>(h),
                            static_cast<const float*>(w2), static_cast<float*>(ye), offsets, E, N, K, d);
     } else {
         return launch_fp8_pipe(0, static_cast<const uint8_t*>(h), h_scale, static_cast<const uint8_t*>(w2), w2_scale,
-                               ye, nullptr, offsets, R, E, N, K, d, s);
+                               ye, nullptr, offsets, R, E, N, K, d, host_counts, s);
     }
     return hipGetLastError();
 }

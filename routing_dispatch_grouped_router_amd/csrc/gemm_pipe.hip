@@ -12,8 +12,8 @@
 // Data movement.  Every 16-byte chunk of a K slice goes from global memory
 // straight into LDS with global_load_lds_dwordx4 (lane l of a wave writes LDS
 // bytes [16 l, 16 l + 16) of a wave-uniform 1 KB block), so no registers are
-// spent on staging and three K slices are in flight while a fourth is
-// consumed.  The loads are issued from inline asm with an SGPR base and a
+// spent on staging; up to three K slices are in flight beyond the one being
+// read into registers.  The loads are issued from inline asm with an SGPR base and a
 // 32-bit lane offset: the compiler spends one VGPR per load and never makes
 // LDS reads wait for them; all waits on them are the explicit wait_vm below.
 // (The compiler's own vmcnt waits stay correct, only more conservative,
@@ -26,12 +26,16 @@
 // cycle from 64 banks).  One ring array with a runtime stage offset keeps the
 // fragment addresses to a few lane bases plus immediates.
 //
-// Schedule of one K-tile kt (two bf16 k-steps, or one fp8 k-step):
-// multiply the fragments already in registers; with those MFMAs queued, wait
-// for K-tile kt + 1, join the barrier (everyone is done with K-tile kt - 1),
-// start the DMA of K-tile kt + 3 into that stage, and read K-tile kt + 1's
-// fragments.  The barrier is a bare s_barrier: __syncthreads() would add a
-// release fence that waits for every DMA in flight.
+// Schedule of one K-tile kt (two bf16 k-steps, or one fp8 k-step): issue a
+// few MFMAs on fragments already in registers, wait for K-tile kt + 1, join
+// the barrier (every wave has all of K-tile kt in registers by then, so its
+// stage is free), start the DMA of K-tile kt + 4 into that stage, and read
+// K-tile kt + 1's fragments between the remaining MFMAs.  So a K-tile has
+// three K-tiles of compute to arrive.  The barrier is a bare s_barrier:
+// __syncthreads() would add a release fence that waits for every DMA in
+// flight.  Every issue starts the same number of loads (past the last K-tile
+// the loads are clamped and land in a stage nobody reads again), so the vmcnt
+// waits are constants and the loop body has no branches.
 #include "grouped_sched.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -47,11 +51,20 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// A wave-uniform pointer forced into SGPRs (the asm operands below need SGPRs
+// whatever the compiler's uniformity analysis concludes).
+__device__ __forceinline__ const void* sgpr_ptr(const void* p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // 16 bytes per lane from base + voff into LDS bytes [lds + 16 lane, +16).
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds), "v"(voff), "s"(base)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sgpr_ptr(base))
                  : "memory", "m0");
 }
 
@@ -59,8 +72,13 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                  :
-                 : "s"(lds), "v"(voff), "s"(base)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sgpr_ptr(base))
                  : "memory", "m0");
+}
+
+// s_waitcnt lgkmcnt(0): every LDS access this wave issued has completed.
+__device__ __forceinline__ void wait_lds() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -313,6 +331,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
     rg.issue(0);
     rg.issue(1);
     rg.issue(2);
+    rg.issue(3);
 
     for (;;) {
         f32x16 acc[TM][TN];
@@ -324,22 +343,24 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
         bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-        wait_vm<2 * P>();   // K-tile 0 landed; 1 and 2 may stay in flight
+        wait_vm<3 * P>();   // K-tile 0 landed; 1, 2 and 3 may stay in flight
         ring_barrier();
         bf_load<TL>(ring, a0, b0, fa0, fb0);
         // K-tile kt: k-step 0 in set 0 (read during the previous K-tile), k-step 1
         // read into set 1 while set 0 multiplies; then a few MFMAs of set 1, the
-        // wait for K-tile kt + 1 and the barrier, the DMA of kt + 3 into the stage
-        // everyone is done with, and set 0 of kt + 1 read between the remaining MFMAs.
+        // wait for K-tile kt + 1 and the barrier.  Both k-steps of kt are in
+        // registers by then, so its stage takes the DMA of kt + 4, and set 0 of
+        // kt + 1 is read between the remaining MFMAs.
         for (int kt = 0; kt < nk - 1; ++kt) {
             bf_load<TL>(ring + (kt & 3) * SC, a1, b1, fa1, fb1);
             bf_mfma<TL, 0, NM>(fa0, fb0, acc);
             interleave_hint<TM + TN, NM>();
             __builtin_amdgcn_sched_barrier(0);
             bf_mfma<TL, 0, EARLY>(fa1, fb1, acc);
-            wait_vm<P>();   // K-tile kt + 1 landed; kt + 2 may stay in flight
+            wait_vm<2 * P>();   // K-tile kt + 1 landed; kt + 2 and kt + 3 may stay in flight
+            wait_lds();         // this wave's reads of stage kt are complete
             ring_barrier();
-            rg.issue(kt + 3);
+            rg.issue(kt + 4);
             bf_load<TL>(ring + ((kt + 1) & 3) * SC, a0, b0, fa0, fb0);
             bf_mfma<TL, EARLY, NM - EARLY>(fa1, fb1, acc);
             interleave_hint<TM + TN, NM - EARLY>();
@@ -351,12 +372,13 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
         __builtin_amdgcn_sched_barrier(0);
         bf_mfma<TL, 0, NM>(fa1, fb1, acc);
 
-        // Start the next tile's first three K-tiles before this tile's epilogue:
+        // Start the next tile's first four K-tiles before this tile's epilogue:
         // once every wave is past its last fragment read (and the clamped loads
         // past the end have landed) the whole ring is free.
         const TileCoord cur = c;
         const int next = tile + G;
         wait_vm<0>();
+        wait_lds();
         ring_barrier();
         if (next < total) {
             c = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
@@ -364,6 +386,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
             rg.issue(0);
             rg.issue(1);
             rg.issue(2);
+            rg.issue(3);
         }
         bf_epilogue<TL, EPI>(acc, C, ldc, N, cur, wm, wn);
         if (next >= total) break;
@@ -382,7 +405,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 // gfx950).  So a lane's fragment is chunks h and 2 + h of the 64-byte slice,
 // and its scale is that of block 2 kt + h.  Scales come in pairs of
 // K-tiles: with every even K-tile t each wave DMAs, for its SR rows of A and
-// of B, the dword of scale bytes of K blocks 2t .. 2t+3 into a two-slot scale
+// of B, the dword of scale bytes of K blocks 2t .. 2t+3 into a four-slot scale
 // ring.  Lanes of the upper half shift that dword right by one byte, so one
 // op_sel (byte 0 for even K-tiles, byte 2 for odd ones) gives every lane the
 // scale of its own block.  Four waves each own a 128 x 128 block whose 256
@@ -429,9 +452,8 @@ __device__ __forceinline__ void fp8_mfma(const i32x8 (&fa)[TL::TM], const i32x8 
 // Epilogue of the MXFP8 kernel.  EPI 0: C = acc as bf16.  EPI 1: h = silu(gate)
 // * up per gate/up column pair, quantised to MXFP8 along h: each 32-column
 // block of one row is split over lanes l and l ^ 32, which agree on the block
-// maximum, take the shared exponent floor(log2 amax) - 8, and encode with the
-// hardware E4M3 conversion (round to nearest even) after clamping to +-448,
-// which is the saturating encode.
+// maximum, take the shared exponent floor(log2 amax) - 8, and encode with
+// e4m3x4 (saturating round-to-nearest-even E4M3).
 template <class TL, int EPI>
 __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], void* __restrict__ C,
                                              uint8_t* __restrict__ Cs, int ldc, int N, const TileCoord& c, int wm,
@@ -468,14 +490,8 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
                 const float inv = mx_inv_scale(se);
                 uint32_t w[4];   // run q: 4 codes of columns 8q + 4 half + 0..3
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float x[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(v[4 * q + i] * inv, -448.f), 448.f);
-                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pk, true);
-                    w[q] = (uint32_t)pk;
-                }
+                for (int q = 0; q < 4; ++q)
+                    w[q] = e4m3x4(v[4 * q] * inv, v[4 * q + 1] * inv, v[4 * q + 2] * inv, v[4 * q + 3] * inv);
                 gather_halves(w);
                 if (valid && pc < N) {
                     const int hb = pc / 64;   // 32-wide h block of this pair
@@ -498,7 +514,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
     constexpr int NM = TL::NM, EARLY = TL::EARLY, NR = 3 * (TM + TN), P = TL::P, SC = TL::STAGE_CHUNKS;
     __shared__ u32x4 ring[TL::STAGES * SC];
-    __shared__ uint32_t sring[2 * (BM + BN)];     // two scale slots: A rows then B rows
+    __shared__ uint32_t sring[4 * (BM + BN)];     // four scale slots: A rows then B rows
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
 
@@ -536,12 +552,12 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         soB = (uint32_t)min(c.n0 + srow, N - 1) * kb;
     };
     // DMA of K-tile kt, plus (kt even) the scale dwords of K-tiles kt, kt + 1
-    // into slot (kt / 2) & 1; clamped past the end like the data.
+    // into slot (kt / 2) % 4; clamped past the end like the data.
     auto issue = [&](int kt) {
         rg.issue(kt);
         if ((kt & 1) == 0) {
             const uint32_t so = (uint32_t)min(kt, nk - 2) * 2u;
-            const uint32_t slot = sring_lds + (uint32_t)((kt >> 1) & 1) * (BM + BN) * 4u;
+            const uint32_t slot = sring_lds + (uint32_t)((kt >> 1) & 3) * (BM + BN) * 4u;
             const uint32_t lsa = __builtin_amdgcn_readfirstlane(slot + rg.wave * SR * 4u);
             const uint32_t lsb = __builtin_amdgcn_readfirstlane(slot + BM * 4u + rg.wave * SR * 4u);
             if (SR == 64 || slane) {
@@ -555,6 +571,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     issue(0);
     issue(1);
     issue(2);
+    issue(3);
 
     for (;;) {
         f32x16 acc[TM][TN];
@@ -567,31 +584,34 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 
         i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
         int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
-        wait_vm<2 * P + PS>();   // K-tile 0 and its scales landed; 1 and 2 may stay in flight
+        wait_vm<3 * P + PS>();   // K-tile 0 and its scales landed; 1, 2 (with scales) and 3 may stay in flight
         ring_barrier();
         fp8_load<TL>(ring, sring, a0, a1, b0, b1, arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
 
         // K-tiles go in pairs (kt even: register set 0, op_sel 0; kt + 1: set 1,
-        // op_sel 2), the pair's scales in slot (kt / 2) & 1.  Each half starts a
+        // op_sel 2), the pair's scales in slot (kt / 2) % 4.  Each half starts a
         // few MFMAs on the fragments in hand, waits for the next K-tile, joins
-        // the barrier, refills the stage everyone is done with, and reads the
-        // next fragments between the remaining MFMAs.
+        // the barrier, refills the stage of the K-tile whose fragments are in
+        // registers (four K-tiles ahead), and reads the next fragments between
+        // the remaining MFMAs.
         for (int kt = 0; kt < nk - 2; kt += 2) {
             fp8_mfma<TL, 0, 0, EARLY>(fa0, fb0, sa0, sb0, acc);
-            wait_vm<P + PS>();   // K-tile kt + 1 landed; kt + 2 (with scales) may stay in flight
+            wait_vm<2 * P + PS>();   // K-tile kt + 1 landed; kt + 2 (with scales) and kt + 3 may stay in flight
+            wait_lds();
             ring_barrier();
-            issue(kt + 3);
-            fp8_load<TL>(ring + ((kt + 1) & 3) * SC, sring + ((kt >> 1) & 1) * (BM + BN), a0, a1, b0, b1, arow_i,
+            issue(kt + 4);
+            fp8_load<TL>(ring + ((kt + 1) & 3) * SC, sring + ((kt >> 1) & 3) * (BM + BN), a0, a1, b0, b1, arow_i,
                          brow_i, sh, fa1, fb1, sa1, sb1);
             fp8_mfma<TL, 0, EARLY, NM - EARLY>(fa0, fb0, sa0, sb0, acc);
             interleave_hint<NR, NM - EARLY>();
             __builtin_amdgcn_sched_barrier(0);
 
             fp8_mfma<TL, 2, 0, EARLY>(fa1, fb1, sa1, sb1, acc);
-            wait_vm<P>();        // K-tile kt + 2 landed; kt + 3 may stay in flight
+            wait_vm<2 * P + PS>();   // K-tile kt + 2 landed; kt + 3 and kt + 4 (with scales) may stay in flight
+            wait_lds();
             ring_barrier();
-            issue(kt + 4);
-            fp8_load<TL>(ring + ((kt + 2) & 3) * SC, sring + (((kt + 2) >> 1) & 1) * (BM + BN), a0, a1, b0, b1,
+            issue(kt + 5);
+            fp8_load<TL>(ring + ((kt + 2) & 3) * SC, sring + (((kt + 2) >> 1) & 3) * (BM + BN), a0, a1, b0, b1,
                          arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
             fp8_mfma<TL, 2, EARLY, NM - EARLY>(fa1, fb1, sa1, sb1, acc);
             interleave_hint<NR, NM - EARLY>();
@@ -601,7 +621,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         fp8_mfma<TL, 0, 0, EARLY>(fa0, fb0, sa0, sb0, acc);
         wait_vm<0>();
         ring_barrier();
-        fp8_load<TL>(ring + ((nk - 1) & 3) * SC, sring + (((nk - 2) >> 1) & 1) * (BM + BN), a0, a1, b0, b1, arow_i,
+        fp8_load<TL>(ring + ((nk - 1) & 3) * SC, sring + (((nk - 2) >> 1) & 3) * (BM + BN), a0, a1, b0, b1, arow_i,
                      brow_i, sh, fa1, fb1, sa1, sb1);
         fp8_mfma<TL, 0, EARLY, NM - EARLY>(fa0, fb0, sa0, sb0, acc);
         interleave_hint<NR, NM - EARLY>();
@@ -611,12 +631,14 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         // next tile's first K-tiles go out before this tile's epilogue
         const TileCoord cur = c;
         const int next = tile + G;
+        wait_lds();
         ring_barrier();   // every wave is past its last fragment and scale read
         if (next < total) {
             setup(next);
             issue(0);
             issue(1);
             issue(2);
+            issue(3);
         }
         fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, cur, wm, wn);
         if (next >= total) break;
@@ -626,28 +648,22 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 
 // ============================================================================ launchers
 
-template <class TL>
-static unsigned ring_grid(int R, int E, int N) {
-    const long mt_bound = (long)R / TL::BM + (long)min(E, R);
-    const long tiles = mt_bound * ((N + TL::BN - 1) / TL::BN);
-    long g = min(tiles, 256L);
-    return (unsigned)max((g + kXcds - 1) / kXcds * kXcds, (long)kXcds);
-}
-
 template <class TL, int EPI>
 hipError_t launch_bf16_pipe_tile(const uint16_t* A, const uint16_t* Bw, uint16_t* C, const int32_t* offsets,
-                                 int R, int E, int N, int K, int ldc, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<TL, EPI>), dim3(ring_grid<TL>(R, E, N)), dim3(TL::NTHR), 0, s, A, Bw,
-                       C, offsets, E, N, K, ldc);
+                                 int R, int E, int N, int K, int ldc, const int32_t* host_counts, hipStream_t s) {
+    const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
+    hipLaunchKernelGGL((gemm_bf16_pipe_kernel<TL, EPI>), dim3(grid), dim3(TL::NTHR), 0, s, A, Bw, C, offsets, E, N,
+                       K, ldc);
     return hipGetLastError();
 }
 
 template <class TL, int EPI>
 hipError_t launch_fp8_pipe_tile(const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                                 void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                                hipStream_t s) {
-    hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI>), dim3(ring_grid<TL>(R, E, N)), dim3(TL::NTHR), 0, s, A, As,
-                       Bw, Bs, C, Cs, offsets, E, N, K, ldc);
+                                const int32_t* host_counts, hipStream_t s) {
+    const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
+    hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs, C, Cs,
+                       offsets, E, N, K, ldc);
     return hipGetLastError();
 }
 
@@ -655,16 +671,17 @@ using BfRing = RingTile<256, 256, 2, 4>;    // 8 waves of 128 x 64
 using Fp8Ring = RingTile<256, 256, 2, 2>;   // 4 waves of 128 x 128
 
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C, const int32_t* offsets,
-                            int R, int E, int N, int K, int ldc, hipStream_t s) {
-    if (epi == 1) return launch_bf16_pipe_tile<BfRing, 1>(A, Bw, C, offsets, R, E, N, K, ldc, s);
-    return launch_bf16_pipe_tile<BfRing, 0>(A, Bw, C, offsets, R, E, N, K, ldc, s);
+                            int R, int E, int N, int K, int ldc, const int32_t* host_counts, hipStream_t s) {
+    if (epi == 1) return launch_bf16_pipe_tile<BfRing, 1>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, s);
+    return launch_bf16_pipe_tile<BfRing, 0>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, s);
 }
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                           hipStream_t s) {
-    if (epi == 1) return launch_fp8_pipe_tile<Fp8Ring, 1>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, s);
-    return launch_fp8_pipe_tile<Fp8Ring, 0>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, s);
+                           const int32_t* host_counts, hipStream_t s) {
+    if (epi == 1)
+        return launch_fp8_pipe_tile<Fp8Ring, 1>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s);
+    return launch_fp8_pipe_tile<Fp8Ring, 0>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s);
 }
 
 }  // namespace moe

@@ -93,4 +93,14 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
     return sign | code;
 }
 
+// Four E4M3 codes (a in byte 0 .. d in byte 3) by the hardware conversion
+// (round to nearest even) after clamping to +-448, which makes it the
+// saturating encode above; checked equal to e4m3_encode over every finite
+// float32 input on gfx950.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(a, -448.f), 448.f), fminf(fmaxf(b, -448.f), 448.f), 0, false);
+    pk = __builtin_amdgcn_cvt_pk_fp8_f32(fminf(fmaxf(c, -448.f), 448.f), fminf(fmaxf(d, -448.f), 448.f), pk, true);
+    return (uint32_t)pk;
+}
+
 }  // namespace moe

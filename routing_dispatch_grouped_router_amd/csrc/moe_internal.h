@@ -24,12 +24,14 @@ hipError_t launch_router_logits(int act, const void* x, const void* w, float* lo
 // Top-k + gates + per-block histogram and within-block ranks.
 //   rank[T][k]   : rank of token t among the tokens of its routing block routed to the same expert
 //   hist[nblk][E]: per-block expert counts
+// psum (optional, [nblk][E]): per-block sums of the full-softmax router probability.
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
-                             float* topk_gate, int32_t* rank, int32_t* hist, hipStream_t s);
+                             float* topk_gate, int32_t* rank, int32_t* hist, float* psum, hipStream_t s);
 
-// counts, offsets and base[nblk][E] = offsets[e] + tokens of earlier blocks routed to e.
+// counts, offsets and base[nblk][E] = offsets[e] + tokens of earlier blocks routed to e;
+// with psum non-NULL also the router statistics stats[E + 2] (see route.hip).
 hipError_t launch_route_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
-                             int32_t* offsets, hipStream_t s);
+                             int32_t* offsets, const float* psum, float* stats, int T, int k, hipStream_t s);
 
 // pos[t][j] (holding the rank on entry) += base[t / kRouteBlock][idx]; row_token[pos] = t.
 hipError_t launch_route_finalize(const int32_t* topk_idx, const int32_t* base, int T, int E, int k,
@@ -49,22 +51,30 @@ hipError_t launch_combine(int act, const void* ye, const float* gate, const int3
 // Grouped GEMMs over expert segments [offsets[e], offsets[e+1]) of R rows.
 //   gemm1: h = silu(xe W_gate) * (xe W_up)   (packed W1 [E][2H][d])
 //   gemm2: ye = h W_down                      (packed W2 [E][d][H])
+// The kernels read the group sizes from `offsets` in device memory.  The grid
+// is sized from the worst case R / BM + E M tiles, or, when the host already
+// holds the per-expert counts (host_counts, E entries; NULL otherwise), from
+// the exact tile count.
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
-                        int R, int E, int d, int H, hipStream_t s);
+                        int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s);
 hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const void* w2,
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
-                        int d, int H, hipStream_t s);
+                        int d, int H, const int32_t* host_counts, hipStream_t s);
+
+// Persistent grid: one workgroup per tile up to per_cu * 256, a multiple of the 8 XCDs.
+int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts);
 
 // Pipelined bf16 grouped GEMM (gemm_pipe.hip); epi 1 = SwiGLU epilogue (C has N/2 columns).
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C,
-                            const int32_t* offsets, int R, int E, int N, int K, int ldc, hipStream_t s);
+                            const int32_t* offsets, int R, int E, int N, int K, int ldc,
+                            const int32_t* host_counts, hipStream_t s);
 
 // Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K.
 // epi 0: bf16 C [.., ldc];  epi 1: SwiGLU then MXFP8 C codes [.., ldc] + scales Cs [.., ldc / 32].
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                           hipStream_t s);
+                           const int32_t* host_counts, hipStream_t s);
 
 // Weight packing (setup).
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,

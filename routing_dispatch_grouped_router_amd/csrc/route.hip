@@ -130,16 +130,24 @@ hipError_t launch_router_logits(int act, const void* x, const void* w, float* lo
 // G lanes cooperate on one token, each holding V of its E logits (expert
 // r + G*v for lane r of the group).  k rounds of a group-wide max over
 // orderable 64-bit keys select the experts in (logit desc, index asc) order.
+//
+// With psum non-NULL the kernel also sums, per expert, the full-softmax router
+// probability over the block's tokens (the soft half of the load-balancing
+// statistics): each lane accumulates its experts over the tokens of its group
+// in token order, and the groups' partial sums are added in group order, so
+// the result does not depend on scheduling.  psum[blk][e] receives the sum.
 template <int V>
 __global__ __launch_bounds__(1024) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int G,
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_gate,
                                                           int32_t* __restrict__ rank,
-                                                          int32_t* __restrict__ hist) {
+                                                          int32_t* __restrict__ hist,
+                                                          float* __restrict__ psum) {
     constexpr int kWords = kRouteBlock / 32;
     __shared__ uint32_t mask[kMaxExperts * kWords];
     __shared__ int32_t s_idx[kRouteBlock * kMaxTopK];   // selected experts of this block
+    __shared__ float s_ps[1024 * V];                    // [group][expert] probability partials
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int blk = blockIdx.x;
@@ -149,14 +157,19 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(const float* __restric
     const int r = tid % G;
     const int grp = tid / G;
     const int per_pass = nthr / G;
+    float pacc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) pacc[v] = 0.f;
     for (int lt = grp; lt < kRouteBlock; lt += per_pass) {
         const int t = blk * kRouteBlock + lt;
         if (t >= T) break;       // uniform within a group: G divides 64
         uint64_t key[V];
+        float lv[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
             int e = r + G * v;
-            key[v] = (e < E) ? route_key(logits[(size_t)t * E + e], e) : 0ull;
+            lv[v] = (e < E) ? logits[(size_t)t * E + e] : 0.f;
+            key[v] = (e < E) ? route_key(lv[v], e) : 0ull;
         }
         uint64_t sel[kMaxTopK];
 #pragma unroll
@@ -193,8 +206,33 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(const float* __restric
                 atomicOr(&mask[e * kWords + (lt >> 5)], 1u << (lt & 31));
             }
         }
+        if (psum != nullptr) {
+            // full softmax over the E logits, l0 being their maximum
+            float z[V], zs = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                z[v] = (r + G * v < E) ? expf(lv[v] - l0) : 0.f;
+                zs += z[v];
+            }
+            for (int m = 1; m < G; m <<= 1) zs += __shfl_xor(zs, m);
+            const float iz = 1.0f / zs;
+#pragma unroll
+            for (int v = 0; v < V; ++v) pacc[v] += z[v] * iz;
+        }
+    }
+    if (psum != nullptr) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            if (r + G * v < E) s_ps[grp * E + r + G * v] = pacc[v];
     }
     __syncthreads();
+    if (psum != nullptr) {
+        for (int e = tid; e < E; e += nthr) {
+            float sum = 0.f;
+            for (int g = 0; g < per_pass; ++g) sum += s_ps[g * E + e];
+            psum[(size_t)blk * E + e] = sum;
+        }
+    }
     // within-block rank of every (token, slot): popcount of earlier tokens of the same expert
     for (int i = tid; i < kRouteBlock * k; i += nthr) {
         const int lt = i / k, j = i % k;
@@ -215,7 +253,7 @@ __global__ __launch_bounds__(1024) void route_topk_kernel(const float* __restric
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
-                             float* topk_gate, int32_t* rank, int32_t* hist, hipStream_t s) {
+                             float* topk_gate, int32_t* rank, int32_t* hist, float* psum, hipStream_t s) {
     // lanes per token: smallest power of two G <= 64 with E / G <= 8 (or 16 at G = 64)
     int G = 1;
     while (G < 64 && (E + G - 1) / G > 8) G <<= 1;
@@ -224,10 +262,10 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     dim3 grid(route_blocks(T)), block(threads);
     if (V <= 8)
         hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, G, topk_idx,
-                           topk_gate, rank, hist);
+                           topk_gate, rank, hist, psum);
     else
         hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, G, topk_idx,
-                           topk_gate, rank, hist);
+                           topk_gate, rank, hist, psum);
     return hipGetLastError();
 }
 
@@ -237,11 +275,19 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 // contiguous chunk c of routing blocks; chunk partials are scanned per expert,
 // expert totals are scanned into offsets, and each thread then writes the
 // global base position of expert e for every block of its chunk.
+//
+// With psum non-NULL it also finishes the router statistics into stats[E + 2]:
+// stats[e] = P_e = (sum over blocks of psum[b][e]) / T, the mean full-softmax
+// probability of expert e; stats[E] = E * sum_e (counts[e] / (T k)) * P_e, the
+// Switch-style load-balancing scalar; stats[E + 1] = max_e counts[e] / (T k / E),
+// the worst-case load over the mean load.  Sums run in a fixed order.
 __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist,
                                                           int nblk, int E,
                                                           int32_t* __restrict__ base,
                                                           int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets) {
+                                                          int32_t* __restrict__ offsets,
+                                                          const float* __restrict__ psum,
+                                                          float* __restrict__ stats, int T, int k) {
     __shared__ int32_t part[1024];
     __shared__ int32_t tot[1024];
     const int tid = threadIdx.x;
@@ -280,6 +326,30 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
         counts[tid] = tot[tid] - excl;
     }
     if (tid == 0) offsets[E] = tot[E - 1];
+    if (psum != nullptr) {
+        __shared__ float s_fp[1024];
+        __shared__ int s_cnt[1024];
+        if (tid < E) {
+            float sum = 0.f;
+            for (int b = 0; b < nblk; ++b) sum += psum[(size_t)b * E + tid];
+            const float P = sum / (float)T;
+            const int c = tot[tid] - (tid == 0 ? 0 : tot[tid - 1]);
+            stats[tid] = P;
+            s_fp[tid] = (float)c / ((float)T * (float)k) * P;
+            s_cnt[tid] = c;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+            int mx = 0;
+            for (int e = 0; e < E; ++e) {
+                acc += s_fp[e];
+                mx = max(mx, s_cnt[e]);
+            }
+            stats[E] = (float)E * acc;
+            stats[E + 1] = (float)mx * (float)E / ((float)T * (float)k);
+        }
+    }
     if (act) {
         int run = (e == 0 ? 0 : tot[e - 1]) + part[c * E + e];
         for (int b = b0; b < b1; ++b) {
@@ -290,9 +360,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 }
 
 hipError_t launch_route_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
-                             int32_t* offsets, hipStream_t s) {
+                             int32_t* offsets, const float* psum, float* stats, int T, int k, hipStream_t s) {
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nblk, E, base, counts,
-                       offsets);
+                       offsets, psum, stats, T, k);
     return hipGetLastError();
 }
 

@@ -79,11 +79,14 @@ def test_null_pointers_rejected_before_any_launch(lib):
     V = ctypes.c_void_p
     fake = V(0x1000)   # never dereferenced: validation fails first
     assert lib.moe_route(ctypes.byref(p), None, None, None, fake, fake, fake, fake, fake, fake,
-                         fake, 1 << 30, None) == -1
+                         None, fake, 1 << 30, None) == -1
     assert lib.moe_dispatch(ctypes.byref(p), fake, None, fake, None, None) == -1
     assert lib.moe_combine(ctypes.byref(p), fake, fake, None, fake, None) == -1
     assert lib.moe_forward(ctypes.byref(p), None, None, fake, fake, fake, None, None, None, None,
-                           None, fake, 1 << 30, None) == -1
+                           None, None, fake, 1 << 30, None) == -1
+    # the host-synchronising variant needs its host buffer
+    assert lib.moe_forward_host_sync(ctypes.byref(p), fake, None, fake, fake, fake, None, None, None, None,
+                                     None, None, fake, 1 << 30, None, None) == -1
     pm = _prob(act="mxfp8", logits_given=True)
     assert lib.moe_dispatch(ctypes.byref(pm), fake, fake, fake, None, None) == -1
     assert lib.moe_grouped_swiglu(ctypes.byref(pm), fake, None, fake, fake, fake, fake, 1 << 30,
@@ -95,9 +98,12 @@ def test_small_workspace_rejected(lib):
     need = B.workspace_bytes(p)
     fake = ctypes.c_void_p(0x1000)
     assert lib.moe_forward(ctypes.byref(p), fake, None, fake, fake, fake, None, None, None, None,
-                           None, fake, need - 1, None) == -4
+                           None, None, fake, need - 1, None) == -4
+    host = (ctypes.c_int32 * p.n_experts)()
+    assert lib.moe_forward_host_sync(ctypes.byref(p), fake, None, fake, fake, fake, None, None, None, None,
+                                     None, None, fake, need - 1, None, ctypes.cast(host, ctypes.c_void_p)) == -4
     assert lib.moe_route(ctypes.byref(p), None, None, fake, fake, fake, fake, fake, fake, fake,
-                         fake, 16, None) == -4
+                         None, fake, 16, None) == -4
 
 
 def test_kernel_times_without_profiled_forward(lib):

@@ -79,6 +79,19 @@ def check_logits(w, host, gpu_logits):
     return got
 
 
+STATS_TOL = 1e-5   # relative, float32 sums of at most a few thousand probabilities in fixed order
+
+
+def check_router_stats(w, stats, logits64, counts):
+    """stats: device float32 [E + 2] (P_e, balance scalar, worst-case imbalance)."""
+    ref = O.router_stats(logits64, counts, w.k)
+    got = _f64(stats)
+    E = w.E
+    assert np.max(np.abs(got[:E] - ref["P"])) <= STATS_TOL * np.max(ref["P"]), "P_e"
+    assert abs(got[E] - ref["lbl"]) <= STATS_TOL * ref["lbl"], "balance scalar"
+    assert abs(got[E + 1] - ref["imbalance"]) <= 1e-6 * ref["imbalance"], "imbalance"
+
+
 def oracle_weights(host):
     return (W.as_f64(host["w_gate"]), W.as_f64(host["w_up"]), W.as_f64(host["w_down"]))
 
@@ -93,10 +106,11 @@ def test_stages_against_oracle(name):
     host, dev = device_inputs(w)
     p = problem_of(w)
     ws = B.new_workspace(p, DEV)
-    r = B.route(p, x=dev["x"], w_router=dev["w_router"], logits=dev["logits"], ws=ws)
+    r = B.route(p, x=dev["x"], w_router=dev["w_router"], logits=dev["logits"], ws=ws, stats=True)
     torch.cuda.synchronize()
     L = check_logits(w, host, r["logits"])
     idx, gate, counts, offsets, pos = check_routing(w, r, L)
+    check_router_stats(w, r["router_stats"], L, counts)
 
     x64 = W.as_f64(host["x"])
     xe, xs = B.dispatch(p, dev["x"], r["pos"])
@@ -172,6 +186,62 @@ def test_deterministic_bitwise(name):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16_e8", "small_mxfp8", "edge_empty_experts",
+                                  "small_f32_learned"])
+def test_host_sync_variant_matches(name):
+    """moe_forward_host_sync runs the same kernels after one host wait: every
+    output is bit-identical to moe_forward's, and the host copy of the counts
+    equals the oracle's counts."""
+    w = W.get(name)
+    print(f"[host-sync] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    outs = []
+    for sync in (False, True):
+        f = B.Forward(p, DEV, host_sync=sync)
+        f(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+        torch.cuda.synchronize()
+        outs.append(f)
+    a, b = outs
+    for name_t in ("y", "logits", "idx", "gate", "counts", "offsets", "pos"):
+        assert torch.equal(getattr(a, name_t), getattr(b, name_t)), name_t
+    L = _f64(a.logits) if w.router == "learned" else W.as_f64(host["logits"])
+    idx, _ = O.route(L, w.k)
+    counts, _, _, _ = O.route_metadata(idx, w.E)
+    assert np.array_equal(b.host_counts.numpy(), counts)
+
+
+@pytest.mark.parametrize("name", ["small_bf16_zipf", "small_f32_learned", "edge_empty_experts", "edge_k_eq_E",
+                                  "edge_one_token"])
+def test_router_stats_forward(name):
+    """Router statistics from moe_forward: equal to the oracle's, bit-identical
+    across calls and to moe_route's, and computing them changes no other output."""
+    w = W.get(name)
+    print(f"[router-stats] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    plain = B.Forward(p, DEV)
+    plain(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    f = B.Forward(p, DEV, stats=True)
+    runs = []
+    for _ in range(2):
+        f(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+        torch.cuda.synchronize()
+        runs.append(f.router_stats.clone())
+    assert torch.equal(runs[0], runs[1])
+    for name_t in ("y", "idx", "gate", "counts", "offsets", "pos", "logits"):
+        assert torch.equal(getattr(plain, name_t), getattr(f, name_t)), name_t
+    L = _f64(f.logits) if w.router == "learned" else W.as_f64(host["logits"])
+    check_router_stats(w, f.router_stats, L, _np(f.counts))
+    r = B.route(p, x=dev["x"], w_router=dev["w_router"], logits=f.logits if w.router != "learned" else None,
+                stats=True)
+    torch.cuda.synchronize()
+    if w.router != "learned":
+        assert torch.equal(r["router_stats"], f.router_stats)
+
+
 def test_graph_capture_replay():
     w = W.get("small_bf16_e32_random")
     print(f"[graph] {w.describe()}", flush=True)
@@ -233,7 +303,7 @@ def test_full_size_config(name):
     host, dev = device_inputs(w)
     p = problem_of(w)
     packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
-    f = B.Forward(p, DEV)
+    f = B.Forward(p, DEV, stats=True)
     f(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
     torch.cuda.synchronize()
     gpu = dict(idx=f.idx, gate=f.gate, counts=f.counts, offsets=f.offsets, pos=f.pos)
@@ -245,6 +315,7 @@ def test_full_size_config(name):
     else:
         L = check_logits(w, host, f.logits)
     idx, gate, counts, offsets, pos = check_routing(w, gpu, L)
+    check_router_stats(w, f.router_stats, L, counts)
     toks = _sample_tokens(w.T)
     ref = O.forward_tokens(W.as_f64(host["x"]), idx, gate, toks, w.act, _LazyF64(host["w_gate"]),
                            _LazyF64(host["w_up"]), _LazyF64(host["w_down"]))
