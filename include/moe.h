@@ -45,7 +45,9 @@
  *    Rows of one expert are ordered by ascending token index (stable), experts
  *    back to back without padding: offsets[e] = sum of counts[e' < e].
  *  - Shapes supported: 1 <= k <= min(E, 16), E <= 1024, T >= 1, and
- *    d, H multiples of 64 (MOE_F32, MOE_BF16) or of 128 (MOE_MXFP8).
+ *    d, H multiples of 64 (MOE_F32, MOE_BF16) or of 128 (MOE_MXFP8); the
+ *    bytes of an [R, max(d, H)] activation buffer and of one expert's
+ *    [2H, d] weights must each stay below 2^32.
  *  - Errors: every entry point returns MOE_OK or a negative MOE_ERR_* code.
  *    Arguments are validated on the host before anything is enqueued; a
  *    failed check enqueues nothing.  MOE_ERR_LAUNCH reports hipGetLastError()
@@ -111,8 +113,10 @@ int32_t moe_packed_weight_bytes(const moe_problem* p, size_t* bytes);
  *                     gate columns then the matching 32 up columns, repeated.
  *     W2 [E][d][H]  : W2[e][n][j] = w_down[e][j][n].
  *     Elements are float32 / bfloat16 / E4M3 by act_dtype.  For MOE_MXFP8 the
- *     E8M0 scales follow: S1 [E][2H][d/32], then S2 [E][d][H/32], each scale
- *     covering 32 consecutive elements of a row.
+ *     E8M0 scales follow, each covering 32 consecutive elements of a row and
+ *     stored slice-major: S1 [E][d/128][2H][4], then S2 [E][H/128][d][4], where
+ *     S[e][s][n][j] is the scale of elements [128 s + 32 j, 128 s + 32 j + 32)
+ *     of packed row n (the layout the GEMM loads without conversion).
  *   Regions are W1, W2, S1, S2 in that order, each starting at a multiple of
  *   256 bytes. */
 int32_t moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
@@ -150,7 +154,13 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, flo
  *   x        : device [T, d]
  *   pos      : device int32 [T, k] from moe_route
  *   xe       : device [R, d] out (MOE_MXFP8: uint8 E4M3 codes)
- *   xe_scale : device uint8 [R, d/32] out for MOE_MXFP8, else ignored (may be NULL) */
+ *   xe_scale : device uint8 [d/128][R][4] out for MOE_MXFP8, else ignored (may
+ *              be NULL): xe_scale[s][r][j] is the E8M0 scale of elements
+ *              [128 s + 32 j, 128 s + 32 j + 32) of row r, so the four scales
+ *              of a 128-wide slice of a row form one dword and the dwords of
+ *              consecutive rows are adjacent, the layout the grouped GEMM reads
+ *              directly (report "Section 24: Conclusion", 24.3: a quantiser
+ *              should emit what the consumer reads without conversion) */
 int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, void* xe,
                      uint8_t* xe_scale, void* stream);
 

@@ -188,14 +188,15 @@ def route(p: Problem, x=None, w_router=None, logits=None, ws=None, stream=None, 
 
 
 def dispatch(p: Problem, x, pos, stream=None):
-    """Returns (xe, xe_scale); xe_scale is None unless MXFP8."""
+    """Returns (xe, xe_scale); xe_scale is None unless MXFP8, else uint8
+    [d/128, R, 4]: the four E8M0 scales of each 128-wide slice of a row."""
     T, d, k = p.T, p.d_model, p.top_k
     R = T * k
     _expect(x, (T, d), storage_dtype(p.act), "x")
     _expect(pos, (T, k), torch.int32, "pos")
     if p.act == "mxfp8":
         xe = torch.empty((R, d), dtype=torch.uint8, device=x.device)
-        xs = torch.empty((R, d // 32), dtype=torch.uint8, device=x.device)
+        xs = torch.empty((d // 128, R, 4), dtype=torch.uint8, device=x.device)   # slice-major scales
     else:
         xe = torch.empty((R, d), dtype=storage_dtype(p.act), device=x.device)
         xs = None

@@ -85,6 +85,11 @@ int32_t check_problem(const moe_problem* p) {
     const long long R = (long long)p->T * p->top_k;
     if (R > INT_MAX / 2 || (long long)p->d_model > INT_MAX / 8 || (long long)p->d_hidden > INT_MAX / 8)
         return MOE_ERR_SHAPE;
+    // the pipelined GEMMs address an activation buffer, and one expert's packed
+    // weights, with 32-bit byte offsets
+    const long long eb = p->act_dtype == MOE_F32 ? 4 : (p->act_dtype == MOE_BF16 ? 2 : 1);
+    const long long wide = std::max<long long>(p->d_model, p->d_hidden);
+    if (R * wide * eb >= (1LL << 32) || 2LL * p->d_hidden * p->d_model * eb >= (1LL << 32)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 

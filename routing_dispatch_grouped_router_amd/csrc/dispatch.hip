@@ -80,6 +80,8 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
 }
 
 // MXFP8: each lane quantises 8 bf16 values; 4 adjacent lanes form one block of 32.
+// Scales are stored [d/128][R][4] (the four scales of a 128-wide slice of a
+// row in one dword, rows adjacent), the layout the MXFP8 GEMM loads directly.
 __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __restrict__ x,
                                                              int32_t* __restrict__ pos,
                                                              const int32_t* __restrict__ topk_idx,
@@ -88,6 +90,7 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __rest
                                                              uint2* __restrict__ xq,
                                                              uint8_t* __restrict__ xs, int T, int d,
                                                              int E, int k) {
+    const size_t R = (size_t)T * k;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -135,7 +138,8 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __rest
             for (int j = 0; j < kMaxTopK; ++j) {
                 if (j < k) {
                     xq[(size_t)p[j] * chunks + c] = q;
-                    if ((lane & 3) == 0) xs[(size_t)p[j] * (d / 32) + (c >> 2)] = (uint8_t)(se + 127);
+                    // scale of block b = c / 4 at [b / 4][row][b % 4]
+                    if ((lane & 3) == 0) xs[(((size_t)(c >> 4)) * R + p[j]) * 4 + ((c >> 2) & 3)] = (uint8_t)(se + 127);
                 }
             }
         }

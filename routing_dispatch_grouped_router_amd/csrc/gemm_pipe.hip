@@ -36,6 +36,8 @@
 // flight.  Every issue starts the same number of loads (past the last K-tile
 // the loads are clamped and land in a stage nobody reads again), so the vmcnt
 // waits are constants and the loop body has no branches.
+#include <type_traits>
+
 #include "grouped_sched.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -97,8 +99,9 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// silu(g) * u with the hardware reciprocal (1 ulp) in place of a division.
 __device__ __forceinline__ float silu_mul_p(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Interleave R fragment reads with M MFMAs in the scheduling region.
@@ -403,14 +406,15 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 // bytes 16..31, and supplies the scale of K block h: scale block b covers
 // bytes 0..15 of both halves for b = 0 and bytes 16..31 for b = 1 (measured on
 // gfx950).  So a lane's fragment is chunks h and 2 + h of the 64-byte slice,
-// and its scale is that of block 2 kt + h.  Scales come in pairs of
-// K-tiles: with every even K-tile t each wave DMAs, for its SR rows of A and
-// of B, the dword of scale bytes of K blocks 2t .. 2t+3 into a four-slot scale
-// ring.  Lanes of the upper half shift that dword right by one byte, so one
-// op_sel (byte 0 for even K-tiles, byte 2 for odd ones) gives every lane the
-// scale of its own block.  Four waves each own a 128 x 128 block whose 256
-// accumulators sit in AGPRs, leaving the VGPRs to the 32-byte fragments (fp8
-// halves the LDS bytes per FLOP, so the larger per-wave block suits it).
+// and its scale is that of block 2 kt + h.  Scales come in pairs of K-tiles:
+// with every even K-tile t each wave DMAs, for its SR rows of A and of B, the
+// dword of scale bytes of K blocks 2t .. 2t+3 into a four-slot scale ring.
+// Scale buffers are stored [K/128][rows][4], so those dwords are one
+// contiguous run per wave.  Each lane reads its own scale byte (byte h for an
+// even K-tile, 2 + h for an odd one) zero-extended, and the MFMA takes scale
+// byte 0.  Four waves each own a 128 x 128 block whose 256 accumulators sit in
+// AGPRs, leaving the VGPRs to the 32-byte fragments (fp8 halves the LDS bytes
+// per FLOP, so the larger per-wave block suits it).
 template <class TL>
 struct Fp8Extra {
     static constexpr int PS = 2;                // scale DMAs per wave per even K-tile
@@ -418,35 +422,38 @@ struct Fp8Extra {
     static_assert(TL::BM == TL::BN && (SR == 32 || SR == 64), "one scale DMA per wave and operand");
 };
 
+// Fragment mi of A (or ni of B) of one K-tile: chunks h and 2 + h of the
+// lane's row, and the lane's scale byte read on its own (zero-extended, so
+// the MFMA always takes scale byte 0).
 template <class TL>
-__device__ __forceinline__ void fp8_load(const u32x4* stage, const uint32_t* sslot, int aoff0, int aoff1,
-                                         int boff0, int boff1, int arow, int brow, int sh, i32x8 (&fa)[TL::TM],
-                                         i32x8 (&fb)[TL::TN], int (&sa)[TL::TM], int (&sb)[TL::TN]) {
-#pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi) {
-        const u32x4 lo = stage[aoff0 + mi * 128], hi = stage[aoff1 + mi * 128];
-        fa[mi] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sa[mi] = (int)(sslot[arow + mi * 32] >> sh);
-    }
-#pragma unroll
-    for (int ni = 0; ni < TL::TN; ++ni) {
-        const u32x4 lo = stage[boff0 + ni * 128], hi = stage[boff1 + ni * 128];
-        fb[ni] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sb[ni] = (int)(sslot[TL::BM + brow + ni * 32] >> sh);
-    }
+__device__ __forceinline__ void fp8_frag(const u32x4* stage, const uint8_t* sbytes, int off0, int off1, int sbyte,
+                                         i32x8& f, int& sc) {
+    const u32x4 lo = stage[off0], hi = stage[off1];
+    f = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    sc = sbytes[sbyte];
 }
 
 // MFMAs [FIRST, FIRST + COUNT) of the TM x TN block, row-major over (mi, ni).
-template <class TL, int OPSEL, int FIRST, int COUNT>
+template <class TL, int FIRST, int COUNT>
 __device__ __forceinline__ void fp8_mfma(const i32x8 (&fa)[TL::TM], const i32x8 (&fb)[TL::TN],
                                          const int (&sa)[TL::TM], const int (&sb)[TL::TN],
                                          f32x16 (&acc)[TL::TM][TL::TN]) {
 #pragma unroll
     for (int i = FIRST; i < FIRST + COUNT; ++i) {
         const int mi = i / TL::TN, ni = i % TL::TN;
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ni], fa[mi], acc[mi][ni], 0, 0, OPSEL,
-                                                                     sb[ni], OPSEL, sa[mi]);
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0, sb[ni],
+                                                                     0, sa[mi]);
     }
+}
+
+// MFMA number i (row-major over (mi, ni)); i is a constant after unrolling.
+template <class TL>
+__device__ __forceinline__ void fp8_mfma1(int i, const i32x8 (&fa)[TL::TM], const i32x8 (&fb)[TL::TN],
+                                          const int (&sa)[TL::TM], const int (&sb)[TL::TN],
+                                          f32x16 (&acc)[TL::TM][TL::TN]) {
+    const int mi = i / TL::TN, ni = i % TL::TN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0, sb[ni], 0,
+                                                                 sa[mi]);
 }
 
 // Epilogue of the MXFP8 kernel.  EPI 0: C = acc as bf16.  EPI 1: h = silu(gate)
@@ -456,8 +463,8 @@ __device__ __forceinline__ void fp8_mfma(const i32x8 (&fa)[TL::TM], const i32x8 
 // e4m3x4 (saturating round-to-nearest-even E4M3).
 template <class TL, int EPI>
 __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], void* __restrict__ C,
-                                             uint8_t* __restrict__ Cs, int ldc, int N, const TileCoord& c, int wm,
-                                             int wn) {
+                                             uint8_t* __restrict__ Cs, int ldc, int N, int R, const TileCoord& c,
+                                             int wm, int wn) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
 #pragma unroll
@@ -473,6 +480,7 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = acc[mi][ni][i];
                 store_bf16_block(static_cast<uint16_t*>(C), (size_t)ldc, (int)grow, valid && col0 < N, col0, v);
+                __builtin_amdgcn_sched_barrier(0);   // one block's values in VGPRs at a time
             }
         } else {
 #pragma unroll
@@ -497,22 +505,38 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
                     const int hb = pc / 64;   // 32-wide h block of this pair
                     uint8_t* Cq = static_cast<uint8_t*>(C);
                     *reinterpret_cast<u32x4*>(Cq + grow * ldc + hb * 32 + 16 * half) = (u32x4){w[0], w[1], w[2], w[3]};
-                    if (half == 0) Cs[grow * (ldc / 32) + hb] = (uint8_t)(se + 127);
+                    // scale planes [ldc/128][R][4]
+                    if (half == 0) Cs[((size_t)(hb >> 2) * R + grow) * 4 + (hb & 3)] = (uint8_t)(se + 127);
                 }
+                __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
         }
     }
 }
 
+// The persistent MXFP8 kernel streams K-tiles without a break at tile
+// boundaries: global K-tile g of this workgroup (g = tiles done * nk + kt) goes
+// through ring stage g % 4 and scale slot (g / 2) % 4, and the DMAs of the last
+// four K-tiles of a tile already fetch the first four of the next one.  Each
+// half-iteration handles one K-tile g: a few MFMAs on the fragments in hand,
+// the wait for K-tile g + 1, the barrier (every wave then holds all of K-tile g
+// in registers, so its stage and the previous pair's scale slot are free),
+// and then, one per MFMA, the DMAs of K-tile g + 4 and the fragment reads of
+// K-tile g + 1.  The epilogue runs between the last MFMA of a tile and the
+// first of the next while the next tile's first K-tiles are in flight; its
+// stores count in vmcnt after those DMAs, which only makes the next waits wait
+// longer, never shorter.
 template <class TL, int EPI>   // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                           const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, void* __restrict__ C,
                           uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets, int E, int N, int K,
-                          int ldc) {
+                          int ldc, int R) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
-    constexpr int NM = TL::NM, EARLY = TL::EARLY, NR = 3 * (TM + TN), P = TL::P, SC = TL::STAGE_CHUNKS;
+    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
+    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
+    static_assert(NM - EARLY >= P + PS && NM - EARLY >= TM + TN, "one DMA and one fragment per MFMA step");
     __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ uint32_t sring[4 * (BM + BN)];     // four scale slots: A rows then B rows
     __shared__ int s_tstart[kMaxExperts + 1];
@@ -523,55 +547,110 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     const int total = MT * NT;
     const int G = gridDim.x;
     const int kb = K / 32;            // scale bytes per row
+    const int nk = K / 64;            // K-tiles per tile (even: K % 128 == 0)
     int tile = xcd_slot(blockIdx.x, G);
     if (tile >= total) return;
 
-    Ring<TL> rg;
-    rg.init(A, lds_addr(ring), K / 64);
-    const int nk = rg.nk;
-    const int lane = threadIdx.x & 63;
-    const uint32_t sring_lds = lds_addr(sring);
-    const int wm = rg.wave / TL::WN, wn = rg.wave % TL::WN;
+    // wave-uniform values are pinned to SGPRs (derived from threadIdx they would
+    // otherwise live in VGPRs)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ring_lds = lds_addr(ring), sring_lds = lds_addr(sring);
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
     const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
     const int arow_i = wm * TL::WROWS + (lane & 31), brow_i = wn * TL::WCOLS + (lane & 31);
     const int a0 = arow_i * 4 + (half ^ fsw), a1 = arow_i * 4 + ((2 + half) ^ fsw);
     const int b0 = (BM + brow_i) * 4 + (half ^ fsw), b1 = (BM + brow_i) * 4 + ((2 + half) ^ fsw);
-    const int sh = half * 8;
-    const int srow = SR * rg.wave + (lane & (SR - 1));    // scale DMA row of this lane
+    const int drow = lane >> 2;
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    const int srow = SR * wave + (lane & (SR - 1));    // scale DMA row of this lane
     const bool slane = lane < SR;
+    // scale byte of this lane in a slot for an even K-tile (+2 for an odd one):
+    // row dword, byte = K block within the pair's four
+    const int sa_byte = arow_i * 4 + half, sb_byte = (BM + brow_i) * 4 + half;
 
-    TileCoord c;
-    const void* Bsg;
-    uint32_t soA, soB;
-    auto setup = [&](int t) {
-        c = tile_coord<BM, BN>(t, NT, s_tstart, E, offsets);
-        const size_t eu = (size_t)c.e;
-        rg.setup(c, B + eu * N * K, N, (uint32_t)K);
-        Bsg = Bs + eu * N * kb;
-        soA = (uint32_t)(c.row0 + min(srow, c.rows - 1)) * kb;
-        soB = (uint32_t)min(c.n0 + srow, N - 1) * kb;
-    };
-    // DMA of K-tile kt, plus (kt even) the scale dwords of K-tiles kt, kt + 1
-    // into slot (kt / 2) % 4; clamped past the end like the data.
-    auto issue = [&](int kt) {
-        rg.issue(kt);
-        if ((kt & 1) == 0) {
-            const uint32_t so = (uint32_t)min(kt, nk - 2) * 2u;
-            const uint32_t slot = sring_lds + (uint32_t)((kt >> 1) & 3) * (BM + BN) * 4u;
-            const uint32_t lsa = __builtin_amdgcn_readfirstlane(slot + rg.wave * SR * 4u);
-            const uint32_t lsb = __builtin_amdgcn_readfirstlane(slot + BM * 4u + rg.wave * SR * 4u);
+    TileCoord cur = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets);
+    int next = tile + G;
+    TileCoord nxt = cur;
+    if (next < total) nxt = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
+    int kbase = 0;   // global K-tile index of the current tile's K-tile 0
+
+    // DMA of global K-tile g: K-tile g - kbase of the current tile, or of the
+    // next one past the current tile's end; past the last tile the source is
+    // clamped to the current tile's last K-tile (a stage nobody reads again).
+    // Step i of P + PS: A rows, then B rows, then (g even) the two scale dwords.
+    auto dma = [&](int g, int i) {
+        const int rel = g - kbase;
+        const bool in_next = rel >= nk && next < total;
+        const TileCoord& t = in_next ? nxt : cur;
+        const int kt = in_next ? rel - nk : min(rel, nk - 1);
+        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        if (i < A_DMA) {
+            const int r = 16 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(t.row0 + min(r, t.rows - 1)) * (uint32_t)K + dchunk + (uint32_t)kt * 64u;
+            dma16(A, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+        } else if (i < A_DMA + B_DMA) {
+            const int j = i - A_DMA;
+            const int r = 16 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(t.n0 + r, N - 1) * (uint32_t)K + dchunk + (uint32_t)kt * 64u;
+            dma16(B + (size_t)t.e * N * K, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+        } else {
+            // scale planes [K/128][rows][4]: the pair's dword of each row
+            const uint32_t slot = sring_lds + (uint32_t)((g >> 1) & 3) * (BM + BN) * 4u;
+            const uint32_t plane = (uint32_t)(in_next ? kt : min(kt, nk - 2)) >> 1;
             if (SR == 64 || slane) {
-                dma4(As, soA + so, lsa);
-                dma4(Bsg, soB + so, lsb);
+                if (i == A_DMA + B_DMA)
+                    dma4(As, (plane * (uint32_t)R + (uint32_t)(t.row0 + min(srow, t.rows - 1))) * 4u,
+                         slot + (uint32_t)(wave * SR) * 4u);
+                else
+                    dma4(Bs + (size_t)t.e * N * kb, (plane * (uint32_t)N + (uint32_t)min(t.n0 + srow, N - 1)) * 4u,
+                         slot + BM * 4u + (uint32_t)(wave * SR) * 4u);
             }
         }
     };
 
-    setup(tile);
-    issue(0);
-    issue(1);
-    issue(2);
-    issue(3);
+    // one half-iteration: K-tile g in (fa, fb, sa, sb), g even for ODD == 0;
+    // reads K-tile g + 1 into (ga, gb, ta, tb); DMAs K-tile g + 4.
+    auto half_step = [&](auto odd, int g, f32x16 (&acc)[TM][TN], const i32x8 (&fa)[TM], const i32x8 (&fb)[TN],
+                         const int (&sa)[TM], const int (&sb)[TN], i32x8 (&ga)[TM], i32x8 (&gb)[TN], int (&ta)[TM],
+                         int (&tb)[TN]) {
+        constexpr int ODD = decltype(odd)::value;
+        constexpr int ND = P + (ODD == 0 ? PS : 0);     // g + 4 has the parity of g
+        constexpr int NB = (1 - ODD) * 2;                // byte offset of K-tile g + 1's scales in its slot
+        fp8_mfma<TL, 0, EARLY>(fa, fb, sa, sb, acc);
+        wait_vm<2 * P + PS>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
+        wait_lds();              // this wave's reads of K-tile g are complete
+        ring_barrier();
+        const u32x4* stage = ring + ((g + 1) & 3) * SC;
+        const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (((g + 1) >> 1) & 3) * (BM + BN)) + NB;
+#pragma unroll
+        for (int i = 0; i < NM - EARLY; ++i) {
+            fp8_mfma1<TL>(EARLY + i, fa, fb, sa, sb, acc);
+            if (i < ND) dma(g + 4, i);
+            if (i < TM)
+                fp8_frag<TL>(stage, slot, a0 + i * 128, a1 + i * 128, sa_byte + i * 128, ga[i], ta[i]);
+            else if (i < TM + TN)
+                fp8_frag<TL>(stage, slot, b0 + (i - TM) * 128, b1 + (i - TM) * 128, sb_byte + (i - TM) * 128,
+                             gb[i - TM], tb[i - TM]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: K-tiles 0..3 in flight, K-tile 0 read into set 0
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < P + PS; ++i)
+            if (i < P || (g & 1) == 0) dma(g, i);
+    i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
+    wait_vm<3 * P + PS>();   // K-tile 0 and its scales landed; 1, 2 (with scales) and 3 may stay in flight
+    ring_barrier();
+    const uint8_t* slot0 = reinterpret_cast<const uint8_t*>(sring);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fp8_frag<TL>(ring, slot0, a0 + i * 128, a1 + i * 128, sa_byte + i * 128, fa0[i], sa0[i]);
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+        fp8_frag<TL>(ring, slot0, b0 + i * 128, b1 + i * 128, sb_byte + i * 128, fb0[i], sb0[i]);
 
     for (;;) {
         f32x16 acc[TM][TN];
@@ -582,68 +661,20 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-        int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
-        wait_vm<3 * P + PS>();   // K-tile 0 and its scales landed; 1, 2 (with scales) and 3 may stay in flight
-        ring_barrier();
-        fp8_load<TL>(ring, sring, a0, a1, b0, b1, arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
-
-        // K-tiles go in pairs (kt even: register set 0, op_sel 0; kt + 1: set 1,
-        // op_sel 2), the pair's scales in slot (kt / 2) % 4.  Each half starts a
-        // few MFMAs on the fragments in hand, waits for the next K-tile, joins
-        // the barrier, refills the stage of the K-tile whose fragments are in
-        // registers (four K-tiles ahead), and reads the next fragments between
-        // the remaining MFMAs.
-        for (int kt = 0; kt < nk - 2; kt += 2) {
-            fp8_mfma<TL, 0, 0, EARLY>(fa0, fb0, sa0, sb0, acc);
-            wait_vm<2 * P + PS>();   // K-tile kt + 1 landed; kt + 2 (with scales) and kt + 3 may stay in flight
-            wait_lds();
-            ring_barrier();
-            issue(kt + 4);
-            fp8_load<TL>(ring + ((kt + 1) & 3) * SC, sring + ((kt >> 1) & 3) * (BM + BN), a0, a1, b0, b1, arow_i,
-                         brow_i, sh, fa1, fb1, sa1, sb1);
-            fp8_mfma<TL, 0, EARLY, NM - EARLY>(fa0, fb0, sa0, sb0, acc);
-            interleave_hint<NR, NM - EARLY>();
-            __builtin_amdgcn_sched_barrier(0);
-
-            fp8_mfma<TL, 2, 0, EARLY>(fa1, fb1, sa1, sb1, acc);
-            wait_vm<2 * P + PS>();   // K-tile kt + 2 landed; kt + 3 and kt + 4 (with scales) may stay in flight
-            wait_lds();
-            ring_barrier();
-            issue(kt + 5);
-            fp8_load<TL>(ring + ((kt + 2) & 3) * SC, sring + (((kt + 2) >> 1) & 3) * (BM + BN), a0, a1, b0, b1,
-                         arow_i, brow_i, sh, fa0, fb0, sa0, sb0);
-            fp8_mfma<TL, 2, EARLY, NM - EARLY>(fa1, fb1, sa1, sb1, acc);
-            interleave_hint<NR, NM - EARLY>();
-            __builtin_amdgcn_sched_barrier(0);
+        for (int kt = 0; kt < nk; kt += 2) {
+            half_step(std::integral_constant<int, 0>{}, kbase + kt, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, acc, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
         }
-        // last pair: K-tile nk - 2 in set 0, nk - 1 still to read
-        fp8_mfma<TL, 0, 0, EARLY>(fa0, fb0, sa0, sb0, acc);
-        wait_vm<0>();
-        ring_barrier();
-        fp8_load<TL>(ring + ((nk - 1) & 3) * SC, sring + (((nk - 2) >> 1) & 3) * (BM + BN), a0, a1, b0, b1, arow_i,
-                     brow_i, sh, fa1, fb1, sa1, sb1);
-        fp8_mfma<TL, 0, EARLY, NM - EARLY>(fa0, fb0, sa0, sb0, acc);
-        interleave_hint<NR, NM - EARLY>();
-        __builtin_amdgcn_sched_barrier(0);
-        fp8_mfma<TL, 2, 0, NM>(fa1, fb1, sa1, sb1, acc);
-
-        // next tile's first K-tiles go out before this tile's epilogue
-        const TileCoord cur = c;
-        const int next = tile + G;
-        wait_lds();
-        ring_barrier();   // every wave is past its last fragment and scale read
-        if (next < total) {
-            setup(next);
-            issue(0);
-            issue(1);
-            issue(2);
-            issue(3);
-        }
-        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, cur, wm, wn);
+        // set 0 now holds K-tile 0 of the next tile (or unused data after the last)
+        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, cur, wm, wn);
         if (next >= total) break;
         tile = next;
+        cur = nxt;
+        kbase += nk;
+        next = tile + G;
+        if (next < total) nxt = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
     }
+    wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
 }
 
 // ============================================================================ launchers
@@ -663,7 +694,7 @@ hipError_t launch_fp8_pipe_tile(const uint8_t* A, const uint8_t* As, const uint8
                                 const int32_t* host_counts, hipStream_t s) {
     const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
     hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs, C, Cs,
-                       offsets, E, N, K, ldc);
+                       offsets, E, N, K, ldc, R);
     return hipGetLastError();
 }
 

@@ -20,15 +20,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// float32 -> bfloat16, round to nearest even (inputs here are finite).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16, round to nearest even.  The conversion is the
+// hardware's (v_cvt_pk_bf16_f32), checked equal to the integer rounding
+// (u + 0x7FFF + bit 16) >> 16 over every finite float32 input on gfx950.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Orderable routing key: larger key <=> larger logit, then lower expert index.

@@ -70,8 +70,9 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
                             const int32_t* offsets, int R, int E, int N, int K, int ldc,
                             const int32_t* host_counts, hipStream_t s);
 
-// Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K.
-// epi 0: bf16 C [.., ldc];  epi 1: SwiGLU then MXFP8 C codes [.., ldc] + scales Cs [.., ldc / 32].
+// Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K,
+// scales stored [K/128][rows][4] (A: R rows; B: per expert, N rows).
+// epi 0: bf16 C [.., ldc];  epi 1: SwiGLU then MXFP8 C codes [.., ldc] + scales Cs [ldc/128][R][4].
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
                            const int32_t* host_counts, hipStream_t s);

@@ -5,7 +5,10 @@
 // transposed.  For MXFP8 the packed rows are quantised in blocks of 32 along
 // K with one E8M0 scale each (OCP MX v1.0), the forward weight cache of the
 // report ("Section 24: Conclusion", 24.3, two MXFP8 weight caches; only the
-// K-major forward one is needed here).
+// K-major forward one is needed here).  Scales are stored [E][K/128][N][4]:
+// the four scales of a 128-wide K slice of row n form one dword, and the
+// dwords of consecutive rows are adjacent, so the GEMM loads a slice's scales
+// for a block of rows as one contiguous run.
 //
 // One workgroup moves a 32 (K) x 64 (N) tile through LDS: reads are
 // coalesced along the source rows (N), writes along the packed rows (K).
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const TIn* __restrict__ wg, c
                 for (int b = 0; b < 4; ++b) word |= e4m3_encode(tile[4 * w + b][nn] * inv) << (8 * b);
                 reinterpret_cast<uint32_t*>(q)[w] = word;
             }
-            scales[(row_base + n0 + nn) * (K / 32) + k0 / 32] = (uint8_t)(se + 127);
+            scales[(((size_t)e * (K / 128) + k0 / 128) * N + n0 + nn) * 4 + (k0 / 32) % 4] = (uint8_t)(se + 127);
         }
     } else {
         for (int i = tid; i < 32 * 64; i += 256) {

@@ -33,6 +33,13 @@ def _f64(t):
     return _np(t).astype(np.float64)
 
 
+def scales_rowmajor(xs):
+    """MXFP8 scales from the library's slice-major [cols/128][rows][4] layout to
+    [rows][cols/32] (the oracle's)."""
+    S, R, _ = xs.shape
+    return xs.transpose(1, 0, 2).reshape(R, 4 * S)
+
+
 def check_y(act, out, ref, what="y"):
     kind, tol = Y_TOL[act]
     err = np.max(np.abs(out - ref))
@@ -117,7 +124,7 @@ def test_stages_against_oracle(name):
     if w.act == "mxfp8":
         xq_ref, xs_ref = O.dispatch(x64, pos, "mxfp8")
         assert np.array_equal(_np(xe), xq_ref), "MXFP8 codes"
-        assert np.array_equal(_np(xs), xs_ref), "MXFP8 scales"
+        assert np.array_equal(scales_rowmajor(_np(xs)), xs_ref), "MXFP8 scales"
         xe_vals = MX.dequantize(xq_ref, xs_ref, axis=1)
     else:
         xe_ref = O.dispatch(x64, pos, w.act)
@@ -365,8 +372,9 @@ def test_packed_weight_layout(act):
         o4 = o3 + al(n1 // 32)
         w1 = buf[o1:o1 + n1].reshape(E, 2 * H, d)
         w2 = buf[o2:o2 + n2].reshape(E, d, H)
-        s1 = buf[o3:o3 + n1 // 32].reshape(E, 2 * H, d // 32)
-        s2 = buf[o4:o4 + n2 // 32].reshape(E, d, H // 32)
+        # slice-major [E][K/128][N][4] -> [E][N][K/32]
+        s1 = buf[o3:o3 + n1 // 32].reshape(E, d // 128, 2 * H, 4).transpose(0, 2, 1, 3).reshape(E, 2 * H, d // 32)
+        s2 = buf[o4:o4 + n2 // 32].reshape(E, H // 128, d, 4).transpose(0, 2, 1, 3).reshape(E, d, H // 32)
         gq, uq = _unpack_w1(w1, E, d, H)
         gs, us = _unpack_w1(s1, E, d // 32, H)
         for e in range(E):
