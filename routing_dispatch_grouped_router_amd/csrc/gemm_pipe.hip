@@ -152,57 +152,19 @@ __device__ __forceinline__ TileCoord tile_coord(int tile, int NT, const int* s_t
     return c;
 }
 
-// Per-lane DMA state: global bases (wave-uniform), this lane's byte offsets of
-// K-tile 0, and the LDS ring.  A K-tile is 64 bytes of every row; rows past the
-// tile's valid range re-read the last valid row (their results are never
-// stored).  issue(kt) always starts the same number of loads, so every vmcnt
-// wait below is a constant: for kt past the last K-tile the source is clamped
-// to the last one and the stage written is one no later read uses.
-template <class TL>
-struct Ring {
-    const void* Ag;
-    const void* Bg;
-    uint32_t offA[TL::A_DMA], offB[TL::B_DMA];
-    uint32_t ring_lds;
-    int nk, wave, drow;
-    uint32_t dchunk;
-
-    __device__ __forceinline__ void init(const void* A, uint32_t ring_addr, int K_tiles) {
-        const int lane = threadIdx.x & 63;
-        wave = threadIdx.x >> 6;
-        Ag = A;
-        ring_lds = ring_addr;
-        nk = K_tiles;
-        drow = lane >> 2;
-        dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
-    }
-
-    // row_bytes: bytes of one A / B row (the K extent)
-    __device__ __forceinline__ void setup(const TileCoord& c, const void* Be, int N, uint32_t row_bytes) {
-        Bg = Be;
-#pragma unroll
-        for (int i = 0; i < TL::A_DMA; ++i) {
-            const int r = 16 * (wave * TL::A_DMA + i) + drow;
-            offA[i] = (uint32_t)(c.row0 + min(r, c.rows - 1)) * row_bytes + dchunk;
-        }
-#pragma unroll
-        for (int i = 0; i < TL::B_DMA; ++i) {
-            const int r = 16 * (wave * TL::B_DMA + i) + drow;
-            offB[i] = (uint32_t)min(c.n0 + r, N - 1) * row_bytes + dchunk;
-        }
-    }
-
-    __device__ __forceinline__ void issue(int kt) const {
-        const uint32_t ko = (uint32_t)min(kt, nk - 1) * 64u;
-        const uint32_t st = ring_lds + (uint32_t)(kt & 3) * TL::STAGE_CHUNKS * 16u;
-        const uint32_t la = __builtin_amdgcn_readfirstlane(st + wave * TL::A_DMA * 1024u);
-        const uint32_t lb = __builtin_amdgcn_readfirstlane(st + TL::BM * 64u + wave * TL::B_DMA * 1024u);
-#pragma unroll
-        for (int i = 0; i < TL::A_DMA; ++i) dma16(Ag, offA[i] + ko, la + i * 1024u);
-#pragma unroll
-        for (int i = 0; i < TL::B_DMA; ++i) dma16(Bg, offB[i] + ko, lb + i * 1024u);
-    }
+// Source of the K-tiles a loop phase prefetches.  A tile's K loop runs in two
+// phases: while kt + 4 < nk the stream prefetches the current tile (kt = rel),
+// and in the last four K-tiles it prefetches the tile q ahead (q = 1, or 2
+// when a tile has only two K-tiles), kt = rel - q nk; past the last tile the
+// current tile's last K-tile stands in (its copy lands in a stage nobody reads
+// again).  The K-tile is kt = rel * mul + add, so the loop bodies need no
+// selects or branches (a branch there would let the compiler move MFMAs away
+// from the loads they are meant to hide).
+struct StreamSrc {
+    TileCoord t;
+    int mul, add;
 };
+
 
 // Output layout.  The MFMAs take the weight fragment as their first operand
 // and the activation fragment as their second, so accumulator (mi, ni) is the
@@ -248,25 +210,6 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
 
 // One ring stage holds 32 K values per row: two 16-wide k-steps; lane l's
 // fragment for k-step s is chunk 2 s + l / 32 of its row.
-template <class TL>
-__device__ __forceinline__ void bf_load(const u32x4* stage, int aoff, int boff, bf16x8 (&fa)[TL::TM],
-                                        bf16x8 (&fb)[TL::TN]) {
-#pragma unroll
-    for (int mi = 0; mi < TL::TM; ++mi) fa[mi] = __builtin_bit_cast(bf16x8, stage[aoff + mi * 128]);
-#pragma unroll
-    for (int ni = 0; ni < TL::TN; ++ni) fb[ni] = __builtin_bit_cast(bf16x8, stage[boff + ni * 128]);
-}
-
-// MFMAs [FIRST, FIRST + COUNT) of the TM x TN block, row-major over (mi, ni).
-template <class TL, int FIRST, int COUNT>
-__device__ __forceinline__ void bf_mfma(const bf16x8 (&fa)[TL::TM], const bf16x8 (&fb)[TL::TN],
-                                        f32x16 (&acc)[TL::TM][TL::TN]) {
-#pragma unroll
-    for (int i = FIRST; i < FIRST + COUNT; ++i) {
-        const int mi = i / TL::TN, ni = i % TL::TN;
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
-    }
-}
 
 // Epilogue of the bf16 kernel.  EPI 0: C = acc as bf16.  EPI 1: columns come
 // in gate/up pairs of 32; C column (pair column)/2 + j = silu(gate_j) * up_j.
@@ -300,6 +243,25 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
     }
 }
 
+// MFMA number i (row-major over (mi, ni)); i is a constant after unrolling.
+template <class TL>
+__device__ __forceinline__ void bf_mfma1(int i, const bf16x8 (&fa)[TL::TM], const bf16x8 (&fb)[TL::TN],
+                                         f32x16 (&acc)[TL::TM][TL::TN]) {
+    const int mi = i / TL::TN, ni = i % TL::TN;
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0);
+}
+
+// The persistent bf16 kernel streams K-tiles without a break at tile
+// boundaries, like the MXFP8 one below: global K-tile g of this workgroup goes
+// through ring stage g % 4, and the DMAs of a tile's last four K-tiles fetch
+// the next tile's first four.  A K-tile holds two k-steps.  k-step 0 (set 0,
+// read during the previous K-tile) multiplies while k-step 1 is read into
+// set 1; then a few MFMAs of set 1, the wait for K-tile g + 1 and the barrier
+// (every wave holds all of K-tile g in registers by then, so its stage is
+// free), and, one per MFMA, the DMAs of K-tile g + 4 and the reads of K-tile
+// g + 1's k-step 0 into set 0.  The epilogue runs between tiles while the
+// next tile's first K-tiles are in flight; its stores count in vmcnt after
+// those DMAs, which only makes later waits wait longer.
 template <class TL, int EPI>   // EPI 0: C = A B (bf16);  1: C = silu(A Bgate) * (A Bup) (bf16, N/2 columns)
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
@@ -307,6 +269,8 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
                            int ldc) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
+    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
+    static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
     __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
@@ -316,25 +280,90 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
     const int total = MT * NT;
     const int G = gridDim.x;
     const uint32_t rowbytes = (uint32_t)K * 2u;
+    const int nk = K / 32;
     int tile = xcd_slot(blockIdx.x, G);
     if (tile >= total) return;
 
-    Ring<TL> rg;
-    rg.init(A, lds_addr(ring), K / 32);
-    const int nk = rg.nk;
-    const int lane = threadIdx.x & 63;
-    const int wm = rg.wave / TL::WN, wn = rg.wave % TL::WN;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ring_lds = lds_addr(ring);
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
     const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
     const int arow = (wm * TL::WROWS + (lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 4;
     const int a0 = arow + ((0 + half) ^ fsw), a1 = arow + ((2 + half) ^ fsw);
     const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
+    const int drow = lane >> 2;
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
 
-    TileCoord c = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets);
-    rg.setup(c, B + (size_t)c.e * N * K, N, rowbytes);
-    rg.issue(0);
-    rg.issue(1);
-    rg.issue(2);
-    rg.issue(3);
+    TileCoord c0 = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
+    if (tile + G < total) c1 = tile_coord<BM, BN>(tile + G, NT, s_tstart, E, offsets);
+    if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
+    int kbase = 0;
+    const int qa = nk >= 4 ? 1 : 2;   // tiles ahead reached by the last four K-tiles' prefetches
+    const int head = max(nk - 4, 0);  // K-tiles whose prefetch stays in the current tile
+
+    // DMA i of global K-tile g (A rows, then B rows) from src.
+    auto dma = [&](const StreamSrc& src, int g, int i) {
+        const TileCoord& t = src.t;
+        const int kt = (g - kbase) * src.mul + src.add;
+        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        if (i < A_DMA) {
+            const int r = 16 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(t.row0 + min(r, t.rows - 1)) * rowbytes + dchunk + (uint32_t)kt * 64u;
+            dma16(A, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+        } else {
+            const int j = i - A_DMA;
+            const int r = 16 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(t.n0 + r, N - 1) * rowbytes + dchunk + (uint32_t)kt * 64u;
+            dma16(B + (size_t)t.e * N * K, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+        }
+    };
+    auto frag = [&](const u32x4* stage, int aoff, int boff, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
+        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
+    };
+
+    // prologue: K-tiles 0..3 of the stream (for two-K-tile tiles, 2 and 3 are the next tile's)
+    {
+        const StreamSrc here{c0, 1, 0};
+        const bool has1 = tile + G < total;
+        const StreamSrc ahead{has1 ? c1 : c0, has1 ? 1 : 0, has1 ? -nk : nk - 1};
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < P; ++i) dma(g < nk ? here : ahead, g, i);
+    }
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    wait_vm<3 * P>();   // K-tile 0 landed; 1, 2 and 3 may stay in flight
+    ring_barrier();
+#pragma unroll
+    for (int i = 0; i < TM + TN; ++i) frag(ring, a0, b0, i, fa0, fb0);
+
+    // One K-tile g: k-step 0 (set 0, read during the previous K-tile) multiplies
+    // while k-step 1 is read into set 1; then a few MFMAs of set 1, the wait for
+    // K-tile g + 1 and the barrier, and, one per MFMA, the DMAs of K-tile g + 4
+    // (from src) and the reads of K-tile g + 1's k-step 0 into set 0.
+    auto ktile = [&](int g, const StreamSrc& src, f32x16 (&acc)[TM][TN]) {
+        const u32x4* stage = ring + (g & 3) * SC;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa0, fb0, acc);
+            frag(stage, a1, b1, i, fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < EARLY; ++i) bf_mfma1<TL>(i, fa1, fb1, acc);
+        wait_vm<2 * P>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
+        wait_lds();         // this wave's reads of K-tile g are complete
+        ring_barrier();
+        const u32x4* nstage = ring + ((g + 1) & 3) * SC;
+#pragma unroll
+        for (int i = 0; i < NM - EARLY; ++i) {
+            bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
+            if (i < P) dma(src, g + 4, i);
+            frag(nstage, a0, b0, i, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
     for (;;) {
         f32x16 acc[TM][TN];
@@ -345,56 +374,22 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-        wait_vm<3 * P>();   // K-tile 0 landed; 1, 2 and 3 may stay in flight
-        ring_barrier();
-        bf_load<TL>(ring, a0, b0, fa0, fb0);
-        // K-tile kt: k-step 0 in set 0 (read during the previous K-tile), k-step 1
-        // read into set 1 while set 0 multiplies; then a few MFMAs of set 1, the
-        // wait for K-tile kt + 1 and the barrier.  Both k-steps of kt are in
-        // registers by then, so its stage takes the DMA of kt + 4, and set 0 of
-        // kt + 1 is read between the remaining MFMAs.
-        for (int kt = 0; kt < nk - 1; ++kt) {
-            bf_load<TL>(ring + (kt & 3) * SC, a1, b1, fa1, fb1);
-            bf_mfma<TL, 0, NM>(fa0, fb0, acc);
-            interleave_hint<TM + TN, NM>();
-            __builtin_amdgcn_sched_barrier(0);
-            bf_mfma<TL, 0, EARLY>(fa1, fb1, acc);
-            wait_vm<2 * P>();   // K-tile kt + 1 landed; kt + 2 and kt + 3 may stay in flight
-            wait_lds();         // this wave's reads of stage kt are complete
-            ring_barrier();
-            rg.issue(kt + 4);
-            bf_load<TL>(ring + ((kt + 1) & 3) * SC, a0, b0, fa0, fb0);
-            bf_mfma<TL, EARLY, NM - EARLY>(fa1, fb1, acc);
-            interleave_hint<TM + TN, NM - EARLY>();
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        bf_load<TL>(ring + ((nk - 1) & 3) * SC, a1, b1, fa1, fb1);
-        bf_mfma<TL, 0, NM>(fa0, fb0, acc);
-        interleave_hint<TM + TN, NM>();
-        __builtin_amdgcn_sched_barrier(0);
-        bf_mfma<TL, 0, NM>(fa1, fb1, acc);
+        const StreamSrc here{c0, 1, 0};
+        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, acc);
+        const bool has = tile + qa * G < total;
+        const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
 
-        // Start the next tile's first four K-tiles before this tile's epilogue:
-        // once every wave is past its last fragment read (and the clamped loads
-        // past the end have landed) the whole ring is free.
-        const TileCoord cur = c;
-        const int next = tile + G;
-        wait_vm<0>();
-        wait_lds();
-        ring_barrier();
-        if (next < total) {
-            c = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
-            rg.setup(c, B + (size_t)c.e * N * K, N, rowbytes);
-            rg.issue(0);
-            rg.issue(1);
-            rg.issue(2);
-            rg.issue(3);
-        }
-        bf_epilogue<TL, EPI>(acc, C, ldc, N, cur, wm, wn);
-        if (next >= total) break;
-        tile = next;
+        // set 0 now holds k-step 0 of the next tile's first K-tile
+        bf_epilogue<TL, EPI>(acc, C, ldc, N, c0, wm, wn);
+        if (tile + G >= total) break;
+        tile += G;
+        c0 = c1;
+        c1 = c2;
+        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
+        kbase += nk;
     }
+    wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
 }
 
 // ============================================================================ MXFP8
@@ -446,6 +441,15 @@ __device__ __forceinline__ void fp8_mfma(const i32x8 (&fa)[TL::TM], const i32x8 
     }
 }
 
+// One accumulator block into VGPRs, at this point of the program: the reads
+// are volatile, so the compiler neither hoists all of them to the start of the
+// epilogue (which would need 256 VGPRs at once) nor reorders them across the
+// stores between blocks.
+__device__ __forceinline__ void acc_read(const f32x16& a, float (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[i]) : "a"(a[i]));
+}
+
 // MFMA number i (row-major over (mi, ni)); i is a constant after unrolling.
 template <class TL>
 __device__ __forceinline__ void fp8_mfma1(int i, const i32x8 (&fa)[TL::TM], const i32x8 (&fb)[TL::TN],
@@ -477,8 +481,7 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
             for (int ni = 0; ni < TL::TN; ++ni) {
                 const int col0 = c.n0 + wn * TL::WCOLS + ni * 32;
                 float v[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = acc[mi][ni][i];
+                acc_read(acc[mi][ni], v);
                 store_bf16_block(static_cast<uint16_t*>(C), (size_t)ldc, (int)grow, valid && col0 < N, col0, v);
                 __builtin_amdgcn_sched_barrier(0);   // one block's values in VGPRs at a time
             }
@@ -486,11 +489,13 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 #pragma unroll
             for (int np = 0; np < TL::TN / 2; ++np) {
                 const int pc = c.n0 + wn * TL::WCOLS + np * 64;
-                float v[16];
+                float v[16], u[16];
+                acc_read(acc[mi][2 * np], v);
+                acc_read(acc[mi][2 * np + 1], u);
                 float amax = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
+                    v[i] = silu_mul_p(v[i], u[i]);
                     amax = fmaxf(amax, fabsf(v[i]));
                 }
                 amax = fmaxf(amax, __shfl_xor(amax, 32));
@@ -568,21 +573,19 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     // row dword, byte = K block within the pair's four
     const int sa_byte = arow_i * 4 + half, sb_byte = (BM + brow_i) * 4 + half;
 
-    TileCoord cur = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets);
-    int next = tile + G;
-    TileCoord nxt = cur;
-    if (next < total) nxt = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
+    TileCoord c0 = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
+    if (tile + G < total) c1 = tile_coord<BM, BN>(tile + G, NT, s_tstart, E, offsets);
+    if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
     int kbase = 0;   // global K-tile index of the current tile's K-tile 0
 
-    // DMA of global K-tile g: K-tile g - kbase of the current tile, or of the
-    // next one past the current tile's end; past the last tile the source is
-    // clamped to the current tile's last K-tile (a stage nobody reads again).
-    // Step i of P + PS: A rows, then B rows, then (g even) the two scale dwords.
-    auto dma = [&](int g, int i) {
-        const int rel = g - kbase;
-        const bool in_next = rel >= nk && next < total;
-        const TileCoord& t = in_next ? nxt : cur;
-        const int kt = in_next ? rel - nk : min(rel, nk - 1);
+    const int qa = nk >= 4 ? 1 : 2;   // tiles ahead reached by the last four K-tiles' prefetches
+    const int head = max(nk - 4, 0);  // K-tiles whose prefetch stays in the current tile (even)
+
+    // DMA step i of global K-tile g from src: A rows, then B rows, then (g
+    // even) the two scale dwords.
+    auto dma = [&](const StreamSrc& src, int g, int i) {
+        const TileCoord& t = src.t;
+        const int kt = (g - kbase) * src.mul + src.add;
         const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
         if (i < A_DMA) {
             const int r = 16 * (wave * A_DMA + i) + drow;
@@ -594,9 +597,10 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
             const uint32_t off = (uint32_t)min(t.n0 + r, N - 1) * (uint32_t)K + dchunk + (uint32_t)kt * 64u;
             dma16(B + (size_t)t.e * N * K, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
         } else {
-            // scale planes [K/128][rows][4]: the pair's dword of each row
+            // scale planes [K/128][rows][4]: the pair's dword of each row (a
+            // stand-in K-tile nk - 1 maps to the last plane too)
             const uint32_t slot = sring_lds + (uint32_t)((g >> 1) & 3) * (BM + BN) * 4u;
-            const uint32_t plane = (uint32_t)(in_next ? kt : min(kt, nk - 2)) >> 1;
+            const uint32_t plane = (uint32_t)kt >> 1;
             if (SR == 64 || slane) {
                 if (i == A_DMA + B_DMA)
                     dma4(As, (plane * (uint32_t)R + (uint32_t)(t.row0 + min(srow, t.rows - 1))) * 4u,
@@ -609,10 +613,10 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     };
 
     // one half-iteration: K-tile g in (fa, fb, sa, sb), g even for ODD == 0;
-    // reads K-tile g + 1 into (ga, gb, ta, tb); DMAs K-tile g + 4.
-    auto half_step = [&](auto odd, int g, f32x16 (&acc)[TM][TN], const i32x8 (&fa)[TM], const i32x8 (&fb)[TN],
-                         const int (&sa)[TM], const int (&sb)[TN], i32x8 (&ga)[TM], i32x8 (&gb)[TN], int (&ta)[TM],
-                         int (&tb)[TN]) {
+    // reads K-tile g + 1 into (ga, gb, ta, tb); DMAs K-tile g + 4 from src.
+    auto half_step = [&](auto odd, int g, const StreamSrc& src, f32x16 (&acc)[TM][TN], const i32x8 (&fa)[TM],
+                         const i32x8 (&fb)[TN], const int (&sa)[TM], const int (&sb)[TN], i32x8 (&ga)[TM],
+                         i32x8 (&gb)[TN], int (&ta)[TM], int (&tb)[TN]) {
         constexpr int ODD = decltype(odd)::value;
         constexpr int ND = P + (ODD == 0 ? PS : 0);     // g + 4 has the parity of g
         constexpr int NB = (1 - ODD) * 2;                // byte offset of K-tile g + 1's scales in its slot
@@ -625,7 +629,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 #pragma unroll
         for (int i = 0; i < NM - EARLY; ++i) {
             fp8_mfma1<TL>(EARLY + i, fa, fb, sa, sb, acc);
-            if (i < ND) dma(g + 4, i);
+            if (i < ND) dma(src, g + 4, i);
             if (i < TM)
                 fp8_frag<TL>(stage, slot, a0 + i * 128, a1 + i * 128, sa_byte + i * 128, ga[i], ta[i]);
             else if (i < TM + TN)
@@ -635,12 +639,17 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         }
     };
 
-    // prologue: K-tiles 0..3 in flight, K-tile 0 read into set 0
+    // prologue: K-tiles 0..3 of the stream (for two-K-tile tiles, 2 and 3 are the next tile's)
+    {
+        const StreamSrc here{c0, 1, 0};
+        const bool has1 = tile + G < total;
+        const StreamSrc ahead{has1 ? c1 : c0, has1 ? 1 : 0, has1 ? -nk : nk - 1};
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int i = 0; i < P + PS; ++i)
-            if (i < P || (g & 1) == 0) dma(g, i);
+            for (int i = 0; i < P + PS; ++i)
+                if (i < P || (g & 1) == 0) dma(g < nk ? here : ahead, g, i);
+    }
     i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
     wait_vm<3 * P + PS>();   // K-tile 0 and its scales landed; 1, 2 (with scales) and 3 may stay in flight
@@ -661,18 +670,30 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        for (int kt = 0; kt < nk; kt += 2) {
-            half_step(std::integral_constant<int, 0>{}, kbase + kt, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
-            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, acc, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
+        // K-tiles go in pairs (kt even: register set 0; kt + 1: set 1), the
+        // pair's scales in slot (kt / 2) % 4
+        const StreamSrc here{c0, 1, 0};
+        for (int kt = 0; kt < head; kt += 2) {
+            half_step(std::integral_constant<int, 0>{}, kbase + kt, here, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, here, acc, fa1, fb1, sa1, sb1, fa0, fb0, sa0,
+                      sb0);
+        }
+        const bool has = tile + qa * G < total;
+        const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
+        for (int kt = head; kt < nk; kt += 2) {
+            half_step(std::integral_constant<int, 0>{}, kbase + kt, ahead, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1,
+                      sb1);
+            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, ahead, acc, fa1, fb1, sa1, sb1, fa0, fb0, sa0,
+                      sb0);
         }
         // set 0 now holds K-tile 0 of the next tile (or unused data after the last)
-        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, cur, wm, wn);
-        if (next >= total) break;
-        tile = next;
-        cur = nxt;
+        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn);
+        if (tile + G >= total) break;
+        tile += G;
+        c0 = c1;
+        c1 = c2;
+        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
         kbase += nk;
-        next = tile + G;
-        if (next < total) nxt = tile_coord<BM, BN>(next, NT, s_tstart, E, offsets);
     }
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
 }
