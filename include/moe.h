@@ -153,8 +153,8 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, flo
  * expert's buffer): xe[pos[t][j]] = x[t] for every slot.
  *   x        : device [T, d]
  *   pos      : device int32 [T, k] from moe_route
- *   xe       : device [R, d] out (MOE_MXFP8: uint8 E4M3 codes)
- *   xe_scale : device uint8 [d/128][R][4] out for MOE_MXFP8, else ignored (may
+ *   xe       : device [R, d] out (MOE_MXFP8: uint8 E4M3 codes), 16-byte aligned
+ *   xe_scale : device uint8 [d/128][R][4], 4-byte aligned, out for MOE_MXFP8, else ignored (may
  *              be NULL): xe_scale[s][r][j] is the E8M0 scale of elements
  *              [128 s + 32 j, 128 s + 32 j + 32) of row r, so the four scales
  *              of a 128-wide slice of a row form one dword and the dwords of

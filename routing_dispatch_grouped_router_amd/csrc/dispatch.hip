@@ -37,6 +37,7 @@ __device__ __forceinline__ int final_pos(int32_t* pos, const int32_t* topk_idx,
     return p;
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restrict__ x,
                                                             int32_t* __restrict__ pos,
                                                             const int32_t* __restrict__ topk_idx,
@@ -47,16 +48,16 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int p[kMaxTopK];
+    int p[KMAX];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
+    for (int j = 0; j < KMAX; ++j)
         if (j < k) p[j] = final_pos(pos, topk_idx, base, row_token, t, j, k, E, lane);
     if (base != nullptr) {
         // all lanes have read the ranks before any lane overwrites them
         __builtin_amdgcn_wave_barrier();
         if (lane < k) {
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j)
+            for (int j = 0; j < KMAX; ++j)
                 if (j == lane) pos[(size_t)t * k + j] = p[j];
         }
     }
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
         for (int g = 0; g < kGroup; ++g)
             if (c0 + 64 * g < row_chunks) v[g] = src[c0 + 64 * g];
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
+        for (int j = 0; j < KMAX; ++j) {
             if (j < k) {
 #pragma unroll
                 for (int g = 0; g < kGroup; ++g)
@@ -79,91 +80,118 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
     }
 }
 
-// MXFP8: each lane quantises 8 bf16 values; 4 adjacent lanes form one block of 32.
-// Scales are stored [d/128][R][4] (the four scales of a 128-wide slice of a
-// row in one dword, rows adjacent), the layout the MXFP8 GEMM loads directly.
+// MXFP8: each lane quantises 16 bf16 values (two 16-byte loads, one 16-byte
+// store of codes); lanes 2b and 2b + 1 form block b of 32 and agree on its
+// maximum with one shuffle.  Scales are stored [d/128][R][4] (the four scales
+// of a 128-wide slice of a row in one dword, rows adjacent), the layout the
+// MXFP8 GEMM loads directly; the even lane of each group of 8 lanes gathers
+// the slice's four scale bytes and writes the dword.
+template <int KMAX>
 __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __restrict__ x,
                                                              int32_t* __restrict__ pos,
                                                              const int32_t* __restrict__ topk_idx,
                                                              const int32_t* __restrict__ base,
                                                              int32_t* __restrict__ row_token,
-                                                             uint2* __restrict__ xq,
-                                                             uint8_t* __restrict__ xs, int T, int d,
+                                                             uint4* __restrict__ xq,
+                                                             uint32_t* __restrict__ xs, int T, int d,
                                                              int E, int k) {
     const size_t R = (size_t)T * k;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int p[kMaxTopK];
+    int p[KMAX];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j)
+    for (int j = 0; j < KMAX; ++j)
         if (j < k) p[j] = final_pos(pos, topk_idx, base, row_token, t, j, k, E, lane);
     if (base != nullptr) {
         __builtin_amdgcn_wave_barrier();
         if (lane < k) {
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j)
+            for (int j = 0; j < KMAX; ++j)
                 if (j == lane) pos[(size_t)t * k + j] = p[j];
         }
     }
-    // d % 128 == 0, so chunks (8 values each) is a multiple of 16 and the four
-    // lanes of a 32-value block are always valid together
-    const int chunks = d / 8;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * chunks;
-    for (int c0 = lane; c0 < chunks; c0 += 64 * kGroup) {
-        u32x4 v[kGroup];
+    // d % 128 == 0: a row is d / 16 lane-slices of 16 values; a group of 8
+    // lanes covers one 128-wide slice, so groups never straddle a row's end
+    const int slices = d / 16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * (d / 8);
+    constexpr int kG = 2;   // lane-slices per lane loaded before any is stored
+    for (int c0 = lane; c0 < slices; c0 += 64 * kG) {
+        u32x4 v[kG][2];
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g)
-            if (c0 + 64 * g < chunks) v[g] = src[c0 + 64 * g];
-#pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
-            const int c = c0 + 64 * g;
-            if (c >= chunks) continue;
-            float f[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f[2 * i] = __uint_as_float(v[g][i] << 16);
-                f[2 * i + 1] = __uint_as_float(v[g][i] & 0xFFFF0000u);
+        for (int g = 0; g < kG; ++g)
+            if (c0 + 64 * g < slices) {
+                v[g][0] = src[2 * (c0 + 64 * g)];
+                v[g][1] = src[2 * (c0 + 64 * g) + 1];
             }
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+            const int c = c0 + 64 * g;
+            if (c >= slices) continue;   // uniform per group of 8 lanes
+            float f[16];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f[8 * h + 2 * i] = __uint_as_float(v[g][h][i] << 16);
+                    f[8 * h + 2 * i + 1] = __uint_as_float(v[g][h][i] & 0xFFFF0000u);
+                }
             float amax = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
             amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
             const int se = mx_shared_exp(amax);
             const float inv = mx_inv_scale(se);
-            const uint2 q = make_uint2(e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
-                                       e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
+            const u32x4 q = {e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                             e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv),
+                             e4m3x4(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv),
+                             e4m3x4(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv)};
+            // scale byte of block c / 2 at position (c / 2) % 4 of slice c / 8's dword
+            uint32_t sw = (uint32_t)(se + 127) << (8 * ((c >> 1) & 3));
+            sw |= __shfl_xor(sw, 2);
+            sw |= __shfl_xor(sw, 4);
 #pragma unroll
-            for (int j = 0; j < kMaxTopK; ++j) {
+            for (int j = 0; j < KMAX; ++j) {
                 if (j < k) {
-                    xq[(size_t)p[j] * chunks + c] = q;
-                    // scale of block b = c / 4 at [b / 4][row][b % 4]
-                    if ((lane & 3) == 0) xs[(((size_t)(c >> 4)) * R + p[j]) * 4 + ((c >> 2) & 3)] = (uint8_t)(se + 127);
+                    reinterpret_cast<u32x4*>(xq)[(size_t)p[j] * (d / 16) + c] = q;
+                    if ((lane & 7) == 0) xs[(size_t)(c >> 3) * R + p[j]] = sw;
                 }
             }
         }
     }
 }
 
+// The per-slot arrays of the kernels are sized by KMAX >= k (a small bound
+// keeps them, and the loops over slots, short).
+template <int KMAX>
+static void launch_dispatch_k(int act, const void* x, int32_t* pos, const int32_t* topk_idx, const int32_t* base,
+                              int32_t* row_token, void* xe, uint8_t* xe_scale, int T, int d, int E, int k,
+                              hipStream_t s) {
+    dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
+    if (act == kMXFP8) {
+        hipLaunchKernelGGL(dispatch_mxfp8_kernel<KMAX>, grid, block, 0, s, static_cast<const uint4*>(x), pos,
+                           topk_idx, base, row_token, static_cast<uint4*>(xe),
+                           reinterpret_cast<uint32_t*>(xe_scale), T, d, E, k);
+    } else {
+        const int row_chunks = d * (act == kF32 ? 4 : 2) / 16;
+        hipLaunchKernelGGL(dispatch_copy_kernel<KMAX>, grid, block, 0, s, static_cast<const uint4*>(x), pos,
+                           topk_idx, base, row_token, static_cast<uint4*>(xe), T, row_chunks, E, k);
+    }
+}
+
 hipError_t launch_dispatch(int act, const void* x, int32_t* pos, const int32_t* topk_idx,
                            const int32_t* base, int32_t* row_token, void* xe, uint8_t* xe_scale,
                            int T, int d, int E, int k, hipStream_t s) {
-    dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
-    if (act == kMXFP8) {
-        hipLaunchKernelGGL(dispatch_mxfp8_kernel, grid, block, 0, s, static_cast<const uint4*>(x), pos,
-                           topk_idx, base, row_token, static_cast<uint2*>(xe), xe_scale, T, d, E, k);
-    } else {
-        const int row_chunks = d * (act == kF32 ? 4 : 2) / 16;
-        hipLaunchKernelGGL(dispatch_copy_kernel, grid, block, 0, s, static_cast<const uint4*>(x), pos,
-                           topk_idx, base, row_token, static_cast<uint4*>(xe), T, row_chunks, E, k);
-    }
+    if (k <= 2) launch_dispatch_k<2>(act, x, pos, topk_idx, base, row_token, xe, xe_scale, T, d, E, k, s);
+    else if (k <= 4) launch_dispatch_k<4>(act, x, pos, topk_idx, base, row_token, xe, xe_scale, T, d, E, k, s);
+    else if (k <= 8) launch_dispatch_k<8>(act, x, pos, topk_idx, base, row_token, xe, xe_scale, T, d, E, k, s);
+    else launch_dispatch_k<kMaxTopK>(act, x, pos, topk_idx, base, row_token, xe, xe_scale, T, d, E, k, s);
     return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------- combine
 
-template <bool kBf16>
+template <bool kBf16, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ ye,
                                                       const float* __restrict__ gate,
                                                       const int32_t* __restrict__ pos,
@@ -172,10 +200,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int p[kMaxTopK];
-    float gt[kMaxTopK];
+    int p[KMAX];
+    float gt[KMAX];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
+    for (int j = 0; j < KMAX; ++j) {
         if (j < k) {
             p[j] = pos[(size_t)t * k + j];
             gt[j] = gate[(size_t)t * k + j];
@@ -191,7 +219,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
 #pragma unroll
             for (int i = 0; i < kN; ++i) acc[g][i] = 0.f;
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
+        for (int j = 0; j < KMAX; ++j) {
             if (j < k) {
                 // the group's rows of slot j are loaded together, then accumulated in slot order
                 u32x4 v[kGroup];
@@ -230,17 +258,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     }
 }
 
-hipError_t launch_combine(int act, const void* ye, const float* gate, const int32_t* pos, void* y,
-                          int T, int d, int k, hipStream_t s) {
+template <int KMAX>
+static void launch_combine_k(int act, const void* ye, const float* gate, const int32_t* pos, void* y, int T,
+                             int d, int k, hipStream_t s) {
     dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock), block(64 * kRowsPerBlock);
     const bool bf = act != kF32;
     const int row_chunks = d * (bf ? 2 : 4) / 16;
     if (bf)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, static_cast<const uint4*>(ye), gate,
+        hipLaunchKernelGGL((combine_kernel<true, KMAX>), grid, block, 0, s, static_cast<const uint4*>(ye), gate,
                            pos, static_cast<uint4*>(y), T, row_chunks, k);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, static_cast<const uint4*>(ye), gate,
+        hipLaunchKernelGGL((combine_kernel<false, KMAX>), grid, block, 0, s, static_cast<const uint4*>(ye), gate,
                            pos, static_cast<uint4*>(y), T, row_chunks, k);
+}
+
+hipError_t launch_combine(int act, const void* ye, const float* gate, const int32_t* pos, void* y,
+                          int T, int d, int k, hipStream_t s) {
+    if (k <= 2) launch_combine_k<2>(act, ye, gate, pos, y, T, d, k, s);
+    else if (k <= 4) launch_combine_k<4>(act, ye, gate, pos, y, T, d, k, s);
+    else if (k <= 8) launch_combine_k<8>(act, ye, gate, pos, y, T, d, k, s);
+    else launch_combine_k<kMaxTopK>(act, ye, gate, pos, y, T, d, k, s);
     return hipGetLastError();
 }
 
