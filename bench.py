@@ -210,6 +210,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(W.ALL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--main-only", action="store_true",
+                    help="skip the comparison measurements (cold cache, host-synchronising path, router "
+                         "statistics), e.g. under a profiler")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB (a known "
                          "byte count that calibrates HBM counters such as FETCH_SIZE / WRITE_SIZE)")
@@ -299,9 +302,10 @@ def main(argv=None):
         "stages": stage_out,
         "host_wall_s": round(wall, 4),
     }
-    result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
-    result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
-    result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
+    if not args.main_only:
+        result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
+        result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
+        result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(result))
