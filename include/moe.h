@@ -72,6 +72,7 @@ extern "C" {
 #define MOE_ERR_WORKSPACE -4   /* ws_bytes smaller than moe_workspace_bytes()      */
 #define MOE_ERR_LAUNCH    -5   /* a kernel launch or HIP runtime call failed       */
 #define MOE_ERR_STATE     -6   /* no profiled forward yet; inconsistent host counts */
+#define MOE_ERR_ARG       -7   /* a setting outside its documented range           */
 
 #define MOE_F32   0
 #define MOE_BF16  1
@@ -173,7 +174,9 @@ int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, vo
  *   packed_w     : from moe_pack_weights
  *   offsets      : device int32 [E+1] from moe_route
  *   ye           : device [R, d] out (float32 for MOE_F32, else bfloat16)
- *   ws           : workspace (holds h) */
+ *   ws           : workspace (holds h)
+ * Every output tile is computed whole by one workgroup in a fixed K order, so
+ * the result does not depend on the grid (moe_set_gemm_grid_cap). */
 int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* xe_scale,
                            const void* packed_w, const int32_t* offsets, void* ye, void* ws,
                            size_t ws_bytes, void* stream);
@@ -225,6 +228,14 @@ int32_t moe_forward_host_sync(const moe_problem* p, const void* x, const void* w
  * Returns MOE_ERR_STATE when no profiled call completed its launches.  Not for
  * use while a graph capture of moe_forward is in progress. */
 int32_t moe_set_profiling(int32_t enable);
+
+/* Caps the persistent grid of the bf16 and MXFP8 grouped GEMMs at `cap`
+ * workgroups (one per compute unit; a multiple of 8 in [8, 256]), for callers
+ * that keep compute units free for concurrent work on another stream; 0
+ * removes the cap.  Process-wide, applies to calls launched afterwards; not
+ * for use while another thread launches.  Returns MOE_ERR_ARG for any other
+ * value. */
+int32_t moe_set_gemm_grid_cap(int32_t cap);
 int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* n);
 
 #ifdef __cplusplus

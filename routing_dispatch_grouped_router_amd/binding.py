@@ -24,7 +24,8 @@ MOE_LOGITS_GIVEN, MOE_IDENTITY_EXPERTS = 1, 2
 # every function the header declares, for the export check
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packed_weight_bytes",
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
-           "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times"]
+           "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times",
+           "moe_set_gemm_grid_cap"]
 
 
 class MoeError(RuntimeError):
@@ -77,6 +78,7 @@ def lib():
         L.moe_forward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.moe_forward_host_sync.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
         L.moe_set_profiling.argtypes = [_I32]
+        L.moe_set_gemm_grid_cap.argtypes = [_I32]
         L.moe_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                        _I32, ctypes.POINTER(_I32)]
         for name in EXPORTS:
@@ -284,6 +286,11 @@ def forward(p: Problem, x, packed=None, w_router=None, logits=None, stream=None,
 
 def set_profiling(enable: bool):
     _check("moe_set_profiling", lib().moe_set_profiling(1 if enable else 0))
+
+
+def set_gemm_grid_cap(cap: int):
+    """Cap the grouped GEMMs' persistent grid at `cap` workgroups (multiple of 8, <= 256; 0 = no cap)."""
+    _check("moe_set_gemm_grid_cap", lib().moe_set_gemm_grid_cap(int(cap)))
 
 
 def kernel_times() -> list[tuple[str, float]]:

@@ -160,7 +160,8 @@ const char* moe_status_string(int32_t status) {
         case MOE_ERR_DTYPE: return "unsupported dtype or flag";
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_LAUNCH: return "kernel launch or HIP runtime call failed";
-        case MOE_ERR_STATE: return "no profiled forward to report";
+        case MOE_ERR_STATE: return "no profiled forward, or inconsistent host counts";
+        case MOE_ERR_ARG: return "setting out of range";
         default: return "unknown status";
     }
 }
@@ -366,6 +367,11 @@ int32_t moe_set_profiling(int32_t enable) {
     g_prof.enabled = enable != 0;
     g_prof.calls = 0;
     return MOE_OK;
+}
+
+int32_t moe_set_gemm_grid_cap(int32_t cap) {
+    if (cap != 0 && cap < 8) return MOE_ERR_ARG;
+    return set_pipe_grid_cap(cap) ? MOE_ERR_ARG : MOE_OK;
 }
 
 int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* n) {

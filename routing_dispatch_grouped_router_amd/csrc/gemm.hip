@@ -106,6 +106,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 
 // ----------------------------------------------------------------------------- launchers
 
+static int g_pipe_grid_cap = 0;   // 0: no cap
+
+int set_pipe_grid_cap(int cap) {
+    if (cap < 0 || cap > 256 || cap % kXcds) return -1;
+    g_pipe_grid_cap = cap;
+    return 0;
+}
+
 int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts) {
     long mt = (long)R / BM + (long)min(E, R);
     if (host_counts) {
@@ -115,7 +123,9 @@ int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32
     const long tiles = mt * ((N + BN - 1) / BN);
     long g = min(tiles, (long)256 * per_cu);
     g = (g + kXcds - 1) / kXcds * kXcds;
-    return (int)max(g, (long)kXcds);
+    g = max(g, (long)kXcds);
+    if (per_cu == 1 && g_pipe_grid_cap) g = min(g, (long)g_pipe_grid_cap);
+    return (int)g;
 }
 
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,

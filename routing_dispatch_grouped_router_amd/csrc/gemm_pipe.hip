@@ -206,6 +206,77 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
     }
 }
 
+// Row-contiguous store of a 32 x 64 bf16 block pair (blocks g and u, columns
+// [pc, pc + 64) of 32 rows starting at global row `row0`; rows at or past
+// `nrows` and blocks at or past column N are skipped).  In the MFMA layout
+// each lane holds one row, so a direct store puts 32 rows into every
+// instruction; instead the pair goes through this wave's LDS buffer `buf`
+// (RR x 8 chunks of 16 bytes, RR = rows per round, 16 or 32) and is read back
+// so that 8 lanes cover one 128-byte row segment: every store instruction
+// then writes whole 128-byte lines of 64 / 8 rows.  Chunk c of buffer row q
+// sits at q * 8 + (c ^ (q & 7)) to spread the writes over the LDS banks.
+// The buffer is private to the wave, so a wait for the wave's own LDS writes
+// (and compiler barriers: lanes read what other lanes wrote) stand in for a
+// workgroup barrier.
+template <int RR>
+__device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, size_t ldc, int row0, int nrows,
+                                                     int pc, int N, const float (&g)[16], const float (&u)[16],
+                                                     u32x4* __restrict__ buf) {
+    static_assert(RR == 16 || RR == 32, "rows per round");
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31, half = lane >> 5;
+    u32x4 ch[4];   // chunks 2 half, 2 half + 1 (block g) and 4 + 2 half, 4 + 2 half + 1 (block u)
+    {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lo[q] = pack_bf16x2(g[4 * q], g[4 * q + 1]);
+            hi[q] = pack_bf16x2(g[4 * q + 2], g[4 * q + 3]);
+        }
+        gather_halves(lo);
+        gather_halves(hi);
+        ch[0] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
+        ch[1] = (u32x4){lo[2], hi[2], lo[3], hi[3]};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lo[q] = pack_bf16x2(u[4 * q], u[4 * q + 1]);
+            hi[q] = pack_bf16x2(u[4 * q + 2], u[4 * q + 3]);
+        }
+        gather_halves(lo);
+        gather_halves(hi);
+        ch[2] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
+        ch[3] = (u32x4){lo[2], hi[2], lo[3], hi[3]};
+    }
+    const int wq = r % RR, wsw = wq & 7;
+    const int c = lane & 7;                  // chunk this lane stores
+    const bool col_ok = pc + 32 * (c >> 2) < N;
+#pragma unroll
+    for (int rho = 0; rho < 32 / RR; ++rho) {
+        if (r / RR == rho) {
+            buf[wq * 8 + ((2 * half) ^ wsw)] = ch[0];
+            buf[wq * 8 + ((2 * half + 1) ^ wsw)] = ch[1];
+            buf[wq * 8 + ((4 + 2 * half) ^ wsw)] = ch[2];
+            buf[wq * 8 + ((5 + 2 * half) ^ wsw)] = ch[3];
+        }
+        asm volatile("" ::: "memory");
+        wait_lds();
+        asm volatile("" ::: "memory");
+        u32x4 o[RR / 8];
+#pragma unroll
+        for (int j = 0; j < RR / 8; ++j) {
+            const int q = 8 * j + (lane >> 3);
+            o[j] = buf[q * 8 + (c ^ (q & 7))];
+        }
+        asm volatile("" ::: "memory");   // the next round's writes stay after these reads
+#pragma unroll
+        for (int j = 0; j < RR / 8; ++j) {
+            const int rr = rho * RR + 8 * j + (lane >> 3);
+            if (rr < nrows && col_ok)
+                *reinterpret_cast<u32x4*>(C + (size_t)(row0 + rr) * ldc + pc + 8 * c) = o[j];
+        }
+    }
+}
+
 // ============================================================================ bf16
 
 // One ring stage holds 32 K values per row: two 16-wide k-steps; lane l's
@@ -215,7 +286,8 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
 // in gate/up pairs of 32; C column (pair column)/2 + j = silu(gate_j) * up_j.
 template <class TL, int EPI>
 __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], uint16_t* __restrict__ C,
-                                            int ldc, int N, const TileCoord& c, int wm, int wn) {
+                                            int ldc, int N, const TileCoord& c, int wm, int wn,
+                                            u32x4* __restrict__ obuf) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
@@ -223,12 +295,16 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
         const bool valid = r < c.rows;
         if (EPI == 0) {
 #pragma unroll
-            for (int ni = 0; ni < TL::TN; ++ni) {
-                const int col0 = c.n0 + wn * TL::WCOLS + ni * 32;
-                float v[16];
+            for (int np = 0; np < TL::TN / 2; ++np) {
+                float g[16], u[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = acc[mi][ni][i];
-                store_bf16_block(C, (size_t)ldc, c.row0 + r, valid && col0 < N, col0, v);
+                for (int i = 0; i < 16; ++i) {
+                    g[i] = acc[mi][2 * np][i];
+                    u[i] = acc[mi][2 * np + 1][i];
+                }
+                const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
+                store_bf16_pair_rows<16>(C, (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS + np * 64,
+                                         N, g, u, obuf);
             }
         } else {
 #pragma unroll
@@ -271,7 +347,9 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
     constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
     constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
     static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
+    constexpr int kObufChunks = EPI == 0 ? 128 : 0;   // per wave: 16 rows x 128 bytes of output
     __shared__ u32x4 ring[TL::STAGES * SC];
+    __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
 
@@ -381,7 +459,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
         for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
 
         // set 0 now holds k-step 0 of the next tile's first K-tile
-        bf_epilogue<TL, EPI>(acc, C, ldc, N, c0, wm, wn);
+        bf_epilogue<TL, EPI>(acc, C, ldc, N, c0, wm, wn, obuf + wave * kObufChunks);
         if (tile + G >= total) break;
         tile += G;
         c0 = c1;
@@ -468,7 +546,7 @@ __device__ __forceinline__ void fp8_mfma1(int i, const i32x8 (&fa)[TL::TM], cons
 template <class TL, int EPI>
 __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], void* __restrict__ C,
                                              uint8_t* __restrict__ Cs, int ldc, int N, int R, const TileCoord& c,
-                                             int wm, int wn) {
+                                             int wm, int wn, u32x4* __restrict__ obuf) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
 #pragma unroll
@@ -478,12 +556,14 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
         const size_t grow = (size_t)(c.row0 + r);
         if (EPI == 0) {
 #pragma unroll
-            for (int ni = 0; ni < TL::TN; ++ni) {
-                const int col0 = c.n0 + wn * TL::WCOLS + ni * 32;
-                float v[16];
-                acc_read(acc[mi][ni], v);
-                store_bf16_block(static_cast<uint16_t*>(C), (size_t)ldc, (int)grow, valid && col0 < N, col0, v);
-                __builtin_amdgcn_sched_barrier(0);   // one block's values in VGPRs at a time
+            for (int np = 0; np < TL::TN / 2; ++np) {
+                float g[16], u[16];
+                acc_read(acc[mi][2 * np], g);
+                acc_read(acc[mi][2 * np + 1], u);
+                const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
+                store_bf16_pair_rows<32>(static_cast<uint16_t*>(C), (size_t)ldc, c.row0 + rb, c.rows - rb,
+                                         c.n0 + wn * TL::WCOLS + np * 64, N, g, u, obuf);
+                __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
         } else {
 #pragma unroll
@@ -542,8 +622,10 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
     constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
     static_assert(NM - EARLY >= P + PS && NM - EARLY >= TM + TN, "one DMA and one fragment per MFMA step");
+    constexpr int kObufChunks = EPI == 0 ? 256 : 0;   // per wave: 32 rows x 128 bytes of output
     __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ uint32_t sring[4 * (BM + BN)];     // four scale slots: A rows then B rows
+    __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
 
@@ -687,7 +769,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
                       sb0);
         }
         // set 0 now holds K-tile 0 of the next tile (or unused data after the last)
-        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn);
+        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks);
         if (tile + G >= total) break;
         tile += G;
         c0 = c1;

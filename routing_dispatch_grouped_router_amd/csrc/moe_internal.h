@@ -62,8 +62,11 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
                         int d, int H, const int32_t* host_counts, hipStream_t s);
 
-// Persistent grid: one workgroup per tile up to per_cu * 256, a multiple of the 8 XCDs.
+// Persistent grid: one workgroup per tile up to per_cu * 256, a multiple of the
+// 8 XCDs; for the pipelined kernels (per_cu 1) at most the cap set by
+// set_pipe_grid_cap (a multiple of 8 up to 256; 0 removes it; -1 if invalid).
 int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts);
+int set_pipe_grid_cap(int cap);
 
 // Pipelined bf16 grouped GEMM (gemm_pipe.hip); epi 1 = SwiGLU epilogue (C has N/2 columns).
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C,

@@ -50,11 +50,13 @@ __device__ __forceinline__ void load8w<float>(const float* p, float (&v)[8]) { l
 template <>
 __device__ __forceinline__ void load8w<uint16_t>(const uint16_t* p, float (&v)[8]) { load8<uint16_t>(p, v); }
 
-// One wave computes 8 tokens x 8 experts at a time; lanes split d in runs of
-// 8 elements.  The 64 partial sums of a lane are reduce-scattered across the
-// wave (halving the value set at each of the 6 butterfly steps: 63 shuffles
-// instead of 6 per value), after which lane l holds the full sum of value l,
-// i.e. token l / 8, expert l % 8.
+// One workgroup of 4 waves computes 8 tokens x 8 experts at a time; wave w
+// takes the w-th quarter of d, its lanes runs of 8 elements of it (so 4x as
+// many waves share the load of x as with one wave per token group).  The 64
+// partial sums of a lane are reduce-scattered across the wave (halving the
+// value set at each of the 6 butterfly steps: 63 shuffles instead of 6 per
+// value), after which lane l holds its wave's sum for token l / 8, expert
+// l % 8; the four waves' sums are added in wave order through LDS.
 constexpr int kRtTok = 8;
 
 template <typename TIn>
@@ -62,16 +64,18 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restric
                                                             const TIn* __restrict__ w,
                                                             float* __restrict__ logits, int T,
                                                             int d, int E) {
+    __shared__ float red[4][64];
     const int lane = threadIdx.x & 63;
-    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int t0 = wave * kRtTok;
-    if (t0 >= T) return;
+    const int wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * kRtTok;
     const bool vec_w = (E & 7) == 0;
+    const int quarter = (d / 8 + 3) / 4 * 8;      // elements per wave, a multiple of 8 (d % 64 == 0)
+    const int k_lo = wave * quarter, k_hi = min(d, k_lo + quarter);
     for (int e0 = 0; e0 < E; e0 += 8) {
         float acc[64];
 #pragma unroll
         for (int i = 0; i < 64; ++i) acc[i] = 0.f;
-        for (int kb = lane * 8; kb < d; kb += 64 * 8) {
+        for (int kb = k_lo + lane * 8; kb < k_hi; kb += 64 * 8) {
             float xv[kRtTok][8];
 #pragma unroll
             for (int a = 0; a < kRtTok; ++a) {
@@ -106,15 +110,20 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restric
                 acc[i] = keep + __shfl_xor(send, m);
             }
         }
-        const int a = lane >> 3, b = lane & 7;
-        if (t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = acc[0];
+        red[wave][lane] = acc[0];
+        __syncthreads();
+        if (wave == 0) {
+            const float sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+            const int a = lane >> 3, b = lane & 7;
+            if (t0 + a < T && e0 + b < E) logits[(size_t)(t0 + a) * E + e0 + b] = sum;
+        }
+        __syncthreads();   // red is rewritten for the next group of experts
     }
 }
 
 hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
                                 int E, hipStream_t s) {
-    int waves = (T + kRtTok - 1) / kRtTok;
-    dim3 grid((waves + 3) / 4), block(256);
+    dim3 grid((T + kRtTok - 1) / kRtTok), block(256);
     if (act == kF32)
         hipLaunchKernelGGL(router_logits_kernel<float>, grid, block, 0, s,
                            static_cast<const float*>(x), static_cast<const float*>(w), logits, T, d, E);

@@ -106,6 +106,13 @@ def test_small_workspace_rejected(lib):
                          None, fake, 16, None) == -4
 
 
+@pytest.mark.parametrize("cap,code", [(0, 0), (8, 0), (256, 0), (64, 0), (-8, -7), (4, -7), (12, -7),
+                                      (264, -7)])
+def test_gemm_grid_cap_range(lib, cap, code):
+    assert lib.moe_set_gemm_grid_cap(cap) == code
+    assert lib.moe_set_gemm_grid_cap(0) == 0
+
+
 def test_kernel_times_without_profiled_forward(lib):
     n = ctypes.c_int32()
     assert lib.moe_set_profiling(0) == 0

@@ -383,3 +383,52 @@ def test_packed_weight_layout(act):
                 q_ref, s_ref = MX.quantize(W.as_f64(src), axis=0)     # blocks along K
                 assert np.array_equal(codes, q_ref.T), "E4M3 codes"
                 assert np.array_equal(scales, s_ref.T), "E8M0 scales"
+
+
+# --------------------------------------------------------------------------- grid cap
+#
+# moe_set_gemm_grid_cap bounds the persistent grid of the bf16 and MXFP8
+# grouped GEMMs.  Each output tile is still computed whole, in the same K
+# order, by whichever workgroup takes it, so capped and uncapped results are
+# bit-identical; with a small cap every workgroup walks many tiles, and rounds
+# end on ragged tails.
+
+CAP_CASES = [
+    # dense single expert, 9 ragged M tiles over 8 workgroups
+    ("bf16_dense_cap8", W.Workload("cap_bf16_dense", T=2200, d=1024, E=1, k=1, H=256, act="bf16",
+                                   router="random", seed=3101), 8),
+    ("bf16_e8_cap40", W.Workload("cap_bf16_e8", T=1500, d=512, E=8, k=2, H=384, act="bf16",
+                                 router="random", seed=3103), 40),
+    ("bf16_sparse_cap16", W.Workload("cap_bf16_sparse", T=1000, d=768, E=64, k=2, H=256, act="bf16",
+                                     router="random", seed=3102, empty_experts=tuple(range(8, 64))), 16),
+    ("mxfp8_dense_cap8", W.Workload("cap_mx_dense", T=2200, d=1024, E=1, k=1, H=512, act="mxfp8",
+                                    router="random", seed=3104, outlier_frac=0.01), 8),
+    ("mxfp8_e16_cap24", W.Workload("cap_mx_e16", T=1200, d=512, E=16, k=4, H=256, act="mxfp8",
+                                   router="zipf", seed=3105), 24),
+]
+
+
+@pytest.fixture
+def grid_cap():
+    yield B.set_gemm_grid_cap
+    B.set_gemm_grid_cap(0)
+
+
+@pytest.mark.parametrize("case,w,cap", CAP_CASES, ids=[c[0] for c in CAP_CASES])
+def test_grid_cap_bitwise_and_oracle(case, w, cap, grid_cap):
+    print(f"[grid cap] {case} cap={cap} {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    ref_out = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    y0 = ref_out["y"].clone()
+    grid_cap(cap)
+    out = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], y0), "capped grid changed y"
+    L = W.as_f64(host["logits"]) if w.router != "learned" else _f64(out["logits"])
+    check_routing(w, out, L)
+    wg, wu, wd = oracle_weights(host)
+    ref = O.forward(W.as_f64(host["x"]), w.E, w.k, w.act, wg, wu, wd, logits=L)
+    check_y(w.act, _f64(out["y"]), ref["y"])
