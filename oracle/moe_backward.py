@@ -1,0 +1,182 @@
+"""Plain CPU oracle of the routed MoE block's backward pass.  TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import or call this module; the product path never does.  It shares no
+code with the HIP library.
+
+The report's pages describe the block's training step only by its parts: the
+dispatch and combine are each other's transposes (a combine's backward moves
+gradient rows to the experts as a dispatch does, a dispatch's backward sums
+them back per token), the expert FFNs run as grouped GEMMs in both directions
+(data gradients with the routed rows grouped by expert, weight gradients
+contracting over each expert's rows), and block forwards are re-executed in
+the backward ("Supercharging Olmo-core ...", "Section 24: Conclusion",
+Evidence 7 (MXFP8 weight gradients: dequantise, then a bf16 grouped GEMM) and
+Evidence 11 (recompute repeats dispatch and combine)).  No formula is printed;
+the gradients below are the chain rule applied to the forward this package's
+``moe_oracle`` defines:
+
+    y[t]  = sum_j g[t, j] ye[pos[t, j]]
+    ye[r] = h[r] Wd[e],  h = silu(a) * b,  a = xe[r] Wg[e],  b = xe[r] Wu[e]
+    g[t, :] = softmax of the k selected logits of token t
+              (the renormalised full softmax: the full denominator cancels)
+
+    dgate[t, j] = dy[t] . ye[pos[t, j]]
+    dye[pos[t, j]] = g[t, j] dy[t]
+    dh = dye Wd^T;  da = dh * b * silu'(a);  db = dh * silu(a)
+    dxe = da Wg^T + db Wu^T
+    dWd[e] = sum over e's rows of h^T dye;  dWg[e] = xe^T da;  dWu[e] = xe^T db
+    dL[t, e_j] = g[t, j] (dgate[t, j] - sum_i g[t, i] dgate[t, i]),  0 for
+                 experts not selected (top-k selection is piecewise constant)
+    dx[t] = sum_j dxe[pos[t, j]]  (+ dL[t] W_r^T for the learned router)
+    dW_r = x^T dL
+
+Storage points mirror the forward's: every activation-sized intermediate that
+the library keeps in memory (dye, the recomputed a and b, dh, da and db, dxe
+and dx) is rounded to the activation storage type where it is stored, while
+weight gradients, router gradients and dgate are float32.  The recomputed a
+and b are rounded to the activation type (the forward never stored them);
+h is recomputed exactly as the forward computed it.  With ``act='f64'`` no
+rounding happens anywhere (used by the finite-difference pins).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import moe_oracle as F
+
+
+def store(v, act: str) -> np.ndarray:
+    """Activation storage of the backward ('f64' keeps float64 exactly)."""
+    if act == "f64":
+        return np.asarray(v, dtype=np.float64)
+    return F.store(v, act)
+
+
+def store_f32(v, act: str) -> np.ndarray:
+    """float32 storage of gradients that are float32 for every activation type."""
+    if act == "f64":
+        return np.asarray(v, dtype=np.float64)
+    return F.round_f32(v)
+
+
+def sigmoid(z) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu_grad(z) -> np.ndarray:
+    """d silu(z) / dz = s (1 + z (1 - s)), s = sigmoid(z)."""
+    s = sigmoid(z)
+    return s * (1.0 + np.asarray(z, np.float64) * (1.0 - s))
+
+
+def forward_f64(x, n_experts: int, k: int, w_gate, w_up, w_down, w_router=None, logits=None) -> dict:
+    """The forward with no rounding at all (routing as ``moe_oracle.route``)."""
+    x = np.asarray(x, dtype=np.float64)
+    if logits is None:
+        logits = x @ np.asarray(w_router, np.float64)
+    logits = np.asarray(logits, dtype=np.float64)
+    idx = F.select_topk(logits, k)
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    g = z / z.sum(axis=1, keepdims=True)
+    counts, offsets, pos, row_token = F.route_metadata(idx, n_experts)
+    T = x.shape[0]
+    d = x.shape[1]
+    xe = np.empty((T * k, d))
+    xe[pos.reshape(-1)] = np.repeat(x, k, axis=0)
+    ye = np.zeros_like(xe)
+    for e in range(n_experts):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            a = xe[lo:hi] @ np.asarray(w_gate[e], np.float64)
+            b = xe[lo:hi] @ np.asarray(w_up[e], np.float64)
+            ye[lo:hi] = (F.silu(a) * b) @ np.asarray(w_down[e], np.float64)
+    y = np.einsum("tk,tkd->td", g, ye[pos.astype(np.int64)])
+    return dict(logits=logits, idx=idx, gate=g, counts=counts, offsets=offsets, pos=pos,
+                row_token=row_token, xe=xe, ye=ye, y=y)
+
+
+def combine_backward(dy, ye, gate, pos, act: str):
+    """dgate[t, j] = dy[t] . ye[pos[t, j]] (float32) and dye[pos[t, j]] = gate[t, j] dy[t]."""
+    dy = np.asarray(dy, dtype=np.float64)
+    ye = np.asarray(ye, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    T, k = pos.shape
+    dgate = store_f32(np.einsum("td,tkd->tk", dy, ye[pos]), act)
+    dye = np.zeros((T * k, dy.shape[1]))
+    dye[pos.reshape(-1)] = store(gate[:, :, None] * dy[:, None, :], act).reshape(T * k, -1)
+    return dgate, dye
+
+
+def router_backward(dgate, gate, idx, n_experts: int, act: str) -> np.ndarray:
+    """dL [T, E] through the softmax over the selected logits; zero elsewhere."""
+    dgate = np.asarray(dgate, dtype=np.float64)
+    gate = np.asarray(gate, dtype=np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    inner = np.sum(gate * dgate, axis=1, keepdims=True)
+    dsel = gate * (dgate - inner)
+    dL = np.zeros((T, n_experts))
+    np.put_along_axis(dL, idx, dsel, axis=1)
+    return store_f32(dL, act)
+
+
+def expert_backward(rows, dye_rows, wg, wu, wd, act: str):
+    """Backward of one expert's SwiGLU FFN on its rows.
+
+    Returns (drows, dwg, dwu, dwd): drows in activation storage, weight
+    gradients float32.  a and b are recomputed from the rows.
+    """
+    h_dt = "f64" if act == "f64" else F.intermediate_dtypes(act)[0]
+    a_exact = rows @ wg
+    b_exact = rows @ wu
+    h = store(F.silu(a_exact) * b_exact, h_dt)      # as the forward stored it
+    a = store(a_exact, act)
+    b = store(b_exact, act)
+    dh = store(dye_rows @ wd.T, act)
+    da = store(dh * b * silu_grad(a), act)
+    db = store(dh * F.silu(a), act)
+    drows = store(da @ wg.T + db @ wu.T, act)
+    return drows, store_f32(rows.T @ da, act), store_f32(rows.T @ db, act), store_f32(h.T @ dye_rows, act)
+
+
+def backward(x, dy, fwd: dict, act: str, w_gate, w_up, w_down, w_router=None) -> dict:
+    """Gradients of sum(y * dy) for the block whose forward is ``fwd``.
+
+    ``fwd`` holds (from ``moe_oracle.forward`` or ``forward_f64``) idx, gate,
+    offsets, pos, xe and ye.  Returns dict(dx [T, d], dlogits [T, E], dw_gate /
+    dw_up [E, d, H], dw_down [E, H, d], dw_router [d, E] or None, dgate, dye).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx, gate, offsets, pos = fwd["idx"], fwd["gate"], fwd["offsets"], np.asarray(fwd["pos"], np.int64)
+    xe, ye = np.asarray(fwd["xe"], np.float64), np.asarray(fwd["ye"], np.float64)
+    E = len(offsets) - 1
+    T, k = pos.shape
+    dgate, dye = combine_backward(dy, ye, gate, pos, act)
+    dL = router_backward(dgate, gate, idx, E, act)
+    d = x.shape[1]
+    H = np.asarray(w_gate[0]).shape[1]
+    dxe = np.zeros_like(xe)
+    dwg = np.zeros((E, d, H))
+    dwu = np.zeros((E, d, H))
+    dwd = np.zeros((E, H, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        wg = np.asarray(w_gate[e], np.float64)
+        wu = np.asarray(w_up[e], np.float64)
+        wd = np.asarray(w_down[e], np.float64)
+        dxe[lo:hi], dwg[e], dwu[e], dwd[e] = expert_backward(xe[lo:hi], dye[lo:hi], wg, wu, wd, act)
+    dx = dxe[pos].sum(axis=1)
+    dwr = None
+    if w_router is not None:
+        wr = np.asarray(w_router, np.float64)
+        dx = dx + dL @ wr.T
+        dwr = store_f32(x.T @ dL, act)
+    return dict(dx=store(dx, act), dlogits=dL, dw_gate=dwg, dw_up=dwu, dw_down=dwd, dw_router=dwr,
+                dgate=dgate, dye=dye)

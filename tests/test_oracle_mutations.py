@@ -8,7 +8,9 @@ the CPU; nothing here touches the HIP library.
 import numpy as np
 import pytest
 
+import tests.test_oracle_backward_pins as PB
 import tests.test_oracle_pins as P
+from oracle import moe_backward as BW
 from oracle import moe_oracle as O
 from oracle import mxfp8 as MX
 
@@ -121,6 +123,50 @@ def _stats_topk_probabilities(logits, counts, k):
 
 _orig_stats = O.router_stats
 
+_orig_expert_backward = BW.expert_backward
+_orig_router_backward = BW.router_backward
+_orig_combine_backward = BW.combine_backward
+
+
+def _silu_grad_sigmoid_only(z):
+    return BW.sigmoid(z)
+
+
+def _expert_bwd_swapped_wgrads(rows, dye_rows, wg, wu, wd, act):
+    drows, dwg, dwu, dwd = _orig_expert_backward(rows, dye_rows, wg, wu, wd, act)
+    return drows, dwu, dwg, dwd
+
+
+def _expert_bwd_dxe_gate_only(rows, dye_rows, wg, wu, wd, act):
+    # the up projection's share of dxe dropped
+    a = rows @ wg
+    b = rows @ wu
+    dh = dye_rows @ wd.T
+    da = dh * b * BW.silu_grad(a)
+    _, dwg, dwu, dwd = _orig_expert_backward(rows, dye_rows, wg, wu, wd, act)
+    return BW.store(da @ wg.T, act), dwg, dwu, dwd
+
+
+def _router_bwd_uncentred(dgate, gate, idx, n_experts, act):
+    dgate = np.asarray(dgate, np.float64)
+    gate = np.asarray(gate, np.float64)
+    idx = np.asarray(idx, np.int64)
+    dL = np.zeros((idx.shape[0], n_experts))
+    np.put_along_axis(dL, idx, gate * dgate, axis=1)
+    return BW.store_f32(dL, act)
+
+
+def _combine_bwd_ungated(dy, ye, gate, pos, act):
+    return _orig_combine_backward(dy, ye, np.ones_like(np.asarray(gate, np.float64)), pos, act)
+
+
+BACKWARD_PINS = [
+    lambda gd: [PB.test_backward_matches_finite_differences(*c, learned) for c in
+                [(5, 4, 4, 2, 3, 11), (4, 4, 5, 1, 3, 13)] for learned in (False, True)],
+    lambda gd: [PB.test_backward_matches_torch_autograd(learned) for learned in (False, True)],
+    lambda gd: PB.test_all_experts_selected_is_softmax_backward(),
+]
+
 ROUTING_PINS = [
     lambda gd: P.test_route_worked_example(gd),
     lambda gd: [P.test_topk_brute_force_with_ties(E, k) for E, k in [(3, 2), (4, 3), (5, 2)]],
@@ -158,6 +204,11 @@ MUTATIONS = [
     ("E4M3 ties rounded away from zero", MX, "e4m3_round", _round_away, MX_PINS),
     ("ceil-based shared exponent", MX, "shared_exponent", _shared_exp_ceil, MX_PINS),
     ("FNUZ decode instead of OCP FN", MX, "e4m3_decode", _decode_fnuz, MX_PINS),
+    ("SiLU gradient taken as the sigmoid", BW, "silu_grad", _silu_grad_sigmoid_only, BACKWARD_PINS),
+    ("gate and up weight gradients swapped", BW, "expert_backward", _expert_bwd_swapped_wgrads, BACKWARD_PINS),
+    ("dxe without the up projection's share", BW, "expert_backward", _expert_bwd_dxe_gate_only, BACKWARD_PINS),
+    ("router gradient without the centring term", BW, "router_backward", _router_bwd_uncentred, BACKWARD_PINS),
+    ("combine backward ignores gates", BW, "combine_backward", _combine_bwd_ungated, BACKWARD_PINS),
 ]
 
 
