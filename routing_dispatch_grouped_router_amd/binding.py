@@ -25,7 +25,8 @@ MOE_LOGITS_GIVEN, MOE_IDENTITY_EXPERTS = 1, 2
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packed_weight_bytes",
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
            "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times",
-           "moe_set_gemm_grid_cap"]
+           "moe_set_gemm_grid_cap", "moe_backward_workspace_bytes", "moe_backward_weight_bytes",
+           "moe_pack_weights_backward", "moe_backward"]
 
 
 class MoeError(RuntimeError):
@@ -79,6 +80,11 @@ def lib():
         L.moe_forward_host_sync.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
         L.moe_set_profiling.argtypes = [_I32]
         L.moe_set_gemm_grid_cap.argtypes = [_I32]
+        L.moe_backward_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
+        L.moe_backward_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
+        L.moe_pack_weights_backward.argtypes = [PP, _P, _P, _P, _P]
+        L.moe_backward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P,
+                                   _P, _SZ, _P]
         L.moe_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                        _I32, ctypes.POINTER(_I32)]
         for name in EXPORTS:
@@ -286,6 +292,62 @@ def forward(p: Problem, x, packed=None, w_router=None, logits=None, stream=None,
 
 def set_profiling(enable: bool):
     _check("moe_set_profiling", lib().moe_set_profiling(1 if enable else 0))
+
+
+def backward_workspace_bytes(p: Problem) -> int:
+    n = _SZ()
+    _check("moe_backward_workspace_bytes", lib().moe_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def backward_weight_bytes(p: Problem) -> int:
+    n = _SZ()
+    _check("moe_backward_weight_bytes", lib().moe_backward_weight_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def pack_weights_backward(p: Problem, w_gate, w_up, stream=None) -> torch.Tensor:
+    """The backward weight cache W1T [E][d][2H] (moe_pack_weights_backward)."""
+    dt = storage_dtype(p.act)
+    E, d, H = p.n_experts, p.d_model, p.d_hidden
+    _expect(w_gate, (E, d, H), dt, "w_gate")
+    _expect(w_up, (E, d, H), dt, "w_up")
+    out = torch.empty(backward_weight_bytes(p), dtype=torch.uint8, device=w_gate.device)
+    _check("moe_pack_weights_backward", lib().moe_pack_weights_backward(
+        ctypes.byref(p), _ptr(w_gate), _ptr(w_up), _ptr(out), _stream(stream)))
+    return out
+
+
+class Backward:
+    """Preallocated gradients and workspace for moe_backward of a Forward's last call."""
+
+    def __init__(self, p: Problem, device):
+        self.p = p
+        T, E, d, H = p.T, p.n_experts, p.d_model, p.d_hidden
+        self.ws = torch.empty(backward_workspace_bytes(p), dtype=torch.uint8, device=device)
+        self.dx = torch.empty((T, d), dtype=storage_dtype(p.act), device=device)
+        self.dlogits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.dw_gate = torch.empty((E, d, H), dtype=torch.float32, device=device)
+        self.dw_up = torch.empty((E, d, H), dtype=torch.float32, device=device)
+        self.dw_down = torch.empty((E, H, d), dtype=torch.float32, device=device)
+        self.dw_router = (None if p.flags & MOE_LOGITS_GIVEN
+                          else torch.empty((d, E), dtype=torch.float32, device=device))
+
+    def __call__(self, fwd: "Forward", dy, w_down, packed, packed_bwd, x=None, w_router=None, stream=None):
+        p = self.p
+        dt = storage_dtype(p.act)
+        _expect(dy, (p.T, p.d_model), dt, "dy")
+        _expect(w_down, (p.n_experts, p.d_hidden, p.d_model), dt, "w_down")
+        if not p.flags & MOE_LOGITS_GIVEN:
+            _expect(x, (p.T, p.d_model), dt, "x")
+            _expect(w_router, (p.d_model, p.n_experts), dt, "w_router")
+        _check("moe_backward", lib().moe_backward(
+            ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(w_down), _ptr(packed), _ptr(packed_bwd),
+            _ptr(fwd.idx), _ptr(fwd.gate), _ptr(fwd.offsets), _ptr(fwd.pos), _ptr(fwd.ws), fwd.ws.numel(),
+            _ptr(self.dx), _ptr(self.dlogits), _ptr(self.dw_gate), _ptr(self.dw_up), _ptr(self.dw_down),
+            _ptr(self.dw_router), _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        return dict(dx=self.dx, dlogits=self.dlogits, dw_gate=self.dw_gate, dw_up=self.dw_up,
+                    dw_down=self.dw_down, dw_router=self.dw_router)
 
 
 def set_gemm_grid_cap(cap: int):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "gemm_pipe.hip", "pack.hip", "api.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "gemm.hip", "gemm_pipe.hip", "pack.hip", "backward.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

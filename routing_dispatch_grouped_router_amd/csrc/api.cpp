@@ -70,6 +70,25 @@ Packed packed_layout(const moe_problem& p) {
     return P;
 }
 
+// Backward workspace: a | b (then da | db) [R][2H], dye (then dxe) [R][d],
+// dh [R][H], dsel [T][k] (router gradient at the selected experts).
+struct BwdLayout {
+    size_t ab, dye, dh, dsel, total;
+};
+
+BwdLayout bwd_layout(const moe_problem& p) {
+    BwdLayout B{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t R = (size_t)p.T * p.top_k, d = p.d_model, H = p.d_hidden, b = act_bytes(p.act_dtype);
+    B.ab = take(R * 2 * H * b);
+    B.dye = take(R * d * b);
+    B.dh = take(R * H * b);
+    B.dsel = take((size_t)p.T * p.top_k * 4);
+    B.total = off;
+    return B;
+}
+
 int32_t check_problem(const moe_problem* p) {
     if (p == nullptr) return MOE_ERR_NULL;
     if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16 && p->act_dtype != MOE_MXFP8)
@@ -393,6 +412,89 @@ int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* 
         if (ms) ms[i] = (float)(sum / calls);
         if (names) names[i] = g_prof.names[i];
     }
+    return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------- backward
+
+static int32_t check_backward(const moe_problem* p) {
+    int32_t st = check_problem(p);
+    if (st) return st;
+    if (p->act_dtype == MOE_MXFP8 || (p->flags & MOE_IDENTITY_EXPERTS)) return MOE_ERR_DTYPE;
+    // the data-gradient GEMM over 2H reads rows of 2H activations with 32-bit offsets
+    const long long eb = act_bytes(p->act_dtype);
+    if ((long long)p->T * p->top_k * 2 * p->d_hidden * eb >= (1LL << 32)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+int32_t moe_backward_workspace_bytes(const moe_problem* p, size_t* bytes) {
+    int32_t st = check_backward(p);
+    if (st) return st;
+    if (!bytes) return MOE_ERR_NULL;
+    *bytes = bwd_layout(*p).total;
+    return MOE_OK;
+}
+
+int32_t moe_backward_weight_bytes(const moe_problem* p, size_t* bytes) {
+    int32_t st = check_backward(p);
+    if (st) return st;
+    if (!bytes) return MOE_ERR_NULL;
+    *bytes = align256((size_t)p->n_experts * p->d_model * 2 * p->d_hidden * act_bytes(p->act_dtype));
+    return MOE_OK;
+}
+
+int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up, void* packed_bwd,
+                                  void* stream) {
+    int32_t st = check_backward(p);
+    if (st) return st;
+    if (!w_gate || !w_up || !packed_bwd) return MOE_ERR_NULL;
+    return launched(launch_pack_w1t(p->act_dtype, w_gate, w_up, packed_bwd, p->n_experts, p->d_model, p->d_hidden,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const void* w_router,
+                     const void* w_down, const void* packed_w, const void* packed_bwd, const int32_t* topk_idx,
+                     const float* topk_gate, const int32_t* offsets, const int32_t* pos, const void* fwd_ws,
+                     size_t fwd_ws_bytes, void* dx, float* dlogits, float* dw_gate, float* dw_up, float* dw_down,
+                     float* dw_router, void* ws, size_t ws_bytes, void* stream) {
+    int32_t st = check_backward(p);
+    if (st) return st;
+    const bool given = p->flags & MOE_LOGITS_GIVEN;
+    if (!dy || !w_down || !packed_w || !packed_bwd || !fwd_ws || !dx || !dlogits || !dw_gate || !dw_up ||
+        !dw_down || !ws)
+        return MOE_ERR_NULL;
+    if (!given && (!w_router || !x || !dw_router)) return MOE_ERR_NULL;
+    const Layout L = layout(*p);
+    const BwdLayout BL = bwd_layout(*p);
+    if (fwd_ws_bytes < L.total || ws_bytes < BL.total) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int T = p->T, E = p->n_experts, k = p->top_k, d = p->d_model, H = p->d_hidden;
+    const int R = T * k, act = p->act_dtype;
+    // forward state: the caller's arrays, or the workspace copies moe_forward wrote
+    void* fw = const_cast<void*>(fwd_ws);
+    const int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<const int32_t*>(at(fw, L.idx));
+    const float* gate = topk_gate ? topk_gate : reinterpret_cast<const float*>(at(fw, L.gate));
+    const int32_t* off = offsets ? offsets : reinterpret_cast<const int32_t*>(at(fw, L.offsets));
+    const int32_t* ps = pos ? pos : reinterpret_cast<const int32_t*>(at(fw, L.pos));
+    const void* xe = at(fw, L.xe);
+    const void* h = at(fw, L.h);
+    const void* ye = at(fw, L.ye);
+    void* ab = at(ws, BL.ab);
+    void* dye = at(ws, BL.dye);   // later dxe
+    void* dh = at(ws, BL.dh);
+    float* dsel = reinterpret_cast<float*>(at(ws, BL.dsel));
+    const Packed P = packed_layout(*p);
+    const char* pw = static_cast<const char*>(packed_w);
+
+    if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, T, d, E, k, s)))) return st;
+    if ((st = launched(launch_gemm_plain(act, xe, pw + P.w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
+    if ((st = launched(launch_gemm_plain(act, dye, w_down, dh, off, R, E, H, d, H, s)))) return st;
+    if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) return st;
+    if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;
+    if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) return st;
+    if ((st = launched(launch_gemm_plain(act, ab, packed_bwd, dye, off, R, E, d, 2 * H, d, s)))) return st;
+    if ((st = launched(launch_dx(act, dye, ps, idx, dsel, given ? nullptr : w_router, dx, T, d, E, k, s)))) return st;
+    if (!given && (st = launched(launch_wgrad_router(act, x, dlogits, T, d, E, dw_router, s)))) return st;
     return MOE_OK;
 }
 

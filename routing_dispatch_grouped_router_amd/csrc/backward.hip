@@ -1,0 +1,373 @@
+// Backward pass of the routed block on gfx950 (float32 and bf16 activations).
+//
+// The report treats dispatch and combine as each other's transposes and runs
+// the expert FFN as grouped GEMMs in both directions, with data gradients
+// grouped by expert rows and weight gradients contracting over each expert's
+// rows ("Supercharging Olmo-core ...", "Section 24: Conclusion", Evidence 7
+// and Evidence 11).  The steps and their storage points:
+//
+//   combine backward   dgate[t, j] = dy[t] . ye[pos[t, j]],  dye[pos[t, j]] = g[t, j] dy[t]
+//   router backward    dL[t, e_j] = g_j (dgate_j - sum_i g_i dgate_i), 0 elsewhere
+//                      (the gates are the softmax of the k selected logits)
+//   recompute          a | b = xe W1 (gate/up interleaved as packed), stored
+//   down dgrad         dh = dye W_down^T  (B operand: W_down [E][H][d] as given)
+//   SwiGLU backward    da = dh b silu'(a), db = dh silu(a), written over a | b
+//   up/gate dgrad      dxe = (da | db) W1T  (W1T [E][d][2H], the backward weight cache)
+//   weight gradients   dW_down[e] = h^T dye, dW_gate[e] | dW_up[e] = xe^T (da | db),
+//                      dW_r = x^T dL   (K-grouped: contraction over an expert's rows)
+//   dispatch backward  dx[t] = sum_j dxe[pos[t, j]] + sum_j dL[t, e_j] W_r[:, e_j]
+//
+// Every reduction runs in a fixed order, so results are bitwise reproducible.
+#include <algorithm>
+
+#include "grouped_sched.h"
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kTokPerBlock = 4;   // one wave per token
+
+struct bf16raw {
+    uint16_t v;
+};
+__device__ __forceinline__ float ldv(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ldv(const bf16raw* p, size_t i) { return bf16_to_f32(p[i].v); }
+
+template <bool BF>
+__device__ __forceinline__ void load_chunk(const void* base, size_t chunk, float (&v)[8]) {
+    if (BF) {
+        const u32x4 w = reinterpret_cast<const u32x4*>(base)[chunk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const u32x4 w = reinterpret_cast<const u32x4*>(base)[chunk];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
+    }
+}
+
+template <bool BF>
+__device__ __forceinline__ void store_chunk(void* base, size_t chunk, const float (&v)[8]) {
+    u32x4 w;
+    if (BF) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = __float_as_uint(v[i]);
+    }
+    reinterpret_cast<u32x4*>(base)[chunk] = w;
+}
+
+// Fixed-pattern butterfly: every lane ends with the same sum.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+}  // namespace
+
+// One wave per token: the k dot products dy . ye[pos] (each lane sums its
+// 16-byte chunks in order, then one butterfly), dye rows, the router
+// gradient row dL[t][:] and dsel[t][j] = dL[t][idx[t][j]].
+template <bool BF, int KMAX>
+__global__ __launch_bounds__(64 * kTokPerBlock) void combine_bwd_kernel(
+    const void* __restrict__ dy, const void* __restrict__ ye, const float* __restrict__ gate,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ idx, void* __restrict__ dye,
+    float* __restrict__ dL, float* __restrict__ dsel, int T, int row_chunks, int E, int k) {
+    constexpr int NV = BF ? 8 : 4;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int p[KMAX], ex[KMAX];
+    float g[KMAX], dot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        dot[j] = 0.f;
+        if (j < k) {
+            p[j] = pos[(size_t)t * k + j];
+            ex[j] = idx[(size_t)t * k + j];
+            g[j] = gate[(size_t)t * k + j];
+        }
+    }
+    for (int c = lane; c < row_chunks; c += 64) {
+        float v[8];
+        load_chunk<BF>(dy, (size_t)t * row_chunks + c, v);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j >= k) continue;
+            float w[8], o[8];
+            load_chunk<BF>(ye, (size_t)p[j] * row_chunks + c, w);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                dot[j] = fmaf(v[i], w[i], dot[j]);
+                o[i] = g[j] * v[i];
+            }
+            store_chunk<BF>(dye, (size_t)p[j] * row_chunks + c, o);
+        }
+    }
+    float inner = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) continue;
+        dot[j] = wave_sum(dot[j]);
+        inner = fmaf(g[j], dot[j], inner);
+    }
+    float ds[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (j < k) ds[j] = g[j] * (dot[j] - inner);
+    if (lane < k) {
+        float mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j == lane) mine = ds[j];
+        dsel[(size_t)t * k + lane] = mine;
+    }
+    for (int e = lane; e < E; e += 64) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k && ex[j] == e) v = ds[j];
+        dL[(size_t)t * E + e] = v;
+    }
+}
+
+// da | db over a | b in place.  Columns of ab interleave 32 gate and 32 up
+// columns per 64; thread item = 8 consecutive h of one row.
+template <bool BF>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const void* __restrict__ dh, void* __restrict__ ab,
+                                                         int R, int H) {
+    constexpr int NV = BF ? 8 : 4;
+    const int per_row = H / NV;
+    const size_t items = (size_t)R * per_row;
+    for (size_t it = (size_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (size_t)gridDim.x * blockDim.x) {
+        const int r = (int)(it / per_row);
+        const int h0 = (int)(it - (size_t)r * per_row) * NV;
+        const int ga = 64 * (h0 / 32) + h0 % 32;     // column of gate h0 in a | b
+        float d[8], a[8], b[8];
+        load_chunk<BF>(dh, ((size_t)r * H + h0) / NV, d);
+        load_chunk<BF>(ab, ((size_t)r * 2 * H + ga) / NV, a);
+        load_chunk<BF>(ab, ((size_t)r * 2 * H + ga + 32) / NV, b);
+        float da[8], db[8];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const float s = 1.0f / (1.0f + __expf(-a[i]));
+            da[i] = d[i] * b[i] * (s * (1.0f + a[i] * (1.0f - s)));
+            db[i] = d[i] * (a[i] * s);
+        }
+        store_chunk<BF>(ab, ((size_t)r * 2 * H + ga) / NV, da);
+        store_chunk<BF>(ab, ((size_t)r * 2 * H + ga + 32) / NV, db);
+    }
+}
+
+// Weight gradient of one group: C[m][n] = sum over rows r of the group of
+// A[r][m] B[r][n] (both row-major over r), float32 FMA through LDS, workgroup
+// tile 64 x 64, 16 rows per step, each thread 4 x 4 outputs; rows past the
+// group contribute zero.  Group e = blockIdx.z is [offsets[e], offsets[e+1])
+// (offsets NULL: one group [0, R)).  OMAP 0: C[e][m][n] (ldc N).  OMAP 1: the
+// N axis is a | b interleaved (32 gate, 32 up columns per 64) and column n
+// goes to C (gate) or C2 (up) [e][m][h].
+template <typename TA, typename TB, int OMAP>
+__global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, const TB* __restrict__ B,
+                                                    const int32_t* __restrict__ offsets, int R, int M, int N,
+                                                    float* __restrict__ C, float* __restrict__ C2) {
+    __shared__ float As[16][64 + 4];
+    __shared__ float Bs[16][64 + 4];
+    const int e = blockIdx.z;
+    const int r0 = offsets ? offsets[e] : 0, r1 = offsets ? offsets[e + 1] : R;
+    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int lr = tid >> 4, lc = (tid & 15) * 4;   // loader: row lr of the step, 4 columns from lc
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int rb = r0; rb < r1; rb += 16) {
+        const int r = rb + lr;
+        float va[4], vb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = m0 + lc + q, n = n0 + lc + q;
+            va[q] = (r < r1 && m < M) ? (float)ldv(A, (size_t)r * M + m) : 0.f;
+            vb[q] = (r < r1 && n < N) ? (float)ldv(B, (size_t)r * N + n) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            As[lr][lc + q] = va[q];
+            Bs[lr][lc + q] = vb[q];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty + 16 * i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tx + 16 * j;
+            if (n >= N) continue;
+            if (OMAP == 0) {
+                C[((size_t)e * M + m) * N + n] = acc[i][j];
+            } else {
+                const int Hh = N / 2, h = 32 * (n / 64) + n % 32;
+                float* dst = ((n / 32) & 1) ? C2 : C;
+                dst[((size_t)e * M + m) * Hh + h] = acc[i][j];
+            }
+        }
+    }
+}
+
+// dx[t] = sum_j dxe[pos[t, j]] (slot order) + sum_j dsel[t, j] W_r[:, idx[t, j]]
+// (learned router; W_r [d][E]), one wave per token.
+template <bool BF, int KMAX, typename TW>
+__global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __restrict__ dxe,
+                                                               const int32_t* __restrict__ pos,
+                                                               const int32_t* __restrict__ idx,
+                                                               const float* __restrict__ dsel,
+                                                               const TW* __restrict__ wr, void* __restrict__ dx,
+                                                               int T, int row_chunks, int E, int k) {
+    constexpr int NV = BF ? 8 : 4;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int p[KMAX], ex[KMAX];
+    float ds[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (j < k) {
+            p[j] = pos[(size_t)t * k + j];
+            ex[j] = idx[(size_t)t * k + j];
+            ds[j] = dsel[(size_t)t * k + j];
+        }
+    for (int c = lane; c < row_chunks; c += 64) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j >= k) continue;
+            float w[8];
+            load_chunk<BF>(dxe, (size_t)p[j] * row_chunks + c, w);
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc[i] += w[i];
+        }
+        if (wr) {
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                if (j >= k) continue;
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    acc[i] = fmaf(ds[j], (float)ldv(wr, (size_t)(c * NV + i) * E + ex[j]), acc[i]);
+            }
+        }
+        store_chunk<BF>(dx, (size_t)t * row_chunks + c, acc);
+    }
+}
+
+// ----------------------------------------------------------------------------- launchers
+
+template <int KMAX>
+static void launch_combine_bwd_k(int act, const void* dy, const void* ye, const float* gate, const int32_t* pos,
+                                 const int32_t* idx, void* dye, float* dL, float* dsel, int T, int d, int E, int k,
+                                 hipStream_t s) {
+    dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock), block(64 * kTokPerBlock);
+    if (act == kF32)
+        hipLaunchKernelGGL((combine_bwd_kernel<false, KMAX>), grid, block, 0, s, dy, ye, gate, pos, idx, dye, dL,
+                           dsel, T, d / 4, E, k);
+    else
+        hipLaunchKernelGGL((combine_bwd_kernel<true, KMAX>), grid, block, 0, s, dy, ye, gate, pos, idx, dye, dL,
+                           dsel, T, d / 8, E, k);
+}
+
+hipError_t launch_combine_bwd(int act, const void* dy, const void* ye, const float* gate, const int32_t* pos,
+                              const int32_t* idx, void* dye, float* dL, float* dsel, int T, int d, int E, int k,
+                              hipStream_t s) {
+    if (k <= 2) launch_combine_bwd_k<2>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
+    else if (k <= 4) launch_combine_bwd_k<4>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
+    else if (k <= 8) launch_combine_bwd_k<8>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
+    else launch_combine_bwd_k<kMaxTopK>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(int act, const void* dh, void* ab, int R, int H, hipStream_t s) {
+    const int nv = act == kF32 ? 4 : 8;
+    const size_t items = (size_t)R * (H / nv);
+    const int grid = (int)std::min<size_t>((items + 255) / 256, 256 * 16);
+    if (act == kF32) hipLaunchKernelGGL((swiglu_bwd_kernel<false>), dim3(grid), dim3(256), 0, s, dh, ab, R, H);
+    else hipLaunchKernelGGL((swiglu_bwd_kernel<true>), dim3(grid), dim3(256), 0, s, dh, ab, R, H);
+    return hipGetLastError();
+}
+
+template <typename TA, typename TB, int OMAP>
+static void launch_wgrad_t(const void* A, const void* B, const int32_t* offsets, int G, int R, int M, int N,
+                           float* C, float* C2, hipStream_t s) {
+    dim3 grid((N + 63) / 64, (M + 63) / 64, G), block(256);
+    hipLaunchKernelGGL((wgrad_kernel<TA, TB, OMAP>), grid, block, 0, s, static_cast<const TA*>(A),
+                       static_cast<const TB*>(B), offsets, R, M, N, C, C2);
+}
+
+hipError_t launch_wgrad_down(int act, const void* h, const void* dye, const int32_t* offsets, int E, int R, int H,
+                             int d, float* dw_down, hipStream_t s) {
+    if (act == kF32) launch_wgrad_t<float, float, 0>(h, dye, offsets, E, R, H, d, dw_down, nullptr, s);
+    else launch_wgrad_t<bf16raw, bf16raw, 0>(h, dye, offsets, E, R, H, d, dw_down, nullptr, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_w1(int act, const void* xe, const void* dab, const int32_t* offsets, int E, int R, int d,
+                           int H, float* dw_gate, float* dw_up, hipStream_t s) {
+    if (act == kF32) launch_wgrad_t<float, float, 1>(xe, dab, offsets, E, R, d, 2 * H, dw_gate, dw_up, s);
+    else launch_wgrad_t<bf16raw, bf16raw, 1>(xe, dab, offsets, E, R, d, 2 * H, dw_gate, dw_up, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_router(int act, const void* x, const float* dL, int T, int d, int E, float* dw_router,
+                               hipStream_t s) {
+    if (act == kF32) launch_wgrad_t<float, float, 0>(x, dL, nullptr, 1, T, d, E, dw_router, nullptr, s);
+    else launch_wgrad_t<bf16raw, float, 0>(x, dL, nullptr, 1, T, d, E, dw_router, nullptr, s);
+    return hipGetLastError();
+}
+
+template <int KMAX>
+static void launch_dx_k(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
+                        const void* wr, void* dx, int T, int d, int E, int k, hipStream_t s) {
+    dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock), block(64 * kTokPerBlock);
+    if (act == kF32)
+        hipLaunchKernelGGL((dx_kernel<false, KMAX, float>), grid, block, 0, s, dxe, pos, idx, dsel,
+                           static_cast<const float*>(wr), dx, T, d / 4, E, k);
+    else
+        hipLaunchKernelGGL((dx_kernel<true, KMAX, bf16raw>), grid, block, 0, s, dxe, pos, idx, dsel,
+                           static_cast<const bf16raw*>(wr), dx, T, d / 8, E, k);
+}
+
+hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
+                     const void* w_router, void* dx, int T, int d, int E, int k, hipStream_t s) {
+    if (k <= 2) launch_dx_k<2>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
+    else if (k <= 4) launch_dx_k<4>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
+    else if (k <= 8) launch_dx_k<8>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
+    else launch_dx_k<kMaxTopK>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
+    return hipGetLastError();
+}
+
+}  // namespace moe

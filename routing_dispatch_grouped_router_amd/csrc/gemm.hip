@@ -164,4 +164,15 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
     return hipGetLastError();
 }
 
+hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, const int32_t* offsets, int R, int E,
+                             int N, int K, int ldc, hipStream_t s) {
+    if (act == kBF16)
+        return launch_bf16_pipe(0, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B),
+                                static_cast<uint16_t*>(C), offsets, R, E, N, K, ldc, nullptr, s);
+    dim3 grid(persistent_grid(R, E, N, f32g::BM, f32g::BN, 4, nullptr)), block(f32g::NTHR);
+    hipLaunchKernelGGL(gemm_f32_kernel<0>, grid, block, 0, s, static_cast<const float*>(A),
+                       static_cast<const float*>(B), static_cast<float*>(C), offsets, E, N, K, ldc);
+    return hipGetLastError();
+}
+
 }  // namespace moe

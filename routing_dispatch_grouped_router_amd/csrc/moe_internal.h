@@ -84,4 +84,36 @@ hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const u
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
                        void* w2, uint8_t* s1, uint8_t* s2, int E, int d, int H, hipStream_t s);
 
+// ---------------------------------------------------------------- backward (backward.hip, pack.hip)
+
+// W1T [E][d][2H] from w_gate, w_up [E][d][H] (float32 or bfloat16).
+hipError_t launch_pack_w1t(int act, const void* w_gate, const void* w_up, void* out, int E, int d, int H,
+                           hipStream_t s);
+
+// dye[pos[t][j]] = gate[t][j] dy[t]; dL[T][E] (router gradient through the softmax of
+// the selected logits); dsel[t][j] = dL[t][idx[t][j]].
+hipError_t launch_combine_bwd(int act, const void* dy, const void* ye, const float* gate, const int32_t* pos,
+                              const int32_t* idx, void* dye, float* dL, float* dsel, int T, int d, int E, int k,
+                              hipStream_t s);
+
+// ab [R][2H] (a | b interleaved as packed W1) := da | db from dh [R][H].
+hipError_t launch_swiglu_bwd(int act, const void* dh, void* ab, int R, int H, hipStream_t s);
+
+// Weight gradients (float32 outputs), contraction over each expert's rows.
+hipError_t launch_wgrad_down(int act, const void* h, const void* dye, const int32_t* offsets, int E, int R, int H,
+                             int d, float* dw_down, hipStream_t s);
+hipError_t launch_wgrad_w1(int act, const void* xe, const void* dab, const int32_t* offsets, int E, int R, int d,
+                           int H, float* dw_gate, float* dw_up, hipStream_t s);
+hipError_t launch_wgrad_router(int act, const void* x, const float* dL, int T, int d, int E, float* dw_router,
+                               hipStream_t s);
+
+// dx[t] = sum_j dxe[pos[t][j]] (+ sum_j dsel[t][j] W_r[:, idx[t][j]] when w_router is given).
+hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
+                     const void* w_router, void* dx, int T, int d, int E, int k, hipStream_t s);
+
+// C = A B^T per expert segment, stored as computed (float32 or bfloat16): the
+// grouped GEMM without an epilogue (recompute and data gradients).
+hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, const int32_t* offsets, int R, int E,
+                             int N, int K, int ldc, hipStream_t s);
+
 }  // namespace moe

@@ -12,6 +12,8 @@
 //
 // One workgroup moves a 32 (K) x 64 (N) tile through LDS: reads are
 // coalesced along the source rows (N), writes along the packed rows (K).
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -73,6 +75,38 @@ __global__ __launch_bounds__(256) void pack_kernel(const TIn* __restrict__ wg, c
             else static_cast<uint16_t*>(out)[o] = f32_to_bf16(tile[kk][nn]);   // exact: input is bf16
         }
     }
+}
+
+// Backward weight cache W1T [E][d][2H]: row c holds, for every column n of
+// the packed W1 (32 gate, then 32 up columns per 64), W1[e][n][c], i.e. the
+// gate or up weight of input c and hidden unit 32 (n / 64) + n % 32: the B
+// operand of the grouped GEMM dxe = (da | db) W1T, contraction axis 2H
+// contiguous.  Both the source rows (over h) and the packed rows (over n) are
+// contiguous in runs of 32, so this is a strided copy without a transpose.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_w1t_kernel(const T* __restrict__ wg, const T* __restrict__ wu,
+                                                       T* __restrict__ out, int E, int d, int H) {
+    const size_t n_all = (size_t)E * d * 2 * H;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_all; i += (size_t)gridDim.x * blockDim.x) {
+        const int n = (int)(i % (2 * H));
+        const size_t ec = i / (2 * H);      // e * d + c
+        const int h = 32 * (n >> 6) + (n & 31);
+        out[i] = (((n >> 5) & 1) ? wu : wg)[ec * H + h];
+    }
+}
+
+hipError_t launch_pack_w1t(int act, const void* w_gate, const void* w_up, void* out, int E, int d, int H,
+                           hipStream_t s) {
+    const size_t n_all = (size_t)E * d * 2 * H;
+    const int grid = (int)std::min<size_t>((n_all + 255) / 256, 256 * 64);
+    if (act == kF32)
+        hipLaunchKernelGGL((pack_w1t_kernel<float>), dim3(grid), dim3(256), 0, s, static_cast<const float*>(w_gate),
+                           static_cast<const float*>(w_up), static_cast<float*>(out), E, d, H);
+    else
+        hipLaunchKernelGGL((pack_w1t_kernel<uint16_t>), dim3(grid), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+                           static_cast<uint16_t*>(out), E, d, H);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,

@@ -134,3 +134,33 @@ def test_workspace_and_packed_sizes(lib, name):
     if w.act == "mxfp8":
         want = want * 33 // 32          # one E8M0 byte per 32 elements
     assert want <= pw < want + 4 * 256
+
+
+def test_backward_rejects_mxfp8_nulls_and_small_workspaces(lib):
+    n = ctypes.c_size_t()
+    pm = _prob(act="mxfp8", d=128, H=128)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(pm), ctypes.byref(n)) == -3
+    p = _prob(logits_given=True)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
+    bws = n.value
+    assert bws >= p.T * p.top_k * (2 * p.d_hidden + p.d_model + p.d_hidden) * 2
+    assert lib.moe_backward_weight_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value >= p.n_experts * p.d_model * 2 * p.d_hidden * 2
+    fws = B.workspace_bytes(p)
+    fake = ctypes.c_void_p(0x1000)
+    args = [ctypes.byref(p), fake, None, None, fake, fake, fake, None, None, None, None, fake, fws,
+            fake, fake, fake, fake, fake, None, fake, bws, None]
+    bad_fwd = list(args)
+    bad_fwd[12] = fws - 1
+    assert lib.moe_backward(*bad_fwd) == -4
+    bad_ws = list(args)
+    bad_ws[20] = bws - 1
+    assert lib.moe_backward(*bad_ws) == -4
+    no_dy = list(args)
+    no_dy[1] = None
+    assert lib.moe_backward(*no_dy) == -1
+    # learned router: x, w_router and dw_router are required
+    pl = _prob()
+    args_l = list(args)
+    args_l[0] = ctypes.byref(pl)
+    assert lib.moe_backward(*args_l) == -1

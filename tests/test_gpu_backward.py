@@ -1,0 +1,95 @@
+"""Parity of the block backward (moe_backward) against the CPU oracle (marked gpu).
+
+The oracle is fed the routing the GPU forward produced (for the learned
+router, the float32 logits it computed; routing itself is checked bit-exact
+by the forward tests) and differentiates its own forward of that routing.
+
+Bars (normwise relative = max|got - ref| / max|ref|, per output): float32
+1e-5; bf16 2e-2 (as the forward outputs).  Two calls are bitwise equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_backward as BW
+from oracle import moe_oracle as O
+from routing_dispatch_grouped_router_amd import binding as B
+from routing_dispatch_grouped_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def _f64(t):
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def _check(name, got, ref, act):
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref))
+    if scale == 0:
+        assert err == 0, f"{name}: expected zeros, max |got| {err:.3e}"
+        return
+    assert err / scale <= TOL[act], f"{name}: normwise rel err {err / scale:.3e} > {TOL[act]}"
+
+
+CASES = [
+    W.Workload("bwd_f32_learned", T=333, d=192, E=12, k=3, H=128, act="f32", router="learned", seed=4001),
+    W.Workload("bwd_f32_random", T=300, d=128, E=8, k=2, H=192, act="f32", router="random", seed=4002),
+    W.Workload("bwd_f32_dense_E1", T=257, d=128, E=1, k=1, H=320, act="f32", router="random", seed=4003),
+    W.Workload("bwd_bf16_learned", T=1000, d=256, E=8, k=4, H=192, act="bf16", router="learned", seed=4004),
+    W.Workload("bwd_bf16_e32_random", T=777, d=384, E=32, k=4, H=320, act="bf16", router="random", seed=4005),
+    W.Workload("bwd_bf16_zipf", T=1500, d=256, E=16, k=8, H=128, act="bf16", router="zipf", seed=4006),
+    W.Workload("bwd_bf16_empty", T=200, d=128, E=8, k=2, H=128, act="bf16", router="random", seed=4007,
+               empty_experts=(0, 3, 7)),
+    W.Workload("bwd_bf16_k_eq_E", T=130, d=64, E=4, k=4, H=128, act="bf16", router="random", seed=4008),
+    W.Workload("bwd_bf16_tk_lt_E", T=3, d=64, E=16, k=2, H=64, act="bf16", router="random", seed=4009),
+]
+
+
+def _run(w):
+    host = W.make_inputs(w)
+    dev = {k: (None if v is None else v.to(DEV)) for k, v in host.items()}
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned")
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    packed_bwd = B.pack_weights_backward(p, dev["w_gate"], dev["w_up"])
+    fwd = B.Forward(p, DEV)
+    fwd(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    rng = np.random.default_rng(w.seed + 17)
+    dy_host = torch.from_numpy(rng.standard_normal((w.T, w.d)).astype(np.float32)).to(B.storage_dtype(w.act))
+    dy = dy_host.to(DEV)
+    bwd = B.Backward(p, DEV)
+    outs = []
+    for _ in range(2):
+        g = bwd(fwd, dy, dev["w_down"], packed, packed_bwd, x=dev["x"], w_router=dev["w_router"])
+        torch.cuda.synchronize()
+        outs.append({k: (None if v is None else v.clone()) for k, v in g.items()})
+    return host, fwd, dy_host, outs
+
+
+@pytest.mark.parametrize("w", CASES, ids=[c.name for c in CASES])
+def test_backward_against_oracle(w):
+    print(f"[backward] {w.describe()}", flush=True)
+    host, fwd, dy_host, outs = _run(w)
+    for k in outs[0]:
+        if outs[0][k] is not None:
+            assert torch.equal(outs[0][k], outs[1][k]), f"{k} differs between two calls"
+    g = outs[0]
+    logits = _f64(fwd.logits)
+    wg, wu, wd = (W.as_f64(host[n]) for n in ("w_gate", "w_up", "w_down"))
+    x = W.as_f64(host["x"])
+    fo = O.forward(x, w.E, w.k, w.act, wg, wu, wd, logits=logits)
+    assert np.array_equal(fo["idx"], fwd.idx.cpu().numpy()), "routing differs from the oracle's"
+    wr = W.as_f64(host["w_router"]) if w.router == "learned" else None
+    ref = BW.backward(x, W.as_f64(dy_host), fo, w.act, wg, wu, wd, w_router=wr)
+    for name in ("dx", "dlogits", "dw_gate", "dw_up", "dw_down"):
+        _check(name, _f64(g[name]), ref[name], w.act)
+    if wr is not None:
+        _check("dw_router", _f64(g["dw_router"]), ref["dw_router"], w.act)
+    if w.E == 1:
+        assert torch.count_nonzero(g["dlogits"]) == 0
