@@ -203,6 +203,35 @@ def router_stats_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device:
             "mean_router_prob_min_max": [float(st[:E].min()), float(st[:E].max())]}
 
 
+def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_device: float) -> dict:
+    """moe_backward of the last forward (f's workspace), timed like the main loop.
+
+    Useful FLOPs: the gate/up recompute 4 R d H, the data gradients 2 R d H
+    (down) + 4 R d H (gate/up), the weight gradients 2 R d H + 4 R d H, plus the
+    router's 2 T d E twice for the learned router."""
+    packed_bwd = B.pack_weights_backward(p, d_in["w_gate"], d_in["w_up"])
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 17)
+    dy = torch.randn((w.T, w.d), generator=g).to(B.storage_dtype(w.act)).to(dev)
+    bwd = B.Backward(p, dev)
+    run = lambda: bwd(f, dy, d_in["w_down"], packed, packed_bwd, w_router=d_in["w_router"])
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    flops = 16.0 * w.R * w.d * w.H + (2 * 2.0 * w.T * w.d * w.E if w.router == "learned" else 0.0)
+    peak = 2500.0 if w.act == "bf16" else 157.3
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "useful_tflops": round(tf, 2), "frac_of_peak": round(tf / peak, 4),
+            "peak_tflops": peak, "vs_forward": round(ms / ms_device, 3)}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +335,8 @@ def main(argv=None):
         result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
         result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
         result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
+        if w.act != "mxfp8":
+            result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(result))

@@ -255,7 +255,8 @@ int32_t moe_set_gemm_grid_cap(int32_t cap);
  *   dw_down[e] = h^T dye,  dw_gate[e] = xe^T da,  dw_up[e] = xe^T db
  *                                              (sums over expert e's rows)
  *   dx[t] = sum_j dxe[pos[t,j]]  (+ dlogits[t] W_r^T for the learned router)
- *   dw_router = x^T dlogits                     (learned router only)
+ *   dw_router = x^T dlogits                     (learned router only; summed
+ *               per expert over the dispatched rows xe, which hold x)
  *
  * Storage: dye, a, b, dh, da, db, dxe and dx in the activation type (bf16
  * rounded to nearest even where stored), dlogits and all weight gradients
@@ -271,8 +272,6 @@ int32_t moe_set_gemm_grid_cap(int32_t cap);
  *
  * moe_backward arguments (device pointers unless noted):
  *   dy          [T, d] activation type
- *   x           [T, d] the forward input (learned router only; may be NULL
- *               with MOE_LOGITS_GIVEN)
  *   w_router    [d, E] activation type (learned router only)
  *   w_down      [E, H, d] as given to moe_pack_weights
  *   packed_w    the forward weight cache (moe_pack_weights)
@@ -295,7 +294,7 @@ int32_t moe_backward_workspace_bytes(const moe_problem* p, size_t* bytes);
 int32_t moe_backward_weight_bytes(const moe_problem* p, size_t* bytes);
 int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up, void* packed_bwd,
                                   void* stream);
-int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const void* w_router,
+int32_t moe_backward(const moe_problem* p, const void* dy, const void* w_router,
                      const void* w_down, const void* packed_w, const void* packed_bwd, const int32_t* topk_idx,
                      const float* topk_gate, const int32_t* offsets, const int32_t* pos, const void* fwd_ws,
                      size_t fwd_ws_bytes, void* dx, float* dlogits, float* dw_gate, float* dw_up, float* dw_down,

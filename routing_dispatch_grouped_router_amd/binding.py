@@ -83,7 +83,7 @@ def lib():
         L.moe_backward_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_backward_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_pack_weights_backward.argtypes = [PP, _P, _P, _P, _P]
-        L.moe_backward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P,
+        L.moe_backward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P,
                                    _P, _SZ, _P]
         L.moe_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
                                        _I32, ctypes.POINTER(_I32)]
@@ -333,16 +333,15 @@ class Backward:
         self.dw_router = (None if p.flags & MOE_LOGITS_GIVEN
                           else torch.empty((d, E), dtype=torch.float32, device=device))
 
-    def __call__(self, fwd: "Forward", dy, w_down, packed, packed_bwd, x=None, w_router=None, stream=None):
+    def __call__(self, fwd: "Forward", dy, w_down, packed, packed_bwd, w_router=None, stream=None):
         p = self.p
         dt = storage_dtype(p.act)
         _expect(dy, (p.T, p.d_model), dt, "dy")
         _expect(w_down, (p.n_experts, p.d_hidden, p.d_model), dt, "w_down")
         if not p.flags & MOE_LOGITS_GIVEN:
-            _expect(x, (p.T, p.d_model), dt, "x")
             _expect(w_router, (p.d_model, p.n_experts), dt, "w_router")
         _check("moe_backward", lib().moe_backward(
-            ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(w_down), _ptr(packed), _ptr(packed_bwd),
+            ctypes.byref(p), _ptr(dy), _ptr(w_router), _ptr(w_down), _ptr(packed), _ptr(packed_bwd),
             _ptr(fwd.idx), _ptr(fwd.gate), _ptr(fwd.offsets), _ptr(fwd.pos), _ptr(fwd.ws), fwd.ws.numel(),
             _ptr(self.dx), _ptr(self.dlogits), _ptr(self.dw_gate), _ptr(self.dw_up), _ptr(self.dw_down),
             _ptr(self.dw_router), _ptr(self.ws), self.ws.numel(), _stream(stream)))

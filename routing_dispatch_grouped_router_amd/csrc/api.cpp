@@ -71,10 +71,18 @@ Packed packed_layout(const moe_problem& p) {
 }
 
 // Backward workspace: a | b (then da | db) [R][2H], dye (then dxe) [R][d],
-// dh [R][H], dsel [T][k] (router gradient at the selected experts).
+// dh [R][H], dsel [T][k] (router gradient at the selected experts); for bf16
+// also the padded segment starts poff [E+1] and two transposed operands of the
+// weight-gradient GEMMs, [max(H, d)][Rp] (h, then xe) and [max(d, 2H)][Rp]
+// (dye, then da | db), Rp = T k + 40 E rounded up to 32 (each segment adds at
+// most 7 lead and 31 tail columns); for the learned router W_r^T [E][d] and
+// the per-256-token partials of dW_r.
 struct BwdLayout {
-    size_t ab, dye, dh, dsel, total;
+    size_t ab, dye, dh, dsel, poff, rowdst, ta, tb, wrt, srow, rpart, total;
+    int Rp;
 };
+
+int bwd_rp(const moe_problem& p) { return (p.T * p.top_k + 40 * p.n_experts + 31) / 32 * 32; }
 
 BwdLayout bwd_layout(const moe_problem& p) {
     BwdLayout B{};
@@ -85,6 +93,16 @@ BwdLayout bwd_layout(const moe_problem& p) {
     B.dye = take(R * d * b);
     B.dh = take(R * H * b);
     B.dsel = take((size_t)p.T * p.top_k * 4);
+    const bool bf = p.act_dtype == MOE_BF16;
+    B.Rp = bwd_rp(p);
+    B.poff = take(bf ? ((size_t)p.n_experts + 1) * 4 : 0);
+    B.rowdst = take(bf ? R * 4 : 0);
+    B.ta = take(bf ? std::max(H, d) * (size_t)B.Rp * 2 : 0);
+    B.tb = take(bf ? std::max(d, 2 * H) * (size_t)B.Rp * 2 : 0);
+    const bool learned = !(p.flags & MOE_LOGITS_GIVEN);
+    B.wrt = take(learned ? (size_t)p.n_experts * d * b : 0);
+    B.srow = take(learned ? R * 4 : 0);
+    B.rpart = take(learned ? router_wgrad_part_bytes((int)R, p.n_experts, p.d_model) : 0);
     B.total = off;
     return B;
 }
@@ -424,6 +442,10 @@ static int32_t check_backward(const moe_problem* p) {
     // the data-gradient GEMM over 2H reads rows of 2H activations with 32-bit offsets
     const long long eb = act_bytes(p->act_dtype);
     if ((long long)p->T * p->top_k * 2 * p->d_hidden * eb >= (1LL << 32)) return MOE_ERR_SHAPE;
+    // the weight-gradient GEMMs read the transposed operands with 32-bit offsets
+    if (p->act_dtype == MOE_BF16 &&
+        (long long)std::max(p->d_model, 2 * p->d_hidden) * bwd_rp(*p) * 2 >= (1LL << 32))
+        return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -452,7 +474,7 @@ int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, cons
                                     static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const void* w_router,
+int32_t moe_backward(const moe_problem* p, const void* dy, const void* w_router,
                      const void* w_down, const void* packed_w, const void* packed_bwd, const int32_t* topk_idx,
                      const float* topk_gate, const int32_t* offsets, const int32_t* pos, const void* fwd_ws,
                      size_t fwd_ws_bytes, void* dx, float* dlogits, float* dw_gate, float* dw_up, float* dw_down,
@@ -463,7 +485,7 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     if (!dy || !w_down || !packed_w || !packed_bwd || !fwd_ws || !dx || !dlogits || !dw_gate || !dw_up ||
         !dw_down || !ws)
         return MOE_ERR_NULL;
-    if (!given && (!w_router || !x || !dw_router)) return MOE_ERR_NULL;
+    if (!given && (!w_router || !dw_router)) return MOE_ERR_NULL;
     const Layout L = layout(*p);
     const BwdLayout BL = bwd_layout(*p);
     if (fwd_ws_bytes < L.total || ws_bytes < BL.total) return MOE_ERR_WORKSPACE;
@@ -489,12 +511,40 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, T, d, E, k, s)))) return st;
     if ((st = launched(launch_gemm_plain(act, xe, pw + P.w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
     if ((st = launched(launch_gemm_plain(act, dye, w_down, dh, off, R, E, H, d, H, s)))) return st;
-    if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) return st;
+    const bool bf = act == MOE_BF16;
+    int32_t* poff = reinterpret_cast<int32_t*>(at(ws, BL.poff));
+    int32_t* rowdst = reinterpret_cast<int32_t*>(at(ws, BL.rowdst));
+    uint16_t* ta = reinterpret_cast<uint16_t*>(at(ws, BL.ta));
+    uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, BL.tb));
+    if (bf) {
+        if ((st = launched(launch_seg_pad(off, E, R, poff, rowdst, s)))) return st;
+        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(h), R, H, off, poff, rowdst, E, BL.Rp, ta, s))))
+            return st;
+        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(dye), R, d, off, poff, rowdst, E, BL.Rp, tb, s))))
+            return st;
+        if ((st = launched(launch_wgrad_mfma(0, ta, tb, poff, E, H, d, BL.Rp, dw_down, nullptr, s)))) return st;
+    } else if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) {
+        return st;
+    }
     if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;
-    if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) return st;
+    if (bf) {
+        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(xe), R, d, off, poff, rowdst, E, BL.Rp, ta, s))))
+            return st;
+        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(ab), R, 2 * H, off, poff, rowdst, E, BL.Rp, tb,
+                                                s))))
+            return st;
+        if ((st = launched(launch_wgrad_mfma(1, ta, tb, poff, E, d, 2 * H, BL.Rp, dw_gate, dw_up, s)))) return st;
+    } else if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) {
+        return st;
+    }
     if ((st = launched(launch_gemm_plain(act, ab, packed_bwd, dye, off, R, E, d, 2 * H, d, s)))) return st;
-    if ((st = launched(launch_dx(act, dye, ps, idx, dsel, given ? nullptr : w_router, dx, T, d, E, k, s)))) return st;
-    if (!given && (st = launched(launch_wgrad_router(act, x, dlogits, T, d, E, dw_router, s)))) return st;
+    void* wrt = given ? nullptr : at(ws, BL.wrt);
+    if (!given && (st = launched(launch_router_transpose(act, w_router, d, E, wrt, s)))) return st;
+    if ((st = launched(launch_dx(act, dye, ps, idx, dsel, wrt, dx, T, d, E, k, s)))) return st;
+    if (!given && (st = launched(launch_wgrad_router(act, xe, ps, dsel, off, T, k, d, E,
+                                                      reinterpret_cast<float*>(at(ws, BL.srow)),
+                                                      reinterpret_cast<float*>(at(ws, BL.rpart)), dw_router, s))))
+        return st;
     return MOE_OK;
 }
 

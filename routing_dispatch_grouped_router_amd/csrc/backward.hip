@@ -239,14 +239,14 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const TA* __restrict__ A, co
     }
 }
 
-// dx[t] = sum_j dxe[pos[t, j]] (slot order) + sum_j dsel[t, j] W_r[:, idx[t, j]]
-// (learned router; W_r [d][E]), one wave per token.
-template <bool BF, int KMAX, typename TW>
+// dx[t] = sum_j dxe[pos[t, j]] (slot order) + sum_j dsel[t, j] W_r^T[idx[t, j]]
+// (learned router; W_r^T [E][d]), one wave per token.
+template <bool BF, int KMAX>
 __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __restrict__ dxe,
                                                                const int32_t* __restrict__ pos,
                                                                const int32_t* __restrict__ idx,
                                                                const float* __restrict__ dsel,
-                                                               const TW* __restrict__ wr, void* __restrict__ dx,
+                                                               const void* __restrict__ wrt, void* __restrict__ dx,
                                                                int T, int row_chunks, int E, int k) {
     constexpr int NV = BF ? 8 : 4;
     const int lane = threadIdx.x & 63;
@@ -273,16 +273,196 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __res
 #pragma unroll
             for (int i = 0; i < NV; ++i) acc[i] += w[i];
         }
-        if (wr) {
+        if (wrt) {
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) {
                 if (j >= k) continue;
+                float w[8];
+                load_chunk<BF>(wrt, (size_t)ex[j] * row_chunks + c, w);   // row e_j of W_r^T
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    acc[i] = fmaf(ds[j], (float)ldv(wr, (size_t)(c * NV + i) * E + ex[j]), acc[i]);
+                for (int i = 0; i < NV; ++i) acc[i] = fmaf(ds[j], w[i], acc[i]);
             }
         }
         store_chunk<BF>(dx, (size_t)t * row_chunks + c, acc);
+    }
+}
+
+// Padded segments of the transposed operands.  Expert e's rows start at
+// column poff[e] + (offsets[e] % 8), after a lead of offsets[e] % 8 zero
+// columns, so that row r lands in a column congruent to r mod 8 and runs of 8
+// aligned rows become 16-byte stores; the segment is zero-padded to a multiple
+// of 32 columns.  poff[E] is the total.  One workgroup: per-expert lengths,
+// a Hillis-Steele scan in LDS.
+__global__ __launch_bounds__(1024) void seg_pad_kernel(const int32_t* __restrict__ offsets, int E,
+                                                       int32_t* __restrict__ poff) {
+    __shared__ int s_scan[1024];
+    const int e = threadIdx.x;
+    int len = 0;
+    if (e < E) {
+        const int n = offsets[e + 1] - offsets[e];
+        len = n > 0 ? (offsets[e] % 8 + n + 31) / 32 * 32 : 0;
+    }
+    s_scan[e] = len;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int v = e >= o ? s_scan[e - o] : 0;
+        __syncthreads();
+        s_scan[e] += v;
+        __syncthreads();
+    }
+    if (e < E) poff[e] = s_scan[e] - len;
+    if (e == 1023) poff[E] = s_scan[1023];
+}
+
+// Destination column of every row r (expert e): poff[e] + offsets[e] % 8 + r
+// - offsets[e], congruent to r mod 8 (binary search over the offsets).
+__global__ __launch_bounds__(256) void seg_dst_kernel(const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ poff, int E, int R,
+                                                      int32_t* __restrict__ rowdst) {
+    for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256) {
+        int lo = 0, hi = E;   // the expert whose segment holds r: largest e with offsets[e] <= r
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (offsets[mid] <= r) lo = mid; else hi = mid;
+        }
+        rowdst[r] = poff[lo] + offsets[lo] % 8 + r - offsets[lo];
+    }
+}
+
+// XT [M][Rp] from X [R][M] (bfloat16): row r goes to column rowdst[r].
+// 64 (rows) x 128 (columns) tiles through LDS: 16-byte loads along the rows of
+// X; each thread then gathers 8 aligned consecutive rows of one column and
+// stores them as one 16-byte run when the 8 rows belong to one expert
+// (element by element at an expert boundary); lanes 8 i .. 8 i + 7 write 128
+// contiguous bytes.
+__global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __restrict__ X, int R, int M,
+                                                            const int32_t* __restrict__ rowdst, int Rp,
+                                                            uint16_t* __restrict__ XT) {
+    __shared__ uint16_t tile[64][128];   // 16-byte chunk c of row r at chunk c ^ ((r / 8) % 8)
+    __shared__ int s_dst[64];
+    const int r0 = blockIdx.x * 64, m0 = blockIdx.y * 128;
+    const int tid = threadIdx.x;
+    if (tid < 64) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
+    u32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid + 256 * q;
+        const int rr = i >> 4, c8 = (i & 15) * 8;
+        const int r = r0 + rr, m = m0 + c8;
+        v[q] = (u32x4){0u, 0u, 0u, 0u};
+        if (r < R && m < M) v[q] = *reinterpret_cast<const u32x4*>(X + (size_t)r * M + m);   // M % 8 == 0
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid + 256 * q;
+        const int rr = i >> 4, c8 = (i & 15) * 8;
+        *reinterpret_cast<u32x4*>(&tile[rr][((c8 >> 3) ^ ((rr >> 3) & 7)) << 3]) = v[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid + 256 * q;
+        const int mm = i >> 3, g = (i & 7) * 8;
+        const int m = m0 + mm;
+        if (m >= M) continue;
+        const int d0 = s_dst[g];
+        uint16_t w[8];
+        const int pc = (((mm >> 3) ^ (g >> 3)) << 3) | (mm & 7);   // rows g .. g + 7 share the swizzle
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w[u] = tile[g + u][pc];
+        if (d0 >= 0 && s_dst[g + 7] == d0 + 7) {
+            const u32x4 o = {(uint32_t)w[0] | ((uint32_t)w[1] << 16), (uint32_t)w[2] | ((uint32_t)w[3] << 16),
+                             (uint32_t)w[4] | ((uint32_t)w[5] << 16), (uint32_t)w[6] | ((uint32_t)w[7] << 16)};
+            *reinterpret_cast<u32x4*>(XT + (size_t)m * Rp + d0) = o;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s_dst[g + u] >= 0) XT[(size_t)m * Rp + s_dst[g + u]] = w[u];
+        }
+    }
+}
+
+// srow[pos[t][j]] = dsel[t][j]: the router gradient of each routed row.
+__global__ __launch_bounds__(256) void srow_kernel(const int32_t* __restrict__ pos, const float* __restrict__ dsel,
+                                                   int n, float* __restrict__ srow) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) srow[pos[i]] = dsel[i];
+}
+
+// dW_r[c][e] = sum over expert e's rows r of xe[r][c] srow[r], in two passes.
+// Pass 1: the rows are cut into tiles of 64 within each expert (the grouped
+// GEMMs' tile schedule with 64-row tiles); a workgroup sums its tile's rows in
+// order, 8 columns per thread with 16-byte loads, into part[tile][d], and
+// workgroup 0 stores the schedule tstart[E + 1].  Pass 2: dW_r[c][e] = sum of
+// part[tile][c] over expert e's tiles in order.
+template <bool BF>
+__global__ __launch_bounds__(256) void router_wgrad_rows_kernel(const void* __restrict__ xe,
+                                                                const float* __restrict__ srow,
+                                                                const int32_t* __restrict__ offsets, int E, int d,
+                                                                float* __restrict__ part, int32_t* __restrict__ tstart) {
+    constexpr int NV = BF ? 8 : 4;
+    __shared__ int s_tstart[kMaxExperts + 1];
+    __shared__ int s_scan[256];
+    const int MT = build_tile_schedule<64, 256>(offsets, E, s_tstart, s_scan);
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e <= E; e += 256) tstart[e] = s_tstart[e];
+    const int tile = blockIdx.x;
+    if (tile >= MT) return;
+    const int e = tile_expert(s_tstart, E, tile);
+    const int row0 = offsets[e] + (tile - s_tstart[e]) * 64;
+    const int rows = min(64, offsets[e + 1] - row0);
+    const int chunks = d / NV;
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int r = 0; r < rows; ++r) {
+            float v[8];
+            load_chunk<BF>(xe, (size_t)(row0 + r) * chunks + c, v);
+            const float sv = srow[row0 + r];
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc[i] = fmaf(v[i], sv, acc[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) part[(size_t)tile * d + c * NV + i] = acc[i];
+    }
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* __restrict__ part,
+                                                                  const int32_t* __restrict__ tstart, int d, int E,
+                                                                  float* __restrict__ dw) {
+    const int n = d * E;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+        const int c = i / E, e = i - c * E;
+        float s = 0.f;
+        for (int t = tstart[e]; t < tstart[e + 1]; ++t) s += part[(size_t)t * d + c];
+        dw[i] = s;
+    }
+}
+
+// Zero the lead and tail padding of every expert segment in every row of XT.
+__global__ __launch_bounds__(256) void zero_pad_kernel(const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ poff, int M, int Rp,
+                                                       uint16_t* __restrict__ XT) {
+    const int e = blockIdx.y;
+    const int n = offsets[e + 1] - offsets[e];
+    const int lead = n > 0 ? offsets[e] % 8 : 0;
+    const int a = poff[e], b = poff[e] + lead + n, z = poff[e + 1];
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < M * 40; i += gridDim.x * 256) {
+        const int m = i / 40, c = i % 40;   // at most 7 lead and 31 tail columns
+        const int col = c < 8 ? a + c : b + (c - 8);
+        const bool pad = c < 8 ? c < lead : col < z;
+        if (pad) XT[(size_t)m * Rp + col] = 0;
+    }
+}
+
+// W_r^T [E][d] from W_r [d][E], for 16-byte reads of one expert's column in dx.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_small_kernel(const T* __restrict__ w, int d, int E,
+                                                              T* __restrict__ wt) {
+    const size_t n = (size_t)d * E;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        const int e = (int)(i / d), c = (int)(i % d);
+        wt[i] = w[(size_t)c * E + e];
     }
 }
 
@@ -342,23 +522,50 @@ hipError_t launch_wgrad_w1(int act, const void* xe, const void* dab, const int32
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad_router(int act, const void* x, const float* dL, int T, int d, int E, float* dw_router,
+size_t router_wgrad_part_bytes(int R, int E, int d) {
+    return (size_t)(R / 64 + std::min(E, R)) * d * 4 + ((size_t)E + 1) * 4 + 256;
+}
+
+hipError_t launch_wgrad_router(int act, const void* xe, const int32_t* pos, const float* dsel, const int32_t* offsets,
+                               int T, int k, int d, int E, float* srow, float* part, float* dw_router,
                                hipStream_t s) {
-    if (act == kF32) launch_wgrad_t<float, float, 0>(x, dL, nullptr, 1, T, d, E, dw_router, nullptr, s);
-    else launch_wgrad_t<bf16raw, float, 0>(x, dL, nullptr, 1, T, d, E, dw_router, nullptr, s);
+    const int R = T * k;
+    hipLaunchKernelGGL(srow_kernel, dim3(std::min((R + 255) / 256, 1024)), dim3(256), 0, s, pos, dsel, R, srow);
+    const int tiles = R / 64 + std::min(E, R);
+    int32_t* tstart = reinterpret_cast<int32_t*>(part + (size_t)tiles * d);
+    if (act == kF32)
+        hipLaunchKernelGGL(router_wgrad_rows_kernel<false>, dim3(tiles), dim3(256), 0, s, xe, srow, offsets, E, d,
+                           part, tstart);
+    else
+        hipLaunchKernelGGL(router_wgrad_rows_kernel<true>, dim3(tiles), dim3(256), 0, s, xe, srow, offsets, E, d,
+                           part, tstart);
+    const int n = d * E;
+    hipLaunchKernelGGL(router_wgrad_reduce_kernel, dim3(std::min((n + 255) / 256, 1024)), dim3(256), 0, s, part,
+                       tstart, d, E, dw_router);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_transpose(int act, const void* w_router, int d, int E, void* wrt, hipStream_t s) {
+    const size_t n = (size_t)d * E;
+    const int grid = (int)std::min<size_t>((n + 255) / 256, 1024);
+    if (act == kF32)
+        hipLaunchKernelGGL(transpose_small_kernel<float>, dim3(grid), dim3(256), 0, s,
+                           static_cast<const float*>(w_router), d, E, static_cast<float*>(wrt));
+    else
+        hipLaunchKernelGGL(transpose_small_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(w_router), d, E, static_cast<uint16_t*>(wrt));
     return hipGetLastError();
 }
 
 template <int KMAX>
 static void launch_dx_k(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
-                        const void* wr, void* dx, int T, int d, int E, int k, hipStream_t s) {
+                        const void* wrt, void* dx, int T, int d, int E, int k, hipStream_t s) {
     dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock), block(64 * kTokPerBlock);
     if (act == kF32)
-        hipLaunchKernelGGL((dx_kernel<false, KMAX, float>), grid, block, 0, s, dxe, pos, idx, dsel,
-                           static_cast<const float*>(wr), dx, T, d / 4, E, k);
+        hipLaunchKernelGGL((dx_kernel<false, KMAX>), grid, block, 0, s, dxe, pos, idx, dsel, wrt, dx, T, d / 4, E,
+                           k);
     else
-        hipLaunchKernelGGL((dx_kernel<true, KMAX, bf16raw>), grid, block, 0, s, dxe, pos, idx, dsel,
-                           static_cast<const bf16raw*>(wr), dx, T, d / 8, E, k);
+        hipLaunchKernelGGL((dx_kernel<true, KMAX>), grid, block, 0, s, dxe, pos, idx, dsel, wrt, dx, T, d / 8, E, k);
 }
 
 hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
@@ -367,6 +574,22 @@ hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t
     else if (k <= 4) launch_dx_k<4>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
     else if (k <= 8) launch_dx_k<8>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
     else launch_dx_k<kMaxTopK>(act, dxe, pos, idx, dsel, w_router, dx, T, d, E, k, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s) {
+    hipLaunchKernelGGL(seg_pad_kernel, dim3(1), dim3(1024), 0, s, offsets, E, poff);
+    const int grid = std::min((R + 255) / 256, 1024);
+    hipLaunchKernelGGL(seg_dst_kernel, dim3(grid), dim3(256), 0, s, offsets, poff, E, R, rowdst);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
+                                const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s) {
+    dim3 grid((R + 63) / 64, (M + 127) / 128);
+    hipLaunchKernelGGL(transpose_seg_kernel, grid, dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
+    dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
+    hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);
     return hipGetLastError();
 }
 

@@ -780,6 +780,144 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
 }
 
+// ============================================================================ weight gradients
+
+// K-grouped bf16 GEMM on MFMA for the weight gradients: for expert e
+//   C[e][m][n] = sum over k in [poff[e], poff[e+1]) of XA[m][k] XB[n][k]
+// where XA [M][Rp] and XB [N][Rp] are the transposed activations, each
+// expert's rows a run of columns at poff[e] zero-padded to a multiple of 32,
+// so the contraction axis is contiguous and no K-tile straddles two experts.
+// Workgroup tile 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA blocks of 32 x 32),
+// 64-byte K-tiles in a 4-stage ring loaded with global_load_lds and swizzled
+// as in the forward kernels, one barrier per K-tile: after it, the DMA of
+// K-tile kt + 3 refills the stage every wave finished reading in the previous
+// step.  Two workgroups share a CU.  An expert without rows writes zeros.
+// OMAP 0: C[e][m][n].  OMAP 1: the N axis interleaves gate and up columns (32
+// + 32 per 64); column n goes to C (gate) or C2 (up) [e][m][h], h = 32 (n /
+// 64) + n % 32.  Rows or columns past M, N are clamped in the loads and not
+// stored.
+template <class WT, int OMAP>
+__global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_kernel(const uint16_t* __restrict__ XA,
+                                                                      const uint16_t* __restrict__ XB,
+                                                                      const int32_t* __restrict__ poff, int M, int N,
+                                                                      int Rp, float* __restrict__ C,
+                                                                      float* __restrict__ C2) {
+    constexpr int BM = WT::BM, BN = WT::BN, STAGES = 4, SC = (BM + BN) * 4, NW = WT::NW;
+    constexpr int A_DMA = BM / 16 / NW, B_DMA = BN / 16 / NW, P = A_DMA + B_DMA;
+    constexpr int TM = BM / WT::WM / 32, TN = BN / WT::WN / 32;
+    constexpr int WROWS = BM / WT::WM, WCOLS = BN / WT::WN;
+    __shared__ u32x4 ring[STAGES * SC];
+    const int e = blockIdx.z, m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int k0 = poff[e], nk = (poff[e + 1] - k0) / 32;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WT::WN, wn = wave % WT::WN;
+    const uint32_t ring_lds = lds_addr(ring);
+    const uint32_t rowbytes = (uint32_t)Rp * 2u;
+    const int drow = lane >> 2;
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    uint32_t offa[A_DMA], offb[B_DMA];
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i)
+        offa[i] = (uint32_t)min(m0 + 16 * (wave * A_DMA + i) + drow, M - 1) * rowbytes + (uint32_t)k0 * 2u + dchunk;
+#pragma unroll
+    for (int i = 0; i < B_DMA; ++i)
+        offb[i] = (uint32_t)min(n0 + 16 * (wave * B_DMA + i) + drow, N - 1) * rowbytes + (uint32_t)k0 * 2u + dchunk;
+    // K-tile kt into stage kt % 4; past the last K-tile a clamped copy lands in a stage nobody reads
+    auto issue = [&](int kt) {
+        const uint32_t ko = (uint32_t)min(kt, nk - 1) * 64u;
+        const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SC * 16u;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) dma16(XA, offa[i] + ko, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i) dma16(XB, offb[i] + ko, st + BM * 64u + (uint32_t)(wave * B_DMA + i) * 1024u);
+    };
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
+    const int arow = (wm * WROWS + (lane & 31)) * 4, brow = (BM + wn * WCOLS + (lane & 31)) * 4;
+    if (nk > 0) {
+        issue(0);
+        issue(1);
+        issue(2);
+        for (int kt = 0; kt < nk; ++kt) {
+            wait_vm<2 * P>();   // K-tile kt landed; kt + 1 and kt + 2 may still be in flight
+            ring_barrier();     // every wave's reads of kt - 1 are complete (its MFMAs used them)
+            issue(kt + 3);      // into the stage of kt - 1
+            const u32x4* stage = ring + (kt & (STAGES - 1)) * SC;
+            bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    fa[s2][i] = __builtin_bit_cast(bf16x8, stage[arow + i * 128 + ((2 * s2 + half) ^ fsw)]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    fb[s2][j] = __builtin_bit_cast(bf16x8, stage[brow + j * 128 + ((2 * s2 + half) ^ fsw)]);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s2][j], fa[s2][i], acc[i][j], 0, 0, 0);
+        }
+    }
+    wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
+    // lane l holds row m of its block and, per run q, 4 consecutive columns 8 q + 4 (l / 32) + 0..3
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int m = m0 + wm * WROWS + i * 32 + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * WCOLS + j * 32 + 8 * q + 4 * half;
+                if (n >= N) continue;
+                const u32x4 v = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                                 __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
+                if (OMAP == 0) {
+                    *reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n) = v;
+                } else {
+                    const int Hh = N / 2, h = 32 * (n / 64) + n % 32;
+                    float* dst = ((n / 32) & 1) ? C2 : C;
+                    *reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + h) = v;
+                }
+            }
+    }
+}
+
+// Weight-gradient tile shapes: BM x BN workgroup tile, WM x WN waves, OCC
+// workgroups per CU (4 ring stages of (BM + BN) x 64 bytes each).
+template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+struct WgradTile {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM * WN, NTHR = 64 * NW, OCC = OCC_;
+};
+using WgradSmall = WgradTile<128, 128, 2, 2, 2>;   // 4 waves of 64 x 64, two workgroups per CU
+using WgradBig = WgradTile<256, 256, 2, 4, 1>;     // 8 waves of 128 x 64, as the forward bf16 tiles
+
+template <class WT>
+hipError_t launch_wgrad_tile(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
+                             int N, int Rp, float* C, float* C2, hipStream_t s) {
+    dim3 grid((N + WT::BN - 1) / WT::BN, (M + WT::BM - 1) / WT::BM, E), block(WT::NTHR);
+    if (omap == 1)
+        hipLaunchKernelGGL((gemm_wgrad_kernel<WT, 1>), grid, block, 0, s, XA, XB, poff, M, N, Rp, C, C2);
+    else
+        hipLaunchKernelGGL((gemm_wgrad_kernel<WT, 0>), grid, block, 0, s, XA, XB, poff, M, N, Rp, C, C2);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_mfma(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
+                             int N, int Rp, float* C, float* C2, hipStream_t s) {
+    return launch_wgrad_tile<WgradBig>(omap, XA, XB, poff, E, M, N, Rp, C, C2, s);
+}
+
 // ============================================================================ launchers
 
 template <class TL, int EPI>

@@ -104,16 +104,34 @@ hipError_t launch_wgrad_down(int act, const void* h, const void* dye, const int3
                              int d, float* dw_down, hipStream_t s);
 hipError_t launch_wgrad_w1(int act, const void* xe, const void* dab, const int32_t* offsets, int E, int R, int d,
                            int H, float* dw_gate, float* dw_up, hipStream_t s);
-hipError_t launch_wgrad_router(int act, const void* x, const float* dL, int T, int d, int E, float* dw_router,
+// dw_router[c][e] = sum over expert e's rows of xe[r][c] srow[r], srow[pos[t][j]] = dsel[t][j]
+// (= x^T dL, dL being zero outside the selected experts): srow T k floats, part
+// router_wgrad_part_bytes(T k, E, d) bytes.
+size_t router_wgrad_part_bytes(int R, int E, int d);
+hipError_t launch_wgrad_router(int act, const void* xe, const int32_t* pos, const float* dsel, const int32_t* offsets,
+                               int T, int k, int d, int E, float* srow, float* part, float* dw_router,
                                hipStream_t s);
+// W_r^T [E][d] from W_r [d][E] (activation type).
+hipError_t launch_router_transpose(int act, const void* w_router, int d, int E, void* wrt, hipStream_t s);
 
-// dx[t] = sum_j dxe[pos[t][j]] (+ sum_j dsel[t][j] W_r[:, idx[t][j]] when w_router is given).
+// dx[t] = sum_j dxe[pos[t][j]] (+ sum_j dsel[t][j] W_r^T[idx[t][j]] when wrt [E][d] is given).
 hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
-                     const void* w_router, void* dx, int T, int d, int E, int k, hipStream_t s);
+                     const void* wrt, void* dx, int T, int d, int E, int k, hipStream_t s);
 
 // C = A B^T per expert segment, stored as computed (float32 or bfloat16): the
 // grouped GEMM without an epilogue (recompute and data gradients).
 hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, const int32_t* offsets, int R, int E,
                              int N, int K, int ldc, hipStream_t s);
+
+// bf16 weight gradients on MFMA (gemm_pipe.hip): per-expert transposed, zero-padded
+// operands XA [M][Rp], XB [N][Rp] with expert e's segment at poff[e] (seg_pad: a lead of
+// offsets[e] % 8 zero columns, the rows, zeros up to a multiple of 32; Rp >= T k + 40 E);
+// launch_transpose_seg writes such an operand from X [R][M].
+// launch_seg_pad also writes rowdst [R], the destination column of every row.
+hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s);
+hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
+                                const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s);
+hipError_t launch_wgrad_mfma(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
+                             int N, int Rp, float* C, float* C2, hipStream_t s);
 
 }  // namespace moe

@@ -148,18 +148,18 @@ def test_backward_rejects_mxfp8_nulls_and_small_workspaces(lib):
     assert n.value >= p.n_experts * p.d_model * 2 * p.d_hidden * 2
     fws = B.workspace_bytes(p)
     fake = ctypes.c_void_p(0x1000)
-    args = [ctypes.byref(p), fake, None, None, fake, fake, fake, None, None, None, None, fake, fws,
+    args = [ctypes.byref(p), fake, None, fake, fake, fake, None, None, None, None, fake, fws,
             fake, fake, fake, fake, fake, None, fake, bws, None]
     bad_fwd = list(args)
-    bad_fwd[12] = fws - 1
+    bad_fwd[11] = fws - 1
     assert lib.moe_backward(*bad_fwd) == -4
     bad_ws = list(args)
-    bad_ws[20] = bws - 1
+    bad_ws[19] = bws - 1
     assert lib.moe_backward(*bad_ws) == -4
     no_dy = list(args)
     no_dy[1] = None
     assert lib.moe_backward(*no_dy) == -1
-    # learned router: x, w_router and dw_router are required
+    # learned router: w_router and dw_router are required
     pl = _prob()
     args_l = list(args)
     args_l[0] = ctypes.byref(pl)

@@ -66,7 +66,7 @@ def _run(w):
     bwd = B.Backward(p, DEV)
     outs = []
     for _ in range(2):
-        g = bwd(fwd, dy, dev["w_down"], packed, packed_bwd, x=dev["x"], w_router=dev["w_router"])
+        g = bwd(fwd, dy, dev["w_down"], packed, packed_bwd, w_router=dev["w_router"])
         torch.cuda.synchronize()
         outs.append({k: (None if v is None else v.clone()) for k, v in g.items()})
     return host, fwd, dy_host, outs
