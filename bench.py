@@ -242,6 +242,8 @@ def main(argv=None):
     ap.add_argument("--main-only", action="store_true",
                     help="skip the comparison measurements (cold cache, host-synchronising path, router "
                          "statistics), e.g. under a profiler")
+    ap.add_argument("--with-backward", action="store_true",
+                    help="also time moe_backward when --main-only is given (float32 and bf16 blocks)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB (a known "
                          "byte count that calibrates HBM counters such as FETCH_SIZE / WRITE_SIZE)")
@@ -337,6 +339,8 @@ def main(argv=None):
         result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
         if w.act != "mxfp8":
             result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
+    elif args.with_backward and w.act != "mxfp8":
+        result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(result))
