@@ -209,11 +209,11 @@ def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_devic
     Useful FLOPs: the gate/up recompute 4 R d H, the data gradients 2 R d H
     (down) + 4 R d H (gate/up), the weight gradients 2 R d H + 4 R d H, plus the
     router's 2 T d E twice for the learned router."""
-    packed_bwd = B.pack_weights_backward(p, d_in["w_gate"], d_in["w_up"])
+    packed_bwd = B.pack_weights_backward(p, d_in["w_gate"], d_in["w_up"], d_in["w_down"])
     g = torch.Generator(device="cpu").manual_seed(w.seed + 17)
     dy = torch.randn((w.T, w.d), generator=g).to(B.storage_dtype(w.act)).to(dev)
     bwd = B.Backward(p, dev)
-    run = lambda: bwd(f, dy, d_in["w_down"], packed, packed_bwd, w_router=d_in["w_router"])
+    run = lambda: bwd(f, dy, packed, packed_bwd, x=d_in["x"], w_router=d_in["w_router"])
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -225,7 +225,7 @@ def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_devic
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
     flops = 16.0 * w.R * w.d * w.H + (2 * 2.0 * w.T * w.d * w.E if w.router == "learned" else 0.0)
-    peak = 2500.0 if w.act == "bf16" else 157.3
+    peak = 157.3 if w.act == "f32" else 2500.0   # MXFP8 blocks run their backward in bf16
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
             "useful_tflops": round(tf, 2), "frac_of_peak": round(tf / peak, 4),
@@ -243,7 +243,7 @@ def main(argv=None):
                     help="skip the comparison measurements (cold cache, host-synchronising path, router "
                          "statistics), e.g. under a profiler")
     ap.add_argument("--with-backward", action="store_true",
-                    help="also time moe_backward when --main-only is given (float32 and bf16 blocks)")
+                    help="also time moe_backward when --main-only is given")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="before the timed steps, run one plain device copy of this many MiB (a known "
                          "byte count that calibrates HBM counters such as FETCH_SIZE / WRITE_SIZE)")
@@ -337,9 +337,8 @@ def main(argv=None):
         result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
         result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
         result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
-        if w.act != "mxfp8":
-            result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
-    elif args.with_backward and w.act != "mxfp8":
+        result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
+    elif args.with_backward:
         result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host)

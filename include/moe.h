@@ -241,12 +241,12 @@ int32_t moe_set_gemm_grid_cap(int32_t cap);
 
 /* ---------------------------------------------------------------- backward
  *
- * Gradients of the block for a loss L with dL/dy = dy, float32 and bf16
- * activations (MOE_MXFP8 and MOE_IDENTITY_EXPERTS return MOE_ERR_DTYPE).  The
- * report runs the block's backward with the dispatch and combine as each
- * other's transposes, grouped GEMMs for data and weight gradients and the
- * block forward re-executed ("Section 24: Conclusion", Evidence 7 and
- * Evidence 11).  With g the gates (the softmax of the k selected logits):
+ * Gradients of the block for a loss L with dL/dy = dy (MOE_IDENTITY_EXPERTS
+ * returns MOE_ERR_DTYPE).  The report runs the block's backward with the
+ * dispatch and combine as each other's transposes, grouped GEMMs for data and
+ * weight gradients and the block forward re-executed ("Section 24:
+ * Conclusion", Evidence 7 and Evidence 11).  With g the gates (the softmax of
+ * the k selected logits):
  *
  *   dgate[t,j] = dy[t] . ye[pos[t,j]]          dye[pos[t,j]] = g[t,j] dy[t]
  *   dlogits[t,e_j] = g_j (dgate_j - sum_i g_i dgate_i), 0 for unselected e
@@ -256,25 +256,34 @@ int32_t moe_set_gemm_grid_cap(int32_t cap);
  *                                              (sums over expert e's rows)
  *   dx[t] = sum_j dxe[pos[t,j]]  (+ dlogits[t] W_r^T for the learned router)
  *   dw_router = x^T dlogits                     (learned router only; summed
- *               per expert over the dispatched rows xe, which hold x)
+ *               per expert over that expert's token rows)
  *
  * Storage: dye, a, b, dh, da, db, dxe and dx in the activation type (bf16
  * rounded to nearest even where stored), dlogits and all weight gradients
- * float32.  Every reduction runs in a fixed order: results are bitwise
- * reproducible.  All work is enqueued on `stream`; nothing allocates or
- * synchronises, so the call is capturable in a HIP graph.
+ * float32.  MOE_MXFP8 blocks follow Evidence 7 (dequantise, then bf16): the
+ * saved MXFP8 xe and h are dequantised to bf16 (exactly), the weights are the
+ * bf16 values of the forward's MXFP8 weights, and every step above runs in
+ * bf16 (dy, dx bf16).  Every reduction runs in a fixed order: results are
+ * bitwise reproducible.  All work is enqueued on `stream`; nothing allocates
+ * or synchronises, so the call is capturable in a HIP graph.
  *
  * moe_backward_weight_bytes / moe_pack_weights_backward: the backward weight
- * cache W1T [E][d][2H] (the activation type), row c holding for each column n
- * of the packed W1 (32 gate then 32 up hidden units per 64) the weight of input
- * c, built once from w_gate and w_up [E][d][H] (device, the activation type;
- * the report's second weight cache, 24.3).
+ * cache (the report's second weight cache, 24.3), built once from w_gate,
+ * w_up [E, d, H] and w_down [E, H, d] (device, the activation type; bf16 for
+ * MOE_MXFP8): W1T [E][d][2H], row c holding for each column n of the packed
+ * W1 (32 gate then 32 up hidden units per 64) the weight of input c; W_down
+ * [E][H][d]; for MOE_MXFP8 also the packed W1 in bf16.  MOE_MXFP8 stores the
+ * dequantised MXFP8 values (blocks of 32 along each forward GEMM's
+ * contraction axis, as moe_pack_weights quantises them).
  *
  * moe_backward arguments (device pointers unless noted):
- *   dy          [T, d] activation type
- *   w_router    [d, E] activation type (learned router only)
- *   w_down      [E, H, d] as given to moe_pack_weights
- *   packed_w    the forward weight cache (moe_pack_weights)
+ *   dy          [T, d] activation type (bf16 for MOE_MXFP8)
+ *   x           [T, d] the forward's input (learned router only; may be NULL
+ *               with MOE_LOGITS_GIVEN)
+ *   w_router    [d, E] activation type (learned router only; may be NULL with
+ *               MOE_LOGITS_GIVEN)
+ *   packed_w    the forward weight cache (moe_pack_weights); unused, may be
+ *               NULL, for MOE_MXFP8
  *   packed_bwd  the backward weight cache (moe_pack_weights_backward)
  *   topk_idx, topk_gate, offsets, pos : the forward's routing arrays, or NULL
  *               for the copies moe_forward kept in its workspace when it was
@@ -282,23 +291,24 @@ int32_t moe_set_gemm_grid_cap(int32_t cap);
  *   fwd_ws      the workspace of the moe_forward call being differentiated,
  *               unchanged since (it holds xe, h and ye); fwd_ws_bytes >=
  *               moe_workspace_bytes
- *   dx          [T, d] out, activation type
+ *   dx          [T, d] out, activation type (bf16 for MOE_MXFP8)
  *   dlogits     [T, E] out, float32
  *   dw_gate, dw_up [E, d, H] out, dw_down [E, H, d] out, float32
  *   dw_router   [d, E] out, float32 (learned router only; may be NULL with
  *               MOE_LOGITS_GIVEN)
  *   ws          backward workspace, ws_bytes >= moe_backward_workspace_bytes
  * Errors: as moe_forward; MOE_ERR_SHAPE also when T*k*2H elements of the
- * activation type exceed 2^32 bytes. */
+ * backward's activation type exceed 2^32 bytes. */
 int32_t moe_backward_workspace_bytes(const moe_problem* p, size_t* bytes);
 int32_t moe_backward_weight_bytes(const moe_problem* p, size_t* bytes);
-int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up, void* packed_bwd,
-                                  void* stream);
-int32_t moe_backward(const moe_problem* p, const void* dy, const void* w_router,
-                     const void* w_down, const void* packed_w, const void* packed_bwd, const int32_t* topk_idx,
-                     const float* topk_gate, const int32_t* offsets, const int32_t* pos, const void* fwd_ws,
-                     size_t fwd_ws_bytes, void* dx, float* dlogits, float* dw_gate, float* dw_up, float* dw_down,
-                     float* dw_router, void* ws, size_t ws_bytes, void* stream);
+int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
+                                  void* packed_bwd, void* stream);
+int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const void* w_router, const void* packed_w,
+                     const void* packed_bwd, const int32_t* topk_idx, const float* topk_gate, const int32_t* offsets,
+                     const int32_t* pos, const void* fwd_ws, size_t fwd_ws_bytes, void* dx, float* dlogits,
+                     float* dw_gate, float* dw_up, float* dw_down, float* dw_router, void* ws, size_t ws_bytes,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,6 +38,13 @@ weight gradients, router gradients and dgate are float32.  The recomputed a
 and b are rounded to the activation type (the forward never stored them);
 h is recomputed exactly as the forward computed it.  With ``act='f64'`` no
 rounding happens anywhere (used by the finite-difference pins).
+
+MXFP8 blocks: the report found that MXFP8 weight gradients are fastest as a
+dequantise followed by bf16 grouped GEMMs (Evidence 7); the backward here does
+the whole block that way.  The saved activations are the forward's MXFP8
+values (exact in bf16), the weights are the forward's MXFP8 weight values
+(the caller passes them, e.g. from ``moe_oracle.expert_weights``), and every
+activation-sized gradient is stored in bf16.
 """
 from __future__ import annotations
 
@@ -47,10 +54,11 @@ from . import moe_oracle as F
 
 
 def store(v, act: str) -> np.ndarray:
-    """Activation storage of the backward ('f64' keeps float64 exactly)."""
+    """Activation-gradient storage of the backward ('f64' keeps float64
+    exactly; MXFP8 blocks store their gradients in bf16)."""
     if act == "f64":
         return np.asarray(v, dtype=np.float64)
-    return F.store(v, act)
+    return F.store(v, "bf16" if act == "mxfp8" else act)
 
 
 def store_f32(v, act: str) -> np.ndarray:
@@ -131,10 +139,11 @@ def expert_backward(rows, dye_rows, wg, wu, wd, act: str):
     Returns (drows, dwg, dwu, dwd): drows in activation storage, weight
     gradients float32.  a and b are recomputed from the rows.
     """
-    h_dt = "f64" if act == "f64" else F.intermediate_dtypes(act)[0]
     a_exact = rows @ wg
     b_exact = rows @ wu
-    h = store(F.silu(a_exact) * b_exact, h_dt)      # as the forward stored it
+    h = F.silu(a_exact) * b_exact
+    if act != "f64":
+        h = F.store(h, F.intermediate_dtypes(act)[0])   # as the forward stored it (MXFP8: blocks along H)
     a = store(a_exact, act)
     b = store(b_exact, act)
     dh = store(dye_rows @ wd.T, act)

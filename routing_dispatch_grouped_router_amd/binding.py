@@ -82,7 +82,7 @@ def lib():
         L.moe_set_gemm_grid_cap.argtypes = [_I32]
         L.moe_backward_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_backward_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
-        L.moe_pack_weights_backward.argtypes = [PP, _P, _P, _P, _P]
+        L.moe_pack_weights_backward.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_backward.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P,
                                    _P, _SZ, _P]
         L.moe_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
@@ -306,15 +306,16 @@ def backward_weight_bytes(p: Problem) -> int:
     return n.value
 
 
-def pack_weights_backward(p: Problem, w_gate, w_up, stream=None) -> torch.Tensor:
-    """The backward weight cache W1T [E][d][2H] (moe_pack_weights_backward)."""
+def pack_weights_backward(p: Problem, w_gate, w_up, w_down, stream=None) -> torch.Tensor:
+    """The backward weight cache (moe_pack_weights_backward)."""
     dt = storage_dtype(p.act)
     E, d, H = p.n_experts, p.d_model, p.d_hidden
     _expect(w_gate, (E, d, H), dt, "w_gate")
     _expect(w_up, (E, d, H), dt, "w_up")
+    _expect(w_down, (E, H, d), dt, "w_down")
     out = torch.empty(backward_weight_bytes(p), dtype=torch.uint8, device=w_gate.device)
     _check("moe_pack_weights_backward", lib().moe_pack_weights_backward(
-        ctypes.byref(p), _ptr(w_gate), _ptr(w_up), _ptr(out), _stream(stream)))
+        ctypes.byref(p), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), _stream(stream)))
     return out
 
 
@@ -325,7 +326,7 @@ class Backward:
         self.p = p
         T, E, d, H = p.T, p.n_experts, p.d_model, p.d_hidden
         self.ws = torch.empty(backward_workspace_bytes(p), dtype=torch.uint8, device=device)
-        self.dx = torch.empty((T, d), dtype=storage_dtype(p.act), device=device)
+        self.dx = torch.empty((T, d), dtype=out_dtype(p.act), device=device)
         self.dlogits = torch.empty((T, E), dtype=torch.float32, device=device)
         self.dw_gate = torch.empty((E, d, H), dtype=torch.float32, device=device)
         self.dw_up = torch.empty((E, d, H), dtype=torch.float32, device=device)
@@ -333,15 +334,15 @@ class Backward:
         self.dw_router = (None if p.flags & MOE_LOGITS_GIVEN
                           else torch.empty((d, E), dtype=torch.float32, device=device))
 
-    def __call__(self, fwd: "Forward", dy, w_down, packed, packed_bwd, w_router=None, stream=None):
+    def __call__(self, fwd: "Forward", dy, packed, packed_bwd, x=None, w_router=None, stream=None):
         p = self.p
         dt = storage_dtype(p.act)
         _expect(dy, (p.T, p.d_model), dt, "dy")
-        _expect(w_down, (p.n_experts, p.d_hidden, p.d_model), dt, "w_down")
         if not p.flags & MOE_LOGITS_GIVEN:
+            _expect(x, (p.T, p.d_model), dt, "x")
             _expect(w_router, (p.d_model, p.n_experts), dt, "w_router")
         _check("moe_backward", lib().moe_backward(
-            ctypes.byref(p), _ptr(dy), _ptr(w_router), _ptr(w_down), _ptr(packed), _ptr(packed_bwd),
+            ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(packed), _ptr(packed_bwd),
             _ptr(fwd.idx), _ptr(fwd.gate), _ptr(fwd.offsets), _ptr(fwd.pos), _ptr(fwd.ws), fwd.ws.numel(),
             _ptr(self.dx), _ptr(self.dlogits), _ptr(self.dw_gate), _ptr(self.dw_up), _ptr(self.dw_down),
             _ptr(self.dw_router), _ptr(self.ws), self.ws.numel(), _stream(stream)))

@@ -75,25 +75,31 @@ Packed packed_layout(const moe_problem& p) {
 // also the padded segment starts poff [E+1] and two transposed operands of the
 // weight-gradient GEMMs, [max(H, d)][Rp] (h, then xe) and [max(d, 2H)][Rp]
 // (dye, then da | db), Rp = T k + 40 E rounded up to 32 (each segment adds at
-// most 7 lead and 31 tail columns); for the learned router W_r^T [E][d] and
-// the per-256-token partials of dW_r.
+// most 7 lead and 31 tail columns); for the learned router W_r^T [E][d], the
+// router gradient per routed row and the per-tile partials of dW_r; for MXFP8
+// blocks the dequantised xe [R][d] and h [R][H] (bfloat16).
 struct BwdLayout {
-    size_t ab, dye, dh, dsel, poff, rowdst, ta, tb, wrt, srow, rpart, total;
+    size_t ab, dye, dh, dsel, poff, rowdst, ta, tb, wrt, srow, rpart, xe16, h16, total;
     int Rp;
 };
 
 int bwd_rp(const moe_problem& p) { return (p.T * p.top_k + 40 * p.n_experts + 31) / 32 * 32; }
 
+// The backward runs in the activation type, bfloat16 for MXFP8 blocks (their
+// saved activations are dequantised first).
+int bwd_act(int act) { return act == MOE_MXFP8 ? MOE_BF16 : act; }
+
 BwdLayout bwd_layout(const moe_problem& p) {
     BwdLayout B{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    const size_t R = (size_t)p.T * p.top_k, d = p.d_model, H = p.d_hidden, b = act_bytes(p.act_dtype);
+    const int ba = bwd_act(p.act_dtype);
+    const size_t R = (size_t)p.T * p.top_k, d = p.d_model, H = p.d_hidden, b = act_bytes(ba);
     B.ab = take(R * 2 * H * b);
     B.dye = take(R * d * b);
     B.dh = take(R * H * b);
     B.dsel = take((size_t)p.T * p.top_k * 4);
-    const bool bf = p.act_dtype == MOE_BF16;
+    const bool bf = ba == MOE_BF16;
     B.Rp = bwd_rp(p);
     B.poff = take(bf ? ((size_t)p.n_experts + 1) * 4 : 0);
     B.rowdst = take(bf ? R * 4 : 0);
@@ -103,8 +109,30 @@ BwdLayout bwd_layout(const moe_problem& p) {
     B.wrt = take(learned ? (size_t)p.n_experts * d * b : 0);
     B.srow = take(learned ? R * 4 : 0);
     B.rpart = take(learned ? router_wgrad_part_bytes((int)R, p.n_experts, p.d_model) : 0);
+    const bool mx = p.act_dtype == MOE_MXFP8;
+    B.xe16 = take(mx ? R * d * 2 : 0);
+    B.h16 = take(mx ? R * H * 2 : 0);
     B.total = off;
     return B;
+}
+
+// Backward weight cache: W1T [E][d][2H], W_down [E][H][d] and, for MXFP8
+// blocks, the packed W1 [E][2H][d] the gate/up recompute multiplies with; in
+// the backward's activation type (MXFP8: bfloat16 of the quantised values).
+struct BwdPacked {
+    size_t w1t, wd, w1, total;
+};
+
+BwdPacked bwd_packed_layout(const moe_problem& p) {
+    BwdPacked P{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    const size_t E = p.n_experts, d = p.d_model, H = p.d_hidden, b = act_bytes(bwd_act(p.act_dtype));
+    P.w1t = take(E * d * 2 * H * b);
+    P.wd = take(E * H * d * b);
+    P.w1 = take(p.act_dtype == MOE_MXFP8 ? E * 2 * H * d * b : 0);
+    P.total = off;
+    return P;
 }
 
 int32_t check_problem(const moe_problem* p) {
@@ -438,12 +466,12 @@ int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* 
 static int32_t check_backward(const moe_problem* p) {
     int32_t st = check_problem(p);
     if (st) return st;
-    if (p->act_dtype == MOE_MXFP8 || (p->flags & MOE_IDENTITY_EXPERTS)) return MOE_ERR_DTYPE;
+    if (p->flags & MOE_IDENTITY_EXPERTS) return MOE_ERR_DTYPE;
     // the data-gradient GEMM over 2H reads rows of 2H activations with 32-bit offsets
-    const long long eb = act_bytes(p->act_dtype);
+    const long long eb = act_bytes(bwd_act(p->act_dtype));
     if ((long long)p->T * p->top_k * 2 * p->d_hidden * eb >= (1LL << 32)) return MOE_ERR_SHAPE;
     // the weight-gradient GEMMs read the transposed operands with 32-bit offsets
-    if (p->act_dtype == MOE_BF16 &&
+    if (bwd_act(p->act_dtype) == MOE_BF16 &&
         (long long)std::max(p->d_model, 2 * p->d_hidden) * bwd_rp(*p) * 2 >= (1LL << 32))
         return MOE_ERR_SHAPE;
     return MOE_OK;
@@ -461,37 +489,44 @@ int32_t moe_backward_weight_bytes(const moe_problem* p, size_t* bytes) {
     int32_t st = check_backward(p);
     if (st) return st;
     if (!bytes) return MOE_ERR_NULL;
-    *bytes = align256((size_t)p->n_experts * p->d_model * 2 * p->d_hidden * act_bytes(p->act_dtype));
+    *bytes = bwd_packed_layout(*p).total;
     return MOE_OK;
 }
 
-int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up, void* packed_bwd,
-                                  void* stream) {
+int32_t moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up, const void* w_down,
+                                  void* packed_bwd, void* stream) {
     int32_t st = check_backward(p);
     if (st) return st;
-    if (!w_gate || !w_up || !packed_bwd) return MOE_ERR_NULL;
-    return launched(launch_pack_w1t(p->act_dtype, w_gate, w_up, packed_bwd, p->n_experts, p->d_model, p->d_hidden,
-                                    static_cast<hipStream_t>(stream)));
+    if (!w_gate || !w_up || !w_down || !packed_bwd) return MOE_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const BwdPacked P = bwd_packed_layout(*p);
+    const int E = p->n_experts, d = p->d_model, H = p->d_hidden;
+    if (p->act_dtype == MOE_MXFP8)
+        return launched(launch_pack_bwd_mx(w_gate, w_up, w_down, at(packed_bwd, P.w1t), at(packed_bwd, P.w1),
+                                           at(packed_bwd, P.wd), E, d, H, s));
+    if ((st = launched(launch_pack_w1t(p->act_dtype, w_gate, w_up, at(packed_bwd, P.w1t), E, d, H, s)))) return st;
+    return launched(launch_copy_bytes(w_down, at(packed_bwd, P.wd), (size_t)E * H * d * act_bytes(p->act_dtype), s));
 }
 
-int32_t moe_backward(const moe_problem* p, const void* dy, const void* w_router,
-                     const void* w_down, const void* packed_w, const void* packed_bwd, const int32_t* topk_idx,
-                     const float* topk_gate, const int32_t* offsets, const int32_t* pos, const void* fwd_ws,
-                     size_t fwd_ws_bytes, void* dx, float* dlogits, float* dw_gate, float* dw_up, float* dw_down,
-                     float* dw_router, void* ws, size_t ws_bytes, void* stream) {
+int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const void* w_router, const void* packed_w,
+                     const void* packed_bwd, const int32_t* topk_idx, const float* topk_gate, const int32_t* offsets,
+                     const int32_t* pos, const void* fwd_ws, size_t fwd_ws_bytes, void* dx, float* dlogits,
+                     float* dw_gate, float* dw_up, float* dw_down, float* dw_router, void* ws, size_t ws_bytes,
+                     void* stream) {
     int32_t st = check_backward(p);
     if (st) return st;
     const bool given = p->flags & MOE_LOGITS_GIVEN;
-    if (!dy || !w_down || !packed_w || !packed_bwd || !fwd_ws || !dx || !dlogits || !dw_gate || !dw_up ||
-        !dw_down || !ws)
+    const bool mx = p->act_dtype == MOE_MXFP8;
+    if (!dy || !packed_bwd || !fwd_ws || !dx || !dlogits || !dw_gate || !dw_up || !dw_down || !ws ||
+        (!mx && !packed_w))
         return MOE_ERR_NULL;
-    if (!given && (!w_router || !dw_router)) return MOE_ERR_NULL;
+    if (!given && (!x || !w_router || !dw_router)) return MOE_ERR_NULL;
     const Layout L = layout(*p);
     const BwdLayout BL = bwd_layout(*p);
     if (fwd_ws_bytes < L.total || ws_bytes < BL.total) return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int T = p->T, E = p->n_experts, k = p->top_k, d = p->d_model, H = p->d_hidden;
-    const int R = T * k, act = p->act_dtype;
+    const int R = T * k, act = bwd_act(p->act_dtype);
     // forward state: the caller's arrays, or the workspace copies moe_forward wrote
     void* fw = const_cast<void*>(fwd_ws);
     const int32_t* idx = topk_idx ? topk_idx : reinterpret_cast<const int32_t*>(at(fw, L.idx));
@@ -501,47 +536,58 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* w_router,
     const void* xe = at(fw, L.xe);
     const void* h = at(fw, L.h);
     const void* ye = at(fw, L.ye);
+    const BwdPacked BP = bwd_packed_layout(*p);
+    const char* pb = static_cast<const char*>(packed_bwd);
+    const void* w1 = mx ? static_cast<const void*>(pb + BP.w1)
+                        : static_cast<const void*>(static_cast<const char*>(packed_w) + packed_layout(*p).w1);
+    if (mx) {   // dequantise the saved MXFP8 activations; the rest runs in bf16
+        uint16_t* xe16 = reinterpret_cast<uint16_t*>(at(ws, BL.xe16));
+        uint16_t* h16 = reinterpret_cast<uint16_t*>(at(ws, BL.h16));
+        if ((st = launched(launch_dq_mxfp8(static_cast<const uint8_t*>(xe),
+                                           reinterpret_cast<const uint8_t*>(at(fw, L.xe_scale)), R, d, xe16, s))))
+            return st;
+        if ((st = launched(launch_dq_mxfp8(static_cast<const uint8_t*>(h),
+                                           reinterpret_cast<const uint8_t*>(at(fw, L.h_scale)), R, H, h16, s))))
+            return st;
+        xe = xe16;
+        h = h16;
+    }
     void* ab = at(ws, BL.ab);
     void* dye = at(ws, BL.dye);   // later dxe
     void* dh = at(ws, BL.dh);
     float* dsel = reinterpret_cast<float*>(at(ws, BL.dsel));
-    const Packed P = packed_layout(*p);
-    const char* pw = static_cast<const char*>(packed_w);
 
     if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, T, d, E, k, s)))) return st;
-    if ((st = launched(launch_gemm_plain(act, xe, pw + P.w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
-    if ((st = launched(launch_gemm_plain(act, dye, w_down, dh, off, R, E, H, d, H, s)))) return st;
+    if ((st = launched(launch_gemm_plain(act, xe, w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
+    if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
     const bool bf = act == MOE_BF16;
     int32_t* poff = reinterpret_cast<int32_t*>(at(ws, BL.poff));
     int32_t* rowdst = reinterpret_cast<int32_t*>(at(ws, BL.rowdst));
     uint16_t* ta = reinterpret_cast<uint16_t*>(at(ws, BL.ta));
     uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, BL.tb));
+    auto transpose = [&](const void* X, int M, uint16_t* XT) {
+        return launched(launch_transpose_seg(static_cast<const uint16_t*>(X), R, M, off, poff, rowdst, E, BL.Rp, XT, s));
+    };
     if (bf) {
         if ((st = launched(launch_seg_pad(off, E, R, poff, rowdst, s)))) return st;
-        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(h), R, H, off, poff, rowdst, E, BL.Rp, ta, s))))
-            return st;
-        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(dye), R, d, off, poff, rowdst, E, BL.Rp, tb, s))))
-            return st;
+        if ((st = transpose(h, H, ta)) || (st = transpose(dye, d, tb))) return st;
         if ((st = launched(launch_wgrad_mfma(0, ta, tb, poff, E, H, d, BL.Rp, dw_down, nullptr, s)))) return st;
     } else if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) {
         return st;
     }
     if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;
     if (bf) {
-        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(xe), R, d, off, poff, rowdst, E, BL.Rp, ta, s))))
-            return st;
-        if ((st = launched(launch_transpose_seg(static_cast<const uint16_t*>(ab), R, 2 * H, off, poff, rowdst, E, BL.Rp, tb,
-                                                s))))
-            return st;
+        if ((st = transpose(xe, d, ta)) || (st = transpose(ab, 2 * H, tb))) return st;
         if ((st = launched(launch_wgrad_mfma(1, ta, tb, poff, E, d, 2 * H, BL.Rp, dw_gate, dw_up, s)))) return st;
     } else if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) {
         return st;
     }
-    if ((st = launched(launch_gemm_plain(act, ab, packed_bwd, dye, off, R, E, d, 2 * H, d, s)))) return st;
+    if ((st = launched(launch_gemm_plain(act, ab, pb + BP.w1t, dye, off, R, E, d, 2 * H, d, s)))) return st;
     void* wrt = given ? nullptr : at(ws, BL.wrt);
     if (!given && (st = launched(launch_router_transpose(act, w_router, d, E, wrt, s)))) return st;
     if ((st = launched(launch_dx(act, dye, ps, idx, dsel, wrt, dx, T, d, E, k, s)))) return st;
-    if (!given && (st = launched(launch_wgrad_router(act, xe, ps, dsel, off, T, k, d, E,
+    const int32_t* row_token = reinterpret_cast<const int32_t*>(at(fw, L.row_token));
+    if (!given && (st = launched(launch_wgrad_router(act, x, row_token, ps, dsel, off, T, k, d, E,
                                                       reinterpret_cast<float*>(at(ws, BL.srow)),
                                                       reinterpret_cast<float*>(at(ws, BL.rpart)), dw_router, s))))
         return st;

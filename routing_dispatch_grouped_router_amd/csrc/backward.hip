@@ -36,6 +36,13 @@ struct bf16raw {
 __device__ __forceinline__ float ldv(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ float ldv(const bf16raw* p, size_t i) { return bf16_to_f32(p[i].v); }
 
+// E4M3 "FN" code to float (bias 7; exponent 0 is subnormal with step 2^-9).
+__device__ __forceinline__ float e4m3_val(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float a = e ? ldexpf(1.0f + (float)m * 0.125f, (int)e - 7) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -a : a;
+}
+
 template <bool BF>
 __device__ __forceinline__ void load_chunk(const void* base, size_t chunk, float (&v)[8]) {
     if (BF) {
@@ -388,14 +395,17 @@ __global__ __launch_bounds__(256) void srow_kernel(const int32_t* __restrict__ p
     for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) srow[pos[i]] = dsel[i];
 }
 
-// dW_r[c][e] = sum over expert e's rows r of xe[r][c] srow[r], in two passes.
+// dW_r[c][e] = sum over expert e's rows r of x[row_token[r]][c] srow[r] (the
+// token rows themselves: for MXFP8 blocks xe holds their quantised values), in
+// two passes.
 // Pass 1: the rows are cut into tiles of 64 within each expert (the grouped
 // GEMMs' tile schedule with 64-row tiles); a workgroup sums its tile's rows in
 // order, 8 columns per thread with 16-byte loads, into part[tile][d], and
 // workgroup 0 stores the schedule tstart[E + 1].  Pass 2: dW_r[c][e] = sum of
 // part[tile][c] over expert e's tiles in order.
 template <bool BF>
-__global__ __launch_bounds__(256) void router_wgrad_rows_kernel(const void* __restrict__ xe,
+__global__ __launch_bounds__(256) void router_wgrad_rows_kernel(const void* __restrict__ x,
+                                                                const int32_t* __restrict__ row_token,
                                                                 const float* __restrict__ srow,
                                                                 const int32_t* __restrict__ offsets, int E, int d,
                                                                 float* __restrict__ part, int32_t* __restrict__ tstart) {
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(256) void router_wgrad_rows_kernel(const void* __re
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
         for (int r = 0; r < rows; ++r) {
             float v[8];
-            load_chunk<BF>(xe, (size_t)(row0 + r) * chunks + c, v);
+            load_chunk<BF>(x, (size_t)row_token[row0 + r] * chunks + c, v);
             const float sv = srow[row0 + r];
 #pragma unroll
             for (int i = 0; i < NV; ++i) acc[i] = fmaf(v[i], sv, acc[i]);
@@ -463,6 +473,31 @@ __global__ __launch_bounds__(256) void transpose_small_kernel(const T* __restric
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
         const int e = (int)(i / d), c = (int)(i % d);
         wt[i] = w[(size_t)c * E + e];
+    }
+}
+
+// MXFP8 activations to bfloat16: codes [R][K] with E8M0 scales [K/128][R][4]
+// (the dispatch / GEMM1 layout); 16 codes per thread, exact (an E4M3 value
+// times a power of two has at most 4 significant bits).
+__global__ __launch_bounds__(256) void dq_mxfp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sc,
+                                                       int R, int K, uint16_t* __restrict__ out) {
+    const int per_row = K / 16;
+    const size_t n = (size_t)R * per_row;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        const int r = (int)(i / per_row), c16 = (int)(i - (size_t)r * per_row);
+        const int blk = c16 / 2;   // 32-value block
+        const int se = (int)sc[((size_t)(blk / 4) * R + r) * 4 + (blk % 4)] - 127;
+        const u32x4 w = reinterpret_cast<const u32x4*>(q + (size_t)r * K)[c16];
+        uint32_t o[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint32_t word = w[b >> 1];
+            const uint32_t c0 = (word >> (16 * (b & 1))) & 0xFFu, c1 = (word >> (16 * (b & 1) + 8)) & 0xFFu;
+            o[b] = pack_bf16x2(ldexpf(e4m3_val(c0), se), ldexpf(e4m3_val(c1), se));
+        }
+        u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)r * K) + 2 * c16;
+        dst[0] = (u32x4){o[0], o[1], o[2], o[3]};
+        dst[1] = (u32x4){o[4], o[5], o[6], o[7]};
     }
 }
 
@@ -526,19 +561,19 @@ size_t router_wgrad_part_bytes(int R, int E, int d) {
     return (size_t)(R / 64 + std::min(E, R)) * d * 4 + ((size_t)E + 1) * 4 + 256;
 }
 
-hipError_t launch_wgrad_router(int act, const void* xe, const int32_t* pos, const float* dsel, const int32_t* offsets,
-                               int T, int k, int d, int E, float* srow, float* part, float* dw_router,
-                               hipStream_t s) {
+hipError_t launch_wgrad_router(int act, const void* x, const int32_t* row_token, const int32_t* pos,
+                               const float* dsel, const int32_t* offsets, int T, int k, int d, int E, float* srow,
+                               float* part, float* dw_router, hipStream_t s) {
     const int R = T * k;
     hipLaunchKernelGGL(srow_kernel, dim3(std::min((R + 255) / 256, 1024)), dim3(256), 0, s, pos, dsel, R, srow);
     const int tiles = R / 64 + std::min(E, R);
     int32_t* tstart = reinterpret_cast<int32_t*>(part + (size_t)tiles * d);
     if (act == kF32)
-        hipLaunchKernelGGL(router_wgrad_rows_kernel<false>, dim3(tiles), dim3(256), 0, s, xe, srow, offsets, E, d,
-                           part, tstart);
+        hipLaunchKernelGGL(router_wgrad_rows_kernel<false>, dim3(tiles), dim3(256), 0, s, x, row_token, srow, offsets,
+                           E, d, part, tstart);
     else
-        hipLaunchKernelGGL(router_wgrad_rows_kernel<true>, dim3(tiles), dim3(256), 0, s, xe, srow, offsets, E, d,
-                           part, tstart);
+        hipLaunchKernelGGL(router_wgrad_rows_kernel<true>, dim3(tiles), dim3(256), 0, s, x, row_token, srow, offsets,
+                           E, d, part, tstart);
     const int n = d * E;
     hipLaunchKernelGGL(router_wgrad_reduce_kernel, dim3(std::min((n + 255) / 256, 1024)), dim3(256), 0, s, part,
                        tstart, d, E, dw_router);
@@ -590,6 +625,13 @@ hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* 
     hipLaunchKernelGGL(transpose_seg_kernel, grid, dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
     dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
     hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);
+    return hipGetLastError();
+}
+
+hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s) {
+    const size_t n = (size_t)R * (K / 16);
+    const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid), dim3(256), 0, s, q, sc, R, K, out);
     return hipGetLastError();
 }
 

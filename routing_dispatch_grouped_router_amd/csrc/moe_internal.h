@@ -86,6 +86,14 @@ hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void
 
 // ---------------------------------------------------------------- backward (backward.hip, pack.hip)
 
+// MXFP8 blocks' backward caches (bfloat16, the forward's quantised values): W1T [E][d][2H],
+// packed W1 [E][2H][d] and W_down [E][H][d] from bf16 w_gate, w_up, w_down.
+hipError_t launch_pack_bwd_mx(const void* w_gate, const void* w_up, const void* w_down, void* w1t, void* w1,
+                              void* wdq, int E, int d, int H, hipStream_t s);
+hipError_t launch_copy_bytes(const void* src, void* dst, size_t bytes, hipStream_t s);
+// MXFP8 codes [R][K] + scales [K/128][R][4] to bfloat16 [R][K].
+hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s);
+
 // W1T [E][d][2H] from w_gate, w_up [E][d][H] (float32 or bfloat16).
 hipError_t launch_pack_w1t(int act, const void* w_gate, const void* w_up, void* out, int E, int d, int H,
                            hipStream_t s);
@@ -104,13 +112,13 @@ hipError_t launch_wgrad_down(int act, const void* h, const void* dye, const int3
                              int d, float* dw_down, hipStream_t s);
 hipError_t launch_wgrad_w1(int act, const void* xe, const void* dab, const int32_t* offsets, int E, int R, int d,
                            int H, float* dw_gate, float* dw_up, hipStream_t s);
-// dw_router[c][e] = sum over expert e's rows of xe[r][c] srow[r], srow[pos[t][j]] = dsel[t][j]
-// (= x^T dL, dL being zero outside the selected experts): srow T k floats, part
+// dw_router[c][e] = sum over expert e's rows r of x[row_token[r]][c] srow[r], srow[pos[t][j]] =
+// dsel[t][j] (= x^T dL, dL being zero outside the selected experts): srow T k floats, part
 // router_wgrad_part_bytes(T k, E, d) bytes.
 size_t router_wgrad_part_bytes(int R, int E, int d);
-hipError_t launch_wgrad_router(int act, const void* xe, const int32_t* pos, const float* dsel, const int32_t* offsets,
-                               int T, int k, int d, int E, float* srow, float* part, float* dw_router,
-                               hipStream_t s);
+hipError_t launch_wgrad_router(int act, const void* x, const int32_t* row_token, const int32_t* pos,
+                               const float* dsel, const int32_t* offsets, int T, int k, int d, int E, float* srow,
+                               float* part, float* dw_router, hipStream_t s);
 // W_r^T [E][d] from W_r [d][E] (activation type).
 hipError_t launch_router_transpose(int act, const void* w_router, int d, int E, void* wrt, hipStream_t s);
 

@@ -109,6 +109,82 @@ hipError_t launch_pack_w1t(int act, const void* w_gate, const void* w_up, void* 
     return hipGetLastError();
 }
 
+// E4M3 "FN" code to float (sign, 4-bit exponent with bias 7, 3-bit mantissa;
+// exponent 0 is subnormal with step 2^-9).  Codes 0x7F / 0xFF (NaN) are never
+// produced by the saturating encoder.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float a = e ? ldexpf(1.0f + (float)m * 0.125f, (int)e - 7) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -a : a;
+}
+
+// Backward weight caches of an MXFP8 block, in bfloat16, holding the values the
+// forward multiplied with (quantise then dequantise in the forward's blocks).
+// which == 1: a 32 (d) x 64 (packed W1 column n) tile of w_gate / w_up, blocks
+// of 32 along d, written both as W1T [E][d][2H] and as packed W1 [E][2H][d].
+// which == 2: a 32 (H) x 64 (d) tile of w_down [E][H][d], blocks of 32 along H,
+// written back in the same layout.
+__global__ __launch_bounds__(256) void fq_pack_kernel(const uint16_t* __restrict__ wg, const uint16_t* __restrict__ wu,
+                                                      const uint16_t* __restrict__ wd, uint16_t* __restrict__ w1t,
+                                                      uint16_t* __restrict__ w1, uint16_t* __restrict__ wdq, int which,
+                                                      int E, int d, int H) {
+    __shared__ float tile[32][65];
+    const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 32, e = blockIdx.z;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 32 * 64; i += 256) {
+        const int kk = i >> 6, nn = i & 63;
+        const int n = n0 + nn, k = k0 + kk;
+        float v;
+        if (which == 1) {
+            const int h = 32 * (n >> 6) + (n & 31);
+            v = bf16_to_f32((((n >> 5) & 1) ? wu : wg)[((size_t)e * d + k) * H + h]);
+        } else {
+            v = bf16_to_f32(wd[((size_t)e * H + k) * d + n]);
+        }
+        tile[kk][nn] = v;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        float amax = 0.f;
+        for (int kk = 0; kk < 32; ++kk) amax = fmaxf(amax, fabsf(tile[kk][tid]));
+        const int se = mx_shared_exp(amax);
+        const float inv = mx_inv_scale(se);
+        for (int kk = 0; kk < 32; ++kk) tile[kk][tid] = ldexpf(e4m3_value(e4m3_encode(tile[kk][tid] * inv)), se);
+    }
+    __syncthreads();
+    if (which == 1) {
+        const int N = 2 * H;
+        for (int i = tid; i < 32 * 64; i += 256) {   // W1T rows k (d), contiguous n
+            const int kk = i >> 6, nn = i & 63;
+            w1t[((size_t)e * d + k0 + kk) * N + n0 + nn] = f32_to_bf16(tile[kk][nn]);
+        }
+        for (int i = tid; i < 32 * 64; i += 256) {   // packed W1 rows n, contiguous k
+            const int nn = i >> 5, kk = i & 31;
+            w1[((size_t)e * N + n0 + nn) * d + k0 + kk] = f32_to_bf16(tile[kk][nn]);
+        }
+    } else {
+        for (int i = tid; i < 32 * 64; i += 256) {
+            const int kk = i >> 6, nn = i & 63;
+            wdq[((size_t)e * H + k0 + kk) * d + n0 + nn] = f32_to_bf16(tile[kk][nn]);
+        }
+    }
+}
+
+hipError_t launch_pack_bwd_mx(const void* w_gate, const void* w_up, const void* w_down, void* w1t, void* w1,
+                              void* wdq, int E, int d, int H, hipStream_t s) {
+    auto wg = static_cast<const uint16_t*>(w_gate), wu = static_cast<const uint16_t*>(w_up),
+         wd = static_cast<const uint16_t*>(w_down);
+    auto o1 = static_cast<uint16_t*>(w1t), o2 = static_cast<uint16_t*>(w1), o3 = static_cast<uint16_t*>(wdq);
+    hipLaunchKernelGGL(fq_pack_kernel, dim3((2 * H) / 64, d / 32, E), dim3(256), 0, s, wg, wu, wd, o1, o2, o3, 1, E, d,
+                       H);
+    hipLaunchKernelGGL(fq_pack_kernel, dim3(d / 64, H / 32, E), dim3(256), 0, s, wg, wu, wd, o1, o2, o3, 2, E, d, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_bytes(const void* src, void* dst, size_t bytes, hipStream_t s) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+}
+
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
                        void* w2, uint8_t* s1, uint8_t* s2, int E, int d, int H, hipStream_t s) {
     dim3 block(256);

@@ -136,10 +136,12 @@ def test_workspace_and_packed_sizes(lib, name):
     assert want <= pw < want + 4 * 256
 
 
-def test_backward_rejects_mxfp8_nulls_and_small_workspaces(lib):
+def test_backward_rejects_identity_nulls_and_small_workspaces(lib):
     n = ctypes.c_size_t()
     pm = _prob(act="mxfp8", d=128, H=128)
-    assert lib.moe_backward_workspace_bytes(ctypes.byref(pm), ctypes.byref(n)) == -3
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(pm), ctypes.byref(n)) == 0
+    pi = _prob(identity=True)
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(pi), ctypes.byref(n)) == -3
     p = _prob(logits_given=True)
     assert lib.moe_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
     bws = n.value
@@ -148,7 +150,9 @@ def test_backward_rejects_mxfp8_nulls_and_small_workspaces(lib):
     assert n.value >= p.n_experts * p.d_model * 2 * p.d_hidden * 2
     fws = B.workspace_bytes(p)
     fake = ctypes.c_void_p(0x1000)
-    args = [ctypes.byref(p), fake, None, fake, fake, fake, None, None, None, None, fake, fws,
+    # p, dy, x, w_router, packed_w, packed_bwd, idx, gate, offsets, pos, fwd_ws, fwd_ws_bytes,
+    # dx, dlogits, dw_gate, dw_up, dw_down, dw_router, ws, ws_bytes, stream
+    args = [ctypes.byref(p), fake, None, None, fake, fake, None, None, None, None, fake, fws,
             fake, fake, fake, fake, fake, None, fake, bws, None]
     bad_fwd = list(args)
     bad_fwd[11] = fws - 1
@@ -159,7 +163,7 @@ def test_backward_rejects_mxfp8_nulls_and_small_workspaces(lib):
     no_dy = list(args)
     no_dy[1] = None
     assert lib.moe_backward(*no_dy) == -1
-    # learned router: w_router and dw_router are required
+    # learned router: x, w_router and dw_router are required
     pl = _prob()
     args_l = list(args)
     args_l[0] = ctypes.byref(pl)

@@ -5,7 +5,9 @@ router, the float32 logits it computed; routing itself is checked bit-exact
 by the forward tests) and differentiates its own forward of that routing.
 
 Bars (normwise relative = max|got - ref| / max|ref|, per output): float32
-1e-5; bf16 2e-2 (as the forward outputs).  Two calls are bitwise equal.
+1e-5; bf16 2e-2 (as the forward outputs); MXFP8 blocks, whose backward runs in
+bf16 on the dequantised activations and the forward's MXFP8 weight values,
+2e-2.  Two calls are bitwise equal.
 """
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ from routing_dispatch_grouped_router_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "mxfp8": 2e-2}
 
 
 def _f64(t):
@@ -49,6 +51,11 @@ CASES = [
                empty_experts=(0, 3, 7)),
     W.Workload("bwd_bf16_k_eq_E", T=130, d=64, E=4, k=4, H=128, act="bf16", router="random", seed=4008),
     W.Workload("bwd_bf16_tk_lt_E", T=3, d=64, E=16, k=2, H=64, act="bf16", router="random", seed=4009),
+    W.Workload("bwd_mx_random", T=600, d=256, E=16, k=4, H=256, act="mxfp8", router="random", seed=4010,
+               outlier_frac=0.01),
+    W.Workload("bwd_mx_learned", T=400, d=256, E=8, k=2, H=128, act="mxfp8", router="learned", seed=4011),
+    W.Workload("bwd_mx_empty", T=70, d=128, E=8, k=2, H=128, act="mxfp8", router="random", seed=4012,
+               empty_experts=(1, 6), outlier_frac=0.05),
 ]
 
 
@@ -57,7 +64,7 @@ def _run(w):
     dev = {k: (None if v is None else v.to(DEV)) for k, v in host.items()}
     p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned")
     packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
-    packed_bwd = B.pack_weights_backward(p, dev["w_gate"], dev["w_up"])
+    packed_bwd = B.pack_weights_backward(p, dev["w_gate"], dev["w_up"], dev["w_down"])
     fwd = B.Forward(p, DEV)
     fwd(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
     rng = np.random.default_rng(w.seed + 17)
@@ -66,7 +73,7 @@ def _run(w):
     bwd = B.Backward(p, DEV)
     outs = []
     for _ in range(2):
-        g = bwd(fwd, dy, dev["w_down"], packed, packed_bwd, w_router=dev["w_router"])
+        g = bwd(fwd, dy, packed, packed_bwd, x=dev["x"], w_router=dev["w_router"])
         torch.cuda.synchronize()
         outs.append({k: (None if v is None else v.clone()) for k, v in g.items()})
     return host, fwd, dy_host, outs
@@ -86,6 +93,9 @@ def test_backward_against_oracle(w):
     fo = O.forward(x, w.E, w.k, w.act, wg, wu, wd, logits=logits)
     assert np.array_equal(fo["idx"], fwd.idx.cpu().numpy()), "routing differs from the oracle's"
     wr = W.as_f64(host["w_router"]) if w.router == "learned" else None
+    if w.act == "mxfp8":   # the forward's weight values: MXFP8 blocks along each GEMM's contraction axis
+        q = [O.expert_weights(wg, wu, wd, e, "mxfp8") for e in range(w.E)]
+        wg, wu, wd = (np.stack([t[i] for t in q]) for i in range(3))
     ref = BW.backward(x, W.as_f64(dy_host), fo, w.act, wg, wu, wd, w_router=wr)
     for name in ("dx", "dlogits", "dw_gate", "dw_up", "dw_down"):
         _check(name, _f64(g[name]), ref[name], w.act)
