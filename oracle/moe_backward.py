@@ -51,6 +51,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import moe_oracle as F
+from . import mxfp8
 
 
 def store(v, act: str) -> np.ndarray:
@@ -189,3 +190,69 @@ def backward(x, dy, fwd: dict, act: str, w_gate, w_up, w_down, w_router=None) ->
         dwr = store_f32(x.T @ dL, act)
     return dict(dx=store(dx, act), dlogits=dL, dw_gate=dwg, dw_up=dwu, dw_down=dwd, dw_router=dwr,
                 dgate=dgate, dye=dye)
+
+
+# ----------------------------------------------------------------------------- sampled outputs (large blocks)
+
+
+def backward_tokens(x, dy, idx, gate, tokens, n_experts: int, act: str, w_gate, w_up, w_down,
+                    w_router=None) -> dict:
+    """dx and dlogits of the listed tokens only, given the block's routing.
+
+    Every routed row passes through its expert independently, so a token's
+    gradient rows depend only on its own rows; this evaluates ``backward``'s
+    definitions for those rows (expert weights indexed per expert, e.g. lazily
+    converted stacks).  Returns dict(dx [n, d], dlogits [n, E], dgate [n, k]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    idx = np.asarray(idx, dtype=np.int64)
+    gate = np.asarray(gate, dtype=np.float64)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    k = idx.shape[1]
+    rows = x[tokens]
+    if act == "mxfp8":
+        rows = mxfp8.fake_quantize(rows, axis=1)
+    cache = {}
+    dgate = np.zeros((len(tokens), k))
+    drows = np.zeros((len(tokens), k, x.shape[1]))
+    for i, t in enumerate(tokens):
+        for j in range(k):
+            e = int(idx[t, j])
+            if e not in cache:
+                cache[e] = F.expert_weights(w_gate, w_up, w_down, e, act)
+            wg, wu, wd = cache[e]
+            ye = F.expert_ffn(rows[i:i + 1], wg, wu, wd, act)[0]
+            dgate[i, j] = np.dot(dy[t], ye)
+            dye = store(gate[t, j] * dy[t], act)
+            drows[i, j] = expert_backward(rows[i:i + 1], dye[None, :], wg, wu, wd, act)[0][0]
+    dgate = store_f32(dgate, act)
+    dL = router_backward(dgate, gate[tokens], idx[tokens], n_experts, act)
+    dx = drows.sum(axis=1)
+    if w_router is not None:
+        dx = dx + dL @ np.asarray(w_router, np.float64).T
+    return dict(dx=store(dx, act), dlogits=dL, dgate=dgate)
+
+
+def weight_grad_columns(rows, dye_rows, wg, wu, wd, act: str, hcols) -> dict:
+    """Columns hcols of one expert's dW_gate and dW_up and rows hcols of its
+    dW_down, from all of the expert's rows (rows: the dispatched values, dye_rows:
+    the gated output gradients, in the expert's row order).  For MXFP8 blocks
+    hcols must be whole 32-wide blocks of hidden units (h is quantised in
+    blocks along H).  Equal to the same entries of ``expert_backward``.
+    """
+    rows = np.asarray(rows, np.float64)
+    dye_rows = np.asarray(dye_rows, np.float64)
+    hc = np.asarray(hcols, np.int64)
+    a_exact = rows @ wg[:, hc]
+    b_exact = rows @ wu[:, hc]
+    h = F.silu(a_exact) * b_exact
+    if act != "f64":
+        h = F.store(h, F.intermediate_dtypes(act)[0])
+    a = store(a_exact, act)
+    b = store(b_exact, act)
+    dh = store(dye_rows @ wd[hc, :].T, act)
+    da = store(dh * b * silu_grad(a), act)
+    db = store(dh * F.silu(a), act)
+    return dict(dw_gate=store_f32(rows.T @ da, act), dw_up=store_f32(rows.T @ db, act),
+                dw_down=store_f32(h.T @ dye_rows, act))

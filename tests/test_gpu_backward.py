@@ -15,6 +15,7 @@ import torch
 
 from oracle import moe_backward as BW
 from oracle import moe_oracle as O
+from oracle import mxfp8 as MX
 from routing_dispatch_grouped_router_amd import binding as B
 from routing_dispatch_grouped_router_amd import workloads as W
 
@@ -103,3 +104,79 @@ def test_backward_against_oracle(w):
         _check("dw_router", _f64(g["dw_router"]), ref["dw_router"], w.act)
     if w.E == 1:
         assert torch.count_nonzero(g["dlogits"]) == 0
+
+
+# --------------------------------------------------------------------------- full size
+
+
+class _LazyF64:
+    """Per-expert float64 view of a stored weight stack, converted on access."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, e):
+        return W.as_f64(self.t[e])
+
+
+def _sample_tokens(T, seed=0, n=24):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(8, T - 8), size=n - 16, replace=False)
+    return np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T), mid])).astype(np.int64)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["bf16_e8", "bf16_e128_random", "bf16_e64_zipf", "mxfp8_e128"])
+def test_full_size_backward(name):
+    """The backward at the benchmark's block sizes, run as bench.py runs it:
+    dx and dlogits on sampled tokens, every token's router gradient summing to
+    zero and vanishing off the selected experts, and one 32-wide block of
+    hidden units of dW_gate, dW_up and dW_down for the first and the last
+    non-empty expert, all against the oracle."""
+    w = W.CONFIGS[name]
+    print(f"[full backward] {w.describe()}", flush=True)
+    host, fwd, dy_host, outs = _run(w)
+    g = outs[0]
+    idx = fwd.idx.cpu().numpy().astype(np.int64)
+    gate = _f64(fwd.gate)
+    pos = fwd.pos.cpu().numpy().astype(np.int64)
+    offsets = fwd.offsets.cpu().numpy().astype(np.int64)
+    dy = W.as_f64(dy_host)
+    wr = W.as_f64(host["w_router"]) if w.router == "learned" else None
+    lw = [_LazyF64(host[n]) for n in ("w_gate", "w_up", "w_down")]
+    # every token: zero off the selected experts, rows summing to zero
+    dl = _f64(g["dlogits"])
+    mask = np.ones_like(dl, dtype=bool)
+    np.put_along_axis(mask, idx, False, axis=1)
+    assert np.all(dl[mask] == 0.0)
+    assert np.max(np.abs(dl.sum(axis=1))) <= 1e-5 * max(1e-30, np.max(np.abs(dl)))
+    # sampled tokens
+    toks = _sample_tokens(w.T)
+    x64 = W.as_f64(host["x"][torch.from_numpy(toks)])
+    xs = np.zeros((w.T, w.d))
+    xs[toks] = x64
+    ref = BW.backward_tokens(xs, dy, idx, gate, toks, w.E, w.act, *lw, w_router=wr)
+    _check("dx (sampled tokens)", _f64(g["dx"])[toks], ref["dx"], w.act)
+    _check("dlogits (sampled tokens)", dl[toks], ref["dlogits"], w.act)
+    # one block of hidden units of two experts' weight gradients
+    counts = np.diff(offsets)
+    live = np.nonzero(counts)[0]
+    row_token = np.empty(w.R, np.int64)
+    slot = np.empty(w.R, np.int64)
+    row_token[pos.reshape(-1)] = np.repeat(np.arange(w.T), w.k)
+    slot[pos.reshape(-1)] = np.tile(np.arange(w.k), w.T)
+    rng = np.random.default_rng(7)
+    for e in (int(live[0]), int(live[-1])):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        t = row_token[lo:hi]
+        rows = W.as_f64(host["x"][torch.from_numpy(t)])
+        if w.act == "mxfp8":
+            rows = MX.fake_quantize(rows, axis=1)
+        dye = BW.store(gate[t, slot[lo:hi]][:, None] * dy[t], w.act)
+        wg, wu, wd = O.expert_weights(*lw, e, w.act)
+        hb = int(rng.integers(0, w.H // 32)) * 32
+        hc = np.arange(hb, hb + 32)
+        c = BW.weight_grad_columns(rows, dye, wg, wu, wd, w.act, hc)
+        _check(f"dw_gate[{e}][:, {hb}:+32]", _f64(g["dw_gate"][e][:, hb:hb + 32]), c["dw_gate"], w.act)
+        _check(f"dw_up[{e}][:, {hb}:+32]", _f64(g["dw_up"][e][:, hb:hb + 32]), c["dw_up"], w.act)
+        _check(f"dw_down[{e}][{hb}:+32]", _f64(g["dw_down"][e][hb:hb + 32]), c["dw_down"], w.act)

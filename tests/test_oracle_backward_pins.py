@@ -148,3 +148,37 @@ def test_bf16_storage_points():
     for out in ("dx", "dw_gate", "dw_up", "dw_down", "dlogits"):
         rel = np.max(np.abs(g[out] - exact[out])) / np.max(np.abs(exact[out]))
         assert rel < 3e-2, (out, rel)
+
+
+@pytest.mark.parametrize("act,learned", [("f32", True), ("bf16", False), ("bf16", True), ("mxfp8", False)])
+def test_sampled_helpers_equal_the_whole_block(act, learned):
+    """backward_tokens and weight_grad_columns (used for large blocks) give the
+    same values as the whole-block backward."""
+    T, d, E, k, H = 30, 64, 4, 2, 64
+    b = _block(T, d, E, k, H, 61, learned)
+    rb = {n: (O.round_bf16(b[n]) if act != "f32" else O.round_f32(b[n])) for n in ("x", "wg", "wu", "wd", "dy")}
+    wr = None
+    if learned:
+        wr = O.round_bf16(b["wr"]) if act != "f32" else O.round_f32(b["wr"])
+        logits = O.router_logits(rb["x"], wr)
+    else:
+        logits = O.round_f32(b["logits"])
+    fwd = O.forward(rb["x"], E, k, act, rb["wg"], rb["wu"], rb["wd"], logits=logits)
+    q = [O.expert_weights(rb["wg"], rb["wu"], rb["wd"], e, act) for e in range(E)]
+    wg, wu, wd = (np.stack([t[i] for t in q]) for i in range(3))
+    g = BW.backward(rb["x"], rb["dy"], fwd, act, wg, wu, wd, w_router=wr)
+    toks = np.array([0, 3, 17, 29])
+    s = BW.backward_tokens(rb["x"], rb["dy"], fwd["idx"], fwd["gate"], toks, E, act, rb["wg"], rb["wu"], rb["wd"],
+                           w_router=wr)
+    np.testing.assert_array_equal(s["dx"], g["dx"][toks])
+    np.testing.assert_array_equal(s["dlogits"], g["dlogits"][toks])
+    off = fwd["offsets"]
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        hc = np.arange(32, 64)
+        c = BW.weight_grad_columns(fwd["xe"][lo:hi], g["dye"][lo:hi], wg[e], wu[e], wd[e], act, hc)
+        np.testing.assert_allclose(c["dw_gate"], g["dw_gate"][e][:, hc], rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(c["dw_up"], g["dw_up"][e][:, hc], rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(c["dw_down"], g["dw_down"][e][hc, :], rtol=1e-6, atol=1e-6)
