@@ -17,9 +17,10 @@ enum Act { kF32 = 0, kBF16 = 1, kMXFP8 = 2 };
 
 inline int route_blocks(int T) { return (T + kRouteBlock - 1) / kRouteBlock; }
 
-// logits[T][E] = x[T][d] . w[d][E]   (x, w float32 or bfloat16; fp32 accumulate)
+// logits[T][E] = x[T][d] . w[d][E]   (x, w float32 or bfloat16; fp32 accumulate).
+// bfloat16: wt is scratch for w^T [E][d] (E d bfloat16), then MFMA.
 hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
-                                int E, hipStream_t s);
+                                int E, uint16_t* wt, hipStream_t s);
 
 // Top-k + gates + per-block histogram and within-block ranks.
 //   rank[T][k]   : rank of token t among the tokens of its routing block routed to the same expert

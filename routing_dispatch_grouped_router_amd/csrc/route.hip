@@ -9,6 +9,8 @@
 // its tokens; a token's rank is a popcount of the bits below it, and a single
 // scan over (block, expert) histograms turns ranks into global positions.
 // Results are therefore identical from run to run.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -50,7 +52,7 @@ __device__ __forceinline__ void load8w<float>(const float* p, float (&v)[8]) { l
 template <>
 __device__ __forceinline__ void load8w<uint16_t>(const uint16_t* p, float (&v)[8]) { load8<uint16_t>(p, v); }
 
-// One workgroup of 4 waves computes 8 tokens x 8 experts at a time; wave w
+// float32 router logits.  One workgroup of 4 waves computes 8 tokens x 8 experts at a time; wave w
 // takes the w-th quarter of d, its lanes runs of 8 elements of it (so 4x as
 // many waves share the load of x as with one wave per token group).  The 64
 // partial sums of a lane are reduce-scattered across the wave (halving the
@@ -121,16 +123,80 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TIn* __restric
     }
 }
 
+// W^T [E][d] from the router weight W [d][E] (bfloat16), so that each
+// expert's weights are contiguous along d for the MFMA operand loads.
+__global__ __launch_bounds__(256) void router_wt_kernel(const uint16_t* __restrict__ w, int d, int E,
+                                                        uint16_t* __restrict__ wt) {
+    const int n = d * E;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+        const int e = i / d, c = i - e * d;
+        wt[i] = w[(size_t)c * E + e];
+    }
+}
+
+typedef __bf16 bf16x8_r __attribute__((ext_vector_type(8)));
+typedef float f32x4_r __attribute__((ext_vector_type(4)));
+
+// bf16 router logits on MFMA: L = x W as 16 x 16 output blocks of
+// v_mfma_f32_16x16x32_bf16 (lane l holds row l % 16 and k 8 (l / 16) .. +8 of
+// each operand; output element i of lane l is token row 4 (l / 16) + i and
+// expert column l % 16).  A workgroup owns 16 tokens and 16 experts; its four
+// waves take the four quarters of d, walking them in steps of 32 with both
+// operands loaded straight from global memory (x rows and rows of W^T, 16
+// bytes per lane, eight steps in flight), and the quarters' float32 sums are
+// added in wave order through LDS.  Rows past T and experts past E are
+// clamped in the loads and not stored.
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wt,
+                                                                 float* __restrict__ logits, int T, int d, int E) {
+    __shared__ f32x4_r red[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int ta = min(t0 + (lane & 15), T - 1), eb = min(e0 + (lane & 15), E - 1);
+    const int ns = d / 32, s_lo = wave * ns / 4, s_hi = (wave + 1) * ns / 4;   // this wave's 32-wide steps
+    const int kq = 8 * (lane >> 4);
+    const uint16_t* xa = x + (size_t)ta * d + kq;
+    const uint16_t* wb = wt + (size_t)eb * d + kq;
+    f32x4_r acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = s_lo; s0 < s_hi; s0 += 8) {
+        bf16x8_r a[8], b[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = 32 * min(s0 + u, s_hi - 1);   // a clamped step is loaded but not accumulated
+            a[u] = *reinterpret_cast<const bf16x8_r*>(xa + k);
+            b[u] = *reinterpret_cast<const bf16x8_r*>(wb + k);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < s_hi) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u], acc, 0, 0, 0);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        const f32x4_r s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        const int e = e0 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * (lane >> 4) + i;
+            if (t < T && e < E) logits[(size_t)t * E + e] = s[i];
+        }
+    }
+}
+
 hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
-                                int E, hipStream_t s) {
-    dim3 grid((T + kRtTok - 1) / kRtTok), block(256);
-    if (act == kF32)
+                                int E, uint16_t* wt, hipStream_t s) {
+    if (act == kF32) {
+        dim3 grid((T + kRtTok - 1) / kRtTok), block(256);
         hipLaunchKernelGGL(router_logits_kernel<float>, grid, block, 0, s,
                            static_cast<const float*>(x), static_cast<const float*>(w), logits, T, d, E);
-    else
-        hipLaunchKernelGGL(router_logits_kernel<uint16_t>, grid, block, 0, s,
-                           static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), logits, T,
-                           d, E);
+    } else {
+        const int n = d * E;
+        hipLaunchKernelGGL(router_wt_kernel, dim3(std::min((n + 255) / 256, 1024)), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(w), d, E, wt);
+        dim3 grid((T + 15) / 16, (E + 15) / 16), block(256);
+        hipLaunchKernelGGL(router_logits_mfma_kernel, grid, block, 0, s, static_cast<const uint16_t*>(x), wt, logits,
+                           T, d, E);
+    }
     return hipGetLastError();
 }
 
@@ -300,7 +366,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     __shared__ int32_t part[1024];
     __shared__ int32_t tot[1024];
     const int tid = threadIdx.x;
-    const int NC = 1024 / E;                       // chunks per expert (E <= 1024)
+    const int NC = max(1, min(1024 / E, nblk));    // chunks per expert (E <= 1024), at most one block each when few
     const int CS = (nblk + NC - 1) / NC;           // blocks per chunk
     const int e = tid % E, c = tid / E;
     const bool act = c < NC;
@@ -322,8 +388,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
         tot[tid] = 0;
     }
     __syncthreads();
-    // inclusive Hillis-Steele scan of tot[0..1024)
-    for (int off = 1; off < 1024; off <<= 1) {
+    // inclusive Hillis-Steele scan of tot[0..E) (entries past E are zero)
+    for (int off = 1; off < E; off <<= 1) {
         int v = tid >= off ? tot[tid - off] : 0;
         __syncthreads();
         tot[tid] += v;
