@@ -6,8 +6,10 @@ A step is one moe_forward (router -> top-k -> counts/offsets/positions ->
 dispatch -> grouped SwiGLU GEMMs -> combine) over one synthetic batch whose
 inputs already sit in HBM.  W untimed steps, then exactly K steps between two
 device synchronisations; one JSON line is printed.  Per-kernel durations come
-from HIP events the library records on the forward's own stream during the
-same timed steps; the dominant kernel is reported against its roofline.
+from HIP events the library records on the forward's own stream during K
+further steps run just before the timed ones (the events add small gaps
+between kernels, so those steps are reported separately and are not the
+headline); the dominant kernel is reported against its roofline.
 The CPU baseline times the float64 oracle on a bounded sample of the same
 batch on the host cores.
 
@@ -166,15 +168,18 @@ def host_sync_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device: fl
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    B.set_profiling(True)
+    B.set_profiling(True)      # the host wait measured by the library's events, in separate steps
+    for _ in range(min(steps, 20)):
+        run()
+    stages = dict(B.kernel_times())
+    B.set_profiling(False)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     start.record()
     for _ in range(steps):
         run()
     stop.record()
     torch.cuda.synchronize()
-    stages = dict(B.kernel_times())
-    B.set_profiling(False)
     ms = start.elapsed_time(stop) / steps
     return {"ms_per_step": round(ms, 5), "host_count_wait_ms": round(stages.get("host_count_wait", 0.0), 5),
             "slowdown_vs_device_resident": round(ms / ms_device, 4)}
@@ -242,6 +247,8 @@ def main(argv=None):
     ap.add_argument("--main-only", action="store_true",
                     help="skip the comparison measurements (cold cache, host-synchronising path, router "
                          "statistics), e.g. under a profiler")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph instead of eager launches")
     ap.add_argument("--with-backward", action="store_true",
                     help="also time moe_backward when --main-only is given")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -279,19 +286,43 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     torch.cuda.synchronize()
+    # per-stage breakdown: K eager steps with the library's HIP events between kernels
     B.set_profiling(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     stop.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = start.elapsed_time(stop)
+    ms_eager = start.elapsed_time(stop) / args.steps
     stages = B.kernel_times()
     B.set_profiling(False)
+    # the timed K steps, without profiling events: eager launches, or with
+    # --graph replays of one step captured in a HIP graph (fixed buffer addresses)
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        run = graph.replay
+    torch.cuda.synchronize()
+    start.record()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
 
     models = stage_models(w)
@@ -330,6 +361,8 @@ def main(argv=None):
         if gemm_ms > 0 else None,
         "dispatch_frac_of_hbm": stage_out.get("dispatch", {}).get("frac"),
         "combine_frac_of_hbm": stage_out.get("combine", {}).get("frac"),
+        "launch": "HIP graph replay, one moe_forward per step" if args.graph else "eager, one moe_forward per step",
+        "ms_per_step_with_stage_events": round(ms_eager, 5),
         "stages": stage_out,
         "host_wall_s": round(wall, 4),
     }
