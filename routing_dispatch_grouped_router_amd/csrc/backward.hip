@@ -337,24 +337,24 @@ __global__ __launch_bounds__(256) void seg_dst_kernel(const int32_t* __restrict_
 }
 
 // XT [M][Rp] from X [R][M] (bfloat16): row r goes to column rowdst[r].
-// 64 (rows) x 128 (columns) tiles through LDS: 16-byte loads along the rows of
+// 128 (rows) x 64 (columns) tiles through LDS: 16-byte loads along the rows of
 // X; each thread then gathers 8 aligned consecutive rows of one column and
 // stores them as one 16-byte run when the 8 rows belong to one expert
-// (element by element at an expert boundary); lanes 8 i .. 8 i + 7 write 128
-// contiguous bytes.
+// (element by element at an expert boundary); lanes 16 i .. 16 i + 15 write
+// 256 contiguous bytes of one row of XT.
 __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __restrict__ X, int R, int M,
                                                             const int32_t* __restrict__ rowdst, int Rp,
                                                             uint16_t* __restrict__ XT) {
-    __shared__ uint16_t tile[64][128];   // 16-byte chunk c of row r at chunk c ^ ((r / 8) % 8)
-    __shared__ int s_dst[64];
-    const int r0 = blockIdx.x * 64, m0 = blockIdx.y * 128;
+    __shared__ uint16_t tile[128][64];   // 16-byte chunk c of row r at chunk c ^ ((r / 8) % 8)
+    __shared__ int s_dst[128];
+    const int r0 = blockIdx.x * 128, m0 = blockIdx.y * 64;
     const int tid = threadIdx.x;
-    if (tid < 64) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
+    if (tid < 128) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
     u32x4 v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int i = tid + 256 * q;
-        const int rr = i >> 4, c8 = (i & 15) * 8;
+        const int rr = i >> 3, c8 = (i & 7) * 8;
         const int r = r0 + rr, m = m0 + c8;
         v[q] = (u32x4){0u, 0u, 0u, 0u};
         if (r < R && m < M) v[q] = *reinterpret_cast<const u32x4*>(X + (size_t)r * M + m);   // M % 8 == 0
@@ -362,19 +362,19 @@ __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __re
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int i = tid + 256 * q;
-        const int rr = i >> 4, c8 = (i & 15) * 8;
+        const int rr = i >> 3, c8 = (i & 7) * 8;
         *reinterpret_cast<u32x4*>(&tile[rr][((c8 >> 3) ^ ((rr >> 3) & 7)) << 3]) = v[q];
     }
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int i = tid + 256 * q;
-        const int mm = i >> 3, g = (i & 7) * 8;
+        const int mm = i >> 4, g = (i & 15) * 8;
         const int m = m0 + mm;
         if (m >= M) continue;
         const int d0 = s_dst[g];
         uint16_t w[8];
-        const int pc = (((mm >> 3) ^ (g >> 3)) << 3) | (mm & 7);   // rows g .. g + 7 share the swizzle
+        const int pc = (((mm >> 3) ^ ((g >> 3) & 7)) << 3) | (mm & 7);   // rows g .. g + 7 share the swizzle
 #pragma unroll
         for (int u = 0; u < 8; ++u) w[u] = tile[g + u][pc];
         if (d0 >= 0 && s_dst[g + 7] == d0 + 7) {
@@ -621,7 +621,7 @@ hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, i
 
 hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
                                 const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s) {
-    dim3 grid((R + 63) / 64, (M + 127) / 128);
+    dim3 grid((R + 127) / 128, (M + 63) / 64);
     hipLaunchKernelGGL(transpose_seg_kernel, grid, dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
     dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
     hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);

@@ -98,6 +98,13 @@ SMALL = {
     "edge_mxfp8_empty": Workload("edge_mxfp8_empty", T=70, d=128, E=8, k=2, H=128,
                                  act=ACT_MXFP8, router="random", seed=2012,
                                  empty_experts=(1, 6), outlier_frac=0.05),
+    # the largest expert count and top-k the library supports (1024, 16): many tiny segments
+    "edge_max_E_k": Workload("edge_max_E_k", T=700, d=64, E=1024, k=16, H=64, act=ACT_BF16,
+                             router="random", seed=2013),
+    "edge_max_E_k_learned_f32": Workload("edge_max_E_k_learned_f32", T=300, d=64, E=1024, k=16, H=64,
+                                         act=ACT_F32, router="learned", seed=2014),
+    "edge_max_E_k_mxfp8": Workload("edge_max_E_k_mxfp8", T=500, d=128, E=1024, k=16, H=128,
+                                   act=ACT_MXFP8, router="random", seed=2015),
 }
 
 ALL = {**CONFIGS, **SMALL}

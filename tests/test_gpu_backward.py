@@ -57,6 +57,9 @@ CASES = [
     W.Workload("bwd_mx_learned", T=400, d=256, E=8, k=2, H=128, act="mxfp8", router="learned", seed=4011),
     W.Workload("bwd_mx_empty", T=70, d=128, E=8, k=2, H=128, act="mxfp8", router="random", seed=4012,
                empty_experts=(1, 6), outlier_frac=0.05),
+    W.Workload("bwd_bf16_max_E_k", T=700, d=64, E=1024, k=16, H=64, act="bf16", router="random", seed=4013),
+    W.Workload("bwd_f32_max_E_k_learned", T=300, d=64, E=1024, k=16, H=64, act="f32", router="learned",
+               seed=4014),
 ]
 
 
