@@ -579,9 +579,15 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     } else if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) {
         return st;
     }
-    if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;
+    if (bf) {   // da | db written in place and transposed into tb in one pass
+        if ((st = launched(launch_swiglu_bwd_t(static_cast<const uint16_t*>(dh), static_cast<uint16_t*>(ab), R, H, off,
+                                               poff, rowdst, E, BL.Rp, tb, s))))
+            return st;
+    } else if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) {
+        return st;
+    }
     if (bf) {
-        if ((st = transpose(xe, d, ta)) || (st = transpose(ab, 2 * H, tb))) return st;
+        if ((st = transpose(xe, d, ta))) return st;
         if ((st = launched(launch_wgrad_mfma(1, ta, tb, poff, E, d, 2 * H, BL.Rp, dw_gate, dw_up, s)))) return st;
     } else if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) {
         return st;

@@ -389,6 +389,81 @@ __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __re
     }
 }
 
+// SwiGLU backward fused with the transpose of its output (bfloat16): over a
+// tile of 128 rows and 64 hidden units (the 128 interleaved columns of a | b
+// holding them), da | db are written over a | b in place and, through LDS,
+// into the transposed, padded operand XT [2H][Rp] of the gate/up weight
+// gradient (row r to column rowdst[r], 8 aligned rows per 16-byte store as in
+// transpose_seg_kernel).
+__global__ __launch_bounds__(256) void swiglu_bwd_t_kernel(const uint16_t* __restrict__ dh, uint16_t* __restrict__ ab,
+                                                           int R, int H, const int32_t* __restrict__ rowdst, int Rp,
+                                                           uint16_t* __restrict__ XT) {
+    __shared__ uint16_t tile[128][128];   // 16-byte chunk c of row r at chunk c ^ ((r / 8) % 16)
+    __shared__ int s_dst[128];
+    const int r0 = blockIdx.x * 128, h0 = blockIdx.y * 64, c0 = 2 * h0;   // c0: first interleaved column
+    const int tid = threadIdx.x;
+    const int N = 2 * H;
+    if (tid < 128) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid + 256 * q;                 // unit: row rr, hidden block hb (of 2), chunk qq (of 4)
+        const int rr = i >> 3, hb = (i >> 2) & 1, qq = i & 3;
+        const int r = r0 + rr;
+        const int ca = 64 * hb + 8 * qq;             // column of the a chunk within the tile (b: +32)
+        float da[8], db[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            da[u] = 0.f;
+            db[u] = 0.f;
+        }
+        if (r < R && h0 + 32 * hb + 8 * qq < H) {
+            float d[8], a[8], b[8];
+            load_chunk<true>(dh, ((size_t)r * H + h0 + 32 * hb + 8 * qq) / 8, d);
+            load_chunk<true>(ab, ((size_t)r * N + c0 + ca) / 8, a);
+            load_chunk<true>(ab, ((size_t)r * N + c0 + ca + 32) / 8, b);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float s = 1.0f / (1.0f + __expf(-a[u]));
+                da[u] = d[u] * b[u] * (s * (1.0f + a[u] * (1.0f - s)));
+                db[u] = d[u] * (a[u] * s);
+            }
+            store_chunk<true>(ab, ((size_t)r * N + c0 + ca) / 8, da);
+            store_chunk<true>(ab, ((size_t)r * N + c0 + ca + 32) / 8, db);
+        }
+        u32x4 wa, wb;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            wa[u] = pack_bf16x2(da[2 * u], da[2 * u + 1]);
+            wb[u] = pack_bf16x2(db[2 * u], db[2 * u + 1]);
+        }
+        const int sw = (rr >> 3) & 15;
+        *reinterpret_cast<u32x4*>(&tile[rr][((ca >> 3) ^ sw) << 3]) = wa;
+        *reinterpret_cast<u32x4*>(&tile[rr][(((ca + 32) >> 3) ^ sw) << 3]) = wb;
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int q = 0; q < 8; ++q) {
+        const int i = tid + 256 * q;
+        const int cc = i >> 4, g = (i & 15) * 8;     // tile column, first of 8 rows
+        const int c = c0 + cc;
+        if (c >= N) continue;
+        const int d0 = s_dst[g];
+        uint16_t w[8];
+        const int pc = (((cc >> 3) ^ ((g >> 3) & 15)) << 3) | (cc & 7);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) w[u] = tile[g + u][pc];
+        if (d0 >= 0 && s_dst[g + 7] == d0 + 7) {
+            const u32x4 o = {(uint32_t)w[0] | ((uint32_t)w[1] << 16), (uint32_t)w[2] | ((uint32_t)w[3] << 16),
+                             (uint32_t)w[4] | ((uint32_t)w[5] << 16), (uint32_t)w[6] | ((uint32_t)w[7] << 16)};
+            *reinterpret_cast<u32x4*>(XT + (size_t)c * Rp + d0) = o;
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (s_dst[g + u] >= 0) XT[(size_t)c * Rp + s_dst[g + u]] = w[u];
+        }
+    }
+}
+
 // srow[pos[t][j]] = dsel[t][j]: the router gradient of each routed row.
 __global__ __launch_bounds__(256) void srow_kernel(const int32_t* __restrict__ pos, const float* __restrict__ dsel,
                                                    int n, float* __restrict__ srow) {
@@ -632,6 +707,17 @@ hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, ui
     const size_t n = (size_t)R * (K / 16);
     const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
     hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid), dim3(256), 0, s, q, sc, R, K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_t(const uint16_t* dh, uint16_t* ab, int R, int H, const int32_t* offsets,
+                               const int32_t* poff, const int32_t* rowdst, int E, int Rp, uint16_t* XT,
+                               hipStream_t s) {
+    dim3 grid((R + 127) / 128, (H + 63) / 64);
+    hipLaunchKernelGGL(swiglu_bwd_t_kernel, grid, dim3(256), 0, s, dh, ab, R, H, rowdst, Rp, XT);
+    const int M = 2 * H;
+    dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
+    hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);
     return hipGetLastError();
 }
 

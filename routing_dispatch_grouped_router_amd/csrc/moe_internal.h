@@ -140,6 +140,10 @@ hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, con
 hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s);
 hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
                                 const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s);
+// bf16 SwiGLU backward fused with the transpose of da | db into XT [2H][Rp] (as launch_transpose_seg).
+hipError_t launch_swiglu_bwd_t(const uint16_t* dh, uint16_t* ab, int R, int H, const int32_t* offsets,
+                               const int32_t* poff, const int32_t* rowdst, int E, int Rp, uint16_t* XT,
+                               hipStream_t s);
 hipError_t launch_wgrad_mfma(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
                              int N, int Rp, float* C, float* C2, hipStream_t s);
 
