@@ -19,7 +19,7 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t hist, base, psum, rwt, h, h_scale, route_end, gemm_end;
+    size_t hist, base, psum, ppart, rwt, h, h_scale, route_end, gemm_end;
     size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, ye, total;
 };
 
@@ -35,6 +35,7 @@ Layout layout(const moe_problem& p) {
     L.hist = take(nblk * E * 4);
     L.base = take(nblk * E * 4);
     L.psum = take(nblk * E * 4);
+    L.ppart = take(nblk * route_lanes(p.n_experts) * E * 4);
     L.rwt = take(p.act_dtype != MOE_F32 && !(p.flags & MOE_LOGITS_GIVEN) ? E * d * 2 : 0);   // router W^T
     L.route_end = off;
     L.h = take(R * H * act_bytes(p.act_dtype));
@@ -280,7 +281,8 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, flo
     if (!given && (st = launched(launch_router_logits(p->act_dtype, x, w_router, logits, T, d, E,
                                                        reinterpret_cast<uint16_t*>(at(ws, L.rwt)), s))))
         return st;
-    if ((st = launched(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, pos, hist, psum, s)))) return st;
+    if ((st = launched(launch_route_topk(logits, T, E, k, topk_idx, topk_gate, pos, hist, psum,
+                                                  reinterpret_cast<float*>(at(ws, L.ppart)), s)))) return st;
     if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, counts, offsets, psum, router_stats, T,
                                          k, s))))
         return st;
@@ -374,7 +376,8 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
             return st;
         if ((st = prof_mark("router_logits", s))) return st;
     }
-    if ((st = launched(launch_route_topk(logits, T, E, k, idx, gate, ps, hist, psum, s)))) return st;
+    if ((st = launched(launch_route_topk(logits, T, E, k, idx, gate, ps, hist, psum,
+                                                  reinterpret_cast<float*>(at(ws, L.ppart)), s)))) return st;
     if ((st = prof_mark("route_topk", s))) return st;
     if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, cnt, off, psum, router_stats, T, k, s))))
         return st;

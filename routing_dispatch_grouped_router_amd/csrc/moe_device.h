@@ -34,30 +34,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Orderable routing key: larger key <=> larger logit, then lower expert index.
-// -0.0 is folded onto +0.0 so the two compare equal.
-__device__ __forceinline__ uint64_t route_key(float logit, int e) {
-    uint32_t u = __float_as_uint(logit);
-    if (u == 0x80000000u) u = 0u;
-    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
-}
-__device__ __forceinline__ int key_expert(uint64_t key) {
-    return (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFull));
-}
-__device__ __forceinline__ float key_logit(uint64_t key) {
-    uint32_t ord = (uint32_t)(key >> 32);
-    uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
-    return __uint_as_float(u);
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = __shfl_xor(lo, m);
-    hi = __shfl_xor(hi, m);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // ---------------------------------------------------------------- MXFP8 (OCP MX v1.0)
 
 // Shared block exponent floor(log2(amax)) - 8 clamped to [-127, 127], from the

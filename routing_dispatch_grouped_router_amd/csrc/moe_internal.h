@@ -17,6 +17,14 @@ enum Act { kF32 = 0, kBF16 = 1, kMXFP8 = 2 };
 
 inline int route_blocks(int T) { return (T + kRouteBlock - 1) / kRouteBlock; }
 
+// Lanes per token in top-k selection: the smallest power of two G <= 64 with
+// E / G <= 8 (E / 64 <= 16 at E > 512).
+inline int route_lanes(int E) {
+    int G = 1;
+    while (G < 64 && (E + G - 1) / G > 8) G <<= 1;
+    return G;
+}
+
 // logits[T][E] = x[T][d] . w[d][E]   (x, w float32 or bfloat16; fp32 accumulate).
 // bfloat16: wt is scratch for w^T [E][d] (E d bfloat16), then MFMA.
 hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
@@ -25,9 +33,11 @@ hipError_t launch_router_logits(int act, const void* x, const void* w, float* lo
 // Top-k + gates + per-block histogram and within-block ranks.
 //   rank[T][k]   : rank of token t among the tokens of its routing block routed to the same expert
 //   hist[nblk][E]: per-block expert counts
-// psum (optional, [nblk][E]): per-block sums of the full-softmax router probability.
+// psum (optional, [nblk][E]): per-block sums of the full-softmax router probability;
+// ppart is then scratch for nblk * route_lanes(E) * E floats.
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
-                             float* topk_gate, int32_t* rank, int32_t* hist, float* psum, hipStream_t s);
+                             float* topk_gate, int32_t* rank, int32_t* hist, float* psum, float* ppart,
+                             hipStream_t s);
 
 // counts, offsets and base[nblk][E] = offsets[e] + tokens of earlier blocks routed to e;
 // with psum non-NULL also the router statistics stats[E + 2] (see route.hip).

@@ -202,145 +202,255 @@ hipError_t launch_router_logits(int act, const void* x, const void* w, float* lo
 
 // ----------------------------------------------------------------------------- top-k
 
-// G lanes cooperate on one token, each holding V of its E logits (expert
-// r + G*v for lane r of the group).  k rounds of a group-wide max over
-// orderable 64-bit keys select the experts in (logit desc, index asc) order.
-//
-// With psum non-NULL the kernel also sums, per expert, the full-softmax router
-// probability over the block's tokens (the soft half of the load-balancing
-// statistics): each lane accumulates its experts over the tokens of its group
-// in token order, and the groups' partial sums are added in group order, so
-// the result does not depend on scheduling.  psum[blk][e] receives the sum.
-template <int V>
-__global__ __launch_bounds__(1024) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                          int E, int k, int G,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_gate,
-                                                          int32_t* __restrict__ rank,
-                                                          int32_t* __restrict__ hist,
-                                                          float* __restrict__ psum) {
-    constexpr int kWords = kRouteBlock / 32;
-    __shared__ uint32_t mask[kMaxExperts * kWords];
-    __shared__ int32_t s_idx[kRouteBlock * kMaxTopK];   // selected experts of this block
-    __shared__ float s_ps[1024 * V];                    // [group][expert] probability partials
-    const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int blk = blockIdx.x;
-    for (int i = tid; i < E * kWords; i += nthr) mask[i] = 0u;
-    __syncthreads();
+// Top-k runs as two kernels.  route_select_kernel gives every token G lanes
+// (each holding V of its logits, experts r*V .. r*V+V-1 for lane r of the
+// group) and as many workgroups as the tokens need, so the whole chip works on
+// the selection; route_rank_kernel then turns the selected experts of each
+// routing block into within-block ranks and the block's expert histogram.
 
-    const int r = tid % G;
-    const int grp = tid / G;
-    const int per_pass = nthr / G;
-    float pacc[V];
+// Orderable 32-bit image of a float32 logit: larger logits give larger values,
+// -0.0 maps like +0.0, and 0 stays free to mark an expert already taken (the
+// one pattern that would map there, the all-ones NaN, is moved up by one).
+__device__ __forceinline__ uint32_t logit_ord(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (u == 0x80000000u) u = 0u;
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return o > 1u ? o : 1u;
+}
+__device__ __forceinline__ float ord_logit(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Cross-lane steps inside aligned groups of G lanes (G a power of two <= 64):
+// quad permutations and the row mirrors are DPP operand modifiers (no LDS
+// round trip); only groups wider than a 16-lane row use ds_bpermute.  Every
+// lane of a group ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int G, typename Op>
+__device__ __forceinline__ uint32_t group_reduce(uint32_t v, Op op) {
+    if constexpr (G >= 2) v = op(v, dpp_u32<0xB1>(v));     // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (G >= 4) v = op(v, dpp_u32<0x4E>(v));     // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (G >= 8) v = op(v, dpp_u32<0x141>(v));    // row_half_mirror: the other quad of 8
+    if constexpr (G >= 16) v = op(v, dpp_u32<0x140>(v));   // row_mirror: the other half of 16
+    if constexpr (G >= 32) v = op(v, (uint32_t)__shfl_xor((int)v, 16));
+    if constexpr (G >= 64) v = op(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+struct MaxU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct MinU32 {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; }
+};
+struct AddF32 {   // a + b == b + a bitwise, so both lanes of a pair agree
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }
+};
+
+constexpr int kSelThreads = 256;
+
+// One token per group of G lanes, kSelThreads / G tokens per workgroup.  k
+// rounds each take the group's largest remaining key and, among the lanes
+// holding it, the lowest expert index, so slot j holds the j-th largest logit
+// with ties to the lower index.
+//
+// With ppart non-NULL the workgroup also sums, per expert, the full-softmax
+// probability over its tokens (in token order, through a fixed two-level
+// tree) into ppart[blockIdx.x][E]; the rank kernel adds the G partial rows of
+// a routing block in order, so the statistics do not depend on scheduling.
+template <int G, int V>
+__global__ __launch_bounds__(kSelThreads) void route_select_kernel(const float* __restrict__ logits, int T,
+                                                                   int E, int k, int32_t* __restrict__ topk_idx,
+                                                                   float* __restrict__ topk_gate,
+                                                                   float* __restrict__ ppart) {
+    constexpr int TA = kSelThreads / G;
+    __shared__ float s_p[kSelThreads * V + kSelThreads];
+    const int tid = threadIdx.x, r = tid % G, grp = tid / G;
+    const int t = blockIdx.x * TA + grp;
+    const bool live = t < T;
+    const int e0 = r * V;                        // this lane's first expert
+    float lv[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) pacc[v] = 0.f;
-    for (int lt = grp; lt < kRouteBlock; lt += per_pass) {
-        const int t = blk * kRouteBlock + lt;
-        if (t >= T) break;       // uniform within a group: G divides 64
-        uint64_t key[V];
-        float lv[V];
+    for (int v = 0; v < V; ++v) lv[v] = 0.f;
+    if (live) {
+        const float* row = logits + (size_t)t * E + e0;
+        if ((E & 3) == 0 && e0 + V <= E) {       // whole run in range and 16-byte aligned
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-            int e = r + G * v;
-            lv[v] = (e < E) ? logits[(size_t)t * E + e] : 0.f;
-            key[v] = (e < E) ? route_key(lv[v], e) : 0ull;
-        }
-        uint64_t sel[kMaxTopK];
-#pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j) {
-            if (j < k) {
-                uint64_t best = 0ull;
-#pragma unroll
-                for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
-                for (int m = 1; m < G; m <<= 1) {
-                    uint64_t o = shfl_xor_u64(best, m);
-                    best = o > best ? o : best;
-                }
-                sel[j] = best;
-#pragma unroll
-                for (int v = 0; v < V; ++v)
-                    if (key[v] == best) key[v] = 0ull;
+            for (int v = 0; v < V; v += 4) {
+                const float4 q = *reinterpret_cast<const float4*>(row + v);
+                lv[v] = q.x; lv[v + 1] = q.y; lv[v + 2] = q.z; lv[v + 3] = q.w;
             }
-        }
-        // gates: softmax over all E renormalised over the selected k equals the
-        // softmax over the k selected logits
-        const float l0 = key_logit(sel[0]);
-        float den = 0.f;
+        } else {
 #pragma unroll
-        for (int j = 0; j < kMaxTopK; ++j)
-            if (j < k) den += expf(key_logit(sel[j]) - l0);
-        const float inv = 1.0f / den;
+            for (int v = 0; v < V; ++v)
+                if (e0 + v < E) lv[v] = row[v];
+        }
+    }
+    uint32_t o[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) o[v] = (live && e0 + v < E) ? logit_ord(lv[v]) : 0u;
+
+    uint32_t so[kMaxTopK];
+    int se[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+            uint32_t m = o[0];
+#pragma unroll
+            for (int v = 1; v < V; ++v) m = o[v] > m ? o[v] : m;
+            m = group_reduce<G>(m, MaxU32{});
+            int cv = V;
+#pragma unroll
+            for (int v = V - 1; v >= 0; --v) cv = (o[v] == m) ? v : cv;
+            const uint32_t e = group_reduce<G>(cv < V ? (uint32_t)(e0 + cv) : 0xFFFFFFFFu, MinU32{});
+            so[j] = m;
+            se[j] = (int)e;
+            const int q = (int)e - e0;           // in [0, V) only on the lane holding e
+#pragma unroll
+            for (int v = 0; v < V; ++v) o[v] = (q == v) ? 0u : o[v];
+        }
+    }
+    // gates: softmax over all E renormalised over the selected k equals the
+    // softmax over the k selected logits
+    const float l0 = ord_logit(so[0]);
+    float den = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) den += expf(ord_logit(so[j]) - l0);
+    const float inv = 1.0f / den;
+    if (live) {
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
             if (j < k && (j % G) == r) {
-                int e = key_expert(sel[j]);
-                topk_idx[(size_t)t * k + j] = e;
-                s_idx[lt * k + j] = e;
-                topk_gate[(size_t)t * k + j] = expf(key_logit(sel[j]) - l0) * inv;
-                atomicOr(&mask[e * kWords + (lt >> 5)], 1u << (lt & 31));
+                topk_idx[(size_t)t * k + j] = se[j];
+                topk_gate[(size_t)t * k + j] = expf(ord_logit(so[j]) - l0) * inv;
             }
-        }
-        if (psum != nullptr) {
-            // full softmax over the E logits, l0 being their maximum
-            float z[V], zs = 0.f;
-#pragma unroll
-            for (int v = 0; v < V; ++v) {
-                z[v] = (r + G * v < E) ? expf(lv[v] - l0) : 0.f;
-                zs += z[v];
-            }
-            for (int m = 1; m < G; m <<= 1) zs += __shfl_xor(zs, m);
-            const float iz = 1.0f / zs;
-#pragma unroll
-            for (int v = 0; v < V; ++v) pacc[v] += z[v] * iz;
         }
     }
-    if (psum != nullptr) {
+    if (ppart == nullptr) return;
+    // full softmax over the E logits, l0 being their maximum
+    float z[V], zs = 0.f;
 #pragma unroll
-        for (int v = 0; v < V; ++v)
-            if (r + G * v < E) s_ps[grp * E + r + G * v] = pacc[v];
+    for (int v = 0; v < V; ++v) {
+        z[v] = (live && e0 + v < E) ? expf(lv[v] - l0) : 0.f;
+        zs += z[v];
+    }
+    zs = __uint_as_float(group_reduce<G>(__float_as_uint(zs), AddF32{}));
+    const float iz = live ? 1.0f / zs : 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+        if (e0 + v < E) s_p[grp * E + e0 + v] = z[v] * iz;
+    __syncthreads();
+    if (E <= kSelThreads) {
+        int C = 1;                               // chunks of TA / C tokens, summed first
+        while (2 * C * E <= kSelThreads && 2 * C <= TA) C *= 2;
+        float* s_c = s_p + TA * E;
+        const int e = tid % E, c = tid / E, cs = TA / C;
+        if (c < C) {
+            float sum = 0.f;
+            for (int g = c * cs; g < (c + 1) * cs; ++g) sum += s_p[g * E + e];
+            s_c[c * E + e] = sum;
+        }
+        __syncthreads();
+        if (tid < E) {
+            float sum = 0.f;
+            for (int cc = 0; cc < C; ++cc) sum += s_c[cc * E + tid];
+            ppart[(size_t)blockIdx.x * E + tid] = sum;
+        }
+    } else {
+        for (int e = tid; e < E; e += kSelThreads) {
+            float sum = 0.f;
+            for (int g = 0; g < TA; ++g) sum += s_p[g * E + e];
+            ppart[(size_t)blockIdx.x * E + e] = sum;
+        }
+    }
+}
+
+// One workgroup per routing block: each selected (token, slot) sets its
+// token's bit in its expert's bitmask; a token's rank is the popcount of the
+// bits below it, the block's count of expert e the popcount of e's mask.
+// With psum non-NULL it adds the block's G partial probability rows in order.
+__global__ __launch_bounds__(256) void route_rank_kernel(const int32_t* __restrict__ topk_idx, int T, int E,
+                                                         int k, int32_t* __restrict__ rank,
+                                                         int32_t* __restrict__ hist,
+                                                         const float* __restrict__ ppart, int G,
+                                                         float* __restrict__ psum) {
+    constexpr int kWords = kRouteBlock / 32;
+    __shared__ uint32_t mask[kMaxExperts * kWords];
+    const int tid = threadIdx.x, blk = blockIdx.x;
+    const int t0 = blk * kRouteBlock, n = min(kRouteBlock, T - t0) * k;
+    for (int i = tid; i < E * kWords; i += 256) mask[i] = 0u;
+    __syncthreads();
+    const int32_t* bidx = topk_idx + (size_t)t0 * k;
+    int ev[kMaxTopK];
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+        const int i = tid + 256 * q;             // entry (i / k, i % k) of the block
+        ev[q] = -1;
+        if (q < k && i < n) {
+            ev[q] = bidx[i];
+            const int lt = i / k;
+            atomicOr(&mask[ev[q] * kWords + (lt >> 5)], 1u << (lt & 31));
+        }
     }
     __syncthreads();
-    if (psum != nullptr) {
-        for (int e = tid; e < E; e += nthr) {
-            float sum = 0.f;
-            for (int g = 0; g < per_pass; ++g) sum += s_ps[g * E + e];
-            psum[(size_t)blk * E + e] = sum;
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+        if (q < k && ev[q] >= 0) {
+            const int i = tid + 256 * q, lt = i / k;
+            const uint32_t* me = mask + ev[q] * kWords;
+            int c = __popc(me[lt >> 5] & ((1u << (lt & 31)) - 1u));
+            for (int w = 0; w < (lt >> 5); ++w) c += __popc(me[w]);
+            rank[(size_t)t0 * k + i] = c;
         }
     }
-    // within-block rank of every (token, slot): popcount of earlier tokens of the same expert
-    for (int i = tid; i < kRouteBlock * k; i += nthr) {
-        const int lt = i / k, j = i % k;
-        const int t = blk * kRouteBlock + lt;
-        if (t >= T) continue;
-        const int e = s_idx[lt * k + j];
-        const uint32_t* me = mask + e * kWords;
-        int c = __popc(me[lt >> 5] & ((1u << (lt & 31)) - 1u));
-        for (int w = 0; w < (lt >> 5); ++w) c += __popc(me[w]);
-        rank[(size_t)t * k + j] = c;
-    }
-    for (int e = tid; e < E; e += nthr) {
+    for (int e = tid; e < E; e += 256) {
         int c = 0;
 #pragma unroll
         for (int w = 0; w < kWords; ++w) c += __popc(mask[e * kWords + w]);
         hist[(size_t)blk * E + e] = c;
     }
+    if (psum != nullptr) {
+        const int TA = kSelThreads / G;
+        for (int e = tid; e < E; e += 256) {
+            float sum = 0.f;
+            for (int g = 0; g < G; ++g) {
+                const int a = blk * G + g;       // selection workgroup a covers tokens [a TA, a TA + TA)
+                if (a * TA < T) sum += ppart[(size_t)a * E + e];
+            }
+            psum[(size_t)blk * E + e] = sum;
+        }
+    }
+}
+
+template <int G, int V>
+static void launch_select(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_gate,
+                          float* ppart, hipStream_t s) {
+    constexpr int TA = kSelThreads / G;
+    hipLaunchKernelGGL((route_select_kernel<G, V>), dim3((T + TA - 1) / TA), dim3(kSelThreads), 0, s, logits, T, E,
+                       k, topk_idx, topk_gate, ppart);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
-                             float* topk_gate, int32_t* rank, int32_t* hist, float* psum, hipStream_t s) {
-    // lanes per token: smallest power of two G <= 64 with E / G <= 8 (or 16 at G = 64)
-    int G = 1;
-    while (G < 64 && (E + G - 1) / G > 8) G <<= 1;
-    const int V = (E + G - 1) / G;
-    const int threads = min(1024, kRouteBlock * G);
-    dim3 grid(route_blocks(T)), block(threads);
-    if (V <= 8)
-        hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, G, topk_idx,
-                           topk_gate, rank, hist, psum);
-    else
-        hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, G, topk_idx,
-                           topk_gate, rank, hist, psum);
+                             float* topk_gate, int32_t* rank, int32_t* hist, float* psum, float* ppart,
+                             hipStream_t s) {
+    const int G = route_lanes(E);
+    float* pp = psum != nullptr ? ppart : nullptr;
+    switch (G) {
+        case 1: launch_select<1, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+        case 2: launch_select<2, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+        case 4: launch_select<4, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+        case 8: launch_select<8, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+        case 16: launch_select<16, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+        case 32: launch_select<32, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+        default: launch_select<64, 16>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+    }
+    hipLaunchKernelGGL(route_rank_kernel, dim3(route_blocks(T)), dim3(256), 0, s, topk_idx, T, E, k, rank, hist, pp,
+                       G, psum);
     return hipGetLastError();
 }
 

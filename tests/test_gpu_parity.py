@@ -220,7 +220,7 @@ def test_host_sync_variant_matches(name):
 
 
 @pytest.mark.parametrize("name", ["small_bf16_zipf", "small_f32_learned", "edge_empty_experts", "edge_k_eq_E",
-                                  "edge_one_token"])
+                                  "edge_one_token", "edge_ties", "edge_max_E_k", "edge_max_E_k_learned_f32"])
 def test_router_stats_forward(name):
     """Router statistics from moe_forward: equal to the oracle's, bit-identical
     across calls and to moe_route's, and computing them changes no other output."""
