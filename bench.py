@@ -61,7 +61,7 @@ def stage_models(w: W.Workload) -> dict:
                              else ("mfma", MFMA_TFLOPS[w.act]))
     return {
         "router_logits": ("hbm", T * d * bin_ + d * E * bin_ + T * E * 4, "GB/s", HBM_GBPS),
-        "route_topk": ("hbm", T * E * 4 + R * 4 * 3 + ((T + 255) // 256) * E * 4, "GB/s", HBM_GBPS),
+        "route_topk": ("hbm", T * E * 4 + R * 4 * 4 + ((T + 255) // 256) * E * 4, "GB/s", HBM_GBPS),
         "route_scan": ("hbm", 3 * ((T + 255) // 256) * E * 4 + (2 * E + 1) * 4, "GB/s", HBM_GBPS),
         "dispatch": ("hbm", T * d * bin_ + R * d * bxe + scale_b + R * 4 * 3 + R * 4, "GB/s", HBM_GBPS),
         "gemm1_gate_up_swiglu": (gemm_bound, 4.0 * R * d * H, "TFLOP/s", gemm_peak),

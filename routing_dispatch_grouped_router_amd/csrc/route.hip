@@ -466,6 +466,8 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 // probability of expert e; stats[E] = E * sum_e (counts[e] / (T k)) * P_e, the
 // Switch-style load-balancing scalar; stats[E + 1] = max_e counts[e] / (T k / E),
 // the worst-case load over the mean load.  Sums run in a fixed order.
+constexpr int kScanBatch = 8;
+
 __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist,
                                                           int nblk, int E,
                                                           int32_t* __restrict__ base,
@@ -481,9 +483,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     const int e = tid % E, c = tid / E;
     const bool act = c < NC;
     const int b0 = c * CS, b1 = min(nblk, b0 + CS);
+    // hist is read kScanBatch blocks at a time: the loads of a batch are
+    // independent, so one memory latency covers the batch
     int s = 0;
-    if (act)
-        for (int b = b0; b < b1; ++b) s += hist[(size_t)b * E + e];
+    if (act) {
+        for (int b = b0; b < b1; b += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) v[u] = b + u < b1 ? hist[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) s += v[u];
+        }
+    }
     part[tid] = s;
     __syncthreads();
     if (tid < E) {
@@ -516,7 +527,14 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
         __shared__ int s_cnt[1024];
         if (tid < E) {
             float sum = 0.f;
-            for (int b = 0; b < nblk; ++b) sum += psum[(size_t)b * E + tid];
+            for (int b = 0; b < nblk; b += kScanBatch) {
+                float v[kScanBatch];
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u) v[u] = b + u < nblk ? psum[(size_t)(b + u) * E + tid] : 0.f;
+#pragma unroll
+                for (int u = 0; u < kScanBatch; ++u)
+                    if (b + u < nblk) sum += v[u];
+            }
             const float P = sum / (float)T;
             const int c = tot[tid] - (tid == 0 ? 0 : tot[tid - 1]);
             stats[tid] = P;
@@ -537,9 +555,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     }
     if (act) {
         int run = (e == 0 ? 0 : tot[e - 1]) + part[c * E + e];
-        for (int b = b0; b < b1; ++b) {
-            base[(size_t)b * E + e] = run;
-            run += hist[(size_t)b * E + e];
+        for (int b = b0; b < b1; b += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) v[u] = b + u < b1 ? hist[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {
+                if (b + u < b1) base[(size_t)(b + u) * E + e] = run;
+                run += v[u];
+            }
         }
     }
 }
