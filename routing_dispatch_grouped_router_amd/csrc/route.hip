@@ -202,11 +202,13 @@ hipError_t launch_router_logits(int act, const void* x, const void* w, float* lo
 
 // ----------------------------------------------------------------------------- top-k
 
-// Top-k runs as two kernels.  route_select_kernel gives every token G lanes
-// (each holding V of its logits, experts r*V .. r*V+V-1 for lane r of the
-// group) and as many workgroups as the tokens need, so the whole chip works on
-// the selection; route_rank_kernel then turns the selected experts of each
-// routing block into within-block ranks and the block's expert histogram.
+// Top-k.  route_select_kernel gives every token G lanes (each holding V of
+// its logits, experts r*V .. r*V+V-1 for lane r of the group).  For G > 4 a
+// workgroup of 256 threads holds 256 / G tokens, so there are as many
+// workgroups as the tokens need and the whole chip works on the selection;
+// route_rank_kernel then turns each routing block's selected experts into
+// within-block ranks and the block's expert histogram.  For G <= 4 one
+// workgroup of 256 G threads holds a whole routing block and ranks it itself.
 
 // Orderable 32-bit image of a float32 logit: larger logits give larger values,
 // -0.0 maps like +0.0, and 0 stays free to mark an expert already taken (the
@@ -253,22 +255,36 @@ struct AddF32 {   // a + b == b + a bitwise, so both lanes of a pair agree
 
 constexpr int kSelThreads = 256;
 
-// One token per group of G lanes, kSelThreads / G tokens per workgroup.  k
-// rounds each take the group's largest remaining key and, among the lanes
-// holding it, the lowest expert index, so slot j holds the j-th largest logit
-// with ties to the lower index.
+// One token per group of G lanes.  k rounds each take the group's largest
+// remaining key and, among the lanes holding it, the lowest expert index, so
+// slot j holds the j-th largest logit with ties to the lower index.
 //
-// With ppart non-NULL the workgroup also sums, per expert, the full-softmax
+// FUSE (G <= 4): the workgroup is one routing block of kRouteBlock tokens and
+// also writes the ranks and the block histogram: each selected (token, slot)
+// sets its token's bit in its expert's LDS bitmask, a token's rank is the
+// popcount of the bits below it, the block's count of expert e the popcount
+// of e's mask.
+//
+// With psum non-NULL the workgroup also sums, per expert, the full-softmax
 // probability over its tokens (in token order, through a fixed two-level
-// tree) into ppart[blockIdx.x][E]; the rank kernel adds the G partial rows of
-// a routing block in order, so the statistics do not depend on scheduling.
-template <int G, int V>
-__global__ __launch_bounds__(kSelThreads) void route_select_kernel(const float* __restrict__ logits, int T,
-                                                                   int E, int k, int32_t* __restrict__ topk_idx,
-                                                                   float* __restrict__ topk_gate,
-                                                                   float* __restrict__ ppart) {
-    constexpr int TA = kSelThreads / G;
-    __shared__ float s_p[kSelThreads * V + kSelThreads];
+// tree) into psum[blockIdx.x][E]; without FUSE these are partial rows that the
+// rank kernel adds G at a time in order, so the statistics do not depend on
+// scheduling.
+template <int G, int V, bool FUSE>
+__global__ __launch_bounds__(FUSE ? kRouteBlock * G : kSelThreads) void route_select_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_gate, int32_t* __restrict__ rank, int32_t* __restrict__ hist,
+    float* __restrict__ psum) {
+    constexpr int NTHR = FUSE ? kRouteBlock * G : kSelThreads;
+    constexpr int TA = NTHR / G;                 // tokens per workgroup
+    constexpr int kWords = kRouteBlock / 32;
+    static_assert(!FUSE || G <= 4, "a fused workgroup holds 256 G threads");
+    __shared__ float s_p[NTHR * V + NTHR];
+    __shared__ uint32_t mask[FUSE ? G * V * kWords : 1];
+    if (FUSE) {
+        for (int i = threadIdx.x; i < E * kWords; i += NTHR) mask[i] = 0u;
+        __syncthreads();
+    }
     const int tid = threadIdx.x, r = tid % G, grp = tid / G;
     const int t = blockIdx.x * TA + grp;
     const bool live = t < T;
@@ -328,10 +344,31 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(const float* 
             if (j < k && (j % G) == r) {
                 topk_idx[(size_t)t * k + j] = se[j];
                 topk_gate[(size_t)t * k + j] = expf(ord_logit(so[j]) - l0) * inv;
+                if (FUSE) atomicOr(&mask[se[j] * kWords + (grp >> 5)], 1u << (grp & 31));
             }
         }
     }
-    if (ppart == nullptr) return;
+    if (FUSE) {
+        __syncthreads();
+        if (live) {
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (j < k && (j % G) == r) {
+                    const uint32_t* me = mask + se[j] * kWords;
+                    int c = __popc(me[grp >> 5] & ((1u << (grp & 31)) - 1u));
+                    for (int w = 0; w < (grp >> 5); ++w) c += __popc(me[w]);
+                    rank[(size_t)t * k + j] = c;
+                }
+            }
+        }
+        for (int e = tid; e < E; e += NTHR) {
+            int c = 0;
+#pragma unroll
+            for (int w = 0; w < kWords; ++w) c += __popc(mask[e * kWords + w]);
+            hist[(size_t)blockIdx.x * E + e] = c;
+        }
+    }
+    if (psum == nullptr) return;
     // full softmax over the E logits, l0 being their maximum
     float z[V], zs = 0.f;
 #pragma unroll
@@ -345,9 +382,9 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(const float* 
     for (int v = 0; v < V; ++v)
         if (e0 + v < E) s_p[grp * E + e0 + v] = z[v] * iz;
     __syncthreads();
-    if (E <= kSelThreads) {
+    if (E <= NTHR) {
         int C = 1;                               // chunks of TA / C tokens, summed first
-        while (2 * C * E <= kSelThreads && 2 * C <= TA) C *= 2;
+        while (2 * C * E <= NTHR && 2 * C <= TA) C *= 2;
         float* s_c = s_p + TA * E;
         const int e = tid % E, c = tid / E, cs = TA / C;
         if (c < C) {
@@ -359,13 +396,13 @@ __global__ __launch_bounds__(kSelThreads) void route_select_kernel(const float* 
         if (tid < E) {
             float sum = 0.f;
             for (int cc = 0; cc < C; ++cc) sum += s_c[cc * E + tid];
-            ppart[(size_t)blockIdx.x * E + tid] = sum;
+            psum[(size_t)blockIdx.x * E + tid] = sum;
         }
     } else {
-        for (int e = tid; e < E; e += kSelThreads) {
+        for (int e = tid; e < E; e += NTHR) {
             float sum = 0.f;
             for (int g = 0; g < TA; ++g) sum += s_p[g * E + e];
-            ppart[(size_t)blockIdx.x * E + e] = sum;
+            psum[(size_t)blockIdx.x * E + e] = sum;
         }
     }
 }
@@ -429,28 +466,32 @@ __global__ __launch_bounds__(256) void route_rank_kernel(const int32_t* __restri
 
 template <int G, int V>
 static void launch_select(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_gate,
-                          float* ppart, hipStream_t s) {
-    constexpr int TA = kSelThreads / G;
-    hipLaunchKernelGGL((route_select_kernel<G, V>), dim3((T + TA - 1) / TA), dim3(kSelThreads), 0, s, logits, T, E,
-                       k, topk_idx, topk_gate, ppart);
+                          int32_t* rank, int32_t* hist, float* psum, float* ppart, hipStream_t s) {
+    if constexpr (G <= 4) {
+        hipLaunchKernelGGL((route_select_kernel<G, V, true>), dim3(route_blocks(T)), dim3(kRouteBlock * G), 0, s,
+                           logits, T, E, k, topk_idx, topk_gate, rank, hist, psum);
+    } else {
+        constexpr int TA = kSelThreads / G;
+        float* pp = psum != nullptr ? ppart : nullptr;
+        hipLaunchKernelGGL((route_select_kernel<G, V, false>), dim3((T + TA - 1) / TA), dim3(kSelThreads), 0, s,
+                           logits, T, E, k, topk_idx, topk_gate, nullptr, nullptr, pp);
+        hipLaunchKernelGGL(route_rank_kernel, dim3(route_blocks(T)), dim3(256), 0, s, topk_idx, T, E, k, rank, hist,
+                           pp, G, psum);
+    }
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_idx,
                              float* topk_gate, int32_t* rank, int32_t* hist, float* psum, float* ppart,
                              hipStream_t s) {
-    const int G = route_lanes(E);
-    float* pp = psum != nullptr ? ppart : nullptr;
-    switch (G) {
-        case 1: launch_select<1, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
-        case 2: launch_select<2, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
-        case 4: launch_select<4, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
-        case 8: launch_select<8, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
-        case 16: launch_select<16, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
-        case 32: launch_select<32, 8>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
-        default: launch_select<64, 16>(logits, T, E, k, topk_idx, topk_gate, pp, s); break;
+    switch (route_lanes(E)) {
+        case 1: launch_select<1, 8>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
+        case 2: launch_select<2, 8>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
+        case 4: launch_select<4, 8>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
+        case 8: launch_select<8, 8>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
+        case 16: launch_select<16, 8>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
+        case 32: launch_select<32, 8>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
+        default: launch_select<64, 16>(logits, T, E, k, topk_idx, topk_gate, rank, hist, psum, ppart, s); break;
     }
-    hipLaunchKernelGGL(route_rank_kernel, dim3(route_blocks(T)), dim3(256), 0, s, topk_idx, T, E, k, rank, hist, pp,
-                       G, psum);
     return hipGetLastError();
 }
 
