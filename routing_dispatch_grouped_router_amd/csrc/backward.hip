@@ -95,26 +95,28 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void combine_bwd_kernel(
     if (t >= T) return;
     int p[KMAX], ex[KMAX];
     float g[KMAX], dot[KMAX];
+    // slots past k repeat slot k - 1 (loaded, never used), so every load is
+    // unconditional and a chunk's k + 1 loads are in flight together
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         dot[j] = 0.f;
-        if (j < k) {
-            p[j] = pos[(size_t)t * k + j];
-            ex[j] = idx[(size_t)t * k + j];
-            g[j] = gate[(size_t)t * k + j];
-        }
+        const size_t i = (size_t)t * k + min(j, k - 1);
+        p[j] = pos[i];
+        ex[j] = idx[i];
+        g[j] = gate[i];
     }
     for (int c = lane; c < row_chunks; c += 64) {
-        float v[8];
+        float v[8], w[KMAX][8];
         load_chunk<BF>(dy, (size_t)t * row_chunks + c, v);
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) load_chunk<BF>(ye, (size_t)p[j] * row_chunks + c, w[j]);
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j >= k) continue;
-            float w[8], o[8];
-            load_chunk<BF>(ye, (size_t)p[j] * row_chunks + c, w);
+            float o[8];
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                dot[j] = fmaf(v[i], w[i], dot[j]);
+                dot[j] = fmaf(v[i], w[j][i], dot[j]);
                 o[i] = g[j] * v[i];
             }
             store_chunk<BF>(dye, (size_t)p[j] * row_chunks + c, o);
@@ -261,33 +263,35 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __res
     if (t >= T) return;
     int p[KMAX], ex[KMAX];
     float ds[KMAX];
+    // slots past k repeat slot k - 1 (loaded, never used): unconditional loads
+    // keep a chunk's loads in flight together
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        if (j < k) {
-            p[j] = pos[(size_t)t * k + j];
-            ex[j] = idx[(size_t)t * k + j];
-            ds[j] = dsel[(size_t)t * k + j];
-        }
+    for (int j = 0; j < KMAX; ++j) {
+        const size_t i = (size_t)t * k + min(j, k - 1);
+        p[j] = pos[i];
+        ex[j] = idx[i];
+        ds[j] = dsel[i];
+    }
     for (int c = lane; c < row_chunks; c += 64) {
-        float acc[8];
+        float acc[8], w[KMAX][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
+        for (int j = 0; j < KMAX; ++j) load_chunk<BF>(dxe, (size_t)p[j] * row_chunks + c, w[j]);
+#pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j >= k) continue;
-            float w[8];
-            load_chunk<BF>(dxe, (size_t)p[j] * row_chunks + c, w);
 #pragma unroll
-            for (int i = 0; i < NV; ++i) acc[i] += w[i];
+            for (int i = 0; i < NV; ++i) acc[i] += w[j][i];
         }
         if (wrt) {
 #pragma unroll
+            for (int j = 0; j < KMAX; ++j) load_chunk<BF>(wrt, (size_t)ex[j] * row_chunks + c, w[j]);   // W_r^T rows
+#pragma unroll
             for (int j = 0; j < KMAX; ++j) {
                 if (j >= k) continue;
-                float w[8];
-                load_chunk<BF>(wrt, (size_t)ex[j] * row_chunks + c, w);   // row e_j of W_r^T
 #pragma unroll
-                for (int i = 0; i < NV; ++i) acc[i] = fmaf(ds[j], w[i], acc[i]);
+                for (int i = 0; i < NV; ++i) acc[i] = fmaf(ds[j], w[j][i], acc[i]);
             }
         }
         store_chunk<BF>(dx, (size_t)t * row_chunks + c, acc);
@@ -336,57 +340,96 @@ __global__ __launch_bounds__(256) void seg_dst_kernel(const int32_t* __restrict_
     }
 }
 
+// 8 x 8 bfloat16 block transpose in registers: in[u] holds columns 0..7 of
+// row u (two per 32-bit word, the lower column in the low half); on return
+// out[j] holds rows 0..7 of column j the same way.
+__device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        // v_perm_b32 selects bytes of {src0, src1} = bytes 7..4, 3..0: the low
+        // half (bytes 1, 0) or the high half (bytes 3, 2) of each source word
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[j][q] = __builtin_amdgcn_perm(in[2 * q + 1][w], in[2 * q][w], sel);
+    }
+}
+
+// Tile of a 1-D grid of 8 * ceil(n / 8) workgroups over n tiles: workgroups
+// are dealt to the 8 XCDs in turn, so this gives each XCD a contiguous run of
+// tiles (neighbouring row blocks share DRAM pages and that XCD's L2); -1 for
+// the padding workgroups.
+__device__ __forceinline__ int xcd_tile(int n) {
+    const int per = gridDim.x / 8;
+    const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+    return t < n ? t : -1;
+}
+
+inline unsigned xcd_grid(long n) { return (unsigned)((n + 7) / 8 * 8); }
+
+// Second half of a 128 x 128 tile transpose: the tile (16-byte chunk c of
+// tile row r at chunk c ^ (r / 8 % 16)) goes to rows m0 .. m0 + 127 of XT
+// (rows at or past M skipped), tile row r to column s_dst[r] (skipped when
+// negative).  Thread (a, c) reads the 8 x 8 block of rows 8a .. 8a + 7 and
+// columns 8c .. 8c + 7 (eight 16-byte LDS reads, bank-conflict free under the
+// swizzle), transposes it in registers and stores the 8 rows of each column
+// as one 16-byte run when they land in 8 consecutive columns (element by
+// element at an expert boundary).  The 16 lanes sharing c write 256
+// contiguous bytes of a row of XT.
+__device__ __forceinline__ void store_tile_t(const u32x4* tile, const int* s_dst, uint16_t* __restrict__ XT, int Rp,
+                                             int m0, int M) {
+    const int a = threadIdx.x & 15, c = threadIdx.x >> 4;
+    if (m0 + 8 * c >= M) return;
+    const int d0 = s_dst[8 * a];
+    uint16_t* dst = XT + (size_t)(m0 + 8 * c) * Rp;
+    if (d0 >= 0 && s_dst[8 * a + 7] == d0 + 7) {
+        u32x4 in[8], out[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) in[u] = tile[(8 * a + u) * 16 + (c ^ a)];
+        transpose8x8_bf16(in, out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(dst + (size_t)j * Rp + d0) = out[j];
+    } else {
+#pragma unroll 1
+        for (int u = 0; u < 8; ++u) {
+            const int du = s_dst[8 * a + u];
+            if (du < 0) continue;
+            const u32x4 w = tile[(8 * a + u) * 16 + (c ^ a)];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) dst[(size_t)j * Rp + du] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+        }
+    }
+}
+
 // XT [M][Rp] from X [R][M] (bfloat16): row r goes to column rowdst[r].
-// 128 (rows) x 64 (columns) tiles through LDS: 16-byte loads along the rows of
-// X; each thread then gathers 8 aligned consecutive rows of one column and
-// stores them as one 16-byte run when the 8 rows belong to one expert
-// (element by element at an expert boundary); lanes 16 i .. 16 i + 15 write
-// 256 contiguous bytes of one row of XT.
+// 128 x 128 tiles through LDS: 16 lanes load the 256 bytes of one row of X
+// into the swizzled tile, then store_tile_t writes it out transposed.
 __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __restrict__ X, int R, int M,
                                                             const int32_t* __restrict__ rowdst, int Rp,
                                                             uint16_t* __restrict__ XT) {
-    __shared__ uint16_t tile[128][64];   // 16-byte chunk c of row r at chunk c ^ ((r / 8) % 8)
+    __shared__ u32x4 tile[128 * 16];
     __shared__ int s_dst[128];
-    const int r0 = blockIdx.x * 128, m0 = blockIdx.y * 64;
+    const int nr = (R + 127) / 128;
+    const int tl = xcd_tile(nr * ((M + 127) / 128));   // row blocks fastest
+    if (tl < 0) return;
+    const int r0 = (tl % nr) * 128, m0 = (tl / nr) * 128;
     const int tid = threadIdx.x;
     if (tid < 128) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
-    u32x4 v[4];
+    // rows past R and columns past M are loaded clamped and never stored
+    u32x4 v[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = tid + 256 * q;
-        const int rr = i >> 3, c8 = (i & 7) * 8;
-        const int r = r0 + rr, m = m0 + c8;
-        v[q] = (u32x4){0u, 0u, 0u, 0u};
-        if (r < R && m < M) v[q] = *reinterpret_cast<const u32x4*>(X + (size_t)r * M + m);   // M % 8 == 0
+    for (int q = 0; q < 8; ++q) {
+        const int rr = (tid >> 4) + 16 * q, c = tid & 15;
+        const int r = min(r0 + rr, R - 1), m = min(m0 + 8 * c, M - 8);   // M % 8 == 0
+        v[q] = *reinterpret_cast<const u32x4*>(X + (size_t)r * M + m);
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = tid + 256 * q;
-        const int rr = i >> 3, c8 = (i & 7) * 8;
-        *reinterpret_cast<u32x4*>(&tile[rr][((c8 >> 3) ^ ((rr >> 3) & 7)) << 3]) = v[q];
+    for (int q = 0; q < 8; ++q) {
+        const int rr = (tid >> 4) + 16 * q, c = tid & 15;
+        tile[rr * 16 + (c ^ ((rr >> 3) & 15))] = v[q];
     }
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = tid + 256 * q;
-        const int mm = i >> 4, g = (i & 15) * 8;
-        const int m = m0 + mm;
-        if (m >= M) continue;
-        const int d0 = s_dst[g];
-        uint16_t w[8];
-        const int pc = (((mm >> 3) ^ ((g >> 3) & 7)) << 3) | (mm & 7);   // rows g .. g + 7 share the swizzle
-#pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = tile[g + u][pc];
-        if (d0 >= 0 && s_dst[g + 7] == d0 + 7) {
-            const u32x4 o = {(uint32_t)w[0] | ((uint32_t)w[1] << 16), (uint32_t)w[2] | ((uint32_t)w[3] << 16),
-                             (uint32_t)w[4] | ((uint32_t)w[5] << 16), (uint32_t)w[6] | ((uint32_t)w[7] << 16)};
-            *reinterpret_cast<u32x4*>(XT + (size_t)m * Rp + d0) = o;
-        } else {
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s_dst[g + u] >= 0) XT[(size_t)m * Rp + s_dst[g + u]] = w[u];
-        }
-    }
+    store_tile_t(tile, s_dst, XT, Rp, m0, M);
 }
 
 // SwiGLU backward fused with the transpose of its output (bfloat16): over a
@@ -398,35 +441,42 @@ __global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __re
 __global__ __launch_bounds__(256) void swiglu_bwd_t_kernel(const uint16_t* __restrict__ dh, uint16_t* __restrict__ ab,
                                                            int R, int H, const int32_t* __restrict__ rowdst, int Rp,
                                                            uint16_t* __restrict__ XT) {
-    __shared__ uint16_t tile[128][128];   // 16-byte chunk c of row r at chunk c ^ ((r / 8) % 16)
+    __shared__ u32x4 tile[128 * 16];
     __shared__ int s_dst[128];
-    const int r0 = blockIdx.x * 128, h0 = blockIdx.y * 64, c0 = 2 * h0;   // c0: first interleaved column
+    const int nr = (R + 127) / 128;
+    const int tl = xcd_tile(nr * (H / 64));   // row blocks fastest
+    if (tl < 0) return;
+    const int r0 = (tl % nr) * 128, h0 = (tl / nr) * 64, c0 = 2 * h0;   // c0: first interleaved column
     const int tid = threadIdx.x;
-    const int N = 2 * H;
+    const int N = 2 * H;   // H % 64 == 0: every tile holds 64 whole hidden units
     if (tid < 128) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
+    // units (row rr, hidden block hb of 2, chunk qq of 4): all 12 loads first
+    // (rows past R loaded clamped; their results are neither stored nor used)
+    float d[4][8], a[4][8], b[4][8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int i = tid + 256 * q;                 // unit: row rr, hidden block hb (of 2), chunk qq (of 4)
+        const int i = tid + 256 * q;
+        const int rr = i >> 3, hb = (i >> 2) & 1, qq = i & 3;
+        const size_t r = (size_t)min(r0 + rr, R - 1);
+        const int ca = 64 * hb + 8 * qq;             // column of the a chunk within the tile (b: +32)
+        load_chunk<true>(dh, (r * H + h0 + 32 * hb + 8 * qq) / 8, d[q]);
+        load_chunk<true>(ab, (r * N + c0 + ca) / 8, a[q]);
+        load_chunk<true>(ab, (r * N + c0 + ca + 32) / 8, b[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int i = tid + 256 * q;
         const int rr = i >> 3, hb = (i >> 2) & 1, qq = i & 3;
         const int r = r0 + rr;
-        const int ca = 64 * hb + 8 * qq;             // column of the a chunk within the tile (b: +32)
+        const int ca = 64 * hb + 8 * qq;
         float da[8], db[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            da[u] = 0.f;
-            db[u] = 0.f;
+            const float s = 1.0f / (1.0f + __expf(-a[q][u]));
+            da[u] = d[q][u] * b[q][u] * (s * (1.0f + a[q][u] * (1.0f - s)));
+            db[u] = d[q][u] * (a[q][u] * s);
         }
-        if (r < R && h0 + 32 * hb + 8 * qq < H) {
-            float d[8], a[8], b[8];
-            load_chunk<true>(dh, ((size_t)r * H + h0 + 32 * hb + 8 * qq) / 8, d);
-            load_chunk<true>(ab, ((size_t)r * N + c0 + ca) / 8, a);
-            load_chunk<true>(ab, ((size_t)r * N + c0 + ca + 32) / 8, b);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float s = 1.0f / (1.0f + __expf(-a[u]));
-                da[u] = d[u] * b[u] * (s * (1.0f + a[u] * (1.0f - s)));
-                db[u] = d[u] * (a[u] * s);
-            }
+        if (r < R) {
             store_chunk<true>(ab, ((size_t)r * N + c0 + ca) / 8, da);
             store_chunk<true>(ab, ((size_t)r * N + c0 + ca + 32) / 8, db);
         }
@@ -437,31 +487,11 @@ __global__ __launch_bounds__(256) void swiglu_bwd_t_kernel(const uint16_t* __res
             wb[u] = pack_bf16x2(db[2 * u], db[2 * u + 1]);
         }
         const int sw = (rr >> 3) & 15;
-        *reinterpret_cast<u32x4*>(&tile[rr][((ca >> 3) ^ sw) << 3]) = wa;
-        *reinterpret_cast<u32x4*>(&tile[rr][(((ca + 32) >> 3) ^ sw) << 3]) = wb;
+        tile[rr * 16 + ((ca >> 3) ^ sw)] = wa;
+        tile[rr * 16 + (((ca + 32) >> 3) ^ sw)] = wb;
     }
     __syncthreads();
-#pragma unroll 2
-    for (int q = 0; q < 8; ++q) {
-        const int i = tid + 256 * q;
-        const int cc = i >> 4, g = (i & 15) * 8;     // tile column, first of 8 rows
-        const int c = c0 + cc;
-        if (c >= N) continue;
-        const int d0 = s_dst[g];
-        uint16_t w[8];
-        const int pc = (((cc >> 3) ^ ((g >> 3) & 15)) << 3) | (cc & 7);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) w[u] = tile[g + u][pc];
-        if (d0 >= 0 && s_dst[g + 7] == d0 + 7) {
-            const u32x4 o = {(uint32_t)w[0] | ((uint32_t)w[1] << 16), (uint32_t)w[2] | ((uint32_t)w[3] << 16),
-                             (uint32_t)w[4] | ((uint32_t)w[5] << 16), (uint32_t)w[6] | ((uint32_t)w[7] << 16)};
-            *reinterpret_cast<u32x4*>(XT + (size_t)c * Rp + d0) = o;
-        } else {
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (s_dst[g + u] >= 0) XT[(size_t)c * Rp + s_dst[g + u]] = w[u];
-        }
-    }
+    store_tile_t(tile, s_dst, XT, Rp, c0, N);
 }
 
 // srow[pos[t][j]] = dsel[t][j]: the router gradient of each routed row.
@@ -478,6 +508,8 @@ __global__ __launch_bounds__(256) void srow_kernel(const int32_t* __restrict__ p
 // order, 8 columns per thread with 16-byte loads, into part[tile][d], and
 // workgroup 0 stores the schedule tstart[E + 1].  Pass 2: dW_r[c][e] = sum of
 // part[tile][c] over expert e's tiles in order.
+constexpr int kWgBatch = 8;
+
 template <bool BF>
 __global__ __launch_bounds__(256) void router_wgrad_rows_kernel(const void* __restrict__ x,
                                                                 const int32_t* __restrict__ row_token,
@@ -500,12 +532,23 @@ __global__ __launch_bounds__(256) void router_wgrad_rows_kernel(const void* __re
         float acc[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-        for (int r = 0; r < rows; ++r) {
-            float v[8];
-            load_chunk<BF>(x, (size_t)row_token[row0 + r] * chunks + c, v);
-            const float sv = srow[row0 + r];
+        // rows in batches of kWgBatch whose loads are issued together (one
+        // memory latency per batch); the sum still runs in row order
+        for (int r0 = 0; r0 < rows; r0 += kWgBatch) {
+            float v[kWgBatch][8], sv[kWgBatch];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) acc[i] = fmaf(v[i], sv, acc[i]);
+            for (int u = 0; u < kWgBatch; ++u) {
+                const int r = min(r0 + u, rows - 1);
+                load_chunk<BF>(x, (size_t)row_token[row0 + r] * chunks + c, v[u]);
+                sv[u] = r0 + u < rows ? srow[row0 + r] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kWgBatch; ++u) {
+                if (r0 + u < rows) {
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc[i] = fmaf(v[u][i], sv[u], acc[i]);
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) part[(size_t)tile * d + c * NV + i] = acc[i];
@@ -519,7 +562,15 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
     for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
         const int c = i / E, e = i - c * E;
         float s = 0.f;
-        for (int t = tstart[e]; t < tstart[e + 1]; ++t) s += part[(size_t)t * d + c];
+        const int t1 = tstart[e + 1];
+        for (int t0 = tstart[e]; t0 < t1; t0 += kWgBatch) {
+            float v[kWgBatch];
+#pragma unroll
+            for (int u = 0; u < kWgBatch; ++u) v[u] = t0 + u < t1 ? part[(size_t)(t0 + u) * d + c] : 0.f;
+#pragma unroll
+            for (int u = 0; u < kWgBatch; ++u)
+                if (t0 + u < t1) s += v[u];
+        }
         dw[i] = s;
     }
 }
@@ -696,8 +747,8 @@ hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, i
 
 hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
                                 const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s) {
-    dim3 grid((R + 127) / 128, (M + 63) / 64);
-    hipLaunchKernelGGL(transpose_seg_kernel, grid, dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
+    const long tiles = (long)((R + 127) / 128) * ((M + 127) / 128);
+    hipLaunchKernelGGL(transpose_seg_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
     dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
     hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);
     return hipGetLastError();
@@ -713,8 +764,8 @@ hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, ui
 hipError_t launch_swiglu_bwd_t(const uint16_t* dh, uint16_t* ab, int R, int H, const int32_t* offsets,
                                const int32_t* poff, const int32_t* rowdst, int E, int Rp, uint16_t* XT,
                                hipStream_t s) {
-    dim3 grid((R + 127) / 128, (H + 63) / 64);
-    hipLaunchKernelGGL(swiglu_bwd_t_kernel, grid, dim3(256), 0, s, dh, ab, R, H, rowdst, Rp, XT);
+    const long tiles = (long)((R + 127) / 128) * (H / 64);
+    hipLaunchKernelGGL(swiglu_bwd_t_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, dh, ab, R, H, rowdst, Rp, XT);
     const int M = 2 * H;
     dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
     hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);

@@ -21,20 +21,34 @@ namespace moe {
 constexpr int kRowsPerBlock = 4;   // one wave per token, 4 waves per workgroup
 constexpr int kGroup = 4;          // 16-byte chunks per lane loaded before they are stored
 
-// Final position of (t, j): with `base` non-NULL, pos holds the within-block
-// rank and is rewritten here; every lane computes the value, lane j writes it.
-__device__ __forceinline__ int final_pos(int32_t* pos, const int32_t* topk_idx,
-                                         const int32_t* base, int32_t* row_token, int t, int j,
-                                         int k, int E, int lane) {
-    const size_t i = (size_t)t * k + j;
-    int p = pos[i];
-    if (base != nullptr) {
-        p += base[(size_t)(t / kRouteBlock) * E + topk_idx[i]];
-        if (lane == 0) {
-            row_token[p] = t;
+// Final positions of token t's k slots: with `base` non-NULL, pos holds the
+// within-block ranks and is rewritten here (rank + the block's base for the
+// expert), and row_token[p] = t.  Every lane computes the values (slots past k
+// repeat slot k - 1, so the loads are unconditional and issued together);
+// lane j writes slot j.
+template <int KMAX>
+__device__ __forceinline__ void final_positions(int32_t* pos, const int32_t* topk_idx, const int32_t* base,
+                                                int32_t* row_token, int t, int k, int E, int lane, int (&p)[KMAX]) {
+    int ex[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const size_t i = (size_t)t * k + min(j, k - 1);
+        p[j] = pos[i];
+        ex[j] = topk_idx[i];
+    }
+    if (base == nullptr) return;
+    const int32_t* b = base + (size_t)(t / kRouteBlock) * E;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) p[j] += b[ex[j]];
+    // all lanes have read the ranks before any lane overwrites them
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j < k && lane == j) {
+            pos[(size_t)t * k + j] = p[j];
+            row_token[p[j]] = t;
         }
     }
-    return p;
 }
 
 template <int KMAX>
@@ -48,27 +62,21 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(const uint4* __restr
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int p[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        if (j < k) p[j] = final_pos(pos, topk_idx, base, row_token, t, j, k, E, lane);
-    if (base != nullptr) {
-        // all lanes have read the ranks before any lane overwrites them
-        __builtin_amdgcn_wave_barrier();
-        if (lane < k) {
-#pragma unroll
-            for (int j = 0; j < KMAX; ++j)
-                if (j == lane) pos[(size_t)t * k + j] = p[j];
-        }
-    }
-    // all of a lane's loads of a group are issued before any store
+    // the row's first chunks are requested before the positions, which they do
+    // not depend on; a lane's loads of a group are issued before any store
+    // (chunks past the row end are loaded clamped and not stored)
     const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * row_chunks;
     u32x4* dst = reinterpret_cast<u32x4*>(xe);
-    for (int c0 = lane; c0 < row_chunks; c0 += 64 * kGroup) {
-        u32x4 v[kGroup];
+    u32x4 v[kGroup];
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g)
-            if (c0 + 64 * g < row_chunks) v[g] = src[c0 + 64 * g];
+    for (int g = 0; g < kGroup; ++g) v[g] = src[min(lane + 64 * g, row_chunks - 1)];
+    int p[KMAX];
+    final_positions<KMAX>(pos, topk_idx, base, row_token, t, k, E, lane, p);
+    for (int c0 = lane; c0 < row_chunks; c0 += 64 * kGroup) {
+        if (c0 != lane) {
+#pragma unroll
+            for (int g = 0; g < kGroup; ++g) v[g] = src[min(c0 + 64 * g, row_chunks - 1)];
+        }
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j < k) {
@@ -99,31 +107,31 @@ __global__ __launch_bounds__(256) void dispatch_mxfp8_kernel(const uint4* __rest
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
-    int p[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-        if (j < k) p[j] = final_pos(pos, topk_idx, base, row_token, t, j, k, E, lane);
-    if (base != nullptr) {
-        __builtin_amdgcn_wave_barrier();
-        if (lane < k) {
-#pragma unroll
-            for (int j = 0; j < KMAX; ++j)
-                if (j == lane) pos[(size_t)t * k + j] = p[j];
-        }
-    }
     // d % 128 == 0: a row is d / 16 lane-slices of 16 values; a group of 8
-    // lanes covers one 128-wide slice, so groups never straddle a row's end
+    // lanes covers one 128-wide slice, so groups never straddle a row's end.
+    // The first slices are requested before the positions (slices past the
+    // row end are loaded clamped and not stored).
     const int slices = d / 16;
     const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * (d / 8);
     constexpr int kG = 2;   // lane-slices per lane loaded before any is stored
-    for (int c0 = lane; c0 < slices; c0 += 64 * kG) {
-        u32x4 v[kG][2];
+    u32x4 v[kG][2];
 #pragma unroll
-        for (int g = 0; g < kG; ++g)
-            if (c0 + 64 * g < slices) {
-                v[g][0] = src[2 * (c0 + 64 * g)];
-                v[g][1] = src[2 * (c0 + 64 * g) + 1];
+    for (int g = 0; g < kG; ++g) {
+        const int c = min(lane + 64 * g, slices - 1);
+        v[g][0] = src[2 * c];
+        v[g][1] = src[2 * c + 1];
+    }
+    int p[KMAX];
+    final_positions<KMAX>(pos, topk_idx, base, row_token, t, k, E, lane, p);
+    for (int c0 = lane; c0 < slices; c0 += 64 * kG) {
+        if (c0 != lane) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                const int c = min(c0 + 64 * g, slices - 1);
+                v[g][0] = src[2 * c];
+                v[g][1] = src[2 * c + 1];
             }
+        }
 #pragma unroll
         for (int g = 0; g < kG; ++g) {
             const int c = c0 + 64 * g;
@@ -200,34 +208,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (t >= T) return;
+    // slots past k repeat slot k - 1 (loaded, never used) so that every load
+    // is unconditional: all KMAX x CG loads of a chunk group are in flight
+    // together, then accumulated in slot order
+    constexpr int CG = KMAX <= 4 ? kGroup : (KMAX <= 8 ? 2 : 1);
     int p[KMAX];
     float gt[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-            p[j] = pos[(size_t)t * k + j];
-            gt[j] = gate[(size_t)t * k + j];
-        }
+        const size_t i = (size_t)t * k + min(j, k - 1);
+        p[j] = pos[i];
+        gt[j] = gate[i];
     }
     const u32x4* src = reinterpret_cast<const u32x4*>(ye);
     u32x4* dst = reinterpret_cast<u32x4*>(y);
     constexpr int kN = kBf16 ? 8 : 4;
-    for (int c0 = lane; c0 < row_chunks; c0 += 64 * kGroup) {
-        float acc[kGroup][kN];
+    for (int c0 = lane; c0 < row_chunks; c0 += 64 * CG) {
+        float acc[CG][kN];
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g)
+        for (int g = 0; g < CG; ++g)
 #pragma unroll
             for (int i = 0; i < kN; ++i) acc[g][i] = 0.f;
+        u32x4 vv[KMAX][CG];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+            for (int g = 0; g < CG; ++g)
+                vv[j][g] = src[(size_t)p[j] * row_chunks + min(c0 + 64 * g, row_chunks - 1)];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             if (j < k) {
-                // the group's rows of slot j are loaded together, then accumulated in slot order
-                u32x4 v[kGroup];
+                const u32x4 (&v)[CG] = vv[j];
 #pragma unroll
-                for (int g = 0; g < kGroup; ++g)
-                    if (c0 + 64 * g < row_chunks) v[g] = src[(size_t)p[j] * row_chunks + c0 + 64 * g];
-#pragma unroll
-                for (int g = 0; g < kGroup; ++g) {
+                for (int g = 0; g < CG; ++g) {
                     if (c0 + 64 * g >= row_chunks) continue;
                     if (kBf16) {
 #pragma unroll
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
             }
         }
 #pragma unroll
-        for (int g = 0; g < kGroup; ++g) {
+        for (int g = 0; g < CG; ++g) {
             if (c0 + 64 * g >= row_chunks) continue;
             u32x4 o;
             if (kBf16) {
