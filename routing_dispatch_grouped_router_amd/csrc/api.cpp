@@ -564,7 +564,9 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     void* dh = at(ws, BL.dh);
     float* dsel = reinterpret_cast<float*>(at(ws, BL.dsel));
 
-    if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, T, d, E, k, s)))) return st;
+    float* srow = given ? nullptr : reinterpret_cast<float*>(at(ws, BL.srow));
+    if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, srow, T, d, E, k, s))))
+        return st;
     if ((st = launched(launch_gemm_plain(act, xe, w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
     if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
     const bool bf = act == MOE_BF16;
@@ -577,6 +579,9 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     };
     if (bf) {
         if ((st = launched(launch_seg_pad(off, E, R, poff, rowdst, s)))) return st;
+        // ta holds h^T then xe^T, tb dye^T then (da | db)^T
+        if ((st = launched(launch_zero_pads(off, poff, E, BL.Rp, ta, std::max(H, d), tb, std::max(d, 2 * H), s))))
+            return st;
         if ((st = transpose(h, H, ta)) || (st = transpose(dye, d, tb))) return st;
         if ((st = launched(launch_wgrad_mfma(0, ta, tb, poff, E, H, d, BL.Rp, dw_down, nullptr, s)))) return st;
     } else if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) {
@@ -600,8 +605,7 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     if (!given && (st = launched(launch_router_transpose(act, w_router, d, E, wrt, s)))) return st;
     if ((st = launched(launch_dx(act, dye, ps, idx, dsel, wrt, dx, T, d, E, k, s)))) return st;
     const int32_t* row_token = reinterpret_cast<const int32_t*>(at(fw, L.row_token));
-    if (!given && (st = launched(launch_wgrad_router(act, x, row_token, ps, dsel, off, T, k, d, E,
-                                                      reinterpret_cast<float*>(at(ws, BL.srow)),
+    if (!given && (st = launched(launch_wgrad_router(act, x, row_token, srow, off, T, k, d, E,
                                                       reinterpret_cast<float*>(at(ws, BL.rpart)), dw_router, s))))
         return st;
     return MOE_OK;

@@ -88,7 +88,7 @@ template <bool BF, int KMAX>
 __global__ __launch_bounds__(64 * kTokPerBlock) void combine_bwd_kernel(
     const void* __restrict__ dy, const void* __restrict__ ye, const float* __restrict__ gate,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ idx, void* __restrict__ dye,
-    float* __restrict__ dL, float* __restrict__ dsel, int T, int row_chunks, int E, int k) {
+    float* __restrict__ dL, float* __restrict__ dsel, float* __restrict__ srow, int T, int row_chunks, int E, int k) {
     constexpr int NV = BF ? 8 : 4;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * kTokPerBlock + (threadIdx.x >> 6);
@@ -135,10 +135,15 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void combine_bwd_kernel(
         if (j < k) ds[j] = g[j] * (dot[j] - inner);
     if (lane < k) {
         float mine = 0.f;
+        int row = 0;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
-            if (j == lane) mine = ds[j];
+            if (j == lane) {
+                mine = ds[j];
+                row = p[j];
+            }
         dsel[(size_t)t * k + lane] = mine;
+        if (srow != nullptr) srow[row] = mine;   // the same value at the routed row
     }
     for (int e = lane; e < E; e += 64) {
         float v = 0.f;
@@ -302,17 +307,22 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __res
 // column poff[e] + (offsets[e] % 8), after a lead of offsets[e] % 8 zero
 // columns, so that row r lands in a column congruent to r mod 8 and runs of 8
 // aligned rows become 16-byte stores; the segment is zero-padded to a multiple
-// of 32 columns.  poff[E] is the total.  One workgroup: per-expert lengths,
-// a Hillis-Steele scan in LDS.
-__global__ __launch_bounds__(1024) void seg_pad_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int32_t* __restrict__ poff) {
+// of 32 columns.  poff[E] is the total.  Every workgroup scans the padded
+// lengths in LDS (Hillis-Steele over up to 1024 experts; workgroup 0 stores
+// poff) and then writes rowdst for its rows: poff[e] + offsets[e] % 8 + r -
+// offsets[e] for the expert e holding row r (binary search over the offsets).
+__global__ __launch_bounds__(1024) void seg_map_kernel(const int32_t* __restrict__ offsets, int E, int R,
+                                                       int32_t* __restrict__ poff, int32_t* __restrict__ rowdst) {
     __shared__ int s_scan[1024];
+    __shared__ int s_off[kMaxExperts + 1];
     const int e = threadIdx.x;
     int len = 0;
     if (e < E) {
-        const int n = offsets[e + 1] - offsets[e];
-        len = n > 0 ? (offsets[e] % 8 + n + 31) / 32 * 32 : 0;
+        const int o0 = offsets[e], n = offsets[e + 1] - o0;
+        s_off[e] = o0;
+        len = n > 0 ? (o0 % 8 + n + 31) / 32 * 32 : 0;
     }
+    if (e == 0) s_off[E] = offsets[E];
     s_scan[e] = len;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {
@@ -321,22 +331,18 @@ __global__ __launch_bounds__(1024) void seg_pad_kernel(const int32_t* __restrict
         s_scan[e] += v;
         __syncthreads();
     }
-    if (e < E) poff[e] = s_scan[e] - len;
-    if (e == 1023) poff[E] = s_scan[1023];
-}
-
-// Destination column of every row r (expert e): poff[e] + offsets[e] % 8 + r
-// - offsets[e], congruent to r mod 8 (binary search over the offsets).
-__global__ __launch_bounds__(256) void seg_dst_kernel(const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ poff, int E, int R,
-                                                      int32_t* __restrict__ rowdst) {
-    for (int r = blockIdx.x * 256 + threadIdx.x; r < R; r += gridDim.x * 256) {
+    if (blockIdx.x == 0) {
+        if (e < E) poff[e] = s_scan[e] - len;
+        if (e == 1023) poff[E] = s_scan[1023];
+    }
+    for (int r = blockIdx.x * 1024 + e; r < R; r += gridDim.x * 1024) {
         int lo = 0, hi = E;   // the expert whose segment holds r: largest e with offsets[e] <= r
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (offsets[mid] <= r) lo = mid; else hi = mid;
+            if (s_off[mid] <= r) lo = mid; else hi = mid;
         }
-        rowdst[r] = poff[lo] + offsets[lo] % 8 + r - offsets[lo];
+        const int p0 = lo == 0 ? 0 : s_scan[lo - 1];   // poff[lo]
+        rowdst[r] = p0 + s_off[lo] % 8 + r - s_off[lo];
     }
 }
 
@@ -494,12 +500,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_t_kernel(const uint16_t* __res
     store_tile_t(tile, s_dst, XT, Rp, c0, N);
 }
 
-// srow[pos[t][j]] = dsel[t][j]: the router gradient of each routed row.
-__global__ __launch_bounds__(256) void srow_kernel(const int32_t* __restrict__ pos, const float* __restrict__ dsel,
-                                                   int n, float* __restrict__ srow) {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) srow[pos[i]] = dsel[i];
-}
-
 // dW_r[c][e] = sum over expert e's rows r of x[row_token[r]][c] srow[r] (the
 // token rows themselves: for MXFP8 blocks xe holds their quantised values), in
 // two passes.
@@ -575,10 +575,14 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
     }
 }
 
-// Zero the lead and tail padding of every expert segment in every row of XT.
+// Zero the lead and tail padding of every expert segment in the first MA rows
+// of XA and the first MB rows of XB (the transposes write only the rows'
+// columns, so the padding stays zero for every later operand in the buffers).
 __global__ __launch_bounds__(256) void zero_pad_kernel(const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ poff, int M, int Rp,
-                                                       uint16_t* __restrict__ XT) {
+                                                       const int32_t* __restrict__ poff, int MA, int MB, int Rp,
+                                                       uint16_t* __restrict__ XA, uint16_t* __restrict__ XB) {
+    const int M = blockIdx.z == 0 ? MA : MB;   // z selects the operand
+    uint16_t* __restrict__ XT = blockIdx.z == 0 ? XA : XB;
     const int e = blockIdx.y;
     const int n = offsets[e + 1] - offsets[e];
     const int lead = n > 0 ? offsets[e] % 8 : 0;
@@ -631,24 +635,24 @@ __global__ __launch_bounds__(256) void dq_mxfp8_kernel(const uint8_t* __restrict
 
 template <int KMAX>
 static void launch_combine_bwd_k(int act, const void* dy, const void* ye, const float* gate, const int32_t* pos,
-                                 const int32_t* idx, void* dye, float* dL, float* dsel, int T, int d, int E, int k,
-                                 hipStream_t s) {
+                                 const int32_t* idx, void* dye, float* dL, float* dsel, float* srow, int T, int d,
+                                 int E, int k, hipStream_t s) {
     dim3 grid((T + kTokPerBlock - 1) / kTokPerBlock), block(64 * kTokPerBlock);
     if (act == kF32)
         hipLaunchKernelGGL((combine_bwd_kernel<false, KMAX>), grid, block, 0, s, dy, ye, gate, pos, idx, dye, dL,
-                           dsel, T, d / 4, E, k);
+                           dsel, srow, T, d / 4, E, k);
     else
         hipLaunchKernelGGL((combine_bwd_kernel<true, KMAX>), grid, block, 0, s, dy, ye, gate, pos, idx, dye, dL,
-                           dsel, T, d / 8, E, k);
+                           dsel, srow, T, d / 8, E, k);
 }
 
 hipError_t launch_combine_bwd(int act, const void* dy, const void* ye, const float* gate, const int32_t* pos,
-                              const int32_t* idx, void* dye, float* dL, float* dsel, int T, int d, int E, int k,
-                              hipStream_t s) {
-    if (k <= 2) launch_combine_bwd_k<2>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
-    else if (k <= 4) launch_combine_bwd_k<4>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
-    else if (k <= 8) launch_combine_bwd_k<8>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
-    else launch_combine_bwd_k<kMaxTopK>(act, dy, ye, gate, pos, idx, dye, dL, dsel, T, d, E, k, s);
+                              const int32_t* idx, void* dye, float* dL, float* dsel, float* srow, int T, int d, int E,
+                              int k, hipStream_t s) {
+    if (k <= 2) launch_combine_bwd_k<2>(act, dy, ye, gate, pos, idx, dye, dL, dsel, srow, T, d, E, k, s);
+    else if (k <= 4) launch_combine_bwd_k<4>(act, dy, ye, gate, pos, idx, dye, dL, dsel, srow, T, d, E, k, s);
+    else if (k <= 8) launch_combine_bwd_k<8>(act, dy, ye, gate, pos, idx, dye, dL, dsel, srow, T, d, E, k, s);
+    else launch_combine_bwd_k<kMaxTopK>(act, dy, ye, gate, pos, idx, dye, dL, dsel, srow, T, d, E, k, s);
     return hipGetLastError();
 }
 
@@ -687,11 +691,10 @@ size_t router_wgrad_part_bytes(int R, int E, int d) {
     return (size_t)(R / 64 + std::min(E, R)) * d * 4 + ((size_t)E + 1) * 4 + 256;
 }
 
-hipError_t launch_wgrad_router(int act, const void* x, const int32_t* row_token, const int32_t* pos,
-                               const float* dsel, const int32_t* offsets, int T, int k, int d, int E, float* srow,
-                               float* part, float* dw_router, hipStream_t s) {
+hipError_t launch_wgrad_router(int act, const void* x, const int32_t* row_token, const float* srow,
+                               const int32_t* offsets, int T, int k, int d, int E, float* part, float* dw_router,
+                               hipStream_t s) {
     const int R = T * k;
-    hipLaunchKernelGGL(srow_kernel, dim3(std::min((R + 255) / 256, 1024)), dim3(256), 0, s, pos, dsel, R, srow);
     const int tiles = R / 64 + std::min(E, R);
     int32_t* tstart = reinterpret_cast<int32_t*>(part + (size_t)tiles * d);
     if (act == kF32)
@@ -739,9 +742,16 @@ hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t
 }
 
 hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s) {
-    hipLaunchKernelGGL(seg_pad_kernel, dim3(1), dim3(1024), 0, s, offsets, E, poff);
-    const int grid = std::min((R + 255) / 256, 1024);
-    hipLaunchKernelGGL(seg_dst_kernel, dim3(grid), dim3(256), 0, s, offsets, poff, E, R, rowdst);
+    const int grid = std::max(1, std::min((R + 1023) / 1024, 64));
+    hipLaunchKernelGGL(seg_map_kernel, dim3(grid), dim3(1024), 0, s, offsets, E, R, poff, rowdst);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_pads(const int32_t* offsets, const int32_t* poff, int E, int Rp, uint16_t* XA, int MA,
+                            uint16_t* XB, int MB, hipStream_t s) {
+    const int M = std::max(MA, MB);
+    dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E, 2);
+    hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, MA, MB, Rp, XA, XB);
     return hipGetLastError();
 }
 
@@ -749,8 +759,6 @@ hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* 
                                 const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s) {
     const long tiles = (long)((R + 127) / 128) * ((M + 127) / 128);
     hipLaunchKernelGGL(transpose_seg_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
-    dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
-    hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);
     return hipGetLastError();
 }
 
@@ -766,9 +774,6 @@ hipError_t launch_swiglu_bwd_t(const uint16_t* dh, uint16_t* ab, int R, int H, c
                                hipStream_t s) {
     const long tiles = (long)((R + 127) / 128) * (H / 64);
     hipLaunchKernelGGL(swiglu_bwd_t_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, dh, ab, R, H, rowdst, Rp, XT);
-    const int M = 2 * H;
-    dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E);
-    hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, M, Rp, XT);
     return hipGetLastError();
 }
 

@@ -110,10 +110,11 @@ hipError_t launch_pack_w1t(int act, const void* w_gate, const void* w_up, void* 
                            hipStream_t s);
 
 // dye[pos[t][j]] = gate[t][j] dy[t]; dL[T][E] (router gradient through the softmax of
-// the selected logits); dsel[t][j] = dL[t][idx[t][j]].
+// the selected logits); dsel[t][j] = dL[t][idx[t][j]], and with srow non-NULL also
+// srow[pos[t][j]] = dsel[t][j] (T k floats, the router gradient of every routed row).
 hipError_t launch_combine_bwd(int act, const void* dy, const void* ye, const float* gate, const int32_t* pos,
-                              const int32_t* idx, void* dye, float* dL, float* dsel, int T, int d, int E, int k,
-                              hipStream_t s);
+                              const int32_t* idx, void* dye, float* dL, float* dsel, float* srow, int T, int d, int E,
+                              int k, hipStream_t s);
 
 // ab [R][2H] (a | b interleaved as packed W1) := da | db from dh [R][H].
 hipError_t launch_swiglu_bwd(int act, const void* dh, void* ab, int R, int H, hipStream_t s);
@@ -123,13 +124,13 @@ hipError_t launch_wgrad_down(int act, const void* h, const void* dye, const int3
                              int d, float* dw_down, hipStream_t s);
 hipError_t launch_wgrad_w1(int act, const void* xe, const void* dab, const int32_t* offsets, int E, int R, int d,
                            int H, float* dw_gate, float* dw_up, hipStream_t s);
-// dw_router[c][e] = sum over expert e's rows r of x[row_token[r]][c] srow[r], srow[pos[t][j]] =
-// dsel[t][j] (= x^T dL, dL being zero outside the selected experts): srow T k floats, part
+// dw_router[c][e] = sum over expert e's rows r of x[row_token[r]][c] srow[r] (= x^T dL, dL
+// being zero outside the selected experts; srow from launch_combine_bwd): part
 // router_wgrad_part_bytes(T k, E, d) bytes.
 size_t router_wgrad_part_bytes(int R, int E, int d);
-hipError_t launch_wgrad_router(int act, const void* x, const int32_t* row_token, const int32_t* pos,
-                               const float* dsel, const int32_t* offsets, int T, int k, int d, int E, float* srow,
-                               float* part, float* dw_router, hipStream_t s);
+hipError_t launch_wgrad_router(int act, const void* x, const int32_t* row_token, const float* srow,
+                               const int32_t* offsets, int T, int k, int d, int E, float* part, float* dw_router,
+                               hipStream_t s);
 // W_r^T [E][d] from W_r [d][E] (activation type).
 hipError_t launch_router_transpose(int act, const void* w_router, int d, int E, void* wrt, hipStream_t s);
 
@@ -145,9 +146,13 @@ hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, con
 // bf16 weight gradients on MFMA (gemm_pipe.hip): per-expert transposed, zero-padded
 // operands XA [M][Rp], XB [N][Rp] with expert e's segment at poff[e] (seg_pad: a lead of
 // offsets[e] % 8 zero columns, the rows, zeros up to a multiple of 32; Rp >= T k + 40 E);
-// launch_transpose_seg writes such an operand from X [R][M].
+// launch_transpose_seg writes the rows of such an operand from X [R][M]; launch_zero_pads
+// zeroes the padding columns of the first MA rows of XA and MB rows of XB once (the
+// transposes never write there, so it stays zero for every operand later stored in them).
 // launch_seg_pad also writes rowdst [R], the destination column of every row.
 hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s);
+hipError_t launch_zero_pads(const int32_t* offsets, const int32_t* poff, int E, int Rp, uint16_t* XA, int MA,
+                            uint16_t* XB, int MB, hipStream_t s);
 hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
                                 const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s);
 // bf16 SwiGLU backward fused with the transpose of da | db into XT [2H][Rp] (as launch_transpose_seg).
