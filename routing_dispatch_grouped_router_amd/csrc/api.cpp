@@ -73,19 +73,13 @@ Packed packed_layout(const moe_problem& p) {
 }
 
 // Backward workspace: a | b (then da | db) [R][2H], dye (then dxe) [R][d],
-// dh [R][H], dsel [T][k] (router gradient at the selected experts); for bf16
-// also the padded segment starts poff [E+1] and two transposed operands of the
-// weight-gradient GEMMs, [max(H, d)][Rp] (h, then xe) and [max(d, 2H)][Rp]
-// (dye, then da | db), Rp = T k + 40 E rounded up to 32 (each segment adds at
-// most 7 lead and 31 tail columns); for the learned router W_r^T [E][d], the
-// router gradient per routed row and the per-tile partials of dW_r; for MXFP8
-// blocks the dequantised xe [R][d] and h [R][H] (bfloat16).
+// dh [R][H], dsel [T][k] (router gradient at the selected experts); for the
+// learned router W_r^T [E][d], the router gradient per routed row and the
+// per-tile partials of dW_r; for MXFP8 blocks the dequantised xe [R][d] and h
+// [R][H] (bfloat16).
 struct BwdLayout {
-    size_t ab, dye, dh, dsel, poff, rowdst, ta, tb, wrt, srow, rpart, xe16, h16, total;
-    int Rp;
+    size_t ab, dye, dh, dsel, wrt, srow, rpart, xe16, h16, total;
 };
-
-int bwd_rp(const moe_problem& p) { return (p.T * p.top_k + 40 * p.n_experts + 31) / 32 * 32; }
 
 // The backward runs in the activation type, bfloat16 for MXFP8 blocks (their
 // saved activations are dequantised first).
@@ -101,12 +95,6 @@ BwdLayout bwd_layout(const moe_problem& p) {
     B.dye = take(R * d * b);
     B.dh = take(R * H * b);
     B.dsel = take((size_t)p.T * p.top_k * 4);
-    const bool bf = ba == MOE_BF16;
-    B.Rp = bwd_rp(p);
-    B.poff = take(bf ? ((size_t)p.n_experts + 1) * 4 : 0);
-    B.rowdst = take(bf ? R * 4 : 0);
-    B.ta = take(bf ? std::max(H, d) * (size_t)B.Rp * 2 : 0);
-    B.tb = take(bf ? std::max(d, 2 * H) * (size_t)B.Rp * 2 : 0);
     const bool learned = !(p.flags & MOE_LOGITS_GIVEN);
     B.wrt = take(learned ? (size_t)p.n_experts * d * b : 0);
     B.srow = take(learned ? R * 4 : 0);
@@ -477,10 +465,6 @@ static int32_t check_backward(const moe_problem* p) {
     // the data-gradient GEMM over 2H reads rows of 2H activations with 32-bit offsets
     const long long eb = act_bytes(bwd_act(p->act_dtype));
     if ((long long)p->T * p->top_k * 2 * p->d_hidden * eb >= (1LL << 32)) return MOE_ERR_SHAPE;
-    // the weight-gradient GEMMs read the transposed operands with 32-bit offsets
-    if (bwd_act(p->act_dtype) == MOE_BF16 &&
-        (long long)std::max(p->d_model, 2 * p->d_hidden) * bwd_rp(*p) * 2 >= (1LL << 32))
-        return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -570,33 +554,19 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     if ((st = launched(launch_gemm_plain(act, xe, w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
     if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
     const bool bf = act == MOE_BF16;
-    int32_t* poff = reinterpret_cast<int32_t*>(at(ws, BL.poff));
-    int32_t* rowdst = reinterpret_cast<int32_t*>(at(ws, BL.rowdst));
-    uint16_t* ta = reinterpret_cast<uint16_t*>(at(ws, BL.ta));
-    uint16_t* tb = reinterpret_cast<uint16_t*>(at(ws, BL.tb));
-    auto transpose = [&](const void* X, int M, uint16_t* XT) {
-        return launched(launch_transpose_seg(static_cast<const uint16_t*>(X), R, M, off, poff, rowdst, E, BL.Rp, XT, s));
-    };
+    // weight gradients: dW_down = h^T dye, dW_gate | dW_up = xe^T (da | db) per expert
     if (bf) {
-        if ((st = launched(launch_seg_pad(off, E, R, poff, rowdst, s)))) return st;
-        // ta holds h^T then xe^T, tb dye^T then (da | db)^T
-        if ((st = launched(launch_zero_pads(off, poff, E, BL.Rp, ta, std::max(H, d), tb, std::max(d, 2 * H), s))))
+        if ((st = launched(launch_wgrad_rows(0, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(dye), off,
+                                             E, H, d, dw_down, nullptr, s))))
             return st;
-        if ((st = transpose(h, H, ta)) || (st = transpose(dye, d, tb))) return st;
-        if ((st = launched(launch_wgrad_mfma(0, ta, tb, poff, E, H, d, BL.Rp, dw_down, nullptr, s)))) return st;
     } else if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) {
         return st;
     }
-    if (bf) {   // da | db written in place and transposed into tb in one pass
-        if ((st = launched(launch_swiglu_bwd_t(static_cast<const uint16_t*>(dh), static_cast<uint16_t*>(ab), R, H, off,
-                                               poff, rowdst, E, BL.Rp, tb, s))))
-            return st;
-    } else if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) {
-        return st;
-    }
+    if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;   // da | db over a | b in place
     if (bf) {
-        if ((st = transpose(xe, d, ta))) return st;
-        if ((st = launched(launch_wgrad_mfma(1, ta, tb, poff, E, d, 2 * H, BL.Rp, dw_gate, dw_up, s)))) return st;
+        if ((st = launched(launch_wgrad_rows(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(ab), off,
+                                             E, d, 2 * H, dw_gate, dw_up, s))))
+            return st;
     } else if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) {
         return st;
     }

@@ -303,203 +303,6 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __res
     }
 }
 
-// Padded segments of the transposed operands.  Expert e's rows start at
-// column poff[e] + (offsets[e] % 8), after a lead of offsets[e] % 8 zero
-// columns, so that row r lands in a column congruent to r mod 8 and runs of 8
-// aligned rows become 16-byte stores; the segment is zero-padded to a multiple
-// of 32 columns.  poff[E] is the total.  Every workgroup scans the padded
-// lengths in LDS (Hillis-Steele over up to 1024 experts; workgroup 0 stores
-// poff) and then writes rowdst for its rows: poff[e] + offsets[e] % 8 + r -
-// offsets[e] for the expert e holding row r (binary search over the offsets).
-__global__ __launch_bounds__(1024) void seg_map_kernel(const int32_t* __restrict__ offsets, int E, int R,
-                                                       int32_t* __restrict__ poff, int32_t* __restrict__ rowdst) {
-    __shared__ int s_scan[1024];
-    __shared__ int s_off[kMaxExperts + 1];
-    const int e = threadIdx.x;
-    int len = 0;
-    if (e < E) {
-        const int o0 = offsets[e], n = offsets[e + 1] - o0;
-        s_off[e] = o0;
-        len = n > 0 ? (o0 % 8 + n + 31) / 32 * 32 : 0;
-    }
-    if (e == 0) s_off[E] = offsets[E];
-    s_scan[e] = len;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int v = e >= o ? s_scan[e - o] : 0;
-        __syncthreads();
-        s_scan[e] += v;
-        __syncthreads();
-    }
-    if (blockIdx.x == 0) {
-        if (e < E) poff[e] = s_scan[e] - len;
-        if (e == 1023) poff[E] = s_scan[1023];
-    }
-    for (int r = blockIdx.x * 1024 + e; r < R; r += gridDim.x * 1024) {
-        int lo = 0, hi = E;   // the expert whose segment holds r: largest e with offsets[e] <= r
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_off[mid] <= r) lo = mid; else hi = mid;
-        }
-        const int p0 = lo == 0 ? 0 : s_scan[lo - 1];   // poff[lo]
-        rowdst[r] = p0 + s_off[lo] % 8 + r - s_off[lo];
-    }
-}
-
-// 8 x 8 bfloat16 block transpose in registers: in[u] holds columns 0..7 of
-// row u (two per 32-bit word, the lower column in the low half); on return
-// out[j] holds rows 0..7 of column j the same way.
-__device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        // v_perm_b32 selects bytes of {src0, src1} = bytes 7..4, 3..0: the low
-        // half (bytes 1, 0) or the high half (bytes 3, 2) of each source word
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) out[j][q] = __builtin_amdgcn_perm(in[2 * q + 1][w], in[2 * q][w], sel);
-    }
-}
-
-// Tile of a 1-D grid of 8 * ceil(n / 8) workgroups over n tiles: workgroups
-// are dealt to the 8 XCDs in turn, so this gives each XCD a contiguous run of
-// tiles (neighbouring row blocks share DRAM pages and that XCD's L2); -1 for
-// the padding workgroups.
-__device__ __forceinline__ int xcd_tile(int n) {
-    const int per = gridDim.x / 8;
-    const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    return t < n ? t : -1;
-}
-
-inline unsigned xcd_grid(long n) { return (unsigned)((n + 7) / 8 * 8); }
-
-// Second half of a 128 x 128 tile transpose: the tile (16-byte chunk c of
-// tile row r at chunk c ^ (r / 8 % 16)) goes to rows m0 .. m0 + 127 of XT
-// (rows at or past M skipped), tile row r to column s_dst[r] (skipped when
-// negative).  Thread (a, c) reads the 8 x 8 block of rows 8a .. 8a + 7 and
-// columns 8c .. 8c + 7 (eight 16-byte LDS reads, bank-conflict free under the
-// swizzle), transposes it in registers and stores the 8 rows of each column
-// as one 16-byte run when they land in 8 consecutive columns (element by
-// element at an expert boundary).  The 16 lanes sharing c write 256
-// contiguous bytes of a row of XT.
-__device__ __forceinline__ void store_tile_t(const u32x4* tile, const int* s_dst, uint16_t* __restrict__ XT, int Rp,
-                                             int m0, int M) {
-    const int a = threadIdx.x & 15, c = threadIdx.x >> 4;
-    if (m0 + 8 * c >= M) return;
-    const int d0 = s_dst[8 * a];
-    uint16_t* dst = XT + (size_t)(m0 + 8 * c) * Rp;
-    if (d0 >= 0 && s_dst[8 * a + 7] == d0 + 7) {
-        u32x4 in[8], out[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) in[u] = tile[(8 * a + u) * 16 + (c ^ a)];
-        transpose8x8_bf16(in, out);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4*>(dst + (size_t)j * Rp + d0) = out[j];
-    } else {
-#pragma unroll 1
-        for (int u = 0; u < 8; ++u) {
-            const int du = s_dst[8 * a + u];
-            if (du < 0) continue;
-            const u32x4 w = tile[(8 * a + u) * 16 + (c ^ a)];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) dst[(size_t)j * Rp + du] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-        }
-    }
-}
-
-// XT [M][Rp] from X [R][M] (bfloat16): row r goes to column rowdst[r].
-// 128 x 128 tiles through LDS: 16 lanes load the 256 bytes of one row of X
-// into the swizzled tile, then store_tile_t writes it out transposed.
-__global__ __launch_bounds__(256) void transpose_seg_kernel(const uint16_t* __restrict__ X, int R, int M,
-                                                            const int32_t* __restrict__ rowdst, int Rp,
-                                                            uint16_t* __restrict__ XT) {
-    __shared__ u32x4 tile[128 * 16];
-    __shared__ int s_dst[128];
-    const int nr = (R + 127) / 128;
-    const int tl = xcd_tile(nr * ((M + 127) / 128));   // row blocks fastest
-    if (tl < 0) return;
-    const int r0 = (tl % nr) * 128, m0 = (tl / nr) * 128;
-    const int tid = threadIdx.x;
-    if (tid < 128) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
-    // rows past R and columns past M are loaded clamped and never stored
-    u32x4 v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int rr = (tid >> 4) + 16 * q, c = tid & 15;
-        const int r = min(r0 + rr, R - 1), m = min(m0 + 8 * c, M - 8);   // M % 8 == 0
-        v[q] = *reinterpret_cast<const u32x4*>(X + (size_t)r * M + m);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int rr = (tid >> 4) + 16 * q, c = tid & 15;
-        tile[rr * 16 + (c ^ ((rr >> 3) & 15))] = v[q];
-    }
-    __syncthreads();
-    store_tile_t(tile, s_dst, XT, Rp, m0, M);
-}
-
-// SwiGLU backward fused with the transpose of its output (bfloat16): over a
-// tile of 128 rows and 64 hidden units (the 128 interleaved columns of a | b
-// holding them), da | db are written over a | b in place and, through LDS,
-// into the transposed, padded operand XT [2H][Rp] of the gate/up weight
-// gradient (row r to column rowdst[r], 8 aligned rows per 16-byte store as in
-// transpose_seg_kernel).
-__global__ __launch_bounds__(256) void swiglu_bwd_t_kernel(const uint16_t* __restrict__ dh, uint16_t* __restrict__ ab,
-                                                           int R, int H, const int32_t* __restrict__ rowdst, int Rp,
-                                                           uint16_t* __restrict__ XT) {
-    __shared__ u32x4 tile[128 * 16];
-    __shared__ int s_dst[128];
-    const int nr = (R + 127) / 128;
-    const int tl = xcd_tile(nr * (H / 64));   // row blocks fastest
-    if (tl < 0) return;
-    const int r0 = (tl % nr) * 128, h0 = (tl / nr) * 64, c0 = 2 * h0;   // c0: first interleaved column
-    const int tid = threadIdx.x;
-    const int N = 2 * H;   // H % 64 == 0: every tile holds 64 whole hidden units
-    if (tid < 128) s_dst[tid] = r0 + tid < R ? rowdst[r0 + tid] : -1;
-    // units (row rr, hidden block hb of 2, chunk qq of 4): all 12 loads first
-    // (rows past R loaded clamped; their results are neither stored nor used)
-    float d[4][8], a[4][8], b[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = tid + 256 * q;
-        const int rr = i >> 3, hb = (i >> 2) & 1, qq = i & 3;
-        const size_t r = (size_t)min(r0 + rr, R - 1);
-        const int ca = 64 * hb + 8 * qq;             // column of the a chunk within the tile (b: +32)
-        load_chunk<true>(dh, (r * H + h0 + 32 * hb + 8 * qq) / 8, d[q]);
-        load_chunk<true>(ab, (r * N + c0 + ca) / 8, a[q]);
-        load_chunk<true>(ab, (r * N + c0 + ca + 32) / 8, b[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int i = tid + 256 * q;
-        const int rr = i >> 3, hb = (i >> 2) & 1, qq = i & 3;
-        const int r = r0 + rr;
-        const int ca = 64 * hb + 8 * qq;
-        float da[8], db[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float s = 1.0f / (1.0f + __expf(-a[q][u]));
-            da[u] = d[q][u] * b[q][u] * (s * (1.0f + a[q][u] * (1.0f - s)));
-            db[u] = d[q][u] * (a[q][u] * s);
-        }
-        if (r < R) {
-            store_chunk<true>(ab, ((size_t)r * N + c0 + ca) / 8, da);
-            store_chunk<true>(ab, ((size_t)r * N + c0 + ca + 32) / 8, db);
-        }
-        u32x4 wa, wb;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            wa[u] = pack_bf16x2(da[2 * u], da[2 * u + 1]);
-            wb[u] = pack_bf16x2(db[2 * u], db[2 * u + 1]);
-        }
-        const int sw = (rr >> 3) & 15;
-        tile[rr * 16 + ((ca >> 3) ^ sw)] = wa;
-        tile[rr * 16 + (((ca + 32) >> 3) ^ sw)] = wb;
-    }
-    __syncthreads();
-    store_tile_t(tile, s_dst, XT, Rp, c0, N);
-}
-
 // dW_r[c][e] = sum over expert e's rows r of x[row_token[r]][c] srow[r] (the
 // token rows themselves: for MXFP8 blocks xe holds their quantised values), in
 // two passes.
@@ -572,26 +375,6 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(const float* _
                 if (t0 + u < t1) s += v[u];
         }
         dw[i] = s;
-    }
-}
-
-// Zero the lead and tail padding of every expert segment in the first MA rows
-// of XA and the first MB rows of XB (the transposes write only the rows'
-// columns, so the padding stays zero for every later operand in the buffers).
-__global__ __launch_bounds__(256) void zero_pad_kernel(const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ poff, int MA, int MB, int Rp,
-                                                       uint16_t* __restrict__ XA, uint16_t* __restrict__ XB) {
-    const int M = blockIdx.z == 0 ? MA : MB;   // z selects the operand
-    uint16_t* __restrict__ XT = blockIdx.z == 0 ? XA : XB;
-    const int e = blockIdx.y;
-    const int n = offsets[e + 1] - offsets[e];
-    const int lead = n > 0 ? offsets[e] % 8 : 0;
-    const int a = poff[e], b = poff[e] + lead + n, z = poff[e + 1];
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < M * 40; i += gridDim.x * 256) {
-        const int m = i / 40, c = i % 40;   // at most 7 lead and 31 tail columns
-        const int col = c < 8 ? a + c : b + (c - 8);
-        const bool pad = c < 8 ? c < lead : col < z;
-        if (pad) XT[(size_t)m * Rp + col] = 0;
     }
 }
 
@@ -741,39 +524,10 @@ hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t
     return hipGetLastError();
 }
 
-hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s) {
-    const int grid = std::max(1, std::min((R + 1023) / 1024, 64));
-    hipLaunchKernelGGL(seg_map_kernel, dim3(grid), dim3(1024), 0, s, offsets, E, R, poff, rowdst);
-    return hipGetLastError();
-}
-
-hipError_t launch_zero_pads(const int32_t* offsets, const int32_t* poff, int E, int Rp, uint16_t* XA, int MA,
-                            uint16_t* XB, int MB, hipStream_t s) {
-    const int M = std::max(MA, MB);
-    dim3 gz((M * 40 + 255) / 256 < 64 ? (M * 40 + 255) / 256 : 64, E, 2);
-    hipLaunchKernelGGL(zero_pad_kernel, gz, dim3(256), 0, s, offsets, poff, MA, MB, Rp, XA, XB);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
-                                const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s) {
-    const long tiles = (long)((R + 127) / 128) * ((M + 127) / 128);
-    hipLaunchKernelGGL(transpose_seg_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, X, R, M, rowdst, Rp, XT);
-    return hipGetLastError();
-}
-
 hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s) {
     const size_t n = (size_t)R * (K / 16);
     const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
     hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid), dim3(256), 0, s, q, sc, R, K, out);
-    return hipGetLastError();
-}
-
-hipError_t launch_swiglu_bwd_t(const uint16_t* dh, uint16_t* ab, int R, int H, const int32_t* offsets,
-                               const int32_t* poff, const int32_t* rowdst, int E, int Rp, uint16_t* XT,
-                               hipStream_t s) {
-    const long tiles = (long)((R + 127) / 128) * (H / 64);
-    hipLaunchKernelGGL(swiglu_bwd_t_kernel, dim3(xcd_grid(tiles)), dim3(256), 0, s, dh, ab, R, H, rowdst, Rp, XT);
     return hipGetLastError();
 }
 

@@ -783,53 +783,81 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 // ============================================================================ weight gradients
 
 // K-grouped bf16 GEMM on MFMA for the weight gradients: for expert e
-//   C[e][m][n] = sum over k in [poff[e], poff[e+1]) of XA[m][k] XB[n][k]
-// where XA [M][Rp] and XB [N][Rp] are the transposed activations, each
-// expert's rows a run of columns at poff[e] zero-padded to a multiple of 32,
-// so the contraction axis is contiguous and no K-tile straddles two experts.
-// Workgroup tile 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA blocks of 32 x 32),
-// 64-byte K-tiles in a 4-stage ring loaded with global_load_lds and swizzled
-// as in the forward kernels, one barrier per K-tile: after it, the DMA of
-// K-tile kt + 3 refills the stage every wave finished reading in the previous
-// step.  Two workgroups share a CU.  An expert without rows writes zeros.
-// OMAP 0: C[e][m][n].  OMAP 1: the N axis interleaves gate and up columns (32
-// + 32 per 64); column n goes to C (gate) or C2 (up) [e][m][h], h = 32 (n /
-// 64) + n % 32.  Rows or columns past M, N are clamped in the loads and not
-// stored.
+//   C[e][m][n] = sum over rows r in [offsets[e], offsets[e+1]) of XA[r][m] XB[r][n]
+// with the activations as stored, XA [R][M] and XB [R][N], so no transposed
+// copy is made.  Workgroup tile 256 x 256, 8 waves of 128 x 64, a 4-stage
+// ring of K-tiles loaded with global_load_lds, one barrier per K-tile: after
+// it, the DMA of K-tile kt + 3 refills the stage every wave finished reading
+// in the previous step.  An expert without rows writes zeros.  OMAP 0:
+// C[e][m][n].  OMAP 1: the N axis interleaves gate and up columns (32 + 32 per
+// 64); column n goes to C (gate) or C2 (up) [e][m][h], h = 32 (n / 64) + n %
+// 32.  Rows or columns past M, N are clamped in the loads and not stored.  A K-tile is 32 rows:
+// each 1 KB DMA brings two 512-byte tile rows (256 columns), lane l's 16 bytes
+// landing at chunk l % 32 of row l / 32, which holds global chunk (l % 32) ^
+// 4 (row % 4).  The MFMA fragments (8 consecutive rows of one column per
+// lane) come from ds_read_b64_tr_b16: in each group of 16 lanes, lane L
+// addresses 4 columns of one row and receives element L % 4 of the 64-bit
+// reads of lanes 4 j + L / 4, j = 0..3 (measured on gfx950), so lane L
+// addressing row k0 + L / 4, columns c + 4 (L % 4) .. + 3 gets rows k0 .. k0
+// + 3 of column c + L.  Two such reads give the 8 rows of a fragment; the
+// XOR swizzle puts the 4 rows of a read in 4 different 64-byte bank windows.
+// Rows past the expert's segment (the last K-tile) are loaded clamped and
+// zeroed in the XB fragments.
+__device__ __forceinline__ bf16x8 tr_frag(const __attribute__((address_space(3))) char* base, uint32_t b0,
+                                          uint32_t b1) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lp;
+    const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(base + b0));
+    const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(base + b1));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 template <class WT, int OMAP>
-__global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_kernel(const uint16_t* __restrict__ XA,
-                                                                      const uint16_t* __restrict__ XB,
-                                                                      const int32_t* __restrict__ poff, int M, int N,
-                                                                      int Rp, float* __restrict__ C,
-                                                                      float* __restrict__ C2) {
-    constexpr int BM = WT::BM, BN = WT::BN, STAGES = 4, SC = (BM + BN) * 4, NW = WT::NW;
-    constexpr int A_DMA = BM / 16 / NW, B_DMA = BN / 16 / NW, P = A_DMA + B_DMA;
+__global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const uint16_t* __restrict__ XA,
+                                                                         const uint16_t* __restrict__ XB,
+                                                                         const int32_t* __restrict__ offsets, int M,
+                                                                         int N, float* __restrict__ C,
+                                                                         float* __restrict__ C2) {
+    constexpr int BM = WT::BM, BN = WT::BN, STAGES = 4, NW = WT::NW, KT = 32;
+    static_assert(BM == 256 && BN == 256, "a 1 KB DMA covers two 512-byte tile rows");
+    constexpr uint32_t SA = KT * BM * 2, SBYTES = KT * (BM + BN) * 2;
+    constexpr int A_DMA = KT / 2 / NW, B_DMA = KT / 2 / NW, P = A_DMA + B_DMA;
     constexpr int TM = BM / WT::WM / 32, TN = BN / WT::WN / 32;
     constexpr int WROWS = BM / WT::WM, WCOLS = BN / WT::WN;
-    __shared__ u32x4 ring[STAGES * SC];
+    __shared__ u32x4 ring[STAGES * SBYTES / 16];
     const int e = blockIdx.z, m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int k0 = poff[e], nk = (poff[e + 1] - k0) / 32;
+    const int o0 = offsets[e], len = offsets[e + 1] - o0, nk = (len + KT - 1) / KT;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WT::WN, wn = wave % WT::WN;
     const uint32_t ring_lds = lds_addr(ring);
-    const uint32_t rowbytes = (uint32_t)Rp * 2u;
-    const int drow = lane >> 2;
-    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
-    uint32_t offa[A_DMA], offb[B_DMA];
+    const __attribute__((address_space(3))) char* lbase = (const __attribute__((address_space(3))) char*)ring;
+    // DMA slot i: tile rows 2 q and 2 q + 1, q = wave * A_DMA + i (A; likewise B)
+    const int hr = lane >> 5, ch = lane & 31;
+    int trA[A_DMA], trB[B_DMA];
+    uint32_t colA[A_DMA], colB[B_DMA];
 #pragma unroll
-    for (int i = 0; i < A_DMA; ++i)
-        offa[i] = (uint32_t)min(m0 + 16 * (wave * A_DMA + i) + drow, M - 1) * rowbytes + (uint32_t)k0 * 2u + dchunk;
+    for (int i = 0; i < A_DMA; ++i) {
+        trA[i] = 2 * (wave * A_DMA + i) + hr;
+        colA[i] = (uint32_t)min(m0 + 8 * (ch ^ (4 * (trA[i] & 3))), M - 8) * 2u;
+    }
 #pragma unroll
-    for (int i = 0; i < B_DMA; ++i)
-        offb[i] = (uint32_t)min(n0 + 16 * (wave * B_DMA + i) + drow, N - 1) * rowbytes + (uint32_t)k0 * 2u + dchunk;
+    for (int i = 0; i < B_DMA; ++i) {
+        trB[i] = 2 * (wave * B_DMA + i) + hr;
+        colB[i] = (uint32_t)min(n0 + 8 * (ch ^ (4 * (trB[i] & 3))), N - 8) * 2u;
+    }
+    const uint32_t rbA = (uint32_t)M * 2u, rbB = (uint32_t)N * 2u;
     // K-tile kt into stage kt % 4; past the last K-tile a clamped copy lands in a stage nobody reads
     auto issue = [&](int kt) {
-        const uint32_t ko = (uint32_t)min(kt, nk - 1) * 64u;
-        const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SC * 16u;
+        const int kb = min(kt, nk - 1) * KT;
+        const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
 #pragma unroll
-        for (int i = 0; i < A_DMA; ++i) dma16(XA, offa[i] + ko, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+        for (int i = 0; i < A_DMA; ++i)
+            dma16(XA, (uint32_t)(o0 + min(kb + trA[i], len - 1)) * rbA + colA[i],
+                  st + (uint32_t)(wave * A_DMA + i) * 1024u);
 #pragma unroll
-        for (int i = 0; i < B_DMA; ++i) dma16(XB, offb[i] + ko, st + BM * 64u + (uint32_t)(wave * B_DMA + i) * 1024u);
+        for (int i = 0; i < B_DMA; ++i)
+            dma16(XB, (uint32_t)(o0 + min(kb + trB[i], len - 1)) * rbB + colB[i],
+                  st + SA + (uint32_t)(wave * B_DMA + i) * 1024u);
     };
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -838,8 +866,14 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_kernel(const uin
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
-    const int arow = (wm * WROWS + (lane & 31)) * 4, brow = (BM + wn * WCOLS + (lane & 31)) * 4;
+    // transposed-read addresses (bytes within a stage) of k-step s, read r:
+    // row 16 s + 8 h + 4 r + L / 4, column c + 16 (G % 2) + 4 (L % 4)
+    const int L = lane & 15, G = lane >> 4, h = lane >> 5;
+    auto tr_addr = [&](int s2, int r, int col) -> uint32_t {
+        const int row = 16 * s2 + 8 * h + 4 * r + (L >> 2);
+        const int c = col + 16 * (G & 1) + 4 * (L & 3);
+        return (uint32_t)row * (BM * 2u) + (((uint32_t)c * 2u) ^ (64u * (uint32_t)(L >> 2)));
+    };
     if (nk > 0) {
         issue(0);
         issue(1);
@@ -848,16 +882,31 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_kernel(const uin
             wait_vm<2 * P>();   // K-tile kt landed; kt + 1 and kt + 2 may still be in flight
             ring_barrier();     // every wave's reads of kt - 1 are complete (its MFMAs used them)
             issue(kt + 3);      // into the stage of kt - 1
-            const u32x4* stage = ring + (kt & (STAGES - 1)) * SC;
+            const __attribute__((address_space(3))) char* sa = lbase + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
+            const __attribute__((address_space(3))) char* sb = sa + SA;
             bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
-                    fa[s2][i] = __builtin_bit_cast(bf16x8, stage[arow + i * 128 + ((2 * s2 + half) ^ fsw)]);
+                for (int i = 0; i < TM; ++i) {
+                    const int col = wm * WROWS + i * 32;
+                    fa[s2][i] = tr_frag(sa, tr_addr(s2, 0, col), tr_addr(s2, 1, col));
+                }
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    fb[s2][j] = __builtin_bit_cast(bf16x8, stage[brow + j * 128 + ((2 * s2 + half) ^ fsw)]);
+                for (int j = 0; j < TN; ++j) {
+                    const int col = wn * WCOLS + j * 32;
+                    fb[s2][j] = tr_frag(sb, tr_addr(s2, 0, col), tr_addr(s2, 1, col));
+                }
+            }
+            const int rem = len - kt * KT;
+            if (rem < KT) {   // rows at or past rem belong to the next expert (or are clamped copies)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            if (16 * s2 + 8 * h + u >= rem) fb[s2][j][u] = (__bf16)0.0f;
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
@@ -869,7 +918,7 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_kernel(const uin
         }
     }
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
-    // lane l holds row m of its block and, per run q, 4 consecutive columns 8 q + 4 (l / 32) + 0..3
+    const int half = lane >> 5;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int m = m0 + wm * WROWS + i * 32 + (lane & 31);
@@ -885,9 +934,9 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_kernel(const uin
                 if (OMAP == 0) {
                     *reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n) = v;
                 } else {
-                    const int Hh = N / 2, h = 32 * (n / 64) + n % 32;
+                    const int Hh = N / 2, hh = 32 * (n / 64) + n % 32;
                     float* dst = ((n / 32) & 1) ? C2 : C;
-                    *reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + h) = v;
+                    *reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh) = v;
                 }
             }
     }
@@ -899,23 +948,17 @@ template <int BM_, int BN_, int WM_, int WN_, int OCC_>
 struct WgradTile {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NW = WM * WN, NTHR = 64 * NW, OCC = OCC_;
 };
-using WgradSmall = WgradTile<128, 128, 2, 2, 2>;   // 4 waves of 64 x 64, two workgroups per CU
-using WgradBig = WgradTile<256, 256, 2, 4, 1>;     // 8 waves of 128 x 64, as the forward bf16 tiles
+using WgradBig = WgradTile<256, 256, 2, 4, 1>;   // 8 waves of 128 x 64, as the forward bf16 tiles
 
-template <class WT>
-hipError_t launch_wgrad_tile(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
-                             int N, int Rp, float* C, float* C2, hipStream_t s) {
+hipError_t launch_wgrad_rows(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* offsets, int E, int M,
+                             int N, float* C, float* C2, hipStream_t s) {
+    using WT = WgradBig;
     dim3 grid((N + WT::BN - 1) / WT::BN, (M + WT::BM - 1) / WT::BM, E), block(WT::NTHR);
     if (omap == 1)
-        hipLaunchKernelGGL((gemm_wgrad_kernel<WT, 1>), grid, block, 0, s, XA, XB, poff, M, N, Rp, C, C2);
+        hipLaunchKernelGGL((gemm_wgrad_rm_kernel<WT, 1>), grid, block, 0, s, XA, XB, offsets, M, N, C, C2);
     else
-        hipLaunchKernelGGL((gemm_wgrad_kernel<WT, 0>), grid, block, 0, s, XA, XB, poff, M, N, Rp, C, C2);
+        hipLaunchKernelGGL((gemm_wgrad_rm_kernel<WT, 0>), grid, block, 0, s, XA, XB, offsets, M, N, C, C2);
     return hipGetLastError();
-}
-
-hipError_t launch_wgrad_mfma(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
-                             int N, int Rp, float* C, float* C2, hipStream_t s) {
-    return launch_wgrad_tile<WgradBig>(omap, XA, XB, poff, E, M, N, Rp, C, C2, s);
 }
 
 // ============================================================================ launchers

@@ -143,23 +143,11 @@ hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t
 hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, const int32_t* offsets, int R, int E,
                              int N, int K, int ldc, hipStream_t s);
 
-// bf16 weight gradients on MFMA (gemm_pipe.hip): per-expert transposed, zero-padded
-// operands XA [M][Rp], XB [N][Rp] with expert e's segment at poff[e] (seg_pad: a lead of
-// offsets[e] % 8 zero columns, the rows, zeros up to a multiple of 32; Rp >= T k + 40 E);
-// launch_transpose_seg writes the rows of such an operand from X [R][M]; launch_zero_pads
-// zeroes the padding columns of the first MA rows of XA and MB rows of XB once (the
-// transposes never write there, so it stays zero for every operand later stored in them).
-// launch_seg_pad also writes rowdst [R], the destination column of every row.
-hipError_t launch_seg_pad(const int32_t* offsets, int E, int R, int32_t* poff, int32_t* rowdst, hipStream_t s);
-hipError_t launch_zero_pads(const int32_t* offsets, const int32_t* poff, int E, int Rp, uint16_t* XA, int MA,
-                            uint16_t* XB, int MB, hipStream_t s);
-hipError_t launch_transpose_seg(const uint16_t* X, int R, int M, const int32_t* offsets, const int32_t* poff,
-                                const int32_t* rowdst, int E, int Rp, uint16_t* XT, hipStream_t s);
-// bf16 SwiGLU backward fused with the transpose of da | db into XT [2H][Rp] (as launch_transpose_seg).
-hipError_t launch_swiglu_bwd_t(const uint16_t* dh, uint16_t* ab, int R, int H, const int32_t* offsets,
-                               const int32_t* poff, const int32_t* rowdst, int E, int Rp, uint16_t* XT,
-                               hipStream_t s);
-hipError_t launch_wgrad_mfma(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* poff, int E, int M,
-                             int N, int Rp, float* C, float* C2, hipStream_t s);
+// bf16 weight gradients on MFMA (gemm_pipe.hip), per expert e over its rows
+// [offsets[e], offsets[e+1]) of the row-major activations XA [R][M], XB [R][N]:
+// omap 0: C[e][m][n] = sum_r XA[r][m] XB[r][n]; omap 1: XB's columns interleave gate
+// and up (32 + 32 per 64) and go to C (gate) or C2 (up) [e][m][N/2].
+hipError_t launch_wgrad_rows(int omap, const uint16_t* XA, const uint16_t* XB, const int32_t* offsets, int E, int M,
+                             int N, float* C, float* C2, hipStream_t s);
 
 }  // namespace moe
