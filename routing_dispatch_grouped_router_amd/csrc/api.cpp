@@ -551,24 +551,25 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     float* srow = given ? nullptr : reinterpret_cast<float*>(at(ws, BL.srow));
     if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, srow, T, d, E, k, s))))
         return st;
-    if ((st = launched(launch_gemm_plain(act, xe, w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
-    if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
     const bool bf = act == MOE_BF16;
-    // weight gradients: dW_down = h^T dye, dW_gate | dW_up = xe^T (da | db) per expert
     if (bf) {
+        // dh = dye W_down^T, then the gate/up recompute with the SwiGLU backward
+        // in its epilogue: da | db straight into ab
+        if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
+        if ((st = launched(launch_gemm_dswiglu(xe, w1, dh, ab, off, R, E, d, H, s)))) return st;
+        // weight gradients: dW_down = h^T dye, dW_gate | dW_up = xe^T (da | db) per expert
         if ((st = launched(launch_wgrad_rows(0, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(dye), off,
                                              E, H, d, dw_down, nullptr, s))))
             return st;
-    } else if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) {
-        return st;
-    }
-    if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;   // da | db over a | b in place
-    if (bf) {
         if ((st = launched(launch_wgrad_rows(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(ab), off,
                                              E, d, 2 * H, dw_gate, dw_up, s))))
             return st;
-    } else if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) {
-        return st;
+    } else {
+        if ((st = launched(launch_gemm_plain(act, xe, w1, ab, off, R, E, 2 * H, d, 2 * H, s)))) return st;
+        if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
+        if ((st = launched(launch_wgrad_down(act, h, dye, off, E, R, H, d, dw_down, s)))) return st;
+        if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;   // da | db over a | b in place
+        if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) return st;
     }
     if ((st = launched(launch_gemm_plain(act, ab, pb + BP.w1t, dye, off, R, E, d, 2 * H, d, s)))) return st;
     void* wrt = given ? nullptr : at(ws, BL.wrt);

@@ -164,6 +164,13 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
     return hipGetLastError();
 }
 
+hipError_t launch_gemm_dswiglu(const void* xe, const void* w1, const void* dh, void* dab, const int32_t* offsets,
+                               int R, int E, int d, int H, hipStream_t s) {
+    return launch_bf16_pipe(2, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
+                            static_cast<uint16_t*>(dab), offsets, R, E, 2 * H, d, 2 * H, nullptr, s,
+                            static_cast<const uint16_t*>(dh));
+}
+
 hipError_t launch_gemm_plain(int act, const void* A, const void* B, void* C, const int32_t* offsets, int R, int E,
                              int N, int K, int ldc, hipStream_t s) {
     if (act == kBF16)

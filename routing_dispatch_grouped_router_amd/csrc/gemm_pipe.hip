@@ -284,16 +284,51 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
 
 // Epilogue of the bf16 kernel.  EPI 0: C = acc as bf16.  EPI 1: columns come
 // in gate/up pairs of 32; C column (pair column)/2 + j = silu(gate_j) * up_j.
+// EPI 2 (SwiGLU backward): the gate/up pairs a, b are rounded to bf16 (the
+// values a stored recompute would hold) and, with dh [rows][N/2] (aux), C
+// receives da = dh b s (1 + a (1 - s)), db = dh a s, s = sigmoid(a), in the
+// layout of a | b.  The dh values of all of a wave's rows are requested
+// before any is used.
 template <class TL, int EPI>
 __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], uint16_t* __restrict__ C,
                                             int ldc, int N, const TileCoord& c, int wm, int wn,
-                                            u32x4* __restrict__ obuf) {
+                                            u32x4* __restrict__ obuf, const uint16_t* __restrict__ aux) {
     const int lane = threadIdx.x & 63;
+    static_assert(EPI != 2 || TL::TN == 2, "one gate/up pair per wave row block");
+    uint32_t dhw[EPI == 2 ? TL::TM : 1][4][2];   // dh runs: [mi][q] = 4 bf16 of h 8 q + 4 half + 0..3
+    if (EPI == 2) {
+        // the wave's 32 hidden units (clamped for a pair past N, whose stores are skipped)
+        const int hb = min((c.n0 + wn * TL::WCOLS) / 2, N / 2 - 32) + 4 * (lane >> 5);
+#pragma unroll
+        for (int mi = 0; mi < TL::TM; ++mi) {
+            const int r = min(wm * TL::WROWS + mi * 32 + (lane & 31), c.rows - 1);   // clamped rows not stored
+            const uint16_t* src = aux + (size_t)(c.row0 + r) * (N / 2) + hb;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint2 w = *reinterpret_cast<const uint2*>(src + 8 * q);
+                dhw[mi][q][0] = w.x;
+                dhw[mi][q][1] = w.y;
+            }
+        }
+    }
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
         const int r = wm * TL::WROWS + mi * 32 + (lane & 31);
         const bool valid = r < c.rows;
-        if (EPI == 0) {
+        if (EPI == 2) {
+            float g[16], u[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float a = bf16_round(acc[mi][0][i]), b = bf16_round(acc[mi][1][i]);
+                const uint32_t w = dhw[mi][i / 4][(i % 4) / 2];
+                const float d = __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                const float sg = 1.0f / (1.0f + __expf(-a));
+                g[i] = d * b * (sg * (1.0f + a * (1.0f - sg)));
+                u[i] = d * (a * sg);
+            }
+            const int rb = wm * TL::WROWS + mi * 32;
+            store_bf16_pair_rows<16>(C, (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS, N, g, u, obuf);
+        } else if (EPI == 0) {
 #pragma unroll
             for (int np = 0; np < TL::TN / 2; ++np) {
                 float g[16], u[16];
@@ -338,16 +373,18 @@ __device__ __forceinline__ void bf_mfma1(int i, const bf16x8 (&fa)[TL::TM], cons
 // g + 1's k-step 0 into set 0.  The epilogue runs between tiles while the
 // next tile's first K-tiles are in flight; its stores count in vmcnt after
 // those DMAs, which only makes later waits wait longer.
-template <class TL, int EPI>   // EPI 0: C = A B (bf16);  1: C = silu(A Bgate) * (A Bup) (bf16, N/2 columns)
+// EPI 0: C = A B (bf16);  1: C = silu(A Bgate) * (A Bup) (bf16, N/2 columns);
+// 2: C = the SwiGLU backward of (A Bgate, A Bup) given dh = aux (bf16, N columns)
+template <class TL, int EPI>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                            uint16_t* __restrict__ C, const int32_t* __restrict__ offsets, int E, int N, int K,
-                           int ldc) {
+                           int ldc, const uint16_t* __restrict__ aux) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
     constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
     static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
-    constexpr int kObufChunks = EPI == 0 ? 128 : 0;   // per wave: 16 rows x 128 bytes of output
+    constexpr int kObufChunks = EPI != 1 ? 128 : 0;   // per wave: 16 rows x 128 bytes of output
     __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
     __shared__ int s_tstart[kMaxExperts + 1];
@@ -459,7 +496,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
         for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
 
         // set 0 now holds k-step 0 of the next tile's first K-tile
-        bf_epilogue<TL, EPI>(acc, C, ldc, N, c0, wm, wn, obuf + wave * kObufChunks);
+        bf_epilogue<TL, EPI>(acc, C, ldc, N, c0, wm, wn, obuf + wave * kObufChunks, aux);
         if (tile + G >= total) break;
         tile += G;
         c0 = c1;
@@ -965,10 +1002,11 @@ hipError_t launch_wgrad_rows(int omap, const uint16_t* XA, const uint16_t* XB, c
 
 template <class TL, int EPI>
 hipError_t launch_bf16_pipe_tile(const uint16_t* A, const uint16_t* Bw, uint16_t* C, const int32_t* offsets,
-                                 int R, int E, int N, int K, int ldc, const int32_t* host_counts, hipStream_t s) {
+                                 int R, int E, int N, int K, int ldc, const int32_t* host_counts,
+                                 const uint16_t* aux, hipStream_t s) {
     const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
     hipLaunchKernelGGL((gemm_bf16_pipe_kernel<TL, EPI>), dim3(grid), dim3(TL::NTHR), 0, s, A, Bw, C, offsets, E, N,
-                       K, ldc);
+                       K, ldc, aux);
     return hipGetLastError();
 }
 
@@ -986,9 +1024,11 @@ using BfRing = RingTile<256, 256, 2, 4>;    // 8 waves of 128 x 64
 using Fp8Ring = RingTile<256, 256, 2, 2>;   // 4 waves of 128 x 128
 
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C, const int32_t* offsets,
-                            int R, int E, int N, int K, int ldc, const int32_t* host_counts, hipStream_t s) {
-    if (epi == 1) return launch_bf16_pipe_tile<BfRing, 1>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, s);
-    return launch_bf16_pipe_tile<BfRing, 0>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, s);
+                            int R, int E, int N, int K, int ldc, const int32_t* host_counts, hipStream_t s,
+                            const uint16_t* aux) {
+    if (epi == 1) return launch_bf16_pipe_tile<BfRing, 1>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
+    if (epi == 2) return launch_bf16_pipe_tile<BfRing, 2>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
+    return launch_bf16_pipe_tile<BfRing, 0>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
 }
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,

@@ -29,6 +29,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// x rounded to the nearest bfloat16 (ties to even), as a float32.
+__device__ __forceinline__ float bf16_round(float x) { return __uint_as_float((uint32_t)f32_to_bf16(x) << 16); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const bf16x2 v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);

@@ -79,10 +79,11 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
 int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts);
 int set_pipe_grid_cap(int cap);
 
-// Pipelined bf16 grouped GEMM (gemm_pipe.hip); epi 1 = SwiGLU epilogue (C has N/2 columns).
+// Pipelined bf16 grouped GEMM (gemm_pipe.hip); epi 1 = SwiGLU epilogue (C has N/2 columns);
+// epi 2 = SwiGLU backward epilogue (C = da | db from the gate/up pairs and dh = aux [R][N/2]).
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C,
                             const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                            const int32_t* host_counts, hipStream_t s);
+                            const int32_t* host_counts, hipStream_t s, const uint16_t* aux = nullptr);
 
 // Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K,
 // scales stored [K/128][rows][4] (A: R rows; B: per expert, N rows).
@@ -137,6 +138,11 @@ hipError_t launch_router_transpose(int act, const void* w_router, int d, int E, 
 // dx[t] = sum_j dxe[pos[t][j]] (+ sum_j dsel[t][j] W_r^T[idx[t][j]] when wrt [E][d] is given).
 hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t* idx, const float* dsel,
                      const void* wrt, void* dx, int T, int d, int E, int k, hipStream_t s);
+
+// bf16: da | db [R][2H] (a | b interleaved as packed W1) from the recomputed gate/up
+// projections xe W1 (rounded to bf16) and dh [R][H], in one grouped GEMM.
+hipError_t launch_gemm_dswiglu(const void* xe, const void* w1, const void* dh, void* dab, const int32_t* offsets,
+                               int R, int E, int d, int H, hipStream_t s);
 
 // C = A B^T per expert segment, stored as computed (float32 or bfloat16): the
 // grouped GEMM without an epilogue (recompute and data gradients).
