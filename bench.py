@@ -66,6 +66,8 @@ def stage_models(w: W.Workload) -> dict:
         "dispatch": ("hbm", T * d * bin_ + R * d * bxe + scale_b + R * 4 * 3 + R * 4, "GB/s", HBM_GBPS),
         "gemm1_gate_up_swiglu": (gemm_bound, 4.0 * R * d * H, "TFLOP/s", gemm_peak),
         "gemm2_down": (gemm_bound, 2.0 * R * H * d, "TFLOP/s", gemm_peak),
+        # bf16: both projections in one launch
+        "grouped_ffn": (gemm_bound, 6.0 * R * d * H, "TFLOP/s", gemm_peak),
         "combine": ("hbm", R * d * bye + R * 8 + T * d * bye, "GB/s", HBM_GBPS),
     }
 
@@ -83,6 +85,8 @@ KERNEL_SOURCES = {
                              "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
     "gemm2_down": ["routing_dispatch_grouped_router_amd/csrc/gemm_pipe.hip",
                    "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
+    "grouped_ffn": ["routing_dispatch_grouped_router_amd/csrc/gemm_pipe.hip",
+                    "routing_dispatch_grouped_router_amd/csrc/grouped_sched.h"],
     "dispatch": ["routing_dispatch_grouped_router_amd/csrc/dispatch.hip"],
     "combine": ["routing_dispatch_grouped_router_amd/csrc/dispatch.hip"],
 }
@@ -336,7 +340,7 @@ def main(argv=None):
     bound, amount, unit, peak = models[dom]
     ach = stage_out[dom]["achieved"]
     traffic = measured_traffic(w.name, dom)
-    gemm_ms = sum(ms for n, ms in stages if n.startswith("gemm"))
+    gemm_ms = sum(ms for n, ms in stages if n.startswith("gemm") or n == "grouped_ffn")
     gemm_peak = models["gemm1_gate_up_swiglu"][3]
     flops = w.expert_flops + w.router_flops
     result = {

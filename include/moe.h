@@ -174,7 +174,12 @@ int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, vo
  *   packed_w     : from moe_pack_weights
  *   offsets      : device int32 [E+1] from moe_route
  *   ye           : device [R, d] out (float32 for MOE_F32, else bfloat16)
- *   ws           : workspace (holds h)
+ *   ws           : workspace (holds h and, for bfloat16, the counters of the
+ *                  fused launch, cleared by each call; calls sharing a
+ *                  workspace must not overlap)
+ * bfloat16 (d_model and d_hidden >= 128) runs both projections in one
+ * persistent launch: a GEMM2 tile starts once the GEMM1 tiles of its rows have
+ * finished, so neither GEMM ends in a partly filled round.
  * Every output tile is computed whole by one workgroup in a fixed K order, so
  * the result does not depend on the grid (moe_set_gemm_grid_cap). */
 int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* xe_scale,

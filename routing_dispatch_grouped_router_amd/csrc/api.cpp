@@ -19,11 +19,17 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t hist, base, psum, ppart, rwt, h, h_scale, route_end, gemm_end;
+    size_t hist, base, psum, ppart, rwt, h, h_scale, sync, route_end, gemm_end;
     size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, ye, total;
 };
 
 size_t act_bytes(int act) { return act == MOE_F32 ? 4 : (act == MOE_BF16 ? 2 : 1); }
+
+// bf16 experts run both projections in one launch when each has at least four
+// 32-wide K-tiles (the fused kernel streams a tile's first four K-tiles ahead)
+bool use_ffn(const moe_problem& p) {
+    return p.act_dtype == MOE_BF16 && p.d_model >= 128 && p.d_hidden >= 128;
+}
 
 Layout layout(const moe_problem& p) {
     Layout L{};
@@ -40,6 +46,7 @@ Layout layout(const moe_problem& p) {
     L.route_end = off;
     L.h = take(R * H * act_bytes(p.act_dtype));
     L.h_scale = take(mx ? R * H / 32 : 0);
+    L.sync = take(use_ffn(p) ? (size_t)ffn_sync_ints((int)R, (int)E) * 4 : 0);   // fused FFN counters
     L.gemm_end = off;
     L.idx = take(R * 4);
     L.gate = take(R * 4);
@@ -304,6 +311,15 @@ int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* 
     const uint8_t* s2 = reinterpret_cast<const uint8_t*>(static_cast<const char*>(pw) + P.s2);
     void* h = at(ws, L.h);
     uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
+    if (use_ffn(*p)) {
+        int32_t* ffn_sync = reinterpret_cast<int32_t*>(at(ws, L.sync));
+        if ((st = launched(launch_zero_i32(ffn_sync, ffn_sync_ints(R, E), s)))) return st;
+        return launched(launch_bf16_ffn(static_cast<const uint16_t*>(xe),
+                                        reinterpret_cast<const uint16_t*>(static_cast<const char*>(pw) + P.w1),
+                                        static_cast<uint16_t*>(h),
+                                        reinterpret_cast<const uint16_t*>(static_cast<const char*>(pw) + P.w2),
+                                        static_cast<uint16_t*>(ye), offsets, ffn_sync, R, E, d, H, nullptr, s));
+    }
     if ((st = launched(launch_gemm1(p->act_dtype, xe, xe_scale, static_cast<const char*>(pw) + P.w1, s1,
                                     offsets, h, hs, R, E, d, H, nullptr, s))))
         return st;
@@ -367,7 +383,10 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
     if ((st = launched(launch_route_topk(logits, T, E, k, idx, gate, ps, hist, psum,
                                                   reinterpret_cast<float*>(at(ws, L.ppart)), s)))) return st;
     if ((st = prof_mark("route_topk", s))) return st;
-    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, cnt, off, psum, router_stats, T, k, s))))
+    const bool ffn = !identity && use_ffn(*p);
+    int32_t* ffn_sync = reinterpret_cast<int32_t*>(at(ws, L.sync));
+    if ((st = launched(launch_route_scan(hist, route_blocks(T), E, base, cnt, off, psum, router_stats, T, k, s,
+                                         ffn ? ffn_sync : nullptr, ffn ? ffn_sync_ints(R, E) : 0))))
         return st;
     if ((st = prof_mark("route_scan", s))) return st;
     if (host_counts) {
@@ -387,14 +406,23 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
         const char* pw = static_cast<const char*>(packed_w);
         void* h = at(ws, L.h);
         uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
-        if ((st = launched(launch_gemm1(act, xe, xs, pw + P.w1, reinterpret_cast<const uint8_t*>(pw + P.s1),
-                                        off, h, hs, R, E, d, H, host_counts, s))))
-            return st;
-        if ((st = prof_mark("gemm1_gate_up_swiglu", s))) return st;
-        if ((st = launched(launch_gemm2(act, h, hs, pw + P.w2, reinterpret_cast<const uint8_t*>(pw + P.s2),
-                                        off, ye, R, E, d, H, host_counts, s))))
-            return st;
-        if ((st = prof_mark("gemm2_down", s))) return st;
+        if (ffn) {
+            if ((st = launched(launch_bf16_ffn(static_cast<const uint16_t*>(xe),
+                                               reinterpret_cast<const uint16_t*>(pw + P.w1), static_cast<uint16_t*>(h),
+                                               reinterpret_cast<const uint16_t*>(pw + P.w2),
+                                               static_cast<uint16_t*>(ye), off, ffn_sync, R, E, d, H, host_counts, s))))
+                return st;
+            if ((st = prof_mark("grouped_ffn", s))) return st;
+        } else {
+            if ((st = launched(launch_gemm1(act, xe, xs, pw + P.w1, reinterpret_cast<const uint8_t*>(pw + P.s1),
+                                            off, h, hs, R, E, d, H, host_counts, s))))
+                return st;
+            if ((st = prof_mark("gemm1_gate_up_swiglu", s))) return st;
+            if ((st = launched(launch_gemm2(act, h, hs, pw + P.w2, reinterpret_cast<const uint8_t*>(pw + P.s2),
+                                            off, ye, R, E, d, H, host_counts, s))))
+                return st;
+            if ((st = prof_mark("gemm2_down", s))) return st;
+        }
     }
     if ((st = launched(launch_combine(act, ye, gate, ps, y, T, d, k, s)))) return st;
     if ((st = prof_mark("combine", s))) return st;

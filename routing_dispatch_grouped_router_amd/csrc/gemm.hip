@@ -104,7 +104,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
     }
 }
 
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
 // ----------------------------------------------------------------------------- launchers
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(std::max(1, std::min((n + 255) / 256, 64))), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 
 static int g_pipe_grid_cap = 0;   // 0: no cap
 

@@ -185,10 +185,20 @@ __device__ __forceinline__ void gather_halves(uint32_t (&w)[4]) {
     w[3] = s13[1];
 }
 
+// Cache policy of a device-scope store (sc1): the encoding of an agent-scope
+// store on gfx950, complete only once it is coherent across the XCDs' L2s.
+constexpr int kCpolSc1 = 16;
+// Buffer resource word 3 of a raw (unformatted) gfx9 buffer.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // bf16 block store: the 16 values of acc (one 32 x 32 block, this lane's row)
 // as bf16 columns [col0, col0 + 32) of row `grow` of C (if the row is valid).
+// DEV: the two 16-byte stores go through the raw buffer resource `rc` over C
+// with device scope (byte offsets past its size are dropped by the hardware).
+template <bool DEV = false>
 __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_t ldc, int grow, bool valid,
-                                                 int col0, const float (&v)[16]) {
+                                                 int col0, const float (&v)[16],
+                                                 __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t()) {
     uint32_t lo[4], hi[4];   // run q: columns 8q + 4 half + (0, 1) and (2, 3)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -200,9 +210,15 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
     // half 0: columns 0..15 = runs (w0 = q0 lo/hi of half 0, w1 = q0 of half 1, ...)
     const int half = (threadIdx.x >> 5) & 1;
     if (valid) {
-        u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)grow * ldc + col0 + 16 * half);
-        dst[0] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
-        dst[1] = (u32x4){lo[2], hi[2], lo[3], hi[3]};
+        if constexpr (DEV) {
+            const uint32_t off = (uint32_t)((size_t)grow * ldc + col0 + 16 * half) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){lo[0], hi[0], lo[1], hi[1]}, rc, off, 0, kCpolSc1);
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4){lo[2], hi[2], lo[3], hi[3]}, rc, off + 16u, 0, kCpolSc1);
+        } else {
+            u32x4* dst = reinterpret_cast<u32x4*>(C + (size_t)grow * ldc + col0 + 16 * half);
+            dst[0] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
+            dst[1] = (u32x4){lo[2], hi[2], lo[3], hi[3]};
+        }
     }
 }
 
@@ -288,11 +304,14 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
 // values a stored recompute would hold) and, with dh [rows][N/2] (aux), C
 // receives da = dh b s (1 + a (1 - s)), db = dh a s, s = sigmoid(a), in the
 // layout of a | b.  The dh values of all of a wave's rows are requested
-// before any is used.
+// before any is used.  EPI 3: EPI 1 with device-scope stores through the raw
+// buffer resource rc over C (the fused FFN, whose GEMM2 tiles on other XCDs
+// read h while the kernel runs).
 template <class TL, int EPI>
 __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], uint16_t* __restrict__ C,
                                             int ldc, int N, const TileCoord& c, int wm, int wn,
-                                            u32x4* __restrict__ obuf, const uint16_t* __restrict__ aux) {
+                                            u32x4* __restrict__ obuf, const uint16_t* __restrict__ aux,
+                                            __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t()) {
     const int lane = threadIdx.x & 63;
     static_assert(EPI != 2 || TL::TN == 2, "one gate/up pair per wave row block");
     uint32_t dhw[EPI == 2 ? TL::TM : 1][4][2];   // dh runs: [mi][q] = 4 bf16 of h 8 q + 4 half + 0..3
@@ -348,7 +367,7 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
-                store_bf16_block(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v);
+                store_bf16_block<EPI == 3>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v, rc);
             }
         }
     }
@@ -503,6 +522,310 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
         c1 = c2;
         if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
         kbase += nk;
+    }
+    wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
+}
+
+// ============================================================================ fused bf16 FFN
+//
+// GEMM1 (h = silu(xe W_gate) * (xe W_up)) and GEMM2 (ye = h W_down) in one
+// persistent launch, so that no round of either GEMM runs on a partly idle
+// chip: with 256 workgroups and, say, 1040 tiles per GEMM, two separate
+// launches each end in a round of 16 tiles, while here the workgroups that
+// finish their GEMM1 share early go straight on to GEMM2 tiles.  The design
+// keeps the device-resident schedule of the pages' grouped GEMM (the group
+// sizes never reach the host) and removes the launch boundary between the two
+// projections.
+//
+// Tile ids: [0, T1) are GEMM1 tiles (M tile major, NT1 = 2H / BN per M tile),
+// [T1, T1 + T2) GEMM2 tiles (NT2 = d / BN per M tile).  Every tile is
+// computed whole, in the same K order and with the same epilogue as in the
+// separate kernels above, so the results are bitwise those of the two
+// launches, whatever the grid.
+//
+// Scheduling.  Workgroup b works for "XCD" x = b % 8 (the hardware deals
+// workgroups round-robin over the 8 XCDs).  The ids up to the last multiple
+// of 256 form blocks of 32 consecutive ids (4 M tiles x 8 N tiles, or 2 x 16),
+// and XCD x takes every 8th block from block x, so the tiles running together
+// on one XCD share rows and weight slices in its L2; the remaining ids (less
+// than one round) are dealt in blocks of 4 the same way, so that every XCD
+// gets the same number of tiles.  Within an XCD's sequence the tiles are handed out dynamically from
+// a counter (sync[x]): each workgroup holds two tiles ahead (the next one is
+// prefetched across the tile boundary; the one after is claimed at the end of
+// every tile and read back at the end of the next, by when it has long returned, so
+// the atomic's latency never stalls the K loop).  Placement only affects
+// speed: every ticket maps to one tile, whichever workgroup draws it.
+//
+// Dependencies.  A GEMM2 tile of M tile mt reads the h rows that the NT1
+// GEMM1 tiles of mt write.  GEMM1 stores h with device scope (sc1, the
+// encoding of an agent-scope store), so a store is coherent across the XCDs'
+// L2s once it is complete and no L2 write-back is needed; at the end of a
+// GEMM1 tile every wave waits for its stores, and after a barrier one lane
+// adds 1 to sync[8 + mt].  Before the cross-tile prefetch of a GEMM2 tile, wave
+// 0 copies sync[8 + mt] into LDS with a device-scope direct-to-LDS load issued
+// among the K-tile DMAs (so its completion is covered by the ring's own vmcnt
+// waits and every wave reads the same value after a barrier).  If the count is
+// complete the prefetch goes ahead; if not, the prefetch slots take a dummy
+// copy and, after the current tile's epilogue, the workgroup spins (bounded,
+// with s_sleep) until the count is complete, acquires, and restarts the
+// stream.  No workgroup can wait on itself (the dependency is only checked
+// for the next tile after the current one is finished), and a waiting
+// workgroup holds no unfinished GEMM1 tile (it draws ids in increasing order
+// and GEMM1 ids precede GEMM2 ids), so every wait ends once the GEMM1 tiles,
+// all held by running workgroups, are done; the spin bound ends it regardless.
+// The h rows of an M tile are read by nobody before its count is complete
+// (rows are clamped inside each tile), so no cache can hold a stale copy of
+// them when the prefetch path reads them.
+// sync layout (int32, zeroed before the launch): [0, 8) per-XCD tile
+// counters, [8, 8 + MTmax) finished GEMM1 tiles per M tile.
+constexpr int kFfnSyncHead = 8;
+
+struct FfnParams {
+    const uint16_t* xe;
+    const uint16_t* w1;
+    uint16_t* h;
+    const uint16_t* w2;
+    uint16_t* ye;
+    const int32_t* offsets;
+    int32_t* sync;
+    int R, E, d, H;
+    uint32_t spin_limit;
+};
+
+struct FfnTile {
+    int row0, rows, n0, e, mt, phase;   // phase 0: GEMM1, 1: GEMM2, -1: no tile
+};
+
+// Id of ticket q of XCD x: blocks of 32 ids over the first 256 k32 ids, then
+// blocks of 4; XCD x takes every 8th block.
+__device__ __forceinline__ int ffn_ticket_id(int x, int q, int k32) {
+    if (q < 32 * k32) return 256 * (q >> 5) + 32 * x + (q & 31);
+    const int r = q - 32 * k32;
+    return 256 * k32 + 32 * (r >> 2) + 4 * x + (r & 3);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ FfnTile ffn_tile(int id, int total, int T1, int NT1, int NT2, const int* s_tstart, int E,
+                                            const int32_t* __restrict__ offsets) {
+    FfnTile c{0, 1, 0, 0, 0, -1};
+    if (id >= total) return c;
+    const bool two = id >= T1;
+    const int j = two ? id - T1 : id, nt_per = two ? NT2 : NT1;
+    c.mt = j / nt_per;
+    c.phase = two ? 1 : 0;
+    c.e = __builtin_amdgcn_readfirstlane(tile_expert(s_tstart, E, c.mt));
+    const int o0 = offsets[c.e], o1 = offsets[c.e + 1];
+    c.row0 = o0 + (c.mt - __builtin_amdgcn_readfirstlane(s_tstart[c.e])) * BM;
+    c.rows = min(BM, o1 - c.row0);
+    c.n0 = (j - c.mt * nt_per) * BN;
+    return c;
+}
+
+// K-tile source of one loop phase (see StreamSrc): K-tile kt = rel * mul + add
+// of the tile's rows of A and its weight slice B (the expert's packed matrix).
+struct FfnSrc {
+    const uint16_t* a;
+    const uint16_t* b;
+    uint32_t rowbytes;
+    int row0, rows, n0, nmax, mul, add;
+};
+
+__device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, int mul, int add) {
+    FfnSrc s;
+    const bool one = t.phase != 1;
+    s.a = one ? p.xe : p.h;
+    s.b = one ? p.w1 + (size_t)t.e * (2 * p.H) * p.d : p.w2 + (size_t)t.e * p.d * p.H;
+    s.rowbytes = (uint32_t)(one ? p.d : p.H) * 2u;
+    s.nmax = one ? 2 * p.H : p.d;
+    s.row0 = t.row0;
+    s.rows = t.rows;
+    s.n0 = t.n0;
+    s.mul = mul;
+    s.add = add;
+    return s;
+}
+
+// 4 bytes per lane from base + voff into LDS dword [lds + 4 lane], device
+// scope (sc1): the load observes atomics performed by other XCDs.
+__device__ __forceinline__ void dma4_dev(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 sc1"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sgpr_ptr(base))
+                 : "memory", "m0");
+}
+
+template <class TL>
+__global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
+void gemm_bf16_ffn_kernel(FfnParams p) {
+    constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
+    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
+    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
+    static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
+    constexpr int kObufChunks = 128;   // per wave: 16 rows x 128 bytes of GEMM2 output
+    __shared__ u32x4 ring[TL::STAGES * SC];
+    __shared__ u32x4 obuf[TL::NW * kObufChunks];
+    __shared__ int s_tstart[kMaxExperts + 1];
+    __shared__ int s_scan[NTHR];
+    __shared__ int s_flag[64];
+    __shared__ int s_next;
+
+    const int MT = build_tile_schedule<BM, NTHR>(p.offsets, p.E, s_tstart, s_scan);
+    const int NT1 = (2 * p.H + BN - 1) / BN, NT2 = (p.d + BN - 1) / BN;
+    const int T1 = MT * NT1, total = T1 + MT * NT2;
+    const int nk1 = p.d / 32, nk2 = p.H / 32;
+    const int G = gridDim.x, GX = G / kXcds;   // G is a multiple of 8
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int k32 = total / 256;
+    const int id0 = ffn_ticket_id(xcd, slot, k32);
+    if (id0 >= total) return;
+    const int id1 = ffn_ticket_id(xcd, slot + GX, k32);
+
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ring_lds = lds_addr(ring);
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
+    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
+    const int arow = (wm * TL::WROWS + (lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 4;
+    const int a0 = arow + ((0 + half) ^ fsw), a1 = arow + ((2 + half) ^ fsw);
+    const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
+    const int drow = lane >> 2;
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    int32_t* const done = p.sync + kFfnSyncHead;
+    const __amdgpu_buffer_rsrc_t hrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(p.h, 0, (int)((uint32_t)p.R * (uint32_t)p.H * 2u), kRawBufferWord3);
+
+    // the ticket after the two static ones, claimed now and read back at the end of the first tile
+    int pending = total;
+    if (threadIdx.x == 0 && id1 < total)
+        pending = ffn_ticket_id(xcd, 2 * GX + __hip_atomic_fetch_add(p.sync + xcd, 1, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT), k32);
+
+    FfnTile c0 = ffn_tile<BM, BN>(id0, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
+    FfnTile c1 = ffn_tile<BM, BN>(id1, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
+    int kbase = 0;
+
+    auto dma = [&](const FfnSrc& src, int g, int i) {
+        const int kt = (g - kbase) * src.mul + src.add;
+        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        if (i < A_DMA) {
+            const int r = 16 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
+            dma16(src.a, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+        } else {
+            const int j = i - A_DMA;
+            const int r = 16 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
+            dma16(src.b, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+        }
+    };
+    auto frag = [&](const u32x4* stage, int aoff, int boff, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
+        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
+    };
+    // GEMM2 tile t may start once all NT1 GEMM1 tiles of its M tile are done
+    auto wait_rows = [&](const FfnTile& t) {
+        if (t.phase != 1) return;
+        uint32_t it = 0;
+        while (__hip_atomic_load(done + t.mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NT1 &&
+               ++it < p.spin_limit)
+            __builtin_amdgcn_s_sleep(8);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    };
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    // (re)start the K-tile stream at the first K-tile of tile t (global K-tile kbase)
+    auto start_stream = [&](const FfnTile& t) {
+        const FfnSrc here = ffn_src(p, t, 1, 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < P; ++i) dma(here, kbase + g, i);
+        wait_vm<3 * P>();   // the first K-tile landed; 1, 2 and 3 may stay in flight
+        ring_barrier();
+#pragma unroll
+        for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 3) * SC, a0, b0, i, fa0, fb0);
+    };
+
+    wait_rows(c0);
+    start_stream(c0);
+
+    auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
+        const u32x4* stage = ring + (g & 3) * SC;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa0, fb0, acc);
+            frag(stage, a1, b1, i, fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < EARLY; ++i) bf_mfma1<TL>(i, fa1, fb1, acc);
+        wait_vm<2 * P>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
+        wait_lds();         // this wave's reads of K-tile g are complete
+        ring_barrier();
+        const u32x4* nstage = ring + ((g + 1) & 3) * SC;
+#pragma unroll
+        for (int i = 0; i < NM - EARLY; ++i) {
+            bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
+            if (i < P) dma(src, g + 4, i);
+            frag(nstage, a0, b0, i, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    for (;;) {
+        f32x16 acc[TM][TN];
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+        const int nk = c0.phase == 0 ? nk1 : nk2;
+        const int head = nk - 4;
+        // The count of the next tile's M tile is copied into LDS before the
+        // DMAs of K-tile head + 1, so the vmcnt wait of K-tile head - 1 (which
+        // leaves only K-tiles head + 1 and head + 2 in flight) covers it.
+        const bool probe = c1.phase == 1 && head >= 4;
+        const int split = probe ? head - 3 : head;
+        const FfnSrc here = ffn_src(p, c0, 1, 0);
+        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, acc);
+        if (probe && wave == 0) dma4_dev(done, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
+        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, acc);
+        const int flag = __builtin_amdgcn_readfirstlane(s_flag[0]);
+        const bool go = c1.phase == 0 || (probe && flag >= NT1);
+        const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk) : ffn_src(p, c0, 0, nk - 1);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
+
+        const TileCoord tc{c0.row0, c0.rows, c0.n0, c0.e};
+        if (c0.phase == 0)
+            bf_epilogue<TL, 3>(acc, p.h, p.H, 2 * p.H, tc, wm, wn, obuf + wave * kObufChunks, nullptr, hrsrc);
+        else
+            bf_epilogue<TL, 0>(acc, p.ye, p.d, p.d, tc, wm, wn, obuf + wave * kObufChunks, nullptr);
+
+        // tile end: a GEMM1 tile's stores complete (h coherent at device
+        // scope), the ticket claimed one tile ago published, the finished GEMM1
+        // tile counted
+        if (c0.phase == 0) wait_vm<0>();
+        if (threadIdx.x == 0) s_next = pending;
+        wait_lds();
+        ring_barrier();
+        if (threadIdx.x == 0 && c0.phase == 0)
+            __hip_atomic_fetch_add(done + c0.mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int id2 = __builtin_amdgcn_readfirstlane(s_next);
+        if (threadIdx.x == 0 && id2 < total)
+            pending = ffn_ticket_id(xcd, 2 * GX + __hip_atomic_fetch_add(p.sync + xcd, 1, __ATOMIC_RELAXED,
+                                                                           __HIP_MEMORY_SCOPE_AGENT), k32);
+        if (c1.phase < 0) break;
+        kbase += nk;
+        c0 = c1;
+        c1 = ffn_tile<BM, BN>(id2, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
+        if (!go) {
+            // the next tile's first K-tiles were not prefetched: wait for its
+            // rows, let the dummy copies land, and restart the stream there
+            wait_rows(c0);
+            wait_vm<0>();
+            ring_barrier();
+            start_stream(c0);
+        }
     }
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
 }
@@ -1029,6 +1352,16 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
     if (epi == 1) return launch_bf16_pipe_tile<BfRing, 1>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
     if (epi == 2) return launch_bf16_pipe_tile<BfRing, 2>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
     return launch_bf16_pipe_tile<BfRing, 0>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
+}
+
+hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
+                           const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
+                           const int32_t* host_counts, hipStream_t s) {
+    using TL = BfRing;
+    const int grid = persistent_grid(R, E, 2 * H + d, TL::BM, TL::BN, 1, host_counts);
+    const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, kFfnSpinLimit};
+    hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL>), dim3(grid), dim3(TL::NTHR), 0, s, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,

@@ -40,9 +40,11 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
                              hipStream_t s);
 
 // counts, offsets and base[nblk][E] = offsets[e] + tokens of earlier blocks routed to e;
-// with psum non-NULL also the router statistics stats[E + 2] (see route.hip).
+// with psum non-NULL also the router statistics stats[E + 2] (see route.hip); zero[0, nzero)
+// := 0 on the side (the fused FFN's synchronisation words, so that no separate launch clears them).
 hipError_t launch_route_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
-                             int32_t* offsets, const float* psum, float* stats, int T, int k, hipStream_t s);
+                             int32_t* offsets, const float* psum, float* stats, int T, int k, hipStream_t s,
+                             int32_t* zero = nullptr, int nzero = 0);
 
 // pos[t][j] (holding the rank on entry) += base[t / kRouteBlock][idx]; row_token[pos] = t.
 hipError_t launch_route_finalize(const int32_t* topk_idx, const int32_t* base, int T, int E, int k,
@@ -84,6 +86,18 @@ int set_pipe_grid_cap(int cap);
 hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint16_t* C,
                             const int32_t* offsets, int R, int E, int N, int K, int ldc,
                             const int32_t* host_counts, hipStream_t s, const uint16_t* aux = nullptr);
+
+// Fused bf16 expert FFN (gemm_pipe.hip): GEMM1 with the SwiGLU epilogue into h and
+// GEMM2 into ye in one persistent launch (d and H at least 128).  sync holds
+// ffn_sync_ints(R, E) int32 that must be zero when the kernel starts; a GEMM2 tile
+// waits at most about kFfnSpinLimit sleeps for the GEMM1 tiles of its rows.
+constexpr uint32_t kFfnSpinLimit = 1u << 20;
+inline int ffn_sync_ints(int R, int E) { return 8 + R / 256 + E; }
+hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
+                           const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
+                           const int32_t* host_counts, hipStream_t s);
+// p[0, n) := 0 (a fill kernel, so that callers may capture it in a graph).
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 
 // Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K,
 // scales stored [K/128][rows][4] (A: R rows; B: per expert, N rows).

@@ -515,10 +515,12 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ offsets,
                                                           const float* __restrict__ psum,
-                                                          float* __restrict__ stats, int T, int k) {
+                                                          float* __restrict__ stats, int T, int k,
+                                                          int32_t* __restrict__ zero, int nzero) {
     __shared__ int32_t part[1024];
     __shared__ int32_t tot[1024];
     const int tid = threadIdx.x;
+    for (int i = tid; i < nzero; i += 1024) zero[i] = 0;
     const int NC = max(1, min(1024 / E, nblk));    // chunks per expert (E <= 1024), at most one block each when few
     const int CS = (nblk + NC - 1) / NC;           // blocks per chunk
     const int e = tid % E, c = tid / E;
@@ -610,9 +612,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 }
 
 hipError_t launch_route_scan(const int32_t* hist, int nblk, int E, int32_t* base, int32_t* counts,
-                             int32_t* offsets, const float* psum, float* stats, int T, int k, hipStream_t s) {
+                             int32_t* offsets, const float* psum, float* stats, int T, int k, hipStream_t s,
+                             int32_t* zero, int nzero) {
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nblk, E, base, counts,
-                       offsets, psum, stats, T, k);
+                       offsets, psum, stats, T, k, zero, nzero);
     return hipGetLastError();
 }
 

@@ -432,3 +432,45 @@ def test_grid_cap_bitwise_and_oracle(case, w, cap, grid_cap):
     wg, wu, wd = oracle_weights(host)
     ref = O.forward(W.as_f64(host["x"]), w.E, w.k, w.act, wg, wu, wd, logits=L)
     check_y(w.act, _f64(out["y"]), ref["y"])
+
+
+# ----------------------------------------------------------------------------- fused bf16 FFN counters
+
+@pytest.mark.parametrize("cap", [0, 8], ids=["full_grid", "cap8"])
+def test_fused_ffn_counters_reset_between_calls(cap, grid_cap):
+    """The bf16 expert FFN runs GEMM1 and GEMM2 in one launch whose GEMM2 tiles
+    wait on per-M-tile counters in the workspace.  Two calls through the same
+    workspace with different inputs and routing must each give the result of a
+    fresh workspace: stale counters from the first call would let GEMM2 read
+    the first call's h."""
+    wa = W.Workload("ffn_a", T=1500, d=512, E=8, k=2, H=384, act="bf16", router="random", seed=3201)
+    wb = W.Workload("ffn_b", T=1500, d=512, E=8, k=2, H=384, act="bf16", router="zipf", seed=3202)
+    print(f"[fused ffn] cap={cap} {wa.describe()} then {wb.describe()}", flush=True)
+    grid_cap(cap)
+    ha, da = device_inputs(wa)
+    hb, db = device_inputs(wb)
+    p = problem_of(wa)
+    packed = B.pack_weights(p, da["w_gate"], da["w_up"], da["w_down"])
+    f = B.Forward(p, DEV)
+    f(da["x"], packed=packed, logits=da["logits"])
+    f(db["x"], packed=packed, logits=db["logits"])
+    torch.cuda.synchronize()
+    y_reused = f.y.clone()
+    fresh = B.Forward(p, DEV)
+    fresh(db["x"], packed=packed, logits=db["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(y_reused, fresh.y), "second call through a reused workspace differs"
+    wg, wu, wd = oracle_weights(ha)
+    ref = O.forward(W.as_f64(hb["x"]), wb.E, wb.k, wb.act, wg, wu, wd, logits=W.as_f64(hb["logits"]))
+    check_y(wb.act, _f64(y_reused), ref["y"])
+    # the standalone grouped FFN entry point, twice through one workspace
+    ws = B.new_workspace(p, DEV)
+    ra = B.route(p, logits=da["logits"], ws=ws)
+    rb = B.route(p, logits=db["logits"], ws=ws)
+    xe_a, _ = B.dispatch(p, da["x"], ra["pos"])
+    xe_b, _ = B.dispatch(p, db["x"], rb["pos"])
+    B.grouped_swiglu(p, xe_a, None, packed, ra["offsets"], ws=ws)
+    ye_b = B.grouped_swiglu(p, xe_b, None, packed, rb["offsets"], ws=ws)
+    ye_fresh = B.grouped_swiglu(p, xe_b, None, packed, rb["offsets"])
+    torch.cuda.synchronize()
+    assert torch.equal(ye_b, ye_fresh), "grouped_swiglu through a reused workspace differs"
