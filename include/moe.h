@@ -244,6 +244,15 @@ int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* 
  * value. */
 int32_t moe_set_gemm_grid_cap(int32_t cap);
 
+/* Test hook for the fused bfloat16 expert FFN (see moe_grouped_swiglu):
+ * MOE_TEST_FFN_WAIT makes every GEMM2 tile skip the early check of its rows
+ * and start only after waiting for them (the path a tile takes when its rows
+ * are not yet done), so tests can show that this path gives the same result.
+ * Outputs are unchanged; only speed drops.  Process-wide, applies to calls
+ * launched afterwards; 0 clears it.  Returns MOE_ERR_ARG for unknown bits. */
+#define MOE_TEST_FFN_WAIT 1
+int32_t moe_set_test_flags(int32_t flags);
+
 /* ---------------------------------------------------------------- backward
  *
  * Gradients of the block for a loss L with dL/dy = dy (MOE_IDENTITY_EXPERTS

@@ -26,7 +26,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packe
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
            "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times",
            "moe_set_gemm_grid_cap", "moe_backward_workspace_bytes", "moe_backward_weight_bytes",
-           "moe_pack_weights_backward", "moe_backward"]
+           "moe_pack_weights_backward", "moe_backward", "moe_set_test_flags"]
 
 
 class MoeError(RuntimeError):
@@ -80,6 +80,7 @@ def lib():
         L.moe_forward_host_sync.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]
         L.moe_set_profiling.argtypes = [_I32]
         L.moe_set_gemm_grid_cap.argtypes = [_I32]
+        L.moe_set_test_flags.argtypes = [_I32]
         L.moe_backward_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_backward_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_pack_weights_backward.argtypes = [PP, _P, _P, _P, _P, _P]
@@ -353,6 +354,15 @@ class Backward:
 def set_gemm_grid_cap(cap: int):
     """Cap the grouped GEMMs' persistent grid at `cap` workgroups (multiple of 8, <= 256; 0 = no cap)."""
     _check("moe_set_gemm_grid_cap", lib().moe_set_gemm_grid_cap(int(cap)))
+
+
+MOE_TEST_FFN_WAIT = 1
+
+
+def set_test_flags(flags: int):
+    """Test hook (MOE_TEST_FFN_WAIT: every GEMM2 tile of the fused bf16 FFN waits for its rows
+    before starting, the path taken when they are not yet done); 0 clears it."""
+    _check("moe_set_test_flags", lib().moe_set_test_flags(int(flags)))
 
 
 def kernel_times() -> list[tuple[str, float]]:

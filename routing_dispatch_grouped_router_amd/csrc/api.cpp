@@ -462,6 +462,12 @@ int32_t moe_set_gemm_grid_cap(int32_t cap) {
     return set_pipe_grid_cap(cap) ? MOE_ERR_ARG : MOE_OK;
 }
 
+int32_t moe_set_test_flags(int32_t flags) {
+    if (flags & ~MOE_TEST_FFN_WAIT) return MOE_ERR_ARG;
+    set_ffn_force_wait(flags & MOE_TEST_FFN_WAIT);
+    return MOE_OK;
+}
+
 int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* n) {
     if (!n) return MOE_ERR_NULL;
     if (g_prof.calls == 0) return MOE_ERR_STATE;

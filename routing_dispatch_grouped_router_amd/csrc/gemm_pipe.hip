@@ -590,6 +590,7 @@ struct FfnParams {
     int32_t* sync;
     int R, E, d, H;
     uint32_t spin_limit;
+    int force_wait;   // test hook: treat every GEMM2 tile's rows as not yet done at the early check
 };
 
 struct FfnTile {
@@ -791,7 +792,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         if (probe && wave == 0) dma4_dev(done, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
         for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, acc);
         const int flag = __builtin_amdgcn_readfirstlane(s_flag[0]);
-        const bool go = c1.phase == 0 || (probe && flag >= NT1);
+        const bool go = c1.phase == 0 || (probe && flag >= NT1 && !p.force_wait);
         const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk) : ffn_src(p, c0, 0, nk - 1);
         for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
 
@@ -1354,12 +1355,16 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
     return launch_bf16_pipe_tile<BfRing, 0>(A, Bw, C, offsets, R, E, N, K, ldc, host_counts, aux, s);
 }
 
+static int g_ffn_force_wait = 0;
+
+void set_ffn_force_wait(int on) { g_ffn_force_wait = on ? 1 : 0; }
+
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
                            const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
                            const int32_t* host_counts, hipStream_t s) {
     using TL = BfRing;
     const int grid = persistent_grid(R, E, 2 * H + d, TL::BM, TL::BN, 1, host_counts);
-    const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, kFfnSpinLimit};
+    const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, kFfnSpinLimit, g_ffn_force_wait};
     hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL>), dim3(grid), dim3(TL::NTHR), 0, s, p);
     return hipGetLastError();
 }

@@ -96,6 +96,8 @@ inline int ffn_sync_ints(int R, int E) { return 8 + R / 256 + E; }
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
                            const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
                            const int32_t* host_counts, hipStream_t s);
+// Test hook: nonzero makes every GEMM2 tile of the fused FFN take the wait-and-restart path.
+void set_ffn_force_wait(int on);
 // p[0, n) := 0 (a fill kernel, so that callers may capture it in a graph).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 

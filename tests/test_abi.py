@@ -113,6 +113,12 @@ def test_gemm_grid_cap_range(lib, cap, code):
     assert lib.moe_set_gemm_grid_cap(0) == 0
 
 
+@pytest.mark.parametrize("flags,code", [(0, 0), (1, 0), (2, -7), (-1, -7)])
+def test_test_flags_range(lib, flags, code):
+    assert lib.moe_set_test_flags(flags) == code
+    assert lib.moe_set_test_flags(0) == 0
+
+
 def test_kernel_times_without_profiled_forward(lib):
     n = ctypes.c_int32()
     assert lib.moe_set_profiling(0) == 0

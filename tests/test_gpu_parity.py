@@ -474,3 +474,41 @@ def test_fused_ffn_counters_reset_between_calls(cap, grid_cap):
     ye_fresh = B.grouped_swiglu(p, xe_b, None, packed, rb["offsets"])
     torch.cuda.synchronize()
     assert torch.equal(ye_b, ye_fresh), "grouped_swiglu through a reused workspace differs"
+
+
+@pytest.fixture
+def ffn_wait_flag():
+    yield B.set_test_flags
+    B.set_test_flags(0)
+
+
+FFN_WAIT_CASES = [
+    ("e8_full", W.Workload("ffnw_e8", T=1500, d=512, E=8, k=2, H=384, act="bf16", router="random", seed=3301), 0),
+    ("e8_cap8", W.Workload("ffnw_e8c", T=1500, d=512, E=8, k=2, H=384, act="bf16", router="random", seed=3302), 8),
+    ("sparse_cap16", W.Workload("ffnw_sp", T=1000, d=768, E=64, k=2, H=256, act="bf16", router="random", seed=3303,
+                                empty_experts=tuple(range(8, 64))), 16),
+    ("zipf_full", W.Workload("ffnw_zipf", T=2048, d=1024, E=16, k=4, H=512, act="bf16", router="zipf",
+                             seed=3304), 0),
+]
+
+
+@pytest.mark.parametrize("case,w,cap", FFN_WAIT_CASES, ids=[c[0] for c in FFN_WAIT_CASES])
+def test_fused_ffn_wait_path(case, w, cap, grid_cap, ffn_wait_flag):
+    """Every GEMM2 tile of the fused FFN forced through the wait-and-restart
+    path (the one taken when its rows are not yet done at the early check)
+    gives bitwise the output of the normal path, and the oracle's."""
+    print(f"[fused ffn wait path] {case} cap={cap} {w.describe()}", flush=True)
+    grid_cap(cap)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    normal = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    y0 = normal["y"].clone()
+    ffn_wait_flag(B.MOE_TEST_FFN_WAIT)
+    waited = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(waited["y"], y0), "wait-and-restart path changed y"
+    wg, wu, wd = oracle_weights(host)
+    ref = O.forward(W.as_f64(host["x"]), w.E, w.k, w.act, wg, wu, wd, logits=W.as_f64(host["logits"]))
+    check_y(w.act, _f64(waited["y"]), ref["y"])
