@@ -85,12 +85,18 @@ Packed packed_layout(const moe_problem& p) {
 // per-tile partials of dW_r; for MXFP8 blocks the dequantised xe [R][d] and h
 // [R][H] (bfloat16).
 struct BwdLayout {
-    size_t ab, dye, dh, dsel, wrt, srow, rpart, xe16, h16, total;
+    size_t ab, dye, dh, dsel, wrt, srow, rpart, xe16, h16, sync, total;
 };
 
 // The backward runs in the activation type, bfloat16 for MXFP8 blocks (their
 // saved activations are dequantised first).
 int bwd_act(int act) { return act == MOE_MXFP8 ? MOE_BF16 : act; }
+
+// bf16 backward data-gradient GEMMs (dh, da | db, dxe) as one fused launch when
+// every phase has at least four 32-wide K-tiles
+bool use_bwd_chain(const moe_problem& p) {
+    return bwd_act(p.act_dtype) == MOE_BF16 && p.d_model >= 128 && p.d_hidden >= 128;
+}
 
 BwdLayout bwd_layout(const moe_problem& p) {
     BwdLayout B{};
@@ -109,6 +115,7 @@ BwdLayout bwd_layout(const moe_problem& p) {
     const bool mx = p.act_dtype == MOE_MXFP8;
     B.xe16 = take(mx ? R * d * 2 : 0);
     B.h16 = take(mx ? R * H * 2 : 0);
+    B.sync = take(use_bwd_chain(p) ? (size_t)fused_sync_ints((int)R, p.n_experts, 3) * 4 : 0);
     B.total = off;
     return B;
 }
@@ -586,15 +593,30 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     if ((st = launched(launch_combine_bwd(act, dy, ye, gate, ps, idx, dye, dlogits, dsel, srow, T, d, E, k, s))))
         return st;
     const bool bf = act == MOE_BF16;
+    const bool chain = use_bwd_chain(*p);
     if (bf) {
-        // dh = dye W_down^T, then the gate/up recompute with the SwiGLU backward
-        // in its epilogue: da | db straight into ab
-        if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
-        if ((st = launched(launch_gemm_dswiglu(xe, w1, dh, ab, off, R, E, d, H, s)))) return st;
-        // weight gradients: dW_down = h^T dye, dW_gate | dW_up = xe^T (da | db) per expert
+        // dW_down = h^T dye per expert (before dxe overwrites dye)
         if ((st = launched(launch_wgrad_rows(0, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(dye), off,
                                              E, H, d, dw_down, nullptr, s))))
             return st;
+        if (chain) {
+            // dh = dye W_down^T, da | db from the gate/up recompute and dh, and
+            // dxe = (da | db) W1^T (into dye) in one launch
+            int32_t* sync = reinterpret_cast<int32_t*>(at(ws, BL.sync));
+            if ((st = launched(launch_zero_i32(sync, fused_sync_ints(R, E, 3), s)))) return st;
+            if ((st = launched(launch_bf16_bwd_chain(
+                     static_cast<const uint16_t*>(dye), reinterpret_cast<const uint16_t*>(pb + BP.wd),
+                     static_cast<uint16_t*>(dh), static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
+                     static_cast<uint16_t*>(ab), reinterpret_cast<const uint16_t*>(pb + BP.w1t),
+                     static_cast<uint16_t*>(dye), off, sync, R, E, d, H, s))))
+                return st;
+        } else {
+            // dh = dye W_down^T, then the gate/up recompute with the SwiGLU
+            // backward in its epilogue: da | db straight into ab
+            if ((st = launched(launch_gemm_plain(act, dye, pb + BP.wd, dh, off, R, E, H, d, H, s)))) return st;
+            if ((st = launched(launch_gemm_dswiglu(xe, w1, dh, ab, off, R, E, d, H, s)))) return st;
+        }
+        // dW_gate | dW_up = xe^T (da | db) per expert
         if ((st = launched(launch_wgrad_rows(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(ab), off,
                                              E, d, 2 * H, dw_gate, dw_up, s))))
             return st;
@@ -605,7 +627,8 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
         if ((st = launched(launch_swiglu_bwd(act, dh, ab, R, H, s)))) return st;   // da | db over a | b in place
         if ((st = launched(launch_wgrad_w1(act, xe, ab, off, E, R, d, H, dw_gate, dw_up, s)))) return st;
     }
-    if ((st = launched(launch_gemm_plain(act, ab, pb + BP.w1t, dye, off, R, E, d, 2 * H, d, s)))) return st;
+    if (!(bf && chain) && (st = launched(launch_gemm_plain(act, ab, pb + BP.w1t, dye, off, R, E, d, 2 * H, d, s))))
+        return st;
     void* wrt = given ? nullptr : at(ws, BL.wrt);
     if (!given && (st = launched(launch_router_transpose(act, w_router, d, E, wrt, s)))) return st;
     if ((st = launched(launch_dx(act, dye, ps, idx, dsel, wrt, dx, T, d, E, k, s)))) return st;

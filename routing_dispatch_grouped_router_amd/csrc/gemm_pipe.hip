@@ -233,11 +233,13 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
 // sits at q * 8 + (c ^ (q & 7)) to spread the writes over the LDS banks.
 // The buffer is private to the wave, so a wait for the wave's own LDS writes
 // (and compiler barriers: lanes read what other lanes wrote) stand in for a
-// workgroup barrier.
-template <int RR>
+// workgroup barrier.  DEV: the 16-byte stores go through the raw buffer
+// resource `rc` over C with device scope (see store_bf16_block).
+template <int RR, bool DEV = false>
 __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, size_t ldc, int row0, int nrows,
                                                      int pc, int N, const float (&g)[16], const float (&u)[16],
-                                                     u32x4* __restrict__ buf) {
+                                                     u32x4* __restrict__ buf,
+                                                     __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t()) {
     static_assert(RR == 16 || RR == 32, "rows per round");
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, half = lane >> 5;
@@ -287,8 +289,13 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
 #pragma unroll
         for (int j = 0; j < RR / 8; ++j) {
             const int rr = rho * RR + 8 * j + (lane >> 3);
-            if (rr < nrows && col_ok)
-                *reinterpret_cast<u32x4*>(C + (size_t)(row0 + rr) * ldc + pc + 8 * c) = o[j];
+            if (rr < nrows && col_ok) {
+                if constexpr (DEV)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        o[j], rc, (uint32_t)((size_t)(row0 + rr) * ldc + pc + 8 * c) * 2u, 0, kCpolSc1);
+                else
+                    *reinterpret_cast<u32x4*>(C + (size_t)(row0 + rr) * ldc + pc + 8 * c) = o[j];
+            }
         }
     }
 }
@@ -304,10 +311,10 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
 // values a stored recompute would hold) and, with dh [rows][N/2] (aux), C
 // receives da = dh b s (1 + a (1 - s)), db = dh a s, s = sigmoid(a), in the
 // layout of a | b.  The dh values of all of a wave's rows are requested
-// before any is used.  EPI 3: EPI 1 with device-scope stores through the raw
-// buffer resource rc over C (the fused FFN, whose GEMM2 tiles on other XCDs
-// read h while the kernel runs).
-template <class TL, int EPI>
+// before any is used.  DEV: every store goes through the raw buffer resource
+// rc over C with device scope (the fused grouped GEMMs, whose next phase reads
+// C on other XCDs while the kernel runs).
+template <class TL, int EPI, bool DEV = false>
 __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], uint16_t* __restrict__ C,
                                             int ldc, int N, const TileCoord& c, int wm, int wn,
                                             u32x4* __restrict__ obuf, const uint16_t* __restrict__ aux,
@@ -346,7 +353,8 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
                 u[i] = d * (a * sg);
             }
             const int rb = wm * TL::WROWS + mi * 32;
-            store_bf16_pair_rows<16>(C, (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS, N, g, u, obuf);
+            store_bf16_pair_rows<16, DEV>(C, (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS, N, g, u,
+                                          obuf, rc);
         } else if (EPI == 0) {
 #pragma unroll
             for (int np = 0; np < TL::TN / 2; ++np) {
@@ -357,8 +365,8 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
                     u[i] = acc[mi][2 * np + 1][i];
                 }
                 const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
-                store_bf16_pair_rows<16>(C, (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS + np * 64,
-                                         N, g, u, obuf);
+                store_bf16_pair_rows<16, DEV>(C, (size_t)ldc, c.row0 + rb, c.rows - rb,
+                                              c.n0 + wn * TL::WCOLS + np * 64, N, g, u, obuf, rc);
             }
         } else {
 #pragma unroll
@@ -367,7 +375,7 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
-                store_bf16_block<EPI == 3>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v, rc);
+                store_bf16_block<DEV>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v, rc);
             }
         }
     }
@@ -526,22 +534,25 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
 }
 
-// ============================================================================ fused bf16 FFN
+// ============================================================================ fused bf16 grouped GEMMs
 //
-// GEMM1 (h = silu(xe W_gate) * (xe W_up)) and GEMM2 (ye = h W_down) in one
-// persistent launch, so that no round of either GEMM runs on a partly idle
-// chip: with 256 workgroups and, say, 1040 tiles per GEMM, two separate
-// launches each end in a round of 16 tiles, while here the workgroups that
-// finish their GEMM1 share early go straight on to GEMM2 tiles.  The design
-// keeps the device-resident schedule of the pages' grouped GEMM (the group
-// sizes never reach the host) and removes the launch boundary between the two
-// projections.
+// Up to three grouped GEMMs over the same expert segments in one persistent
+// launch, each phase's M tile depending on the previous phase's tiles of the
+// same rows:
+//   forward:  GEMM1 (h = silu(xe W_gate) * (xe W_up)), then GEMM2 (ye = h W_down);
+//   backward: dh = dye W_down^T, then the gate/up recompute with the SwiGLU
+//             backward in its epilogue (da | db, reading dh), then dxe = (da | db) W1^T.
+// So no phase ends in a round of tiles on a partly idle chip: with 256
+// workgroups and, say, 1040 tiles per GEMM, separate launches each end in a
+// round of 16 tiles, while here the workgroups that finish their share of one
+// phase go straight on to the next.  The schedule stays device-resident (the
+// group sizes never reach the host) and the launch boundaries between the
+// projections disappear.
 //
-// Tile ids: [0, T1) are GEMM1 tiles (M tile major, NT1 = 2H / BN per M tile),
-// [T1, T1 + T2) GEMM2 tiles (NT2 = d / BN per M tile).  Every tile is
-// computed whole, in the same K order and with the same epilogue as in the
-// separate kernels above, so the results are bitwise those of the two
-// launches, whatever the grid.
+// Tile ids: phase 0 takes [0, T0), phase 1 [T0, T0 + T1), ... (M tile major,
+// NTp = Np / BN tiles per M tile).  Every tile is computed whole, in the same K
+// order and with the same epilogue as by gemm_bf16_pipe_kernel, so the results
+// are bitwise those of separate launches, whatever the grid.
 //
 // Scheduling.  Workgroup b works for "XCD" x = b % 8 (the hardware deals
 // workgroups round-robin over the 8 XCDs).  The ids up to the last multiple
@@ -549,37 +560,353 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 // and XCD x takes every 8th block from block x, so the tiles running together
 // on one XCD share rows and weight slices in its L2; the remaining ids (less
 // than one round) are dealt in blocks of 4 the same way, so that every XCD
-// gets the same number of tiles.  Within an XCD's sequence the tiles are handed out dynamically from
-// a counter (sync[x]): each workgroup holds two tiles ahead (the next one is
-// prefetched across the tile boundary; the one after is claimed at the end of
-// every tile and read back at the end of the next, by when it has long returned, so
-// the atomic's latency never stalls the K loop).  Placement only affects
-// speed: every ticket maps to one tile, whichever workgroup draws it.
+// gets the same number of tiles.  Within an XCD's sequence the tiles are handed
+// out dynamically from a counter (sync[x]): each workgroup holds two tiles
+// ahead (the next one is prefetched across the tile boundary; the one after is
+// claimed at the end of every tile and read back at the end of the next, by
+// when it has long returned, so the atomic's latency never stalls the K loop).
+// Placement only affects speed: every ticket maps to one tile, whichever
+// workgroup draws it.
 //
-// Dependencies.  A GEMM2 tile of M tile mt reads the h rows that the NT1
-// GEMM1 tiles of mt write.  GEMM1 stores h with device scope (sc1, the
-// encoding of an agent-scope store), so a store is coherent across the XCDs'
-// L2s once it is complete and no L2 write-back is needed; at the end of a
-// GEMM1 tile every wave waits for its stores, and after a barrier one lane
-// adds 1 to sync[8 + mt].  Before the cross-tile prefetch of a GEMM2 tile, wave
-// 0 copies sync[8 + mt] into LDS with a device-scope direct-to-LDS load issued
-// among the K-tile DMAs (so its completion is covered by the ring's own vmcnt
-// waits and every wave reads the same value after a barrier).  If the count is
-// complete the prefetch goes ahead; if not, the prefetch slots take a dummy
-// copy and, after the current tile's epilogue, the workgroup spins (bounded,
-// with s_sleep) until the count is complete, acquires, and restarts the
-// stream.  No workgroup can wait on itself (the dependency is only checked
-// for the next tile after the current one is finished), and a waiting
-// workgroup holds no unfinished GEMM1 tile (it draws ids in increasing order
-// and GEMM1 ids precede GEMM2 ids), so every wait ends once the GEMM1 tiles,
-// all held by running workgroups, are done; the spin bound ends it regardless.
-// The h rows of an M tile are read by nobody before its count is complete
-// (rows are clamped inside each tile), so no cache can hold a stale copy of
-// them when the prefetch path reads them.
+// Dependencies.  A tile of phase p > 0 and M tile mt reads rows that the NT
+// tiles of phase p - 1 and M tile mt write.  Those tiles store with device
+// scope (sc1, the encoding of an agent-scope store on gfx950), so a store is
+// coherent across the XCDs' L2s once it is complete and no L2 write-back is
+// needed; at the end of such a tile every wave waits for its stores, and after
+// a barrier one lane adds 1 to the phase's counter of mt.  Before the
+// cross-tile prefetch of a dependent tile, wave 0 copies the counter into LDS
+// with a device-scope direct-to-LDS load issued among the K-tile DMAs (so its
+// completion is covered by the ring's own vmcnt waits and every wave reads the
+// same value after a barrier).  If the count is complete the prefetch goes
+// ahead; if not, the prefetch slots take a dummy copy and, after the current
+// tile's epilogue, the workgroup spins (bounded, with s_sleep) until the count
+// is complete, acquires, and restarts the stream.  No workgroup can wait on
+// itself (the dependency is only checked for the next tile after the current
+// one is finished), and a waiting workgroup holds no unfinished tile of an
+// earlier phase (it draws ids in increasing order and earlier phases' ids come
+// first), so every wait ends once the earlier tiles, all held by running
+// workgroups, are done; the spin bound ends it regardless.  The rows an M tile
+// of one phase writes are read by nobody before its count is complete (rows
+// are clamped inside each tile), so no cache can hold a stale copy of them.
 // sync layout (int32, zeroed before the launch): [0, 8) per-XCD tile
-// counters, [8, 8 + MTmax) finished GEMM1 tiles per M tile.
+// counters, then one array of MTmax counters per phase that others wait on.
 constexpr int kFfnSyncHead = 8;
+constexpr int kFusedMaxPhases = 3;
 
+// Epilogue kinds of a fused phase.
+enum FusedEpi : int {
+    kEpiPlain = 0,     // C = A B (bf16)
+    kEpiSwiglu = 1,    // C = silu(A Bgate) * (A Bup)
+    kEpiDswiglu = 2,   // C = SwiGLU backward of (A Bgate, A Bup) given dh = aux
+};
+
+// An instantiation compiles the epilogues of the (kind, device scope) pairs in
+// its KINDS mask only, bit 2 epi + dev, so the forward's kernel does not carry
+// the SwiGLU backward's registers.
+constexpr int fused_kind_bit(int epi, int dev) { return 1 << (2 * epi + dev); }
+constexpr int kFusedBackwardKinds =
+    fused_kind_bit(kEpiPlain, 1) | fused_kind_bit(kEpiDswiglu, 1) | fused_kind_bit(kEpiPlain, 0);
+
+struct FusedPhase {
+    const uint16_t* a;      // A rows [R][K]
+    const uint16_t* b;      // B [E][N][K]
+    uint16_t* c;            // C [R][ldc]
+    const uint16_t* aux;    // kEpiDswiglu: dh [R][N/2]
+    int32_t* done;          // counters raised per finished tile (NULL: none)
+    const int32_t* need;    // counters of the previous phase waited on (NULL: none)
+    int N, K, ldc, epi;
+    int need_count;         // tiles of the previous phase per M tile
+    int dev;                // stores with device scope (a later phase reads C)
+};
+
+struct FusedParams {
+    FusedPhase ph[kFusedMaxPhases];
+    int nph;
+    const int32_t* offsets;
+    int32_t* sync;
+    int R, E;
+    uint32_t spin_limit;
+    int force_wait;   // test hook: treat every dependent tile's rows as not yet done at the early check
+};
+
+struct FfnTile {
+    int row0, rows, n0, e, mt, phase;   // phase -1: no tile
+};
+
+// Id of ticket q of XCD x: blocks of 32 ids over the first 256 k32 ids, then
+// blocks of 4; XCD x takes every 8th block.
+__device__ __forceinline__ int ffn_ticket_id(int x, int q, int k32) {
+    if (q < 32 * k32) return 256 * (q >> 5) + 32 * x + (q & 31);
+    const int r = q - 32 * k32;
+    return 256 * k32 + 32 * (r >> 2) + 4 * x + (r & 3);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ FfnTile ffn_tile(const FusedParams& p, int id, int MT, const int* s_tstart) {
+    FfnTile c{0, 1, 0, 0, 0, -1};
+    int j = id;
+    for (int q = 0; q < p.nph; ++q) {
+        const int nt_per = (p.ph[q].N + BN - 1) / BN;
+        if (j < MT * nt_per) {
+            c.phase = q;
+            c.mt = j / nt_per;
+            c.n0 = (j - c.mt * nt_per) * BN;
+            break;
+        }
+        j -= MT * nt_per;
+    }
+    if (c.phase < 0) return c;
+    // everything below is wave-uniform; saying so keeps it in SGPRs (and the
+    // buffer resources built from it out of waterfall loops)
+    c.phase = __builtin_amdgcn_readfirstlane(c.phase);
+    c.mt = __builtin_amdgcn_readfirstlane(c.mt);
+    c.n0 = __builtin_amdgcn_readfirstlane(c.n0);
+    c.e = __builtin_amdgcn_readfirstlane(tile_expert(s_tstart, p.E, c.mt));
+    const int o0 = p.offsets[c.e], o1 = p.offsets[c.e + 1];
+    c.row0 = o0 + (c.mt - __builtin_amdgcn_readfirstlane(s_tstart[c.e])) * BM;
+    c.rows = min(BM, o1 - c.row0);
+    return c;
+}
+
+// K-tile source of one loop phase (see StreamSrc): K-tile kt = rel * mul + add
+// of the tile's rows of A and its weight slice B (the expert's packed matrix).
+struct FfnSrc {
+    const uint16_t* a;
+    const uint16_t* b;
+    uint32_t rowbytes;
+    int row0, rows, n0, nmax, mul, add;
+};
+
+// Built once per loop phase and wave-uniform throughout (pinned to SGPRs, so
+// the K loop does not re-derive the DMA bases from the phase table).
+__device__ __forceinline__ FfnSrc ffn_src(const FusedParams& p, const FfnTile& t, int mul, int add) {
+    const FusedPhase& q = p.ph[t.phase];
+    const int N = __builtin_amdgcn_readfirstlane(q.N), K = __builtin_amdgcn_readfirstlane(q.K);
+    FfnSrc s;
+    s.a = static_cast<const uint16_t*>(sgpr_ptr(q.a));
+    s.b = static_cast<const uint16_t*>(sgpr_ptr(q.b + (size_t)t.e * N * K));
+    s.rowbytes = (uint32_t)K * 2u;
+    s.nmax = N;
+    s.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    s.rows = __builtin_amdgcn_readfirstlane(t.rows);
+    s.n0 = t.n0;
+    s.mul = mul;
+    s.add = __builtin_amdgcn_readfirstlane(add);
+    return s;
+}
+
+// 4 bytes per lane from base + voff into LDS dword [lds + 4 lane], device
+// scope (sc1): the load observes atomics performed by other XCDs.
+__device__ __forceinline__ void dma4_dev(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 sc1"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sgpr_ptr(base))
+                 : "memory", "m0");
+}
+
+template <class TL, int KINDS>
+__global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
+void gemm_bf16_fused_kernel(FusedParams p) {
+    constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
+    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
+    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
+    static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
+    constexpr int kObufChunks = 128;   // per wave: 16 rows x 128 bytes of row-contiguous output
+    __shared__ u32x4 ring[TL::STAGES * SC];
+    __shared__ u32x4 obuf[TL::NW * kObufChunks];
+    __shared__ int s_tstart[kMaxExperts + 1];
+    __shared__ int s_scan[NTHR];
+    __shared__ int s_flag[64];
+    __shared__ int s_next;
+
+    const int MT = __builtin_amdgcn_readfirstlane(build_tile_schedule<BM, NTHR>(p.offsets, p.E, s_tstart, s_scan));
+    int total = 0;
+    for (int q = 0; q < p.nph; ++q) total += MT * ((p.ph[q].N + BN - 1) / BN);
+    const int G = gridDim.x, GX = G / kXcds;   // G is a multiple of 8
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int k32 = total / 256;
+    const int id0 = ffn_ticket_id(xcd, slot, k32);
+    if (id0 >= total) return;
+    const int id1 = ffn_ticket_id(xcd, slot + GX, k32);
+
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t ring_lds = lds_addr(ring);
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
+    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
+    const int arow = (wm * TL::WROWS + (lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 4;
+    const int a0 = arow + ((0 + half) ^ fsw), a1 = arow + ((2 + half) ^ fsw);
+    const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
+    const int drow = lane >> 2;
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+
+    // the ticket after the two static ones, claimed now and read back at the end of the first tile
+    int pending = total;
+    if (threadIdx.x == 0 && id1 < total)
+        pending = ffn_ticket_id(xcd, 2 * GX + __hip_atomic_fetch_add(p.sync + xcd, 1, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT), k32);
+
+    FfnTile c0 = ffn_tile<BM, BN>(p, id0, MT, s_tstart);
+    FfnTile c1 = ffn_tile<BM, BN>(p, id1, MT, s_tstart);
+    int kbase = 0;
+
+    auto dma = [&](const FfnSrc& src, int g, int i) {
+        const int kt = (g - kbase) * src.mul + src.add;
+        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        if (i < A_DMA) {
+            const int r = 16 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
+            dma16(src.a, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+        } else {
+            const int j = i - A_DMA;
+            const int r = 16 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
+            dma16(src.b, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+        }
+    };
+    auto frag = [&](const u32x4* stage, int aoff, int boff, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
+        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
+    };
+    // tile t may start once the previous phase's tiles of its rows are done
+    auto wait_rows = [&](const FfnTile& t) {
+        const int32_t* need = p.ph[t.phase].need;
+        if (!need) return;
+        const int cnt = p.ph[t.phase].need_count;
+        uint32_t it = 0;
+        while (__hip_atomic_load(need + t.mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < cnt &&
+               ++it < p.spin_limit)
+            __builtin_amdgcn_s_sleep(8);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    };
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    // (re)start the K-tile stream at the first K-tile of tile t (global K-tile kbase)
+    auto start_stream = [&](const FfnTile& t) {
+        const FfnSrc here = ffn_src(p, t, 1, 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < P; ++i) dma(here, kbase + g, i);
+        wait_vm<3 * P>();   // the first K-tile landed; 1, 2 and 3 may stay in flight
+        ring_barrier();
+#pragma unroll
+        for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 3) * SC, a0, b0, i, fa0, fb0);
+    };
+
+    wait_rows(c0);
+    start_stream(c0);
+
+    auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
+        const u32x4* stage = ring + (g & 3) * SC;
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa0, fb0, acc);
+            frag(stage, a1, b1, i, fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < EARLY; ++i) bf_mfma1<TL>(i, fa1, fb1, acc);
+        wait_vm<2 * P>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
+        wait_lds();         // this wave's reads of K-tile g are complete
+        ring_barrier();
+        const u32x4* nstage = ring + ((g + 1) & 3) * SC;
+#pragma unroll
+        for (int i = 0; i < NM - EARLY; ++i) {
+            bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
+            if (i < P) dma(src, g + 4, i);
+            frag(nstage, a0, b0, i, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    for (;;) {
+        f32x16 acc[TM][TN];
+#pragma unroll
+        for (int mi = 0; mi < TM; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+
+        const int nk = __builtin_amdgcn_readfirstlane(p.ph[c0.phase].K / 32);
+        const int head = nk - 4;
+        // The count of the next tile's M tile is copied into LDS before the
+        // DMAs of K-tile head + 1, so the vmcnt wait of K-tile head - 1 (which
+        // leaves only K-tiles head + 1 and head + 2 in flight) covers it.
+        const int32_t* need1 = c1.phase >= 0 ? p.ph[c1.phase].need : nullptr;
+        const bool probe = need1 != nullptr && head >= 4;
+        const int split = probe ? head - 3 : head;
+        const FfnSrc here = ffn_src(p, c0, 1, 0);
+        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, acc);
+        if (probe && wave == 0) dma4_dev(need1, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
+        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, acc);
+        const int flag = __builtin_amdgcn_readfirstlane(s_flag[0]);
+        const bool go = c1.phase >= 0 &&
+                        (need1 == nullptr || (probe && flag >= p.ph[c1.phase].need_count && !p.force_wait));
+        const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk) : ffn_src(p, c0, 0, nk - 1);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
+
+        {
+            FusedPhase q = p.ph[c0.phase];
+            q.c = static_cast<uint16_t*>(const_cast<void*>(sgpr_ptr(q.c)));
+            q.aux = static_cast<const uint16_t*>(sgpr_ptr(q.aux));
+            q.N = __builtin_amdgcn_readfirstlane(q.N);
+            q.ldc = __builtin_amdgcn_readfirstlane(q.ldc);
+            q.epi = __builtin_amdgcn_readfirstlane(q.epi);
+            q.dev = __builtin_amdgcn_readfirstlane(q.dev);
+            const TileCoord tc{c0.row0, c0.rows, c0.n0, c0.e};
+            u32x4* const ob = obuf + wave * kObufChunks;
+            // C is [R][ldc] bf16 (below 4 GiB, checked on the host)
+            const __amdgpu_buffer_rsrc_t rc =
+                __builtin_amdgcn_make_buffer_rsrc(q.c, 0, (int)((uint32_t)p.R * (uint32_t)q.ldc * 2u), kRawBufferWord3);
+            const int kind = fused_kind_bit(q.epi, q.dev);
+            if ((KINDS & fused_kind_bit(kEpiSwiglu, 1)) && kind == fused_kind_bit(kEpiSwiglu, 1))
+                bf_epilogue<TL, 1, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc);
+            else if ((KINDS & fused_kind_bit(kEpiDswiglu, 1)) && kind == fused_kind_bit(kEpiDswiglu, 1))
+                bf_epilogue<TL, 2, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, q.aux, rc);
+            else if ((KINDS & fused_kind_bit(kEpiPlain, 1)) && kind == fused_kind_bit(kEpiPlain, 1))
+                bf_epilogue<TL, 0, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc);
+            else
+                bf_epilogue<TL, 0, false>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc);
+        }
+
+        // tile end: a counted tile's stores complete (coherent at device
+        // scope), the ticket claimed one tile ago published, the tile counted
+        int32_t* const done0 = p.ph[c0.phase].done;
+        if (done0) wait_vm<0>();
+        if (threadIdx.x == 0) s_next = pending;
+        wait_lds();
+        ring_barrier();
+        if (threadIdx.x == 0 && done0)
+            __hip_atomic_fetch_add(done0 + c0.mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int id2 = __builtin_amdgcn_readfirstlane(s_next);
+        if (threadIdx.x == 0 && id2 < total)
+            pending = ffn_ticket_id(xcd, 2 * GX + __hip_atomic_fetch_add(p.sync + xcd, 1, __ATOMIC_RELAXED,
+                                                                           __HIP_MEMORY_SCOPE_AGENT), k32);
+        if (c1.phase < 0) break;
+        kbase += nk;
+        c0 = c1;
+        c1 = ffn_tile<BM, BN>(p, id2, MT, s_tstart);
+        if (!go) {
+            // the next tile's first K-tiles were not prefetched: wait for its
+            // rows, let the dummy copies land, and restart the stream there
+            wait_rows(c0);
+            wait_vm<0>();
+            ring_barrier();
+            start_stream(c0);
+        }
+    }
+    wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
+}
+
+// ---------------------------------------------------------------------------- forward, two phases
+//
+// The forward's expert FFN (GEMM1 with the SwiGLU epilogue into h, then GEMM2
+// into ye) has its own kernel with the two phases written out rather than read
+// from a phase table: the same schedule, dependency counters and per-tile
+// computation as gemm_bf16_fused_kernel, but every per-phase value is a kernel
+// argument or a select on them, which keeps the DMA bases in SGPRs.  Measured
+// on one box against the phase-table kernel running the same two phases: 395
+// against 413 us for the bf16_e8 block's FFN.
 struct FfnParams {
     const uint16_t* xe;
     const uint16_t* w1;
@@ -592,18 +919,6 @@ struct FfnParams {
     uint32_t spin_limit;
     int force_wait;   // test hook: treat every GEMM2 tile's rows as not yet done at the early check
 };
-
-struct FfnTile {
-    int row0, rows, n0, e, mt, phase;   // phase 0: GEMM1, 1: GEMM2, -1: no tile
-};
-
-// Id of ticket q of XCD x: blocks of 32 ids over the first 256 k32 ids, then
-// blocks of 4; XCD x takes every 8th block.
-__device__ __forceinline__ int ffn_ticket_id(int x, int q, int k32) {
-    if (q < 32 * k32) return 256 * (q >> 5) + 32 * x + (q & 31);
-    const int r = q - 32 * k32;
-    return 256 * k32 + 32 * (r >> 2) + 4 * x + (r & 3);
-}
 
 template <int BM, int BN>
 __device__ __forceinline__ FfnTile ffn_tile(int id, int total, int T1, int NT1, int NT2, const int* s_tstart, int E,
@@ -622,15 +937,6 @@ __device__ __forceinline__ FfnTile ffn_tile(int id, int total, int T1, int NT1, 
     return c;
 }
 
-// K-tile source of one loop phase (see StreamSrc): K-tile kt = rel * mul + add
-// of the tile's rows of A and its weight slice B (the expert's packed matrix).
-struct FfnSrc {
-    const uint16_t* a;
-    const uint16_t* b;
-    uint32_t rowbytes;
-    int row0, rows, n0, nmax, mul, add;
-};
-
 __device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, int mul, int add) {
     FfnSrc s;
     const bool one = t.phase != 1;
@@ -644,15 +950,6 @@ __device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, 
     s.mul = mul;
     s.add = add;
     return s;
-}
-
-// 4 bytes per lane from base + voff into LDS dword [lds + 4 lane], device
-// scope (sc1): the load observes atomics performed by other XCDs.
-__device__ __forceinline__ void dma4_dev(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 sc1"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sgpr_ptr(base))
-                 : "memory", "m0");
 }
 
 template <class TL>
@@ -798,7 +1095,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
 
         const TileCoord tc{c0.row0, c0.rows, c0.n0, c0.e};
         if (c0.phase == 0)
-            bf_epilogue<TL, 3>(acc, p.h, p.H, 2 * p.H, tc, wm, wn, obuf + wave * kObufChunks, nullptr, hrsrc);
+            bf_epilogue<TL, 1, true>(acc, p.h, p.H, 2 * p.H, tc, wm, wn, obuf + wave * kObufChunks, nullptr, hrsrc);
         else
             bf_epilogue<TL, 0>(acc, p.ye, p.d, p.d, tc, wm, wn, obuf + wave * kObufChunks, nullptr);
 
@@ -1359,6 +1656,24 @@ static int g_ffn_force_wait = 0;
 
 void set_ffn_force_wait(int on) { g_ffn_force_wait = on ? 1 : 0; }
 
+namespace {
+
+template <int KINDS>
+hipError_t launch_fused(FusedParams& p, int R, int E, int ntiles_n, const int32_t* host_counts, hipStream_t s) {
+    using TL = BfRing;
+    p.R = R;
+    p.E = E;
+    p.spin_limit = kFfnSpinLimit;
+    p.force_wait = g_ffn_force_wait;
+    const int grid = persistent_grid(R, E, ntiles_n * TL::BN, TL::BM, TL::BN, 1, host_counts);
+    hipLaunchKernelGGL((gemm_bf16_fused_kernel<TL, KINDS>), dim3(grid), dim3(TL::NTHR), 0, s, p);
+    return hipGetLastError();
+}
+
+int ntiles(int n) { return (n + BfRing::BN - 1) / BfRing::BN; }
+
+}  // namespace
+
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
                            const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
                            const int32_t* host_counts, hipStream_t s) {
@@ -1367,6 +1682,22 @@ hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, 
     const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, kFfnSpinLimit, g_ffn_force_wait};
     hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL>), dim3(grid), dim3(TL::NTHR), 0, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16_t* dh, const uint16_t* xe,
+                                 const uint16_t* w1, uint16_t* dab, const uint16_t* w1t, uint16_t* dxe,
+                                 const int32_t* offsets, int32_t* sync, int R, int E, int d, int H, hipStream_t s) {
+    const int mtmax = R / BfRing::BM + E;
+    int32_t* done0 = sync + kFfnSyncHead;
+    int32_t* done1 = done0 + mtmax;
+    FusedParams p{};
+    p.ph[0] = FusedPhase{dye, wd, dh, nullptr, done0, nullptr, H, d, H, kEpiPlain, 0, 1};
+    p.ph[1] = FusedPhase{xe, w1, dab, dh, done1, done0, 2 * H, d, 2 * H, kEpiDswiglu, ntiles(H), 1};
+    p.ph[2] = FusedPhase{dab, w1t, dxe, nullptr, nullptr, done1, d, 2 * H, d, kEpiPlain, ntiles(2 * H), 0};
+    p.nph = 3;
+    p.offsets = offsets;
+    p.sync = sync;
+    return launch_fused<kFusedBackwardKinds>(p, R, E, ntiles(H) + ntiles(2 * H) + ntiles(d), nullptr, s);
 }
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,

@@ -87,16 +87,23 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
                             const int32_t* offsets, int R, int E, int N, int K, int ldc,
                             const int32_t* host_counts, hipStream_t s, const uint16_t* aux = nullptr);
 
-// Fused bf16 expert FFN (gemm_pipe.hip): GEMM1 with the SwiGLU epilogue into h and
-// GEMM2 into ye in one persistent launch (d and H at least 128).  sync holds
-// ffn_sync_ints(R, E) int32 that must be zero when the kernel starts; a GEMM2 tile
-// waits at most about kFfnSpinLimit sleeps for the GEMM1 tiles of its rows.
+// Fused bf16 grouped GEMMs (gemm_pipe.hip), d and H at least 128, one persistent
+// launch each: the forward expert FFN (GEMM1 with the SwiGLU epilogue into h, then
+// GEMM2 into ye) and the backward chain (dh = dye W_down^T, then da | db from the
+// gate/up recompute and dh, then dxe = (da | db) W1^T, W1T [E][d][2H]).  sync holds
+// fused_sync_ints(R, E, phases) int32 (phases = 2 forward, 3 backward) that must be
+// zero when the kernel starts; a dependent tile waits at most about kFfnSpinLimit
+// sleeps for the previous phase's tiles of its rows.
 constexpr uint32_t kFfnSpinLimit = 1u << 20;
-inline int ffn_sync_ints(int R, int E) { return 8 + R / 256 + E; }
+inline int fused_sync_ints(int R, int E, int phases) { return 8 + (phases - 1) * (R / 256 + E); }
+inline int ffn_sync_ints(int R, int E) { return fused_sync_ints(R, E, 2); }
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
                            const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
                            const int32_t* host_counts, hipStream_t s);
-// Test hook: nonzero makes every GEMM2 tile of the fused FFN take the wait-and-restart path.
+hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16_t* dh, const uint16_t* xe,
+                                 const uint16_t* w1, uint16_t* dab, const uint16_t* w1t, uint16_t* dxe,
+                                 const int32_t* offsets, int32_t* sync, int R, int E, int d, int H, hipStream_t s);
+// Test hook: nonzero makes every dependent tile of the fused GEMMs take the wait-and-restart path.
 void set_ffn_force_wait(int on);
 // p[0, n) := 0 (a fill kernel, so that callers may capture it in a graph).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);

@@ -183,3 +183,24 @@ def test_full_size_backward(name):
         _check(f"dw_gate[{e}][:, {hb}:+32]", _f64(g["dw_gate"][e][:, hb:hb + 32]), c["dw_gate"], w.act)
         _check(f"dw_up[{e}][:, {hb}:+32]", _f64(g["dw_up"][e][:, hb:hb + 32]), c["dw_up"], w.act)
         _check(f"dw_down[{e}][{hb}:+32]", _f64(g["dw_down"][e][hb:hb + 32]), c["dw_down"], w.act)
+
+
+@pytest.mark.parametrize("cap", [0, 8], ids=["full_grid", "cap8"])
+def test_backward_chain_wait_path(cap):
+    """The bf16 backward runs dh, da | db and dxe as one fused launch whose
+    dependent tiles wait on per-M-tile counters; forcing every dependent tile
+    through the wait-and-restart path (and a capped grid) leaves every gradient
+    bitwise unchanged."""
+    w = W.Workload("bwd_chain", T=1200, d=512, E=8, k=2, H=384, act="bf16", router="learned", seed=3401)
+    print(f"[backward chain wait path] cap={cap} {w.describe()}", flush=True)
+    try:
+        B.set_gemm_grid_cap(cap)
+        _, _, _, normal = _run(w)
+        B.set_test_flags(B.MOE_TEST_FFN_WAIT)
+        _, _, _, waited = _run(w)
+    finally:
+        B.set_test_flags(0)
+        B.set_gemm_grid_cap(0)
+    for k in normal[0]:
+        if normal[0][k] is not None:
+            assert torch.equal(normal[0][k], waited[0][k]), f"{k} changed on the wait-and-restart path"
