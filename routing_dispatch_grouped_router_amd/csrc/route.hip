@@ -183,6 +183,78 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(const uint16_t*
     }
 }
 
+// The same logits with W read in its stored [d][E] layout, for E a multiple
+// of 8, so no transposed copy is made first: per batch of eight 32-wide steps
+// each wave stages the 256 rows of its 16 expert columns (8 KB, columns past E
+// zero) in its own LDS slab, row-major with 32 bytes per row, and builds each
+// B operand (8 consecutive k of one expert column per lane) from two
+// transposing LDS reads (ds_read_b64_tr_b16: 16 lanes addressing rows
+// r0 + L / 4 and columns 4 (L % 4) .. + 3 receive rows r0 .. r0 + 3 of column
+// L).  The x loads of the batch are issued together with the slab's, and the
+// MFMA operands are the same bf16 values in the same order as above, so the
+// logits are bitwise those of the transposed path.
+__global__ __launch_bounds__(256) void router_logits_mfma_wr_kernel(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ w,
+                                                                    float* __restrict__ logits, int T, int d, int E) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lp;
+    __shared__ f32x4_r red[4][64];
+    __shared__ u32x4 slab[4][512];   // per wave: 256 rows x 2 halves of 8 columns
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int ta = min(t0 + (lane & 15), T - 1);
+    const int ns = d / 32, s_lo = wave * ns / 4, s_hi = (wave + 1) * ns / 4;   // this wave's 32-wide steps
+    const uint16_t* xa = x + (size_t)ta * d + 8 * (lane >> 4);
+    u32x4* const sw = slab[wave];
+    const __attribute__((address_space(3))) char* const sb =
+        (const __attribute__((address_space(3))) char*)(const __attribute__((address_space(3))) void*)sw;
+    const int L = lane & 15, g = lane >> 4;
+    const uint32_t tr0 = (uint32_t)(8 * g + L / 4) * 32u + (uint32_t)(L % 4) * 8u;   // step 0, first read
+    f32x4_r acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = s_lo; s0 < s_hi; s0 += 8) {
+        bf16x8_r a[8];
+        u32x4 wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = 32 * min(s0 + u, s_hi - 1);   // a clamped step is loaded but not accumulated
+            a[u] = *reinterpret_cast<const bf16x8_r*>(xa + k);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = lane + 64 * i, row = q >> 1, half = q & 1;
+            const int k = min(32 * s0 + row, d - 1);   // rows of clamped steps are never read
+            wv[i] = e0 + 8 * half + 8 <= E ? *reinterpret_cast<const u32x4*>(w + (size_t)k * E + e0 + 8 * half)
+                                           : (u32x4){0u, 0u, 0u, 0u};
+        }
+        // the previous batch's reads of the slab are complete before it is overwritten
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sw[lane + 64 * i] = wv[i];
+        // the slab is private to the wave: its own writes complete, then any lane reads any row
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (s0 + u < s_hi) {
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(sb + tr0 + 1024u * u));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(sb + tr0 + 1024u * u + 128u));
+                const bf16x8_r b = __builtin_bit_cast(bf16x8_r, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b, acc, 0, 0, 0);
+            }
+        }
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        const f32x4_r sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        const int e = e0 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 4 * (lane >> 4) + i;
+            if (t < T && e < E) logits[(size_t)t * E + e] = sum[i];
+        }
+    }
+}
+
 hipError_t launch_router_logits(int act, const void* x, const void* w, float* logits, int T, int d,
                                 int E, uint16_t* wt, hipStream_t s) {
     if (act == kF32) {
@@ -190,10 +262,15 @@ hipError_t launch_router_logits(int act, const void* x, const void* w, float* lo
         hipLaunchKernelGGL(router_logits_kernel<float>, grid, block, 0, s,
                            static_cast<const float*>(x), static_cast<const float*>(w), logits, T, d, E);
     } else {
+        dim3 grid((T + 15) / 16, (E + 15) / 16), block(256);
+        if (E % 8 == 0) {
+            hipLaunchKernelGGL(router_logits_mfma_wr_kernel, grid, block, 0, s, static_cast<const uint16_t*>(x),
+                               static_cast<const uint16_t*>(w), logits, T, d, E);
+            return hipGetLastError();
+        }
         const int n = d * E;
         hipLaunchKernelGGL(router_wt_kernel, dim3(std::min((n + 255) / 256, 1024)), dim3(256), 0, s,
                            static_cast<const uint16_t*>(w), d, E, wt);
-        dim3 grid((T + 15) / 16, (E + 15) / 16), block(256);
         hipLaunchKernelGGL(router_logits_mfma_kernel, grid, block, 0, s, static_cast<const uint16_t*>(x), wt, logits,
                            T, d, E);
     }
