@@ -179,7 +179,10 @@ int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, vo
  *                  workspace must not overlap)
  * bfloat16 (d_model and d_hidden >= 128) runs both projections in one
  * persistent launch: a GEMM2 tile starts once the GEMM1 tiles of its rows have
- * finished, so neither GEMM ends in a partly filled round.
+ * finished, so neither GEMM ends in a partly filled round.  That wait is
+ * bounded (about 2 s): if other work kept this launch's GEMM1 workgroups off
+ * the compute units for longer, the GEMM2 tile would go ahead and ye would be
+ * wrong, rather than the launch hanging.
  * Every output tile is computed whole by one workgroup in a fixed K order, so
  * the result does not depend on the grid (moe_set_gemm_grid_cap). */
 int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* xe_scale,

@@ -93,8 +93,10 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
 // gate/up recompute and dh, then dxe = (da | db) W1^T, W1T [E][d][2H]).  sync holds
 // fused_sync_ints(R, E, phases) int32 (phases = 2 forward, 3 backward) that must be
 // zero when the kernel starts; a dependent tile waits at most about kFfnSpinLimit
-// sleeps for the previous phase's tiles of its rows.
-constexpr uint32_t kFfnSpinLimit = 1u << 20;
+// sleeps of 512 cycles (about 2 s) for the previous phase's tiles of its rows, which
+// take tens of microseconds unless other work holds the compute units that long: the
+// bound trades a hang of the whole GPU for a wrong result in that case.
+constexpr uint32_t kFfnSpinLimit = 1u << 22;
 inline int fused_sync_ints(int R, int E, int phases) { return 8 + (phases - 1) * (R / 256 + E); }
 inline int ffn_sync_ints(int R, int E) { return fused_sync_ints(R, E, 2); }
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
