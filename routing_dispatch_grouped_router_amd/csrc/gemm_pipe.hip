@@ -538,11 +538,12 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 //
 // Up to three grouped GEMMs over the same expert segments in one persistent
 // launch, each phase's M tile depending on the previous phase's tiles of the
-// same rows:
-//   forward:  GEMM1 (h = silu(xe W_gate) * (xe W_up)), then GEMM2 (ye = h W_down);
-//   backward: dh = dye W_down^T, then the gate/up recompute with the SwiGLU
-//             backward in its epilogue (da | db, reading dh), then dxe = (da | db) W1^T.
-// So no phase ends in a round of tiles on a partly idle chip: with 256
+// same rows.  The phase-table kernel below runs the backward chain: dh = dye
+// W_down^T, then the gate/up recompute with the SwiGLU backward in its
+// epilogue (da | db, reading dh), then dxe = (da | db) W1^T.  The forward's
+// GEMM1 (h = silu(xe W_gate) * (xe W_up)) then GEMM2 (ye = h W_down) follows
+// the same design with the two phases written out (gemm_bf16_ffn_kernel,
+// after this one).  So no phase ends in a round of tiles on a partly idle chip: with 256
 // workgroups and, say, 1040 tiles per GEMM, separate launches each end in a
 // round of 16 tiles, while here the workgroups that finish their share of one
 // phase go straight on to the next.  The schedule stays device-resident (the
