@@ -105,21 +105,34 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void combine_bwd_kernel(
         ex[j] = idx[i];
         g[j] = gate[i];
     }
-    for (int c = lane; c < row_chunks; c += 64) {
-        float v[8], w[KMAX][8];
-        load_chunk<BF>(dy, (size_t)t * row_chunks + c, v);
+    // CG chunk groups per round: their (k + 1) CG loads are in flight together;
+    // each lane still takes its chunks in ascending order, so the dot products
+    // accumulate in the same order as one chunk per round
+    constexpr int CG = KMAX <= 4 ? 2 : 1;
+    for (int c0 = lane; c0 < row_chunks; c0 += 64 * CG) {
+        float v[CG][8], w[CG][KMAX][8];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) load_chunk<BF>(ye, (size_t)p[j] * row_chunks + c, w[j]);
+        for (int q = 0; q < CG; ++q) {
+            const int c = min(c0 + 64 * q, row_chunks - 1);   // a clamped chunk is loaded but not used
+            load_chunk<BF>(dy, (size_t)t * row_chunks + c, v[q]);
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            if (j >= k) continue;
-            float o[8];
+            for (int j = 0; j < KMAX; ++j) load_chunk<BF>(ye, (size_t)p[j] * row_chunks + c, w[q][j]);
+        }
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                dot[j] = fmaf(v[i], w[j][i], dot[j]);
-                o[i] = g[j] * v[i];
+        for (int q = 0; q < CG; ++q) {
+            const int c = c0 + 64 * q;
+            if (c >= row_chunks) continue;
+#pragma unroll
+            for (int j = 0; j < KMAX; ++j) {
+                if (j >= k) continue;
+                float o[8];
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    dot[j] = fmaf(v[q][i], w[q][j][i], dot[j]);
+                    o[i] = g[j] * v[q][i];
+                }
+                store_chunk<BF>(dye, (size_t)p[j] * row_chunks + c, o);
             }
-            store_chunk<BF>(dye, (size_t)p[j] * row_chunks + c, o);
         }
     }
     float inner = 0.f;
@@ -277,29 +290,50 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __res
         ex[j] = idx[i];
         ds[j] = dsel[i];
     }
-    for (int c = lane; c < row_chunks; c += 64) {
-        float acc[8], w[KMAX][8];
+    // all k dxe chunks and k W_r^T chunks of CG chunk groups are loaded
+    // together, then summed: the dxe rows in slot order, then the router terms
+    // in slot order
+    constexpr int CG = KMAX <= 4 ? 2 : 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(dxe);
+    const u32x4* wsrc = reinterpret_cast<const u32x4*>(wrt);
+    auto val = [](const u32x4& v, int i) {
+        return BF ? __uint_as_float((i & 1) ? (v[i / 2] & 0xFFFF0000u) : (v[i / 2] << 16)) : __uint_as_float(v[i]);
+    };
+    for (int c0 = lane; c0 < row_chunks; c0 += 64 * CG) {
+        u32x4 v[KMAX][CG], wv[KMAX][CG];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < KMAX; ++j)
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) load_chunk<BF>(dxe, (size_t)p[j] * row_chunks + c, w[j]);
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            if (j >= k) continue;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) acc[i] += w[j][i];
-        }
+            for (int g = 0; g < CG; ++g) v[j][g] = src[(size_t)p[j] * row_chunks + min(c0 + 64 * g, row_chunks - 1)];
         if (wrt) {
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j) load_chunk<BF>(wrt, (size_t)ex[j] * row_chunks + c, w[j]);   // W_r^T rows
+            for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+                for (int g = 0; g < CG; ++g)
+                    wv[j][g] = wsrc[(size_t)ex[j] * row_chunks + min(c0 + 64 * g, row_chunks - 1)];   // W_r^T rows
+        }
+#pragma unroll
+        for (int g = 0; g < CG; ++g) {
+            if (c0 + 64 * g >= row_chunks) continue;
+            float acc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) {
                 if (j >= k) continue;
 #pragma unroll
-                for (int i = 0; i < NV; ++i) acc[i] = fmaf(ds[j], w[j][i], acc[i]);
+                for (int i = 0; i < NV; ++i) acc[i] += val(v[j][g], i);
             }
+            if (wrt) {
+#pragma unroll
+                for (int j = 0; j < KMAX; ++j) {
+                    if (j >= k) continue;
+#pragma unroll
+                    for (int i = 0; i < NV; ++i) acc[i] = fmaf(ds[j], val(wv[j][g], i), acc[i]);
+                }
+            }
+            store_chunk<BF>(dx, (size_t)t * row_chunks + c0 + 64 * g, acc);
         }
-        store_chunk<BF>(dx, (size_t)t * row_chunks + c, acc);
     }
 }
 
