@@ -222,6 +222,50 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
     }
 }
 
+// Row-contiguous device-scope store of one 32 x 32 bf16 block (the 16 values
+// of acc of this lane's row, columns [col0, col0 + 32) of rows row0 .. row0 +
+// 31; rows at or past nrows and the whole block when !col_ok are skipped):
+// the block goes through this wave's LDS buffer `buf` (32 rows x 4 chunks of
+// 16 bytes, chunk c of row q at q * 4 + (c ^ (q & 3))) and is read back so that
+// 4 lanes cover one row's 64 bytes, which reach memory as whole 64-byte
+// segments instead of 16-byte pieces.  The buffer is private to the wave (see
+// store_bf16_pair_rows).
+__device__ __forceinline__ void store_bf16_block_rows_dev(int row0, int nrows, size_t ldc, int col0, bool col_ok,
+                                                          const float (&v)[16], u32x4* __restrict__ buf,
+                                                          __amdgpu_buffer_rsrc_t rc) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31, half = lane >> 5;
+    uint32_t lo[4], hi[4];   // run q: columns 8q + 4 half + (0, 1) and (2, 3)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        lo[q] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
+        hi[q] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
+    }
+    gather_halves(lo);
+    gather_halves(hi);
+    // this lane: row r, columns 16 half .. 16 half + 15 = chunks 2 half, 2 half + 1
+    const int sw = r & 3;
+    buf[r * 4 + ((2 * half) ^ sw)] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
+    buf[r * 4 + ((2 * half + 1) ^ sw)] = (u32x4){lo[2], hi[2], lo[3], hi[3]};
+    asm volatile("" ::: "memory");
+    wait_lds();
+    asm volatile("" ::: "memory");
+    u32x4 o[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = 16 * j + (lane >> 2), c = lane & 3;
+        o[j] = buf[q * 4 + (c ^ (q & 3))];
+    }
+    asm volatile("" ::: "memory");   // the next block's writes stay after these reads
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = 16 * j + (lane >> 2), c = lane & 3;
+        if (q < nrows && col_ok)
+            __builtin_amdgcn_raw_buffer_store_b128(o[j], rc, (uint32_t)((size_t)(row0 + q) * ldc + col0 + 8 * c) * 2u,
+                                                   0, kCpolSc1);
+    }
+}
+
 // Row-contiguous store of a 32 x 64 bf16 block pair (blocks g and u, columns
 // [pc, pc + 64) of 32 rows starting at global row `row0`; rows at or past
 // `nrows` and blocks at or past column N are skipped).  In the MFMA layout
@@ -375,7 +419,12 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
                 float v[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
-                store_bf16_block<DEV>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v, rc);
+                if constexpr (DEV) {
+                    const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
+                    store_bf16_block_rows_dev(c.row0 + rb, c.rows - rb, (size_t)ldc, pc / 2, pc < N, v, obuf, rc);
+                } else {
+                    store_bf16_block<false>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v);
+                }
             }
         }
     }
