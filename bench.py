@@ -38,7 +38,7 @@ from routing_dispatch_grouped_router_amd import binding as B  # noqa: E402
 from routing_dispatch_grouped_router_amd import workloads as W  # noqa: E402
 
 METRIC = "MoE-block fwd tokens/s on 1 MI355X; grouped-GEMM % MFMA peak; dispatch % HBM"
-DEFAULT_CONFIG = "bf16_e8"
+DEFAULT_CONFIG = "bf16_e64_zipf"   # the largest block that fits one GPU
 
 # MI355X published peaks
 HBM_GBPS = 8000.0
@@ -109,6 +109,37 @@ def measured_traffic(config: str, kernel: str):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def single_thread_tiny() -> dict:
+    """The oracle on the whole 256-token float32 block with one BLAS thread:
+    one warm-up, then the median of three runs."""
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_limits
+    w = W.CONFIGS["tiny_f32"]
+    h = W.make_inputs(w)
+    args = [W.as_f64(h[n]) for n in ("x", "w_gate", "w_up", "w_down")]
+    wr = W.as_f64(h["w_router"])
+    times = []
+    with threadpool_limits(limits=1):
+        for _ in range(4):
+            t0 = time.perf_counter()
+            O.forward(args[0], w.E, w.k, w.act, *args[1:], w_router=wr)
+            times.append(time.perf_counter() - t0)
+    ms = sorted(times[1:])[1] * 1e3
+    return {"workload": w.describe(), "ms": round(ms, 3), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+            "threads": 1}
+
+
 def cpu_baseline(w: W.Workload, host: dict, budget_s: float = 12.0) -> dict:
     """Times the oracle (float64 NumPy) on the first tokens of the same batch."""
     from oracle import moe_oracle as O
@@ -138,8 +169,10 @@ def cpu_baseline(w: W.Workload, host: dict, budget_s: float = 12.0) -> dict:
         toks += n
         reps += 1
     return {"value": toks / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"oracle.forward (float64 NumPy) on the first {n} of {w.T} tokens of the "
-                      f"{w.name} batch, {reps} run(s), {total:.1f} s"}
+                      f"{w.name} batch, {reps} run(s), {total:.1f} s",
+            "single_thread_tiny_f32": single_thread_tiny()}
 
 
 def cold_cache_steps(step, dev, steps: int) -> dict:
