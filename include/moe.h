@@ -150,6 +150,30 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, flo
                   int32_t* pos, int32_t* row_token, float* router_stats, void* ws, size_t ws_bytes,
                   void* stream);
 
+/* moe_route for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Arguments, outputs and results are those of moe_route (bit for bit: the
+ * same kernels run); there is no workspace argument.  The routing scratch
+ * (per-block expert histograms and bases, per-block router-probability
+ * partials and, for a bfloat16 / MXFP8 learned router, the transposed router
+ * weights) lives in a library-owned device array of MOE_ROUTE_SCRATCH_BYTES
+ * bytes, one per GPU, set up on the first call on that GPU and held until
+ * the process ends.  The call allocates and frees nothing.
+ * The kernels write every scratch byte they read, so no state carries from
+ * one call to the next; but every call on one GPU uses that GPU's single
+ * array, so calls that overlap on one GPU (other streams, other threads)
+ * race and give wrong results: serialise them.
+ * Errors: as moe_route; MOE_ERR_WORKSPACE (nothing enqueued) when the
+ * problem's routing scratch, the routing part of moe_workspace_bytes' layout
+ * (about ceil(T/256) * E * (12 + 4 G) bytes, G <= 64 the lanes per token in
+ * top-k selection, plus E * d * 2 for a bfloat16 / MXFP8 learned router,
+ * each region rounded up to 256 bytes), exceeds MOE_ROUTE_SCRATCH_BYTES;
+ * MOE_ERR_LAUNCH if the array's device address cannot be obtained. */
+#define MOE_ROUTE_SCRATCH_BYTES (4 << 20)
+int32_t moe_route_noalloc(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                          int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                          int32_t* pos, int32_t* row_token, float* router_stats, void* stream);
+
 /* Rowwise dispatch (report Abstract: each token row written directly into its
  * expert's buffer): xe[pos[t][j]] = x[t] for every slot.
  *   x        : device [T, d]

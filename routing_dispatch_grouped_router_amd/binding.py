@@ -26,7 +26,7 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packe
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
            "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times",
            "moe_set_gemm_grid_cap", "moe_backward_workspace_bytes", "moe_backward_weight_bytes",
-           "moe_pack_weights_backward", "moe_backward", "moe_set_test_flags"]
+           "moe_pack_weights_backward", "moe_backward", "moe_set_test_flags", "moe_route_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -73,6 +73,7 @@ def lib():
         L.moe_packed_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_pack_weights.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_route.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+        L.moe_route_noalloc.argtypes = [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.moe_dispatch.argtypes = [PP, _P, _P, _P, _P, _P]
         L.moe_grouped_swiglu.argtypes = [PP, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.moe_combine.argtypes = [PP, _P, _P, _P, _P, _P]
@@ -193,6 +194,41 @@ def route(p: Problem, x=None, w_router=None, logits=None, ws=None, stream=None, 
         ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(logits), _ptr(out["idx"]), _ptr(out["gate"]),
         _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["pos"]), _ptr(out["row_token"]),
         _ptr(out["router_stats"]), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def route_outputs(p: Problem, device, stats=False) -> dict:
+    """Output tensors of route / route_noalloc for problem p (logits included)."""
+    T, E, k = p.T, p.n_experts, p.top_k
+    return dict(logits=torch.empty((T, E), dtype=torch.float32, device=device),
+                idx=torch.empty((T, k), dtype=torch.int32, device=device),
+                gate=torch.empty((T, k), dtype=torch.float32, device=device),
+                counts=torch.empty((E,), dtype=torch.int32, device=device),
+                offsets=torch.empty((E + 1,), dtype=torch.int32, device=device),
+                pos=torch.empty((T, k), dtype=torch.int32, device=device),
+                row_token=torch.empty((T * k,), dtype=torch.int32, device=device),
+                router_stats=torch.empty((E + 2,), dtype=torch.float32, device=device) if stats else None)
+
+
+def route_noalloc(p: Problem, out: dict, x=None, w_router=None, stream=None) -> dict:
+    """moe_route_noalloc into the caller's tensors `out` (as route_outputs makes
+    them; with MOE_LOGITS_GIVEN out["logits"] holds the input logits).  Neither
+    this function nor the library allocates device memory."""
+    T, E, k, d = p.T, p.n_experts, p.top_k, p.d_model
+    _expect(out["logits"], (T, E), torch.float32, "logits")
+    if not p.flags & MOE_LOGITS_GIVEN:
+        _expect(x, (T, d), storage_dtype(p.act), "x")
+        _expect(w_router, (d, E), storage_dtype(p.act), "w_router")
+    for name, shape in (("idx", (T, k)), ("pos", (T, k)), ("counts", (E,)), ("offsets", (E + 1,)),
+                        ("row_token", (T * k,))):
+        _expect(out[name], shape, torch.int32, name)
+    _expect(out["gate"], (T, k), torch.float32, "gate")
+    if out.get("router_stats") is not None:
+        _expect(out["router_stats"], (E + 2,), torch.float32, "router_stats")
+    _check("moe_route_noalloc", lib().moe_route_noalloc(
+        ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(out["logits"]), _ptr(out["idx"]), _ptr(out["gate"]),
+        _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["pos"]), _ptr(out["row_token"]),
+        _ptr(out.get("router_stats")), _stream(stream)))
     return out
 
 

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_internal.h"
@@ -263,19 +264,30 @@ int32_t moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w
                                 p->d_hidden, static_cast<hipStream_t>(stream)));
 }
 
-int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, float* logits,
-                  int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
-                  int32_t* pos, int32_t* row_token, float* router_stats, void* ws, size_t ws_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+int32_t check_route_args(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                         int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
+                         int32_t* row_token) {
     int32_t st = check_problem(p);
     if (st) return st;
+    if (!logits || !topk_idx || !topk_gate || !counts || !offsets || !pos || !row_token) return MOE_ERR_NULL;
+    if (!(p->flags & MOE_LOGITS_GIVEN) && (!x || !w_router)) return MOE_ERR_NULL;
+    return MOE_OK;
+}
+
+// The routing kernels on arguments already validated; ws holds at least
+// layout(*p).route_end bytes (histograms, block bases, probability partials
+// and the bf16 router's transposed weights), every byte of which the kernels
+// write before they read it.
+int32_t route_impl(const moe_problem* p, const void* x, const void* w_router, float* logits, int32_t* topk_idx,
+                   float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* row_token,
+                   float* router_stats, void* ws, hipStream_t s) {
+    int32_t st = MOE_OK;
     const bool given = p->flags & MOE_LOGITS_GIVEN;
-    if (!logits || !topk_idx || !topk_gate || !counts || !offsets || !pos || !row_token || !ws)
-        return MOE_ERR_NULL;
-    if (!given && (!x || !w_router)) return MOE_ERR_NULL;
     const Layout L = layout(*p);
-    if (ws_bytes < L.route_end) return MOE_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* hist = reinterpret_cast<int32_t*>(at(ws, L.hist));
     int32_t* base = reinterpret_cast<int32_t*>(at(ws, L.base));
     float* psum = router_stats ? reinterpret_cast<float*>(at(ws, L.psum)) : nullptr;
@@ -289,6 +301,63 @@ int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, flo
                                          k, s))))
         return st;
     return launched(launch_route_finalize(topk_idx, base, T, E, k, pos, row_token, s));
+}
+
+}  // namespace
+
+// Scratch of moe_route_noalloc: one array per device, which holds it until the
+// process ends.  In host code the name `scratch` is a host-side stand-in, not
+// a device address; the device address of each device's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MOE_ROUTE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int32_t route_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return MOE_ERR_LAUNCH;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_route(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                  int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                  int32_t* pos, int32_t* row_token, float* router_stats, void* ws, size_t ws_bytes,
+                  void* stream) {
+    int32_t st = check_route_args(p, x, w_router, logits, topk_idx, topk_gate, counts, offsets, pos, row_token);
+    if (st) return st;
+    if (!ws) return MOE_ERR_NULL;
+    if (ws_bytes < layout(*p).route_end) return MOE_ERR_WORKSPACE;
+    return route_impl(p, x, w_router, logits, topk_idx, topk_gate, counts, offsets, pos, row_token, router_stats,
+                      ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t moe_route_noalloc(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                          int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets, int32_t* pos,
+                          int32_t* row_token, float* router_stats, void* stream) {
+    int32_t st = check_route_args(p, x, w_router, logits, topk_idx, topk_gate, counts, offsets, pos, row_token);
+    if (st) return st;
+    if (layout(*p).route_end > (size_t)MOE_ROUTE_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = route_scratch(&ws))) return st;
+    return route_impl(p, x, w_router, logits, topk_idx, topk_gate, counts, offsets, pos, row_token, router_stats,
+                      ws, static_cast<hipStream_t>(stream));
 }
 
 int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, void* xe,

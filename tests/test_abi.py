@@ -119,6 +119,14 @@ def test_test_flags_range(lib, flags, code):
     assert lib.moe_set_test_flags(0) == 0
 
 
+def test_route_noalloc_host_checks(lib):
+    # a problem whose routing scratch exceeds MOE_ROUTE_SCRATCH_BYTES is rejected before any device access
+    p = B.problem(8192, 64, 1024, 16, 64, "bf16", logits_given=True)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_route_noalloc(ctypes.byref(p), None, None, *([fake] * 7), None, None) == -4
+    assert lib.moe_route_noalloc(ctypes.byref(p), None, None, None, *([fake] * 6), None, None) == -1
+
+
 def test_kernel_times_without_profiled_forward(lib):
     n = ctypes.c_int32()
     assert lib.moe_set_profiling(0) == 0
