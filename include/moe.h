@@ -19,8 +19,9 @@
  *  - Pointers named as device pointers must point to device memory of the
  *    current HIP device; the caller owns every buffer.  The library never
  *    allocates device memory, never frees, never copies to the host and never
- *    synchronises inside these calls (except moe_kernel_times and the
- *    comparison path moe_forward_host_sync, see there).
+ *    synchronises inside these calls (except moe_kernel_times, the status
+ *    query moe_fused_status and the comparison path moe_forward_host_sync,
+ *    see there).
  *    All work is enqueued on `stream` (a hipStream_t; NULL = default stream),
  *    so calls on one stream are ordered and the whole sequence is capturable
  *    in a HIP graph.
@@ -204,9 +205,12 @@ int32_t moe_dispatch(const moe_problem* p, const void* x, const int32_t* pos, vo
  * bfloat16 (d_model and d_hidden >= 128) runs both projections in one
  * persistent launch: a GEMM2 tile starts once the GEMM1 tiles of its rows have
  * finished, so neither GEMM ends in a partly filled round.  That wait is
- * bounded (about 2 s): if other work kept this launch's GEMM1 workgroups off
- * the compute units for longer, the GEMM2 tile would go ahead and ye would be
- * wrong, rather than the launch hanging.
+ * bounded (about 2 s) so that the launch cannot hang the GPU: if other work
+ * kept this launch's GEMM1 workgroups off the compute units for longer, the
+ * GEMM2 tile stops waiting, writes its rows of ye as NaN (never a wrong
+ * finite value) and sets an error word in the workspace, which
+ * moe_fused_status reports.  The grid never exceeds the device's compute-unit
+ * count, so on an otherwise idle GPU every wait ends normally.
  * Every output tile is computed whole by one workgroup in a fixed K order, so
  * the result does not depend on the grid (moe_set_gemm_grid_cap). */
 int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* xe_scale,
@@ -271,14 +275,45 @@ int32_t moe_kernel_times(const char** names, float* ms, int32_t max_n, int32_t* 
  * value. */
 int32_t moe_set_gemm_grid_cap(int32_t cap);
 
-/* Test hook for the fused bfloat16 expert FFN (see moe_grouped_swiglu):
- * MOE_TEST_FFN_WAIT makes every GEMM2 tile skip the early check of its rows
- * and start only after waiting for them (the path a tile takes when its rows
- * are not yet done), so tests can show that this path gives the same result.
- * Outputs are unchanged; only speed drops.  Process-wide, applies to calls
- * launched afterwards; 0 clears it.  Returns MOE_ERR_ARG for unknown bits. */
+/* Test hooks for the fused bfloat16 grouped GEMMs (the forward expert FFN of
+ * moe_grouped_swiglu / moe_forward and the backward's data-gradient chain):
+ * MOE_TEST_FFN_WAIT makes every dependent tile skip the early check of its
+ * rows and start only after waiting for them (the path a tile takes when its
+ * rows are not yet done), so tests can show that this path gives the same
+ * result; outputs are unchanged, only speed drops.  MOE_TEST_FFN_GIVE_UP makes
+ * every such wait end at once as if its bound had been reached, without
+ * looking at the counter: the tile writes NaN and raises the error word that
+ * moe_fused_status reports (every kernel still runs to completion), so tests
+ * can check the failure path.  Process-wide, applies to calls launched
+ * afterwards; 0 clears them.  Returns MOE_ERR_ARG for unknown bits. */
 #define MOE_TEST_FFN_WAIT 1
+#define MOE_TEST_FFN_GIVE_UP 2
 int32_t moe_set_test_flags(int32_t flags);
+
+/* Outcome of the bounded dependency waits of the last fused grouped-GEMM
+ * launch that used workspace ws (the report's Section 24.3 asks that buffers be
+ * reused only after their last consumer has finished and that such
+ * dependencies be explicit at component interfaces; in the fused launches one
+ * GEMM's tiles consume rows another GEMM's tiles produce, and a tile that
+ * stops waiting for its producers makes the broken dependency explicit here).
+ *   which  : MOE_STATUS_FORWARD for the workspace of moe_forward /
+ *            moe_forward_host_sync / moe_grouped_swiglu (ws_bytes >= the
+ *            grouped-GEMM part of moe_workspace_bytes), MOE_STATUS_BACKWARD
+ *            for the workspace of moe_backward (ws_bytes >=
+ *            moe_backward_workspace_bytes)
+ *   status : host int32 out: MOE_OK, or MOE_ERR_STATE if some dependent tile
+ *            gave up waiting, in which case its output rows (ye in the
+ *            forward; dh, da | db or dxe and what derives from them in the
+ *            backward) hold NaN.
+ * The word is cleared by every call that launches a fused kernel on ws, so it
+ * describes the last such call; for problems that run no fused launch (other
+ * dtypes or small d, H) the status is MOE_OK without a device access.
+ * Synchronises: the word is copied to the host after the work already queued
+ * on `stream` and the calling thread waits for it. */
+#define MOE_STATUS_FORWARD 0
+#define MOE_STATUS_BACKWARD 1
+int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, int32_t which, int32_t* status,
+                         void* stream);
 
 /* ---------------------------------------------------------------- backward
  *

@@ -26,7 +26,8 @@ EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packe
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_grouped_swiglu", "moe_combine",
            "moe_forward", "moe_forward_host_sync", "moe_set_profiling", "moe_kernel_times",
            "moe_set_gemm_grid_cap", "moe_backward_workspace_bytes", "moe_backward_weight_bytes",
-           "moe_pack_weights_backward", "moe_backward", "moe_set_test_flags", "moe_route_noalloc"]
+           "moe_pack_weights_backward", "moe_backward", "moe_set_test_flags", "moe_route_noalloc",
+           "moe_fused_status"]
 
 
 class MoeError(RuntimeError):
@@ -82,6 +83,7 @@ def lib():
         L.moe_set_profiling.argtypes = [_I32]
         L.moe_set_gemm_grid_cap.argtypes = [_I32]
         L.moe_set_test_flags.argtypes = [_I32]
+        L.moe_fused_status.argtypes = [PP, _P, _SZ, _I32, ctypes.POINTER(_I32), _P]
         L.moe_backward_workspace_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_backward_weight_bytes.argtypes = [PP, ctypes.POINTER(_SZ)]
         L.moe_pack_weights_backward.argtypes = [PP, _P, _P, _P, _P, _P]
@@ -392,13 +394,24 @@ def set_gemm_grid_cap(cap: int):
     _check("moe_set_gemm_grid_cap", lib().moe_set_gemm_grid_cap(int(cap)))
 
 
-MOE_TEST_FFN_WAIT = 1
+MOE_TEST_FFN_WAIT, MOE_TEST_FFN_GIVE_UP = 1, 2
+MOE_STATUS_FORWARD, MOE_STATUS_BACKWARD = 0, 1
 
 
 def set_test_flags(flags: int):
-    """Test hook (MOE_TEST_FFN_WAIT: every GEMM2 tile of the fused bf16 FFN waits for its rows
-    before starting, the path taken when they are not yet done); 0 clears it."""
+    """Test hooks of the fused bf16 grouped GEMMs (MOE_TEST_FFN_WAIT: every dependent tile waits
+    for its rows before starting, the path taken when they are not yet done; MOE_TEST_FFN_GIVE_UP:
+    every such wait ends at once as if its bound had been reached); 0 clears them."""
     _check("moe_set_test_flags", lib().moe_set_test_flags(int(flags)))
+
+
+def fused_status(p: Problem, ws, which=MOE_STATUS_FORWARD, stream=None) -> int:
+    """MOE_OK (0) or MOE_ERR_STATE (-6) from the error word of the last fused grouped-GEMM launch
+    on workspace ws (synchronises on the stream)."""
+    st = _I32()
+    _check("moe_fused_status", lib().moe_fused_status(ctypes.byref(p), _ptr(ws), ws.numel(), int(which),
+                                                      ctypes.byref(st), _stream(stream)))
+    return st.value
 
 
 def kernel_times() -> list[tuple[str, float]]:

@@ -538,9 +538,44 @@ int32_t moe_set_gemm_grid_cap(int32_t cap) {
     return set_pipe_grid_cap(cap) ? MOE_ERR_ARG : MOE_OK;
 }
 
+static int32_t check_backward(const moe_problem* p);
+
 int32_t moe_set_test_flags(int32_t flags) {
-    if (flags & ~MOE_TEST_FFN_WAIT) return MOE_ERR_ARG;
+    if (flags & ~(MOE_TEST_FFN_WAIT | MOE_TEST_FFN_GIVE_UP)) return MOE_ERR_ARG;
     set_ffn_force_wait(flags & MOE_TEST_FFN_WAIT);
+    set_ffn_give_up(flags & MOE_TEST_FFN_GIVE_UP);
+    return MOE_OK;
+}
+
+int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, int32_t which, int32_t* status,
+                         void* stream) {
+    int32_t st = which == MOE_STATUS_BACKWARD ? check_backward(p) : check_problem(p);
+    if (st) return st;
+    if (which != MOE_STATUS_FORWARD && which != MOE_STATUS_BACKWARD) return MOE_ERR_ARG;
+    if (!ws || !status) return MOE_ERR_NULL;
+    size_t sync = 0, need = 0;
+    bool fused = false;
+    if (which == MOE_STATUS_FORWARD) {
+        const Layout L = layout(*p);
+        sync = L.sync;
+        need = L.gemm_end;
+        fused = use_ffn(*p);
+    } else {
+        const BwdLayout B = bwd_layout(*p);
+        sync = B.sync;
+        need = B.total;
+        fused = use_bwd_chain(*p);
+    }
+    if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+    *status = MOE_OK;
+    if (!fused) return MOE_OK;   // no fused launch, nothing waits
+    int32_t word = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = launched(hipMemcpyAsync(&word, static_cast<const char*>(ws) + sync + 4 * (size_t)kSyncErrWord, 4,
+                                      hipMemcpyDeviceToHost, s))))
+        return st;
+    if ((st = launched(hipStreamSynchronize(s)))) return st;
+    *status = word ? MOE_ERR_STATE : MOE_OK;
     return MOE_OK;
 }
 

@@ -13,6 +13,8 @@
 // interleaves 32 gate columns with the matching 32 up columns, so the
 // accumulators for gate and up of one (row, h) land in the same lane and the
 // SwiGLU is applied in registers before h is stored.
+#include <mutex>
+
 #include "grouped_sched.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -124,6 +126,21 @@ int set_pipe_grid_cap(int cap) {
     return 0;
 }
 
+int device_compute_units() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int cus[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts) {
     long mt = (long)R / BM + (long)min(E, R);
     if (host_counts) {
@@ -131,7 +148,12 @@ int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32
         for (int e = 0; e < E; ++e) mt += (host_counts[e] + BM - 1) / BM;
     }
     const long tiles = mt * ((N + BN - 1) / BN);
-    long g = min(tiles, (long)256 * per_cu);
+    // at most one workgroup per compute unit for the pipelined kernels (their
+    // LDS allows no more), as a multiple of the 8 XCDs: every workgroup is
+    // resident at once, which the fused launches' dependency waits rely on
+    const long cus = max(device_compute_units(), kXcds);
+    const long cap = per_cu == 1 ? cus / kXcds * kXcds : cus * per_cu;
+    long g = min(tiles, cap);
     g = (g + kXcds - 1) / kXcds * kXcds;
     g = max(g, (long)kXcds);
     if (per_cu == 1 && g_pipe_grid_cap) g = min(g, (long)g_pipe_grid_cap);

@@ -190,6 +190,14 @@ __device__ __forceinline__ void gather_halves(uint32_t (&w)[4]) {
 constexpr int kCpolSc1 = 16;
 // Buffer resource word 3 of a raw (unformatted) gfx9 buffer.
 constexpr int kRawBufferWord3 = 0x00020000;
+// Two bfloat16 quiet NaNs: the stored output of a tile whose input rows were
+// not seen complete (the bounded wait of the fused grouped GEMMs gave up).
+constexpr uint32_t kBf16NanPair = 0x7FC07FC0u;
+
+__device__ __forceinline__ void poison_words(uint32_t (&w)[4], bool poison) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = poison ? kBf16NanPair : w[q];
+}
 
 // bf16 block store: the 16 values of acc (one 32 x 32 block, this lane's row)
 // as bf16 columns [col0, col0 + 32) of row `grow` of C (if the row is valid).
@@ -198,13 +206,16 @@ constexpr int kRawBufferWord3 = 0x00020000;
 template <bool DEV = false>
 __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_t ldc, int grow, bool valid,
                                                  int col0, const float (&v)[16],
-                                                 __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t()) {
+                                                 __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t(),
+                                                 bool poison = false) {
     uint32_t lo[4], hi[4];   // run q: columns 8q + 4 half + (0, 1) and (2, 3)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         lo[q] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
         hi[q] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
     }
+    poison_words(lo, poison);
+    poison_words(hi, poison);
     gather_halves(lo);
     gather_halves(hi);
     // half 0: columns 0..15 = runs (w0 = q0 lo/hi of half 0, w1 = q0 of half 1, ...)
@@ -232,7 +243,7 @@ __device__ __forceinline__ void store_bf16_block(uint16_t* __restrict__ C, size_
 // store_bf16_pair_rows).
 __device__ __forceinline__ void store_bf16_block_rows_dev(int row0, int nrows, size_t ldc, int col0, bool col_ok,
                                                           const float (&v)[16], u32x4* __restrict__ buf,
-                                                          __amdgpu_buffer_rsrc_t rc) {
+                                                          __amdgpu_buffer_rsrc_t rc, bool poison) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, half = lane >> 5;
     uint32_t lo[4], hi[4];   // run q: columns 8q + 4 half + (0, 1) and (2, 3)
@@ -241,6 +252,8 @@ __device__ __forceinline__ void store_bf16_block_rows_dev(int row0, int nrows, s
         lo[q] = pack_bf16x2(v[4 * q], v[4 * q + 1]);
         hi[q] = pack_bf16x2(v[4 * q + 2], v[4 * q + 3]);
     }
+    poison_words(lo, poison);
+    poison_words(hi, poison);
     gather_halves(lo);
     gather_halves(hi);
     // this lane: row r, columns 16 half .. 16 half + 15 = chunks 2 half, 2 half + 1
@@ -283,7 +296,8 @@ template <int RR, bool DEV = false>
 __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, size_t ldc, int row0, int nrows,
                                                      int pc, int N, const float (&g)[16], const float (&u)[16],
                                                      u32x4* __restrict__ buf,
-                                                     __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t()) {
+                                                     __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t(),
+                                                     bool poison = false) {
     static_assert(RR == 16 || RR == 32, "rows per round");
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, half = lane >> 5;
@@ -295,6 +309,8 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
             lo[q] = pack_bf16x2(g[4 * q], g[4 * q + 1]);
             hi[q] = pack_bf16x2(g[4 * q + 2], g[4 * q + 3]);
         }
+        poison_words(lo, poison);
+        poison_words(hi, poison);
         gather_halves(lo);
         gather_halves(hi);
         ch[0] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
@@ -304,6 +320,8 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
             lo[q] = pack_bf16x2(u[4 * q], u[4 * q + 1]);
             hi[q] = pack_bf16x2(u[4 * q + 2], u[4 * q + 3]);
         }
+        poison_words(lo, poison);
+        poison_words(hi, poison);
         gather_halves(lo);
         gather_halves(hi);
         ch[2] = (u32x4){lo[0], hi[0], lo[1], hi[1]};
@@ -344,6 +362,28 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
     }
 }
 
+// One accumulator block into VGPRs, at this point of the program: the reads
+// are volatile, so the compiler neither hoists all of them to the start of the
+// epilogue (which would need 256 VGPRs at once) nor reorders them across the
+// stores between blocks.
+__device__ __forceinline__ void acc_read(const f32x16& a, float (&v)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[i]) : "a"(a[i]));
+}
+
+// Accumulator block of a tile geometry: waves of 128 x 128 (one wave per SIMD)
+// keep their 256 accumulators in AGPRs and read them block by block; smaller
+// wave tiles keep them in VGPRs.
+template <class TL>
+__device__ __forceinline__ void acc_block(const f32x16& a, float (&v)[16]) {
+    if constexpr (TL::TM * TL::TN >= 16) {
+        acc_read(a, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = a[i];
+    }
+}
+
 // ============================================================================ bf16
 
 // One ring stage holds 32 K values per row: two 16-wide k-steps; lane l's
@@ -362,7 +402,8 @@ template <class TL, int EPI, bool DEV = false>
 __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], uint16_t* __restrict__ C,
                                             int ldc, int N, const TileCoord& c, int wm, int wn,
                                             u32x4* __restrict__ obuf, const uint16_t* __restrict__ aux,
-                                            __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t()) {
+                                            __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t(),
+                                            bool poison = false) {
     const int lane = threadIdx.x & 63;
     static_assert(EPI != 2 || TL::TN == 2, "one gate/up pair per wave row block");
     uint32_t dhw[EPI == 2 ? TL::TM : 1][4][2];   // dh runs: [mi][q] = 4 bf16 of h 8 q + 4 half + 0..3
@@ -398,33 +439,34 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
             }
             const int rb = wm * TL::WROWS + mi * 32;
             store_bf16_pair_rows<16, DEV>(C, (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS, N, g, u,
-                                          obuf, rc);
+                                          obuf, rc, poison);
         } else if (EPI == 0) {
 #pragma unroll
             for (int np = 0; np < TL::TN / 2; ++np) {
                 float g[16], u[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    g[i] = acc[mi][2 * np][i];
-                    u[i] = acc[mi][2 * np + 1][i];
-                }
+                acc_block<TL>(acc[mi][2 * np], g);
+                acc_block<TL>(acc[mi][2 * np + 1], u);
                 const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
                 store_bf16_pair_rows<16, DEV>(C, (size_t)ldc, c.row0 + rb, c.rows - rb,
-                                              c.n0 + wn * TL::WCOLS + np * 64, N, g, u, obuf, rc);
+                                              c.n0 + wn * TL::WCOLS + np * 64, N, g, u, obuf, rc, poison);
+                __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
         } else {
 #pragma unroll
             for (int np = 0; np < TL::TN / 2; ++np) {
                 const int pc = c.n0 + wn * TL::WCOLS + np * 64;
-                float v[16];
+                float v[16], u[16];
+                acc_block<TL>(acc[mi][2 * np], v);
+                acc_block<TL>(acc[mi][2 * np + 1], u);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = silu_mul_p(acc[mi][2 * np][i], acc[mi][2 * np + 1][i]);
+                for (int i = 0; i < 16; ++i) v[i] = silu_mul_p(v[i], u[i]);
                 if constexpr (DEV) {
                     const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
-                    store_bf16_block_rows_dev(c.row0 + rb, c.rows - rb, (size_t)ldc, pc / 2, pc < N, v, obuf, rc);
+                    store_bf16_block_rows_dev(c.row0 + rb, c.rows - rb, (size_t)ldc, pc / 2, pc < N, v, obuf, rc, poison);
                 } else {
-                    store_bf16_block<false>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v);
+                    store_bf16_block<false>(C, (size_t)ldc, c.row0 + r, valid && pc < N, pc / 2, v, rc, poison);
                 }
+                __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
         }
     }
@@ -638,9 +680,14 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
 // workgroups, are done; the spin bound ends it regardless.  The rows an M tile
 // of one phase writes are read by nobody before its count is complete (rows
 // are clamped inside each tile), so no cache can hold a stale copy of them.
+// The wait is bounded: one lane spins (with s_sleep) on the counter and
+// shares the outcome with the workgroup through LDS; if the bound is reached
+// the lane raises the error word and the whole tile, computed on rows it could
+// not see complete, stores NaN instead of its values, so a caller can detect
+// the failure (the error word) and no wrong value passes for a right one.
 // sync layout (int32, zeroed before the launch): [0, 8) per-XCD tile
-// counters, then one array of MTmax counters per phase that others wait on.
-constexpr int kFfnSyncHead = 8;
+// counters, word kSyncErrWord the error word, then from kSyncHead one array
+// of MTmax counters per phase that others wait on.
 constexpr int kFusedMaxPhases = 3;
 
 // Epilogue kinds of a fused phase.
@@ -754,6 +801,20 @@ __device__ __forceinline__ void dma4_dev(const void* base, uint32_t voff, uint32
                  : "memory", "m0");
 }
 
+// One lane's bounded wait for *count >= need: at most `limit` sleeps of 512
+// cycles (limit 0: gives up at once without looking, the test hook).  On
+// giving up it sets the error word and returns 0; otherwise 1.
+__device__ __forceinline__ int bounded_wait(const int32_t* count, int need, uint32_t limit, int32_t* err) {
+    for (uint32_t it = 0;; ++it) {
+        if (it >= limit) {
+            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return 0;
+        }
+        if (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) return 1;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
 template <class TL, int KINDS>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_bf16_fused_kernel(FusedParams p) {
@@ -768,6 +829,7 @@ void gemm_bf16_fused_kernel(FusedParams p) {
     __shared__ int s_scan[NTHR];
     __shared__ int s_flag[64];
     __shared__ int s_next;
+    __shared__ int s_ok;
 
     const int MT = __builtin_amdgcn_readfirstlane(build_tile_schedule<BM, NTHR>(p.offsets, p.E, s_tstart, s_scan));
     int total = 0;
@@ -817,16 +879,17 @@ void gemm_bf16_fused_kernel(FusedParams p) {
         if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
         else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
     };
-    // tile t may start once the previous phase's tiles of its rows are done
-    auto wait_rows = [&](const FfnTile& t) {
+    // tile t may start once the previous phase's tiles of its rows are done;
+    // false if the bounded wait gave up (error word raised)
+    auto wait_rows = [&](const FfnTile& t) -> bool {
         const int32_t* need = p.ph[t.phase].need;
-        if (!need) return;
-        const int cnt = p.ph[t.phase].need_count;
-        uint32_t it = 0;
-        while (__hip_atomic_load(need + t.mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < cnt &&
-               ++it < p.spin_limit)
-            __builtin_amdgcn_s_sleep(8);
+        if (!need) return true;
+        if (threadIdx.x == 0)
+            s_ok = bounded_wait(need + t.mt, p.ph[t.phase].need_count, p.spin_limit, p.sync + kSyncErrWord);
+        wait_lds();
+        ring_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return __builtin_amdgcn_readfirstlane(s_ok) != 0;
     };
     bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     // (re)start the K-tile stream at the first K-tile of tile t (global K-tile kbase)
@@ -842,7 +905,7 @@ void gemm_bf16_fused_kernel(FusedParams p) {
         for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 3) * SC, a0, b0, i, fa0, fb0);
     };
 
-    wait_rows(c0);
+    bool poison = !wait_rows(c0);   // the current tile's rows were not seen complete
     start_stream(c0);
 
     auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
@@ -910,13 +973,13 @@ void gemm_bf16_fused_kernel(FusedParams p) {
                 __builtin_amdgcn_make_buffer_rsrc(q.c, 0, (int)((uint32_t)p.R * (uint32_t)q.ldc * 2u), kRawBufferWord3);
             const int kind = fused_kind_bit(q.epi, q.dev);
             if ((KINDS & fused_kind_bit(kEpiSwiglu, 1)) && kind == fused_kind_bit(kEpiSwiglu, 1))
-                bf_epilogue<TL, 1, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc);
+                bf_epilogue<TL, 1, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc, poison);
             else if ((KINDS & fused_kind_bit(kEpiDswiglu, 1)) && kind == fused_kind_bit(kEpiDswiglu, 1))
-                bf_epilogue<TL, 2, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, q.aux, rc);
+                bf_epilogue<TL, 2, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, q.aux, rc, poison);
             else if ((KINDS & fused_kind_bit(kEpiPlain, 1)) && kind == fused_kind_bit(kEpiPlain, 1))
-                bf_epilogue<TL, 0, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc);
+                bf_epilogue<TL, 0, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc, poison);
             else
-                bf_epilogue<TL, 0, false>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc);
+                bf_epilogue<TL, 0, false>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc, poison);
         }
 
         // tile end: a counted tile's stores complete (coherent at device
@@ -936,10 +999,11 @@ void gemm_bf16_fused_kernel(FusedParams p) {
         kbase += nk;
         c0 = c1;
         c1 = ffn_tile<BM, BN>(p, id2, MT, s_tstart);
+        poison = false;
         if (!go) {
             // the next tile's first K-tiles were not prefetched: wait for its
             // rows, let the dummy copies land, and restart the stream there
-            wait_rows(c0);
+            poison = !wait_rows(c0);
             wait_vm<0>();
             ring_barrier();
             start_stream(c0);
@@ -1016,6 +1080,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     __shared__ int s_scan[NTHR];
     __shared__ int s_flag[64];
     __shared__ int s_next;
+    __shared__ int s_ok;
 
     const int MT = build_tile_schedule<BM, NTHR>(p.offsets, p.E, s_tstart, s_scan);
     const int NT1 = (2 * p.H + BN - 1) / BN, NT2 = (p.d + BN - 1) / BN;
@@ -1037,7 +1102,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
     const int drow = lane >> 2;
     const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
-    int32_t* const done = p.sync + kFfnSyncHead;
+    int32_t* const done = p.sync + kSyncHead;
     const __amdgpu_buffer_rsrc_t hrsrc =
         __builtin_amdgcn_make_buffer_rsrc(p.h, 0, (int)((uint32_t)p.R * (uint32_t)p.H * 2u), kRawBufferWord3);
 
@@ -1069,14 +1134,15 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
         else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
     };
-    // GEMM2 tile t may start once all NT1 GEMM1 tiles of its M tile are done
-    auto wait_rows = [&](const FfnTile& t) {
-        if (t.phase != 1) return;
-        uint32_t it = 0;
-        while (__hip_atomic_load(done + t.mt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NT1 &&
-               ++it < p.spin_limit)
-            __builtin_amdgcn_s_sleep(8);
+    // GEMM2 tile t may start once all NT1 GEMM1 tiles of its M tile are done;
+    // false if the bounded wait gave up (error word raised)
+    auto wait_rows = [&](const FfnTile& t) -> bool {
+        if (t.phase != 1) return true;
+        if (threadIdx.x == 0) s_ok = bounded_wait(done + t.mt, NT1, p.spin_limit, p.sync + kSyncErrWord);
+        wait_lds();
+        ring_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return __builtin_amdgcn_readfirstlane(s_ok) != 0;
     };
     bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     // (re)start the K-tile stream at the first K-tile of tile t (global K-tile kbase)
@@ -1092,7 +1158,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 3) * SC, a0, b0, i, fa0, fb0);
     };
 
-    wait_rows(c0);
+    bool poison = !wait_rows(c0);   // the current tile's rows were not seen complete
     start_stream(c0);
 
     auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
@@ -1147,7 +1213,8 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         if (c0.phase == 0)
             bf_epilogue<TL, 1, true>(acc, p.h, p.H, 2 * p.H, tc, wm, wn, obuf + wave * kObufChunks, nullptr, hrsrc);
         else
-            bf_epilogue<TL, 0>(acc, p.ye, p.d, p.d, tc, wm, wn, obuf + wave * kObufChunks, nullptr);
+            bf_epilogue<TL, 0>(acc, p.ye, p.d, p.d, tc, wm, wn, obuf + wave * kObufChunks, nullptr,
+                               __amdgpu_buffer_rsrc_t(), poison);
 
         // tile end: a GEMM1 tile's stores complete (h coherent at device
         // scope), the ticket claimed one tile ago published, the finished GEMM1
@@ -1166,10 +1233,11 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         kbase += nk;
         c0 = c1;
         c1 = ffn_tile<BM, BN>(id2, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
+        poison = false;
         if (!go) {
             // the next tile's first K-tiles were not prefetched: wait for its
             // rows, let the dummy copies land, and restart the stream there
-            wait_rows(c0);
+            poison = !wait_rows(c0);
             wait_vm<0>();
             ring_barrier();
             start_stream(c0);
@@ -1225,15 +1293,6 @@ __device__ __forceinline__ void fp8_mfma(const i32x8 (&fa)[TL::TM], const i32x8 
         acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[ni], fa[mi], acc[mi][ni], 0, 0, 0, sb[ni],
                                                                      0, sa[mi]);
     }
-}
-
-// One accumulator block into VGPRs, at this point of the program: the reads
-// are volatile, so the compiler neither hoists all of them to the start of the
-// epilogue (which would need 256 VGPRs at once) nor reorders them across the
-// stores between blocks.
-__device__ __forceinline__ void acc_read(const f32x16& a, float (&v)[16]) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[i]) : "a"(a[i]));
 }
 
 // MFMA number i (row-major over (mi, ni)); i is a constant after unrolling.
@@ -1703,17 +1762,23 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
 }
 
 static int g_ffn_force_wait = 0;
+static int g_ffn_give_up = 0;
 
 void set_ffn_force_wait(int on) { g_ffn_force_wait = on ? 1 : 0; }
+void set_ffn_give_up(int on) { g_ffn_give_up = on ? 1 : 0; }
+
+static uint32_t ffn_spin_limit() { return g_ffn_give_up ? 0u : kFfnSpinLimit; }
 
 namespace {
 
 template <int KINDS>
 hipError_t launch_fused(FusedParams& p, int R, int E, int ntiles_n, const int32_t* host_counts, hipStream_t s) {
     using TL = BfRing;
+    // the fused launches need their whole grid (a multiple of 8) resident at once
+    if (device_compute_units() < kXcds) return hipErrorInvalidConfiguration;
     p.R = R;
     p.E = E;
-    p.spin_limit = kFfnSpinLimit;
+    p.spin_limit = ffn_spin_limit();
     p.force_wait = g_ffn_force_wait;
     const int grid = persistent_grid(R, E, ntiles_n * TL::BN, TL::BM, TL::BN, 1, host_counts);
     hipLaunchKernelGGL((gemm_bf16_fused_kernel<TL, KINDS>), dim3(grid), dim3(TL::NTHR), 0, s, p);
@@ -1728,8 +1793,9 @@ hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, 
                            const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
                            const int32_t* host_counts, hipStream_t s) {
     using TL = BfRing;
+    if (device_compute_units() < kXcds) return hipErrorInvalidConfiguration;
     const int grid = persistent_grid(R, E, 2 * H + d, TL::BM, TL::BN, 1, host_counts);
-    const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, kFfnSpinLimit, g_ffn_force_wait};
+    const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, ffn_spin_limit(), g_ffn_force_wait};
     hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL>), dim3(grid), dim3(TL::NTHR), 0, s, p);
     return hipGetLastError();
 }
@@ -1738,7 +1804,7 @@ hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16
                                  const uint16_t* w1, uint16_t* dab, const uint16_t* w1t, uint16_t* dxe,
                                  const int32_t* offsets, int32_t* sync, int R, int E, int d, int H, hipStream_t s) {
     const int mtmax = R / BfRing::BM + E;
-    int32_t* done0 = sync + kFfnSyncHead;
+    int32_t* done0 = sync + kSyncHead;
     int32_t* done1 = done0 + mtmax;
     FusedParams p{};
     p.ph[0] = FusedPhase{dye, wd, dh, nullptr, done0, nullptr, H, d, H, kEpiPlain, 0, 1};

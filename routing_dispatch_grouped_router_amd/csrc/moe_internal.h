@@ -79,6 +79,8 @@ hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const vo
 // 8 XCDs; for the pipelined kernels (per_cu 1) at most the cap set by
 // set_pipe_grid_cap (a multiple of 8 up to 256; 0 removes it; -1 if invalid).
 int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32_t* host_counts);
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_compute_units();
 int set_pipe_grid_cap(int cap);
 
 // Pipelined bf16 grouped GEMM (gemm_pipe.hip); epi 1 = SwiGLU epilogue (C has N/2 columns);
@@ -92,12 +94,17 @@ hipError_t launch_bf16_pipe(int epi, const uint16_t* A, const uint16_t* Bw, uint
 // GEMM2 into ye) and the backward chain (dh = dye W_down^T, then da | db from the
 // gate/up recompute and dh, then dxe = (da | db) W1^T, W1T [E][d][2H]).  sync holds
 // fused_sync_ints(R, E, phases) int32 (phases = 2 forward, 3 backward) that must be
-// zero when the kernel starts; a dependent tile waits at most about kFfnSpinLimit
-// sleeps of 512 cycles (about 2 s) for the previous phase's tiles of its rows, which
-// take tens of microseconds unless other work holds the compute units that long: the
-// bound trades a hang of the whole GPU for a wrong result in that case.
+// zero when the kernel starts: [0, 8) per-XCD tile counters, word kSyncErrWord the
+// error word, then from kSyncHead one counter per M tile for every phase that a later
+// phase waits on.  A dependent tile waits at most about kFfnSpinLimit sleeps of 512
+// cycles (about 2 s) for the previous phase's tiles of its rows, which take tens of
+// microseconds unless other work holds the compute units that long.  A tile that
+// reaches the bound sets the error word to 1 and writes its output rows as NaN, so the
+// failure is visible (moe_fused_status) instead of a hang of the whole GPU.
 constexpr uint32_t kFfnSpinLimit = 1u << 22;
-inline int fused_sync_ints(int R, int E, int phases) { return 8 + (phases - 1) * (R / 256 + E); }
+constexpr int kSyncErrWord = 8;
+constexpr int kSyncHead = 16;
+inline int fused_sync_ints(int R, int E, int phases) { return kSyncHead + (phases - 1) * (R / 256 + E); }
 inline int ffn_sync_ints(int R, int E) { return fused_sync_ints(R, E, 2); }
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
                            const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
@@ -105,8 +112,11 @@ hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, 
 hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16_t* dh, const uint16_t* xe,
                                  const uint16_t* w1, uint16_t* dab, const uint16_t* w1t, uint16_t* dxe,
                                  const int32_t* offsets, int32_t* sync, int R, int E, int d, int H, hipStream_t s);
-// Test hook: nonzero makes every dependent tile of the fused GEMMs take the wait-and-restart path.
+// Test hooks of the fused GEMMs: force_wait nonzero makes every dependent tile take the
+// wait-and-restart path; give_up nonzero makes every such wait end at once as if its bound
+// had been reached (error word raised, the tile's output written as NaN).
 void set_ffn_force_wait(int on);
+void set_ffn_give_up(int on);
 // p[0, n) := 0 (a fill kernel, so that callers may capture it in a graph).
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 

@@ -113,10 +113,26 @@ def test_gemm_grid_cap_range(lib, cap, code):
     assert lib.moe_set_gemm_grid_cap(0) == 0
 
 
-@pytest.mark.parametrize("flags,code", [(0, 0), (1, 0), (2, -7), (-1, -7)])
+@pytest.mark.parametrize("flags,code", [(0, 0), (1, 0), (2, 0), (3, 0), (4, -7), (-1, -7)])
 def test_test_flags_range(lib, flags, code):
     assert lib.moe_set_test_flags(flags) == code
     assert lib.moe_set_test_flags(0) == 0
+
+
+def test_fused_status_host_checks(lib):
+    # argument checks run on the host before any device access
+    p = B.problem(64, 128, 8, 2, 128, "bf16", logits_given=True)
+    st = ctypes.c_int32(123)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_fused_status(ctypes.byref(p), None, 1 << 20, 0, ctypes.byref(st), None) == -1
+    assert lib.moe_fused_status(ctypes.byref(p), fake, 1 << 20, 0, None, None) == -1
+    assert lib.moe_fused_status(ctypes.byref(p), fake, 1 << 20, 5, ctypes.byref(st), None) == -7
+    assert lib.moe_fused_status(ctypes.byref(p), fake, 16, 0, ctypes.byref(st), None) == -4
+    assert lib.moe_fused_status(ctypes.byref(p), fake, 16, 1, ctypes.byref(st), None) == -4
+    # no fused launch for this shape (d, H >= 128 needed): OK without touching the device
+    small = B.problem(64, 64, 8, 2, 64, "bf16", logits_given=True)
+    assert lib.moe_fused_status(ctypes.byref(small), fake, 1 << 20, 0, ctypes.byref(st), None) == 0
+    assert st.value == 0
 
 
 def test_route_noalloc_host_checks(lib):
