@@ -160,6 +160,18 @@ def _combine_bwd_ungated(dy, ye, gate, pos, act):
     return _orig_combine_backward(dy, ye, np.ones_like(np.asarray(gate, np.float64)), pos, act)
 
 
+def _weights_blocked_along_n(w_gate, w_up, w_down, e, act):
+    # MXFP8 weight blocks taken along the GEMM output axis instead of its contraction axis
+    wg, wu, wd = (np.asarray(w[e], np.float64) for w in (w_gate, w_up, w_down))
+    if act == "mxfp8":
+        wg, wu, wd = (MX.fake_quantize(w, axis=1) for w in (wg, wu, wd))
+    return wg, wu, wd
+
+
+WEIGHT_PINS = [
+    lambda gd: P.test_mxfp8_weights_blocked_along_contraction_axis(),
+]
+
 BACKWARD_PINS = [
     lambda gd: [PB.test_backward_matches_finite_differences(*c, learned) for c in
                 [(5, 4, 4, 2, 3, 11), (4, 4, 5, 1, 3, 13)] for learned in (False, True)],
@@ -204,6 +216,7 @@ MUTATIONS = [
     ("E4M3 ties rounded away from zero", MX, "e4m3_round", _round_away, MX_PINS),
     ("ceil-based shared exponent", MX, "shared_exponent", _shared_exp_ceil, MX_PINS),
     ("FNUZ decode instead of OCP FN", MX, "e4m3_decode", _decode_fnuz, MX_PINS),
+    ("MXFP8 weights blocked along the output axis", O, "expert_weights", _weights_blocked_along_n, WEIGHT_PINS),
     ("SiLU gradient taken as the sigmoid", BW, "silu_grad", _silu_grad_sigmoid_only, BACKWARD_PINS),
     ("gate and up weight gradients swapped", BW, "expert_backward", _expert_bwd_swapped_wgrads, BACKWARD_PINS),
     ("dxe without the up projection's share", BW, "expert_backward", _expert_bwd_dxe_gate_only, BACKWARD_PINS),

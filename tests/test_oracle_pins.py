@@ -475,3 +475,24 @@ def test_router_stats_scalar_can_fall_while_imbalance_stays():
     # with all rows on expert 0, lbl = E * P_0 exactly
     p0 = math.exp(0.5) / (math.exp(0.5) + 3.0)
     assert abs(b["lbl"] - E * p0) < 1e-14
+
+
+def test_mxfp8_weights_blocked_along_contraction_axis():
+    """MXFP8 expert weights are quantised in blocks of 32 along each GEMM's
+    contraction axis: d for W_gate / W_up [d, H], H for W_down [H, d] (axis 0
+    of each).  Hand-built 32 x 32 matrices, all v = 11 * 2^-10 except 384 at
+    [0, 0]: the block holding 384 has shared exponent floor(log2 384) - 8 = 0,
+    so its other entries go to the subnormal grid m * 2^-9, where v / 2^-9 =
+    5.5 is a tie that rounds to the even 6 (6 * 2^-9); every other block has
+    amax v, shared exponent floor(log2 v) - 8 = -15, and v / 2^-15 = 352 is an
+    E4M3 value, so v stays exact.  Blocking along the contraction axis
+    coarsens column 0 below the 384; blocking along the output axis would
+    coarsen row 0 instead."""
+    v = 11 * 2.0 ** -10
+    w = np.full((1, 32, 32), v)
+    w[0, 0, 0] = 384.0
+    for q in O.expert_weights(w, w.copy(), w.copy(), 0, "mxfp8"):
+        assert q[0, 0] == 384.0
+        assert np.all(q[1:, 0] == 6 * 2.0 ** -9), "the contraction-axis block of [0, 0] is not coarsened"
+        assert np.all(q[0, 1:] == v), "an output-axis block was coarsened"
+        assert np.all(q[1:, 1:] == v)
