@@ -304,7 +304,8 @@ def forward_tokens(x, idx, gate, tokens, act: str, w_gate, w_up, w_down) -> np.n
 
     Each (token, slot) row passes through its expert independently of every
     other row, so y[t] depends only on x[t], the token's routing and the
-    weights; this evaluates the same steps 4-6 for the listed tokens.
+    weights; this evaluates the same steps 4-6 for the listed tokens, the rows
+    routed to one expert together (one expert's weights at a time).
     Returns [len(tokens), d] in the output storage type.
     """
     x = np.asarray(x, dtype=np.float64)
@@ -315,13 +316,11 @@ def forward_tokens(x, idx, gate, tokens, act: str, w_gate, w_up, w_down) -> np.n
     if act == "mxfp8":
         rows = mxfp8.fake_quantize(rows, axis=1)
     k = idx.shape[1]
+    sel = idx[tokens]                                   # [n, k] experts of the listed tokens
     ye = np.zeros((len(tokens), k, x.shape[1]), dtype=np.float64)
-    cache = {}
-    for i, t in enumerate(tokens):
-        for j in range(k):
-            e = int(idx[t, j])
-            if e not in cache:
-                cache[e] = expert_weights(w_gate, w_up, w_down, e, act)
-            ye[i, j] = expert_ffn(rows[i:i + 1], *cache[e], act)[0]
+    for e in np.unique(sel):
+        ii, jj = np.nonzero(sel == e)
+        wg, wu, wd = expert_weights(w_gate, w_up, w_down, int(e), act)
+        ye[ii, jj] = expert_ffn(rows[ii], wg, wu, wd, act)
     y = np.einsum("tk,tkd->td", gate[tokens], ye)
     return store(y, out_dtype(act))

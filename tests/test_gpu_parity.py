@@ -299,12 +299,26 @@ def _sample_tokens(T, seed=0):
     return np.unique(np.concatenate([np.arange(min(8, T)), np.arange(max(0, T - 8), T), mid])).astype(np.int64)
 
 
+def _tile_tokens(offsets, row_token, T, block=128, seed=0):
+    """Tokens that cover every `block`-row piece of every expert segment (one
+    routed row drawn from each piece, so every M tile of the grouped GEMMs is
+    checked), plus the first and last 8 tokens."""
+    rng = np.random.default_rng(seed)
+    toks = [np.arange(min(8, T)), np.arange(max(0, T - 8), T)]
+    for e in range(len(offsets) - 1):
+        for r0 in range(int(offsets[e]), int(offsets[e + 1]), block):
+            r1 = min(r0 + block, int(offsets[e + 1]))
+            toks.append(np.array([row_token[int(rng.integers(r0, r1))]]))
+    return np.unique(np.concatenate(toks)).astype(np.int64)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name", W.CONFIG_ORDER)
 def test_full_size_config(name):
     """The five block configurations at full size, run exactly as the benchmark
     runs them (moe_forward with packed weights): routing checked bit-exactly on
-    every token, y on sampled tokens against the oracle."""
+    every token, y against the oracle on tokens that cover every 128-row piece
+    of every expert segment (so every output tile of both grouped GEMMs)."""
     w = W.CONFIGS[name]
     print(f"[full] {w.describe()}", flush=True)
     host, dev = device_inputs(w)
@@ -323,12 +337,47 @@ def test_full_size_config(name):
         L = check_logits(w, host, f.logits)
     idx, gate, counts, offsets, pos = check_routing(w, gpu, L)
     check_router_stats(w, f.router_stats, L, counts)
-    toks = _sample_tokens(w.T)
+    _, _, _, row_token = O.route_metadata(idx, w.E)
+    toks = _tile_tokens(offsets, row_token, w.T)
+    print(f"[full] y checked on {len(toks)} tokens", flush=True)
     ref = O.forward_tokens(W.as_f64(host["x"]), idx, gate, toks, w.act, _LazyF64(host["w_gate"]),
                            _LazyF64(host["w_up"]), _LazyF64(host["w_down"]))
     check_y(w.act, _f64(f.y)[toks], ref)
     yall = _f64(f.y)
     assert np.all(np.isfinite(yall))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", [n for n in W.CONFIG_ORDER if n != "tiny_f32"])
+def test_full_size_dispatch_bitexact(name):
+    """The whole dispatched buffer of each large block, through moe_route and
+    moe_dispatch at full size: bf16 rows equal x[row_token] bit for bit; MXFP8
+    codes and scales equal the oracle quantiser's for every row."""
+    w = W.CONFIGS[name]
+    print(f"[full dispatch] {w.describe()}", flush=True)
+    host, dev = device_inputs(w)
+    p = problem_of(w)
+    r = B.route(p, x=dev["x"], w_router=dev["w_router"], logits=dev["logits"])
+    xe, xs = B.dispatch(p, dev["x"], r["pos"])
+    torch.cuda.synchronize()
+    L = _f64(r["logits"]) if w.router == "learned" else W.as_f64(host["logits"])
+    idx, _ = O.route(L, w.k)
+    _, _, pos, row_token = O.route_metadata(idx, w.E)
+    assert np.array_equal(_np(r["row_token"]), row_token), "row_token"
+    if w.act != "mxfp8":
+        rt = torch.from_numpy(row_token.astype(np.int64)).to(DEV)
+        assert torch.equal(xe, dev["x"][rt]), "dispatched rows differ from x[row_token]"
+        return
+    q_gpu = _np(xe)
+    s_gpu = scales_rowmajor(_np(xs))
+    x64 = W.as_f64(host["x"])
+    for t0 in range(0, w.T, 4096):
+        t1 = min(w.T, t0 + 4096)
+        q, sc = MX.quantize(x64[t0:t1], axis=1)
+        for j in range(w.k):
+            rows = pos[t0:t1, j]
+            assert np.array_equal(q_gpu[rows], q), f"MXFP8 codes, tokens {t0}..{t1} slot {j}"
+            assert np.array_equal(s_gpu[rows], sc), f"MXFP8 scales, tokens {t0}..{t1} slot {j}"
 
 
 # ----------------------------------------------------------------------------- MXFP8 packing
