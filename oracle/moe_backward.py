@@ -31,20 +31,21 @@ the gradients below are the chain rule applied to the forward this package's
     dx[t] = sum_j dxe[pos[t, j]]  (+ dL[t] W_r^T for the learned router)
     dW_r = x^T dL
 
-Storage points mirror the forward's: every activation-sized intermediate that
-the library keeps in memory (dye, the recomputed a and b, dh, da and db, dxe
-and dx) is rounded to the activation storage type where it is stored, while
-weight gradients, router gradients and dgate are float32.  The recomputed a
-and b are rounded to the activation type (the forward never stored them);
-h is recomputed exactly as the forward computed it.  With ``act='f64'`` no
+Precision: the pages fix no rounding points for the backward, so the chain
+rule above runs in float64 without rounding any intermediate (dgate, dye, the
+recomputed a and b, dh, da, db, dxe).  What enters as stored is what the
+forward stored: the dispatched rows xe, h (rounded to the forward's h storage
+type, as the forward oracle rounds it) and ye, and the inputs themselves.
+Only the outputs are rounded, to their declared types: dx to the activation
+type, dlogits and the weight gradients to float32.  With ``act='f64'`` no
 rounding happens anywhere (used by the finite-difference pins).
 
 MXFP8 blocks: the report found that MXFP8 weight gradients are fastest as a
 dequantise followed by bf16 grouped GEMMs (Evidence 7); the backward here does
 the whole block that way.  The saved activations are the forward's MXFP8
 values (exact in bf16), the weights are the forward's MXFP8 weight values
-(the caller passes them, e.g. from ``moe_oracle.expert_weights``), and every
-activation-sized gradient is stored in bf16.
+(the caller passes them, e.g. from ``moe_oracle.expert_weights``), and dx is
+stored in bf16.
 """
 from __future__ import annotations
 
@@ -55,15 +56,16 @@ from . import mxfp8
 
 
 def store(v, act: str) -> np.ndarray:
-    """Activation-gradient storage of the backward ('f64' keeps float64
-    exactly; MXFP8 blocks store their gradients in bf16)."""
+    """Storage of the input gradient dx ('f64' keeps float64 exactly; MXFP8
+    blocks store it in bf16)."""
     if act == "f64":
         return np.asarray(v, dtype=np.float64)
     return F.store(v, "bf16" if act == "mxfp8" else act)
 
 
 def store_f32(v, act: str) -> np.ndarray:
-    """float32 storage of gradients that are float32 for every activation type."""
+    """float32 storage of the outputs that are float32 for every activation
+    type (dlogits, weight gradients)."""
     if act == "f64":
         return np.asarray(v, dtype=np.float64)
     return F.round_f32(v)
@@ -109,20 +111,22 @@ def forward_f64(x, n_experts: int, k: int, w_gate, w_up, w_down, w_router=None, 
 
 
 def combine_backward(dy, ye, gate, pos, act: str):
-    """dgate[t, j] = dy[t] . ye[pos[t, j]] (float32) and dye[pos[t, j]] = gate[t, j] dy[t]."""
+    """dgate[t, j] = dy[t] . ye[pos[t, j]] and dye[pos[t, j]] = gate[t, j] dy[t] (exact).
+    ``act`` is unused: both are intermediates of the chain rule."""
     dy = np.asarray(dy, dtype=np.float64)
     ye = np.asarray(ye, dtype=np.float64)
     gate = np.asarray(gate, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.int64)
     T, k = pos.shape
-    dgate = store_f32(np.einsum("td,tkd->tk", dy, ye[pos]), act)
+    dgate = np.einsum("td,tkd->tk", dy, ye[pos])
     dye = np.zeros((T * k, dy.shape[1]))
-    dye[pos.reshape(-1)] = store(gate[:, :, None] * dy[:, None, :], act).reshape(T * k, -1)
+    dye[pos.reshape(-1)] = (gate[:, :, None] * dy[:, None, :]).reshape(T * k, -1)
     return dgate, dye
 
 
 def router_backward(dgate, gate, idx, n_experts: int, act: str) -> np.ndarray:
-    """dL [T, E] through the softmax over the selected logits; zero elsewhere."""
+    """dL [T, E] through the softmax over the selected logits; zero elsewhere
+    (the dlogits output, stored float32)."""
     dgate = np.asarray(dgate, dtype=np.float64)
     gate = np.asarray(gate, dtype=np.float64)
     idx = np.asarray(idx, dtype=np.int64)
@@ -137,20 +141,19 @@ def router_backward(dgate, gate, idx, n_experts: int, act: str) -> np.ndarray:
 def expert_backward(rows, dye_rows, wg, wu, wd, act: str):
     """Backward of one expert's SwiGLU FFN on its rows.
 
-    Returns (drows, dwg, dwu, dwd): drows in activation storage, weight
-    gradients float32.  a and b are recomputed from the rows.
+    Returns (drows, dwg, dwu, dwd): drows (the rows' share of dxe) exact,
+    weight gradients float32.  a and b are recomputed exactly from the rows; h
+    is the value the forward stored.
     """
-    a_exact = rows @ wg
-    b_exact = rows @ wu
-    h = F.silu(a_exact) * b_exact
+    a = rows @ wg
+    b = rows @ wu
+    h = F.silu(a) * b
     if act != "f64":
         h = F.store(h, F.intermediate_dtypes(act)[0])   # as the forward stored it (MXFP8: blocks along H)
-    a = store(a_exact, act)
-    b = store(b_exact, act)
-    dh = store(dye_rows @ wd.T, act)
-    da = store(dh * b * silu_grad(a), act)
-    db = store(dh * F.silu(a), act)
-    drows = store(da @ wg.T + db @ wu.T, act)
+    dh = dye_rows @ wd.T
+    da = dh * b * silu_grad(a)
+    db = dh * F.silu(a)
+    drows = da @ wg.T + db @ wu.T
     return drows, store_f32(rows.T @ da, act), store_f32(rows.T @ db, act), store_f32(h.T @ dye_rows, act)
 
 
@@ -224,9 +227,8 @@ def backward_tokens(x, dy, idx, gate, tokens, n_experts: int, act: str, w_gate, 
             wg, wu, wd = cache[e]
             ye = F.expert_ffn(rows[i:i + 1], wg, wu, wd, act)[0]
             dgate[i, j] = np.dot(dy[t], ye)
-            dye = store(gate[t, j] * dy[t], act)
+            dye = gate[t, j] * dy[t]
             drows[i, j] = expert_backward(rows[i:i + 1], dye[None, :], wg, wu, wd, act)[0][0]
-    dgate = store_f32(dgate, act)
     dL = router_backward(dgate, gate[tokens], idx[tokens], n_experts, act)
     dx = drows.sum(axis=1)
     if w_router is not None:
@@ -244,15 +246,13 @@ def weight_grad_columns(rows, dye_rows, wg, wu, wd, act: str, hcols) -> dict:
     rows = np.asarray(rows, np.float64)
     dye_rows = np.asarray(dye_rows, np.float64)
     hc = np.asarray(hcols, np.int64)
-    a_exact = rows @ wg[:, hc]
-    b_exact = rows @ wu[:, hc]
-    h = F.silu(a_exact) * b_exact
+    a = rows @ wg[:, hc]
+    b = rows @ wu[:, hc]
+    h = F.silu(a) * b
     if act != "f64":
         h = F.store(h, F.intermediate_dtypes(act)[0])
-    a = store(a_exact, act)
-    b = store(b_exact, act)
-    dh = store(dye_rows @ wd[hc, :].T, act)
-    da = store(dh * b * silu_grad(a), act)
-    db = store(dh * F.silu(a), act)
+    dh = dye_rows @ wd[hc, :].T
+    da = dh * b * silu_grad(a)
+    db = dh * F.silu(a)
     return dict(dw_gate=store_f32(rows.T @ da, act), dw_up=store_f32(rows.T @ db, act),
                 dw_down=store_f32(h.T @ dye_rows, act))
