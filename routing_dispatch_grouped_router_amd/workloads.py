@@ -98,6 +98,18 @@ SMALL = {
     "edge_mxfp8_empty": Workload("edge_mxfp8_empty", T=70, d=128, E=8, k=2, H=128,
                                  act=ACT_MXFP8, router="random", seed=2012,
                                  empty_experts=(1, 6), outlier_frac=0.05),
+    # learned routers whose expert count is not a multiple of 8 (W_r transposed first) or
+    # spans several 16-expert tiles of the router GEMM
+    "small_bf16_learned_e12": Workload("small_bf16_learned_e12", T=600, d=256, E=12, k=3, H=128,
+                                       act=ACT_BF16, router="learned", seed=2016),
+    "small_bf16_learned_e20": Workload("small_bf16_learned_e20", T=700, d=384, E=20, k=4, H=128,
+                                       act=ACT_BF16, router="learned", seed=2017),
+    "small_bf16_learned_e64": Workload("small_bf16_learned_e64", T=900, d=256, E=64, k=6, H=128,
+                                       act=ACT_BF16, router="learned", seed=2018),
+    "small_mxfp8_learned_e20": Workload("small_mxfp8_learned_e20", T=500, d=256, E=20, k=2, H=128,
+                                        act=ACT_MXFP8, router="learned", seed=2019, outlier_frac=0.01),
+    "small_mxfp8_learned_e64": Workload("small_mxfp8_learned_e64", T=400, d=384, E=64, k=4, H=256,
+                                        act=ACT_MXFP8, router="learned", seed=2020),
     # the largest expert count and top-k the library supports (1024, 16): many tiny segments
     "edge_max_E_k": Workload("edge_max_E_k", T=700, d=64, E=1024, k=16, H=64, act=ACT_BF16,
                              router="random", seed=2013),
