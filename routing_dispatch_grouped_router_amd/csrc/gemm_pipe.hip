@@ -140,9 +140,10 @@ struct TileCoord {
 };
 
 template <int BM, int BN>
-__device__ __forceinline__ TileCoord tile_coord(int tile, int NT, const int* s_tstart, int E,
+__device__ __forceinline__ TileCoord tile_coord(int tile, int MT, int NT, const int* s_tstart, int E,
                                                 const int32_t* __restrict__ offsets) {
-    const int mt = tile / NT, nt = tile - mt * NT;
+    int mt, nt;
+    block_tile(tile, MT, NT, mt, nt);
     TileCoord c;
     c.e = __builtin_amdgcn_readfirstlane(tile_expert(s_tstart, E, mt));
     const int o0 = offsets[c.e], o1 = offsets[c.e + 1];
@@ -527,9 +528,9 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
     const int drow = lane >> 2;
     const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
 
-    TileCoord c0 = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
-    if (tile + G < total) c1 = tile_coord<BM, BN>(tile + G, NT, s_tstart, E, offsets);
-    if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
+    TileCoord c0 = tile_coord<BM, BN>(tile, MT, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
+    if (tile + G < total) c1 = tile_coord<BM, BN>(tile + G, MT, NT, s_tstart, E, offsets);
+    if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
     int kbase = 0;
     const int qa = nk >= 4 ? 1 : 2;   // tiles ahead reached by the last four K-tiles' prefetches
     const int head = max(nk - 4, 0);  // K-tiles whose prefetch stays in the current tile
@@ -619,7 +620,7 @@ void gemm_bf16_pipe_kernel(const uint16_t* __restrict__ A, const uint16_t* __res
         tile += G;
         c0 = c1;
         c1 = c2;
-        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
+        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
         kbase += nk;
     }
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
@@ -745,9 +746,10 @@ __device__ __forceinline__ FfnTile ffn_tile(const FusedParams& p, int id, int MT
     for (int q = 0; q < p.nph; ++q) {
         const int nt_per = (p.ph[q].N + BN - 1) / BN;
         if (j < MT * nt_per) {
+            int nt;
             c.phase = q;
-            c.mt = j / nt_per;
-            c.n0 = (j - c.mt * nt_per) * BN;
+            block_tile(j, MT, nt_per, c.mt, nt);
+            c.n0 = nt * BN;
             break;
         }
         j -= MT * nt_per;
@@ -1041,13 +1043,14 @@ __device__ __forceinline__ FfnTile ffn_tile(int id, int total, int T1, int NT1, 
     if (id >= total) return c;
     const bool two = id >= T1;
     const int j = two ? id - T1 : id, nt_per = two ? NT2 : NT1;
-    c.mt = j / nt_per;
+    int nt;
+    block_tile(j, T1 / NT1, nt_per, c.mt, nt);
     c.phase = two ? 1 : 0;
     c.e = __builtin_amdgcn_readfirstlane(tile_expert(s_tstart, E, c.mt));
     const int o0 = offsets[c.e], o1 = offsets[c.e + 1];
     c.row0 = o0 + (c.mt - __builtin_amdgcn_readfirstlane(s_tstart[c.e])) * BM;
     c.rows = min(BM, o1 - c.row0);
-    c.n0 = (j - c.mt * nt_per) * BN;
+    c.n0 = nt * BN;
     return c;
 }
 
@@ -1066,15 +1069,34 @@ __device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, 
     return s;
 }
 
+// K-tiles of 64 bf16 values.  A ring stage holds 128 bytes of K per row, so
+// every global -> LDS DMA instruction moves 8 whole 128-byte lines (8 lanes per
+// row) instead of 16 half lines: the L1 -> L2 path then carries twice the bytes
+// per request, which is what bounds this kernel (its data movement alone takes
+// most of its time).  Two stages of (BM + BN) x 128 bytes, four 16-wide
+// k-steps per K-tile.  Chunk c of row r sits at chunk c ^ ((r >> 1) & 7) of
+// the row, so the 16 rows read by each 16-lane group of a fragment load fall
+// on 64 distinct banks, and the 8 lanes of one row of a DMA write 8 distinct
+// chunks.
+template <class TL>
+struct Ring128 {
+    static constexpr int A_DMA = TL::BM / 8 / TL::NW, B_DMA = TL::BN / 8 / TL::NW;   // 1 KB DMAs per wave
+    static constexpr int P = A_DMA + B_DMA;                                            // per wave per K-tile
+    static constexpr int SC = (TL::BM + TL::BN) * 8;                                   // 16-byte chunks per stage
+    static_assert(TL::BM % (8 * TL::NW) == 0 && TL::BN % (8 * TL::NW) == 0 && A_DMA % 2 == 0 && B_DMA % 2 == 0,
+                  "DMA blocks of 8 rows, an even number per wave");
+};
+
 template <class TL>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_bf16_ffn_kernel(FfnParams p) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
-    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
-    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
-    static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
+    constexpr int NM = TL::NM, EARLY = TL::EARLY;
+    constexpr int A_DMA = Ring128<TL>::A_DMA, B_DMA = Ring128<TL>::B_DMA, P = Ring128<TL>::P, SC = Ring128<TL>::SC;
+    constexpr int SL = NM - EARLY;   // MFMA slots after the barrier of a K-tile
+    static_assert(NM >= TM + TN && SL >= TM + TN && SL > 0, "one fragment read per MFMA slot");
     constexpr int kObufChunks = 128;   // per wave: 16 rows x 128 bytes of GEMM2 output
-    __shared__ u32x4 ring[TL::STAGES * SC];
+    __shared__ u32x4 ring[2 * SC];
     __shared__ u32x4 obuf[TL::NW * kObufChunks];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
@@ -1085,7 +1107,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     const int MT = build_tile_schedule<BM, NTHR>(p.offsets, p.E, s_tstart, s_scan);
     const int NT1 = (2 * p.H + BN - 1) / BN, NT2 = (p.d + BN - 1) / BN;
     const int T1 = MT * NT1, total = T1 + MT * NT2;
-    const int nk1 = p.d / 32, nk2 = p.H / 32;
+    const int nk1 = p.d / 64, nk2 = p.H / 64;
     const int G = gridDim.x, GX = G / kXcds;   // G is a multiple of 8
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
     const int k32 = total / 256;
@@ -1096,12 +1118,20 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t ring_lds = lds_addr(ring);
     const int wm = wave / TL::WN, wn = wave % TL::WN;
-    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
-    const int arow = (wm * TL::WROWS + (lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 4;
-    const int a0 = arow + ((0 + half) ^ fsw), a1 = arow + ((2 + half) ^ fsw);
-    const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
-    const int drow = lane >> 2;
-    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    // fragments: lane row (lane & 31) of its 32-row block, chunk 2 s + half of k-step s, swizzled
+    const int key = ((lane & 31) >> 1) & 7, half = lane >> 5;
+    const int arow = (wm * TL::WROWS + (lane & 31)) * 8, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 8;
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        aoff[s] = arow + ((2 * s + half) ^ key);
+        boff[s] = brow + ((2 * s + half) ^ key);
+    }
+    // DMA lanes: row lane / 8 of an 8-row block, physical chunk lane % 8; block i of a
+    // wave starts at row 8 (wave * A_DMA + i), so the row's swizzle key is 4 (i & 1) + (lane / 8) / 2
+    const int drow = lane >> 3;
+    const uint32_t dch0 = (uint32_t)((lane & 7) ^ (drow >> 1)) * 16u;
+    const uint32_t dch1 = (uint32_t)((lane & 7) ^ (4 + (drow >> 1))) * 16u;
     int32_t* const done = p.sync + kSyncHead;
     const __amdgpu_buffer_rsrc_t hrsrc =
         __builtin_amdgcn_make_buffer_rsrc(p.h, 0, (int)((uint32_t)p.R * (uint32_t)p.H * 2u), kRawBufferWord3);
@@ -1116,23 +1146,26 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     FfnTile c1 = ffn_tile<BM, BN>(id1, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
     int kbase = 0;
 
+    // DMA i of global K-tile g (A blocks, then B blocks) from src
     auto dma = [&](const FfnSrc& src, int g, int i) {
         const int kt = (g - kbase) * src.mul + src.add;
-        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        const uint32_t st = ring_lds + (uint32_t)(g & 1) * SC * 16u;
+        const uint32_t dch = (i & 1) ? dch1 : dch0;
         if (i < A_DMA) {
-            const int r = 16 * (wave * A_DMA + i) + drow;
-            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
+            const int r = 8 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dch + (uint32_t)kt * 128u;
             dma16(src.a, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
         } else {
             const int j = i - A_DMA;
-            const int r = 16 * (wave * B_DMA + j) + drow;
-            const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
-            dma16(src.b, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+            const int r = 8 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dch + (uint32_t)kt * 128u;
+            dma16(src.b, off, st + BM * 128u + (uint32_t)(wave * B_DMA + j) * 1024u);
         }
     };
-    auto frag = [&](const u32x4* stage, int aoff, int boff, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
-        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
+    // fragment i (A blocks, then B blocks) of k-step s from a stage
+    auto frag = [&](const u32x4* stage, int s, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff[s] + i * 32 * 8]);
+        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff[s] + (i - TM) * 32 * 8]);
     };
     // GEMM2 tile t may start once all NT1 GEMM1 tiles of its M tile are done;
     // false if the bounded wait gave up (error word raised)
@@ -1149,37 +1182,56 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     auto start_stream = [&](const FfnTile& t) {
         const FfnSrc here = ffn_src(p, t, 1, 0);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < P; ++i) dma(here, kbase + g, i);
-        wait_vm<3 * P>();   // the first K-tile landed; 1, 2 and 3 may stay in flight
+        wait_vm<P>();   // the first K-tile landed; the second may stay in flight
         ring_barrier();
 #pragma unroll
-        for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 3) * SC, a0, b0, i, fa0, fb0);
+        for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 1) * SC, 0, i, fa0, fb0);
     };
 
     bool poison = !wait_rows(c0);   // the current tile's rows were not seen complete
     start_stream(c0);
 
+    // One K-tile g, four k-steps: k-steps 0..2 multiply while the next one's
+    // fragments are read; k-step 3 issues a few MFMAs, waits for K-tile g + 1
+    // and joins the barrier (every wave has all of K-tile g in registers by
+    // then, so its stage is free), then, between its remaining MFMAs, starts
+    // the DMAs of K-tile g + 2 into that stage and reads K-tile g + 1's k-step
+    // 0 into set 0.
     auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
-        const u32x4* stage = ring + (g & 3) * SC;
+        const u32x4* stage = ring + (g & 1) * SC;
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             bf_mfma1<TL>(i, fa0, fb0, acc);
-            frag(stage, a1, b1, i, fa1, fb1);
+            frag(stage, 1, i, fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa1, fb1, acc);
+            frag(stage, 2, i, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa0, fb0, acc);
+            frag(stage, 3, i, fa1, fb1);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < EARLY; ++i) bf_mfma1<TL>(i, fa1, fb1, acc);
-        wait_vm<2 * P>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
-        wait_lds();         // this wave's reads of K-tile g are complete
+        wait_vm<0>();   // K-tile g + 1 landed (the only DMAs in flight)
+        wait_lds();     // this wave's reads of K-tile g are complete
         ring_barrier();
-        const u32x4* nstage = ring + ((g + 1) & 3) * SC;
+        const u32x4* nstage = ring + ((g + 1) & 1) * SC;
 #pragma unroll
-        for (int i = 0; i < NM - EARLY; ++i) {
+        for (int i = 0; i < SL; ++i) {
             bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
-            if (i < P) dma(src, g + 4, i);
-            frag(nstage, a0, b0, i, fa0, fb0);
+#pragma unroll
+            for (int j = i * P / SL; j < (i + 1) * P / SL; ++j) dma(src, g + 2, j);
+            frag(nstage, 0, i, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -1194,12 +1246,11 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
         const int nk = c0.phase == 0 ? nk1 : nk2;
-        const int head = nk - 4;
-        // The count of the next tile's M tile is copied into LDS before the
-        // DMAs of K-tile head + 1, so the vmcnt wait of K-tile head - 1 (which
-        // leaves only K-tiles head + 1 and head + 2 in flight) covers it.
-        const bool probe = c1.phase == 1 && head >= 4;
-        const int split = probe ? head - 3 : head;
+        const int head = nk - 2;   // K-tiles whose DMAs (two ahead) stay in the current tile
+        // The count of the next tile's M tile is copied into LDS before K-tile
+        // head - 1's wait, which then covers it.
+        const bool probe = c1.phase == 1 && head >= 1;
+        const int split = probe ? head - 1 : head;
         const FfnSrc here = ffn_src(p, c0, 1, 0);
         for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, acc);
         if (probe && wave == 0) dma4_dev(done, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
@@ -1268,6 +1319,7 @@ template <class TL>
 struct Fp8Extra {
     static constexpr int PS = 2;                // scale DMAs per wave per even K-tile
     static constexpr int SR = TL::BM / TL::NW;  // scale rows per wave and operand
+    static constexpr int OBUF_RR = TL::NW == 4 ? 32 : 16;   // output rows staged per round (LDS budget)
     static_assert(TL::BM == TL::BN && (SR == 32 || SR == 64), "one scale DMA per wave and operand");
 };
 
@@ -1325,10 +1377,10 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 #pragma unroll
             for (int np = 0; np < TL::TN / 2; ++np) {
                 float g[16], u[16];
-                acc_read(acc[mi][2 * np], g);
-                acc_read(acc[mi][2 * np + 1], u);
+                acc_block<TL>(acc[mi][2 * np], g);
+                acc_block<TL>(acc[mi][2 * np + 1], u);
                 const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
-                store_bf16_pair_rows<32>(static_cast<uint16_t*>(C), (size_t)ldc, c.row0 + rb, c.rows - rb,
+                store_bf16_pair_rows<Fp8Extra<TL>::OBUF_RR>(static_cast<uint16_t*>(C), (size_t)ldc, c.row0 + rb, c.rows - rb,
                                          c.n0 + wn * TL::WCOLS + np * 64, N, g, u, obuf);
                 __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
@@ -1337,8 +1389,8 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
             for (int np = 0; np < TL::TN / 2; ++np) {
                 const int pc = c.n0 + wn * TL::WCOLS + np * 64;
                 float v[16], u[16];
-                acc_read(acc[mi][2 * np], v);
-                acc_read(acc[mi][2 * np + 1], u);
+                acc_block<TL>(acc[mi][2 * np], v);
+                acc_block<TL>(acc[mi][2 * np + 1], u);
                 float amax = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -1389,7 +1441,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
     constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
     static_assert(NM - EARLY >= P + PS && NM - EARLY >= TM + TN, "one DMA and one fragment per MFMA step");
-    constexpr int kObufChunks = EPI == 0 ? 256 : 0;   // per wave: 32 rows x 128 bytes of output
+    constexpr int kObufChunks = EPI == 0 ? 8 * Fp8Extra<TL>::OBUF_RR : 0;   // per wave: rows x 128 bytes of output
     __shared__ u32x4 ring[TL::STAGES * SC];
     __shared__ uint32_t sring[4 * (BM + BN)];     // four scale slots: A rows then B rows
     __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
@@ -1422,9 +1474,9 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     // row dword, byte = K block within the pair's four
     const int sa_byte = arow_i * 4 + half, sb_byte = (BM + brow_i) * 4 + half;
 
-    TileCoord c0 = tile_coord<BM, BN>(tile, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
-    if (tile + G < total) c1 = tile_coord<BM, BN>(tile + G, NT, s_tstart, E, offsets);
-    if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
+    TileCoord c0 = tile_coord<BM, BN>(tile, MT, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
+    if (tile + G < total) c1 = tile_coord<BM, BN>(tile + G, MT, NT, s_tstart, E, offsets);
+    if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
     int kbase = 0;   // global K-tile index of the current tile's K-tile 0
 
     const int qa = nk >= 4 ? 1 : 2;   // tiles ahead reached by the last four K-tiles' prefetches
@@ -1522,18 +1574,19 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         // K-tiles go in pairs (kt even: register set 0; kt + 1: set 1), the
         // pair's scales in slot (kt / 2) % 4
         const StreamSrc here{c0, 1, 0};
-        for (int kt = 0; kt < head; kt += 2) {
-            half_step(std::integral_constant<int, 0>{}, kbase + kt, here, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
-            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, here, acc, fa1, fb1, sa1, sb1, fa0, fb0, sa0,
-                      sb0);
-        }
         const bool has = tile + qa * G < total;
         const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
+        for (int kt = 0; kt < head; kt += 2) {
+            half_step(std::integral_constant<int, 0>{}, kbase + kt, here, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1,
+                      sb1);
+            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, here, acc, fa1, fb1, sa1, sb1, fa0, fb0,
+                      sa0, sb0);
+        }
         for (int kt = head; kt < nk; kt += 2) {
             half_step(std::integral_constant<int, 0>{}, kbase + kt, ahead, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1,
                       sb1);
-            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, ahead, acc, fa1, fb1, sa1, sb1, fa0, fb0, sa0,
-                      sb0);
+            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, ahead, acc, fa1, fb1, sa1, sb1, fa0, fb0,
+                      sa0, sb0);
         }
         // set 0 now holds K-tile 0 of the next tile (or unused data after the last)
         fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks);
@@ -1541,7 +1594,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         tile += G;
         c0 = c1;
         c1 = c2;
-        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, NT, s_tstart, E, offsets);
+        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
         kbase += nk;
     }
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left

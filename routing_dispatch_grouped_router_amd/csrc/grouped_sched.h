@@ -6,9 +6,9 @@
 // uneven per-expert shapes run without padding every expert to a common
 // capacity).  Every workgroup derives the same schedule in LDS:
 //   tstart[e] = sum over e' < e of ceil(n_e' / BM)   (M tiles before expert e)
-// and walks linear tile ids  tile = mtile * NT + ntile,  so all tiles of one
-// expert are consecutive and the N tiles sharing one block of rows follow each
-// other.  The grid is persistent (bounded by the CU count times the occupancy,
+// and walks tile ids in block order (block_tile: 4 M tiles x 8 N tiles per
+// block), so the tiles of one expert are consecutive and each run of 32 ids
+// shares 4 row blocks and 8 weight slices.  The grid is persistent (bounded by the CU count times the occupancy,
 // and by the worst-case tile count the host can bound without reading the
 // offsets); workgroup b takes tiles b', b' + G, b' + 2G, ... where b' spreads
 // consecutive ids over one XCD (the hardware deals workgroups round-robin over
@@ -59,6 +59,25 @@ __device__ __forceinline__ int build_tile_schedule(const int32_t* __restrict__ o
     if (tid == NTHREADS - 1) s_tstart[E] = s_scan[NTHREADS - 1];
     __syncthreads();
     return s_tstart[E];
+}
+
+// Tile j of a GEMM with MT x NT output tiles, in block order: blocks of 4 M
+// tiles x 8 N tiles (smaller at the edges), the blocks of one row of 4 M tiles
+// in N order, rows in M order, the tiles of a block M-major.  A persistent
+// grid deals consecutive runs of 32 tile ids to one XCD, so with this order a
+// run is one 4 x 8 block: it reads 4 row blocks of activations and 8 weight
+// slices, the fewest distinct bytes (and L2 misses) for 32 tiles, whatever NT
+// is (M-major ids give 32 / NT row blocks x NT slices when NT is not 8).
+__device__ __forceinline__ void block_tile(int j, int MT, int NT, int& mt, int& nt) {
+    const int mg = j / (4 * NT);
+    const int r = j - mg * 4 * NT;
+    const int mc = min(4, MT - 4 * mg);   // M tiles in this row of blocks
+    const int ng = r / (mc * 8);
+    const int s = r - ng * mc * 8;
+    const int nc = min(8, NT - 8 * ng);   // N tiles in this block
+    const int mi = s / nc;
+    mt = 4 * mg + mi;
+    nt = 8 * ng + (s - mi * nc);
 }
 
 // Expert owning global M tile `mt`: the largest e < E with tstart[e] <= mt
