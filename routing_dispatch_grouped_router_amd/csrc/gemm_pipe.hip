@@ -1300,32 +1300,39 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
 // ============================================================================ MXFP8
 //
 // Operands are E4M3 codes with one E8M0 scale per 32 K values (OCP MX v1.0).
-// A ring stage holds 64 K values per row, consumed by one MFMA per fragment
-// pair.  In that instruction lane l of half h = l / 32 holds, for row l % 32,
-// K values [16 h, 16 h + 16) in its bytes 0..15 and [32 + 16 h, 48 + 16 h) in
-// bytes 16..31, and supplies the scale of K block h: scale block b covers
-// bytes 0..15 of both halves for b = 0 and bytes 16..31 for b = 1 (measured on
-// gfx950).  So a lane's fragment is chunks h and 2 + h of the 64-byte slice,
-// and its scale is that of block 2 kt + h.  Scales come in pairs of K-tiles:
-// with every even K-tile t each wave DMAs, for its SR rows of A and of B, the
-// dword of scale bytes of K blocks 2t .. 2t+3 into a four-slot scale ring.
-// Scale buffers are stored [K/128][rows][4], so those dwords are one
-// contiguous run per wave.  Each lane reads its own scale byte (byte h for an
-// even K-tile, 2 + h for an odd one) zero-extended, and the MFMA takes scale
-// byte 0.  Four waves each own a 128 x 128 block whose 256 accumulators sit in
+// A ring stage holds 128 K values per row (128 bytes, so every DMA instruction
+// moves 8 whole lines, as in the bf16 FFN), consumed as two k-steps of one
+// MFMA per fragment pair.  In that instruction lane l of half h = l / 32 holds,
+// for row l % 32, K values [16 h, 16 h + 16) of the k-step's 64 in its bytes
+// 0..15 and [32 + 16 h, 48 + 16 h) in bytes 16..31, and supplies the scale of
+// the k-step's K block h: scale block b covers bytes 0..15 of both halves for
+// b = 0 and bytes 16..31 for b = 1 (measured on gfx950).  So a lane's fragment
+// of k-step s is chunks 4 s + h and 4 s + 2 + h of the 128-byte row, and its
+// scale is that of block 2 s + h of the K-tile.  Scale buffers are stored
+// [K/128][rows][4]: the four scales of one K-tile of a row form one dword and
+// the dwords of consecutive rows are adjacent, so with every K-tile each wave
+// DMAs, for its SR rows of A and of B, one contiguous run of dwords into the
+// stage's scale slot.  Each lane reads its own scale byte (byte 2 s + h of its
+// row's dword) zero-extended, and the MFMA takes scale byte 0.  Chunk c of row
+// r sits at chunk c ^ ((r >> 1) & 7) of the row (bank-conflict-free fragment
+// reads).  Four waves each own a 128 x 128 block whose 256 accumulators sit in
 // AGPRs, leaving the VGPRs to the 32-byte fragments (fp8 halves the LDS bytes
 // per FLOP, so the larger per-wave block suits it).
 template <class TL>
 struct Fp8Extra {
-    static constexpr int PS = 2;                // scale DMAs per wave per even K-tile
+    static constexpr int PS = 2;                // scale DMAs per wave per K-tile (A rows, B rows)
     static constexpr int SR = TL::BM / TL::NW;  // scale rows per wave and operand
     static constexpr int OBUF_RR = TL::NW == 4 ? 32 : 16;   // output rows staged per round (LDS budget)
+    static constexpr int A_DMA = TL::BM / 8 / TL::NW, B_DMA = TL::BN / 8 / TL::NW;   // 1 KB DMAs per wave
+    static constexpr int P = A_DMA + B_DMA;     // data DMAs per wave per K-tile
+    static constexpr int SC = (TL::BM + TL::BN) * 8;   // 16-byte chunks per stage
     static_assert(TL::BM == TL::BN && (SR == 32 || SR == 64), "one scale DMA per wave and operand");
+    static_assert(A_DMA % 2 == 0 && B_DMA % 2 == 0, "DMA blocks of 8 rows, an even number per wave");
 };
 
-// Fragment mi of A (or ni of B) of one K-tile: chunks h and 2 + h of the
-// lane's row, and the lane's scale byte read on its own (zero-extended, so
-// the MFMA always takes scale byte 0).
+// Fragment mi of A (or ni of B) of one k-step: two 16-byte chunks of the
+// lane's row, and the lane's scale byte read on its own (zero-extended, so the
+// MFMA always takes scale byte 0).
 template <class TL>
 __device__ __forceinline__ void fp8_frag(const u32x4* stage, const uint8_t* sbytes, int off0, int off1, int sbyte,
                                          i32x8& f, int& sc) {
@@ -1420,16 +1427,16 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 
 // The persistent MXFP8 kernel streams K-tiles without a break at tile
 // boundaries: global K-tile g of this workgroup (g = tiles done * nk + kt) goes
-// through ring stage g % 4 and scale slot (g / 2) % 4, and the DMAs of the last
-// four K-tiles of a tile already fetch the first four of the next one.  Each
-// half-iteration handles one K-tile g: a few MFMAs on the fragments in hand,
-// the wait for K-tile g + 1, the barrier (every wave then holds all of K-tile g
-// in registers, so its stage and the previous pair's scale slot are free),
-// and then, one per MFMA, the DMAs of K-tile g + 4 and the fragment reads of
-// K-tile g + 1.  The epilogue runs between the last MFMA of a tile and the
-// first of the next while the next tile's first K-tiles are in flight; its
-// stores count in vmcnt after those DMAs, which only makes the next waits wait
-// longer, never shorter.
+// through ring stage and scale slot g % 2, and the DMAs of the last two
+// K-tiles of a tile already fetch the first two of the next one (or, when a
+// tile has one K-tile, of the tile after).  K-tile g: k-step 0 multiplies
+// while k-step 1's fragments are read; then a few MFMAs of k-step 1, the wait
+// for K-tile g + 1, the barrier (every wave then holds all of K-tile g in
+// registers, so its stage and scale slot are free), and, between the remaining
+// MFMAs, the DMAs of K-tile g + 2 and the reads of K-tile g + 1's k-step 0.
+// The epilogue runs between the last MFMA of a tile and the first of the next
+// while the next tile's first K-tiles are in flight; its stores count in
+// vmcnt after those DMAs, which only makes the next wait wait longer.
 template <class TL, int EPI>   // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
@@ -1438,12 +1445,13 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
                           int ldc, int R) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
-    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
-    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
-    static_assert(NM - EARLY >= P + PS && NM - EARLY >= TM + TN, "one DMA and one fragment per MFMA step");
+    constexpr int A_DMA = Fp8Extra<TL>::A_DMA, B_DMA = Fp8Extra<TL>::B_DMA, P = Fp8Extra<TL>::P;
+    constexpr int SC = Fp8Extra<TL>::SC, ND = P + PS;
+    constexpr int NM = TL::NM, EARLY = TL::EARLY, SL = NM - EARLY;
+    static_assert(SL >= TM + TN && SL > 0, "one fragment read per MFMA slot");
     constexpr int kObufChunks = EPI == 0 ? 8 * Fp8Extra<TL>::OBUF_RR : 0;   // per wave: rows x 128 bytes of output
-    __shared__ u32x4 ring[TL::STAGES * SC];
-    __shared__ uint32_t sring[4 * (BM + BN)];     // four scale slots: A rows then B rows
+    __shared__ u32x4 ring[2 * SC];
+    __shared__ uint32_t sring[2 * (BM + BN)];     // two scale slots: A rows then B rows
     __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
@@ -1453,7 +1461,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     const int total = MT * NT;
     const int G = gridDim.x;
     const int kb = K / 32;            // scale bytes per row
-    const int nk = K / 64;            // K-tiles per tile (even: K % 128 == 0)
+    const int nk = K / 128;           // K-tiles per tile
     int tile = xcd_slot(blockIdx.x, G);
     if (tile >= total) return;
 
@@ -1462,16 +1470,24 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t ring_lds = lds_addr(ring), sring_lds = lds_addr(sring);
     const int wm = wave / TL::WN, wn = wave % TL::WN;
-    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
+    const int key = ((lane & 31) >> 1) & 7, half = lane >> 5;
     const int arow_i = wm * TL::WROWS + (lane & 31), brow_i = wn * TL::WCOLS + (lane & 31);
-    const int a0 = arow_i * 4 + (half ^ fsw), a1 = arow_i * 4 + ((2 + half) ^ fsw);
-    const int b0 = (BM + brow_i) * 4 + (half ^ fsw), b1 = (BM + brow_i) * 4 + ((2 + half) ^ fsw);
-    const int drow = lane >> 2;
-    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    // fragment chunks of k-step s: 4 s + h and 4 s + 2 + h, swizzled
+    int a_lo[2], a_hi[2], b_lo[2], b_hi[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        a_lo[s] = arow_i * 8 + ((4 * s + half) ^ key);
+        a_hi[s] = arow_i * 8 + ((4 * s + 2 + half) ^ key);
+        b_lo[s] = (BM + brow_i) * 8 + ((4 * s + half) ^ key);
+        b_hi[s] = (BM + brow_i) * 8 + ((4 * s + 2 + half) ^ key);
+    }
+    // DMA lanes: row lane / 8 of an 8-row block, physical chunk lane % 8 (key 4 (i & 1) + (lane / 8) / 2)
+    const int drow = lane >> 3;
+    const uint32_t dch0 = (uint32_t)((lane & 7) ^ (drow >> 1)) * 16u;
+    const uint32_t dch1 = (uint32_t)((lane & 7) ^ (4 + (drow >> 1))) * 16u;
     const int srow = SR * wave + (lane & (SR - 1));    // scale DMA row of this lane
     const bool slane = lane < SR;
-    // scale byte of this lane in a slot for an even K-tile (+2 for an odd one):
-    // row dword, byte = K block within the pair's four
+    // scale byte of this lane in a slot for k-step 0 (+2 for k-step 1): row dword, byte = K block h
     const int sa_byte = arow_i * 4 + half, sb_byte = (BM + brow_i) * 4 + half;
 
     TileCoord c0 = tile_coord<BM, BN>(tile, MT, NT, s_tstart, E, offsets), c1 = c0, c2 = c0;
@@ -1479,88 +1495,89 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
     int kbase = 0;   // global K-tile index of the current tile's K-tile 0
 
-    const int qa = nk >= 4 ? 1 : 2;   // tiles ahead reached by the last four K-tiles' prefetches
-    const int head = max(nk - 4, 0);  // K-tiles whose prefetch stays in the current tile (even)
+    const int qa = nk >= 2 ? 1 : 2;   // tiles ahead reached by the last two K-tiles' prefetches
+    const int head = max(nk - 2, 0);  // K-tiles whose prefetch stays in the current tile
 
-    // DMA step i of global K-tile g from src: A rows, then B rows, then (g
-    // even) the two scale dwords.
+    // DMA step i of global K-tile g from src: A blocks, then B blocks, then
+    // the two scale dword runs (a stand-in K-tile nk - 1 maps to the last plane too)
     auto dma = [&](const StreamSrc& src, int g, int i) {
         const TileCoord& t = src.t;
         const int kt = (g - kbase) * src.mul + src.add;
-        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        const uint32_t st = ring_lds + (uint32_t)(g & 1) * SC * 16u;
+        const uint32_t dch = (i & 1) ? dch1 : dch0;
         if (i < A_DMA) {
-            const int r = 16 * (wave * A_DMA + i) + drow;
-            const uint32_t off = (uint32_t)(t.row0 + min(r, t.rows - 1)) * (uint32_t)K + dchunk + (uint32_t)kt * 64u;
+            const int r = 8 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(t.row0 + min(r, t.rows - 1)) * (uint32_t)K + dch + (uint32_t)kt * 128u;
             dma16(A, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
-        } else if (i < A_DMA + B_DMA) {
+        } else if (i < P) {
             const int j = i - A_DMA;
-            const int r = 16 * (wave * B_DMA + j) + drow;
-            const uint32_t off = (uint32_t)min(t.n0 + r, N - 1) * (uint32_t)K + dchunk + (uint32_t)kt * 64u;
-            dma16(B + (size_t)t.e * N * K, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+            const int r = 8 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(t.n0 + r, N - 1) * (uint32_t)K + dch + (uint32_t)kt * 128u;
+            dma16(B + (size_t)t.e * N * K, off, st + BM * 128u + (uint32_t)(wave * B_DMA + j) * 1024u);
         } else {
-            // scale planes [K/128][rows][4]: the pair's dword of each row (a
-            // stand-in K-tile nk - 1 maps to the last plane too)
-            const uint32_t slot = sring_lds + (uint32_t)((g >> 1) & 3) * (BM + BN) * 4u;
-            const uint32_t plane = (uint32_t)kt >> 1;
+            const uint32_t slot = sring_lds + (uint32_t)(g & 1) * (BM + BN) * 4u;
             if (SR == 64 || slane) {
-                if (i == A_DMA + B_DMA)
-                    dma4(As, (plane * (uint32_t)R + (uint32_t)(t.row0 + min(srow, t.rows - 1))) * 4u,
+                if (i == P)
+                    dma4(As, ((uint32_t)kt * (uint32_t)R + (uint32_t)(t.row0 + min(srow, t.rows - 1))) * 4u,
                          slot + (uint32_t)(wave * SR) * 4u);
                 else
-                    dma4(Bs + (size_t)t.e * N * kb, (plane * (uint32_t)N + (uint32_t)min(t.n0 + srow, N - 1)) * 4u,
+                    dma4(Bs + (size_t)t.e * N * kb, ((uint32_t)kt * (uint32_t)N + (uint32_t)min(t.n0 + srow, N - 1)) * 4u,
                          slot + BM * 4u + (uint32_t)(wave * SR) * 4u);
             }
         }
     };
+    auto frags = [&](const u32x4* stage, const uint8_t* slot, int s, int i, i32x8 (&fa)[TM], i32x8 (&fb)[TN],
+                     int (&sa)[TM], int (&sb)[TN]) {
+        if (i < TM)
+            fp8_frag<TL>(stage, slot, a_lo[s] + i * 256, a_hi[s] + i * 256, sa_byte + 2 * s + i * 128, fa[i], sa[i]);
+        else if (i < TM + TN)
+            fp8_frag<TL>(stage, slot, b_lo[s] + (i - TM) * 256, b_hi[s] + (i - TM) * 256,
+                         sb_byte + 2 * s + (i - TM) * 128, fb[i - TM], sb[i - TM]);
+    };
+    i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
 
-    // one half-iteration: K-tile g in (fa, fb, sa, sb), g even for ODD == 0;
-    // reads K-tile g + 1 into (ga, gb, ta, tb); DMAs K-tile g + 4 from src.
-    auto half_step = [&](auto odd, int g, const StreamSrc& src, f32x16 (&acc)[TM][TN], const i32x8 (&fa)[TM],
-                         const i32x8 (&fb)[TN], const int (&sa)[TM], const int (&sb)[TN], i32x8 (&ga)[TM],
-                         i32x8 (&gb)[TN], int (&ta)[TM], int (&tb)[TN]) {
-        constexpr int ODD = decltype(odd)::value;
-        constexpr int ND = P + (ODD == 0 ? PS : 0);     // g + 4 has the parity of g
-        constexpr int NB = (1 - ODD) * 2;                // byte offset of K-tile g + 1's scales in its slot
-        fp8_mfma<TL, 0, EARLY>(fa, fb, sa, sb, acc);
-        wait_vm<2 * P + PS>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
-        wait_lds();              // this wave's reads of K-tile g are complete
-        ring_barrier();
-        const u32x4* stage = ring + ((g + 1) & 3) * SC;
-        const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (((g + 1) >> 1) & 3) * (BM + BN)) + NB;
+    // one K-tile g: k-step 0 in set 0 (read during the previous K-tile), k-step 1 in set 1
+    auto ktile = [&](int g, const StreamSrc& src, f32x16 (&acc)[TM][TN]) {
+        const u32x4* stage = ring + (g & 1) * SC;
+        const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (g & 1) * (BM + BN));
 #pragma unroll
-        for (int i = 0; i < NM - EARLY; ++i) {
-            fp8_mfma1<TL>(EARLY + i, fa, fb, sa, sb, acc);
-            if (i < ND) dma(src, g + 4, i);
-            if (i < TM)
-                fp8_frag<TL>(stage, slot, a0 + i * 128, a1 + i * 128, sa_byte + i * 128, ga[i], ta[i]);
-            else if (i < TM + TN)
-                fp8_frag<TL>(stage, slot, b0 + (i - TM) * 128, b1 + (i - TM) * 128, sb_byte + (i - TM) * 128,
-                             gb[i - TM], tb[i - TM]);
+        for (int i = 0; i < NM; ++i) {
+            fp8_mfma1<TL>(i, fa0, fb0, sa0, sb0, acc);
+            frags(stage, slot, 1, i, fa1, fb1, sa1, sb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fp8_mfma<TL, 0, EARLY>(fa1, fb1, sa1, sb1, acc);
+        wait_vm<0>();   // K-tile g + 1 landed (the only DMAs in flight)
+        wait_lds();     // this wave's reads of K-tile g are complete
+        ring_barrier();
+        const u32x4* nstage = ring + ((g + 1) & 1) * SC;
+        const uint8_t* nslot = reinterpret_cast<const uint8_t*>(sring + ((g + 1) & 1) * (BM + BN));
+#pragma unroll
+        for (int i = 0; i < SL; ++i) {
+            fp8_mfma1<TL>(EARLY + i, fa1, fb1, sa1, sb1, acc);
+#pragma unroll
+            for (int j = i * ND / SL; j < (i + 1) * ND / SL; ++j) dma(src, g + 2, j);
+            frags(nstage, nslot, 0, i, fa0, fb0, sa0, sb0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // prologue: K-tiles 0..3 of the stream (for two-K-tile tiles, 2 and 3 are the next tile's)
+    // prologue: K-tiles 0 and 1 of the stream (for one-K-tile tiles, 1 is the next tile's)
     {
         const StreamSrc here{c0, 1, 0};
         const bool has1 = tile + G < total;
         const StreamSrc ahead{has1 ? c1 : c0, has1 ? 1 : 0, has1 ? -nk : nk - 1};
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int i = 0; i < P + PS; ++i)
-                if (i < P || (g & 1) == 0) dma(g < nk ? here : ahead, g, i);
+            for (int i = 0; i < ND; ++i) dma(g < nk ? here : ahead, g, i);
     }
-    i32x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-    int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
-    wait_vm<3 * P + PS>();   // K-tile 0 and its scales landed; 1, 2 (with scales) and 3 may stay in flight
+    wait_vm<ND>();   // K-tile 0 and its scales landed; K-tile 1 may stay in flight
     ring_barrier();
-    const uint8_t* slot0 = reinterpret_cast<const uint8_t*>(sring);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fp8_frag<TL>(ring, slot0, a0 + i * 128, a1 + i * 128, sa_byte + i * 128, fa0[i], sa0[i]);
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-        fp8_frag<TL>(ring, slot0, b0 + i * 128, b1 + i * 128, sb_byte + i * 128, fb0[i], sb0[i]);
+    for (int i = 0; i < TM + TN; ++i)
+        frags(ring, reinterpret_cast<const uint8_t*>(sring), 0, i, fa0, fb0, sa0, sb0);
 
     for (;;) {
         f32x16 acc[TM][TN];
@@ -1571,24 +1588,12 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        // K-tiles go in pairs (kt even: register set 0; kt + 1: set 1), the
-        // pair's scales in slot (kt / 2) % 4
         const StreamSrc here{c0, 1, 0};
         const bool has = tile + qa * G < total;
         const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
-        for (int kt = 0; kt < head; kt += 2) {
-            half_step(std::integral_constant<int, 0>{}, kbase + kt, here, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1,
-                      sb1);
-            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, here, acc, fa1, fb1, sa1, sb1, fa0, fb0,
-                      sa0, sb0);
-        }
-        for (int kt = head; kt < nk; kt += 2) {
-            half_step(std::integral_constant<int, 0>{}, kbase + kt, ahead, acc, fa0, fb0, sa0, sb0, fa1, fb1, sa1,
-                      sb1);
-            half_step(std::integral_constant<int, 1>{}, kbase + kt + 1, ahead, acc, fa1, fb1, sa1, sb1, fa0, fb0,
-                      sa0, sb0);
-        }
-        // set 0 now holds K-tile 0 of the next tile (or unused data after the last)
+        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, acc);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
+        // set 0 now holds k-step 0 of the next tile's first K-tile (or unused data after the last)
         fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks);
         if (tile + G >= total) break;
         tile += G;
