@@ -817,15 +817,25 @@ __device__ __forceinline__ int bounded_wait(const int32_t* count, int need, uint
     }
 }
 
+template <class TL>
+struct Ring128 {
+    static constexpr int A_DMA = TL::BM / 8 / TL::NW, B_DMA = TL::BN / 8 / TL::NW;   // 1 KB DMAs per wave
+    static constexpr int P = A_DMA + B_DMA;                                            // per wave per K-tile
+    static constexpr int SC = (TL::BM + TL::BN) * 8;                                   // 16-byte chunks per stage
+    static_assert(TL::BM % (8 * TL::NW) == 0 && TL::BN % (8 * TL::NW) == 0 && A_DMA % 2 == 0 && B_DMA % 2 == 0,
+                  "DMA blocks of 8 rows, an even number per wave");
+};
+
 template <class TL, int KINDS>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_bf16_fused_kernel(FusedParams p) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
-    constexpr int NM = TL::NM, EARLY = TL::EARLY, P = TL::P, SC = TL::STAGE_CHUNKS;
-    constexpr int A_DMA = TL::A_DMA, B_DMA = TL::B_DMA;
-    static_assert(NM - EARLY >= P && NM >= TM + TN && NM - EARLY >= TM + TN, "one DMA / fragment per MFMA step");
+    constexpr int NM = TL::NM, EARLY = TL::EARLY;
+    constexpr int A_DMA = Ring128<TL>::A_DMA, B_DMA = Ring128<TL>::B_DMA, P = Ring128<TL>::P, SC = Ring128<TL>::SC;
+    constexpr int SL = NM - EARLY;   // MFMA slots after the barrier of a K-tile
+    static_assert(NM >= TM + TN && SL >= TM + TN && SL > 0, "one fragment read per MFMA slot");
     constexpr int kObufChunks = 128;   // per wave: 16 rows x 128 bytes of row-contiguous output
-    __shared__ u32x4 ring[TL::STAGES * SC];
+    __shared__ u32x4 ring[2 * SC];
     __shared__ u32x4 obuf[TL::NW * kObufChunks];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
@@ -846,12 +856,17 @@ void gemm_bf16_fused_kernel(FusedParams p) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t ring_lds = lds_addr(ring);
     const int wm = wave / TL::WN, wn = wave % TL::WN;
-    const int fsw = ((lane & 31) >> 2) & 3, half = lane >> 5;
-    const int arow = (wm * TL::WROWS + (lane & 31)) * 4, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 4;
-    const int a0 = arow + ((0 + half) ^ fsw), a1 = arow + ((2 + half) ^ fsw);
-    const int b0 = brow + ((0 + half) ^ fsw), b1 = brow + ((2 + half) ^ fsw);
-    const int drow = lane >> 2;
-    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+    const int key = ((lane & 31) >> 1) & 7, half = lane >> 5;
+    const int arow = (wm * TL::WROWS + (lane & 31)) * 8, brow = (BM + wn * TL::WCOLS + (lane & 31)) * 8;
+    int aoff[4], boff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        aoff[s] = arow + ((2 * s + half) ^ key);
+        boff[s] = brow + ((2 * s + half) ^ key);
+    }
+    const int drow = lane >> 3;
+    const uint32_t dch0 = (uint32_t)((lane & 7) ^ (drow >> 1)) * 16u;
+    const uint32_t dch1 = (uint32_t)((lane & 7) ^ (4 + (drow >> 1))) * 16u;
 
     // the ticket after the two static ones, claimed now and read back at the end of the first tile
     int pending = total;
@@ -865,21 +880,22 @@ void gemm_bf16_fused_kernel(FusedParams p) {
 
     auto dma = [&](const FfnSrc& src, int g, int i) {
         const int kt = (g - kbase) * src.mul + src.add;
-        const uint32_t st = ring_lds + (uint32_t)(g & 3) * SC * 16u;
+        const uint32_t st = ring_lds + (uint32_t)(g & 1) * SC * 16u;
+        const uint32_t dch = (i & 1) ? dch1 : dch0;
         if (i < A_DMA) {
-            const int r = 16 * (wave * A_DMA + i) + drow;
-            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
+            const int r = 8 * (wave * A_DMA + i) + drow;
+            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dch + (uint32_t)kt * 128u;
             dma16(src.a, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
         } else {
             const int j = i - A_DMA;
-            const int r = 16 * (wave * B_DMA + j) + drow;
-            const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dchunk + (uint32_t)kt * 64u;
-            dma16(src.b, off, st + BM * 64u + (uint32_t)(wave * B_DMA + j) * 1024u);
+            const int r = 8 * (wave * B_DMA + j) + drow;
+            const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dch + (uint32_t)kt * 128u;
+            dma16(src.b, off, st + BM * 128u + (uint32_t)(wave * B_DMA + j) * 1024u);
         }
     };
-    auto frag = [&](const u32x4* stage, int aoff, int boff, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
-        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff + i * 128]);
-        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff + (i - TM) * 128]);
+    auto frag = [&](const u32x4* stage, int s, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+        if (i < TM) fa[i] = __builtin_bit_cast(bf16x8, stage[aoff[s] + i * 32 * 8]);
+        else if (i < TM + TN) fb[i - TM] = __builtin_bit_cast(bf16x8, stage[boff[s] + (i - TM) * 32 * 8]);
     };
     // tile t may start once the previous phase's tiles of its rows are done;
     // false if the bounded wait gave up (error word raised)
@@ -898,37 +914,51 @@ void gemm_bf16_fused_kernel(FusedParams p) {
     auto start_stream = [&](const FfnTile& t) {
         const FfnSrc here = ffn_src(p, t, 1, 0);
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 2; ++g)
 #pragma unroll
             for (int i = 0; i < P; ++i) dma(here, kbase + g, i);
-        wait_vm<3 * P>();   // the first K-tile landed; 1, 2 and 3 may stay in flight
+        wait_vm<P>();   // the first K-tile landed; the second may stay in flight
         ring_barrier();
 #pragma unroll
-        for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 3) * SC, a0, b0, i, fa0, fb0);
+        for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 1) * SC, 0, i, fa0, fb0);
     };
 
     bool poison = !wait_rows(c0);   // the current tile's rows were not seen complete
     start_stream(c0);
 
+    // one K-tile g of four k-steps, as in gemm_bf16_ffn_kernel below
     auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
-        const u32x4* stage = ring + (g & 3) * SC;
+        const u32x4* stage = ring + (g & 1) * SC;
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             bf_mfma1<TL>(i, fa0, fb0, acc);
-            frag(stage, a1, b1, i, fa1, fb1);
+            frag(stage, 1, i, fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa1, fb1, acc);
+            frag(stage, 2, i, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            bf_mfma1<TL>(i, fa0, fb0, acc);
+            frag(stage, 3, i, fa1, fb1);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < EARLY; ++i) bf_mfma1<TL>(i, fa1, fb1, acc);
-        wait_vm<2 * P>();   // K-tile g + 1 landed; g + 2 and g + 3 may stay in flight
-        wait_lds();         // this wave's reads of K-tile g are complete
+        wait_vm<0>();   // K-tile g + 1 landed (the only DMAs in flight)
+        wait_lds();     // this wave's reads of K-tile g are complete
         ring_barrier();
-        const u32x4* nstage = ring + ((g + 1) & 3) * SC;
+        const u32x4* nstage = ring + ((g + 1) & 1) * SC;
 #pragma unroll
-        for (int i = 0; i < NM - EARLY; ++i) {
+        for (int i = 0; i < SL; ++i) {
             bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
-            if (i < P) dma(src, g + 4, i);
-            frag(nstage, a0, b0, i, fa0, fb0);
+#pragma unroll
+            for (int j = i * P / SL; j < (i + 1) * P / SL; ++j) dma(src, g + 2, j);
+            frag(nstage, 0, i, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -942,14 +972,13 @@ void gemm_bf16_fused_kernel(FusedParams p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-        const int nk = __builtin_amdgcn_readfirstlane(p.ph[c0.phase].K / 32);
-        const int head = nk - 4;
-        // The count of the next tile's M tile is copied into LDS before the
-        // DMAs of K-tile head + 1, so the vmcnt wait of K-tile head - 1 (which
-        // leaves only K-tiles head + 1 and head + 2 in flight) covers it.
+        const int nk = __builtin_amdgcn_readfirstlane(p.ph[c0.phase].K / 64);
+        const int head = nk - 2;
+        // The count of the next tile's M tile is copied into LDS before K-tile
+        // head - 1's wait, which then covers it.
         const int32_t* need1 = c1.phase >= 0 ? p.ph[c1.phase].need : nullptr;
-        const bool probe = need1 != nullptr && head >= 4;
-        const int split = probe ? head - 3 : head;
+        const bool probe = need1 != nullptr && head >= 1;
+        const int split = probe ? head - 1 : head;
         const FfnSrc here = ffn_src(p, c0, 1, 0);
         for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, acc);
         if (probe && wave == 0) dma4_dev(need1, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
@@ -959,7 +988,6 @@ void gemm_bf16_fused_kernel(FusedParams p) {
                         (need1 == nullptr || (probe && flag >= p.ph[c1.phase].need_count && !p.force_wait));
         const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk) : ffn_src(p, c0, 0, nk - 1);
         for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
-
         {
             FusedPhase q = p.ph[c0.phase];
             q.c = static_cast<uint16_t*>(const_cast<void*>(sgpr_ptr(q.c)));
@@ -1078,14 +1106,6 @@ __device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, 
 // the row, so the 16 rows read by each 16-lane group of a fragment load fall
 // on 64 distinct banks, and the 8 lanes of one row of a DMA write 8 distinct
 // chunks.
-template <class TL>
-struct Ring128 {
-    static constexpr int A_DMA = TL::BM / 8 / TL::NW, B_DMA = TL::BN / 8 / TL::NW;   // 1 KB DMAs per wave
-    static constexpr int P = A_DMA + B_DMA;                                            // per wave per K-tile
-    static constexpr int SC = (TL::BM + TL::BN) * 8;                                   // 16-byte chunks per stage
-    static_assert(TL::BM % (8 * TL::NW) == 0 && TL::BN % (8 * TL::NW) == 0 && A_DMA % 2 == 0 && B_DMA % 2 == 0,
-                  "DMA blocks of 8 rows, an even number per wave");
-};
 
 template <class TL>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
