@@ -195,6 +195,36 @@ def cold_cache_steps(step, dev, steps: int) -> dict:
             "flush": "512 MiB device write before each step"}
 
 
+def copy_ceiling(step, dev, models: dict, reps: int = 10) -> dict:
+    """The HBM rate a plain device copy reaches in the cache state dispatch and
+    combine run in: for each of the two stages, a copy moving the stage's
+    algorithmic bytes (half read, half written) is timed right after a forward
+    step, so the caches hold the step's dirty lines as they do for the stage;
+    median over `reps` steps."""
+    out = {}
+    for stage in ("dispatch", "combine"):
+        nbytes = int(models[stage][1])
+        half = max(nbytes // 2, 1 << 20)
+        src = torch.empty(half, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        times = []
+        for _ in range(reps):
+            step()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dst.copy_(src)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = sorted(times)[len(times) // 2]
+        gbps = 2 * half / (ms * 1e-3) / 1e9
+        out[stage] = {"bytes": 2 * half, "ms": round(ms, 5), "gbps": round(gbps, 1),
+                      "frac_of_peak": round(gbps / HBM_GBPS, 4)}
+        del src, dst
+    out["note"] = "plain device copy of the stage's bytes right after a forward step (median of 10)"
+    return out
+
+
 def host_sync_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device: float) -> dict:
     """The same block through moe_forward_host_sync (counts copied to the host and
     waited for before the grouped GEMMs), timed like the main loop."""
@@ -405,6 +435,7 @@ def main(argv=None):
     }
     if not args.main_only:
         result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
+        result["copy_ceiling"] = copy_ceiling(step, dev, models)
         result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
         result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
         result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)

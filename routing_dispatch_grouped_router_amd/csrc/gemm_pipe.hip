@@ -1,5 +1,5 @@
-// Pipelined grouped GEMMs for gfx950: direct global -> LDS loads feeding a
-// four-stage LDS ring; bf16 (v_mfma_f32_32x32x16_bf16) and MXFP8
+// Pipelined grouped GEMMs for gfx950: direct global -> LDS loads feeding an
+// LDS ring; bf16 (v_mfma_f32_32x32x16_bf16) and MXFP8
 // (v_mfma_scale_f32_32x32x64_f8f6f4) variants.
 //
 // Contract shared with the rest of the library: the rows of expert e are the
@@ -12,30 +12,35 @@
 // Data movement.  Every 16-byte chunk of a K slice goes from global memory
 // straight into LDS with global_load_lds_dwordx4 (lane l of a wave writes LDS
 // bytes [16 l, 16 l + 16) of a wave-uniform 1 KB block), so no registers are
-// spent on staging; up to three K slices are in flight beyond the one being
-// read into registers.  The loads are issued from inline asm with an SGPR base and a
-// 32-bit lane offset: the compiler spends one VGPR per load and never makes
-// LDS reads wait for them; all waits on them are the explicit wait_vm below.
-// (The compiler's own vmcnt waits stay correct, only more conservative,
-// because vector loads retire in order.)
+// spent on staging.  The loads are issued from inline asm with an SGPR base
+// and a 32-bit lane offset: the compiler spends one VGPR per load and never
+// makes LDS reads wait for them; all waits on them are the explicit wait_vm
+// below.  (The compiler's own vmcnt waits stay correct, only more
+// conservative, because vector loads retire in order.)
 //
-// Stage layout: BM rows of A then BN rows of B, each row one 64-byte K slice
-// (32 bf16 or 64 fp8 values) = 4 chunks; chunk c of row r is stored at
-// c ^ ((r >> 2) & 3), which keeps the 16 rows read by each 16-lane group of a
-// fragment load on distinct banks (16 lanes of a ds_read_b128 are served per
-// cycle from 64 banks).  One ring array with a runtime stage offset keeps the
-// fragment addresses to a few lane bases plus immediates.
+// Two ring geometries.  The kernels that carry the large blocks (the fused
+// bf16 FFN, the fused backward chain, the MXFP8 GEMMs) stream K-tiles of 128
+// bytes per row (64 bf16 or 128 fp8 values) in two stages: each DMA
+// instruction then moves 8 whole 128-byte lines, and the L1 -> L2 request
+// path, which bounds these kernels, carries twice the bytes per request than
+// with half lines.  Chunk c (of 8) of row r sits at c ^ ((r >> 1) & 7).  The
+// plain bf16 kernel (small d or H) keeps K-tiles of 64 bytes (32 values) in
+// four stages, chunk c (of 4) of row r at c ^ ((r >> 2) & 3).  Both swizzles
+// keep the 16 rows read by each 16-lane group of a fragment load on distinct
+// banks (16 lanes of a ds_read_b128 are served per cycle from 64 banks).  One
+// ring array with a runtime stage offset keeps the fragment addresses to a
+// few lane bases plus immediates.
 //
-// Schedule of one K-tile kt (two bf16 k-steps, or one fp8 k-step): issue a
-// few MFMAs on fragments already in registers, wait for K-tile kt + 1, join
-// the barrier (every wave has all of K-tile kt in registers by then, so its
-// stage is free), start the DMA of K-tile kt + 4 into that stage, and read
-// K-tile kt + 1's fragments between the remaining MFMAs.  So a K-tile has
-// three K-tiles of compute to arrive.  The barrier is a bare s_barrier:
-// __syncthreads() would add a release fence that waits for every DMA in
-// flight.  Every issue starts the same number of loads (past the last K-tile
-// the loads are clamped and land in a stage nobody reads again), so the vmcnt
-// waits are constants and the loop body has no branches.
+// Schedule of one K-tile: multiply the k-steps whose fragments are in
+// registers while reading the next k-step's, then issue a few MFMAs of the
+// last k-step, wait for the next K-tile, join the barrier (every wave has all
+// of this K-tile in registers by then, so its stage is free), start the DMAs
+// of the K-tile one ring length ahead into that stage, and read the next
+// K-tile's first fragments between the remaining MFMAs.  The barrier is a
+// bare s_barrier: __syncthreads() would add a release fence that waits for
+// every DMA in flight.  Every issue starts the same number of loads (past the
+// last K-tile the loads are clamped and land in a stage nobody reads again),
+// so the vmcnt waits are constants and the loop body has no branches.
 #include <type_traits>
 
 #include "grouped_sched.h"
