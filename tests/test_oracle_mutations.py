@@ -122,6 +122,8 @@ def _stats_topk_probabilities(logits, counts, k):
 
 
 _orig_stats = O.router_stats
+_orig_expert_weights = O.expert_weights
+_orig_combine = O.combine
 
 _orig_expert_backward = BW.expert_backward
 _orig_router_backward = BW.router_backward
@@ -168,6 +170,16 @@ def _weights_blocked_along_n(w_gate, w_up, w_down, e, act):
     return wg, wu, wd
 
 
+def _weights_of_next_expert(w_gate, w_up, w_down, e, act):
+    # expert e's rows multiplied by expert e + 1's weights (an index shifted by one)
+    return _orig_expert_weights(w_gate, w_up, w_down, (e + 1) % np.asarray(w_gate).shape[0], act)
+
+
+def _combine_slots_reversed(ye, gate, pos, out_dtype):
+    # gate j applied to the row of slot k - 1 - j
+    return _orig_combine(ye, np.asarray(gate, np.float64)[:, ::-1], pos, out_dtype)
+
+
 WEIGHT_PINS = [
     lambda gd: P.test_mxfp8_weights_blocked_along_contraction_axis(),
 ]
@@ -190,6 +202,7 @@ EXPERT_PINS = [
     lambda gd: [P.test_single_expert_top1_is_dense_swiglu(a) for a in ("f32", "bf16")],
     lambda gd: P.test_identity_experts_round_trip(),
     lambda gd: [P.test_expert_relabelling_invariance(a) for a in ("f32", "bf16")],
+    lambda gd: [P.test_routed_block_equals_dense_gate_matrix(a, t) for a, t in (("f32", 1e-6), ("bf16", 1e-2))],
 ]
 STATS_PINS = [
     lambda gd: P.test_router_stats_hand_examples(),
@@ -217,6 +230,8 @@ MUTATIONS = [
     ("ceil-based shared exponent", MX, "shared_exponent", _shared_exp_ceil, MX_PINS),
     ("FNUZ decode instead of OCP FN", MX, "e4m3_decode", _decode_fnuz, MX_PINS),
     ("MXFP8 weights blocked along the output axis", O, "expert_weights", _weights_blocked_along_n, WEIGHT_PINS),
+    ("rows multiplied by the next expert's weights", O, "expert_weights", _weights_of_next_expert, EXPERT_PINS),
+    ("gates applied to the slots in reverse", O, "combine", _combine_slots_reversed, EXPERT_PINS),
     ("SiLU gradient taken as the sigmoid", BW, "silu_grad", _silu_grad_sigmoid_only, BACKWARD_PINS),
     ("gate and up weight gradients swapped", BW, "expert_backward", _expert_bwd_swapped_wgrads, BACKWARD_PINS),
     ("dxe without the up projection's share", BW, "expert_backward", _expert_bwd_dxe_gate_only, BACKWARD_PINS),

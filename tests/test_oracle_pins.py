@@ -335,6 +335,41 @@ def test_single_expert_top1_is_dense_swiglu(act):
     assert np.all(out["gate"] == 1.0)
 
 
+@pytest.mark.parametrize("act,tol", [("f32", 1e-6), ("bf16", 1e-2), ("mxfp8", 0.12)])
+def test_routed_block_equals_dense_gate_matrix(act, tol):
+    """The routed block is the dense mixture sum_e G[t, e] SwiGLU_e(x[t]) with G
+    the renormalised softmax of each token's k largest logits and zero
+    elsewhere (Olmo-core report, Figure 5 and Section 24: the routed rows are
+    this sum computed only where G is non-zero).  Written here in torch over
+    every (token, expert) pair with torch's topk, softmax and SiLU, so the
+    oracle's grouping, positions, weight indexing and combine are checked
+    against a formulation that has none of them.  MXFP8 is compared with the
+    unquantised mixture at a bar that E4M3's 3-bit mantissa leaves room for."""
+    rng = np.random.default_rng(31)
+    T, d, E, k, H = 90, 64, 6, 2, 96          # d != H and E > k: transposes and wrong experts fail
+    rnd = O.round_f32 if act == "f32" else O.round_bf16
+    x = rnd(rng.standard_normal((T, d)))
+    wg = rnd(rng.standard_normal((E, d, H)) * 0.15)
+    wu = rnd(rng.standard_normal((E, d, H)) * 0.15)
+    wd = rnd(rng.standard_normal((E, H, d)) * 0.15)
+    logits = O.round_f32(rng.standard_normal((T, E)))
+    out = O.forward(x, E, k, act, wg, wu, wd, logits=logits)
+
+    lt = torch.from_numpy(logits)
+    top = torch.topk(lt, k, dim=1)
+    G = torch.zeros(T, E, dtype=torch.float64)
+    G.scatter_(1, top.indices, torch.softmax(top.values, dim=1))
+    xt = torch.from_numpy(x)
+    y = torch.zeros(T, d, dtype=torch.float64)
+    for e in range(E):
+        g, u, dn = (torch.from_numpy(np.asarray(a[e], np.float64)) for a in (wg, wu, wd))
+        y += G[:, e:e + 1] * ((torch.nn.functional.silu(xt @ g) * (xt @ u)) @ dn)
+    want = y.numpy()
+    err = np.linalg.norm(out["y"] - want) / np.linalg.norm(want)
+    assert err <= tol, err
+    assert np.array_equal(np.sort(out["idx"], axis=1), np.sort(top.indices.numpy(), axis=1))
+
+
 def test_identity_experts_round_trip():
     """With ye := xe the combine returns sum_j g_j x[t] = x[t]: bit-exact in bf16
     because the renormalised gates sum to 1 within far less than a bf16 half-ulp."""
