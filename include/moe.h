@@ -99,14 +99,27 @@ const char* moe_status_string(int32_t status);
 
 /* Device workspace, in bytes, that is enough for every entry point below on
  * problem p (host only, no GPU call).  Contents need no initialisation and are
- * overwritten by every call. */
+ * overwritten by every call.  The caller allocates it once and passes it to
+ * every call, so the block's buffers keep fixed addresses from step to step
+ * (report "Section 24: Conclusion", 24.3: graph replay needs buffers at stable
+ * addresses, reused only after their last consumer).  Errors: MOE_ERR_NULL,
+ * MOE_ERR_SHAPE / MOE_ERR_DTYPE for an invalid problem. */
 int32_t moe_workspace_bytes(const moe_problem* p, size_t* bytes);
 
-/* Size in bytes of the packed expert weights for p (host only). */
+/* Size in bytes of the packed expert weights for p (host only, no GPU call):
+ * the regions moe_pack_weights writes, described there (report "Section 24:
+ * Conclusion", 24.3: weight caches built once, in the layout the GEMM reads).
+ * Errors: as moe_workspace_bytes. */
 int32_t moe_packed_weight_bytes(const moe_problem* p, size_t* bytes);
 
 /* Packs the expert weights once, outside the timed path: re-lays them out with
- * the contraction axis contiguous and, for MOE_MXFP8, quantises them.
+ * the contraction axis contiguous and, for MOE_MXFP8, quantises them (report
+ * "Section 24: Conclusion", 24.3: MXFP8 weight caches kept beside the
+ * high-precision weights, produced by a quantiser in the layout the GEMM
+ * consumes, so no per-step conversion kernel runs).  The caller owns both
+ * buffers; the inputs are not modified.  Errors: MOE_ERR_NULL for a NULL
+ * pointer, shape/dtype errors as moe_workspace_bytes; nothing is enqueued on
+ * an error.
  *   w_gate, w_up : device [E, d, H]   (x . W convention), storage type above
  *   w_down       : device [E, H, d]
  *   packed       : device, moe_packed_weight_bytes() bytes, layout:
@@ -225,7 +238,13 @@ int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate
                     const int32_t* pos, void* y, void* stream);
 
 /* The whole block on one stream: route, dispatch, grouped SwiGLU, combine, with
- * no host synchronisation between them.  Arguments as above; topk_idx,
+ * no host synchronisation between them ("Supercharging Olmo-core ...",
+ * Section 2, the design paragraph after Figure 5: no extra permutation, no
+ * device-to-host synchronisation and no gap between launches; Abstract:
+ * device-scheduled grouped GEMMs).  The caller owns every buffer; ws is at
+ * least moe_workspace_bytes(p) bytes, and calls sharing a workspace must not
+ * overlap.  All arguments are validated on the host before anything is
+ * enqueued: a non-zero status means nothing ran.  Arguments as above; topk_idx,
  * topk_gate, counts, offsets, pos and router_stats are optional outputs (NULL:
  * kept in the workspace only, or for router_stats not computed).  With
  * MOE_IDENTITY_EXPERTS the grouped GEMM is skipped and ye := xe (MOE_F32 /
