@@ -43,17 +43,19 @@ __device__ __forceinline__ float e4m3_val(uint32_t c) {
     return (c & 0x80u) ? -a : a;
 }
 
+// A 16-byte chunk of a row as float32 values.  Streams read exactly once per
+// step (dy, ye, dxe) are loaded non-temporal, so they do not displace what the
+// caches hold for later kernels.
 template <bool BF>
 __device__ __forceinline__ void load_chunk(const void* base, size_t chunk, float (&v)[8]) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + chunk);
     if (BF) {
-        const u32x4 w = reinterpret_cast<const u32x4*>(base)[chunk];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             v[2 * i] = __uint_as_float(w[i] << 16);
             v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
     } else {
-        const u32x4 w = reinterpret_cast<const u32x4*>(base)[chunk];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(w[i]);
     }
@@ -304,7 +306,8 @@ __global__ __launch_bounds__(64 * kTokPerBlock) void dx_kernel(const void* __res
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
 #pragma unroll
-            for (int g = 0; g < CG; ++g) v[j][g] = src[(size_t)p[j] * row_chunks + min(c0 + 64 * g, row_chunks - 1)];
+            for (int g = 0; g < CG; ++g)
+                v[j][g] = __builtin_nontemporal_load(&src[(size_t)p[j] * row_chunks + min(c0 + 64 * g, row_chunks - 1)]);
         if (wrt) {
 #pragma unroll
             for (int j = 0; j < KMAX; ++j)
