@@ -63,6 +63,9 @@ def stage_models(w: W.Workload) -> dict:
         "router_logits": ("hbm", T * d * bin_ + d * E * bin_ + T * E * 4, "GB/s", HBM_GBPS),
         "route_topk": ("hbm", T * E * 4 + R * 4 * 4 + ((T + 255) // 256) * E * 4, "GB/s", HBM_GBPS),
         "route_scan": ("hbm", 3 * ((T + 255) // 256) * E * 4 + (2 * E + 1) * 4, "GB/s", HBM_GBPS),
+        # positions only (the fused bf16 FFN reads token rows in place): ranks,
+        # expert ids and block bases in, positions and row_token out
+        "route_finalize": ("hbm", R * 4 * 4 + ((T + 255) // 256) * E * 4, "GB/s", HBM_GBPS),
         "dispatch": ("hbm", T * d * bin_ + R * d * bxe + scale_b + R * 4 * 3 + R * 4, "GB/s", HBM_GBPS),
         "gemm1_gate_up_swiglu": (gemm_bound, 4.0 * R * d * H, "TFLOP/s", gemm_peak),
         "gemm2_down": (gemm_bound, 2.0 * R * H * d, "TFLOP/s", gemm_peak),
@@ -223,6 +226,28 @@ def copy_ceiling(step, dev, models: dict, reps: int = 10) -> dict:
         del src, dst
     out["note"] = "plain device copy of the stage's bytes right after a forward step (median of 10)"
     return out
+
+
+def dispatch_standalone(p, d_in, dev, models: dict, reps: int = 20) -> dict:
+    """moe_dispatch alone on this block's routing: `reps` launches back to back
+    between two HIP events.  For blocks whose moe_forward materialises no
+    dispatched copy (the fused bf16 FFN reads token rows in place) this is the
+    row-wise dispatch of the staged API, measured outside the timed steps."""
+    r = B.route(p, x=d_in["x"], w_router=d_in["w_router"], logits=d_in["logits"])
+    B.dispatch(p, d_in["x"], r["pos"])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        B.dispatch(p, d_in["x"], r["pos"])
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = models["dispatch"][1]
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "achieved": round(gbps, 1), "unit": "GB/s", "peak": HBM_GBPS,
+            "frac": round(gbps / HBM_GBPS, 4), "reps": reps,
+            "note": "moe_dispatch of this block's rows, launched alone (not part of moe_forward here)"}
 
 
 def host_sync_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device: float) -> dict:
@@ -404,6 +429,7 @@ def main(argv=None):
     ach = stage_out[dom]["achieved"]
     traffic = measured_traffic(w.name, dom)
     gemm_ms = sum(ms for n, ms in stages if n.startswith("gemm") or n == "grouped_ffn")
+    disp_alone = None if "dispatch" in stage_out else dispatch_standalone(p, d_in, dev, models)
     gemm_peak = models["gemm1_gate_up_swiglu"][3]
     flops = w.expert_flops + w.router_flops
     result = {
@@ -426,11 +452,13 @@ def main(argv=None):
         "block_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "grouped_gemm_frac_of_peak": round(6.0 * w.R * w.d * w.H / (gemm_ms * 1e-3) / 1e12 / gemm_peak, 4)
         if gemm_ms > 0 else None,
-        "dispatch_frac_of_hbm": stage_out.get("dispatch", {}).get("frac"),
+        "dispatch_frac_of_hbm": (stage_out["dispatch"] if disp_alone is None else disp_alone)["frac"]
+        if "dispatch" in stage_out or disp_alone is not None else None,
         "combine_frac_of_hbm": stage_out.get("combine", {}).get("frac"),
         "launch": "HIP graph replay, one moe_forward per step" if args.graph else "eager, one moe_forward per step",
         "ms_per_step_with_stage_events": round(ms_eager, 5),
         "stages": stage_out,
+        **({"dispatch_standalone": disp_alone} if disp_alone is not None else {}),
         "host_wall_s": round(wall, 4),
     }
     if not args.main_only:

@@ -238,7 +238,11 @@ int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate
                     const int32_t* pos, void* y, void* stream);
 
 /* The whole block on one stream: route, dispatch, grouped SwiGLU, combine, with
- * no host synchronisation between them ("Supercharging Olmo-core ...",
+ * no host synchronisation between them.  For MOE_BF16 with d_model and
+ * d_hidden >= 128 the dispatch is not materialised: the fused grouped GEMM
+ * reads each expert-major row r straight from x[row_token[r]] (the row the
+ * dispatch would have copied), so no xe is written and the routing pass only
+ * finalises pos and row_token; y is the same either way ("Supercharging Olmo-core ...",
  * Section 2, the design paragraph after Figure 5: no extra permutation, no
  * device-to-host synchronisation and no gap between launches; Abstract:
  * device-scheduled grouped GEMMs).  The caller owns every buffer; ws is at
@@ -373,8 +377,11 @@ int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, 
  *
  * moe_backward arguments (device pointers unless noted):
  *   dy          [T, d] activation type (bf16 for MOE_MXFP8)
- *   x           [T, d] the forward's input (learned router only; may be NULL
- *               with MOE_LOGITS_GIVEN)
+ *   x           [T, d] the forward's input.  Required for the learned router
+ *               and for MOE_BF16 blocks with d_model and d_hidden >= 128 (their
+ *               forward reads the token rows in place and keeps no dispatched
+ *               copy, so the backward gathers them from x again); otherwise
+ *               unused and may be NULL
  *   w_router    [d, E] activation type (learned router only; may be NULL with
  *               MOE_LOGITS_GIVEN)
  *   packed_w    the forward weight cache (moe_pack_weights); unused, may be
@@ -384,7 +391,8 @@ int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, 
  *               for the copies moe_forward kept in its workspace when it was
  *               given NULL for them
  *   fwd_ws      the workspace of the moe_forward call being differentiated,
- *               unchanged since (it holds xe, h and ye); fwd_ws_bytes >=
+ *               unchanged since (it holds h, ye, row_token and, except for the
+ *               gathering bf16 blocks above, xe); fwd_ws_bytes >=
  *               moe_workspace_bytes
  *   dx          [T, d] out, activation type (bf16 for MOE_MXFP8)
  *   dlogits     [T, E] out, float32

@@ -380,6 +380,8 @@ class Backward:
         if not p.flags & MOE_LOGITS_GIVEN:
             _expect(x, (p.T, p.d_model), dt, "x")
             _expect(w_router, (p.d_model, p.n_experts), dt, "w_router")
+        elif x is not None:
+            _expect(x, (p.T, p.d_model), dt, "x")
         _check("moe_backward", lib().moe_backward(
             ctypes.byref(p), _ptr(dy), _ptr(x), _ptr(w_router), _ptr(packed), _ptr(packed_bwd),
             _ptr(fwd.idx), _ptr(fwd.gate), _ptr(fwd.offsets), _ptr(fwd.pos), _ptr(fwd.ws), fwd.ws.numel(),

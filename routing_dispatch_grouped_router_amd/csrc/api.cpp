@@ -26,11 +26,16 @@ struct Layout {
 
 size_t act_bytes(int act) { return act == MOE_F32 ? 4 : (act == MOE_BF16 ? 2 : 1); }
 
-// bf16 experts run both projections in one launch when each has at least four
-// 32-wide K-tiles (the fused kernel streams a tile's first four K-tiles ahead)
+// bf16 experts run both projections in one launch when each contraction has
+// at least two 64-wide K-tiles (the fused kernel streams a tile's first two
+// K-tiles ahead)
 bool use_ffn(const moe_problem& p) {
     return p.act_dtype == MOE_BF16 && p.d_model >= 128 && p.d_hidden >= 128;
 }
+
+// moe_forward's fused bf16 FFN reads each expert-major row from x through
+// row_token, so that forward writes no dispatched copy xe
+bool forward_gathers(const moe_problem& p) { return use_ffn(p) && !(p.flags & MOE_IDENTITY_EXPERTS); }
 
 Layout layout(const moe_problem& p) {
     Layout L{};
@@ -55,7 +60,7 @@ Layout layout(const moe_problem& p) {
     L.offsets = take((E + 1) * 4);
     L.pos = take(R * 4);
     L.row_token = take(R * 4);
-    L.xe = take(R * d * act_bytes(p.act_dtype));
+    L.xe = take(forward_gathers(p) ? 0 : R * d * act_bytes(p.act_dtype));
     L.xe_scale = take(mx ? R * d / 32 : 0);
     L.ye = take(R * d * (p.act_dtype == MOE_F32 ? 4 : 2));
     L.total = off;
@@ -114,7 +119,7 @@ BwdLayout bwd_layout(const moe_problem& p) {
     B.srow = take(learned ? R * 4 : 0);
     B.rpart = take(learned ? router_wgrad_part_bytes((int)R, p.n_experts, p.d_model) : 0);
     const bool mx = p.act_dtype == MOE_MXFP8;
-    B.xe16 = take(mx ? R * d * 2 : 0);
+    B.xe16 = take(mx || forward_gathers(p) ? R * d * 2 : 0);   // xe dequantised, or gathered again from x
     B.h16 = take(mx ? R * H * 2 : 0);
     B.sync = take(use_bwd_chain(p) ? (size_t)fused_sync_ints((int)R, p.n_experts, 3) * 4 : 0);
     B.total = off;
@@ -390,7 +395,7 @@ int32_t moe_grouped_swiglu(const moe_problem* p, const void* xe, const uint8_t* 
     if (use_ffn(*p)) {
         int32_t* ffn_sync = reinterpret_cast<int32_t*>(at(ws, L.sync));
         if ((st = launched(launch_zero_i32(ffn_sync, ffn_sync_ints(R, E), s)))) return st;
-        return launched(launch_bf16_ffn(static_cast<const uint16_t*>(xe),
+        return launched(launch_bf16_ffn(static_cast<const uint16_t*>(xe), nullptr, nullptr,
                                         reinterpret_cast<const uint16_t*>(static_cast<const char*>(pw) + P.w1),
                                         static_cast<uint16_t*>(h),
                                         reinterpret_cast<const uint16_t*>(static_cast<const char*>(pw) + P.w2),
@@ -474,16 +479,23 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
         // GPU time from the end of routing until work resumes after the host wait
         if ((st = prof_mark("host_count_wait", s))) return st;
     }
-    if ((st = launched(launch_dispatch(act, x, ps, idx, base, row_token, xe, xs, T, d, E, k, s))))
-        return st;
-    if ((st = prof_mark("dispatch", s))) return st;
+    if (ffn) {
+        // the fused bf16 FFN reads each expert-major row straight from x
+        // through row_token, so only the positions are finalised here
+        if ((st = launched(launch_route_finalize(idx, base, T, E, k, ps, row_token, s)))) return st;
+        if ((st = prof_mark("route_finalize", s))) return st;
+    } else {
+        if ((st = launched(launch_dispatch(act, x, ps, idx, base, row_token, xe, xs, T, d, E, k, s))))
+            return st;
+        if ((st = prof_mark("dispatch", s))) return st;
+    }
     if (!identity) {
         const Packed P = packed_layout(*p);
         const char* pw = static_cast<const char*>(packed_w);
         void* h = at(ws, L.h);
         uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
         if (ffn) {
-            if ((st = launched(launch_bf16_ffn(static_cast<const uint16_t*>(xe),
+            if ((st = launched(launch_bf16_ffn(nullptr, static_cast<const uint16_t*>(x), row_token,
                                                reinterpret_cast<const uint16_t*>(pw + P.w1), static_cast<uint16_t*>(h),
                                                reinterpret_cast<const uint16_t*>(pw + P.w2),
                                                static_cast<uint16_t*>(ye), off, ffn_sync, R, E, d, H, host_counts, s))))
@@ -657,6 +669,8 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
         (!mx && !packed_w))
         return MOE_ERR_NULL;
     if (!given && (!x || !w_router || !dw_router)) return MOE_ERR_NULL;
+    const bool regather = forward_gathers(*p);   // the forward kept no xe: rebuilt from x
+    if (regather && !x) return MOE_ERR_NULL;
     const Layout L = layout(*p);
     const BwdLayout BL = bwd_layout(*p);
     if (fwd_ws_bytes < L.total || ws_bytes < BL.total) return MOE_ERR_WORKSPACE;
@@ -687,6 +701,12 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
             return st;
         xe = xe16;
         h = h16;
+    } else if (regather) {
+        uint16_t* xe16 = reinterpret_cast<uint16_t*>(at(ws, BL.xe16));
+        if ((st = launched(launch_dispatch(MOE_BF16, x, const_cast<int32_t*>(ps), idx, nullptr, nullptr, xe16,
+                                           nullptr, T, d, E, k, s))))
+            return st;
+        xe = xe16;
     }
     void* ab = at(ws, BL.ab);
     void* dye = at(ws, BL.dye);   // later dxe

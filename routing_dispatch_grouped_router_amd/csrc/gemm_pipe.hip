@@ -779,6 +779,8 @@ struct FfnSrc {
     const uint16_t* b;
     uint32_t rowbytes;
     int row0, rows, n0, nmax, mul, add;
+    int gather;   // the tile's A rows are rows s_tab[tab + r] of a (token rows), else rows row0 + r
+    int tab;      // first entry of the tile's row table in LDS
 };
 
 // Built once per loop phase and wave-uniform throughout (pinned to SGPRs, so
@@ -796,6 +798,8 @@ __device__ __forceinline__ FfnSrc ffn_src(const FusedParams& p, const FfnTile& t
     s.n0 = t.n0;
     s.mul = mul;
     s.add = __builtin_amdgcn_readfirstlane(add);
+    s.gather = 0;
+    s.tab = 0;
     return s;
 }
 
@@ -1057,7 +1061,9 @@ void gemm_bf16_fused_kernel(FusedParams p) {
 // on one box against the phase-table kernel running the same two phases: 395
 // against 413 us for the bf16_e8 block's FFN.
 struct FfnParams {
-    const uint16_t* xe;
+    const uint16_t* xe;          // dispatched rows [R][d], or
+    const uint16_t* x;           // with row_token: token rows [T][d] read in place of xe
+    const int32_t* row_token;    // [R]: token of each expert-major row, or NULL
     const uint16_t* w1;
     uint16_t* h;
     const uint16_t* w2;
@@ -1087,10 +1093,13 @@ __device__ __forceinline__ FfnTile ffn_tile(int id, int total, int T1, int NT1, 
     return c;
 }
 
-__device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, int mul, int add) {
+__device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, int mul, int add, int tab) {
     FfnSrc s;
     const bool one = t.phase != 1;
-    s.a = one ? p.xe : p.h;
+    const bool gather = one && p.row_token != nullptr;
+    s.a = one ? (gather ? p.x : p.xe) : p.h;
+    s.gather = gather;
+    s.tab = tab;
     s.b = one ? p.w1 + (size_t)t.e * (2 * p.H) * p.d : p.w2 + (size_t)t.e * p.d * p.H;
     s.rowbytes = (uint32_t)(one ? p.d : p.H) * 2u;
     s.nmax = one ? 2 * p.H : p.d;
@@ -1128,6 +1137,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     __shared__ int s_flag[64];
     __shared__ int s_next;
     __shared__ int s_ok;
+    __shared__ int s_tab[2 * BM];   // token of each A row of the current and the next GEMM1 tile
 
     const int MT = build_tile_schedule<BM, NTHR>(p.offsets, p.E, s_tstart, s_scan);
     const int NT1 = (2 * p.H + BN - 1) / BN, NT2 = (p.d + BN - 1) / BN;
@@ -1171,21 +1181,41 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     FfnTile c1 = ffn_tile<BM, BN>(id1, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
     int kbase = 0;
 
+    // byte offsets of this lane's A rows (one per A DMA, chunk included) in a
+    // source: rows of the tile's row table when gathering, else rows row0 + r;
+    // taken once per loop phase, so the K loop reads no table
+    struct ARows { uint32_t off[A_DMA]; };
+    auto arows = [&](const FfnSrc& src) {
+        ARows a;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            const int r = 8 * (wave * A_DMA + i) + drow;
+            const int row = src.gather ? s_tab[src.tab + r] : src.row0 + min(r, src.rows - 1);
+            a.off[i] = (uint32_t)row * src.rowbytes + ((i & 1) ? dch1 : dch0);
+        }
+        return a;
+    };
     // DMA i of global K-tile g (A blocks, then B blocks) from src
-    auto dma = [&](const FfnSrc& src, int g, int i) {
+    auto dma = [&](const FfnSrc& src, const ARows& ar, int g, int i) {
         const int kt = (g - kbase) * src.mul + src.add;
         const uint32_t st = ring_lds + (uint32_t)(g & 1) * SC * 16u;
         const uint32_t dch = (i & 1) ? dch1 : dch0;
         if (i < A_DMA) {
-            const int r = 8 * (wave * A_DMA + i) + drow;
-            const uint32_t off = (uint32_t)(src.row0 + min(r, src.rows - 1)) * src.rowbytes + dch + (uint32_t)kt * 128u;
-            dma16(src.a, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+            dma16(src.a, ar.off[i] + (uint32_t)kt * 128u, st + (uint32_t)(wave * A_DMA + i) * 1024u);
         } else {
             const int j = i - A_DMA;
             const int r = 8 * (wave * B_DMA + j) + drow;
             const uint32_t off = (uint32_t)min(src.n0 + r, src.nmax - 1) * src.rowbytes + dch + (uint32_t)kt * 128u;
             dma16(src.b, off, st + BM * 128u + (uint32_t)(wave * B_DMA + j) * 1024u);
         }
+    };
+    // row table of GEMM1 tile t into slot `slot`: row_token of its BM rows
+    // (rows past the tile clamped), DMA'd by the first BM / 64 waves; the next
+    // K-tile wait and barrier cover it like the K-tile loads
+    auto load_tab = [&](const FfnTile& t, int slot) {
+        if (p.row_token == nullptr || t.phase != 0 || wave >= BM / 64) return;
+        const int r = 64 * wave + lane;
+        dma4(p.row_token, (uint32_t)(t.row0 + min(r, t.rows - 1)) * 4u, lds_addr(s_tab + slot * BM + 64 * wave));
     };
     // fragment i (A blocks, then B blocks) of k-step s from a stage
     auto frag = [&](const u32x4* stage, int s, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
@@ -1204,18 +1234,26 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     };
     bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     // (re)start the K-tile stream at the first K-tile of tile t (global K-tile kbase)
+    int cur = 0;   // row-table slot of the current tile (the next tile's is cur ^ 1)
     auto start_stream = [&](const FfnTile& t) {
-        const FfnSrc here = ffn_src(p, t, 1, 0);
+        const FfnSrc here = ffn_src(p, t, 1, 0, cur * BM);
+        const ARows ah = arows(here);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int i = 0; i < P; ++i) dma(here, kbase + g, i);
+            for (int i = 0; i < P; ++i) dma(here, ah, kbase + g, i);
         wait_vm<P>();   // the first K-tile landed; the second may stay in flight
         ring_barrier();
 #pragma unroll
         for (int i = 0; i < TM + TN; ++i) frag(ring + (kbase & 1) * SC, 0, i, fa0, fb0);
     };
 
+    load_tab(c0, 0);
+    load_tab(c1, 1);
+    if (p.row_token) {
+        wait_vm<0>();   // both row tables landed before any DMA reads them
+        ring_barrier();
+    }
     bool poison = !wait_rows(c0);   // the current tile's rows were not seen complete
     start_stream(c0);
 
@@ -1225,7 +1263,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     // then, so its stage is free), then, between its remaining MFMAs, starts
     // the DMAs of K-tile g + 2 into that stage and reads K-tile g + 1's k-step
     // 0 into set 0.
-    auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
+    auto ktile = [&](int g, const FfnSrc& src, const ARows& ar, f32x16 (&acc)[TM][TN]) {
         const u32x4* stage = ring + (g & 1) * SC;
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
@@ -1255,7 +1293,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         for (int i = 0; i < SL; ++i) {
             bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
 #pragma unroll
-            for (int j = i * P / SL; j < (i + 1) * P / SL; ++j) dma(src, g + 2, j);
+            for (int j = i * P / SL; j < (i + 1) * P / SL; ++j) dma(src, ar, g + 2, j);
             frag(nstage, 0, i, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1276,14 +1314,16 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         // head - 1's wait, which then covers it.
         const bool probe = c1.phase == 1 && head >= 1;
         const int split = probe ? head - 1 : head;
-        const FfnSrc here = ffn_src(p, c0, 1, 0);
-        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, acc);
+        const FfnSrc here = ffn_src(p, c0, 1, 0, cur * BM);
+        const ARows ah = arows(here);
+        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, ah, acc);
         if (probe && wave == 0) dma4_dev(done, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
-        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, acc);
+        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, ah, acc);
         const int flag = __builtin_amdgcn_readfirstlane(s_flag[0]);
         const bool go = c1.phase == 0 || (probe && flag >= NT1 && !p.force_wait);
-        const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk) : ffn_src(p, c0, 0, nk - 1);
-        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
+        const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk, (cur ^ 1) * BM) : ffn_src(p, c0, 0, nk - 1, cur * BM);
+        const ARows aa = arows(ahead);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, acc);
 
         const TileCoord tc{c0.row0, c0.rows, c0.n0, c0.e};
         if (c0.phase == 0)
@@ -1309,6 +1349,10 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         kbase += nk;
         c0 = c1;
         c1 = ffn_tile<BM, BN>(id2, total, T1, NT1, NT2, s_tstart, p.E, p.offsets);
+        // the finished tile's table slot takes the new next tile's rows (every
+        // DMA that read it has been issued); the next K-tile wait covers it
+        cur ^= 1;
+        load_tab(c1, cur ^ 1);
         poison = false;
         if (!go) {
             // the next tile's first K-tiles were not prefetched: wait for its
@@ -1872,13 +1916,13 @@ int ntiles(int n) { return (n + BfRing::BN - 1) / BfRing::BN; }
 
 }  // namespace
 
-hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
-                           const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
-                           const int32_t* host_counts, hipStream_t s) {
+hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* x, const int32_t* row_token, const uint16_t* w1,
+                           uint16_t* h, const uint16_t* w2, uint16_t* ye, const int32_t* offsets, int32_t* sync,
+                           int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s) {
     using TL = BfRing;
     if (device_compute_units() < kXcds) return hipErrorInvalidConfiguration;
     const int grid = persistent_grid(R, E, 2 * H + d, TL::BM, TL::BN, 1, host_counts);
-    const FfnParams p{xe, w1, h, w2, ye, offsets, sync, R, E, d, H, ffn_spin_limit(), g_ffn_force_wait};
+    const FfnParams p{xe, x, row_token, w1, h, w2, ye, offsets, sync, R, E, d, H, ffn_spin_limit(), g_ffn_force_wait};
     hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL>), dim3(grid), dim3(TL::NTHR), 0, s, p);
     return hipGetLastError();
 }

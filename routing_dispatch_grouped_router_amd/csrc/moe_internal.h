@@ -106,9 +106,12 @@ constexpr int kSyncErrWord = 8;
 constexpr int kSyncHead = 16;
 inline int fused_sync_ints(int R, int E, int phases) { return kSyncHead + (phases - 1) * (R / 256 + E); }
 inline int ffn_sync_ints(int R, int E) { return fused_sync_ints(R, E, 2); }
-hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* w1, uint16_t* h, const uint16_t* w2, uint16_t* ye,
-                           const int32_t* offsets, int32_t* sync, int R, int E, int d, int H,
-                           const int32_t* host_counts, hipStream_t s);
+// The fused bf16 expert FFN.  GEMM1's A rows are xe [R][d], or, with row_token
+// non-NULL, row row_token[r] of the token rows x [T][d] for expert-major row r
+// (the rows the dispatch would have copied into xe, read in place).
+hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* x, const int32_t* row_token, const uint16_t* w1,
+                           uint16_t* h, const uint16_t* w2, uint16_t* ye, const int32_t* offsets, int32_t* sync,
+                           int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s);
 hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16_t* dh, const uint16_t* xe,
                                  const uint16_t* w1, uint16_t* dab, const uint16_t* w1t, uint16_t* dxe,
                                  const int32_t* offsets, int32_t* sync, int R, int E, int d, int H, hipStream_t s);

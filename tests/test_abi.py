@@ -156,9 +156,12 @@ def test_workspace_and_packed_sizes(lib, name):
     R = w.T * w.k
     elem = {"f32": 4, "bf16": 2, "mxfp8": 1}[w.act]
     ws = B.workspace_bytes(p)
-    # at least xe, h and ye of R rows
-    assert ws >= R * w.d * elem + R * w.H * elem + R * w.d * (4 if w.act == "f32" else 2)
-    assert ws < 4 * (R * w.d * 6 + R * w.H * 4) + (1 << 26)
+    # at least h and ye of R rows, and xe unless the fused bf16 FFN reads the
+    # token rows in place (bf16 with d_model, d_hidden >= 128: no dispatched copy)
+    gathers = w.act == "bf16" and w.d >= 128 and w.H >= 128
+    xe = 0 if gathers else R * w.d * elem
+    assert ws >= xe + R * w.H * elem + R * w.d * (4 if w.act == "f32" else 2)
+    assert ws < xe + R * w.H * elem + R * w.d * 4 + 16 * R + (1 << 26)
     pw = B.packed_weight_bytes(p)
     want = 3 * w.E * w.d * w.H * elem
     if w.act == "mxfp8":
@@ -182,8 +185,13 @@ def test_backward_rejects_identity_nulls_and_small_workspaces(lib):
     fake = ctypes.c_void_p(0x1000)
     # p, dy, x, w_router, packed_w, packed_bwd, idx, gate, offsets, pos, fwd_ws, fwd_ws_bytes,
     # dx, dlogits, dw_gate, dw_up, dw_down, dw_router, ws, ws_bytes, stream
-    args = [ctypes.byref(p), fake, None, None, fake, fake, None, None, None, None, fake, fws,
+    args = [ctypes.byref(p), fake, fake, None, fake, fake, None, None, None, None, fake, fws,
             fake, fake, fake, fake, fake, None, fake, bws, None]
+    # a bf16 block with d_model, d_hidden >= 128 keeps no dispatched rows in its
+    # forward workspace, so the backward needs x even with given logits
+    no_x = list(args)
+    no_x[2] = None
+    assert lib.moe_backward(*no_x) == -1
     bad_fwd = list(args)
     bad_fwd[11] = fws - 1
     assert lib.moe_backward(*bad_fwd) == -4
