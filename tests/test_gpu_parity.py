@@ -144,6 +144,12 @@ def test_stages_against_oracle(name):
     assert np.max(np.abs(_f64(y) - y_from_gpu_ye)) <= tol * max(1.0, np.max(np.abs(y_from_gpu_ye)))
     check_y(w.act, _f64(y), O.combine(ye_ref, gate, pos, O.out_dtype(w.act)))
 
+    # the whole block gives bitwise the staged result (for bf16 with d, H >= 128
+    # moe_forward's GEMM reads the token rows of x in place of the dispatched copy)
+    out = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], y), "moe_forward differs from the staged calls"
+
 
 @pytest.mark.parametrize("name", SMALL_NAMES)
 def test_forward_against_oracle(name):
@@ -351,8 +357,10 @@ def test_full_size_config(name):
 @pytest.mark.parametrize("name", [n for n in W.CONFIG_ORDER if n != "tiny_f32"])
 def test_full_size_dispatch_bitexact(name):
     """The whole dispatched buffer of each large block, through moe_route and
-    moe_dispatch at full size: bf16 rows equal x[row_token] bit for bit; MXFP8
-    codes and scales equal the oracle quantiser's for every row."""
+    moe_dispatch at full size: bf16 rows equal x[row_token] bit for bit, and
+    moe_forward, whose grouped GEMM reads those rows of x in place, equals the
+    staged grouped SwiGLU and combine on them bit for bit (every output tile);
+    MXFP8 codes and scales equal the oracle quantiser's for every row."""
     w = W.CONFIGS[name]
     print(f"[full dispatch] {w.describe()}", flush=True)
     host, dev = device_inputs(w)
@@ -367,6 +375,15 @@ def test_full_size_dispatch_bitexact(name):
     if w.act != "mxfp8":
         rt = torch.from_numpy(row_token.astype(np.int64)).to(DEV)
         assert torch.equal(xe, dev["x"][rt]), "dispatched rows differ from x[row_token]"
+        # moe_forward reads these rows from x in place (no copy): every output
+        # tile equals the staged grouped SwiGLU on the dispatched buffer, bitwise
+        packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+        ye = B.grouped_swiglu(p, xe, xs, packed, r["offsets"])
+        y = B.combine(p, ye, r["gate"], r["pos"])
+        del xe, ye
+        out = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+        torch.cuda.synchronize()
+        assert torch.equal(out["y"], y), "moe_forward differs from dispatch + grouped SwiGLU + combine"
         return
     q_gpu = _np(xe)
     s_gpu = scales_rowmajor(_np(xs))
