@@ -1811,28 +1811,57 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s2][j], fa[s2][i], acc[i][j], 0, 0, 0);
         }
     }
-    wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
+    wait_vm<0>();   // every DMA has landed: the ring is free once all waves are past their last reads
+    ring_barrier();
+    // Epilogue through LDS: each wave owns 1/8 of the ring (16 KB, 64 rows x 64
+    // float32) and takes its 128 x 64 block in two rounds of 64 rows.  A lane
+    // holds runs of 4 columns of one row (chunk 8 j + 2 q + half of 16 per row,
+    // swizzled by the row so 16 lanes of a write hit 64 banks); it reads back
+    // chunk l % 16 of row l / 16 + 4 t, so 16 lanes cover a row's 256 bytes and
+    // every store instruction writes whole 128-byte lines of 4 rows (direct
+    // stores from the MFMA layout wrote 32-byte pieces of 32 rows).
+    static_assert(WROWS == 128 && WCOLS == 64 && TN == 2 && NW * 16384 <= STAGES * SBYTES, "epilogue staging");
     const int half = lane >> 5;
+    u32x4* stg = reinterpret_cast<u32x4*>(ring) + wave * 1024;
+    const int mrow0 = m0 + wm * WROWS;
+    const int ncol0 = n0 + wn * WCOLS;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int m = m0 + wm * WROWS + i * 32 + (lane & 31);
-        if (m >= M) continue;
+    for (int rho = 0; rho < 2; ++rho) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int ii = 0; ii < 2; ++ii) {
+            const int i = 2 * rho + ii, r = ii * 32 + (lane & 31);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * WCOLS + j * 32 + 8 * q + 4 * half;
-                if (n >= N) continue;
-                const u32x4 v = {__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
-                                 __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
-                if (OMAP == 0) {
-                    *reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n) = v;
-                } else {
-                    const int Hh = N / 2, hh = 32 * (n / 64) + n % 32;
-                    float* dst = ((n / 32) & 1) ? C2 : C;
-                    *reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh) = v;
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 8 * j + 2 * q + half;
+                    stg[r * 16 + (c ^ (r & 15))] = (u32x4){
+                        __float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                        __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
                 }
+        }
+        asm volatile("" ::: "memory");
+        wait_lds();   // this wave's writes are visible to its own lanes (the region is private to the wave)
+        asm volatile("" ::: "memory");
+        const int c = lane & 15;
+        const int n = ncol0 + 4 * c;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int r = (lane >> 4) + 4 * t;
+            const u32x4 v = stg[r * 16 + (c ^ (r & 15))];
+            const int m = mrow0 + 64 * rho + r;
+            if (m >= M || n >= N) continue;
+            if (OMAP == 0) {
+                *reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n) = v;
+            } else {
+                const int Hh = N / 2, hh = 32 * (n / 64) + n % 32;
+                float* dst = ((n / 32) & 1) ? C2 : C;
+                *reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh) = v;
             }
+        }
+        asm volatile("" ::: "memory");   // the next round's writes stay after these reads
+        wait_lds();
+        asm volatile("" ::: "memory");
     }
 }
 
