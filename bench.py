@@ -250,6 +250,39 @@ def dispatch_standalone(p, d_in, dev, models: dict, reps: int = 20) -> dict:
             "note": "moe_dispatch of this block's rows, launched alone (not part of moe_forward here)"}
 
 
+def determinism_check(step, f) -> dict:
+    """Two checks run with every full benchmark: two forward steps of the block
+    give bitwise the same y, and on a block with planted logit ties
+    (edge_ties: 2048 tokens, 64 experts, top-8, logits from 3 integer levels)
+    every token's selection is ordered by (logit descending, index ascending)
+    and no unselected expert beats or ties-with-a-lower-index a selected one."""
+    step()
+    y0 = f.y.clone()
+    step()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(f.y, y0))
+    wt = W.SMALL["edge_ties"]
+    h = W.make_inputs(wt)
+    pt = B.problem(wt.T, wt.d, wt.E, wt.k, wt.H, wt.act, logits_given=True)
+    r = B.route(pt, logits=h["logits"].to(f.y.device))
+    torch.cuda.synchronize()
+    L = h["logits"].numpy()
+    idx = r["idx"].cpu().numpy()
+    ok = True
+    ties = 0
+    for t in range(wt.T):
+        sel = idx[t]
+        key = [(-float(L[t, e]), int(e)) for e in sel]
+        ok &= key == sorted(key) and len(set(sel.tolist())) == wt.k
+        last = key[-1]
+        for e in range(wt.E):
+            if e not in sel:
+                ok &= (-float(L[t, e]), e) > last
+        ties += int(np.sum(L[t] == L[t, sel[-1]]) > 1)
+    return {"bitwise_repeat": same, "ties_lowest_index": bool(ok), "tokens_with_ties_at_kth": ties,
+            "tie_block": wt.describe()}
+
+
 def host_sync_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device: float) -> dict:
     """The same block through moe_forward_host_sync (counts copied to the host and
     waited for before the grouped GEMMs), timed like the main loop."""
@@ -465,6 +498,7 @@ def main(argv=None):
         result["cold_cache"] = cold_cache_steps(step, dev, args.steps)
         result["copy_ceiling"] = copy_ceiling(step, dev, models)
         result["host_sync_variant"] = host_sync_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
+        result["determinism"] = determinism_check(step, f)
         result["with_router_stats"] = router_stats_steps(p, d_in, packed, dev, args.steps, args.warmup, ms_step)
         result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
     elif args.with_backward:
