@@ -67,6 +67,10 @@ def stage_models(w: W.Workload) -> dict:
         # expert ids and block bases in, positions and row_token out
         "route_finalize": ("hbm", R * 4 * 4 + ((T + 255) // 256) * E * 4, "GB/s", HBM_GBPS),
         "dispatch": ("hbm", T * d * bin_ + R * d * bxe + scale_b + R * 4 * 3 + R * 4, "GB/s", HBM_GBPS),
+        # MXFP8 rows in place: each token quantised once (codes + scales, positions
+        # finalised), then the scale dwords laid out per expert-major row
+        "quantize": ("hbm", T * d * bin_ + T * d + T * d // 32 + R * 4 * 4, "GB/s", HBM_GBPS),
+        "scale_gather": ("hbm", R * 4 + 2 * (R * d // 32), "GB/s", HBM_GBPS),
         "gemm1_gate_up_swiglu": (gemm_bound, 4.0 * R * d * H, "TFLOP/s", gemm_peak),
         "gemm2_down": (gemm_bound, 2.0 * R * H * d, "TFLOP/s", gemm_peak),
         # bf16: both projections in one launch

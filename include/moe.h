@@ -242,7 +242,10 @@ int32_t moe_combine(const moe_problem* p, const void* ye, const float* topk_gate
  * d_hidden >= 128 the dispatch is not materialised: the fused grouped GEMM
  * reads each expert-major row r straight from x[row_token[r]] (the row the
  * dispatch would have copied), so no xe is written and the routing pass only
- * finalises pos and row_token; y is the same either way ("Supercharging Olmo-core ...",
+ * finalises pos and row_token.  For MOE_MXFP8 with d_model >= 256 each token
+ * row is quantised once (codes and scales per token, not per routed row),
+ * GEMM1 reads the code rows through row_token, and only the E8M0 scales are
+ * laid out per expert-major row.  y is the same either way ("Supercharging Olmo-core ...",
  * Section 2, the design paragraph after Figure 5: no extra permutation, no
  * device-to-host synchronisation and no gap between launches; Abstract:
  * device-scheduled grouped GEMMs).  The caller owns every buffer; ws is at
@@ -391,8 +394,10 @@ int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, 
  *               for the copies moe_forward kept in its workspace when it was
  *               given NULL for them
  *   fwd_ws      the workspace of the moe_forward call being differentiated,
- *               unchanged since (it holds h, ye, row_token and, except for the
- *               gathering bf16 blocks above, xe); fwd_ws_bytes >=
+ *               unchanged since (it holds h, ye, row_token and the dispatched
+ *               rows: none for the gathering bf16 blocks above, one MXFP8
+ *               code row per token for MXFP8 blocks with d_model >= 256, one
+ *               per routed row otherwise); fwd_ws_bytes >=
  *               moe_workspace_bytes
  *   dx          [T, d] out, activation type (bf16 for MOE_MXFP8)
  *   dlogits     [T, E] out, float32

@@ -21,7 +21,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t hist, base, psum, ppart, rwt, h, h_scale, sync, route_end, gemm_end;
-    size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, ye, total;
+    size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, xst, ye, total;
 };
 
 size_t act_bytes(int act) { return act == MOE_F32 ? 4 : (act == MOE_BF16 ? 2 : 1); }
@@ -36,6 +36,12 @@ bool use_ffn(const moe_problem& p) {
 // moe_forward's fused bf16 FFN reads each expert-major row from x through
 // row_token, so that forward writes no dispatched copy xe
 bool forward_gathers(const moe_problem& p) { return use_ffn(p) && !(p.flags & MOE_IDENTITY_EXPERTS); }
+
+// moe_forward of an MXFP8 block with d_model >= 256 quantises each token row
+// once (codes [T][d], per-token scales) and GEMM1 reads the code rows through
+// row_token; only the scales are laid out per expert-major row.  (GEMM1's row
+// tables run one tile ahead, which needs at least two 128-wide K-tiles.)
+bool forward_quantises_tokens(const moe_problem& p) { return p.act_dtype == MOE_MXFP8 && p.d_model >= 256; }
 
 Layout layout(const moe_problem& p) {
     Layout L{};
@@ -60,8 +66,10 @@ Layout layout(const moe_problem& p) {
     L.offsets = take((E + 1) * 4);
     L.pos = take(R * 4);
     L.row_token = take(R * 4);
-    L.xe = take(forward_gathers(p) ? 0 : R * d * act_bytes(p.act_dtype));
+    const bool tok = forward_quantises_tokens(p);
+    L.xe = take(forward_gathers(p) ? 0 : (tok ? T : R) * d * act_bytes(p.act_dtype));   // MXFP8: codes per token
     L.xe_scale = take(mx ? R * d / 32 : 0);
+    L.xst = take(tok ? T * d / 32 : 0);   // per-token scale dwords [T][d/128]
     L.ye = take(R * d * (p.act_dtype == MOE_F32 ? 4 : 2));
     L.total = off;
     return L;
@@ -484,6 +492,15 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
         // through row_token, so only the positions are finalised here
         if ((st = launched(launch_route_finalize(idx, base, T, E, k, ps, row_token, s)))) return st;
         if ((st = prof_mark("route_finalize", s))) return st;
+    } else if (forward_quantises_tokens(*p)) {
+        // each token quantised once (positions finalised in the same pass);
+        // GEMM1 reads its code rows through row_token, and only the scales are
+        // laid out per expert-major row
+        uint32_t* xst = reinterpret_cast<uint32_t*>(at(ws, L.xst));
+        if ((st = launched(launch_quantize_mxfp8(x, ps, idx, base, row_token, xe, xst, T, d, E, k, s)))) return st;
+        if ((st = prof_mark("quantize", s))) return st;
+        if ((st = launched(launch_scale_gather(xst, row_token, xs, R, d, s)))) return st;
+        if ((st = prof_mark("scale_gather", s))) return st;
     } else {
         if ((st = launched(launch_dispatch(act, x, ps, idx, base, row_token, xe, xs, T, d, E, k, s))))
             return st;
@@ -503,7 +520,8 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
             if ((st = prof_mark("grouped_ffn", s))) return st;
         } else {
             if ((st = launched(launch_gemm1(act, xe, xs, pw + P.w1, reinterpret_cast<const uint8_t*>(pw + P.s1),
-                                            off, h, hs, R, E, d, H, host_counts, s))))
+                                            off, h, hs, R, E, d, H, host_counts, s,
+                                            forward_quantises_tokens(*p) ? row_token : nullptr))))
                 return st;
             if ((st = prof_mark("gemm1_gate_up_swiglu", s))) return st;
             if ((st = launched(launch_gemm2(act, h, hs, pw + P.w2, reinterpret_cast<const uint8_t*>(pw + P.s2),
@@ -693,8 +711,12 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
     if (mx) {   // dequantise the saved MXFP8 activations; the rest runs in bf16
         uint16_t* xe16 = reinterpret_cast<uint16_t*>(at(ws, BL.xe16));
         uint16_t* h16 = reinterpret_cast<uint16_t*>(at(ws, BL.h16));
+        // the forward kept one code row per token when it quantised tokens: gathered through row_token
+        const int32_t* rows = forward_quantises_tokens(*p) ? reinterpret_cast<const int32_t*>(at(fw, L.row_token))
+                                                           : nullptr;
         if ((st = launched(launch_dq_mxfp8(static_cast<const uint8_t*>(xe),
-                                           reinterpret_cast<const uint8_t*>(at(fw, L.xe_scale)), R, d, xe16, s))))
+                                           reinterpret_cast<const uint8_t*>(at(fw, L.xe_scale)), R, d, xe16, s,
+                                           rows))))
             return st;
         if ((st = launched(launch_dq_mxfp8(static_cast<const uint8_t*>(h),
                                            reinterpret_cast<const uint8_t*>(at(fw, L.h_scale)), R, H, h16, s))))

@@ -426,18 +426,21 @@ __global__ __launch_bounds__(256) void transpose_small_kernel(const T* __restric
     }
 }
 
-// MXFP8 activations to bfloat16: codes [R][K] with E8M0 scales [K/128][R][4]
-// (the dispatch / GEMM1 layout); 16 codes per thread, exact (an E4M3 value
-// times a power of two has at most 4 significant bits).
+// MXFP8 activations to bfloat16: codes [R][K] (or, with `rows`, the code row
+// rows[r] of a token matrix: the forward quantised each token once) with E8M0
+// scales [K/128][R][4] (the dispatch / GEMM1 layout); 16 codes per thread,
+// exact (an E4M3 value times a power of two has at most 4 significant bits).
 __global__ __launch_bounds__(256) void dq_mxfp8_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sc,
-                                                       int R, int K, uint16_t* __restrict__ out) {
+                                                       int R, int K, uint16_t* __restrict__ out,
+                                                       const int32_t* __restrict__ rows) {
     const int per_row = K / 16;
     const size_t n = (size_t)R * per_row;
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
         const int r = (int)(i / per_row), c16 = (int)(i - (size_t)r * per_row);
         const int blk = c16 / 2;   // 32-value block
         const int se = (int)sc[((size_t)(blk / 4) * R + r) * 4 + (blk % 4)] - 127;
-        const u32x4 w = reinterpret_cast<const u32x4*>(q + (size_t)r * K)[c16];
+        const size_t src = rows ? (size_t)rows[r] : (size_t)r;
+        const u32x4 w = reinterpret_cast<const u32x4*>(q + src * K)[c16];
         uint32_t o[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -561,10 +564,11 @@ hipError_t launch_dx(int act, const void* dxe, const int32_t* pos, const int32_t
     return hipGetLastError();
 }
 
-hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s) {
+hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s,
+                           const int32_t* rows) {
     const size_t n = (size_t)R * (K / 16);
     const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid), dim3(256), 0, s, q, sc, R, K, out);
+    hipLaunchKernelGGL(dq_mxfp8_kernel, dim3(grid), dim3(256), 0, s, q, sc, R, K, out, rows);
     return hipGetLastError();
 }
 

@@ -197,6 +197,93 @@ hipError_t launch_dispatch(int act, const void* x, int32_t* pos, const int32_t* 
     return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------- MXFP8 rows in place
+//
+// The MXFP8 forward quantises each token row once instead of once per slot:
+// codes xq [T][d] and, per token, the four E8M0 scales of each 128-wide slice
+// as one dword, xst [T][d/128] (both written in whole lines), with the same
+// arithmetic as the dispatch; the wave also finalises the token's positions
+// and row_token, as the dispatch does.  GEMM1 then reads the code rows of x
+// through row_token, and only the scales are laid out per expert-major row
+// (scale_gather_kernel), in the slice-major [d/128][R] dwords the GEMM loads.
+template <int KMAX>
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint4* __restrict__ x, int32_t* __restrict__ pos,
+                                                             const int32_t* __restrict__ topk_idx,
+                                                             const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ row_token, uint4* __restrict__ xq,
+                                                             uint32_t* __restrict__ xst, int T, int d, int E, int k) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (t >= T) return;
+    int p[KMAX];
+    final_positions<KMAX>(pos, topk_idx, base, row_token, t, k, E, lane, p);
+    const int slices = d / 16;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + (size_t)t * (d / 8);
+    for (int c = lane; c < slices; c += 64) {   // a group of 8 lanes covers one 128-wide slice
+        const u32x4 v0 = src[2 * c], v1 = src[2 * c + 1];
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(v0[i] << 16);
+            f[2 * i + 1] = __uint_as_float(v0[i] & 0xFFFF0000u);
+            f[8 + 2 * i] = __uint_as_float(v1[i] << 16);
+            f[8 + 2 * i + 1] = __uint_as_float(v1[i] & 0xFFFF0000u);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        const int se = mx_shared_exp(amax);
+        const float inv = mx_inv_scale(se);
+        const u32x4 q = {e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                         e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv),
+                         e4m3x4(f[8] * inv, f[9] * inv, f[10] * inv, f[11] * inv),
+                         e4m3x4(f[12] * inv, f[13] * inv, f[14] * inv, f[15] * inv)};
+        uint32_t sw = (uint32_t)(se + 127) << (8 * ((c >> 1) & 3));
+        sw |= __shfl_xor(sw, 2);
+        sw |= __shfl_xor(sw, 4);
+        reinterpret_cast<u32x4*>(xq)[(size_t)t * slices + c] = q;
+        if ((lane & 7) == 0) xst[(size_t)t * (d / 128) + (c >> 3)] = sw;
+    }
+}
+
+// xs[s][r] = xst[row_token[r]][s]: the scale dwords of expert-major row r,
+// one thread per (slice, row) with rows fastest, so the stores are contiguous
+// (the reads are scattered but stay in the L2: xst is T * d / 32 bytes).
+__global__ __launch_bounds__(256) void scale_gather_kernel(const uint32_t* __restrict__ xst,
+                                                           const int32_t* __restrict__ row_token,
+                                                           uint32_t* __restrict__ xs, int R, int S) {
+    const int r = blockIdx.x * 256 + threadIdx.x, sl = blockIdx.y;
+    if (r >= R) return;
+    xs[(size_t)sl * R + r] = xst[(size_t)row_token[r] * S + sl];
+}
+
+template <int KMAX>
+static void launch_quantize_k(const void* x, int32_t* pos, const int32_t* topk_idx, const int32_t* base,
+                              int32_t* row_token, void* xq, uint32_t* xst, int T, int d, int E, int k, hipStream_t s) {
+    hipLaunchKernelGGL(quantize_mxfp8_kernel<KMAX>, dim3((T + kRowsPerBlock - 1) / kRowsPerBlock),
+                       dim3(64 * kRowsPerBlock), 0, s, static_cast<const uint4*>(x), pos, topk_idx, base, row_token,
+                       static_cast<uint4*>(xq), xst, T, d, E, k);
+}
+
+hipError_t launch_quantize_mxfp8(const void* x, int32_t* pos, const int32_t* topk_idx, const int32_t* base,
+                                 int32_t* row_token, void* xq, uint32_t* xst, int T, int d, int E, int k,
+                                 hipStream_t s) {
+    if (k <= 2) launch_quantize_k<2>(x, pos, topk_idx, base, row_token, xq, xst, T, d, E, k, s);
+    else if (k <= 4) launch_quantize_k<4>(x, pos, topk_idx, base, row_token, xq, xst, T, d, E, k, s);
+    else if (k <= 8) launch_quantize_k<8>(x, pos, topk_idx, base, row_token, xq, xst, T, d, E, k, s);
+    else launch_quantize_k<kMaxTopK>(x, pos, topk_idx, base, row_token, xq, xst, T, d, E, k, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_gather(const uint32_t* xst, const int32_t* row_token, uint8_t* xs, int R, int d,
+                               hipStream_t s) {
+    const int S = d / 128;
+    hipLaunchKernelGGL(scale_gather_kernel, dim3((unsigned)((R + 255) / 256), (unsigned)S), dim3(256), 0, s, xst,
+                       row_token, reinterpret_cast<uint32_t*>(xs), R, S);
+    return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------- combine
 
 template <bool kBf16, int KMAX>

@@ -162,7 +162,8 @@ int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32
 
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
-                        int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s) {
+                        int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s,
+                        const int32_t* row_token) {
     const int N = 2 * H, K = d;
     if (act == kBF16) {
         return launch_bf16_pipe(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
@@ -172,8 +173,9 @@ hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const 
         hipLaunchKernelGGL(gemm_f32_kernel<1>, grid, block, 0, s, static_cast<const float*>(xe),
                            static_cast<const float*>(w1), static_cast<float*>(h), offsets, E, N, K, H);
     } else {
+        if (row_token && K / 128 < 2) return hipErrorInvalidValue;   // the row tables run one tile ahead
         return launch_fp8_pipe(1, static_cast<const uint8_t*>(xe), xe_scale, static_cast<const uint8_t*>(w1), w1_scale,
-                               h, h_scale, offsets, R, E, N, K, H, host_counts, s);
+                               h, h_scale, offsets, R, E, N, K, H, host_counts, s, row_token);
     }
     return hipGetLastError();
 }

@@ -1511,7 +1511,7 @@ __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW
 void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                           const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, void* __restrict__ C,
                           uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets, int E, int N, int K,
-                          int ldc, int R) {
+                          int ldc, int R, const int32_t* __restrict__ row_token) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
     constexpr int A_DMA = Fp8Extra<TL>::A_DMA, B_DMA = Fp8Extra<TL>::B_DMA, P = Fp8Extra<TL>::P;
@@ -1524,6 +1524,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
     __shared__ int s_tstart[kMaxExperts + 1];
     __shared__ int s_scan[NTHR];
+    __shared__ int s_tab[EPI == 1 ? 3 * BM : 1];   // row tables of gathered A rows (GEMM1 only)
 
     const int MT = build_tile_schedule<BM, NTHR>(offsets, E, s_tstart, s_scan);
     const int NT = (N + BN - 1) / BN;
@@ -1555,6 +1556,34 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     const uint32_t dch0 = (uint32_t)((lane & 7) ^ (drow >> 1)) * 16u;
     const uint32_t dch1 = (uint32_t)((lane & 7) ^ (4 + (drow >> 1))) * 16u;
     const int srow = SR * wave + (lane & (SR - 1));    // scale DMA row of this lane
+    // GEMM1 with row_token: A row r of a tile is code row row_token[row0 + r]
+    // of the token matrix A [T][K] (each token quantised once).  Tile i of this
+    // workgroup keeps its row_token entries in LDS slot i % 3, DMA'd two tiles
+    // ahead (like the K-tiles, covered by the next K-tile wait and barrier);
+    // each lane turns its A rows into byte offsets once per loop phase.
+    static_assert(EPI == 0 || TL::NW * 64 == BM, "one row-table DMA per wave");
+    const bool gather = EPI == 1 && row_token != nullptr;
+    auto load_tab = [&](const TileCoord& t, int slot) {
+        if constexpr (EPI == 1) {
+            if (!gather) return;
+            const int r = 64 * wave + lane;
+            dma4(row_token, (uint32_t)(t.row0 + min(r, t.rows - 1)) * 4u, lds_addr(s_tab + slot * BM + 64 * wave));
+        }
+    };
+    struct ARows { uint32_t off[A_DMA]; };
+    auto arows = [&](const StreamSrc& src, int slot) {
+        ARows a;
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) {
+            const int r = 8 * (wave * A_DMA + i) + drow;
+            int row = src.t.row0 + min(r, src.t.rows - 1);
+            if constexpr (EPI == 1) {
+                if (gather) row = s_tab[slot * BM + r];
+            }
+            a.off[i] = (uint32_t)row * (uint32_t)K + ((i & 1) ? dch1 : dch0);
+        }
+        return a;
+    };
     const bool slane = lane < SR;
     // scale byte of this lane in a slot for k-step 0 (+2 for k-step 1): row dword, byte = K block h
     const int sa_byte = arow_i * 4 + half, sb_byte = (BM + brow_i) * 4 + half;
@@ -1569,15 +1598,13 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 
     // DMA step i of global K-tile g from src: A blocks, then B blocks, then
     // the two scale dword runs (a stand-in K-tile nk - 1 maps to the last plane too)
-    auto dma = [&](const StreamSrc& src, int g, int i) {
+    auto dma = [&](const StreamSrc& src, const ARows& ar, int g, int i) {
         const TileCoord& t = src.t;
         const int kt = (g - kbase) * src.mul + src.add;
         const uint32_t st = ring_lds + (uint32_t)(g & 1) * SC * 16u;
         const uint32_t dch = (i & 1) ? dch1 : dch0;
         if (i < A_DMA) {
-            const int r = 8 * (wave * A_DMA + i) + drow;
-            const uint32_t off = (uint32_t)(t.row0 + min(r, t.rows - 1)) * (uint32_t)K + dch + (uint32_t)kt * 128u;
-            dma16(A, off, st + (uint32_t)(wave * A_DMA + i) * 1024u);
+            dma16(A, ar.off[i] + (uint32_t)kt * 128u, st + (uint32_t)(wave * A_DMA + i) * 1024u);
         } else if (i < P) {
             const int j = i - A_DMA;
             const int r = 8 * (wave * B_DMA + j) + drow;
@@ -1607,7 +1634,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
 
     // one K-tile g: k-step 0 in set 0 (read during the previous K-tile), k-step 1 in set 1
-    auto ktile = [&](int g, const StreamSrc& src, f32x16 (&acc)[TM][TN]) {
+    auto ktile = [&](int g, const StreamSrc& src, const ARows& ar, f32x16 (&acc)[TM][TN]) {
         const u32x4* stage = ring + (g & 1) * SC;
         const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (g & 1) * (BM + BN));
 #pragma unroll
@@ -1626,21 +1653,33 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         for (int i = 0; i < SL; ++i) {
             fp8_mfma1<TL>(EARLY + i, fa1, fb1, sa1, sb1, acc);
 #pragma unroll
-            for (int j = i * ND / SL; j < (i + 1) * ND / SL; ++j) dma(src, g + 2, j);
+            for (int j = i * ND / SL; j < (i + 1) * ND / SL; ++j) dma(src, ar, g + 2, j);
             frags(nstage, nslot, 0, i, fa0, fb0, sa0, sb0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    int ti = 0;   // tiles this workgroup has finished (row-table slot of the current tile: ti % 3)
+    load_tab(c0, 0);
+    if (tile + G < total) load_tab(c1, 1);
+    if (tile + 2 * G < total) load_tab(c2, 2);
+    if (gather) {
+        wait_vm<0>();   // the row tables landed before any DMA reads them
+        ring_barrier();
+    }
     // prologue: K-tiles 0 and 1 of the stream (for one-K-tile tiles, 1 is the next tile's)
     {
         const StreamSrc here{c0, 1, 0};
         const bool has1 = tile + G < total;
         const StreamSrc ahead{has1 ? c1 : c0, has1 ? 1 : 0, has1 ? -nk : nk - 1};
+        const ARows ah = arows(here, 0), aa = arows(ahead, has1 ? 1 : 0);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int i = 0; i < ND; ++i) dma(g < nk ? here : ahead, g, i);
+            for (int i = 0; i < ND; ++i) {
+                if (g < nk) dma(here, ah, g, i);
+                else dma(ahead, aa, g, i);
+            }
     }
     wait_vm<ND>();   // K-tile 0 and its scales landed; K-tile 1 may stay in flight
     ring_barrier();
@@ -1660,15 +1699,21 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         const StreamSrc here{c0, 1, 0};
         const bool has = tile + qa * G < total;
         const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
-        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, acc);
-        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
+        const ARows ah = arows(here, ti % 3);
+        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, ah, acc);
+        const ARows aa = arows(ahead, has ? (ti + qa) % 3 : ti % 3);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, acc);
         // set 0 now holds k-step 0 of the next tile's first K-tile (or unused data after the last)
         fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks);
         if (tile + G >= total) break;
         tile += G;
         c0 = c1;
         c1 = c2;
-        if (tile + 2 * G < total) c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
+        ++ti;
+        if (tile + 2 * G < total) {
+            c2 = tile_coord<BM, BN>(tile + 2 * G, MT, NT, s_tstart, E, offsets);
+            load_tab(c2, (ti + 2) % 3);   // the slot of the tile just finished
+        }
         kbase += nk;
     }
     wait_vm<0>();   // no DMA may land in LDS after the workgroup has left
@@ -1899,10 +1944,10 @@ hipError_t launch_bf16_pipe_tile(const uint16_t* A, const uint16_t* Bw, uint16_t
 template <class TL, int EPI>
 hipError_t launch_fp8_pipe_tile(const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                                 void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                                const int32_t* host_counts, hipStream_t s) {
+                                const int32_t* host_counts, hipStream_t s, const int32_t* row_token) {
     const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
     hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs, C, Cs,
-                       offsets, E, N, K, ldc, R);
+                       offsets, E, N, K, ldc, R, row_token);
     return hipGetLastError();
 }
 
@@ -1974,10 +2019,12 @@ hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                           const int32_t* host_counts, hipStream_t s) {
+                           const int32_t* host_counts, hipStream_t s, const int32_t* row_token) {
     if (epi == 1)
-        return launch_fp8_pipe_tile<Fp8Ring, 1>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s);
-    return launch_fp8_pipe_tile<Fp8Ring, 0>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s);
+        return launch_fp8_pipe_tile<Fp8Ring, 1>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s,
+                                                row_token);
+    return launch_fp8_pipe_tile<Fp8Ring, 0>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s,
+                                            nullptr);
 }
 
 }  // namespace moe

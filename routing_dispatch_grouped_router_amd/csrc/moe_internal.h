@@ -58,6 +58,15 @@ hipError_t launch_dispatch(int act, const void* x, int32_t* pos, const int32_t* 
                            int T, int d, int E, int k, hipStream_t s);
 
 // y[t] = sum_j gate[t][j] * ye[pos[t][j]]   (ye/y float32 for kF32, else bfloat16)
+// MXFP8 rows in place: codes xq [T][d] and per-token scale dwords xst [T][d/128]
+// of each token row, with pos / row_token finalised as by launch_dispatch;
+// then the slice-major scales [d/128][R][4] of the expert-major rows gathered
+// through row_token.
+hipError_t launch_quantize_mxfp8(const void* x, int32_t* pos, const int32_t* topk_idx, const int32_t* base,
+                                 int32_t* row_token, void* xq, uint32_t* xst, int T, int d, int E, int k,
+                                 hipStream_t s);
+hipError_t launch_scale_gather(const uint32_t* xst, const int32_t* row_token, uint8_t* xs, int R, int d,
+                               hipStream_t s);
 hipError_t launch_combine(int act, const void* ye, const float* gate, const int32_t* pos, void* y,
                           int T, int d, int k, hipStream_t s);
 
@@ -68,9 +77,12 @@ hipError_t launch_combine(int act, const void* ye, const float* gate, const int3
 // is sized from the worst case R / BM + E M tiles, or, when the host already
 // holds the per-expert counts (host_counts, E entries; NULL otherwise), from
 // the exact tile count.
+// MXFP8 with row_token non-NULL: xe is the token code matrix [T][d] (d >= 256)
+// read through row_token, xe_scale the expert-major row scales.
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
-                        int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s);
+                        int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s,
+                        const int32_t* row_token = nullptr);
 hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const void* w2,
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
                         int d, int H, const int32_t* host_counts, hipStream_t s);
@@ -126,9 +138,11 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 // Pipelined MXFP8 grouped GEMM (gemm_pipe.hip): A/B E4M3 codes with E8M0 scales per 32 K,
 // scales stored [K/128][rows][4] (A: R rows; B: per expert, N rows).
 // epi 0: bf16 C [.., ldc];  epi 1: SwiGLU then MXFP8 C codes [.., ldc] + scales Cs [ldc/128][R][4].
+// epi 1 with row_token non-NULL: A row r is row row_token[r] of a token matrix
+// A [T][K] (K >= 256), while As stays per expert-major row.
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                           const int32_t* host_counts, hipStream_t s);
+                           const int32_t* host_counts, hipStream_t s, const int32_t* row_token = nullptr);
 
 // Weight packing (setup).
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,
@@ -142,7 +156,10 @@ hipError_t launch_pack_bwd_mx(const void* w_gate, const void* w_up, const void* 
                               void* wdq, int E, int d, int H, hipStream_t s);
 hipError_t launch_copy_bytes(const void* src, void* dst, size_t bytes, hipStream_t s);
 // MXFP8 codes [R][K] + scales [K/128][R][4] to bfloat16 [R][K].
-hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s);
+// out [R][K] bf16 from codes q (row r, or row rows[r] when rows is non-NULL)
+// and the slice-major scales sc [K/128][R][4] of row r.
+hipError_t launch_dq_mxfp8(const uint8_t* q, const uint8_t* sc, int R, int K, uint16_t* out, hipStream_t s,
+                           const int32_t* rows = nullptr);
 
 // W1T [E][d][2H] from w_gate, w_up [E][d][H] (float32 or bfloat16).
 hipError_t launch_pack_w1t(int act, const void* w_gate, const void* w_up, void* out, int E, int d, int H,
