@@ -467,6 +467,16 @@ def main(argv=None):
     traffic = measured_traffic(w.name, dom)
     gemm_ms = sum(ms for n, ms in stages if n.startswith("gemm") or n == "grouped_ffn")
     disp_alone = None if "dispatch" in stage_out else dispatch_standalone(p, d_in, dev, models)
+    # the block's roofline time: each step of the method at its own peak (router
+    # logits for a learned router, routing, dispatch, both expert GEMMs, combine),
+    # whether or not this block materialises the dispatched copy
+    steps_bound = ["route_topk", "route_scan", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
+    if w.router == "learned":
+        steps_bound.insert(0, "router_logits")
+    bound_ms = 0.0
+    for name in steps_bound:
+        _, amount, unit, peak = models[name]
+        bound_ms += amount / (peak * (1e9 if unit == "GB/s" else 1e12)) * 1e3
     gemm_peak = models["gemm1_gate_up_swiglu"][3]
     flops = w.expert_flops + w.router_flops
     result = {
@@ -487,6 +497,8 @@ def main(argv=None):
         "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
                      "frac": round(ach / peak, 4), "traffic": traffic},
         "block_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "block_roofline": {"bound_ms": round(bound_ms, 5), "frac": round(bound_ms / ms_step, 4),
+                           "note": "sum of each step's algorithmic work at its peak (HBM 8 TB/s, MFMA dense peak)"},
         "grouped_gemm_frac_of_peak": round(6.0 * w.R * w.d * w.H / (gemm_ms * 1e-3) / 1e12 / gemm_peak, 4)
         if gemm_ms > 0 else None,
         "dispatch_frac_of_hbm": (stage_out["dispatch"] if disp_alone is None else disp_alone)["frac"]

@@ -8,6 +8,11 @@
 // device; no padding to a common capacity), weights are packed [E][N][K] with
 // the contraction axis contiguous, and GEMM1's N axis interleaves 32 gate
 // columns with the matching 32 up columns so SwiGLU runs in the epilogue.
+// Called from the whole-block forward, GEMM1 takes expert-major row r from
+// the token matrix (bf16 x, or the MXFP8 codes of each token) at row
+// row_token[r] instead of from a dispatched copy: each tile's row_token
+// entries are DMA'd into an LDS row table a tile or two ahead, and each lane
+// turns its A rows into byte offsets once per loop phase.
 //
 // Data movement.  Every 16-byte chunk of a K slice goes from global memory
 // straight into LDS with global_load_lds_dwordx4 (lane l of a wave writes LDS
@@ -41,8 +46,6 @@
 // every DMA in flight.  Every issue starts the same number of loads (past the
 // last K-tile the loads are clamped and land in a stage nobody reads again),
 // so the vmcnt waits are constants and the loop body has no branches.
-#include <type_traits>
-
 #include "grouped_sched.h"
 #include "moe_device.h"
 #include "moe_internal.h"
