@@ -79,6 +79,40 @@ def stage_models(w: W.Workload) -> dict:
     }
 
 
+def stage_rooflines(models: dict, stages) -> dict:
+    """Each timed stage (name, ms) against its roofline: achieved = the stage's
+    algorithmic work per launch / its time, frac = achieved / peak."""
+    out = {}
+    for name, ms in stages:
+        bound, amount, unit, peak = models[name]
+        ach = (amount / (ms * 1e-3) / 1e9) if unit == "GB/s" else (amount / (ms * 1e-3) / 1e12)
+        out[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(ach, 2), "unit": unit,
+                     "peak": peak, "frac": round(ach / peak, 4)}
+    return out
+
+
+def roofline_entry(models: dict, stage_out: dict, dom: str, traffic) -> dict:
+    """The JSON line's `roofline` object for the dominant kernel `dom`."""
+    bound, _, unit, peak = models[dom]
+    ach = stage_out[dom]["achieved"]
+    return {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": traffic}
+
+
+def block_bound_ms(w: W.Workload, models: dict) -> float:
+    """The block's roofline time: each step of the method at its own peak
+    (router logits for a learned router, routing, dispatch, both expert GEMMs,
+    combine), whether or not this block materialises the dispatched copy."""
+    steps = ["route_topk", "route_scan", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
+    if w.router == "learned":
+        steps.insert(0, "router_logits")
+    total = 0.0
+    for name in steps:
+        _, work, unit, peak = models[name]
+        total += work / (peak * (1e9 if unit == "GB/s" else 1e12)) * 1e3
+    return total
+
+
 def source_digest(files) -> str:
     h = hashlib.sha256()
     for f in files:
@@ -455,28 +489,12 @@ def main(argv=None):
     ms_step = ms_total / args.steps
 
     models = stage_models(w)
-    stage_out = {}
-    for name, ms in stages:
-        bound, amount, unit, peak = models[name]
-        ach = (amount / (ms * 1e-3) / 1e9) if unit == "GB/s" else (amount / (ms * 1e-3) / 1e12)
-        stage_out[name] = {"ms": round(ms, 5), "bound": bound, "achieved": round(ach, 2), "unit": unit,
-                           "peak": peak, "frac": round(ach / peak, 4)}
+    stage_out = stage_rooflines(models, stages)
     dom = max(stages, key=lambda s: s[1])[0]
-    bound, amount, unit, peak = models[dom]
-    ach = stage_out[dom]["achieved"]
     traffic = measured_traffic(w.name, dom)
     gemm_ms = sum(ms for n, ms in stages if n.startswith("gemm") or n == "grouped_ffn")
     disp_alone = None if "dispatch" in stage_out else dispatch_standalone(p, d_in, dev, models)
-    # the block's roofline time: each step of the method at its own peak (router
-    # logits for a learned router, routing, dispatch, both expert GEMMs, combine),
-    # whether or not this block materialises the dispatched copy
-    steps_bound = ["route_topk", "route_scan", "dispatch", "gemm1_gate_up_swiglu", "gemm2_down", "combine"]
-    if w.router == "learned":
-        steps_bound.insert(0, "router_logits")
-    bound_ms = 0.0
-    for name in steps_bound:
-        _, amount, unit, peak = models[name]
-        bound_ms += amount / (peak * (1e9 if unit == "GB/s" else 1e12)) * 1e3
+    bound_ms = block_bound_ms(w, models)
     gemm_peak = models["gemm1_gate_up_swiglu"][3]
     flops = w.expert_flops + w.router_flops
     result = {
@@ -494,8 +512,7 @@ def main(argv=None):
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": w.describe(), "T": w.T, "d_model": w.d, "n_experts": w.E, "top_k": w.k,
                    "d_hidden": w.H, "router": w.router, "parallelism": "single GPU"},
-        "roofline": {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
-                     "frac": round(ach / peak, 4), "traffic": traffic},
+        "roofline": roofline_entry(models, stage_out, dom, traffic),
         "block_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "block_roofline": {"bound_ms": round(bound_ms, 5), "frac": round(bound_ms / ms_step, 4),
                            "note": "sum of each step's algorithmic work at its peak (HBM 8 TB/s, MFMA dense peak)"},

@@ -360,7 +360,9 @@ def test_full_size_dispatch_bitexact(name):
     moe_dispatch at full size: bf16 rows equal x[row_token] bit for bit, and
     moe_forward, whose grouped GEMM reads those rows of x in place, equals the
     staged grouped SwiGLU and combine on them bit for bit (every output tile);
-    MXFP8 codes and scales equal the oracle quantiser's for every row."""
+    MXFP8 codes and scales equal the oracle quantiser's for every row, and
+    moe_forward, which quantises each token once and reads its code rows in
+    place, equals the staged path on them bit for bit."""
     w = W.CONFIGS[name]
     print(f"[full dispatch] {w.describe()}", flush=True)
     host, dev = device_inputs(w)
@@ -395,6 +397,16 @@ def test_full_size_dispatch_bitexact(name):
             rows = pos[t0:t1, j]
             assert np.array_equal(q_gpu[rows], q), f"MXFP8 codes, tokens {t0}..{t1} slot {j}"
             assert np.array_equal(s_gpu[rows], sc), f"MXFP8 scales, tokens {t0}..{t1} slot {j}"
+    # moe_forward quantises each token once and GEMM1 reads those code rows
+    # through row_token: every output tile equals the staged path on the
+    # dispatched codes and scales, bit for bit
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    ye = B.grouped_swiglu(p, xe, xs, packed, r["offsets"])
+    y = B.combine(p, ye, r["gate"], r["pos"])
+    del xe, xs, ye
+    out = B.forward(p, dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], y), "moe_forward differs from dispatch + grouped SwiGLU + combine"
 
 
 # ----------------------------------------------------------------------------- MXFP8 packing
