@@ -204,7 +204,7 @@ int32_t prof_begin(hipStream_t s) {
     if (g_prof.device != dev) {
         for (auto& row : g_prof.ev)
             for (auto& e : row) {
-                if (e) hipEventDestroy(e);
+                if (e) (void)hipEventDestroy(e);   // events of the previous device: nothing to do on failure
                 e = nullptr;
             }
         for (auto& row : g_prof.ev)

@@ -71,6 +71,10 @@ __device__ __forceinline__ const void* sgpr_ptr(const void* p) {
 }
 
 // 16 bytes per lane from base + voff into LDS bytes [lds + 16 lane, +16).
+// M0 is set inside each statement; it is listed as clobbered for the reader
+// (the compiler treats M0 as reserved and warns that it ignores the entry: no
+// code of these kernels keeps a value in M0, LDS instructions on gfx950 do not
+// read it, and the only DMAs are these statements).
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
