@@ -26,9 +26,8 @@
 // Two ring geometries.  The kernels that carry the large blocks (the fused
 // bf16 FFN, the fused backward chain, the MXFP8 GEMMs) stream K-tiles of 128
 // bytes per row (64 bf16 or 128 fp8 values) in two stages: each DMA
-// instruction then moves 8 whole 128-byte lines, and the L1 -> L2 request
-// path, which bounds these kernels, carries twice the bytes per request than
-// with half lines.  Chunk c (of 8) of row r sits at c ^ ((r >> 1) & 7).  The
+// instruction then moves 8 whole 128-byte lines, so the requests to L2 carry
+// twice the bytes they carry with half lines (measured 2-5% faster).  Chunk c (of 8) of row r sits at c ^ ((r >> 1) & 7).  The
 // plain bf16 kernel (small d or H) keeps K-tiles of 64 bytes (32 values) in
 // four stages, chunk c (of 4) of row r at c ^ ((r >> 2) & 3).  Both swizzles
 // keep the 16 rows read by each 16-lane group of a fragment load on distinct
@@ -41,7 +40,15 @@
 // last k-step, wait for the next K-tile, join the barrier (every wave has all
 // of this K-tile in registers by then, so its stage is free), start the DMAs
 // of the K-tile one ring length ahead into that stage, and read the next
-// K-tile's first fragments between the remaining MFMAs.  The barrier is a
+// K-tile's first fragments between the remaining MFMAs.  The two-stage
+// kernels issue only the A blocks (and scales) there and the B blocks between
+// the next K-tile's first MFMAs, from the same source: the DMAs slow the
+// MFMAs beside them less when spread out (measured 1-3% faster); a tile's
+// last K-tile issues its B blocks before the epilogue, and the next tile's
+// first K-tile issues them again (identical weight bytes into the same place,
+// landed before that K-tile's wait), which keeps the loop free of branches.
+// The weight-gradient kernel likewise issues a K-tile's B rows after its first
+// k-step's MFMAs.  The barrier is a
 // bare s_barrier: __syncthreads() would add a release fence that waits for
 // every DMA in flight.  Every issue starts the same number of loads (past the
 // last K-tile the loads are clamped and land in a stage nobody reads again),
@@ -943,12 +950,14 @@ void gemm_bf16_fused_kernel(FusedParams p) {
     start_stream(c0);
 
     // one K-tile g of four k-steps, as in gemm_bf16_ffn_kernel below
-    auto ktile = [&](int g, const FfnSrc& src, f32x16 (&acc)[TM][TN]) {
+    auto ktile = [&](int g, const FfnSrc& src, const FfnSrc& prev, f32x16 (&acc)[TM][TN]) {
         const u32x4* stage = ring + (g & 1) * SC;
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             bf_mfma1<TL>(i, fa0, fb0, acc);
             frag(stage, 1, i, fa1, fb1);
+            // the B blocks of K-tile g + 1 (from prev), as in gemm_bf16_ffn_kernel
+            if (i % (NM / B_DMA) == NM / B_DMA - 1) dma(prev, g + 1, A_DMA + i / (NM / B_DMA));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -973,7 +982,7 @@ void gemm_bf16_fused_kernel(FusedParams p) {
         for (int i = 0; i < SL; ++i) {
             bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
 #pragma unroll
-            for (int j = i * P / SL; j < (i + 1) * P / SL; ++j) dma(src, g + 2, j);
+            for (int j = i * A_DMA / SL; j < (i + 1) * A_DMA / SL; ++j) dma(src, g + 2, j);
             frag(nstage, 0, i, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -996,14 +1005,17 @@ void gemm_bf16_fused_kernel(FusedParams p) {
         const bool probe = need1 != nullptr && head >= 1;
         const int split = probe ? head - 1 : head;
         const FfnSrc here = ffn_src(p, c0, 1, 0);
-        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, acc);
+        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, here, acc);
         if (probe && wave == 0) dma4_dev(need1, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
-        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, acc);
+        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, here, acc);
         const int flag = __builtin_amdgcn_readfirstlane(s_flag[0]);
         const bool go = c1.phase >= 0 &&
                         (need1 == nullptr || (probe && flag >= p.ph[c1.phase].need_count && !p.force_wait));
         const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk) : ffn_src(p, c0, 0, nk - 1);
-        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, acc);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, kt == head ? here : ahead, acc);
+        // the B blocks of the last K-tile's DMAs, before the epilogue (see gemm_bf16_ffn_kernel)
+#pragma unroll
+        for (int j = A_DMA; j < P; ++j) dma(ahead, kbase + nk + 1, j);
         {
             FusedPhase q = p.ph[c0.phase];
             q.c = static_cast<uint16_t*>(const_cast<void*>(sgpr_ptr(q.c)));
@@ -1265,17 +1277,21 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
     start_stream(c0);
 
     // One K-tile g, four k-steps: k-steps 0..2 multiply while the next one's
-    // fragments are read; k-step 3 issues a few MFMAs, waits for K-tile g + 1
-    // and joins the barrier (every wave has all of K-tile g in registers by
-    // then, so its stage is free), then, between its remaining MFMAs, starts
-    // the DMAs of K-tile g + 2 into that stage and reads K-tile g + 1's k-step
-    // 0 into set 0.
-    auto ktile = [&](int g, const FfnSrc& src, const ARows& ar, f32x16 (&acc)[TM][TN]) {
+    // fragments are read (k-step 0 also issues the B blocks of K-tile g + 1);
+    // k-step 3 issues a few MFMAs, waits for K-tile g + 1 and joins the
+    // barrier (every wave has all of K-tile g in registers by then, so its
+    // stage is free), then, between its remaining MFMAs, starts the A blocks
+    // of K-tile g + 2 into that stage and reads K-tile g + 1's k-step 0 into
+    // set 0.  prev is the source of K-tile g + 1's DMAs.
+    auto ktile = [&](int g, const FfnSrc& src, const ARows& ar, const FfnSrc& prev, f32x16 (&acc)[TM][TN]) {
         const u32x4* stage = ring + (g & 1) * SC;
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             bf_mfma1<TL>(i, fa0, fb0, acc);
             frag(stage, 1, i, fa1, fb1);
+            // the B blocks of K-tile g + 1, whose A blocks went out after the
+            // previous K-tile's barrier (from prev, the source those used)
+            if (i % (NM / B_DMA) == NM / B_DMA - 1) dma(prev, ar, g + 1, A_DMA + i / (NM / B_DMA));
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -1300,7 +1316,7 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         for (int i = 0; i < SL; ++i) {
             bf_mfma1<TL>(EARLY + i, fa1, fb1, acc);
 #pragma unroll
-            for (int j = i * P / SL; j < (i + 1) * P / SL; ++j) dma(src, ar, g + 2, j);
+            for (int j = i * A_DMA / SL; j < (i + 1) * A_DMA / SL; ++j) dma(src, ar, g + 2, j);
             frag(nstage, 0, i, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1323,14 +1339,19 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         const int split = probe ? head - 1 : head;
         const FfnSrc here = ffn_src(p, c0, 1, 0, cur * BM);
         const ARows ah = arows(here);
-        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, ah, acc);
+        for (int kt = 0; kt < split; ++kt) ktile(kbase + kt, here, ah, here, acc);
         if (probe && wave == 0) dma4_dev(done, (uint32_t)c1.mt * 4u, lds_addr(s_flag));
-        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, ah, acc);
+        for (int kt = split; kt < head; ++kt) ktile(kbase + kt, here, ah, here, acc);
         const int flag = __builtin_amdgcn_readfirstlane(s_flag[0]);
         const bool go = c1.phase == 0 || (probe && flag >= NT1 && !p.force_wait);
         const FfnSrc ahead = go ? ffn_src(p, c1, 1, -nk, (cur ^ 1) * BM) : ffn_src(p, c0, 0, nk - 1, cur * BM);
         const ARows aa = arows(ahead);
-        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, acc);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, kt == head ? here : ahead, acc);
+        // the B blocks of the last K-tile's DMAs go out now rather than after
+        // the epilogue (the next tile's first K-tile issues them again: the
+        // same bytes into the same place, landed before that K-tile's wait)
+#pragma unroll
+        for (int j = A_DMA; j < P; ++j) dma(ahead, aa, kbase + nk + 1, j);
 
         const TileCoord tc{c0.row0, c0.rows, c0.n0, c0.e};
         if (c0.phase == 0)
@@ -1510,10 +1531,13 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 // for K-tile g + 1, the barrier (every wave then holds all of K-tile g in
 // registers, so its stage and scale slot are free), and, between the remaining
 // MFMAs, the DMAs of K-tile g + 2 and the reads of K-tile g + 1's k-step 0.
+// SPLIT (two or more K-tiles per tile): only the A blocks and scales of
+// K-tile g + 2 go out there, its B blocks between the first MFMAs of K-tile
+// g + 1's k-step 0.
 // The epilogue runs between the last MFMA of a tile and the first of the next
 // while the next tile's first K-tiles are in flight; its stores count in
 // vmcnt after those DMAs, which only makes the next wait wait longer.
-template <class TL, int EPI>   // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2
+template <class TL, int EPI, bool SPLIT>   // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                           const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, void* __restrict__ C,
@@ -1522,7 +1546,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
     constexpr int A_DMA = Fp8Extra<TL>::A_DMA, B_DMA = Fp8Extra<TL>::B_DMA, P = Fp8Extra<TL>::P;
-    constexpr int SC = Fp8Extra<TL>::SC, ND = P + PS;
+    constexpr int SC = Fp8Extra<TL>::SC, ND = P + PS, ES = ND - B_DMA;   // ES: DMAs issued after a barrier when SPLIT
     constexpr int NM = TL::NM, EARLY = TL::EARLY, SL = NM - EARLY;
     static_assert(SL >= TM + TN && SL > 0, "one fragment read per MFMA slot");
     constexpr int kObufChunks = EPI == 0 ? 8 * Fp8Extra<TL>::OBUF_RR : 0;   // per wave: rows x 128 bytes of output
@@ -1641,13 +1665,17 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
 
     // one K-tile g: k-step 0 in set 0 (read during the previous K-tile), k-step 1 in set 1
-    auto ktile = [&](int g, const StreamSrc& src, const ARows& ar, f32x16 (&acc)[TM][TN]) {
+    auto ktile = [&](int g, const StreamSrc& src, const ARows& ar, const StreamSrc& prev, f32x16 (&acc)[TM][TN]) {
         const u32x4* stage = ring + (g & 1) * SC;
         const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (g & 1) * (BM + BN));
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
             fp8_mfma1<TL>(i, fa0, fb0, sa0, sb0, acc);
             frags(stage, slot, 1, i, fa1, fb1, sa1, sb1);
+            // SPLIT: the B blocks of K-tile g + 1, whose A blocks and scales
+            // went out after the previous K-tile's barrier (from prev, the
+            // source those used)
+            if (SPLIT && i < B_DMA) dma(prev, ar, g + 1, A_DMA + i);
             __builtin_amdgcn_sched_barrier(0);
         }
         fp8_mfma<TL, 0, EARLY>(fa1, fb1, sa1, sb1, acc);
@@ -1659,8 +1687,13 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 #pragma unroll
         for (int i = 0; i < SL; ++i) {
             fp8_mfma1<TL>(EARLY + i, fa1, fb1, sa1, sb1, acc);
+            if (SPLIT) {   // A blocks and scales
 #pragma unroll
-            for (int j = i * ND / SL; j < (i + 1) * ND / SL; ++j) dma(src, ar, g + 2, j);
+                for (int j = i * ES / SL; j < (i + 1) * ES / SL; ++j) dma(src, ar, g + 2, j < A_DMA ? j : j + B_DMA);
+            } else {
+#pragma unroll
+                for (int j = i * ND / SL; j < (i + 1) * ND / SL; ++j) dma(src, ar, g + 2, j);
+            }
             frags(nstage, nslot, 0, i, fa0, fb0, sa0, sb0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1707,9 +1740,17 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
         const bool has = tile + qa * G < total;
         const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
         const ARows ah = arows(here, ti % 3);
-        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, ah, acc);
+        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, ah, here, acc);
         const ARows aa = arows(ahead, has ? (ti + qa) % 3 : ti % 3);
-        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, acc);
+        for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, kt == head ? here : ahead, acc);
+        if (SPLIT) {
+            // the B blocks of the last K-tile's DMAs go out now rather than
+            // after the epilogue (the next tile's first K-tile issues them
+            // again: the same bytes into the same place, landed before that
+            // K-tile's wait)
+#pragma unroll
+            for (int j = A_DMA; j < P; ++j) dma(ahead, aa, kbase + nk + 1, j);
+        }
         // set 0 now holds k-step 0 of the next tile's first K-tile (or unused data after the last)
         fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks);
         if (tile + G >= total) break;
@@ -1792,18 +1833,27 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
         colB[i] = (uint32_t)min(n0 + 8 * (ch ^ (4 * (trB[i] & 3))), N - 8) * 2u;
     }
     const uint32_t rbA = (uint32_t)M * 2u, rbB = (uint32_t)N * 2u;
-    // K-tile kt into stage kt % 4; past the last K-tile a clamped copy lands in a stage nobody reads
-    auto issue = [&](int kt) {
+    // K-tile kt into stage kt % 4 (the A rows, then the B rows); past the last
+    // K-tile a clamped copy lands in a stage nobody reads
+    auto issue_a = [&](int kt) {
         const int kb = min(kt, nk - 1) * KT;
         const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i)
             dma16(XA, (uint32_t)(o0 + min(kb + trA[i], len - 1)) * rbA + colA[i],
                   st + (uint32_t)(wave * A_DMA + i) * 1024u);
+    };
+    auto issue_b = [&](int kt) {
+        const int kb = min(kt, nk - 1) * KT;
+        const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
 #pragma unroll
         for (int i = 0; i < B_DMA; ++i)
             dma16(XB, (uint32_t)(o0 + min(kb + trB[i], len - 1)) * rbB + colB[i],
                   st + SA + (uint32_t)(wave * B_DMA + i) * 1024u);
+    };
+    auto issue = [&](int kt) {
+        issue_a(kt);
+        issue_b(kt);
     };
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -1827,7 +1877,7 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
         for (int kt = 0; kt < nk; ++kt) {
             wait_vm<2 * P>();   // K-tile kt landed; kt + 1 and kt + 2 may still be in flight
             ring_barrier();     // every wave's reads of kt - 1 are complete (its MFMAs used them)
-            issue(kt + 3);      // into the stage of kt - 1
+            issue_a(kt + 3);    // into the stage of kt - 1 (its B rows after the first k-step's MFMAs)
             const __attribute__((address_space(3))) char* sa = lbase + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
             const __attribute__((address_space(3))) char* sb = sa + SA;
             bf16x8 fa[2][TM], fb[2][TN];
@@ -1855,12 +1905,18 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
                             if (16 * s2 + 8 * h + u >= rem) fb[s2][j][u] = (__bf16)0.0f;
             }
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
                 for (int i = 0; i < TM; ++i)
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s2][j], fa[s2][i], acc[i][j], 0, 0, 0);
+                if (s2 == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_b(kt + 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
     }
     wait_vm<0>();   // every DMA has landed: the ring is free once all waves are past their last reads
@@ -1953,8 +2009,15 @@ hipError_t launch_fp8_pipe_tile(const uint8_t* A, const uint8_t* As, const uint8
                                 void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
                                 const int32_t* host_counts, hipStream_t s, const int32_t* row_token) {
     const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
-    hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs, C, Cs,
-                       offsets, E, N, K, ldc, R, row_token);
+    // with two or more K-tiles per tile a K-tile's B blocks are issued in the
+    // next K-tile (the source of K-tile g + 1 is then the current tile's or,
+    // for the last K-tile, the next one's, as the split code assumes)
+    if (K >= 256)
+        hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI, true>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs,
+                           C, Cs, offsets, E, N, K, ldc, R, row_token);
+    else
+        hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI, false>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs,
+                           C, Cs, offsets, E, N, K, ldc, R, row_token);
     return hipGetLastError();
 }
 
