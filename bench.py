@@ -371,17 +371,7 @@ def router_stats_steps(p, d_in, packed, dev, steps: int, warmup: int, ms_device:
             "mean_router_prob_min_max": [float(st[:E].min()), float(st[:E].max())]}
 
 
-def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_device: float) -> dict:
-    """moe_backward of the last forward (f's workspace), timed like the main loop.
-
-    Useful FLOPs: the gate/up recompute 4 R d H, the data gradients 2 R d H
-    (down) + 4 R d H (gate/up), the weight gradients 2 R d H + 4 R d H, plus the
-    router's 2 T d E twice for the learned router."""
-    packed_bwd = B.pack_weights_backward(p, d_in["w_gate"], d_in["w_up"], d_in["w_down"])
-    g = torch.Generator(device="cpu").manual_seed(w.seed + 17)
-    dy = torch.randn((w.T, w.d), generator=g).to(B.storage_dtype(w.act)).to(dev)
-    bwd = B.Backward(p, dev)
-    run = lambda: bwd(f, dy, packed, packed_bwd, x=d_in["x"], w_router=d_in["w_router"])
+def _timed(run, steps: int, warmup: int) -> float:
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -391,12 +381,59 @@ def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_devic
         run()
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / steps
-    flops = 16.0 * w.R * w.d * w.H + (2 * 2.0 * w.T * w.d * w.E if w.router == "learned" else 0.0)
+    return start.elapsed_time(stop) / steps
+
+
+def kept_gate_up_steps(w, d_in, packed, dev, steps: int, warmup: int, ms_device: float, bwd: dict) -> dict:
+    """The block with MOE_KEEP_GATE_UP (the forward stores a | b, the backward
+    reads them instead of recomputing xe W1), forward and backward timed like
+    the main loop and set against the recomputing path's."""
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned", keep_gate_up=True)
+    f = B.Forward(p, dev, debug_outputs=False)
+    if p.flags & B.MOE_LOGITS_GIVEN:
+        f.logits.copy_(d_in["logits"])
+    ms_f = _timed(lambda: f(d_in["x"], packed=packed, w_router=d_in["w_router"], logits=f.logits), steps, warmup)
+    packed_bwd = B.pack_weights_backward(p, d_in["w_gate"], d_in["w_up"], d_in["w_down"])
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 17)
+    dy = torch.randn((w.T, w.d), generator=g).to(B.storage_dtype(w.act)).to(dev)
+    b = B.Backward(p, dev)
+    ms_b = _timed(lambda: b(f, dy, packed, packed_bwd, x=d_in["x"], w_router=d_in["w_router"]), steps, warmup)
+    # useful FLOPs without the recompute: data gradients 6 R d H, weight gradients 6 R d H
+    flops = 12.0 * w.R * w.d * w.H + (2 * 2.0 * w.T * w.d * w.E if w.router == "learned" else 0.0)
+    tf = flops / (ms_b * 1e-3) / 1e12
+    return {"forward_ms_per_step": round(ms_f, 5), "forward_vs_recompute_path": round(ms_f / ms_device, 4),
+            "backward_ms_per_step": round(ms_b, 5),
+            "backward_vs_recompute_path": round(ms_b / bwd["ms_per_step"], 4),
+            "forward_plus_backward_vs_recompute_path": round((ms_f + ms_b) / (ms_device + bwd["ms_per_step"]), 4),
+            "backward_useful_tflops": round(tf, 2), "backward_frac_of_peak": round(tf / 2500.0, 4),
+            "extra_forward_workspace_bytes": B.workspace_bytes(p) - B.workspace_bytes(
+                B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned"))}
+
+
+def keeps_gate_up(w) -> bool:
+    return w.act == "bf16" and w.d >= 128 and w.H >= 128
+
+
+def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_device: float) -> dict:
+    """moe_backward of the last forward (f's workspace), timed like the main loop.
+
+    Useful FLOPs (the arithmetic the block's gradients require, recompute
+    excluded): the data gradients 2 R d H (down) + 4 R d H (gate/up), the
+    weight gradients 2 R d H + 4 R d H, plus the router's 2 T d E twice for the
+    learned router.  Executed FLOPs add the gate/up recompute's 4 R d H."""
+    packed_bwd = B.pack_weights_backward(p, d_in["w_gate"], d_in["w_up"], d_in["w_down"])
+    g = torch.Generator(device="cpu").manual_seed(w.seed + 17)
+    dy = torch.randn((w.T, w.d), generator=g).to(B.storage_dtype(w.act)).to(dev)
+    bwd = B.Backward(p, dev)
+    ms = _timed(lambda: bwd(f, dy, packed, packed_bwd, x=d_in["x"], w_router=d_in["w_router"]), steps, warmup)
+    router = 2 * 2.0 * w.T * w.d * w.E if w.router == "learned" else 0.0
+    useful = 12.0 * w.R * w.d * w.H + router
+    executed = useful + 4.0 * w.R * w.d * w.H
     peak = 157.3 if w.act == "f32" else 2500.0   # MXFP8 blocks run their backward in bf16
-    tf = flops / (ms * 1e-3) / 1e12
+    tf = useful / (ms * 1e-3) / 1e12
     return {"ms_per_step": round(ms, 5), "tokens_per_s": round(w.T / (ms * 1e-3), 1),
             "useful_tflops": round(tf, 2), "frac_of_peak": round(tf / peak, 4),
+            "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 2),
             "peak_tflops": peak, "vs_forward": round(ms / ms_device, 3)}
 
 
@@ -536,6 +573,9 @@ def main(argv=None):
         result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
     elif args.with_backward:
         result["backward"] = backward_steps(w, p, d_in, packed, f, dev, args.steps, args.warmup, ms_step)
+    if "backward" in result and keeps_gate_up(w):
+        result["kept_gate_up"] = kept_gate_up_steps(w, d_in, packed, dev, args.steps, args.warmup, ms_step,
+                                                    result["backward"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, host)
     print(json.dumps(result))

@@ -82,6 +82,17 @@ extern "C" {
 /* flags */
 #define MOE_LOGITS_GIVEN     1  /* logits are an input; skip the router GEMM x . W_r     */
 #define MOE_IDENTITY_EXPERTS 2  /* test mode of moe_forward: ye := xe (f32 / bf16 only)  */
+/* MOE_KEEP_GATE_UP: moe_forward also stores the experts' pre-activations
+ * a | b = xe W1 (bf16, [T*k][2H] in the packed column order) in its
+ * workspace, and moe_backward reads them instead of recomputing xe W1.  The
+ * report treats recompute as an option that trades throughput for activation
+ * memory ("Section 24: Conclusion", Evidence 11; its per-block recompute cost
+ * about a fifth of the throughput); without this flag the library recomputes,
+ * with it the forward keeps 4 T k H more bytes.  Both ways give the same
+ * gradients bit for bit.  MOE_BF16 with d_model, d_hidden >= 128 only (the
+ * fused FFN's blocks); any other problem with the flag is MOE_ERR_DTYPE.
+ * moe_forward and moe_forward_host_sync honour it; the staged calls ignore it. */
+#define MOE_KEEP_GATE_UP     4
 
 typedef struct moe_problem {
     int32_t T;          /* tokens                                 */
@@ -90,7 +101,7 @@ typedef struct moe_problem {
     int32_t top_k;      /* k                                      */
     int32_t d_hidden;   /* H, expert SwiGLU hidden size           */
     int32_t act_dtype;  /* MOE_F32 | MOE_BF16 | MOE_MXFP8         */
-    int32_t flags;      /* MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS */
+    int32_t flags;      /* MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS | MOE_KEEP_GATE_UP */
 } moe_problem;
 
 /* Library version string and a readable name of a status code (host only). */
@@ -352,7 +363,7 @@ int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, 
  *
  *   dgate[t,j] = dy[t] . ye[pos[t,j]]          dye[pos[t,j]] = g[t,j] dy[t]
  *   dlogits[t,e_j] = g_j (dgate_j - sum_i g_i dgate_i), 0 for unselected e
- *   a | b = xe W1 (recomputed);  dh = dye W_down^T
+ *   a | b = xe W1 (recomputed, or stored with MOE_KEEP_GATE_UP);  dh = dye W_down^T
  *   da = dh b silu'(a);  db = dh silu(a);  dxe = da W_gate^T + db W_up^T
  *   dw_down[e] = h^T dye,  dw_gate[e] = xe^T da,  dw_up[e] = xe^T db
  *                                              (sums over expert e's rows)
@@ -397,8 +408,8 @@ int32_t moe_fused_status(const moe_problem* p, const void* ws, size_t ws_bytes, 
  *               unchanged since (it holds h, ye, row_token and the dispatched
  *               rows: none for the gathering bf16 blocks above, one MXFP8
  *               code row per token for MXFP8 blocks with d_model >= 256, one
- *               per routed row otherwise); fwd_ws_bytes >=
- *               moe_workspace_bytes
+ *               per routed row otherwise; with MOE_KEEP_GATE_UP also a | b);
+ *               fwd_ws_bytes >= moe_workspace_bytes
  *   dx          [T, d] out, activation type (bf16 for MOE_MXFP8)
  *   dlogits     [T, E] out, float32
  *   dw_gate, dw_up [E, d, H] out, dw_down [E, H, d] out, float32

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 ACT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
-MOE_LOGITS_GIVEN, MOE_IDENTITY_EXPERTS = 1, 2
+MOE_LOGITS_GIVEN, MOE_IDENTITY_EXPERTS, MOE_KEEP_GATE_UP = 1, 2, 4
 
 # every function the header declares, for the export check
 EXPORTS = ["moe_version", "moe_status_string", "moe_workspace_bytes", "moe_packed_weight_bytes",
@@ -47,8 +47,9 @@ class Problem(ctypes.Structure):
         return {v: k for k, v in ACT.items()}[self.act_dtype]
 
 
-def problem(T, d, E, k, H, act, logits_given=False, identity=False) -> Problem:
-    flags = (MOE_LOGITS_GIVEN if logits_given else 0) | (MOE_IDENTITY_EXPERTS if identity else 0)
+def problem(T, d, E, k, H, act, logits_given=False, identity=False, keep_gate_up=False) -> Problem:
+    flags = ((MOE_LOGITS_GIVEN if logits_given else 0) | (MOE_IDENTITY_EXPERTS if identity else 0)
+             | (MOE_KEEP_GATE_UP if keep_gate_up else 0))
     return Problem(T, d, E, k, H, ACT[act], flags)
 
 

@@ -21,7 +21,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t hist, base, psum, ppart, rwt, h, h_scale, sync, route_end, gemm_end;
-    size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, xst, ye, total;
+    size_t idx, gate, counts, offsets, pos, row_token, xe, xe_scale, xst, ye, ab, total;
 };
 
 size_t act_bytes(int act) { return act == MOE_F32 ? 4 : (act == MOE_BF16 ? 2 : 1); }
@@ -36,6 +36,10 @@ bool use_ffn(const moe_problem& p) {
 // moe_forward's fused bf16 FFN reads each expert-major row from x through
 // row_token, so that forward writes no dispatched copy xe
 bool forward_gathers(const moe_problem& p) { return use_ffn(p) && !(p.flags & MOE_IDENTITY_EXPERTS); }
+
+// MOE_KEEP_GATE_UP: moe_forward's fused FFN also stores GEMM1's pre-activations
+// a | b, and moe_backward's chain reads them instead of recomputing xe W1
+bool keeps_gate_up(const moe_problem& p) { return (p.flags & MOE_KEEP_GATE_UP) != 0; }
 
 // moe_forward of an MXFP8 block with d_model >= 256 quantises each token row
 // once (codes [T][d], per-token scales) and GEMM1 reads the code rows through
@@ -71,6 +75,7 @@ Layout layout(const moe_problem& p) {
     L.xe_scale = take(mx ? R * d / 32 : 0);
     L.xst = take(tok ? T * d / 32 : 0);   // per-token scale dwords [T][d/128]
     L.ye = take(R * d * (p.act_dtype == MOE_F32 ? 4 : 2));
+    L.ab = take(keeps_gate_up(p) ? R * 2 * H * 2 : 0);   // a | b [R][2H] bf16, packed column order
     L.total = off;
     return L;
 }
@@ -157,8 +162,12 @@ int32_t check_problem(const moe_problem* p) {
     if (p == nullptr) return MOE_ERR_NULL;
     if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16 && p->act_dtype != MOE_MXFP8)
         return MOE_ERR_DTYPE;
-    if (p->flags & ~(MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS)) return MOE_ERR_DTYPE;
+    if (p->flags & ~(MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS | MOE_KEEP_GATE_UP)) return MOE_ERR_DTYPE;
     if ((p->flags & MOE_IDENTITY_EXPERTS) && p->act_dtype == MOE_MXFP8) return MOE_ERR_DTYPE;
+    // a | b are kept by the fused bf16 FFN only (bf16 with d_model, d_hidden >= 128, real experts)
+    if ((p->flags & MOE_KEEP_GATE_UP) &&
+        (p->act_dtype != MOE_BF16 || p->d_model < 128 || p->d_hidden < 128 || (p->flags & MOE_IDENTITY_EXPERTS)))
+        return MOE_ERR_DTYPE;
     if (p->T < 1 || p->n_experts < 1 || p->n_experts > kMaxExperts || p->top_k < 1 ||
         p->top_k > std::min(p->n_experts, kMaxTopK) || p->d_model < 1 || p->d_hidden < 1)
         return MOE_ERR_SHAPE;
@@ -512,10 +521,12 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
         void* h = at(ws, L.h);
         uint8_t* hs = reinterpret_cast<uint8_t*>(at(ws, L.h_scale));
         if (ffn) {
+            uint16_t* ab = keeps_gate_up(*p) ? reinterpret_cast<uint16_t*>(at(ws, L.ab)) : nullptr;
             if ((st = launched(launch_bf16_ffn(nullptr, static_cast<const uint16_t*>(x), row_token,
                                                reinterpret_cast<const uint16_t*>(pw + P.w1), static_cast<uint16_t*>(h),
                                                reinterpret_cast<const uint16_t*>(pw + P.w2),
-                                               static_cast<uint16_t*>(ye), off, ffn_sync, R, E, d, H, host_counts, s))))
+                                               static_cast<uint16_t*>(ye), off, ffn_sync, R, E, d, H, host_counts, s,
+                                               ab))))
                 return st;
             if ((st = prof_mark("grouped_ffn", s))) return st;
         } else {
@@ -745,7 +756,18 @@ int32_t moe_backward(const moe_problem* p, const void* dy, const void* x, const 
         if ((st = launched(launch_wgrad_rows(0, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(dye), off,
                                              E, H, d, dw_down, nullptr, s))))
             return st;
-        if (chain) {
+        if (chain && keeps_gate_up(*p)) {
+            // dh = dye W_down^T with da | db from the forward's a | b in its
+            // epilogue, then dxe = (da | db) W1^T (into dye), in one launch
+            int32_t* sync = reinterpret_cast<int32_t*>(at(ws, BL.sync));
+            if ((st = launched(launch_zero_i32(sync, fused_sync_ints(R, E, 3), s)))) return st;
+            if ((st = launched(launch_bf16_bwd_chain_kept(
+                     static_cast<const uint16_t*>(dye), reinterpret_cast<const uint16_t*>(pb + BP.wd),
+                     reinterpret_cast<const uint16_t*>(at(fw, L.ab)), static_cast<uint16_t*>(ab),
+                     reinterpret_cast<const uint16_t*>(pb + BP.w1t), static_cast<uint16_t*>(dye), off, sync, R, E, d,
+                     H, s))))
+                return st;
+        } else if (chain) {
             // dh = dye W_down^T, da | db from the gate/up recompute and dh, and
             // dxe = (da | db) W1^T (into dye) in one launch
             int32_t* sync = reinterpret_cast<int32_t*>(at(ws, BL.sync));

@@ -415,7 +415,12 @@ __device__ __forceinline__ void acc_block(const f32x16& a, float (&v)[16]) {
 // values a stored recompute would hold) and, with dh [rows][N/2] (aux), C
 // receives da = dh b s (1 + a (1 - s)), db = dh a s, s = sigmoid(a), in the
 // layout of a | b.  The dh values of all of a wave's rows are requested
-// before any is used.  DEV: every store goes through the raw buffer resource
+// before any is used.  EPI 3 (SwiGLU backward from stored pre-activations):
+// acc holds dh over N hidden units; it is rounded to bf16 (the value the
+// recomputing path stores), a | b are read back from aux [rows][2N] (the
+// packed layout above), and C receives da | db as EPI 2 computes them, so the
+// two paths agree bit for bit when the stored a | b are the recompute's
+// values.  DEV: every store goes through the raw buffer resource
 // rc over C with device scope (the fused grouped GEMMs, whose next phase reads
 // C on other XCDs while the kernel runs).
 template <class TL, int EPI, bool DEV = false>
@@ -426,6 +431,7 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
                                             bool poison = false) {
     const int lane = threadIdx.x & 63;
     static_assert(EPI != 2 || TL::TN == 2, "one gate/up pair per wave row block");
+    static_assert(EPI != 3 || TL::WCOLS % 32 == 0, "whole 32-unit hidden blocks per wave");
     uint32_t dhw[EPI == 2 ? TL::TM : 1][4][2];   // dh runs: [mi][q] = 4 bf16 of h 8 q + 4 half + 0..3
     if (EPI == 2) {
         // the wave's 32 hidden units (clamped for a pair past N, whose stores are skipped)
@@ -446,7 +452,41 @@ __device__ __forceinline__ void bf_epilogue(const f32x16 (&acc)[TL::TM][TL::TN],
     for (int mi = 0; mi < TL::TM; ++mi) {
         const int r = wm * TL::WROWS + mi * 32 + (lane & 31);
         const bool valid = r < c.rows;
-        if (EPI == 2) {
+        if (EPI == 3) {
+            const int rc_row = min(r, c.rows - 1);   // clamped rows are read, not stored
+            const uint16_t* src = aux + (size_t)(c.row0 + rc_row) * (2 * N);
+            uint32_t abw[TL::TN][2][4][2];   // [block][a, b][q] = 4 bf16 of units 8 q + 4 half + 0..3
+#pragma unroll
+            for (int ni = 0; ni < TL::TN; ++ni) {
+                const int u0 = min(c.n0 + wn * TL::WCOLS + ni * 32, N - 32);   // a block past N is not stored
+#pragma unroll
+                for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint2 w = *reinterpret_cast<const uint2*>(src + 2 * u0 + 32 * ab + 8 * q + 4 * (lane >> 5));
+                        abw[ni][ab][q][0] = w.x;
+                        abw[ni][ab][q][1] = w.y;
+                    }
+            }
+#pragma unroll
+            for (int ni = 0; ni < TL::TN; ++ni) {
+                float g[16], u[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t wa = abw[ni][0][i / 4][(i % 4) / 2], wb = abw[ni][1][i / 4][(i % 4) / 2];
+                    const float a = __uint_as_float((i & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+                    const float b = __uint_as_float((i & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+                    const float d = bf16_round(acc[mi][ni][i]);
+                    const float sg = 1.0f / (1.0f + __expf(-a));
+                    g[i] = d * b * (sg * (1.0f + a * (1.0f - sg)));
+                    u[i] = d * (a * sg);
+                }
+                const int rb = wm * TL::WROWS + mi * 32;
+                store_bf16_pair_rows<16, DEV>(C, (size_t)ldc, c.row0 + rb, c.rows - rb,
+                                              2 * (c.n0 + wn * TL::WCOLS + ni * 32), 2 * N, g, u, obuf, rc, poison);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (EPI == 2) {
             float g[16], u[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -715,6 +755,7 @@ enum FusedEpi : int {
     kEpiPlain = 0,     // C = A B (bf16)
     kEpiSwiglu = 1,    // C = silu(A Bgate) * (A Bup)
     kEpiDswiglu = 2,   // C = SwiGLU backward of (A Bgate, A Bup) given dh = aux
+    kEpiDswigluKept = 3,   // C = SwiGLU backward of the stored a | b (aux) given dh = A B
 };
 
 // An instantiation compiles the epilogues of the (kind, device scope) pairs in
@@ -723,12 +764,13 @@ enum FusedEpi : int {
 constexpr int fused_kind_bit(int epi, int dev) { return 1 << (2 * epi + dev); }
 constexpr int kFusedBackwardKinds =
     fused_kind_bit(kEpiPlain, 1) | fused_kind_bit(kEpiDswiglu, 1) | fused_kind_bit(kEpiPlain, 0);
+constexpr int kFusedBackwardKeptKinds = fused_kind_bit(kEpiDswigluKept, 1) | fused_kind_bit(kEpiPlain, 0);
 
 struct FusedPhase {
     const uint16_t* a;      // A rows [R][K]
     const uint16_t* b;      // B [E][N][K]
     uint16_t* c;            // C [R][ldc]
-    const uint16_t* aux;    // kEpiDswiglu: dh [R][N/2]
+    const uint16_t* aux;    // kEpiDswiglu: dh [R][N/2]; kEpiDswigluKept: a | b [R][2N]
     int32_t* done;          // counters raised per finished tile (NULL: none)
     const int32_t* need;    // counters of the previous phase waited on (NULL: none)
     int N, K, ldc, epi;
@@ -1034,6 +1076,8 @@ void gemm_bf16_fused_kernel(FusedParams p) {
                 bf_epilogue<TL, 1, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc, poison);
             else if ((KINDS & fused_kind_bit(kEpiDswiglu, 1)) && kind == fused_kind_bit(kEpiDswiglu, 1))
                 bf_epilogue<TL, 2, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, q.aux, rc, poison);
+            else if ((KINDS & fused_kind_bit(kEpiDswigluKept, 1)) && kind == fused_kind_bit(kEpiDswigluKept, 1))
+                bf_epilogue<TL, 3, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, q.aux, rc, poison);
             else if ((KINDS & fused_kind_bit(kEpiPlain, 1)) && kind == fused_kind_bit(kEpiPlain, 1))
                 bf_epilogue<TL, 0, true>(acc, q.c, q.ldc, q.N, tc, wm, wn, ob, nullptr, rc, poison);
             else
@@ -1087,6 +1131,7 @@ struct FfnParams {
     uint16_t* h;
     const uint16_t* w2;
     uint16_t* ye;
+    uint16_t* ab;                // KEEP: the gate/up pre-activations [R][2H] (bf16 of GEMM1's accumulators)
     const int32_t* offsets;
     int32_t* sync;
     int R, E, d, H;
@@ -1140,7 +1185,7 @@ __device__ __forceinline__ FfnSrc ffn_src(const FfnParams& p, const FfnTile& t, 
 // on 64 distinct banks, and the 8 lanes of one row of a DMA write 8 distinct
 // chunks.
 
-template <class TL>
+template <class TL, bool KEEP>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_bf16_ffn_kernel(FfnParams p) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
@@ -1354,6 +1399,8 @@ void gemm_bf16_ffn_kernel(FfnParams p) {
         for (int j = A_DMA; j < P; ++j) dma(ahead, aa, kbase + nk + 1, j);
 
         const TileCoord tc{c0.row0, c0.rows, c0.n0, c0.e};
+        if (KEEP && c0.phase == 0)   // the pre-activations as GEMM1 computed them, for the backward
+            bf_epilogue<TL, 0>(acc, p.ab, 2 * p.H, 2 * p.H, tc, wm, wn, obuf + wave * kObufChunks, nullptr);
         if (c0.phase == 0)
             bf_epilogue<TL, 1, true>(acc, p.h, p.H, 2 * p.H, tc, wm, wn, obuf + wave * kObufChunks, nullptr, hrsrc);
         else
@@ -2062,12 +2109,16 @@ int ntiles(int n) { return (n + BfRing::BN - 1) / BfRing::BN; }
 
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* x, const int32_t* row_token, const uint16_t* w1,
                            uint16_t* h, const uint16_t* w2, uint16_t* ye, const int32_t* offsets, int32_t* sync,
-                           int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s) {
+                           int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s, uint16_t* ab) {
     using TL = BfRing;
     if (device_compute_units() < kXcds) return hipErrorInvalidConfiguration;
     const int grid = persistent_grid(R, E, 2 * H + d, TL::BM, TL::BN, 1, host_counts);
-    const FfnParams p{xe, x, row_token, w1, h, w2, ye, offsets, sync, R, E, d, H, ffn_spin_limit(), g_ffn_force_wait};
-    hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL>), dim3(grid), dim3(TL::NTHR), 0, s, p);
+    const FfnParams p{xe, x, row_token, w1, h, w2, ye, ab, offsets, sync, R, E, d, H, ffn_spin_limit(),
+                      g_ffn_force_wait};
+    if (ab)
+        hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL, true>), dim3(grid), dim3(TL::NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_bf16_ffn_kernel<TL, false>), dim3(grid), dim3(TL::NTHR), 0, s, p);
     return hipGetLastError();
 }
 
@@ -2085,6 +2136,20 @@ hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16
     p.offsets = offsets;
     p.sync = sync;
     return launch_fused<kFusedBackwardKinds>(p, R, E, ntiles(H) + ntiles(2 * H) + ntiles(d), nullptr, s);
+}
+
+hipError_t launch_bf16_bwd_chain_kept(const uint16_t* dye, const uint16_t* wd, const uint16_t* ab, uint16_t* dab,
+                                      const uint16_t* w1t, uint16_t* dxe, const int32_t* offsets, int32_t* sync,
+                                      int R, int E, int d, int H, hipStream_t s) {
+    int32_t* done0 = sync + kSyncHead;
+    FusedParams p{};
+    // dh = dye W_down^T with da | db from the stored a | b in its epilogue, then dxe = (da | db) W1^T
+    p.ph[0] = FusedPhase{dye, wd, dab, ab, done0, nullptr, H, d, 2 * H, kEpiDswigluKept, 0, 1};
+    p.ph[1] = FusedPhase{dab, w1t, dxe, nullptr, nullptr, done0, d, 2 * H, d, kEpiPlain, ntiles(H), 0};
+    p.nph = 2;
+    p.offsets = offsets;
+    p.sync = sync;
+    return launch_fused<kFusedBackwardKeptKinds>(p, R, E, ntiles(H) + ntiles(d), nullptr, s);
 }
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,

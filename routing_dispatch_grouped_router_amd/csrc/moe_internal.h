@@ -120,13 +120,23 @@ inline int fused_sync_ints(int R, int E, int phases) { return kSyncHead + (phase
 inline int ffn_sync_ints(int R, int E) { return fused_sync_ints(R, E, 2); }
 // The fused bf16 expert FFN.  GEMM1's A rows are xe [R][d], or, with row_token
 // non-NULL, row row_token[r] of the token rows x [T][d] for expert-major row r
-// (the rows the dispatch would have copied into xe, read in place).
+// (the rows the dispatch would have copied into xe, read in place).  With ab
+// non-NULL GEMM1 also stores its pre-activations a | b [R][2H] (bf16, the
+// packed column order of W1) for the backward.
 hipError_t launch_bf16_ffn(const uint16_t* xe, const uint16_t* x, const int32_t* row_token, const uint16_t* w1,
                            uint16_t* h, const uint16_t* w2, uint16_t* ye, const int32_t* offsets, int32_t* sync,
-                           int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s);
+                           int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s,
+                           uint16_t* ab = nullptr);
+// The backward's data-gradient GEMMs in one launch: dh = dye W_down^T, a | b
+// = xe W1 recomputed with da | db in its epilogue, dxe = (da | db) W1^T.
 hipError_t launch_bf16_bwd_chain(const uint16_t* dye, const uint16_t* wd, uint16_t* dh, const uint16_t* xe,
                                  const uint16_t* w1, uint16_t* dab, const uint16_t* w1t, uint16_t* dxe,
                                  const int32_t* offsets, int32_t* sync, int R, int E, int d, int H, hipStream_t s);
+// The same from the forward's stored a | b: dh = dye W_down^T with da | db in
+// its epilogue (no recompute), then dxe = (da | db) W1^T.
+hipError_t launch_bf16_bwd_chain_kept(const uint16_t* dye, const uint16_t* wd, const uint16_t* ab, uint16_t* dab,
+                                      const uint16_t* w1t, uint16_t* dxe, const int32_t* offsets, int32_t* sync,
+                                      int R, int E, int d, int H, hipStream_t s);
 // Test hooks of the fused GEMMs: force_wait nonzero makes every dependent tile take the
 // wait-and-restart path; give_up nonzero makes every such wait end at once as if its bound
 // had been reached (error word raised, the tile's output written as NaN).

@@ -74,6 +74,31 @@ def test_bad_dtype_and_flags(lib):
     assert lib.moe_workspace_bytes(None, ctypes.byref(n)) == -1
 
 
+@pytest.mark.parametrize("T, d, E, k, H, act, identity, code", [
+    (512, 256, 8, 2, 256, "bf16", False, 0),      # the fused bf16 FFN: a | b kept
+    (512, 128, 8, 2, 128, "bf16", False, 0),
+    (512, 64, 8, 2, 256, "bf16", False, -3),      # d_model < 128: no fused FFN
+    (512, 256, 8, 2, 64, "bf16", False, -3),      # d_hidden < 128
+    (512, 256, 8, 2, 256, "f32", False, -3),
+    (512, 256, 8, 2, 256, "mxfp8", False, -3),
+    (512, 256, 8, 2, 256, "bf16", True, -3),      # identity experts compute no a | b
+])
+def test_keep_gate_up_flag(lib, T, d, E, k, H, act, identity, code):
+    """MOE_KEEP_GATE_UP is valid for the fused bf16 FFN's problems only; there
+    the forward workspace grows by the T k 2H bf16 pre-activations, and the
+    backward workspace does not change."""
+    p = B.problem(T, d, E, k, H, act, logits_given=True, identity=identity, keep_gate_up=True)
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == code
+    if code:
+        assert lib.moe_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == code
+        return
+    plain = B.problem(T, d, E, k, H, act, logits_given=True)
+    ab = T * k * 2 * H * 2
+    assert B.workspace_bytes(p) - B.workspace_bytes(plain) == -(-ab // 256) * 256
+    assert B.backward_workspace_bytes(p) == B.backward_workspace_bytes(plain)
+
+
 def test_null_pointers_rejected_before_any_launch(lib):
     p = _prob(logits_given=True)
     V = ctypes.c_void_p

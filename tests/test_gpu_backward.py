@@ -63,10 +63,10 @@ CASES = [
 ]
 
 
-def _run(w):
+def _run(w, keep=False):
     host = W.make_inputs(w)
     dev = {k: (None if v is None else v.to(DEV)) for k, v in host.items()}
-    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned")
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned", keep_gate_up=keep)
     packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
     packed_bwd = B.pack_weights_backward(p, dev["w_gate"], dev["w_up"], dev["w_down"])
     fwd = B.Forward(p, DEV)
@@ -204,3 +204,67 @@ def test_backward_chain_wait_path(cap):
     for k in normal[0]:
         if normal[0][k] is not None:
             assert torch.equal(normal[0][k], waited[0][k]), f"{k} changed on the wait-and-restart path"
+
+
+# --------------------------------------------------------------------------- kept pre-activations
+
+KEEP_CASES = [c for c in CASES if c.act == "bf16" and c.d >= 128 and c.H >= 128]
+
+
+def _kept_gate_up(fwd, w):
+    """a | b as the forward stored them: the last region of its workspace,
+    [T k][2H] bf16 (the workspace layout puts it after every other region)."""
+    n = w.R * 2 * w.H * 2
+    off = fwd.ws.numel() - (-(-n // 256) * 256)
+    return fwd.ws[off:off + n].view(torch.bfloat16).view(w.R, 2 * w.H)
+
+
+def _packed_gate_up_ref(host, fwd, w):
+    """xe W_gate | xe W_up per expert-major row in float64, columns in the
+    packed order (32 gate then 32 up hidden units per 64)."""
+    pos = fwd.pos.cpu().numpy().astype(np.int64)
+    offsets = fwd.offsets.cpu().numpy().astype(np.int64)
+    row_token = np.empty(w.R, np.int64)
+    row_token[pos.reshape(-1)] = np.repeat(np.arange(w.T), w.k)
+    x = W.as_f64(host["x"])
+    ref = np.zeros((w.R, 2 * w.H))
+    for e in range(w.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        xe = x[row_token[lo:hi]]
+        a = xe @ W.as_f64(host["w_gate"][e])
+        b = xe @ W.as_f64(host["w_up"][e])
+        n = hi - lo
+        ref[lo:hi] = np.stack([a.reshape(n, w.H // 32, 32), b.reshape(n, w.H // 32, 32)], axis=2).reshape(n, 2 * w.H)
+    return ref
+
+
+def _check_kept(w):
+    host, fwd0, _, rec = _run(w)
+    host, fwd1, _, kept = _run(w, keep=True)
+    assert torch.equal(fwd0.y, fwd1.y), "keeping a | b changed the forward output"
+    for k in rec[0]:
+        if rec[0][k] is not None:
+            assert torch.equal(rec[0][k], kept[0][k]), f"{k}: kept a | b and recompute differ"
+    return host, fwd1
+
+
+@pytest.mark.parametrize("w", KEEP_CASES, ids=[c.name for c in KEEP_CASES])
+def test_backward_kept_gate_up(w):
+    """MOE_KEEP_GATE_UP: the forward's fused FFN stores a | b (checked against
+    xe W1 in float64, in the packed column order), the backward reads them
+    instead of recomputing, and y and every gradient equal the recomputing
+    path's bit for bit."""
+    print(f"[backward kept a|b] {w.describe()}", flush=True)
+    host, fwd = _check_kept(w)
+    ab = _kept_gate_up(fwd, w).float().cpu().numpy().astype(np.float64)
+    _check("stored a | b", ab, _packed_gate_up_ref(host, fwd, w), w.act)
+
+
+@pytest.mark.slow
+def test_full_size_backward_kept_gate_up():
+    """The same bitwise agreement at the 8-expert benchmark block."""
+    w = W.CONFIGS["bf16_e8"]
+    print(f"[full backward kept a|b] {w.describe()}", flush=True)
+    _check_kept(w)
