@@ -1974,7 +1974,8 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
     // swizzled by the row so 16 lanes of a write hit 64 banks); it reads back
     // chunk l % 16 of row l / 16 + 4 t, so 16 lanes cover a row's 256 bytes and
     // every store instruction writes whole 128-byte lines of 4 rows (direct
-    // stores from the MFMA layout wrote 32-byte pieces of 32 rows).
+    // stores from the MFMA layout wrote 32-byte pieces of 32 rows).  The stores
+    // are non-temporal: nothing in the backward reads the weight gradients.
     static_assert(WROWS == 128 && WCOLS == 64 && TN == 2 && NW * 16384 <= STAGES * SBYTES, "epilogue staging");
     const int half = lane >> 5;
     u32x4* stg = reinterpret_cast<u32x4*>(ring) + wave * 1024;
@@ -2007,11 +2008,11 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
             const int m = mrow0 + 64 * rho + r;
             if (m >= M || n >= N) continue;
             if (OMAP == 0) {
-                *reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n));
             } else {
                 const int Hh = N / 2, hh = 32 * (n / 64) + n % 32;
                 float* dst = ((n / 32) & 1) ? C2 : C;
-                *reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh));
             }
         }
         asm volatile("" ::: "memory");   // the next round's writes stay after these reads
