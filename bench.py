@@ -411,7 +411,7 @@ def kept_gate_up_steps(w, d_in, packed, dev, steps: int, warmup: int, ms_device:
 
 
 def keeps_gate_up(w) -> bool:
-    return w.act == "bf16" and w.d >= 128 and w.H >= 128
+    return (w.act == "bf16" and w.d >= 128 and w.H >= 128) or w.act == "mxfp8"
 
 
 def backward_steps(w, p, d_in, packed, f, dev, steps: int, warmup: int, ms_device: float) -> dict:

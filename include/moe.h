@@ -83,15 +83,18 @@ extern "C" {
 #define MOE_LOGITS_GIVEN     1  /* logits are an input; skip the router GEMM x . W_r     */
 #define MOE_IDENTITY_EXPERTS 2  /* test mode of moe_forward: ye := xe (f32 / bf16 only)  */
 /* MOE_KEEP_GATE_UP: moe_forward also stores the experts' pre-activations
- * a | b = xe W1 (bf16, [T*k][2H] in the packed column order) in its
- * workspace, and moe_backward reads them instead of recomputing xe W1.  The
- * report treats recompute as an option that trades throughput for activation
- * memory ("Section 24: Conclusion", Evidence 11; its per-block recompute cost
- * about a fifth of the throughput); without this flag the library recomputes,
- * with it the forward keeps 4 T k H more bytes.  Both ways give the same
- * gradients bit for bit.  MOE_BF16 with d_model, d_hidden >= 128 only (the
- * fused FFN's blocks); any other problem with the flag is MOE_ERR_DTYPE.
- * moe_forward and moe_forward_host_sync honour it; the staged calls ignore it. */
+ * a | b = xe W1 (bf16 of GEMM1's float32 accumulators, [T*k][2H] in the
+ * packed column order) in its workspace, and moe_backward reads them instead
+ * of recomputing xe W1.  The report treats recompute as an option that trades
+ * throughput for activation memory ("Section 24: Conclusion", Evidence 11;
+ * its per-block recompute cost about a fifth of the throughput); without this
+ * flag the library recomputes, with it the forward keeps 4 T k H more bytes.
+ * MOE_BF16 (d_model, d_hidden >= 128: the fused FFN's blocks): the gradients
+ * are bit for bit those of the recomputing path.  MOE_MXFP8: the stored a | b
+ * come from the forward's MXFP8 GEMM, the recompute is a bf16 GEMM of the
+ * dequantised values, so the gradients differ by their accumulation order
+ * only.  Any other problem with the flag is MOE_ERR_DTYPE.  moe_forward and
+ * moe_forward_host_sync honour it; the staged calls ignore it. */
 #define MOE_KEEP_GATE_UP     4
 
 typedef struct moe_problem {

@@ -37,8 +37,9 @@ bool use_ffn(const moe_problem& p) {
 // row_token, so that forward writes no dispatched copy xe
 bool forward_gathers(const moe_problem& p) { return use_ffn(p) && !(p.flags & MOE_IDENTITY_EXPERTS); }
 
-// MOE_KEEP_GATE_UP: moe_forward's fused FFN also stores GEMM1's pre-activations
-// a | b, and moe_backward's chain reads them instead of recomputing xe W1
+// MOE_KEEP_GATE_UP: moe_forward's GEMM1 (the fused bf16 FFN's, or the MXFP8
+// one) also stores its pre-activations a | b as bf16, and moe_backward's chain
+// reads them instead of recomputing xe W1
 bool keeps_gate_up(const moe_problem& p) { return (p.flags & MOE_KEEP_GATE_UP) != 0; }
 
 // moe_forward of an MXFP8 block with d_model >= 256 quantises each token row
@@ -164,9 +165,10 @@ int32_t check_problem(const moe_problem* p) {
         return MOE_ERR_DTYPE;
     if (p->flags & ~(MOE_LOGITS_GIVEN | MOE_IDENTITY_EXPERTS | MOE_KEEP_GATE_UP)) return MOE_ERR_DTYPE;
     if ((p->flags & MOE_IDENTITY_EXPERTS) && p->act_dtype == MOE_MXFP8) return MOE_ERR_DTYPE;
-    // a | b are kept by the fused bf16 FFN only (bf16 with d_model, d_hidden >= 128, real experts)
+    // a | b are kept by the fused bf16 FFN (bf16 with d_model, d_hidden >= 128) and the MXFP8 GEMM1
     if ((p->flags & MOE_KEEP_GATE_UP) &&
-        (p->act_dtype != MOE_BF16 || p->d_model < 128 || p->d_hidden < 128 || (p->flags & MOE_IDENTITY_EXPERTS)))
+        (p->act_dtype == MOE_F32 || (p->flags & MOE_IDENTITY_EXPERTS) ||
+         (p->act_dtype == MOE_BF16 && (p->d_model < 128 || p->d_hidden < 128))))
         return MOE_ERR_DTYPE;
     if (p->T < 1 || p->n_experts < 1 || p->n_experts > kMaxExperts || p->top_k < 1 ||
         p->top_k > std::min(p->n_experts, kMaxTopK) || p->d_model < 1 || p->d_hidden < 1)
@@ -530,9 +532,10 @@ int32_t forward_impl(const moe_problem* p, const void* x, const void* w_router, 
                 return st;
             if ((st = prof_mark("grouped_ffn", s))) return st;
         } else {
+            uint16_t* ab = keeps_gate_up(*p) ? reinterpret_cast<uint16_t*>(at(ws, L.ab)) : nullptr;
             if ((st = launched(launch_gemm1(act, xe, xs, pw + P.w1, reinterpret_cast<const uint8_t*>(pw + P.s1),
                                             off, h, hs, R, E, d, H, host_counts, s,
-                                            forward_quantises_tokens(*p) ? row_token : nullptr))))
+                                            forward_quantises_tokens(*p) ? row_token : nullptr, ab))))
                 return st;
             if ((st = prof_mark("gemm1_gate_up_swiglu", s))) return st;
             if ((st = launched(launch_gemm2(act, h, hs, pw + P.w2, reinterpret_cast<const uint8_t*>(pw + P.s2),

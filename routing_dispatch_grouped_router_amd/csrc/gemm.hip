@@ -163,8 +163,9 @@ int persistent_grid(int R, int E, int N, int BM, int BN, int per_cu, const int32
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                         int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s,
-                        const int32_t* row_token) {
+                        const int32_t* row_token, uint16_t* ab) {
     const int N = 2 * H, K = d;
+    if (ab && act != kMXFP8) return hipErrorInvalidValue;   // a | b are kept by the MXFP8 kernel only
     if (act == kBF16) {
         return launch_bf16_pipe(1, static_cast<const uint16_t*>(xe), static_cast<const uint16_t*>(w1),
                                 static_cast<uint16_t*>(h), offsets, R, E, N, K, H, host_counts, s);
@@ -175,7 +176,7 @@ hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const 
     } else {
         if (row_token && K / 128 < 2) return hipErrorInvalidValue;   // the row tables run one tile ahead
         return launch_fp8_pipe(1, static_cast<const uint8_t*>(xe), xe_scale, static_cast<const uint8_t*>(w1), w1_scale,
-                               h, h_scale, offsets, R, E, N, K, H, host_counts, s, row_token);
+                               h, h_scale, offsets, R, E, N, K, H, host_counts, s, row_token, ab);
     }
     return hipGetLastError();
 }

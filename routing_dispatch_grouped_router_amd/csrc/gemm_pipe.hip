@@ -1512,11 +1512,14 @@ __device__ __forceinline__ void fp8_mfma1(int i, const i32x8 (&fa)[TL::TM], cons
 // * up per gate/up column pair, quantised to MXFP8 along h: each 32-column
 // block of one row is split over lanes l and l ^ 32, which agree on the block
 // maximum, take the shared exponent floor(log2 amax) - 8, and encode with
-// e4m3x4 (saturating round-to-nearest-even E4M3).
-template <class TL, int EPI>
+// e4m3x4 (saturating round-to-nearest-even E4M3).  KEEP (EPI 1): the gate/up
+// accumulators are also stored as bf16 a | b [rows][N] (the pre-activations,
+// for the backward) through the staged row stores.
+template <class TL, int EPI, bool KEEP = false>
 __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], void* __restrict__ C,
                                              uint8_t* __restrict__ Cs, int ldc, int N, int R, const TileCoord& c,
-                                             int wm, int wn, u32x4* __restrict__ obuf) {
+                                             int wm, int wn, u32x4* __restrict__ obuf,
+                                             uint16_t* __restrict__ ab = nullptr) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
 #pragma unroll
@@ -1542,6 +1545,11 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
                 float v[16], u[16];
                 acc_block<TL>(acc[mi][2 * np], v);
                 acc_block<TL>(acc[mi][2 * np + 1], u);
+                if constexpr (KEEP) {
+                    const int rb = wm * TL::WROWS + mi * 32;
+                    store_bf16_pair_rows<Fp8Extra<TL>::OBUF_RR>(ab, (size_t)N, c.row0 + rb, c.rows - rb, pc, N, v, u,
+                                                                obuf);
+                }
                 float amax = 0.f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -1584,19 +1592,20 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 // The epilogue runs between the last MFMA of a tile and the first of the next
 // while the next tile's first K-tiles are in flight; its stores count in
 // vmcnt after those DMAs, which only makes the next wait wait longer.
-template <class TL, int EPI, bool SPLIT>   // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2
+// EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2, with KEEP also a | b into ab
+template <class TL, int EPI, bool SPLIT, bool KEEP>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
 void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                           const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, void* __restrict__ C,
                           uint8_t* __restrict__ Cs, const int32_t* __restrict__ offsets, int E, int N, int K,
-                          int ldc, int R, const int32_t* __restrict__ row_token) {
+                          int ldc, int R, const int32_t* __restrict__ row_token, uint16_t* __restrict__ ab) {
     constexpr int BM = TL::BM, BN = TL::BN, NTHR = TL::NTHR, TM = TL::TM, TN = TL::TN;
     constexpr int SR = Fp8Extra<TL>::SR, PS = Fp8Extra<TL>::PS;
     constexpr int A_DMA = Fp8Extra<TL>::A_DMA, B_DMA = Fp8Extra<TL>::B_DMA, P = Fp8Extra<TL>::P;
     constexpr int SC = Fp8Extra<TL>::SC, ND = P + PS, ES = ND - B_DMA;   // ES: DMAs issued after a barrier when SPLIT
     constexpr int NM = TL::NM, EARLY = TL::EARLY, SL = NM - EARLY;
     static_assert(SL >= TM + TN && SL > 0, "one fragment read per MFMA slot");
-    constexpr int kObufChunks = EPI == 0 ? 8 * Fp8Extra<TL>::OBUF_RR : 0;   // per wave: rows x 128 bytes of output
+    constexpr int kObufChunks = EPI == 0 || KEEP ? 8 * Fp8Extra<TL>::OBUF_RR : 0;   // per wave: rows x 128 bytes
     __shared__ u32x4 ring[2 * SC];
     __shared__ uint32_t sring[2 * (BM + BN)];     // two scale slots: A rows then B rows
     __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
@@ -1799,7 +1808,7 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
             for (int j = A_DMA; j < P; ++j) dma(ahead, aa, kbase + nk + 1, j);
         }
         // set 0 now holds k-step 0 of the next tile's first K-tile (or unused data after the last)
-        fp8_epilogue<TL, EPI>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks);
+        fp8_epilogue<TL, EPI, KEEP>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks, ab);
         if (tile + G >= total) break;
         tile += G;
         c0 = c1;
@@ -2052,20 +2061,20 @@ hipError_t launch_bf16_pipe_tile(const uint16_t* A, const uint16_t* Bw, uint16_t
     return hipGetLastError();
 }
 
-template <class TL, int EPI>
+template <class TL, int EPI, bool KEEP>
 hipError_t launch_fp8_pipe_tile(const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                                 void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                                const int32_t* host_counts, hipStream_t s, const int32_t* row_token) {
+                                const int32_t* host_counts, hipStream_t s, const int32_t* row_token, uint16_t* ab) {
     const int grid = persistent_grid(R, E, N, TL::BM, TL::BN, 1, host_counts);
     // with two or more K-tiles per tile a K-tile's B blocks are issued in the
     // next K-tile (the source of K-tile g + 1 is then the current tile's or,
     // for the last K-tile, the next one's, as the split code assumes)
     if (K >= 256)
-        hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI, true>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs,
-                           C, Cs, offsets, E, N, K, ldc, R, row_token);
+        hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI, true, KEEP>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw,
+                           Bs, C, Cs, offsets, E, N, K, ldc, R, row_token, ab);
     else
-        hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI, false>), dim3(grid), dim3(TL::NTHR), 0, s, A, As, Bw, Bs,
-                           C, Cs, offsets, E, N, K, ldc, R, row_token);
+        hipLaunchKernelGGL((gemm_fp8_pipe_kernel<TL, EPI, false, KEEP>), dim3(grid), dim3(TL::NTHR), 0, s, A, As,
+                           Bw, Bs, C, Cs, offsets, E, N, K, ldc, R, row_token, ab);
     return hipGetLastError();
 }
 
@@ -2155,12 +2164,15 @@ hipError_t launch_bf16_bwd_chain_kept(const uint16_t* dye, const uint16_t* wd, c
 
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                           const int32_t* host_counts, hipStream_t s, const int32_t* row_token) {
+                           const int32_t* host_counts, hipStream_t s, const int32_t* row_token, uint16_t* ab) {
+    if (epi == 1 && ab)
+        return launch_fp8_pipe_tile<Fp8Ring, 1, true>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s,
+                                                      row_token, ab);
     if (epi == 1)
-        return launch_fp8_pipe_tile<Fp8Ring, 1>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s,
-                                                row_token);
-    return launch_fp8_pipe_tile<Fp8Ring, 0>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s,
-                                            nullptr);
+        return launch_fp8_pipe_tile<Fp8Ring, 1, false>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts,
+                                                       s, row_token, nullptr);
+    return launch_fp8_pipe_tile<Fp8Ring, 0, false>(A, As, Bw, Bs, C, Cs, offsets, R, E, N, K, ldc, host_counts, s,
+                                                   nullptr, nullptr);
 }
 
 }  // namespace moe

@@ -82,7 +82,7 @@ hipError_t launch_combine(int act, const void* ye, const float* gate, const int3
 hipError_t launch_gemm1(int act, const void* xe, const uint8_t* xe_scale, const void* w1,
                         const uint8_t* w1_scale, const int32_t* offsets, void* h, uint8_t* h_scale,
                         int R, int E, int d, int H, const int32_t* host_counts, hipStream_t s,
-                        const int32_t* row_token = nullptr);
+                        const int32_t* row_token = nullptr, uint16_t* ab = nullptr);
 hipError_t launch_gemm2(int act, const void* h, const uint8_t* h_scale, const void* w2,
                         const uint8_t* w2_scale, const int32_t* offsets, void* ye, int R, int E,
                         int d, int H, const int32_t* host_counts, hipStream_t s);
@@ -149,10 +149,12 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t s);
 // scales stored [K/128][rows][4] (A: R rows; B: per expert, N rows).
 // epi 0: bf16 C [.., ldc];  epi 1: SwiGLU then MXFP8 C codes [.., ldc] + scales Cs [ldc/128][R][4].
 // epi 1 with row_token non-NULL: A row r is row row_token[r] of a token matrix
-// A [T][K] (K >= 256), while As stays per expert-major row.
+// A [T][K] (K >= 256), while As stays per expert-major row.  epi 1 with ab
+// non-NULL: the gate/up accumulators also go to ab [R][N] as bf16.
 hipError_t launch_fp8_pipe(int epi, const uint8_t* A, const uint8_t* As, const uint8_t* Bw, const uint8_t* Bs,
                            void* C, uint8_t* Cs, const int32_t* offsets, int R, int E, int N, int K, int ldc,
-                           const int32_t* host_counts, hipStream_t s, const int32_t* row_token = nullptr);
+                           const int32_t* host_counts, hipStream_t s, const int32_t* row_token = nullptr,
+                           uint16_t* ab = nullptr);
 
 // Weight packing (setup).
 hipError_t launch_pack(int act, const void* w_gate, const void* w_up, const void* w_down, void* w1,

@@ -80,13 +80,13 @@ def test_bad_dtype_and_flags(lib):
     (512, 64, 8, 2, 256, "bf16", False, -3),      # d_model < 128: no fused FFN
     (512, 256, 8, 2, 64, "bf16", False, -3),      # d_hidden < 128
     (512, 256, 8, 2, 256, "f32", False, -3),
-    (512, 256, 8, 2, 256, "mxfp8", False, -3),
+    (512, 256, 8, 2, 256, "mxfp8", False, 0),     # the MXFP8 GEMM1 keeps them too
     (512, 256, 8, 2, 256, "bf16", True, -3),      # identity experts compute no a | b
 ])
 def test_keep_gate_up_flag(lib, T, d, E, k, H, act, identity, code):
-    """MOE_KEEP_GATE_UP is valid for the fused bf16 FFN's problems only; there
-    the forward workspace grows by the T k 2H bf16 pre-activations, and the
-    backward workspace does not change."""
+    """MOE_KEEP_GATE_UP is valid for the fused bf16 FFN's problems and MXFP8;
+    there the forward workspace grows by the T k 2H bf16 pre-activations, and
+    the backward workspace does not change."""
     p = B.problem(T, d, E, k, H, act, logits_given=True, identity=identity, keep_gate_up=True)
     n = ctypes.c_size_t()
     assert lib.moe_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == code

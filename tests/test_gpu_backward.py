@@ -90,7 +90,10 @@ def test_backward_against_oracle(w):
     for k in outs[0]:
         if outs[0][k] is not None:
             assert torch.equal(outs[0][k], outs[1][k]), f"{k} differs between two calls"
-    g = outs[0]
+    _against_oracle(w, host, fwd, dy_host, outs[0])
+
+
+def _against_oracle(w, host, fwd, dy_host, g):
     logits = _f64(fwd.logits)
     wg, wu, wd = (W.as_f64(host[n]) for n in ("w_gate", "w_up", "w_down"))
     x = W.as_f64(host["x"])
@@ -268,3 +271,40 @@ def test_full_size_backward_kept_gate_up():
     w = W.CONFIGS["bf16_e8"]
     print(f"[full backward kept a|b] {w.describe()}", flush=True)
     _check_kept(w)
+
+
+MX_KEEP_CASES = [c for c in CASES if c.act == "mxfp8"]
+
+
+@pytest.mark.parametrize("w", MX_KEEP_CASES, ids=[c.name for c in MX_KEEP_CASES])
+def test_backward_kept_gate_up_mxfp8(w):
+    """MOE_KEEP_GATE_UP on MXFP8 blocks: the MXFP8 GEMM1 stores its gate/up
+    accumulators as bf16 a | b (checked against the MXFP8 values of xe and W1
+    multiplied in float64), the forward output is unchanged, and the backward
+    from the stored a | b meets the oracle's bars like the recomputing one."""
+    print(f"[backward kept a|b mxfp8] {w.describe()}", flush=True)
+    host, fwd0, _, _ = _run(w)
+    host, fwd, dy_host, outs = _run(w, keep=True)
+    assert torch.equal(fwd0.y, fwd.y), "keeping a | b changed the forward output"
+    for k in outs[0]:
+        if outs[0][k] is not None:
+            assert torch.equal(outs[0][k], outs[1][k]), f"{k} differs between two calls"
+    _against_oracle(w, host, fwd, dy_host, outs[0])
+    # the stored a | b: MXFP8 token rows times the MXFP8 expert weights
+    pos = fwd.pos.cpu().numpy().astype(np.int64)
+    offsets = fwd.offsets.cpu().numpy().astype(np.int64)
+    row_token = np.empty(w.R, np.int64)
+    row_token[pos.reshape(-1)] = np.repeat(np.arange(w.T), w.k)
+    xq = MX.fake_quantize(W.as_f64(host["x"]), axis=1)
+    wg, wu, wd = (W.as_f64(host[n]) for n in ("w_gate", "w_up", "w_down"))
+    ref = np.zeros((w.R, 2 * w.H))
+    for e in range(w.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        qg, qu, _ = O.expert_weights(wg, wu, wd, e, "mxfp8")
+        xe = xq[row_token[lo:hi]]
+        a, b, n = xe @ qg, xe @ qu, hi - lo
+        ref[lo:hi] = np.stack([a.reshape(n, w.H // 32, 32), b.reshape(n, w.H // 32, 32)], axis=2).reshape(n, 2 * w.H)
+    ab = _kept_gate_up(fwd, w).float().cpu().numpy().astype(np.float64)
+    _check("stored a | b", ab, ref, "bf16")
