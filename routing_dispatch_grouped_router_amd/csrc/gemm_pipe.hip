@@ -2010,18 +2010,25 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
         asm volatile("" ::: "memory");
         const int c = lane & 15;
         const int n = ncol0 + 4 * c;
+        // all 16 reads first, then the stores: a read feeding each store in turn
+        // would wait out the LDS latency 16 times
+        u32x4 v[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int r = (lane >> 4) + 4 * t;
-            const u32x4 v = stg[r * 16 + (c ^ (r & 15))];
-            const int m = mrow0 + 64 * rho + r;
-            if (m >= M || n >= N) continue;
-            if (OMAP == 0) {
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n));
-            } else {
-                const int Hh = N / 2, hh = 32 * (n / 64) + n % 32;
-                float* dst = ((n / 32) & 1) ? C2 : C;
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh));
+            v[t] = stg[r * 16 + (c ^ (r & 15))];
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int m = mrow0 + 64 * rho + (lane >> 4) + 4 * t;
+            if (m < M && n < N) {
+                if (OMAP == 0) {
+                    __builtin_nontemporal_store(v[t], reinterpret_cast<u32x4*>(C + ((size_t)e * M + m) * N + n));
+                } else {
+                    const int Hh = N / 2, hh = 32 * (n / 64) + n % 32;
+                    float* dst = ((n / 32) & 1) ? C2 : C;
+                    __builtin_nontemporal_store(v[t], reinterpret_cast<u32x4*>(dst + ((size_t)e * M + m) * Hh + hh));
+                }
             }
         }
         asm volatile("" ::: "memory");   // the next round's writes stay after these reads
