@@ -1829,9 +1829,12 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
 //   C[e][m][n] = sum over rows r in [offsets[e], offsets[e+1]) of XA[r][m] XB[r][n]
 // with the activations as stored, XA [R][M] and XB [R][N], so no transposed
 // copy is made.  Workgroup tile 256 x 256, 8 waves of 128 x 64, a 4-stage
-// ring of K-tiles loaded with global_load_lds, one barrier per K-tile: after
-// it, the DMA of K-tile kt + 3 refills the stage every wave finished reading
-// in the previous step.  An expert without rows writes zeros.  OMAP 0:
+// ring of K-tiles loaded with global_load_lds, one barrier per K-tile, in the
+// schedule of the forward kernels: k-step 0 multiplies while k-step 1's
+// fragments are read; k-step 1 issues a few MFMAs, waits for K-tile kt + 1,
+// joins the barrier (every wave then holds all of kt in registers), and,
+// between its remaining MFMAs, sends the DMAs of K-tile kt + 4 into kt's stage
+// and reads kt + 1's k-step 0.  An expert without rows writes zeros.  OMAP 0:
 // C[e][m][n].  OMAP 1: the N axis interleaves gate and up columns (32 + 32 per
 // 64); column n goes to C (gate) or C2 (up) [e][m][h], h = 32 (n / 64) + n %
 // 32.  Rows or columns past M, N are clamped in the loads and not stored.  A K-tile is 32 rows:
@@ -1889,27 +1892,24 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
         colB[i] = (uint32_t)min(n0 + 8 * (ch ^ (4 * (trB[i] & 3))), N - 8) * 2u;
     }
     const uint32_t rbA = (uint32_t)M * 2u, rbB = (uint32_t)N * 2u;
-    // K-tile kt into stage kt % 4 (the A rows, then the B rows); past the last
-    // K-tile a clamped copy lands in a stage nobody reads
-    auto issue_a = [&](int kt) {
+    // DMA i of K-tile kt's A rows (or B rows) into stage kt % 4; past the last
+    // K-tile a clamped copy lands in a stage whose reads go unused
+    auto dma_a = [&](int kt, int i) {
         const int kb = min(kt, nk - 1) * KT;
         const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
-#pragma unroll
-        for (int i = 0; i < A_DMA; ++i)
-            dma16(XA, (uint32_t)(o0 + min(kb + trA[i], len - 1)) * rbA + colA[i],
-                  st + (uint32_t)(wave * A_DMA + i) * 1024u);
+        dma16(XA, (uint32_t)(o0 + min(kb + trA[i], len - 1)) * rbA + colA[i], st + (uint32_t)(wave * A_DMA + i) * 1024u);
     };
-    auto issue_b = [&](int kt) {
+    auto dma_b = [&](int kt, int i) {
         const int kb = min(kt, nk - 1) * KT;
         const uint32_t st = ring_lds + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
-#pragma unroll
-        for (int i = 0; i < B_DMA; ++i)
-            dma16(XB, (uint32_t)(o0 + min(kb + trB[i], len - 1)) * rbB + colB[i],
-                  st + SA + (uint32_t)(wave * B_DMA + i) * 1024u);
+        dma16(XB, (uint32_t)(o0 + min(kb + trB[i], len - 1)) * rbB + colB[i],
+              st + SA + (uint32_t)(wave * B_DMA + i) * 1024u);
     };
     auto issue = [&](int kt) {
-        issue_a(kt);
-        issue_b(kt);
+#pragma unroll
+        for (int i = 0; i < A_DMA; ++i) dma_a(kt, i);
+#pragma unroll
+        for (int i = 0; i < B_DMA; ++i) dma_b(kt, i);
     };
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -1926,52 +1926,75 @@ __global__ __launch_bounds__(WT::NTHR, WT::OCC) void gemm_wgrad_rm_kernel(const 
         const int c = col + 16 * (G & 1) + 4 * (L & 3);
         return (uint32_t)row * (BM * 2u) + (((uint32_t)c * 2u) ^ (64u * (uint32_t)(L >> 2)));
     };
+    // fragment sets: set 0 holds k-step 0 of the current K-tile, set 1 its k-step 1
+    constexpr int NM = TM * TN, EARLY = TN, SL = NM - EARLY;
+    static_assert(SL >= TM + TN, "one fragment read per MFMA slot");
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    auto frag = [&](int kt, int s2, int i, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+        const __attribute__((address_space(3))) char* sa = lbase + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
+        if (i < TM) {
+            const int col = wm * WROWS + i * 32;
+            fa[i] = tr_frag(sa, tr_addr(s2, 0, col), tr_addr(s2, 1, col));
+        } else if (i < TM + TN) {
+            const int col = wn * WCOLS + (i - TM) * 32;
+            fb[i - TM] = tr_frag(sa + SA, tr_addr(s2, 0, col), tr_addr(s2, 1, col));
+        }
+    };
+    // rows at or past the expert's end (the last K-tile) belong to the next
+    // expert or are clamped copies: zero them in the XB fragments
+    auto mask = [&](int kt, int s2, bf16x8 (&fb)[TN]) {
+        const int rem = len - kt * KT;
+        if (rem < KT) {
+            wait_lds();
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (16 * s2 + 8 * h + u >= rem) fb[j][u] = (__bf16)0.0f;
+        }
+    };
+    auto mfma1 = [&](int i, const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
+        acc[i / TN][i % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[i % TN], fa[i / TN], acc[i / TN][i % TN],
+                                                                       0, 0, 0);
+    };
     if (nk > 0) {
         issue(0);
         issue(1);
         issue(2);
+        issue(3);
+        wait_vm<3 * P>();   // K-tile 0 landed; 1, 2 and 3 may still be in flight
+        ring_barrier();
+#pragma unroll
+        for (int i = 0; i < TM + TN; ++i) frag(0, 0, i, fa0, fb0);
         for (int kt = 0; kt < nk; ++kt) {
-            wait_vm<2 * P>();   // K-tile kt landed; kt + 1 and kt + 2 may still be in flight
-            ring_barrier();     // every wave's reads of kt - 1 are complete (its MFMAs used them)
-            issue_a(kt + 3);    // into the stage of kt - 1 (its B rows after the first k-step's MFMAs)
-            const __attribute__((address_space(3))) char* sa = lbase + (uint32_t)(kt & (STAGES - 1)) * SBYTES;
-            const __attribute__((address_space(3))) char* sb = sa + SA;
-            bf16x8 fa[2][TM], fb[2][TN];
+            mask(kt, 0, fb0);
+            // k-step 0 multiplies while k-step 1 is read
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int col = wm * WROWS + i * 32;
-                    fa[s2][i] = tr_frag(sa, tr_addr(s2, 0, col), tr_addr(s2, 1, col));
-                }
-#pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int col = wn * WCOLS + j * 32;
-                    fb[s2][j] = tr_frag(sb, tr_addr(s2, 0, col), tr_addr(s2, 1, col));
-                }
+            for (int i = 0; i < NM; ++i) {
+                mfma1(i, fa0, fb0);
+                frag(kt, 1, i, fa1, fb1);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            const int rem = len - kt * KT;
-            if (rem < KT) {   // rows at or past rem belong to the next expert (or are clamped copies)
+            mask(kt, 1, fb1);
+            // k-step 1: a few MFMAs, the wait for K-tile kt + 1 and the barrier
+            // (every wave then holds all of kt in registers, so its stage is
+            // free), then, between the remaining MFMAs, the DMAs of kt + 4 into
+            // that stage and the reads of kt + 1's k-step 0
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
+            for (int i = 0; i < EARLY; ++i) mfma1(i, fa1, fb1);
+            wait_vm<2 * P>();   // K-tile kt + 1 landed; kt + 2 and kt + 3 may still be in flight
+            wait_lds();         // this wave's reads of kt are complete
+            ring_barrier();
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+            for (int i = 0; i < SL; ++i) {
+                mfma1(EARLY + i, fa1, fb1);
 #pragma unroll
-                        for (int u = 0; u < 8; ++u)
-                            if (16 * s2 + 8 * h + u >= rem) fb[s2][j][u] = (__bf16)0.0f;
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s2][j], fa[s2][i], acc[i][j], 0, 0, 0);
-                if (s2 == 0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_b(kt + 3);
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int q = i * P / SL; q < (i + 1) * P / SL; ++q) {
+                    if (q < A_DMA) dma_a(kt + 4, q);
+                    else dma_b(kt + 4, q - A_DMA);
                 }
+                frag(kt + 1, 0, i, fa0, fb0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
