@@ -94,7 +94,10 @@ extern "C" {
  * come from the forward's MXFP8 GEMM, the recompute is a bf16 GEMM of the
  * dequantised values, so the gradients differ by their accumulation order
  * only.  Any other problem with the flag is MOE_ERR_DTYPE.  moe_forward and
- * moe_forward_host_sync honour it; the staged calls ignore it. */
+ * moe_forward_host_sync honour it; the staged calls ignore it.  moe_backward
+ * must be given the problem (flags included) its moe_forward ran with: with
+ * the flag it reads a | b from fwd_ws, whose size then includes them (a
+ * forward workspace sized without the flag is MOE_ERR_WORKSPACE). */
 #define MOE_KEEP_GATE_UP     4
 
 typedef struct moe_problem {
