@@ -27,8 +27,9 @@
 // bf16 FFN, the fused backward chain, the MXFP8 GEMMs) stream K-tiles of 128
 // bytes per row (64 bf16 or 128 fp8 values) in two stages: each DMA
 // instruction then moves 8 whole 128-byte lines, so the requests to L2 carry
-// twice the bytes they carry with half lines (measured 2-5% faster).  Chunk c (of 8) of row r sits at c ^ ((r >> 1) & 7).  The
-// plain bf16 kernel (small d or H) keeps K-tiles of 64 bytes (32 values) in
+// twice the bytes they carry with half lines (measured 2-5% faster).  Chunk c
+// (of 8) of row r sits at c ^ ((r >> 1) & 7).  The plain bf16 kernel (small d
+// or H) keeps K-tiles of 64 bytes (32 values) in
 // four stages, chunk c (of 4) of row r at c ^ ((r >> 2) & 3).  Both swizzles
 // keep the 16 rows read by each 16-lane group of a fragment load on distinct
 // banks (16 lanes of a ds_read_b128 are served per cycle from 64 banks).  One
