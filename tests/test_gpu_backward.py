@@ -266,9 +266,11 @@ def test_backward_kept_gate_up(w):
 
 
 @pytest.mark.slow
-def test_full_size_backward_kept_gate_up():
-    """The same bitwise agreement at the 8-expert benchmark block."""
-    w = W.CONFIGS["bf16_e8"]
+@pytest.mark.parametrize("name", ["bf16_e8", "bf16_e128_random"])
+def test_full_size_backward_kept_gate_up(name):
+    """The same bitwise agreement at the 8-expert and 128-expert benchmark
+    blocks (the latter with a partial last M tile in most experts)."""
+    w = W.CONFIGS[name]
     print(f"[full backward kept a|b] {w.describe()}", flush=True)
     _check_kept(w)
 
