@@ -1515,12 +1515,13 @@ __device__ __forceinline__ void fp8_mfma1(int i, const i32x8 (&fa)[TL::TM], cons
 // maximum, take the shared exponent floor(log2 amax) - 8, and encode with
 // e4m3x4 (saturating round-to-nearest-even E4M3).  KEEP (EPI 1): the gate/up
 // accumulators are also stored as bf16 a | b [rows][N] (the pre-activations,
-// for the backward) through the staged row stores.
-template <class TL, int EPI, bool KEEP = false>
+// for the backward) through the staged row stores.  post(mi) runs once the
+// accumulators of row block mi have been read (the caller may reuse them).
+template <class TL, int EPI, bool KEEP, class Post>
 __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN], void* __restrict__ C,
                                              uint8_t* __restrict__ Cs, int ldc, int N, int R, const TileCoord& c,
-                                             int wm, int wn, u32x4* __restrict__ obuf,
-                                             uint16_t* __restrict__ ab = nullptr) {
+                                             int wm, int wn, u32x4* __restrict__ obuf, uint16_t* __restrict__ ab,
+                                             Post&& post) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
 #pragma unroll
@@ -1575,6 +1576,7 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
                 __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
         }
+        post(mi);
     }
 }
 
@@ -1722,12 +1724,14 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     int sa0[TM], sb0[TN], sa1[TM], sb1[TN];
 
     // one K-tile g: k-step 0 in set 0 (read during the previous K-tile), k-step 1 in set 1
-    auto ktile = [&](int g, const StreamSrc& src, const ARows& ar, const StreamSrc& prev, f32x16 (&acc)[TM][TN]) {
+    // MFMA0 false: k-step 0 was multiplied already (during the previous tile's epilogue)
+    auto ktile_impl = [&](auto mfma0, int g, const StreamSrc& src, const ARows& ar, const StreamSrc& prev,
+                          f32x16 (&acc)[TM][TN]) {
         const u32x4* stage = ring + (g & 1) * SC;
         const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (g & 1) * (BM + BN));
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            fp8_mfma1<TL>(i, fa0, fb0, sa0, sb0, acc);
+            if constexpr (decltype(mfma0)::value) fp8_mfma1<TL>(i, fa0, fb0, sa0, sb0, acc);
             frags(stage, slot, 1, i, fa1, fb1, sa1, sb1);
             // SPLIT: the B blocks of K-tile g + 1, whose A blocks and scales
             // went out after the previous K-tile's barrier (from prev, the
@@ -1754,6 +1758,12 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
             frags(nstage, nslot, 0, i, fa0, fb0, sa0, sb0);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    auto ktile = [&](int g, const StreamSrc& src, const ARows& ar, const StreamSrc& prev, f32x16 (&acc)[TM][TN]) {
+        ktile_impl(std::integral_constant<bool, true>{}, g, src, ar, prev, acc);
+    };
+    auto ktile_rest = [&](int g, const StreamSrc& src, const ARows& ar, const StreamSrc& prev, f32x16 (&acc)[TM][TN]) {
+        ktile_impl(std::integral_constant<bool, false>{}, g, src, ar, prev, acc);
     };
 
     int ti = 0;   // tiles this workgroup has finished (row-table slot of the current tile: ti % 3)
@@ -1784,20 +1794,31 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     for (int i = 0; i < TM + TN; ++i)
         frags(ring, reinterpret_cast<const uint8_t*>(sring), 0, i, fa0, fb0, sa0, sb0);
 
-    for (;;) {
-        f32x16 acc[TM][TN];
+    // With three or more K-tiles per tile the epilogue of a tile multiplies the
+    // next tile's k-step 0 (its fragments are in set 0 by then) row block by
+    // row block as it frees the accumulators, so the matrix units work while
+    // the results are stored; that tile's first K-tile then skips k-step 0.
+    const bool overlap_ok = nk >= 3;
+    f32x16 acc[TM][TN];
 #pragma unroll
-        for (int mi = 0; mi < TM; ++mi)
+    for (int mi = 0; mi < TM; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < TN; ++ni)
+        for (int ni = 0; ni < TN; ++ni)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+            for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+    bool pre = false;   // k-step 0 of this tile's first K-tile is already in acc
 
+    for (;;) {
         const StreamSrc here{c0, 1, 0};
         const bool has = tile + qa * G < total;
         const StreamSrc ahead{has ? (qa == 1 ? c1 : c2) : c0, has ? 1 : 0, has ? -qa * nk : nk - 1};
         const ARows ah = arows(here, ti % 3);
-        for (int kt = 0; kt < head; ++kt) ktile(kbase + kt, here, ah, here, acc);
+        int kt0 = 0;
+        if (pre) {   // head >= 1 here, so K-tile 0 belongs to the first phase
+            ktile_rest(kbase, here, ah, here, acc);
+            kt0 = 1;
+        }
+        for (int kt = kt0; kt < head; ++kt) ktile(kbase + kt, here, ah, here, acc);
         const ARows aa = arows(ahead, has ? (ti + qa) % 3 : ti % 3);
         for (int kt = head; kt < nk; ++kt) ktile(kbase + kt, ahead, aa, kt == head ? here : ahead, acc);
         if (SPLIT) {
@@ -1809,7 +1830,22 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
             for (int j = A_DMA; j < P; ++j) dma(ahead, aa, kbase + nk + 1, j);
         }
         // set 0 now holds k-step 0 of the next tile's first K-tile (or unused data after the last)
-        fp8_epilogue<TL, EPI, KEEP>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks, ab);
+        const bool overlap = overlap_ok && tile + G < total;
+        fp8_epilogue<TL, EPI, KEEP>(acc, C, Cs, ldc, N, R, c0, wm, wn, obuf + wave * kObufChunks, ab, [&](int mi) {
+            if (overlap) {   // row block mi of the next tile's k-step 0, from zero
+                const f32x16 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ni = 0; ni < TN; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb0[ni], fa0[mi], z, 0, 0, 0,
+                                                                                 sb0[ni], 0, sa0[mi]);
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < TN; ++ni)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
+            }
+        });
+        pre = overlap;
         if (tile + G >= total) break;
         tile += G;
         c0 = c1;
