@@ -31,10 +31,10 @@ def flags():
     B.set_gemm_grid_cap(0)
 
 
-def _inputs(w):
+def _inputs(w, keep=False):
     host = W.make_inputs(w)
     dev = {k: (None if v is None else v.to(DEV)) for k, v in host.items()}
-    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned")
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned", keep_gate_up=keep)
     return host, dev, p
 
 
@@ -82,10 +82,11 @@ def test_grouped_swiglu_give_up_is_reported(flags):
     assert torch.isfinite(ye.float()).all()
 
 
-def test_backward_give_up_is_reported(flags):
+@pytest.mark.parametrize("keep", [False, True], ids=["recompute", "kept_gate_up"])
+def test_backward_give_up_is_reported(keep, flags):
     w = W.Workload("giveup_bwd", T=1200, d=512, E=8, k=2, H=384, act="bf16", router="learned", seed=3503)
-    print(f"[fused give-up backward] {w.describe()}", flush=True)
-    _, dev, p = _inputs(w)
+    print(f"[fused give-up backward] keep={keep} {w.describe()}", flush=True)
+    _, dev, p = _inputs(w, keep)
     packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
     packed_bwd = B.pack_weights_backward(p, dev["w_gate"], dev["w_up"], dev["w_down"])
     fwd = B.Forward(p, DEV)
@@ -97,7 +98,8 @@ def test_backward_give_up_is_reported(flags):
     g = bwd(fwd, dy, packed, packed_bwd, x=dev["x"], w_router=dev["w_router"])
     assert B.fused_status(p, bwd.ws, which=B.MOE_STATUS_BACKWARD) == -6
     torch.cuda.synchronize()
-    # the gate/up and input-gradient phases gave up: dx holds NaN in every row
+    # the phases that wait gave up (gate/up and input gradient; with kept a | b
+    # the input gradient): dx holds NaN in every row
     assert torch.isnan(g["dx"].float()).any(dim=1).all()
     flags(0)
     g = bwd(fwd, dy, packed, packed_bwd, x=dev["x"], w_router=dev["w_router"])
