@@ -310,3 +310,22 @@ def test_backward_kept_gate_up_mxfp8(w):
         ref[lo:hi] = np.stack([a.reshape(n, w.H // 32, 32), b.reshape(n, w.H // 32, 32)], axis=2).reshape(n, 2 * w.H)
     ab = _kept_gate_up(fwd, w).float().cpu().numpy().astype(np.float64)
     _check("stored a | b", ab, ref, "bf16")
+
+
+@pytest.mark.parametrize("name", ["small_bf16_e8", "small_mxfp8"])
+def test_kept_gate_up_host_sync(name):
+    """moe_forward_host_sync keeps the same a | b as moe_forward (and the same y)."""
+    w = W.get(name)
+    print(f"[kept a|b host-sync] {w.describe()}", flush=True)
+    host = W.make_inputs(w)
+    dev = {k: (None if v is None else v.to(DEV)) for k, v in host.items()}
+    p = B.problem(w.T, w.d, w.E, w.k, w.H, w.act, logits_given=w.router != "learned", keep_gate_up=True)
+    packed = B.pack_weights(p, dev["w_gate"], dev["w_up"], dev["w_down"])
+    outs = []
+    for sync in (False, True):
+        f = B.Forward(p, DEV, host_sync=sync)
+        f(dev["x"], packed=packed, w_router=dev["w_router"], logits=dev["logits"])
+        torch.cuda.synchronize()
+        outs.append(f)
+    assert torch.equal(outs[0].y, outs[1].y)
+    assert torch.equal(_kept_gate_up(outs[0], w), _kept_gate_up(outs[1], w))
