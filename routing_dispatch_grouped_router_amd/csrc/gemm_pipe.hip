@@ -312,13 +312,19 @@ __device__ __forceinline__ void store_bf16_block_rows_dev(int row0, int nrows, s
 // The buffer is private to the wave, so a wait for the wave's own LDS writes
 // (and compiler barriers: lanes read what other lanes wrote) stand in for a
 // workgroup barrier.  DEV: the 16-byte stores go through the raw buffer
-// resource `rc` over C with device scope (see store_bf16_block).
-template <int RR, bool DEV = false>
+// resource `rc` over C with device scope (see store_bf16_block).  COUNTED:
+// every lane issues each of its 32 / 8 stores, through `rc` whose base is the
+// row `rofs` rows above row0 (a tile's first row) and whose size, `oob`
+// bytes, ends at that tile's last row; a lane with nothing to store gives the
+// offset `oob`, past the resource, where the hardware drops the store.  So a
+// call always issues the same number of store instructions, which callers
+// count in vmcnt.
+template <int RR, bool DEV = false, bool COUNTED = false>
 __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, size_t ldc, int row0, int nrows,
                                                      int pc, int N, const float (&g)[16], const float (&u)[16],
                                                      u32x4* __restrict__ buf,
                                                      __amdgpu_buffer_rsrc_t rc = __amdgpu_buffer_rsrc_t(),
-                                                     bool poison = false) {
+                                                     bool poison = false, int rofs = 0, uint32_t oob = 0) {
     static_assert(RR == 16 || RR == 32, "rows per round");
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, half = lane >> 5;
@@ -372,7 +378,10 @@ __device__ __forceinline__ void store_bf16_pair_rows(uint16_t* __restrict__ C, s
 #pragma unroll
         for (int j = 0; j < RR / 8; ++j) {
             const int rr = rho * RR + 8 * j + (lane >> 3);
-            if (rr < nrows && col_ok) {
+            if constexpr (COUNTED) {
+                const uint32_t off = rr < nrows && col_ok ? (uint32_t)((rofs + rr) * ldc + pc + 8 * c) * 2u : oob;
+                __builtin_amdgcn_raw_buffer_store_b128(o[j], rc, off, 0, 0);
+            } else if (rr < nrows && col_ok) {
                 if constexpr (DEV)
                     __builtin_amdgcn_raw_buffer_store_b128(
                         o[j], rc, (uint32_t)((size_t)(row0 + rr) * ldc + pc + 8 * c) * 2u, 0, kCpolSc1);
@@ -1524,6 +1533,10 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
                                              Post&& post) {
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;
+    // EPI 0: the tile's rows of C as a raw buffer resource, for the counted stores
+    const uint32_t tile_bytes = (uint32_t)c.rows * (uint32_t)ldc * 2u;
+    const __amdgpu_buffer_rsrc_t tile_rc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<uint16_t*>(C) + (size_t)c.row0 * ldc, 0, (int)tile_bytes, kRawBufferWord3);
 #pragma unroll
     for (int mi = 0; mi < TL::TM; ++mi) {
         const int r = wm * TL::WROWS + mi * 32 + (lane & 31);
@@ -1536,8 +1549,9 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
                 acc_block<TL>(acc[mi][2 * np], g);
                 acc_block<TL>(acc[mi][2 * np + 1], u);
                 const int rb = wm * TL::WROWS + mi * 32;   // tile row of the block's row 0
-                store_bf16_pair_rows<Fp8Extra<TL>::OBUF_RR>(static_cast<uint16_t*>(C), (size_t)ldc, c.row0 + rb, c.rows - rb,
-                                         c.n0 + wn * TL::WCOLS + np * 64, N, g, u, obuf);
+                store_bf16_pair_rows<Fp8Extra<TL>::OBUF_RR, false, true>(
+                    static_cast<uint16_t*>(C), (size_t)ldc, c.row0 + rb, c.rows - rb, c.n0 + wn * TL::WCOLS + np * 64,
+                    N, g, u, obuf, tile_rc, false, rb, tile_bytes);
                 __builtin_amdgcn_sched_barrier(0);   // one block pair's values in VGPRs at a time
             }
         } else {
@@ -1609,6 +1623,10 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     constexpr int NM = TL::NM, EARLY = TL::EARLY, SL = NM - EARLY;
     static_assert(SL >= TM + TN && SL > 0, "one fragment read per MFMA slot");
     constexpr int kObufChunks = EPI == 0 || KEEP ? 8 * Fp8Extra<TL>::OBUF_RR : 0;   // per wave: rows x 128 bytes
+    // store instructions per wave of an EPI 0 epilogue: TM x TN / 2 counted
+    // pair-row stores of 4 each, whatever the tile's rows and columns
+    constexpr int kEpiStores = EPI == 0 ? 2 * TM * TN : 0;
+    static_assert(kEpiStores < 64, "vmcnt range");
     __shared__ u32x4 ring[2 * SC];
     __shared__ uint32_t sring[2 * (BM + BN)];     // two scale slots: A rows then B rows
     __shared__ u32x4 obuf[kObufChunks ? TL::NW * kObufChunks : 1];
@@ -1727,6 +1745,10 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
     // MFMA0 false: k-step 0 was multiplied already (during the previous tile's epilogue)
     auto ktile_impl = [&](auto mfma0, int g, const StreamSrc& src, const ARows& ar, const StreamSrc& prev,
                           f32x16 (&acc)[TM][TN]) {
+        // after an EPI 0 epilogue (mfma0 false: the tile's first K-tile), K-tile
+        // g + 1's B blocks went out before the epilogue's kEpiStores stores, so
+        // they are not issued again and the wait leaves those stores in flight
+        constexpr bool drain = !decltype(mfma0)::value && EPI == 0 && SPLIT;
         const u32x4* stage = ring + (g & 1) * SC;
         const uint8_t* slot = reinterpret_cast<const uint8_t*>(sring + (g & 1) * (BM + BN));
 #pragma unroll
@@ -1736,11 +1758,14 @@ void gemm_fp8_pipe_kernel(const uint8_t* __restrict__ A, const uint8_t* __restri
             // SPLIT: the B blocks of K-tile g + 1, whose A blocks and scales
             // went out after the previous K-tile's barrier (from prev, the
             // source those used)
-            if (SPLIT && i < B_DMA) dma(prev, ar, g + 1, A_DMA + i);
+            if (SPLIT && !drain && i < B_DMA) dma(prev, ar, g + 1, A_DMA + i);
             __builtin_amdgcn_sched_barrier(0);
         }
         fp8_mfma<TL, 0, EARLY>(fa1, fb1, sa1, sb1, acc);
-        wait_vm<0>();   // K-tile g + 1 landed (the only DMAs in flight)
+        if constexpr (drain)
+            wait_vm<kEpiStores>();   // K-tile g + 1 landed; the stores issued after it may not have
+        else
+            wait_vm<0>();   // K-tile g + 1 landed (the only DMAs in flight)
         wait_lds();     // this wave's reads of K-tile g are complete
         ring_barrier();
         const u32x4* nstage = ring + ((g + 1) & 1) * SC;
