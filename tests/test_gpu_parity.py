@@ -483,6 +483,10 @@ CAP_CASES = [
                                     router="random", seed=3104, outlier_frac=0.01), 8),
     ("mxfp8_e16_cap24", W.Workload("cap_mx_e16", T=1200, d=512, E=16, k=4, H=256, act="mxfp8",
                                    router="zipf", seed=3105), 24),
+    # d = 384: GEMM2's second N tile holds 128 columns, whose missing half the
+    # epilogue drops; 4 K-tiles per GEMM2 tile, 3 tiles per workgroup
+    ("mxfp8_ragged_n_cap8", W.Workload("cap_mx_rn", T=1500, d=384, E=4, k=2, H=512, act="mxfp8",
+                                       router="random", seed=3106, outlier_frac=0.01), 8),
 ]
 
 
