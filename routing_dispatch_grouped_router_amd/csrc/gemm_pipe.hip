@@ -1608,7 +1608,10 @@ __device__ __forceinline__ void fp8_epilogue(const f32x16 (&acc)[TL::TM][TL::TN]
 // g + 1's k-step 0.
 // The epilogue runs between the last MFMA of a tile and the first of the next
 // while the next tile's first K-tiles are in flight; its stores count in
-// vmcnt after those DMAs, which only makes the next wait wait longer.
+// vmcnt after those DMAs, which only makes the next wait wait longer.  EPI 0
+// issues a fixed number of stores per wave, so after an overlapped epilogue
+// the next tile's first K-tile waits for its own DMAs only and the stores
+// drain during that K-tile.
 // EPI 0: C = A B (bf16 out);  1: C = MXFP8(silu(A Bgate) * (A Bup)) along N/2, with KEEP also a | b into ab
 template <class TL, int EPI, bool SPLIT, bool KEEP>
 __global__ __launch_bounds__(TL::NTHR) __attribute__((amdgpu_waves_per_eu(TL::NW / 4, TL::NW / 4)))
